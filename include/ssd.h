@@ -1,0 +1,128 @@
+/*
+ * ssd.h -- C ABI of the MI355X (gfx950) Mamba-2 SSD chunked-scan library (libssd.so).
+ *
+ * The operation.  For every batch row b and head h (group g = h / (H / G)):
+ *     dt'_t = softplus(dt[b,t,h] + dt_bias[h])          softplus(v) = log(1 + e^v)
+ *     h_t   = exp(dt'_t * A[h]) * h_{t-1} + dt'_t * x[b,t,h,:]^T B[b,t,g,:]     (P x N state)
+ *     y_t   = h_t C[b,t,g,:]^T + D[h,:] * x[b,t,h,:]
+ * with h_{-1} = initial_state (zeros when NULL) and final_state = h_{L-1}.
+ * Sources: "Agent 228: MAMBA-2 Reference Implementations Comparison", section 2.2 (SSD as a
+ * 1-semiseparable masked form, A scalar per head) and section 3.2 (softplus(dt + dt_bias),
+ * decay exp(A dt'), input term B dt', chunked evaluation); "Agent 228: MAMBA-2 Implementation
+ * Gaps", Gap 1 (diagonal blocks within a chunk plus the carried inter-chunk state), Gap 3
+ * (softplus), Gap 4 (D skip term); "MAMBA2 Inference Optimization Report", Step 4 (the last
+ * state is kept for stateful inference).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are caller-owned DEVICE pointers on the current HIP device, row-major
+ *    and contiguous with the layouts given below.  The library never allocates, frees,
+ *    synchronises or prints.  Work is enqueued asynchronously on `stream` (0 = null stream).
+ *  - Element type of x, dt, B, C and y is dims->dtype (fp32, or bf16 = the upper 16 bits of an
+ *    IEEE fp32, stored in 2 bytes).  dt_bias, A, D and every state are always fp32.
+ *  - Alignment: x, B, C, y, states and the workspace must be 16-byte aligned; dt, dt_bias, A
+ *    and D must be aligned to their element size.
+ *  - Validation runs completely before anything is launched.  On any error nothing is
+ *    launched and no output is written.  A failure reported by the HIP runtime at launch
+ *    is returned as SSD_ERR_HIP.
+ *  - Calls are stateless and re-entrant; concurrent calls on different streams need separate
+ *    workspaces and outputs.
+ */
+#ifndef SSD_H_
+#define SSD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SSD_OK = 0,
+  SSD_ERR_INVALID_ARG = 1,   /* NULL where a pointer is required, negative size, bad alignment */
+  SSD_ERR_UNSUPPORTED = 2,   /* valid but not implemented: chunk size, headdim, dstate, dtype */
+  SSD_ERR_DEVICE_PTR = 3,    /* a pointer is not device memory of the current device */
+  SSD_ERR_WORKSPACE = 4,     /* workspace NULL or smaller than ssd_fwd_workspace_size() */
+  SSD_ERR_HIP = 5            /* the HIP runtime reported an error when launching */
+} ssd_status_t;
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype_t;
+
+/* Problem sizes.  batch >= 0, seqlen >= 0 (ssd_step ignores it), nheads >= 1,
+ * ngroups >= 1 with nheads % ngroups == 0.  Supported (else SSD_ERR_UNSUPPORTED):
+ * headdim in {16, 32, 64}; dstate in {16, 32, 64} for SSD_F32 and {32, 64, 128} for SSD_BF16. */
+typedef struct {
+  int64_t batch;     /* B */
+  int64_t seqlen;    /* L */
+  int64_t nheads;    /* H */
+  int64_t headdim;   /* P */
+  int64_t dstate;    /* N */
+  int64_t ngroups;   /* G */
+  int32_t dtype;     /* ssd_dtype_t */
+} ssd_dims_t;
+
+/* Bytes of device workspace ssd_fwd needs for these sizes and chunk size; 0 when the
+ * arguments are invalid or unsupported.  Pure host arithmetic.  Layout (each region
+ * 256-byte aligned, nc = ceil(L / chunk_size)):
+ *   [0] dt'  (B, H, nc, chunk_size) fp32   softplus(dt + dt_bias); 0 past the end of the sequence
+ *   [1] dAcs (B, H, nc, chunk_size) fp32   inclusive in-chunk cumulative sum of dt' * A
+ *   [2] states (B, nc, H, P, N) fp32       first the state each chunk contributes (decayed to
+ *                                          the chunk end), then overwritten in place by the
+ *                                          state entering each chunk
+ * The contents after a call are those intermediates and may be inspected. */
+size_t ssd_fwd_workspace_size(const ssd_dims_t* dims, int chunk_size);
+
+/* Chunked SSD forward over a whole sequence (the chunked diagonal-block / carried-state
+ * evaluation of the reference-comparison page, section 3.2, and of Gap 1 of the
+ * implementation-gaps page).  Four kernels run in order on `stream`: chunk_cumsum,
+ * chunk_state, state_passing, chunk_scan.
+ *   x             (B, L, H, P)  dtype       input sequence
+ *   dt            (B, L, H)     dtype       raw step, before bias and softplus
+ *   dt_bias, A    (H)           fp32        A is used as given (pass negative values)
+ *   B, C          (B, L, G, N)  dtype
+ *   D             (H, P)        fp32        NULL means no skip term
+ *   chunk_size    64, 128 or 256; the result does not depend on it beyond rounding
+ *   initial_state (B, H, P, N)  fp32        NULL means zeros
+ *   y             (B, L, H, P)  dtype       output (may not alias an input)
+ *   final_state   (B, H, P, N)  fp32        NULL means not wanted; may alias initial_state
+ *   workspace     >= ssd_fwd_workspace_size(dims, chunk_size) bytes of device memory
+ * batch == 0 is a no-op.  seqlen == 0 writes only final_state (= initial_state or zeros). */
+ssd_status_t ssd_fwd(const ssd_dims_t* dims,
+                     const void* x, const void* dt, const float* dt_bias, const float* A,
+                     const void* B, const void* C, const float* D, int chunk_size,
+                     const float* initial_state, void* y, float* final_state,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ssd_fwd with per-kernel timing: identical arguments and results, plus `stage_events`,
+ * an array of 5 events created by the caller (hipEventCreate).  stage_events[k] is
+ * recorded on `stream` just before kernel k (0 chunk_cumsum, 1 chunk_state,
+ * 2 state_passing, 3 chunk_scan) and stage_events[4] after the last one.  For
+ * measurement tools; NULL stage_events behaves exactly like ssd_fwd. */
+ssd_status_t ssd_fwd_timed(const ssd_dims_t* dims,
+                           const void* x, const void* dt, const float* dt_bias, const float* A,
+                           const void* B, const void* C, const float* D, int chunk_size,
+                           const float* initial_state, void* y, float* final_state,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream,
+                           hipEvent_t* stage_events);
+
+/* One recurrent decode step for every (b, h) ("MAMBA2 Inference Optimization Report", Step 4:
+ * the carried hidden state; same discretisation as ssd_fwd).  dims->seqlen is ignored.
+ *   state  (B, H, P, N) fp32    read and overwritten in place with h_t
+ *   x      (B, H, P)    dtype   dt (B, H) dtype   dt_bias, A (H) fp32
+ *   B, C   (B, G, N)    dtype   D (H, P) fp32 or NULL
+ *   y      (B, H, P)    dtype   output, computed from the UPDATED state
+ * One kernel; no workspace.  batch == 0 is a no-op. */
+ssd_status_t ssd_step(const ssd_dims_t* dims, float* state,
+                      const void* x, const void* dt, const float* dt_bias, const float* A,
+                      const void* B, const void* C, const float* D,
+                      void* y, hipStream_t stream);
+
+/* Static English description of a status code; never NULL. */
+const char* ssd_status_string(ssd_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_H_ */

@@ -1,0 +1,25 @@
+/*
+ * ssd_tuning.h -- process-wide launch-shape knobs of libssd.so, for measurement tools.
+ *
+ * Results never depend on these settings (only the grouping of work into workgroups does).
+ * The setting is global to the process and not synchronised: set it before issuing work,
+ * never while another thread calls into the library.
+ */
+#ifndef SSD_TUNING_H_
+#define SSD_TUNING_H_
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* key 0: heads per chunk_scan workgroup (heads of one group sharing one C B^T evaluation);
+ *        0 restores the built-in choice; ignored unless it divides nheads / ngroups.
+ * key 1: minimum chunk_scan workgroup count the built-in choice aims for (default 512).
+ * Unknown keys are ignored. */
+void ssd_tune_set(int key, int value);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_TUNING_H_ */

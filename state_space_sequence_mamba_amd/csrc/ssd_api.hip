@@ -1,0 +1,248 @@
+// C ABI of libssd.so: argument validation, workspace carving and kernel launch order.
+// Declarations and the contract live in include/ssd.h.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "ssd.h"
+#include "ssd_tuning.h"
+#include "ssd_launch.h"
+
+namespace {
+
+constexpr size_t kRegionAlign = 256;
+
+size_t align_up(size_t v) { return (v + kRegionAlign - 1) / kRegionAlign * kRegionAlign; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t elem_bytes(int dtype) { return dtype == SSD_F32 ? 4 : 2; }
+
+// Shape checks common to both entry points.  Returns SSD_OK or the error.
+ssd_status_t check_dims(const ssd_dims_t* d, bool need_seqlen) {
+  if (!d) return SSD_ERR_INVALID_ARG;
+  if (d->batch < 0 || d->nheads < 1 || d->headdim < 1 || d->dstate < 1 || d->ngroups < 1) return SSD_ERR_INVALID_ARG;
+  if (need_seqlen && d->seqlen < 0) return SSD_ERR_INVALID_ARG;
+  if (d->nheads % d->ngroups != 0) return SSD_ERR_INVALID_ARG;
+  if (d->dtype != SSD_F32 && d->dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
+  if (!ssd::shape_supported(d->dtype, (int)d->headdim, (int)d->dstate)) return SSD_ERR_UNSUPPORTED;
+  // 32-bit index arithmetic bounds of the launchers (grid sizes, per-sequence offsets)
+  if (d->batch > 65535 || d->nheads > 65535 || d->seqlen > (int64_t)1 << 30) return SSD_ERR_UNSUPPORTED;
+  return SSD_OK;
+}
+
+bool chunk_ok(int q) { return q == 64 || q == 128 || q == 256; }
+
+struct WsLayout {
+  size_t dtp_off, dacs_off, states_off, total;
+};
+
+WsLayout ws_layout(const ssd_dims_t* d, int Q) {
+  const int64_t nc = (d->seqlen + Q - 1) / Q;
+  WsLayout w;
+  const size_t cum = align_up((size_t)d->batch * d->nheads * nc * Q * sizeof(float));
+  const size_t st = align_up((size_t)d->batch * nc * d->nheads * d->headdim * d->dstate * sizeof(float));
+  w.dtp_off = 0;
+  w.dacs_off = cum;
+  w.states_off = 2 * cum;
+  w.total = 2 * cum + st;
+  return w;
+}
+
+// Is p device memory usable by the current device?
+bool device_ptr_ok(const void* p) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();  // clear the sticky error the failed query leaves
+    return false;
+  }
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  if (attr.type == hipMemoryTypeDevice) return attr.device == dev;
+  return attr.type == hipMemoryTypeManaged;
+}
+
+// chunk_scan heads per workgroup: heads of one group share a C B^T evaluation; more heads
+// per workgroup amortise it further but leave fewer workgroups to fill 256 CUs.  Choose the
+// largest divisor of H/G that still leaves at least `target` workgroups.
+int g_tune_heads_per_block = 0;  // 0 = heuristic
+int g_tune_min_blocks = 512;
+
+int pick_heads_per_block(int B, int nc, int H, int G, int Q) {
+  const int hpg = H / G;
+  const int pairs = Q / 32;
+  const int npg = pairs / (pairs < 4 ? pairs : 4);
+  if (g_tune_heads_per_block > 0 && hpg % g_tune_heads_per_block == 0) return g_tune_heads_per_block;
+  const long base = (long)B * nc * npg * G;  // workgroups per head of a group
+  int best = 1;
+  for (int hb = 1; hb <= hpg; ++hb) {
+    if (hpg % hb) continue;
+    if (base * (hpg / hb) >= g_tune_min_blocks) best = hb;
+  }
+  return best;
+}
+
+ssd_status_t fwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, const float* dt_bias,
+                      const float* A, const void* B, const void* C, const float* D, int chunk_size,
+                      const float* initial_state, void* y, float* final_state, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream, hipEvent_t* ev) {
+  ssd_status_t st = check_dims(dims, true);
+  if (st != SSD_OK) return st;
+  if (!chunk_ok(chunk_size)) return SSD_ERR_UNSUPPORTED;
+  if (dims->batch == 0) return SSD_OK;
+  const bool has_seq = dims->seqlen > 0;
+  const size_t eb = elem_bytes(dims->dtype);
+
+  // required pointers and alignment
+  if (has_seq) {
+    if (!x || !dt || !dt_bias || !A || !B || !C || !y) return SSD_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16)) return SSD_ERR_INVALID_ARG;
+    if (!aligned(dt, eb) || !aligned(dt_bias, 4) || !aligned(A, 4) || (D && !aligned(D, 4)))
+      return SSD_ERR_INVALID_ARG;
+  }
+  if ((initial_state && !aligned(initial_state, 16)) || (final_state && !aligned(final_state, 16)))
+    return SSD_ERR_INVALID_ARG;
+  const WsLayout wl = ws_layout(dims, chunk_size);
+  if (has_seq) {
+    if (!workspace || workspace_bytes < wl.total) return SSD_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return SSD_ERR_INVALID_ARG;
+  }
+  // every pointer must be device memory of the current device
+  const void* ptrs[] = {x, dt, dt_bias, A, B, C, D, initial_state, y, final_state, has_seq ? workspace : nullptr};
+  for (const void* p : ptrs)
+    if (p && !device_ptr_ok(p)) return SSD_ERR_DEVICE_PTR;
+
+  ssd::FwdArgs a;
+  a.B = (int)dims->batch;
+  a.L = (int)dims->seqlen;
+  a.H = (int)dims->nheads;
+  a.P = (int)dims->headdim;
+  a.N = (int)dims->dstate;
+  a.G = (int)dims->ngroups;
+  a.Q = chunk_size;
+  a.nc = (int)((dims->seqlen + chunk_size - 1) / chunk_size);
+  a.dtype = dims->dtype;
+  a.x = x;
+  a.dt = dt;
+  a.dt_bias = dt_bias;
+  a.A = A;
+  a.Bm = B;
+  a.Cm = C;
+  a.D = D;
+  a.init = initial_state;
+  a.y = y;
+  a.final_state = final_state;
+  char* ws = static_cast<char*>(workspace);
+  a.dtp = has_seq ? reinterpret_cast<float*>(ws + wl.dtp_off) : nullptr;
+  a.dAcs = has_seq ? reinterpret_cast<float*>(ws + wl.dacs_off) : nullptr;
+  a.states = has_seq ? reinterpret_cast<float*>(ws + wl.states_off) : nullptr;
+  a.heads_per_block = pick_heads_per_block(a.B, a.nc, a.H, a.G, a.Q);
+
+  if (!has_seq) {
+    // no tokens: final_state = initial_state (or zeros); state_passing with zero chunks
+    if (!final_state) return SSD_OK;
+    return ssd::launch_state_passing(a, stream) == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+  }
+
+  hipError_t e = hipSuccess;
+  if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return SSD_ERR_HIP;
+  e = ssd::launch_chunk_cumsum(a, stream);
+  if (e != hipSuccess) return SSD_ERR_HIP;
+  if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return SSD_ERR_HIP;
+  e = ssd::launch_chunk_state(a, stream);
+  if (e != hipSuccess) return SSD_ERR_HIP;
+  if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return SSD_ERR_HIP;
+  e = ssd::launch_state_passing(a, stream);
+  if (e != hipSuccess) return SSD_ERR_HIP;
+  if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return SSD_ERR_HIP;
+  e = ssd::launch_chunk_scan(a, stream);
+  if (e != hipSuccess) return SSD_ERR_HIP;
+  if (ev && hipEventRecord(ev[4], stream) != hipSuccess) return SSD_ERR_HIP;
+  return SSD_OK;
+}
+
+}  // namespace
+
+namespace ssd {
+bool shape_supported(int dtype, int P, int N) {
+#define SSD_CASE(T, P_, N_) \
+  if (dtype == SSD_DTYPE_CODE_##T && P == P_ && N == N_) return true;
+  SSD_FOR_EACH_SHAPE(SSD_CASE)
+#undef SSD_CASE
+  return false;
+}
+}  // namespace ssd
+
+extern "C" {
+
+size_t ssd_fwd_workspace_size(const ssd_dims_t* dims, int chunk_size) {
+  if (check_dims(dims, true) != SSD_OK || !chunk_ok(chunk_size)) return 0;
+  return ws_layout(dims, chunk_size).total;
+}
+
+ssd_status_t ssd_fwd(const ssd_dims_t* dims, const void* x, const void* dt, const float* dt_bias, const float* A,
+                     const void* B, const void* C, const float* D, int chunk_size, const float* initial_state,
+                     void* y, float* final_state, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return fwd_impl(dims, x, dt, dt_bias, A, B, C, D, chunk_size, initial_state, y, final_state, workspace,
+                  workspace_bytes, stream, nullptr);
+}
+
+ssd_status_t ssd_fwd_timed(const ssd_dims_t* dims, const void* x, const void* dt, const float* dt_bias,
+                           const float* A, const void* B, const void* C, const float* D, int chunk_size,
+                           const float* initial_state, void* y, float* final_state, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream, hipEvent_t* stage_events) {
+  return fwd_impl(dims, x, dt, dt_bias, A, B, C, D, chunk_size, initial_state, y, final_state, workspace,
+                  workspace_bytes, stream, stage_events);
+}
+
+ssd_status_t ssd_step(const ssd_dims_t* dims, float* state, const void* x, const void* dt, const float* dt_bias,
+                      const float* A, const void* B, const void* C, const float* D, void* y, hipStream_t stream) {
+  ssd_status_t st = check_dims(dims, false);
+  if (st != SSD_OK) return st;
+  if (dims->batch == 0) return SSD_OK;
+  const size_t eb = elem_bytes(dims->dtype);
+  if (!state || !x || !dt || !dt_bias || !A || !B || !C || !y) return SSD_ERR_INVALID_ARG;
+  if (!aligned(state, 16) || !aligned(x, eb) || !aligned(dt, eb) || !aligned(B, eb) || !aligned(C, eb) ||
+      !aligned(y, eb) || !aligned(dt_bias, 4) || !aligned(A, 4) || (D && !aligned(D, 4)))
+    return SSD_ERR_INVALID_ARG;
+  const void* ptrs[] = {state, x, dt, dt_bias, A, B, C, D, y};
+  for (const void* p : ptrs)
+    if (p && !device_ptr_ok(p)) return SSD_ERR_DEVICE_PTR;
+  ssd::StepArgs a;
+  a.B = (int)dims->batch;
+  a.H = (int)dims->nheads;
+  a.P = (int)dims->headdim;
+  a.N = (int)dims->dstate;
+  a.G = (int)dims->ngroups;
+  a.dtype = dims->dtype;
+  a.state = state;
+  a.x = x;
+  a.dt = dt;
+  a.dt_bias = dt_bias;
+  a.A = A;
+  a.Bm = B;
+  a.Cm = C;
+  a.D = D;
+  a.y = y;
+  return ssd::launch_ssd_step(a, stream) == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
+const char* ssd_status_string(ssd_status_t s) {
+  switch (s) {
+    case SSD_OK: return "success";
+    case SSD_ERR_INVALID_ARG: return "invalid argument (null pointer, negative size or misaligned pointer)";
+    case SSD_ERR_UNSUPPORTED: return "unsupported size, chunk size or dtype";
+    case SSD_ERR_DEVICE_PTR: return "pointer is not device memory of the current device";
+    case SSD_ERR_WORKSPACE: return "workspace missing or too small";
+    case SSD_ERR_HIP: return "HIP runtime error at launch";
+  }
+  return "unknown status";
+}
+
+void ssd_tune_set(int key, int value) {
+  if (key == 0) g_tune_heads_per_block = value;
+  if (key == 1) g_tune_min_blocks = value > 0 ? value : 512;
+}
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// Host-side launch interface between the C ABI (ssd_api.hip) and the kernel files.
+// Every launcher assumes its arguments were validated by the API layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssd {
+
+enum { DT_F32 = 0, DT_BF16 = 1 };
+
+struct FwdArgs {
+  int B, L, H, P, N, G, Q, nc;
+  int dtype;
+  const void* x;
+  const void* dt;
+  const float* dt_bias;
+  const float* A;
+  const void* Bm;
+  const void* Cm;
+  const float* D;          // may be null
+  const float* init;       // may be null
+  void* y;
+  float* final_state;      // may be null
+  float* dtp;              // workspace (B, H, nc, Q)
+  float* dAcs;             // workspace (B, H, nc, Q)
+  float* states;           // workspace (B, nc, H, P, N)
+  int heads_per_block;     // chunk_scan: heads sharing one C B^T evaluation (divides H / G)
+};
+
+struct StepArgs {
+  int B, H, P, N, G;
+  int dtype;
+  float* state;
+  const void* x;
+  const void* dt;
+  const float* dt_bias;
+  const float* A;
+  const void* Bm;
+  const void* Cm;
+  const float* D;
+  void* y;
+};
+
+// true when a kernel instantiation exists for (dtype, P, N)
+bool shape_supported(int dtype, int P, int N);
+
+hipError_t launch_chunk_cumsum(const FwdArgs& a, hipStream_t s);
+hipError_t launch_chunk_state(const FwdArgs& a, hipStream_t s);
+hipError_t launch_state_passing(const FwdArgs& a, hipStream_t s);
+hipError_t launch_chunk_scan(const FwdArgs& a, hipStream_t s);
+hipError_t launch_ssd_step(const StepArgs& a, hipStream_t s);
+
+}  // namespace ssd
+
+// (dtype, P, N) instantiation lists.  fp32 MFMA contracts over N in steps of 4, bf16 in
+// steps of 32, hence the different dstate sets.
+#define SSD_FOR_EACH_SHAPE(X) \
+  X(float, 16, 16) X(float, 16, 32) X(float, 16, 64) \
+  X(float, 32, 16) X(float, 32, 32) X(float, 32, 64) \
+  X(float, 64, 16) X(float, 64, 32) X(float, 64, 64) \
+  X(__bf16, 16, 32) X(__bf16, 16, 64) X(__bf16, 16, 128) \
+  X(__bf16, 32, 32) X(__bf16, 32, 64) X(__bf16, 32, 128) \
+  X(__bf16, 64, 32) X(__bf16, 64, 64) X(__bf16, 64, 128)
+
+#define SSD_DTYPE_CODE_float 0
+#define SSD_DTYPE_CODE___bf16 1

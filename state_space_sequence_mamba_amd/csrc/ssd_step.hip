@@ -1,0 +1,99 @@
+// ssd_step: one recurrent decode step for every (b, h),
+//     dt' = softplus(dt + dt_bias),  a = exp(dt' A),
+//     state[p,n] <- a * state[p,n] + dt' x[p] B[n],   y[p] = sum_n state[p,n] C[n] + D[p] x[p]
+// (the carried hidden state of stateful inference: "MAMBA2 Inference Optimization Report",
+// Step 4; the discretisation of section 3.2 of "Agent 228: MAMBA-2 Reference Implementations
+// Comparison"; D skip from Gap 4 of "Agent 228: MAMBA-2 Implementation Gaps").
+//
+// Bandwidth bound: the fp32 state is read and written once; everything else is small.
+// One 256-thread workgroup per (b, h).  A row of N floats is covered by N/4 consecutive
+// lanes (one float4 each), so the state tile streams with fully coalesced 16-byte accesses
+// and the reduction over n is a butterfly of N/4 lanes inside a wavefront.  All state loads
+// of a thread are issued before any use.
+#include "ssd_common.h"
+#include "ssd_launch.h"
+
+namespace ssd {
+
+template <typename T, int P, int N>
+__global__ __launch_bounds__(256) void ssd_step_kernel(float* __restrict__ state,
+                                                       const T* __restrict__ x,
+                                                       const T* __restrict__ dt,
+                                                       const float* __restrict__ dt_bias,
+                                                       const float* __restrict__ A,
+                                                       const T* __restrict__ Bm,
+                                                       const T* __restrict__ Cm,
+                                                       const float* __restrict__ Dw,
+                                                       T* __restrict__ y, int H, int G) {
+  constexpr int TPR = N / 4;           // lanes per state row
+  constexpr int RPP = 256 / TPR;       // rows per pass
+  constexpr int NPASS = (P + RPP - 1) / RPP;
+  const int bh = blockIdx.x;
+  const int h = bh % H, b = bh / H;
+  const int g = h / (H / G);
+  const int tid = threadIdx.x;
+  const int col = (tid % TPR) * 4;
+  const int row0 = tid / TPR;
+
+  const float d = softplus(to_f32(dt[bh]) + dt_bias[h]);
+  const float a = expf(d * A[h]);
+  float bv[4], cv[4];
+  const T* Bp = Bm + ((size_t)b * G + g) * N + col;
+  const T* Cp = Cm + ((size_t)b * G + g) * N + col;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    bv[e] = to_f32(Bp[e]);
+    cv[e] = to_f32(Cp[e]);
+  }
+
+  float* st = state + (size_t)bh * P * N;
+  float4 s[NPASS];
+  float xv[NPASS];
+#pragma unroll
+  for (int u = 0; u < NPASS; ++u) {
+    const int p = row0 + u * RPP;
+    if (p < P) {
+      s[u] = *reinterpret_cast<const float4*>(st + (size_t)p * N + col);
+      xv[u] = to_f32(x[(size_t)bh * P + p]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NPASS; ++u) {
+    const int p = row0 + u * RPP;
+    if (p < P) {
+      const float dx = d * xv[u];
+      float4 v = s[u];
+      v.x = a * v.x + dx * bv[0];
+      v.y = a * v.y + dx * bv[1];
+      v.z = a * v.z + dx * bv[2];
+      v.w = a * v.w + dx * bv[3];
+      *reinterpret_cast<float4*>(st + (size_t)p * N + col) = v;
+      float part = v.x * cv[0] + v.y * cv[1] + v.z * cv[2] + v.w * cv[3];
+#pragma unroll
+      for (int off = TPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+      if ((tid % TPR) == 0) {
+        const float dw = Dw ? Dw[(size_t)h * P + p] : 0.f;
+        y[(size_t)bh * P + p] = from_f32<T>(part + dw * xv[u]);
+      }
+    }
+  }
+}
+
+template <typename T, int P, int N>
+static hipError_t launch_step_impl(const StepArgs& a, hipStream_t s) {
+  const unsigned nblocks = (unsigned)a.B * a.H;
+  ssd_step_kernel<T, P, N><<<nblocks, 256, 0, s>>>(
+      a.state, static_cast<const T*>(a.x), static_cast<const T*>(a.dt), a.dt_bias, a.A,
+      static_cast<const T*>(a.Bm), static_cast<const T*>(a.Cm), a.D, static_cast<T*>(a.y), a.H, a.G);
+  return hipGetLastError();
+}
+
+hipError_t launch_ssd_step(const StepArgs& a, hipStream_t s) {
+#define SSD_CASE(T, P_, N_) \
+  if (a.dtype == SSD_DTYPE_CODE_##T && a.P == P_ && a.N == N_) return launch_step_impl<T, P_, N_>(a, s);
+  SSD_FOR_EACH_SHAPE(SSD_CASE)
+#undef SSD_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ssd

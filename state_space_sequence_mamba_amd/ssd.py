@@ -1,0 +1,167 @@
+"""Thin Python binding of libssd.so (include/ssd.h).
+
+Argument marshalling only: torch supplies device memory and the stream; every step of
+the scan runs in the library's HIP kernels.  There is no fallback: if libssd.so is
+missing or cannot be loaded, every call raises.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssd.so")
+
+SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_DEVICE_PTR, SSD_ERR_WORKSPACE, SSD_ERR_HIP = range(6)
+SSD_F32, SSD_BF16 = 0, 1
+
+_DTYPES = {torch.float32: SSD_F32, torch.bfloat16: SSD_BF16}
+
+
+class ssd_dims_t(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+                ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+                ("dtype", ctypes.c_int32)]
+
+
+class SsdError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {ssd_status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def load_library():
+    """Load libssd.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} not found: build it with `python -m state_space_sequence_mamba_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, f32p, i32, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    dims_p = ctypes.POINTER(ssd_dims_t)
+    lib.ssd_fwd_workspace_size.argtypes = [dims_p, i32]
+    lib.ssd_fwd_workspace_size.restype = sz
+    fwd_args = [dims_p, vp, vp, f32p, f32p, vp, vp, f32p, i32, f32p, vp, f32p, vp, sz, vp]
+    lib.ssd_fwd.argtypes = fwd_args
+    lib.ssd_fwd.restype = i32
+    lib.ssd_fwd_timed.argtypes = fwd_args + [vp]
+    lib.ssd_fwd_timed.restype = i32
+    lib.ssd_step.argtypes = [dims_p, f32p, vp, vp, f32p, f32p, vp, vp, f32p, vp, vp]
+    lib.ssd_step.restype = i32
+    lib.ssd_status_string.argtypes = [i32]
+    lib.ssd_status_string.restype = ctypes.c_char_p
+    lib.ssd_tune_set.argtypes = [i32, i32]
+    lib.ssd_tune_set.restype = None
+    _lib = lib
+    return lib
+
+
+def ssd_status_string(status):
+    return load_library().ssd_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, dtype):
+    code = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return ssd_dims_t(batch, seqlen, nheads, headdim, dstate, ngroups, code)
+
+
+def ssd_fwd_workspace_size(dims, chunk_size):
+    return int(load_library().ssd_fwd_workspace_size(ctypes.byref(dims), int(chunk_size)))
+
+
+def _check_fwd_shapes(x, dt, dt_bias, A, B, C, D, initial_state):
+    if x.dim() != 4 or dt.dim() != 3 or B.dim() != 4 or C.dim() != 4:
+        raise ValueError("x (B,L,H,P), dt (B,L,H), B and C (B,L,G,N) expected")
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if tuple(dt.shape) != (b, L, H) or tuple(B.shape) != (b, L, G, N) or tuple(C.shape) != (b, L, G, N):
+        raise ValueError("inconsistent x / dt / B / C shapes")
+    if tuple(dt_bias.shape) != (H,) or tuple(A.shape) != (H,):
+        raise ValueError("dt_bias and A must have shape (H,)")
+    if D is not None and tuple(D.shape) != (H, P):
+        raise ValueError("D must have shape (H, P)")
+    if initial_state is not None and tuple(initial_state.shape) != (b, H, P, N):
+        raise ValueError("initial_state must have shape (B, H, P, N)")
+    for t in (dt, B, C):
+        if t.dtype != x.dtype:
+            raise ValueError("x, dt, B and C must share one dtype")
+    for t in (dt_bias, A, D, initial_state):
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError("dt_bias, A, D and initial_state must be float32")
+    for t in (x, dt, dt_bias, A, B, C, D, initial_state):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    return b, L, H, P, N, G
+
+
+def ssd_fwd(x, dt, dt_bias, A, B, C, D=None, chunk_size=256, initial_state=None, y=None,
+            final_state=None, return_final_state=True, workspace=None, stream=None, stage_events=None):
+    """Chunked SSD forward.  Returns (y, final_state) (final_state is None if not requested).
+
+    Output and workspace tensors are allocated with torch when not given.  `stage_events`
+    (5 raw hipEvent_t handles as ints) selects the timed entry point.
+    """
+    b, L, H, P, N, G = _check_fwd_shapes(x, dt, dt_bias, A, B, C, D, initial_state)
+    dims = make_dims(b, L, H, P, N, G, x.dtype)
+    lib = load_library()
+    if y is None:
+        y = torch.empty_like(x)
+    if final_state is None and return_final_state:
+        final_state = torch.empty(b, H, P, N, dtype=torch.float32, device=x.device)
+    ws_bytes = ssd_fwd_workspace_size(dims, chunk_size)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+    args = [ctypes.byref(dims), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+            int(chunk_size), _ptr(initial_state), _ptr(y), _ptr(final_state), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream)]
+    if stage_events is None:
+        st = lib.ssd_fwd(*args)
+    else:
+        arr = (ctypes.c_void_p * 5)(*stage_events)
+        st = lib.ssd_fwd_timed(*args, arr)
+    if st != SSD_OK:
+        raise SsdError(st, "ssd_fwd")
+    return y, final_state
+
+
+def ssd_step(state, x, dt, dt_bias, A, B, C, D=None, y=None, stream=None):
+    """One decode step: updates `state` (B,H,P,N) fp32 in place and returns y (B,H,P)."""
+    if state.dim() != 4 or x.dim() != 3 or dt.dim() != 2 or B.dim() != 3 or C.dim() != 3:
+        raise ValueError("state (B,H,P,N), x (B,H,P), dt (B,H), B and C (B,G,N) expected")
+    b, H, P, N = state.shape
+    G = B.shape[1]
+    if tuple(x.shape) != (b, H, P) or tuple(dt.shape) != (b, H) or tuple(B.shape) != (b, G, N) \
+            or tuple(C.shape) != (b, G, N):
+        raise ValueError("inconsistent state / x / dt / B / C shapes")
+    if state.dtype != torch.float32:
+        raise ValueError("state must be float32")
+    for t in (state, x, dt, dt_bias, A, B, C, D):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    dims = make_dims(b, 1, H, P, N, G, x.dtype)
+    if y is None:
+        y = torch.empty_like(x)
+    st = load_library().ssd_step(ctypes.byref(dims), _ptr(state), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A),
+                                 _ptr(B), _ptr(C), _ptr(D), _ptr(y), _stream(stream))
+    if st != SSD_OK:
+        raise SsdError(st, "ssd_step")
+    return y
+
+
+def tune_set(key, value):
+    """Launch-shape knob (include/ssd_tuning.h); results never depend on it."""
+    load_library().ssd_tune_set(int(key), int(value))

@@ -1,0 +1,133 @@
+"""CPU-side checks of the C ABI: the library loads, exports every declared symbol, and its
+host-only logic (workspace sizing, status strings, argument validation that returns before
+any HIP call) behaves as include/ssd.h states.  No kernel is launched here."""
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+from state_space_sequence_mamba_amd import ssd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b(ssd_\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ssd.LIB_PATH):
+        pytest.fail("libssd.so is not built (run __graft_entry__.build())")
+    return ssd.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert {"ssd_fwd", "ssd_fwd_timed", "ssd_step", "ssd_fwd_workspace_size", "ssd_status_string",
+            "ssd_tune_set"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", ssd.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert set(names) <= exported
+
+
+def test_library_is_built_for_gfx950():
+    out = subprocess.run(["strings", ssd.LIB_PATH], capture_output=True, text=True).stdout
+    assert "gfx950" in out
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        s = ssd.ssd_status_string(code)
+        assert s and s != "unknown status"
+    assert ssd.ssd_status_string(99) == "unknown status"
+
+
+def _dims(**kw):
+    d = dict(batch=1, seqlen=256, nheads=4, headdim=16, dstate=16, ngroups=1, dtype=0)
+    d.update(kw)
+    return ssd.ssd_dims_t(**d)
+
+
+def test_workspace_size_layout(lib):
+    # 1 x 256 tokens, H=4, Q=64 -> nc=4; dt' and cumsum: 4*4*64 floats = 4096 B each (256-aligned);
+    # states: 4 chunks * 4 heads * 16 * 16 floats = 16384 B
+    assert ssd.ssd_fwd_workspace_size(_dims(), 64) == 2 * 4096 + 16384
+    # ragged: L=300, Q=128 -> nc=3; 2*4*3*128*4 = 12288 B each; states 2*3*4*64*128*4 = 786432 B
+    d = _dims(batch=2, seqlen=300, headdim=64, dstate=128, dtype=1)
+    assert ssd.ssd_fwd_workspace_size(d, 128) == 2 * 12288 + 786432
+    # 1 x 5 tokens, H=3, Q=64: 3*64*4 = 768 B (already 256-aligned); states 3*16*16*4 = 3072
+    assert ssd.ssd_fwd_workspace_size(_dims(seqlen=5, nheads=3), 64) == 2 * 768 + 3072
+    # alignment padding: H=1, L=1, Q=64 -> 256 B regions
+    assert ssd.ssd_fwd_workspace_size(_dims(seqlen=1, nheads=1, headdim=16, dstate=16), 64) == 2 * 256 + 1024
+
+
+@pytest.mark.parametrize("kw,q", [
+    (dict(headdim=48), 64), (dict(dstate=128, dtype=0), 64), (dict(dstate=16, dtype=1), 64),
+    (dict(dtype=5), 64), ({}, 32), ({}, 512), (dict(nheads=6, ngroups=4), 64), (dict(seqlen=-1), 64),
+    (dict(nheads=0), 64),
+])
+def test_workspace_size_rejects(lib, kw, q):
+    assert ssd.ssd_fwd_workspace_size(_dims(**kw), q) == 0
+
+
+def _fwd_status(lib, dims, chunk=64, ptr=0x100000, **over):
+    p = dict(x=ptr, dt=ptr, dt_bias=ptr, A=ptr, B=ptr, C=ptr, D=None, init=None, y=ptr, fin=None,
+             ws=ptr, ws_bytes=1 << 30)
+    p.update(over)
+    vp = ctypes.c_void_p
+    return lib.ssd_fwd(None if dims is None else ctypes.byref(dims), vp(p["x"]), vp(p["dt"]), vp(p["dt_bias"]),
+                       vp(p["A"]), vp(p["B"]), vp(p["C"]), vp(p["D"]), chunk, vp(p["init"]), vp(p["y"]),
+                       vp(p["fin"]), vp(p["ws"]), p["ws_bytes"], None)
+
+
+def test_fwd_host_validation_returns_before_any_launch(lib):
+    assert _fwd_status(lib, None) == ssd.SSD_ERR_INVALID_ARG
+    assert _fwd_status(lib, _dims(), chunk=100) == ssd.SSD_ERR_UNSUPPORTED
+    assert _fwd_status(lib, _dims(headdim=24)) == ssd.SSD_ERR_UNSUPPORTED
+    assert _fwd_status(lib, _dims(nheads=5, ngroups=2)) == ssd.SSD_ERR_INVALID_ARG
+    assert _fwd_status(lib, _dims(batch=0)) == ssd.SSD_OK               # no-op, nothing touched
+    assert _fwd_status(lib, _dims(), x=None) == ssd.SSD_ERR_INVALID_ARG
+    assert _fwd_status(lib, _dims(), y=None) == ssd.SSD_ERR_INVALID_ARG
+    assert _fwd_status(lib, _dims(), x=0x100004) == ssd.SSD_ERR_INVALID_ARG   # not 16-byte aligned
+    assert _fwd_status(lib, _dims(dtype=1, dstate=32), dt=0x100001) == ssd.SSD_ERR_INVALID_ARG
+    assert _fwd_status(lib, _dims(), ws=None) == ssd.SSD_ERR_WORKSPACE
+    assert _fwd_status(lib, _dims(), ws_bytes=100) == ssd.SSD_ERR_WORKSPACE
+
+
+def test_step_host_validation(lib):
+    vp = ctypes.c_void_p
+    p = vp(0x100000)
+    d = _dims()
+    assert lib.ssd_step(None, p, p, p, p, p, p, p, None, p, None) == ssd.SSD_ERR_INVALID_ARG
+    assert lib.ssd_step(ctypes.byref(_dims(dstate=24)), p, p, p, p, p, p, p, None, p, None) == ssd.SSD_ERR_UNSUPPORTED
+    assert lib.ssd_step(ctypes.byref(d), None, p, p, p, p, p, p, None, p, None) == ssd.SSD_ERR_INVALID_ARG
+    assert lib.ssd_step(ctypes.byref(d), vp(0x100008), p, p, p, p, p, p, None, p, None) == ssd.SSD_ERR_INVALID_ARG
+    assert lib.ssd_step(ctypes.byref(_dims(batch=0)), p, p, p, p, p, p, p, None, p, None) == ssd.SSD_OK
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    """The product path has no fallback: a missing library is an error, not a CPU detour."""
+    monkeypatch.setattr(ssd, "_lib", None)
+    monkeypatch.setattr(ssd, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not found"):
+        ssd.load_library()
+
+
+def test_product_package_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "state_space_sequence_mamba_amd")
+    for f in glob.glob(os.path.join(pkg, "**", "*"), recursive=True):
+        if f.endswith((".py", ".hip", ".h", ".cpp")):
+            text = open(f).read()
+            assert not re.search(r"\boracle\b", text.replace("the oracle", "")) or f.endswith("inputs.py"), f

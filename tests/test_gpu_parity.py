@@ -1,0 +1,300 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Bar: rel_err = max|gpu - oracle| / max|oracle| per output tensor (y, final_state)
+<= 1e-4 for fp32 inputs and <= 2e-2 for bf16 inputs (fp32 accumulation).
+Small shapes are compared element by element in full; the full-size workloads are
+compared on sampled (batch, head) slices that the oracle evaluates on their own.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from helpers import TOL, oracle_slices, oracle_step_slices, rel_err, to64
+from oracle import ssd_recurrence, ssd_step_ref
+from oracle import ssd_stages
+from state_space_sequence_mamba_amd import inputs as I
+from state_space_sequence_mamba_amd import ssd
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _say(msg):
+    print(f"\n[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _fwd_gpu(inp, chunk, initial_state=None):
+    dev = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
+    init = None if initial_state is None else initial_state.to(DEV)
+    y, fin = ssd.ssd_fwd(dev["x"], dev["dt"], dev["dt_bias"], dev["A"], dev["B"], dev["C"], dev.get("D"),
+                         chunk_size=chunk, initial_state=init)
+    torch.cuda.synchronize()
+    return y, fin
+
+
+def _check_full(inp, chunk, tol, initial_state=None):
+    y, fin = _fwd_gpu(inp, chunk, initial_state)
+    yr, fr = ssd_recurrence(to64(inp["x"]), to64(inp["dt"]), to64(inp["dt_bias"]), to64(inp["A"]),
+                            to64(inp["B"]), to64(inp["C"]), None if inp.get("D") is None else to64(inp["D"]),
+                            initial_state=None if initial_state is None else to64(initial_state))
+    ey, ef = rel_err(to64(y), yr), rel_err(to64(fin), fr)
+    assert np.all(np.isfinite(to64(y))) and np.all(np.isfinite(to64(fin)))
+    assert ey <= tol, f"y rel_err {ey:.3e} > {tol}"
+    assert ef <= tol, f"final_state rel_err {ef:.3e} > {tol}"
+    return ey, ef
+
+
+# ------------------------------------------------------------------ the five workloads
+
+def test_workload_fwd_f32_small():
+    w = I.WORKLOAD_LIST[0]
+    _say(w.name)
+    inp = I.make_workload_inputs(w)
+    _check_full(inp, w.chunk, TOL[w.dtype])
+
+
+def test_workload_fwd_f32_b4_l1024():
+    w = I.WORKLOAD_LIST[1]
+    _say(w.name)
+    inp = I.make_workload_inputs(w)
+    _check_full(inp, w.chunk, TOL[w.dtype])
+
+
+@pytest.mark.parametrize("widx", [2, 4])
+def test_workload_fwd_bf16_full_size_sampled(widx):
+    w = I.WORKLOAD_LIST[widx]
+    _say(w.name)
+    inp = I.make_workload_inputs(w)
+    y, fin = _fwd_gpu(inp, w.chunk)
+    yc, fc = to64(y), to64(fin)
+    assert np.all(np.isfinite(yc)) and np.all(np.isfinite(fc))
+    H = w.nheads
+    pairs = [(0, 0), (w.batch - 1, H - 1), (w.batch // 2, H // 2), (0, H // 3), (w.batch - 1, 1)]
+    ref = oracle_slices(inp, pairs)
+    for (b, h), (yr, fr) in ref.items():
+        ey, ef = rel_err(yc[b, :, h], yr), rel_err(fc[b, h], fr)
+        assert ey <= TOL[w.dtype], f"(b={b}, h={h}) y rel_err {ey:.3e}"
+        assert ef <= TOL[w.dtype], f"(b={b}, h={h}) final rel_err {ef:.3e}"
+
+
+def test_workload_step_bf16_1000_steps_sampled():
+    w = I.WORKLOAD_LIST[3]
+    _say(w.name)
+    inp = I.make_step_inputs(w.batch, w.nheads, w.headdim, w.dstate, w.ngroups, w.steps, w.dtype, w.seed,
+                             w.d_init, device=DEV)
+    record = {0, 1, 9, 99, 499, 999}
+    state = inp["state0"].clone()
+    ys = {}
+    for t in range(w.steps):
+        y = ssd.ssd_step(state, inp["x"][t], inp["dt"][t], inp["dt_bias"], inp["A"], inp["B"][t], inp["C"][t],
+                         inp["D"])
+        if t in record:
+            ys[t] = to64(y)
+    torch.cuda.synchronize()
+    stc = to64(state)
+    pairs = [(0, 0), (w.batch - 1, w.nheads - 1), (17, 40), (200, 3)]
+    ref = oracle_step_slices(inp, pairs, w.steps, record)
+    for (b, h), (yr, sr) in ref.items():
+        for t in record:
+            e = rel_err(ys[t][b, h], yr[t])
+            assert e <= TOL[w.dtype], f"(b={b}, h={h}, step {t + 1}) y rel_err {e:.3e}"
+        e = rel_err(stc[b, h], sr)
+        assert e <= TOL[w.dtype], f"(b={b}, h={h}) state rel_err {e:.3e}"
+
+
+# ------------------------------------------------------------------ shape sweep
+
+SWEEP = []
+for dtype, shapes in (("f32", [(16, 16), (32, 32), (64, 64), (16, 64), (64, 16)]),
+                      ("bf16", [(64, 128), (32, 64), (16, 32), (64, 32)])):
+    for i, (P, N) in enumerate(shapes):
+        for L in (1, 7, 63, 64, 65, 200, 513):
+            SWEEP.append((dtype, P, N, L, (64, 128, 256)[(i + L) % 3], (1, 2, 4)[(i + L) % 3]))
+
+
+@pytest.mark.parametrize("dtype,P,N,L,Q,G", SWEEP)
+def test_shape_sweep(dtype, P, N, L, Q, G):
+    _say(f"sweep dtype={dtype} P={P} N={N} L={L} Q={Q} G={G}")
+    H = 4
+    inp = I.make_fwd_inputs(2, L, H, P, N, G, dtype, seed=100 + L + P + N, d_init="normal")
+    _check_full(inp, Q, TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunk_size_invariance(dtype):
+    _say(f"chunk invariance {dtype}")
+    inp = I.make_fwd_inputs(2, 700, 6, 64, 64, 3, dtype, seed=7)
+    outs = []
+    for Q in (64, 128, 256):
+        outs.append(_check_full(inp, Q, TOL[dtype]))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_run_to_run_bitwise_determinism(dtype):
+    _say(f"determinism {dtype}")
+    inp = I.make_fwd_inputs(2, 1000, 8, 64, 64, 2, dtype, seed=8)
+    y1, f1 = _fwd_gpu(inp, 256)
+    y2, f2 = _fwd_gpu(inp, 256)
+    assert torch.equal(y1, y2) and torch.equal(f1, f2)
+
+
+def test_heads_per_block_does_not_change_results():
+    _say("heads per block invariance")
+    inp = I.make_fwd_inputs(1, 512, 12, 64, 64, 1, "f32", seed=9)
+    ref = None
+    try:
+        for hb in (1, 2, 3, 4, 6, 12):
+            ssd.tune_set(0, hb)
+            y, f = _fwd_gpu(inp, 256)
+            if ref is None:
+                ref = (y, f)
+            else:
+                assert torch.equal(y, ref[0]) and torch.equal(f, ref[1])
+    finally:
+        ssd.tune_set(0, 0)
+    _check_full(inp, 256, TOL["f32"])
+
+
+# ------------------------------------------------------------------ state in / out
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_initial_state(dtype):
+    _say(f"initial_state {dtype}")
+    inp = I.make_fwd_inputs(2, 300, 4, 64, 64 if dtype == "f32" else 128, 2, dtype, seed=10)
+    init = torch.randn(2, 4, 64, inp["B"].shape[3], generator=torch.Generator().manual_seed(3))
+    _check_full(inp, 128, TOL[dtype], initial_state=init)
+
+
+def test_split_sequence_resume_and_decode_continuity():
+    """fwd(x[:L1]) -> final_state -> fwd(x[L1:], init) -> final_state -> ssd_step == oracle on all tokens."""
+    _say("resume + decode continuity")
+    L, L1 = 400, 150
+    inp = I.make_fwd_inputs(2, L + 3, 4, 32, 32, 1, "f32", seed=11)
+    dev = {k: v.to(DEV) for k, v in inp.items()}
+    sl = lambda k, a, b: dev[k][:, a:b].contiguous()  # noqa: E731
+    y1, f1 = ssd.ssd_fwd(sl("x", 0, L1), sl("dt", 0, L1), dev["dt_bias"], dev["A"], sl("B", 0, L1),
+                         sl("C", 0, L1), dev["D"], chunk_size=64)
+    y2, f2 = ssd.ssd_fwd(sl("x", L1, L), sl("dt", L1, L), dev["dt_bias"], dev["A"], sl("B", L1, L),
+                         sl("C", L1, L), dev["D"], chunk_size=128, initial_state=f1)
+    state = f2.clone()
+    ys = []
+    for t in range(L, L + 3):
+        ys.append(ssd.ssd_step(state, dev["x"][:, t].contiguous(), dev["dt"][:, t].contiguous(), dev["dt_bias"],
+                               dev["A"], dev["B"][:, t].contiguous(), dev["C"][:, t].contiguous(), dev["D"]))
+    torch.cuda.synchronize()
+    got = np.concatenate([to64(y1), to64(y2), np.stack([to64(v) for v in ys], axis=1)], axis=1)
+    yr, fr = ssd_recurrence(*(to64(inp[k]) for k in ("x", "dt", "dt_bias", "A", "B", "C", "D")))
+    assert rel_err(got, yr) <= TOL["f32"]
+    assert rel_err(to64(state), fr) <= TOL["f32"]
+
+
+def test_seqlen_zero_writes_initial_state():
+    _say("seqlen 0")
+    x = torch.empty(2, 0, 4, 16, device=DEV)
+    dt = torch.empty(2, 0, 4, device=DEV)
+    Bm = torch.empty(2, 0, 1, 16, device=DEV)
+    init = torch.randn(2, 4, 16, 16, device=DEV)
+    y, f = ssd.ssd_fwd(x, dt, torch.zeros(4, device=DEV), -torch.ones(4, device=DEV), Bm, Bm.clone(),
+                       chunk_size=64, initial_state=init)
+    y0, f0 = ssd.ssd_fwd(x, dt, torch.zeros(4, device=DEV), -torch.ones(4, device=DEV), Bm, Bm.clone(),
+                         chunk_size=64)
+    torch.cuda.synchronize()
+    assert y.numel() == 0 and torch.equal(f, init) and torch.count_nonzero(f0) == 0
+
+
+def test_batch_zero_is_noop():
+    _say("batch 0")
+    x = torch.empty(0, 10, 4, 16, device=DEV)
+    y, f = ssd.ssd_fwd(x, torch.empty(0, 10, 4, device=DEV), torch.zeros(4, device=DEV),
+                       -torch.ones(4, device=DEV), torch.empty(0, 10, 1, 16, device=DEV),
+                       torch.empty(0, 10, 1, 16, device=DEV), chunk_size=64)
+    assert y.numel() == 0 and f.numel() == 0
+
+
+def test_special_values_A_zero_and_large_dt():
+    _say("A = 0, large dt")
+    inp = I.make_fwd_inputs(1, 200, 4, 32, 32, 1, "f32", seed=12)
+    inp["A"] = torch.zeros(4)
+    inp["dt"][:, 50:60] = 40.0          # softplus in its linear branch
+    _check_full(inp, 64, TOL["f32"])
+
+
+def test_no_D_term():
+    _say("D = NULL")
+    inp = I.make_fwd_inputs(1, 130, 4, 32, 32, 1, "f32", seed=13)
+    inp["D"] = None
+    _check_full(inp, 64, TOL["f32"])
+
+
+# ------------------------------------------------------------------ stages
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_stage_intermediates_match_staged_oracle(dtype):
+    """Read the workspace after a call: dt', segment cumsum and the states entering each chunk."""
+    _say(f"stages {dtype}")
+    Bt, L, H, P, N, G, Q = 2, 200, 4, 32, 32 if dtype == "f32" else 64, 2, 64
+    inp = I.make_fwd_inputs(Bt, L, H, P, N, G, dtype, seed=14)
+    dev = {k: v.to(DEV) for k, v in inp.items()}
+    dims = ssd.make_dims(Bt, L, H, P, N, G, dev["x"].dtype)
+    ws = torch.zeros(ssd.ssd_fwd_workspace_size(dims, Q), dtype=torch.uint8, device=DEV)
+    ssd.ssd_fwd(dev["x"], dev["dt"], dev["dt_bias"], dev["A"], dev["B"], dev["C"], dev["D"], chunk_size=Q,
+                workspace=ws)
+    torch.cuda.synchronize()
+    nc = (L + Q - 1) // Q
+    cum = Bt * H * nc * Q * 4
+    cum_al = (cum + 255) // 256 * 256
+    f = ws.view(torch.float32) if ws.numel() % 4 == 0 else None
+    dtp = f[: cum // 4].view(Bt, H, nc, Q)
+    dacs = f[cum_al // 4: cum_al // 4 + cum // 4].view(Bt, H, nc, Q)
+    prev = f[2 * cum_al // 4: 2 * cum_al // 4 + Bt * nc * H * P * N].view(Bt, nc, H, P, N)
+    r_dtp, r_dacs = ssd_stages.chunk_cumsum(to64(inp["dt"]), to64(inp["dt_bias"]), to64(inp["A"]), Q)
+    S = ssd_stages.chunk_state(to64(inp["x"]), to64(inp["B"]), r_dtp, r_dacs)
+    r_prev, _ = ssd_stages.state_passing(S, r_dacs)
+    assert rel_err(to64(dtp), r_dtp) <= 1e-6
+    assert rel_err(to64(dacs), r_dacs) <= 1e-5
+    assert rel_err(to64(prev), r_prev) <= TOL[dtype]
+
+
+# ------------------------------------------------------------------ ABI error paths
+
+def test_error_paths_leave_outputs_untouched():
+    _say("error paths")
+    inp = {k: v.to(DEV) for k, v in I.make_fwd_inputs(1, 64, 4, 16, 16, 1, "f32", seed=1).items()}
+    y = torch.full_like(inp["x"], 7.0)
+    f = torch.full((1, 4, 16, 16), 7.0, device=DEV)
+    host_x = inp["x"].cpu()
+    with pytest.raises(ssd.SsdError) as e:
+        ssd.ssd_fwd(host_x, inp["dt"], inp["dt_bias"], inp["A"], inp["B"], inp["C"], inp["D"], chunk_size=64,
+                    y=y, final_state=f)
+    assert e.value.status == ssd.SSD_ERR_DEVICE_PTR
+    with pytest.raises(ssd.SsdError) as e:
+        ssd.ssd_fwd(inp["x"], inp["dt"], inp["dt_bias"], inp["A"], inp["B"], inp["C"], inp["D"], chunk_size=32,
+                    y=y, final_state=f)
+    assert e.value.status == ssd.SSD_ERR_UNSUPPORTED
+    small = torch.empty(16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(ssd.SsdError) as e:
+        ssd.ssd_fwd(inp["x"], inp["dt"], inp["dt_bias"], inp["A"], inp["B"], inp["C"], inp["D"], chunk_size=64,
+                    y=y, final_state=f, workspace=small)
+    assert e.value.status == ssd.SSD_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0) and torch.all(f == 7.0)
+
+
+def test_step_small_shapes_against_oracle():
+    _say("step small shapes")
+    for dtype, P, N, G in (("f32", 16, 16, 1), ("f32", 64, 64, 2), ("bf16", 64, 128, 4), ("bf16", 32, 32, 1)):
+        inp = I.make_step_inputs(3, 4, P, N, G, 5, dtype, seed=P + N, device=DEV)
+        st = inp["state0"].clone()
+        ref_st = to64(inp["state0"])
+        for t in range(5):
+            y = ssd.ssd_step(st, inp["x"][t], inp["dt"][t], inp["dt_bias"], inp["A"], inp["B"][t], inp["C"][t],
+                             inp["D"])
+            yr, ref_st = ssd_step_ref(ref_st, to64(inp["x"][t]), to64(inp["dt"][t]), to64(inp["dt_bias"]),
+                                      to64(inp["A"]), to64(inp["B"][t]), to64(inp["C"][t]), to64(inp["D"]))
+            assert rel_err(to64(y), yr) <= TOL[dtype]
+        torch.cuda.synchronize()
+        assert rel_err(to64(st), ref_st) <= TOL[dtype]
