@@ -1,0 +1,208 @@
+"""Benchmark of the SSD hot path on one MI355X.
+
+One step = one pass of the whole path over one batch: ssd_fwd over the prefill batch
+(chunk_cumsum -> chunk_state -> state_passing -> chunk_scan), writing final_state, then
+one ssd_step decode token per sequence continuing from that state.  Workload: the fp32
+forward of batch 4 x 1024 tokens, 24 heads, headdim 64, dstate 64, 1 group, chunk 256
+(plus its decode token).  Inputs are seeded synthetic tensors resident in HBM before the
+timed region.  Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload NAME]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+from state_space_sequence_mamba_amd import inputs as I  # noqa: E402
+from state_space_sequence_mamba_amd import ssd  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0                         # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}   # dense matrix peaks, TFLOP/s
+DEFAULT_WORKLOAD = "ssd_fwd f32 B4 L1024 H24 P64 N64 G1 Q256"
+KERNELS = ["chunk_cumsum", "chunk_state", "state_passing", "chunk_scan", "ssd_step"]
+
+
+def algorithmic_cost(w):
+    """Bytes each kernel must move (its inputs once, its outputs once) and the flops it must
+    do (causal half of the in-chunk products, C B^T once per group), per launch."""
+    e = 4 if w.dtype == "f32" else 2
+    B, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
+    nc = (L + Q - 1) // Q
+    lens = [min(Q, L - c * Q) for c in range(nc)]
+    cum = 2 * B * H * nc * Q * 4                       # dt' and its cumsum, fp32
+    st = B * nc * H * P * N * 4                        # chunk states, fp32
+    fin = B * H * P * N * 4
+    x = B * L * H * P * e
+    bc = B * L * G * N * e
+    tri = sum(n * (n + 1) // 2 for n in lens)           # causal (i, j) pairs per (b, h) sequence
+    cost = {
+        "chunk_cumsum": dict(bytes=B * L * H * e + cum + 8 * H, flops=0),
+        "chunk_state": dict(bytes=x + bc + cum + st, flops=2 * B * H * L * P * N),
+        "state_passing": dict(bytes=2 * st + fin + B * H * nc * 4, flops=2 * B * nc * H * P * N),
+        "chunk_scan": dict(bytes=2 * x + 2 * bc + cum + st + H * P * 4,
+                           flops=2 * B * H * P * tri + 2 * B * H * L * N * P + 2 * B * G * N * tri),
+        # decode: state read + write, x, y, dt, B, C
+        "ssd_step": dict(bytes=2 * fin + 2 * B * H * P * e + B * H * e + 2 * B * G * N * e,
+                         flops=4 * B * H * P * N),
+    }
+    for k, v in cost.items():
+        peak_f = MFMA_PEAK_TFLOPS[w.dtype] * 1e12
+        t_f = v["flops"] / peak_f if k in ("chunk_state", "chunk_scan") else 0.0
+        t_b = v["bytes"] / (HBM_PEAK_GBS * 1e9)
+        v["bound"] = "mfma" if t_f > t_b else "hbm"
+    return cost
+
+
+def cpu_baseline(w, inp, dec, budget_s):
+    """The float64 oracle (as it stands) on a bounded sample of the same step, single thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import ssd_recurrence
+
+    f64 = lambda t: t.detach().cpu().double().numpy()  # noqa: E731
+    rows = w.batch
+    with threadpool_limits(1):
+        while True:
+            t0 = time.perf_counter()
+            x = np.concatenate([f64(inp["x"][:rows]), f64(dec["x"][0, :rows])[:, None]], axis=1)
+            dt = np.concatenate([f64(inp["dt"][:rows]), f64(dec["dt"][0, :rows])[:, None]], axis=1)
+            Bm = np.concatenate([f64(inp["B"][:rows]), f64(dec["B"][0, :rows])[:, None]], axis=1)
+            Cm = np.concatenate([f64(inp["C"][:rows]), f64(dec["C"][0, :rows])[:, None]], axis=1)
+            ssd_recurrence(x, dt, f64(inp["dt_bias"]), f64(inp["A"]), Bm, Cm, f64(inp["D"]))
+            secs = time.perf_counter() - t0
+            if secs <= budget_s * 1.5 or rows == 1:
+                break
+            rows = max(1, rows // 2)
+    tokens = rows * (w.seqlen + 1)
+    return {"value": tokens / secs, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"float64 sequential recurrence over {rows} of {w.batch} sequences x "
+                      f"{w.seqlen + 1} tokens (prefill + decode token), {secs:.2f} s, numpy, 1 thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--heads-per-block", type=int, default=0, help="chunk_scan launch shape (0 = built-in)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(see the sharding design for more GPUs)", file=sys.stderr)
+        sys.exit(2)
+    w = I.WORKLOADS[args.workload]
+    if w.entry != "fwd":
+        sys.exit("bench.py times forward workloads (prefill + one decode token)")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.heads_per_block:
+        ssd.tune_set(0, args.heads_per_block)
+
+    inp = I.make_workload_inputs(w)
+    dec = I.make_step_inputs(w.batch, w.nheads, w.headdim, w.dstate, w.ngroups, 1, w.dtype,
+                             seed=1000 + w.seed, d_init=w.d_init, device="cpu")
+    d = {k: v.to(dev) for k, v in inp.items()}
+    dd = {k: v[0].contiguous().to(dev) for k, v in dec.items() if k in ("x", "dt", "B", "C")}
+    y = torch.empty_like(d["x"])
+    state = torch.empty(w.batch, w.nheads, w.headdim, w.dstate, dtype=torch.float32, device=dev)
+    y_dec = torch.empty_like(dd["x"])
+    dims = ssd.make_dims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, d["x"].dtype)
+    ws = torch.empty(ssd.ssd_fwd_workspace_size(dims, w.chunk), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    K, W = args.steps, args.warmup
+    nev = 7   # 5 around the forward's kernels, 2 around ssd_step
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(max(K, 1))]
+    for evs in events:          # create the underlying HIP events
+        for e in evs:
+            e.record(stream)
+    torch.cuda.synchronize()
+
+    def step(evs=None):
+        handles = None if evs is None else [e.cuda_event for e in evs[:5]]
+        ssd.ssd_fwd(d["x"], d["dt"], d["dt_bias"], d["A"], d["B"], d["C"], d["D"], chunk_size=w.chunk,
+                    y=y, final_state=state, workspace=ws, stream=stream, stage_events=handles)
+        if evs is not None:
+            evs[5].record(stream)
+        ssd.ssd_step(state, dd["x"], dd["dt"], d["dt_bias"], d["A"], dd["B"], dd["C"], d["D"], y=y_dec,
+                     stream=stream)
+        if evs is not None:
+            evs[6].record(stream)
+
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(K):
+        step(events[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / K
+
+    per_kernel_ms = {k: 0.0 for k in KERNELS}
+    pairs = [(0, 1), (1, 2), (2, 3), (3, 4), (5, 6)]
+    for evs in events[:K]:
+        for k, (a, b) in zip(KERNELS, pairs):
+            per_kernel_ms[k] += evs[a].elapsed_time(evs[b]) / K
+
+    cost = algorithmic_cost(w)
+    kernels = {}
+    for k in KERNELS:
+        t = per_kernel_ms[k] * 1e-3
+        c = cost[k]
+        if c["bound"] == "mfma":
+            ach, peak, unit = c["flops"] / t / 1e12, MFMA_PEAK_TFLOPS[w.dtype], "TFLOP/s"
+        else:
+            ach, peak, unit = c["bytes"] / t / 1e9, HBM_PEAK_GBS, "GB/s"
+        kernels[k] = {"us": round(per_kernel_ms[k] * 1e3, 3), "bound": c["bound"], "achieved": round(ach, 2),
+                      "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
+                      "alg_bytes": c["bytes"], "alg_flops": c["flops"]}
+    dom = max(KERNELS, key=lambda k: per_kernel_ms[k])
+    kd = kernels[dom]
+    roofline = {"kernel": dom, "bound": kd["bound"], "achieved": kd["achieved"], "peak": kd["peak"],
+                "unit": kd["unit"], "frac": kd["frac"], "traffic": None}
+
+    tokens = w.batch * (w.seqlen + 1)
+    out = {
+        "metric": "SSD scan tokens/sec at 1 MI355X + % of MFMA/HBM roofline",
+        "value": round(tokens / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) x/B/C/dt, log-uniform dt bias, A=-U[1,16])",
+        "config": {"workload": w.name + " + 1 decode token", "batch": w.batch, "seqlen": w.seqlen,
+                   "nheads": w.nheads, "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
+                   "chunk_size": w.chunk, "tokens_per_step": tokens},
+        "roofline": roofline,
+        "kernels": kernels,
+        "wall_s_timed_region": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp, dec, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
