@@ -97,6 +97,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--heads-per-block", type=int, default=0, help="chunk_scan launch shape (0 = built-in)")
+    ap.add_argument("--scan-variant", type=int, default=0,
+                    help="chunk_scan decomposition: 1 = 64-row blocks, 2 = whole chunks, 0 = built-in")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -109,6 +111,8 @@ def main():
     torch.cuda.set_device(dev)
     if args.heads_per_block:
         ssd.tune_set(0, args.heads_per_block)
+    if args.scan_variant:
+        ssd.tune_set(2, args.scan_variant)
 
     inp = I.make_workload_inputs(w)
     dec = I.make_step_inputs(w.batch, w.nheads, w.headdim, w.dstate, w.ngroups, 1, w.dtype,

@@ -7,10 +7,13 @@
 // product of the per-step decays exp(dt' A), i.e. exp of the cumsum difference).
 //
 // One workgroup (4 wavefronts) per (b, c, h).  A (P x Q) . (Q x N) product on MFMA with
-// fp32 accumulation: the contraction runs over tokens, which are the slow axis of x and B
-// in HBM, so 64-token tiles are staged transposed in LDS (token-contiguous rows) where both
-// operands can be read with one LDS load per fragment.  The per-token weight w_i is folded
-// into x while staging.  Tokens past the end of the sequence are zero-filled.
+// fp32 accumulation.  The contraction runs over tokens, the slow axis of x and B in HBM, so
+// 64-token tiles are staged transposed in LDS (token-contiguous rows): each thread loads
+// the same 16-byte column slice of two consecutive tokens and writes them as one packed
+// pair, which keeps the transposed LDS writes free of bank conflicts.  The next tile's
+// global loads are issued into registers before the current tile's MFMAs.  The per-token
+// weight w_i is folded into x while staging.  Tokens past the end of the sequence are zero.
+// fp32 fragments use the token permutation k = 16*qd + kk so that each lane reads 128 bits.
 #include "ssd_common.h"
 #include "ssd_launch.h"
 
@@ -24,10 +27,13 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const T* __restrict__ 
                                                           float* __restrict__ states,
                                                           int L, int H, int G, int nc, int Q,
                                                           uint32_t nblocks) {
-  typedef KMma<T> M;
-  constexpr int KT = 64;                           // tokens per LDS tile
-  constexpr int PITCH = KT + (sizeof(T) == 4 ? 2 : 8);
+  constexpr bool F32 = sizeof(T) == 4;
+  constexpr int KT = 64;                                 // tokens per LDS tile
+  constexpr int PITCH = KT + (F32 ? 4 : 8);              // 16-byte aligned rows
   constexpr int VEC = Vec16<T>::n;
+  constexpr int PV = P / VEC, NV = N / VEC;
+  constexpr int XU = (KT / 2) * PV, BU = (KT / 2) * NV;  // token-pair units per tile
+  constexpr int XPT = (XU + 255) / 256, BPT = (BU + 255) / 256;
   constexpr int TP = P / 16, TN = N / 16;
   // wavefront layout over the (TP x TN) grid of 16x16 output tiles
   constexpr int WAVES_N = TN < 4 ? TN : 4;
@@ -35,8 +41,8 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const T* __restrict__ 
   constexpr int WN = TN / WAVES_N;
   constexpr int WP = (TP + WAVES_P - 1) / WAVES_P;
 
-  __shared__ __attribute__((aligned(16))) T s_x[P][PITCH];   // (x * w)^T
-  __shared__ __attribute__((aligned(16))) T s_b[N][PITCH];   // B^T
+  __shared__ __attribute__((aligned(16))) T s_x[P * PITCH];   // (x * w)^T
+  __shared__ __attribute__((aligned(16))) T s_b[N * PITCH];   // B^T
   __shared__ float s_w[256];
 
   uint32_t id = xcd_swizzle(blockIdx.x, nblocks);
@@ -55,6 +61,61 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const T* __restrict__ 
   const float last = dA_c[Q - 1];
   for (int i = tid; i < Q; i += 256) s_w[i] = expf(last - dA_c[i]) * dtp_c[i];
 
+  const size_t xs = (size_t)H * P, bs = (size_t)G * N;    // token strides
+  const T* xb = x + ((size_t)b * L + t0) * xs + (size_t)h * P;
+  const T* bb = Bm + ((size_t)b * L + t0) * bs + (size_t)g * N;
+
+  Vec16<T> xr[XPT][2], br[BPT][2];
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < XPT; ++u) {
+      const int v = tid + 256 * u;
+      if (v < XU) {
+        const int m = v % (KT / 2), pv = (v / (KT / 2)) * VEC;
+        const int tok = k0 + 2 * m;
+        xr[u][0] = (tok < len) ? load16(xb + (size_t)tok * xs + pv) : zero16<T>();
+        xr[u][1] = (tok + 1 < len) ? load16(xb + (size_t)(tok + 1) * xs + pv) : zero16<T>();
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+      const int v = tid + 256 * u;
+      if (v < BU) {
+        const int m = v % (KT / 2), nv = (v / (KT / 2)) * VEC;
+        const int tok = k0 + 2 * m;
+        br[u][0] = (tok < len) ? load16(bb + (size_t)tok * bs + nv) : zero16<T>();
+        br[u][1] = (tok + 1 < len) ? load16(bb + (size_t)(tok + 1) * bs + nv) : zero16<T>();
+      }
+    }
+  };
+  auto store_tile = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < XPT; ++u) {
+      const int v = tid + 256 * u;
+      if (v < XU) {
+        const int m = v % (KT / 2), pv = (v / (KT / 2)) * VEC;
+        const float w0 = s_w[k0 + 2 * m], w1 = s_w[k0 + 2 * m + 1];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          T pair[2] = {from_f32<T>(to_f32(xr[u][0].v[e]) * w0), from_f32<T>(to_f32(xr[u][1].v[e]) * w1)};
+          __builtin_memcpy(&s_x[(pv + e) * PITCH + 2 * m], pair, sizeof(pair));
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+      const int v = tid + 256 * u;
+      if (v < BU) {
+        const int m = v % (KT / 2), nv = (v / (KT / 2)) * VEC;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          T pair[2] = {br[u][0].v[e], br[u][1].v[e]};
+          __builtin_memcpy(&s_b[(nv + e) * PITCH + 2 * m], pair, sizeof(pair));
+        }
+      }
+    }
+  };
+
   const int wn = wave % WAVES_N, wp = wave / WAVES_N;
   f32x4 acc[WP][WN];
 #pragma unroll
@@ -62,43 +123,57 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const T* __restrict__ 
 #pragma unroll
     for (int j = 0; j < WN; ++j) acc[i][j] = zero4();
 
-  const size_t x_tok_stride = (size_t)H * P;
-  const size_t b_tok_stride = (size_t)G * N;
-  const T* xb = x + ((size_t)b * L + t0) * x_tok_stride + (size_t)h * P;
-  const T* bb = Bm + ((size_t)b * L + t0) * b_tok_stride + (size_t)g * N;
-
+  load_tile(0);
   for (int k0 = 0; k0 < len; k0 += KT) {
-    __syncthreads();  // previous tile consumed (and s_w written, first time)
-    for (int v = tid; v < KT * (P / VEC); v += 256) {
-      const int i = v / (P / VEC), pv = (v % (P / VEC)) * VEC;
-      const int tok = k0 + i;
-      Vec16<T> d = (tok < len) ? load16(xb + (size_t)tok * x_tok_stride + pv) : zero16<T>();
-      const float w = s_w[tok];
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) s_x[pv + e][i] = from_f32<T>(to_f32(d.v[e]) * w);
-    }
-    for (int v = tid; v < KT * (N / VEC); v += 256) {
-      const int i = v / (N / VEC), nv = (v % (N / VEC)) * VEC;
-      const int tok = k0 + i;
-      Vec16<T> d = (tok < len) ? load16(bb + (size_t)tok * b_tok_stride + nv) : zero16<T>();
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) s_b[nv + e][i] = d.v[e];
-    }
+    __syncthreads();                       // previous tile consumed; s_w written
+    store_tile(k0);
+    if (k0 + KT < len) load_tile(k0 + KT);  // next tile's loads overlap this tile's MFMAs
     __syncthreads();
+    if (F32) {
 #pragma unroll
-    for (int ks = 0; ks < KT; ks += M::K) {
-      typename M::frag af[WP], bf[WN];
+      for (int m = 0; m < 4; ++m) {
+        float4 af[WP], bf[WN];
 #pragma unroll
-      for (int i = 0; i < WP; ++i) {
-        const int tp = wp * WP + i;
-        af[i] = (tp < TP) ? M::load(&s_x[tp * 16 + r][ks + qd * M::KPL]) : M::zero();
+        for (int i = 0; i < WP; ++i) {
+          const int tp = wp * WP + i;
+          af[i] = (tp < TP) ? *reinterpret_cast<const float4*>(
+                                  reinterpret_cast<const float*>(s_x) + (tp * 16 + r) * PITCH + 16 * qd + 4 * m)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int j = 0; j < WN; ++j)
+          bf[j] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(s_b) +
+                                                   ((wn * WN + j) * 16 + r) * PITCH + 16 * qd + 4 * m);
+#pragma unroll
+        for (int i = 0; i < WP; ++i)
+#pragma unroll
+          for (int j = 0; j < WN; ++j) {
+            acc[i][j] = mfma_16x16x4_f32(af[i].x, bf[j].x, acc[i][j]);
+            acc[i][j] = mfma_16x16x4_f32(af[i].y, bf[j].y, acc[i][j]);
+            acc[i][j] = mfma_16x16x4_f32(af[i].z, bf[j].z, acc[i][j]);
+            acc[i][j] = mfma_16x16x4_f32(af[i].w, bf[j].w, acc[i][j]);
+          }
       }
+    } else {
 #pragma unroll
-      for (int j = 0; j < WN; ++j) bf[j] = M::load(&s_b[(wn * WN + j) * 16 + r][ks + qd * M::KPL]);
+      for (int kk = 0; kk < KT / 32; ++kk) {
+        bf16x8 af[WP], bf[WN];
 #pragma unroll
-      for (int i = 0; i < WP; ++i)
+        for (int i = 0; i < WP; ++i) {
+          const int tp = wp * WP + i;
+          af[i] = (tp < TP) ? *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(s_x) +
+                                                               (tp * 16 + r) * PITCH + 32 * kk + 8 * qd)
+                            : KMma<__bf16>::zero();
+        }
 #pragma unroll
-        for (int j = 0; j < WN; ++j) acc[i][j] = M::mma(af[i], bf[j], acc[i][j]);
+        for (int j = 0; j < WN; ++j)
+          bf[j] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(s_b) +
+                                                   ((wn * WN + j) * 16 + r) * PITCH + 32 * kk + 8 * qd);
+#pragma unroll
+        for (int i = 0; i < WP; ++i)
+#pragma unroll
+          for (int j = 0; j < WN; ++j) acc[i][j] = mfma_16x16x32_bf16(af[i], bf[j], acc[i][j]);
+      }
     }
   }
 

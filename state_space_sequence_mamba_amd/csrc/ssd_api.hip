@@ -63,24 +63,31 @@ bool device_ptr_ok(const void* p) {
   return attr.type == hipMemoryTypeManaged;
 }
 
-// chunk_scan heads per workgroup: heads of one group share a C B^T evaluation; more heads
-// per workgroup amortise it further but leave fewer workgroups to fill 256 CUs.  Choose the
-// largest divisor of H/G that still leaves at least `target` workgroups.
+// chunk_scan launch shape.  Two decompositions: 64-row blocks (many small workgroups: x
+// tiles and the carried state are re-read per row block, which suits compute-bound fp32)
+// and whole chunks (every input and output moves once: memory-bound bf16).  Heads of one
+// group share each C B^T evaluation inside a workgroup; more heads per workgroup amortise it
+// further but leave fewer workgroups to fill 256 CUs.
 int g_tune_heads_per_block = 0;  // 0 = heuristic
 int g_tune_min_blocks = 512;
+int g_tune_scan_variant = 0;     // 0 = by dtype
 
-int pick_heads_per_block(int B, int nc, int H, int G, int Q) {
+int pick_scan_variant(int dtype) {
+  if (g_tune_scan_variant == 1 || g_tune_scan_variant == 2) return g_tune_scan_variant;
+  return dtype == SSD_F32 ? 1 : 2;
+}
+
+int pick_heads_per_block(int B, int nc, int H, int G, int Q, int variant) {
+  static const int kChoices[] = {4, 3, 2, 1};  // instantiated head-block sizes
   const int hpg = H / G;
-  const int pairs = Q / 32;
-  const int npg = pairs / (pairs < 4 ? pairs : 4);
-  if (g_tune_heads_per_block > 0 && hpg % g_tune_heads_per_block == 0) return g_tune_heads_per_block;
-  const long base = (long)B * nc * npg * G;  // workgroups per head of a group
-  int best = 1;
-  for (int hb = 1; hb <= hpg; ++hb) {
-    if (hpg % hb) continue;
-    if (base * (hpg / hb) >= g_tune_min_blocks) best = hb;
+  if (g_tune_heads_per_block > 0) {
+    for (int hb : kChoices)
+      if (hb == g_tune_heads_per_block && hpg % hb == 0) return hb;
   }
-  return best;
+  const long per_head = (long)B * nc * G * (variant == 1 ? Q / 64 : 1);  // workgroups per head of a group
+  for (int hb : kChoices)
+    if (hpg % hb == 0 && per_head * (hpg / hb) >= g_tune_min_blocks) return hb;
+  return 1;
 }
 
 ssd_status_t fwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, const float* dt_bias,
@@ -137,7 +144,8 @@ ssd_status_t fwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   a.dtp = has_seq ? reinterpret_cast<float*>(ws + wl.dtp_off) : nullptr;
   a.dAcs = has_seq ? reinterpret_cast<float*>(ws + wl.dacs_off) : nullptr;
   a.states = has_seq ? reinterpret_cast<float*>(ws + wl.states_off) : nullptr;
-  a.heads_per_block = pick_heads_per_block(a.B, a.nc, a.H, a.G, a.Q);
+  a.scan_variant = pick_scan_variant(a.dtype);
+  a.heads_per_block = pick_heads_per_block(a.B, a.nc, a.H, a.G, a.Q, a.scan_variant);
 
   if (!has_seq) {
     // no tokens: final_state = initial_state (or zeros); state_passing with zero chunks
@@ -243,6 +251,7 @@ const char* ssd_status_string(ssd_status_t s) {
 void ssd_tune_set(int key, int value) {
   if (key == 0) g_tune_heads_per_block = value;
   if (key == 1) g_tune_min_blocks = value > 0 ? value : 512;
+  if (key == 2) g_tune_scan_variant = value;
 }
 
 }  // extern "C"

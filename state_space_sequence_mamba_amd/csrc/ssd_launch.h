@@ -27,6 +27,7 @@ struct FwdArgs {
   float* dAcs;             // workspace (B, H, nc, Q)
   float* states;           // workspace (B, nc, H, P, N)
   int heads_per_block;     // chunk_scan: heads sharing one C B^T evaluation (divides H / G)
+  int scan_variant;        // chunk_scan decomposition: 1 = 64-row blocks, 2 = whole chunks
 };
 
 struct StepArgs {

@@ -142,21 +142,26 @@ def test_run_to_run_bitwise_determinism(dtype):
     assert torch.equal(y1, y2) and torch.equal(f1, f2)
 
 
-def test_heads_per_block_does_not_change_results():
-    _say("heads per block invariance")
-    inp = I.make_fwd_inputs(1, 512, 12, 64, 64, 1, "f32", seed=9)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_launch_shapes_do_not_change_results(dtype):
+    """Both chunk_scan decompositions and every head-block size give bit-identical results."""
+    _say(f"launch shape invariance {dtype}")
+    inp = I.make_fwd_inputs(2, 700, 12, 64, 64, 1, dtype, seed=9)
     ref = None
     try:
-        for hb in (1, 2, 3, 4, 6, 12):
-            ssd.tune_set(0, hb)
-            y, f = _fwd_gpu(inp, 256)
-            if ref is None:
-                ref = (y, f)
-            else:
-                assert torch.equal(y, ref[0]) and torch.equal(f, ref[1])
+        for variant in (1, 2):
+            for hb in (1, 2, 3, 4):
+                ssd.tune_set(2, variant)
+                ssd.tune_set(0, hb)
+                y, f = _fwd_gpu(inp, 256)
+                if ref is None:
+                    ref = (y, f)
+                else:
+                    assert torch.equal(y, ref[0]) and torch.equal(f, ref[1]), (variant, hb)
     finally:
         ssd.tune_set(0, 0)
-    _check_full(inp, 256, TOL["f32"])
+        ssd.tune_set(2, 0)
+    _check_full(inp, 256, TOL[dtype])
 
 
 # ------------------------------------------------------------------ state in / out
