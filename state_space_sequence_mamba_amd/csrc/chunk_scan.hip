@@ -9,63 +9,69 @@
 // MAMBA-2 Implementation Gaps", Gap 1 (off-diagonal block from the previous state) and
 // Gap 4 (D skip).
 //
-// Work decomposition.  A workgroup owns one 64-row block of a chunk (4 wavefronts, one
-// 16-row strip each) for HB heads of one group.  Row blocks lower in the chunk have more
-// causal column tiles; they are dispatched first (longest work first) and every XCD gets an
-// equal share of each row-block class, with consecutive (batch, chunk) pairs on one XCD so
-// that they share its L2 for B and C.
+// Per 16-row strip and 16-column causal sub-tile, CB^T (16x16) is contracted on MFMA and
+// consumed at once by every head of the workgroup's head block: each head applies its decay
+// exp(dAcs_i - dAcs_j) dt'_j and the causal mask in registers (CB^T, not CB, so that the MFMA
+// result layout -- four consecutive columns of one row per lane -- is directly the A operand
+// of the (L o CB) X product), then accumulates into its own (16 x P) tile.  On the diagonal
+// sub-tile the x values a lane loads for that product are exactly its own output rows, so
+// the D x skip term is added there without another read.  Contractions over dstate use the
+// k permutation n = (N/4) qd + kk (fp32) so every lane reads 128 bits of LDS at a time; only
+// consistency between the A and B operands matters for a sum over k.
 //
-// Per strip, per 16-column causal sub-tile: CB^T (16x16) is contracted on MFMA once and
-// consumed at once by all HB heads: each head applies its decay exp(dAcs_i - dAcs_j) dt'_j
-// and the causal mask in registers (CB^T, not CB, so that the MFMA result layout -- four
-// consecutive columns of one row per lane -- is directly the A operand of the (L o CB) X
-// product), then accumulates into its own (16 x P) output tile.
-// Contractions over dstate use the k-permutation n = 16*qd + kk (fp32) so that every lane
-// reads its operand with 128-bit LDS loads; only consistency between the A and B operands
-// matters for a sum over k.
+// Two decompositions share these pieces:
+//  * rows : one workgroup (4 wavefronts, one strip each) per 64-row block of a chunk and
+//           head block; row blocks with more causal tiles are dispatched first.  Many small
+//           workgroups: suits compute-bound (fp32) problems.
+//  * chunk: one workgroup (8 wavefronts) per whole chunk and head block; wavefront w owns
+//           the strip pair (w, S-1-w), S+1 sub-tiles each.  x, the carried state and y move
+//           exactly once: suits memory-bound (bf16) problems.
+// Token tiles (64 tokens of B and of x for every head) are loaded into registers one tile
+// ahead of the MFMA work, then written to LDS.  y leaves through LDS as 16-byte row stores.
 //
-// MFMA use: fp32 inputs -> v_mfma_f32_16x16x4_f32 for all three products;
-// bf16 inputs -> 16x16x32 bf16 for C B^T and C Hprev^T, 16x16x16 bf16 for (L o CB) X.
-// Decay factors use the hardware base-2 exponential on log2(e)-scaled cumsums; factors
-// below 2^-126 become 0.
+// MFMA: fp32 inputs -> v_mfma_f32_16x16x4_f32 for all three products; bf16 inputs ->
+// 16x16x32 bf16 for C B^T and C Hprev^T, 16x16x16 bf16 for (L o CB) X.  Decay factors use
+// the hardware base-2 exponential on log2(e)-scaled cumsums; factors below 2^-126 become 0.
 #include "ssd_common.h"
 #include "ssd_launch.h"
 
 namespace ssd {
 
-constexpr int kKT = 64;                       // tokens per staged tile == rows per workgroup
+constexpr int kKT = 64;                       // tokens per staged tile == rows per row block
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int P> struct TPof { static constexpr int v = P / 16; };
 
-template <typename T, int P, int N, int HB>
+template <typename T, int P, int N, int HB, int ROWS>
 struct ScanLds {
   static constexpr bool F32 = sizeof(T) == 4;
   static constexpr int BP = N + (F32 ? 4 : 8);   // B tile / Hprev rows (n-contiguous), 16-byte rows
   static constexpr int XP = kKT + 4;              // x^T rows (token-contiguous)
+  static constexpr int YP = P + (F32 ? 4 : 8);   // y staging rows
   static constexpr int B_ELEMS = kKT * BP;
   static constexpr int X_ELEMS = HB * P * XP;
   static constexpr int PREV_ELEMS = P * BP;
   static constexpr int XU_ELEMS = X_ELEMS > PREV_ELEMS ? X_ELEMS : PREV_ELEMS;  // x tiles alias Hprev
+  static constexpr int MAIN = B_ELEMS + XU_ELEMS;
+  static constexpr int Y_ELEMS = ROWS * YP;                                      // y staging aliases both
+  static constexpr int TOTAL = MAIN > Y_ELEMS ? MAIN : Y_ELEMS;
 };
 
-// Contraction over dstate of two n-contiguous rows: fp32 takes 16 k values per lane in 4 float4
-// loads (n = 16*qd + kk), bf16 takes 8 per 16x16x32 instruction (n = 32*kk + 8*qd + e).
+// Contraction over dstate of two n-contiguous rows.
 template <typename T, int N> struct NDot;
 template <int N> struct NDot<float, N> {
-  static constexpr int NF = N / 4;                // k values per lane
+  static constexpr int NF = N / 4;                // k values per lane: n = (N/4) qd + kk
   typedef float frag[NF];
-  __device__ static __forceinline__ void load(frag f, const float* row, int qd) {
+  __device__ static __forceinline__ void load(frag f, const float* row, int qd, bool ok = true) {
     const float* p = row + (N / 4) * qd;
 #pragma unroll
     for (int m = 0; m < NF / 4; ++m) {
       const float4 v = *reinterpret_cast<const float4*>(p + 4 * m);
-      f[4 * m + 0] = v.x; f[4 * m + 1] = v.y; f[4 * m + 2] = v.z; f[4 * m + 3] = v.w;
+      f[4 * m + 0] = ok ? v.x : 0.f;
+      f[4 * m + 1] = ok ? v.y : 0.f;
+      f[4 * m + 2] = ok ? v.z : 0.f;
+      f[4 * m + 3] = ok ? v.w : 0.f;
     }
-  }
-  __device__ static __forceinline__ void zero(frag f) {
-#pragma unroll
-    for (int k = 0; k < NF; ++k) f[k] = 0.f;
   }
   __device__ static __forceinline__ f32x4 dot(const frag a, const frag b, f32x4 c) {
 #pragma unroll
@@ -74,17 +80,18 @@ template <int N> struct NDot<float, N> {
   }
 };
 template <int N> struct NDot<__bf16, N> {
-  static constexpr int NF = N / 32;               // 16x16x32 instructions
+  static constexpr int NF = N / 32;               // 16x16x32 instructions: n = 32 k + 8 qd + e
   typedef bf16x8 frag[NF];
-  __device__ static __forceinline__ void load(frag f, const __bf16* row, int qd) {
+  __device__ static __forceinline__ void load(frag f, const __bf16* row, int qd, bool ok = true) {
 #pragma unroll
-    for (int k = 0; k < NF; ++k) f[k] = *reinterpret_cast<const bf16x8*>(row + 32 * k + 8 * qd);
-  }
-  __device__ static __forceinline__ void zero(frag f) {
-#pragma unroll
-    for (int k = 0; k < NF; ++k)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) f[k][e] = static_cast<__bf16>(0.f);
+    for (int k = 0; k < NF; ++k) {
+      uint4 v = *reinterpret_cast<const uint4*>(row + 32 * k + 8 * qd);
+      v.x = ok ? v.x : 0u;
+      v.y = ok ? v.y : 0u;
+      v.z = ok ? v.z : 0u;
+      v.w = ok ? v.w : 0u;
+      f[k] = __builtin_bit_cast(bf16x8, v);
+    }
   }
   __device__ static __forceinline__ f32x4 dot(const frag a, const frag b, f32x4 c) {
 #pragma unroll
@@ -93,69 +100,104 @@ template <int N> struct NDot<__bf16, N> {
   }
 };
 
-// ---------------------------------------------------------------- shared pieces
+// One 64-token tile of B rows and of x for every head of the block, held in registers
+// between its global loads and its LDS stores.  Loads read clamped in-bounds addresses and
+// only record which tokens are real; the zeroing selects happen at store time, so nothing
+// waits for the loads until the tile is written to LDS (after the current tile's MFMAs).
+template <typename T, int P, int N, int HB, int NTHR>
+struct TileRegs {
+  static constexpr int VEC = Vec16<T>::n;
+  static constexpr int NVR = N / VEC, PV = P / VEC;
+  static constexpr int BU = kKT * NVR;                 // 16-byte vectors of B
+  static constexpr int XU = HB * (kKT / 2) * PV;       // token-pair units of x
+  static constexpr int BPT = (BU + NTHR - 1) / NTHR, XPT = (XU + NTHR - 1) / NTHR;
+  static_assert(BPT + 2 * XPT <= 32, "validity mask");
+  Vec16<T> b[BPT];
+  Vec16<T> x[XPT][2];
+  uint32_t okm;
+
+  __device__ __forceinline__ void load(const T* Bb, const T* xb, uint32_t bc_tok, uint32_t x_tok, int J, int len,
+                                       int tid) {
+    okm = 0;
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+      const int v = min(tid + NTHR * u, BU - 1);
+      const int i = v / NVR, nv = (v % NVR) * VEC;
+      const int tok = J * kKT + i;
+      const bool ok = tok < len;
+      b[u] = load16(Bb + (uint32_t)(ok ? tok : 0) * bc_tok + nv);
+      okm |= (uint32_t)ok << u;
+    }
+#pragma unroll
+    for (int u = 0; u < XPT; ++u) {
+      const int v = min(tid + NTHR * u, XU - 1);
+      const int m = v % (kKT / 2), rest = v / (kKT / 2);
+      const int pv = (rest % PV) * VEC, hh = rest / PV;
+      const int tok = J * kKT + 2 * m;
+      const bool ok0 = tok < len, ok1 = tok + 1 < len;
+      const T* src = xb + hh * P + pv;
+      x[u][0] = load16(src + (uint32_t)(ok0 ? tok : 0) * x_tok);
+      x[u][1] = load16(src + (uint32_t)(ok1 ? tok + 1 : 0) * x_tok);
+      okm |= ((uint32_t)ok0 << (BPT + 2 * u)) | ((uint32_t)ok1 << (BPT + 2 * u + 1));
+    }
+  }
+  // B rows n-contiguous; x^T token-contiguous, one packed pair of consecutive tokens per store
+  template <int BP, int XP>
+  __device__ __forceinline__ void store(T* s_b, T* s_x, int tid) const {
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+      const int v = tid + NTHR * u;
+      if (v < BU) {
+        const int i = v / NVR, nv = (v % NVR) * VEC;
+        *reinterpret_cast<Vec16<T>*>(&s_b[i * BP + nv]) = keep_if(b[u], (okm >> u) & 1u);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < XPT; ++u) {
+      const int v = tid + NTHR * u;
+      if (v < XU) {
+        const int m = v % (kKT / 2), rest = v / (kKT / 2);
+        const int pv = (rest % PV) * VEC, hh = rest / PV;
+        const Vec16<T> x0 = keep_if(x[u][0], (okm >> (BPT + 2 * u)) & 1u);
+        const Vec16<T> x1 = keep_if(x[u][1], (okm >> (BPT + 2 * u + 1)) & 1u);
+        T* dst = &s_x[(hh * P + pv) * XP + 2 * m];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          T pair[2] = {x0.v[e], x1.v[e]};
+          __builtin_memcpy(dst + e * XP, pair, sizeof(pair));
+        }
+      }
+    }
+  }
+};
+
 // Stage the (P x N) fp32 state entering the chunk into LDS as T, n-contiguous rows.
-template <typename T, int P, int N, int HB>
+template <typename T, int P, int N, int BP>
 __device__ __forceinline__ void stage_prev(T* s_prev, const float* hp, int tid, int nthr) {
-  typedef ScanLds<T, P, N, HB> SL;
   for (int v = tid; v < P * N / 4; v += nthr) {
     const int p = (v * 4) / N, n = (v * 4) % N;
     const float4 f = *reinterpret_cast<const float4*>(hp + (size_t)p * N + n);
-    T* dst = &s_prev[p * SL::BP + n];
-    if (SL::F32) {
-      *reinterpret_cast<float4*>(dst) = f;
+    T* dst = &s_prev[p * BP + n];
+    if (sizeof(T) == 4) {
+      __builtin_memcpy(dst, &f, sizeof(f));
     } else {
-      dst[0] = from_f32<T>(f.x);
-      dst[1] = from_f32<T>(f.y);
-      dst[2] = from_f32<T>(f.z);
-      dst[3] = from_f32<T>(f.w);
+      T q[4] = {from_f32<T>(f.x), from_f32<T>(f.y), from_f32<T>(f.z), from_f32<T>(f.w)};
+      __builtin_memcpy(dst, q, sizeof(q));
     }
   }
 }
 
-// Stage token tile J: B rows (n-contiguous) and x^T for every head of the block
-// (token-contiguous; each thread writes one packed pair of consecutive tokens).
-template <typename T, int P, int N, int HB>
-__device__ __forceinline__ void stage_tile(T* s_b, T* s_x, const T* Bb, const T* xb, size_t bc_tok, size_t x_tok,
-                                           int J, int len, int tid, int nthr) {
-  typedef ScanLds<T, P, N, HB> SL;
-  constexpr int VEC = Vec16<T>::n;
-  for (int v = tid; v < kKT * (N / VEC); v += nthr) {
-    const int i = v / (N / VEC), nv = (v % (N / VEC)) * VEC;
-    const int tok = J * kKT + i;
-    const Vec16<T> d = (tok < len) ? load16(Bb + (size_t)tok * bc_tok + nv) : zero16<T>();
-    *reinterpret_cast<Vec16<T>*>(&s_b[i * SL::BP + nv]) = d;
-  }
-  constexpr int PV = P / VEC;
-  for (int v = tid; v < HB * (kKT / 2) * PV; v += nthr) {
-    const int m = v % (kKT / 2);
-    const int rest = v / (kKT / 2);
-    const int pv = (rest % PV) * VEC, hh = rest / PV;
-    const int tok = J * kKT + 2 * m;
-    const T* src = xb + (size_t)tok * x_tok + (size_t)hh * P + pv;
-    const Vec16<T> d0 = (tok < len) ? load16(src) : zero16<T>();
-    const Vec16<T> d1 = (tok + 1 < len) ? load16(src + x_tok) : zero16<T>();
-    T* dst = &s_x[(hh * P + pv) * SL::XP + 2 * m];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      T pair[2] = {d0.v[e], d1.v[e]};
-      __builtin_memcpy(dst + e * SL::XP, pair, sizeof(pair));
-    }
-  }
-}
-
-// acc_h += exp(dAcs_i) * C_strip . Hprev^T  (Hprev of head hh staged in s_prev)
-template <typename T, int P, int N, int HB>
+// acc += exp(dAcs_i) * C_strip . Hprev^T   (Hprev staged in s_prev)
+template <typename T, int P, int N, int BP>
 __device__ __forceinline__ void carried_term(f32x4 (&acc)[TPof<P>::v], const typename NDot<T, N>::frag& cf,
                                              const T* s_prev, const float* s_da_h, int strip, int r, int qd) {
-  typedef ScanLds<T, P, N, HB> SL;
   typedef NDot<T, N> ND;
   constexpr int TP = P / 16;
   f32x4 t[TP];
 #pragma unroll
   for (int pt = 0; pt < TP; ++pt) {
     typename ND::frag pf;
-    ND::load(pf, &s_prev[(pt * 16 + r) * SL::BP], qd);
+    ND::load(pf, &s_prev[(pt * 16 + r) * BP], qd);
     t[pt] = ND::dot(cf, pf, zero4());
   }
   float sc[4];
@@ -167,22 +209,25 @@ __device__ __forceinline__ void carried_term(f32x4 (&acc)[TPof<P>::v], const typ
     for (int e = 0; e < 4; ++e) acc[pt][e] += t[pt][e] * sc[e];
 }
 
-// Diagonal-block contributions of staged tile J to one strip, for every head of the block.
-template <typename T, int P, int N, int HB>
+// Diagonal-block contributions of staged tile J to one strip, for every head of the block,
+// plus the skip term on the strip's own (diagonal) sub-tile.
+template <typename T, int P, int N, int HB, int BP, int XP>
 __device__ __forceinline__ void diag_tile(f32x4 (&acc)[HB][TPof<P>::v], const typename NDot<T, N>::frag& cf,
-                                          const T* s_b, const T* s_x, const float (*s_da)[256],
-                                          const float (*s_dt)[256], int strip, int J, int r, int qd) {
-  typedef ScanLds<T, P, N, HB> SL;
+                                          const float (&dco)[HB][TPof<P>::v], const T* s_b, const T* s_x,
+                                          const float (*s_da)[256], const float (*s_dt)[256], int strip, int J,
+                                          int r, int qd) {
   typedef NDot<T, N> ND;
   constexpr int TP = P / 16;
+  constexpr bool F32 = sizeof(T) == 4;
   const int i_row = 16 * strip + r;
 #pragma unroll
   for (int js = 0; js < 4; ++js) {
     const int jt = 4 * J + js;
     if (jt > strip) break;                               // causal: sub-tiles past the diagonal
+    const bool diag = jt == strip;
     // CB^T sub-tile: lane holds CB[i = 16 strip + r][j = 16 jt + 4 qd + e]
     typename ND::frag bfr;
-    ND::load(bfr, &s_b[(js * 16 + r) * SL::BP], qd);
+    ND::load(bfr, &s_b[(js * 16 + r) * BP], qd);
     const f32x4 cbt = ND::dot(bfr, cf, zero4());
     const int j0 = 16 * jt + 4 * qd;
 #pragma unroll
@@ -199,16 +244,22 @@ __device__ __forceinline__ void diag_tile(f32x4 (&acc)[HB][TPof<P>::v], const ty
       lw[1] = (j0 + 1 <= i_row) ? w1 : 0.f;
       lw[2] = (j0 + 2 <= i_row) ? w2 : 0.f;
       lw[3] = (j0 + 3 <= i_row) ? w3 : 0.f;
-      const T* xt = &s_x[(hh * P + r) * SL::XP + js * 16 + 4 * qd];
-      if (SL::F32) {
+      const T* xt = &s_x[(hh * P + r) * XP + js * 16 + 4 * qd];
+      if (F32) {
 #pragma unroll
         for (int pt = 0; pt < TP; ++pt) {
           const float4 xv =
-              *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(xt) + pt * 16 * SL::XP);
+              *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(xt) + pt * 16 * XP);
           acc[hh][pt] = mfma_16x16x4_f32(lw[0], xv.x, acc[hh][pt]);
           acc[hh][pt] = mfma_16x16x4_f32(lw[1], xv.y, acc[hh][pt]);
           acc[hh][pt] = mfma_16x16x4_f32(lw[2], xv.z, acc[hh][pt]);
           acc[hh][pt] = mfma_16x16x4_f32(lw[3], xv.w, acc[hh][pt]);
+          if (diag) {  // x rows 16 jt + 4 qd + e are this lane's output rows
+            acc[hh][pt][0] += dco[hh][pt] * xv.x;
+            acc[hh][pt][1] += dco[hh][pt] * xv.y;
+            acc[hh][pt][2] += dco[hh][pt] * xv.z;
+            acc[hh][pt][3] += dco[hh][pt] * xv.w;
+          }
         }
       } else {
         bf16x4 a;
@@ -219,42 +270,53 @@ __device__ __forceinline__ void diag_tile(f32x4 (&acc)[HB][TPof<P>::v], const ty
 #pragma unroll
         for (int pt = 0; pt < TP; ++pt) {
           const bf16x4 xv =
-              *reinterpret_cast<const bf16x4*>(reinterpret_cast<const __bf16*>(xt) + pt * 16 * SL::XP);
+              *reinterpret_cast<const bf16x4*>(reinterpret_cast<const __bf16*>(xt) + pt * 16 * XP);
           acc[hh][pt] = mfma_16x16x16_bf16(a, xv, acc[hh][pt]);
+          if (diag) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[hh][pt][e] += dco[hh][pt] * static_cast<float>(xv[e]);
+          }
         }
       }
     }
   }
 }
 
-// Skip term and store of one strip: lane holds rows 16 strip + 4 qd + e, column 16 pt + r.
-template <typename T, int P, int HB>
-__device__ __forceinline__ void store_strip(const f32x4 (&acc)[HB][TPof<P>::v], const T* x, const float* Dw, T* y,
-                                            size_t row0, size_t x_tok, int h0, int strip, int len, int r, int qd) {
-  constexpr int TP = P / 16;
+// Write one strip's (16 x P) results of head hh into the y staging rows.
+template <typename T, int P, int HB, int YP>
+__device__ __forceinline__ void put_strip(T* s_y, const f32x4 (&acc)[HB][TPof<P>::v], int hh, int lstrip, int r,
+                                          int qd) {
 #pragma unroll
-  for (int hh = 0; hh < HB; ++hh) {
-    const int h = h0 + hh;
+  for (int pt = 0; pt < P / 16; ++pt)
 #pragma unroll
-    for (int pt = 0; pt < TP; ++pt) {
-      const int p = pt * 16 + r;
-      const float dw = Dw ? Dw[(size_t)h * P + p] : 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 16 * strip + 4 * qd + e;
-        if (i < len) {
-          const size_t o = (row0 + i) * x_tok + (size_t)h * P + p;
-          y[o] = from_f32<T>(acc[hh][pt][e] + dw * to_f32(x[o]));
-        }
-      }
-    }
+    for (int e = 0; e < 4; ++e) s_y[(16 * lstrip + 4 * qd + e) * YP + pt * 16 + r] = from_f32<T>(acc[hh][pt][e]);
+}
+
+// Copy staged rows [0, rows) of y (head h) to global memory as 16-byte row segments.
+template <typename T, int P, int YP>
+__device__ __forceinline__ void flush_rows(T* y, const T* s_y, size_t row0, size_t x_tok, int h, int rows,
+                                           int tid, int nthr) {
+  constexpr int VEC = Vec16<T>::n, PV = P / VEC;
+  for (int v = tid; v < rows * PV; v += nthr) {
+    const int i = v / PV, cv = (v % PV) * VEC;
+    *reinterpret_cast<uint4*>(y + (row0 + i) * x_tok + (size_t)h * P + cv) =
+        *reinterpret_cast<const uint4*>(&s_y[i * YP + cv]);
+  }
+}
+
+template <int HB>
+__device__ __forceinline__ void load_chunk_scalars(float (*s_da)[256], float (*s_dt)[256], const float* dtp,
+                                                   const float* dAcs, int b, int H, int h0, int nc, int c, int Q,
+                                                   int tid, int nthr) {
+  for (int idx = tid; idx < HB * Q; idx += nthr) {
+    const int hh = idx / Q, i = idx % Q;
+    const size_t off = (((size_t)b * H + h0 + hh) * nc + c) * Q + i;
+    s_dt[hh][i] = dtp[off];
+    s_da[hh][i] = dAcs[off] * kLog2e;
   }
 }
 
 // ---------------------------------------------------------------- row-block decomposition
-// One workgroup per (64-row block, HB heads): many small workgroups, for compute-bound
-// (fp32) problems.  Rows of one chunk are spread over Q/64 workgroups, so x tiles and the
-// carried state are read once per row block.
 template <typename T, int P, int N, int HB>
 __global__ __launch_bounds__(256, 2) void chunk_scan_rows_kernel(const T* __restrict__ x,
                                                                  const T* __restrict__ Bm,
@@ -265,14 +327,17 @@ __global__ __launch_bounds__(256, 2) void chunk_scan_rows_kernel(const T* __rest
                                                                  const float* __restrict__ Dw,
                                                                  T* __restrict__ y,
                                                                  int L, int H, int G, int nc, int Q, int B) {
-  typedef ScanLds<T, P, N, HB> SL;
+  constexpr int NTHR = 256;
+  typedef ScanLds<T, P, N, HB, kKT> SL;
   typedef NDot<T, N> ND;
   constexpr int TP = P / 16;
 
-  __shared__ __attribute__((aligned(16))) T s_b[SL::B_ELEMS];
-  __shared__ __attribute__((aligned(16))) T s_xu[SL::XU_ELEMS];   // Hprev, then x^T tiles
+  __shared__ __attribute__((aligned(16))) T s_mem[SL::TOTAL];
   __shared__ __attribute__((aligned(16))) float s_da[HB][256];     // dAcs * log2(e)
   __shared__ __attribute__((aligned(16))) float s_dt[HB][256];
+  T* s_b = s_mem;
+  T* s_xu = s_mem + SL::B_ELEMS;                                   // Hprev, then x^T tiles
+  T* s_y = s_mem;                                                  // y staging, at the end
 
   // work unit: row-block class (heaviest first), then XCD-local (b, c, head block)
   const int nrb = Q / kKT;
@@ -303,18 +368,24 @@ __global__ __launch_bounds__(256, 2) void chunk_scan_rows_kernel(const T* __rest
   const int s = rb * 4 + wave;                          // this wavefront's strip
   const bool strip_ok = 16 * s < len;
 
-  for (int idx = tid; idx < HB * Q; idx += 256) {
-    const int hh = idx / Q, i = idx % Q;
-    const size_t off = (((size_t)b * H + h0 + hh) * nc + c) * Q + i;
-    s_dt[hh][i] = dtp[off];
-    s_da[hh][i] = dAcs[off] * kLog2e;
-  }
   const size_t bc_tok = (size_t)G * N, x_tok = (size_t)H * P;
   const T* Cb = Cm + ((size_t)b * L + t0) * bc_tok + (size_t)g * N;
   const T* Bb = Bm + ((size_t)b * L + t0) * bc_tok + (size_t)g * N;
+  const T* xb = x + ((size_t)b * L + t0) * x_tok + (size_t)h0 * P;
+
+  TileRegs<T, P, N, HB, NTHR> tr;
+  tr.load(Bb, xb, (uint32_t)bc_tok, (uint32_t)x_tok, 0, len, tid);
+  load_chunk_scalars<HB>(s_da, s_dt, dtp, dAcs, b, H, h0, nc, c, Q, tid, NTHR);
   typename ND::frag cf;
-  if (16 * s + r < len) ND::load(cf, Cb + (size_t)(16 * s + r) * bc_tok, qd);
-  else ND::zero(cf);
+  {
+    const int i = 16 * s + r;
+    ND::load(cf, Cb + (size_t)(i < len ? i : 0) * bc_tok, qd, i < len);
+  }
+  float dco[HB][TP];
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh)
+#pragma unroll
+    for (int pt = 0; pt < TP; ++pt) dco[hh][pt] = Dw ? Dw[(size_t)(h0 + hh) * P + pt * 16 + r] : 0.f;
 
   f32x4 acc[HB][TP];
 #pragma unroll
@@ -325,24 +396,28 @@ __global__ __launch_bounds__(256, 2) void chunk_scan_rows_kernel(const T* __rest
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) {
     __syncthreads();
-    stage_prev<T, P, N, HB>(s_xu, states + (((size_t)b * nc + c) * H + h0 + hh) * (size_t)(P * N), tid, 256);
+    stage_prev<T, P, N, SL::BP>(s_xu, states + (((size_t)b * nc + c) * H + h0 + hh) * (size_t)(P * N), tid, NTHR);
     __syncthreads();
-    if (strip_ok) carried_term<T, P, N, HB>(acc[hh], cf, s_xu, s_da[hh], s, r, qd);
+    if (strip_ok) carried_term<T, P, N, SL::BP>(acc[hh], cf, s_xu, s_da[hh], s, r, qd);
   }
-  const T* xb = x + ((size_t)b * L + t0) * x_tok + (size_t)h0 * P;
   for (int J = 0; J <= rb; ++J) {
     __syncthreads();
-    stage_tile<T, P, N, HB>(s_b, s_xu, Bb, xb, bc_tok, x_tok, J, len, tid, 256);
+    tr.template store<SL::BP, SL::XP>(s_b, s_xu, tid);
+    if (J < rb) tr.load(Bb, xb, (uint32_t)bc_tok, (uint32_t)x_tok, J + 1, len, tid);
     __syncthreads();
-    if (strip_ok) diag_tile<T, P, N, HB>(acc, cf, s_b, s_xu, s_da, s_dt, s, J, r, qd);
+    if (strip_ok) diag_tile<T, P, N, HB, SL::BP, SL::XP>(acc, cf, dco, s_b, s_xu, s_da, s_dt, s, J, r, qd);
   }
-  if (strip_ok) store_strip<T, P, HB>(acc, x, Dw, y, (size_t)b * L + t0, x_tok, h0, s, len, r, qd);
+  const int rows = min(kKT, len - rb * kKT);
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) {
+    __syncthreads();
+    if (strip_ok) put_strip<T, P, HB, SL::YP>(s_y, acc, hh, wave, r, qd);
+    __syncthreads();
+    flush_rows<T, P, SL::YP>(y, s_y, (size_t)b * L + t0 + rb * kKT, x_tok, h0 + hh, rows, tid, NTHR);
+  }
 }
 
 // ---------------------------------------------------------------- whole-chunk decomposition
-// One workgroup per (chunk, HB heads) with Q/32 wavefronts; wavefront w owns the strip pair
-// (w, S-1-w), so every wavefront has S+1 causal sub-tiles.  x, the carried state and y move
-// exactly once, for memory-bound (bf16) problems.
 template <typename T, int P, int N, int HB>
 __global__ __launch_bounds__(512) void chunk_scan_chunk_kernel(const T* __restrict__ x,
                                                                const T* __restrict__ Bm,
@@ -353,14 +428,17 @@ __global__ __launch_bounds__(512) void chunk_scan_chunk_kernel(const T* __restri
                                                                const float* __restrict__ Dw,
                                                                T* __restrict__ y,
                                                                int L, int H, int G, int nc, int Q, uint32_t nblocks) {
-  typedef ScanLds<T, P, N, HB> SL;
+  constexpr int NTHR = 512;
+  typedef ScanLds<T, P, N, HB, 256> SL;
   typedef NDot<T, N> ND;
   constexpr int TP = P / 16;
 
-  __shared__ __attribute__((aligned(16))) T s_b[SL::B_ELEMS];
-  __shared__ __attribute__((aligned(16))) T s_xu[SL::XU_ELEMS];
+  __shared__ __attribute__((aligned(16))) T s_mem[SL::TOTAL];
   __shared__ __attribute__((aligned(16))) float s_da[HB][256];
   __shared__ __attribute__((aligned(16))) float s_dt[HB][256];
+  T* s_b = s_mem;
+  T* s_xu = s_mem + SL::B_ELEMS;
+  T* s_y = s_mem;
 
   uint32_t id = xcd_swizzle(blockIdx.x, nblocks);
   const int nhb = H / HB;
@@ -372,29 +450,37 @@ __global__ __launch_bounds__(512) void chunk_scan_chunk_kernel(const T* __restri
   const int t0 = c * Q;
   const int len = min(Q, L - t0);
   const int S = Q >> 4;
-  const int nthr = blockDim.x;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, qd = lane >> 4;
+  const bool active = wave < (S >> 1);                  // wavefronts past Q/32 only stage data
   int strip[2];
   strip[0] = wave;                                      // short strip
   strip[1] = S - 1 - wave;                              // long strip
+  bool ok[2];
+  ok[0] = active && 16 * strip[0] < len;
+  ok[1] = active && 16 * strip[1] < len;
 
-  for (int idx = tid; idx < HB * Q; idx += nthr) {
-    const int hh = idx / Q, i = idx % Q;
-    const size_t off = (((size_t)b * H + h0 + hh) * nc + c) * Q + i;
-    s_dt[hh][i] = dtp[off];
-    s_da[hh][i] = dAcs[off] * kLog2e;
-  }
   const size_t bc_tok = (size_t)G * N, x_tok = (size_t)H * P;
   const T* Cb = Cm + ((size_t)b * L + t0) * bc_tok + (size_t)g * N;
   const T* Bb = Bm + ((size_t)b * L + t0) * bc_tok + (size_t)g * N;
+  const T* xb = x + ((size_t)b * L + t0) * x_tok + (size_t)h0 * P;
+
+  TileRegs<T, P, N, HB, NTHR> tr;
+  tr.load(Bb, xb, (uint32_t)bc_tok, (uint32_t)x_tok, 0, len, tid);
+  load_chunk_scalars<HB>(s_da, s_dt, dtp, dAcs, b, H, h0, nc, c, Q, tid, NTHR);
   typename ND::frag cf[2];
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
-    if (16 * strip[st] + r < len) ND::load(cf[st], Cb + (size_t)(16 * strip[st] + r) * bc_tok, qd);
-    else ND::zero(cf[st]);
+    const int i = 16 * strip[st] + r;
+    const bool in = active && i < len;
+    ND::load(cf[st], Cb + (size_t)(in ? i : 0) * bc_tok, qd, in);
   }
+  float dco[HB][TP];
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh)
+#pragma unroll
+    for (int pt = 0; pt < TP; ++pt) dco[hh][pt] = Dw ? Dw[(size_t)(h0 + hh) * P + pt * 16 + r] : 0.f;
 
   f32x4 acc[2][HB][TP];
 #pragma unroll
@@ -407,34 +493,39 @@ __global__ __launch_bounds__(512) void chunk_scan_chunk_kernel(const T* __restri
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) {
     __syncthreads();
-    stage_prev<T, P, N, HB>(s_xu, states + (((size_t)b * nc + c) * H + h0 + hh) * (size_t)(P * N), tid, nthr);
+    stage_prev<T, P, N, SL::BP>(s_xu, states + (((size_t)b * nc + c) * H + h0 + hh) * (size_t)(P * N), tid, NTHR);
     __syncthreads();
 #pragma unroll
     for (int st = 0; st < 2; ++st)
-      if (16 * strip[st] < len) carried_term<T, P, N, HB>(acc[st][hh], cf[st], s_xu, s_da[hh], strip[st], r, qd);
+      if (ok[st]) carried_term<T, P, N, SL::BP>(acc[st][hh], cf[st], s_xu, s_da[hh], strip[st], r, qd);
   }
-  const T* xb = x + ((size_t)b * L + t0) * x_tok + (size_t)h0 * P;
   const int ntiles = (len + kKT - 1) / kKT;
   for (int J = 0; J < ntiles; ++J) {
     __syncthreads();
-    stage_tile<T, P, N, HB>(s_b, s_xu, Bb, xb, bc_tok, x_tok, J, len, tid, nthr);
+    tr.template store<SL::BP, SL::XP>(s_b, s_xu, tid);
+    if (J + 1 < ntiles) tr.load(Bb, xb, (uint32_t)bc_tok, (uint32_t)x_tok, J + 1, len, tid);
     __syncthreads();
 #pragma unroll
     for (int st = 0; st < 2; ++st)
-      if (16 * strip[st] < len && 4 * J <= strip[st])
-        diag_tile<T, P, N, HB>(acc[st], cf[st], s_b, s_xu, s_da, s_dt, strip[st], J, r, qd);
+      if (ok[st] && 4 * J <= strip[st])
+        diag_tile<T, P, N, HB, SL::BP, SL::XP>(acc[st], cf[st], dco, s_b, s_xu, s_da, s_dt, strip[st], J, r, qd);
   }
 #pragma unroll
-  for (int st = 0; st < 2; ++st)
-    if (16 * strip[st] < len)
-      store_strip<T, P, HB>(acc[st], x, Dw, y, (size_t)b * L + t0, x_tok, h0, strip[st], len, r, qd);
+  for (int hh = 0; hh < HB; ++hh) {
+    __syncthreads();
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+      if (ok[st]) put_strip<T, P, HB, SL::YP>(s_y, acc[st], hh, strip[st], r, qd);
+    __syncthreads();
+    flush_rows<T, P, SL::YP>(y, s_y, (size_t)b * L + t0, x_tok, h0 + hh, len, tid, NTHR);
+  }
 }
 
 template <typename T, int P, int N, int HB>
 static hipError_t launch_scan_hb(const FwdArgs& a, hipStream_t s) {
   if (a.scan_variant == 2) {
     const uint32_t nblocks = (uint32_t)a.B * a.nc * (a.H / HB);
-    chunk_scan_chunk_kernel<T, P, N, HB><<<nblocks, 64 * (a.Q / 32), 0, s>>>(
+    chunk_scan_chunk_kernel<T, P, N, HB><<<nblocks, 512, 0, s>>>(
         static_cast<const T*>(a.x), static_cast<const T*>(a.Bm), static_cast<const T*>(a.Cm), a.dtp, a.dAcs,
         a.states, a.D, static_cast<T*>(a.y), a.L, a.H, a.G, a.nc, a.Q, nblocks);
   } else {

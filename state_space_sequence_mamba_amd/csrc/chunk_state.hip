@@ -65,27 +65,33 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const T* __restrict__ 
   const T* xb = x + ((size_t)b * L + t0) * xs + (size_t)h * P;
   const T* bb = Bm + ((size_t)b * L + t0) * bs + (size_t)g * N;
 
+  // Tile registers: loads read clamped in-bounds addresses and only record which tokens are
+  // real; the zeroing selects happen when the tile is written to LDS, so the next tile's
+  // loads stay in flight during the current tile's MFMAs.
   Vec16<T> xr[XPT][2], br[BPT][2];
+  uint32_t okm = 0;
+  const uint32_t xs32 = (uint32_t)xs, bs32 = (uint32_t)bs;
   auto load_tile = [&](int k0) {
+    okm = 0;
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {
-      const int v = tid + 256 * u;
-      if (v < XU) {
-        const int m = v % (KT / 2), pv = (v / (KT / 2)) * VEC;
-        const int tok = k0 + 2 * m;
-        xr[u][0] = (tok < len) ? load16(xb + (size_t)tok * xs + pv) : zero16<T>();
-        xr[u][1] = (tok + 1 < len) ? load16(xb + (size_t)(tok + 1) * xs + pv) : zero16<T>();
-      }
+      const int v = min(tid + 256 * u, XU - 1);
+      const int m = v % (KT / 2), pv = (v / (KT / 2)) * VEC;
+      const int tok = k0 + 2 * m;
+      const bool ok0 = tok < len, ok1 = tok + 1 < len;
+      xr[u][0] = load16(xb + (uint32_t)(ok0 ? tok : 0) * xs32 + pv);
+      xr[u][1] = load16(xb + (uint32_t)(ok1 ? tok + 1 : 0) * xs32 + pv);
+      okm |= ((uint32_t)ok0 << (2 * u)) | ((uint32_t)ok1 << (2 * u + 1));
     }
 #pragma unroll
     for (int u = 0; u < BPT; ++u) {
-      const int v = tid + 256 * u;
-      if (v < BU) {
-        const int m = v % (KT / 2), nv = (v / (KT / 2)) * VEC;
-        const int tok = k0 + 2 * m;
-        br[u][0] = (tok < len) ? load16(bb + (size_t)tok * bs + nv) : zero16<T>();
-        br[u][1] = (tok + 1 < len) ? load16(bb + (size_t)(tok + 1) * bs + nv) : zero16<T>();
-      }
+      const int v = min(tid + 256 * u, BU - 1);
+      const int m = v % (KT / 2), nv = (v / (KT / 2)) * VEC;
+      const int tok = k0 + 2 * m;
+      const bool ok0 = tok < len, ok1 = tok + 1 < len;
+      br[u][0] = load16(bb + (uint32_t)(ok0 ? tok : 0) * bs32 + nv);
+      br[u][1] = load16(bb + (uint32_t)(ok1 ? tok + 1 : 0) * bs32 + nv);
+      okm |= ((uint32_t)ok0 << (2 * XPT + 2 * u)) | ((uint32_t)ok1 << (2 * XPT + 2 * u + 1));
     }
   };
   auto store_tile = [&](int k0) {
@@ -95,9 +101,11 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const T* __restrict__ 
       if (v < XU) {
         const int m = v % (KT / 2), pv = (v / (KT / 2)) * VEC;
         const float w0 = s_w[k0 + 2 * m], w1 = s_w[k0 + 2 * m + 1];
+        const Vec16<T> x0 = keep_if(xr[u][0], (okm >> (2 * u)) & 1u);
+        const Vec16<T> x1 = keep_if(xr[u][1], (okm >> (2 * u + 1)) & 1u);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          T pair[2] = {from_f32<T>(to_f32(xr[u][0].v[e]) * w0), from_f32<T>(to_f32(xr[u][1].v[e]) * w1)};
+          T pair[2] = {from_f32<T>(to_f32(x0.v[e]) * w0), from_f32<T>(to_f32(x1.v[e]) * w1)};
           __builtin_memcpy(&s_x[(pv + e) * PITCH + 2 * m], pair, sizeof(pair));
         }
       }
@@ -107,9 +115,11 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const T* __restrict__ 
       const int v = tid + 256 * u;
       if (v < BU) {
         const int m = v % (KT / 2), nv = (v / (KT / 2)) * VEC;
+        const Vec16<T> b0 = keep_if(br[u][0], (okm >> (2 * XPT + 2 * u)) & 1u);
+        const Vec16<T> b1 = keep_if(br[u][1], (okm >> (2 * XPT + 2 * u + 1)) & 1u);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          T pair[2] = {br[u][0].v[e], br[u][1].v[e]};
+          T pair[2] = {b0.v[e], b1.v[e]};
           __builtin_memcpy(&s_b[(nv + e) * PITCH + 2 * m], pair, sizeof(pair));
         }
       }
@@ -136,9 +146,10 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const T* __restrict__ 
 #pragma unroll
         for (int i = 0; i < WP; ++i) {
           const int tp = wp * WP + i;
-          af[i] = (tp < TP) ? *reinterpret_cast<const float4*>(
-                                  reinterpret_cast<const float*>(s_x) + (tp * 16 + r) * PITCH + 16 * qd + 4 * m)
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
+          const int tpc = tp < TP ? tp : TP - 1;  // clamped read, zeroed by select
+          const float4 v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(s_x) +
+                                                            (tpc * 16 + r) * PITCH + 16 * qd + 4 * m);
+          af[i] = (tp < TP) ? v : make_float4(0.f, 0.f, 0.f, 0.f);
         }
 #pragma unroll
         for (int j = 0; j < WN; ++j)
@@ -161,9 +172,10 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const T* __restrict__ 
 #pragma unroll
         for (int i = 0; i < WP; ++i) {
           const int tp = wp * WP + i;
-          af[i] = (tp < TP) ? *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(s_x) +
-                                                               (tp * 16 + r) * PITCH + 32 * kk + 8 * qd)
-                            : KMma<__bf16>::zero();
+          const int tpc = tp < TP ? tp : TP - 1;
+          const bf16x8 v = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(s_x) +
+                                                            (tpc * 16 + r) * PITCH + 32 * kk + 8 * qd);
+          af[i] = (tp < TP) ? v : KMma<__bf16>::zero();
         }
 #pragma unroll
         for (int j = 0; j < WN; ++j)

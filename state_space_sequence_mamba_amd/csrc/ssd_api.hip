@@ -84,9 +84,12 @@ int pick_heads_per_block(int B, int nc, int H, int G, int Q, int variant) {
     for (int hb : kChoices)
       if (hb == g_tune_heads_per_block && hpg % hb == 0) return hb;
   }
-  const long per_head = (long)B * nc * G * (variant == 1 ? Q / 64 : 1);  // workgroups per head of a group
+  // workgroups per head of a group; the row-block kernel needs more of them (its units are
+  // small and uneven), so it aims for twice the target
+  const long per_head = (long)B * nc * G * (variant == 1 ? Q / 64 : 1);
+  const long target = (long)g_tune_min_blocks * (variant == 1 ? 2 : 1);
   for (int hb : kChoices)
-    if (hpg % hb == 0 && per_head * (hpg / hb) >= g_tune_min_blocks) return hb;
+    if (hpg % hb == 0 && per_head * (hpg / hb) >= target) return hb;
   return 1;
 }
 

@@ -43,6 +43,32 @@ __device__ __forceinline__ Vec16<T> zero16() {
   *reinterpret_cast<uint4*>(&r) = make_uint4(0, 0, 0, 0);
   return r;
 }
+// Zero a 16-byte vector unless ok (branch-free select).
+template <typename T>
+__device__ __forceinline__ Vec16<T> keep_if(const Vec16<T>& in, bool ok) {
+  uint4 v = *reinterpret_cast<const uint4*>(&in);
+  v.x = ok ? v.x : 0u;
+  v.y = ok ? v.y : 0u;
+  v.z = ok ? v.z : 0u;
+  v.w = ok ? v.w : 0u;
+  Vec16<T> r;
+  *reinterpret_cast<uint4*>(&r) = v;
+  return r;
+}
+// Branch-free guarded load: always reads `p` (the caller passes an in-bounds address,
+// clamped when the element is not wanted) and returns zeros when !ok.  A conditional load
+// would compile to a branch with an immediate wait for the data, serialising every load.
+template <typename T>
+__device__ __forceinline__ Vec16<T> load16_if(const T* p, bool ok) {
+  uint4 v = *reinterpret_cast<const uint4*>(p);
+  v.x = ok ? v.x : 0u;
+  v.y = ok ? v.y : 0u;
+  v.z = ok ? v.z : 0u;
+  v.w = ok ? v.w : 0u;
+  Vec16<T> r;
+  *reinterpret_cast<uint4*>(&r) = v;
+  return r;
+}
 
 // ---------------------------------------------------------------- scalar maths
 // softplus(v) = log(1 + e^v).  Above 20 the correction log1p(e^-v) < 2.1e-9 is below
