@@ -23,6 +23,8 @@ import torch  # noqa: E402
 
 from state_space_sequence_mamba_amd import inputs as I  # noqa: E402
 from state_space_sequence_mamba_amd import ssd  # noqa: E402
+from state_space_sequence_mamba_amd.profiling import load_traffic, workload_slug  # noqa: E402
+from state_space_sequence_mamba_amd.timing import HipEvents  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0                         # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}   # dense matrix peaks, TFLOP/s
@@ -96,6 +98,9 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch the timed steps eagerly, not as a HIP graph")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="after timing, run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--heads-per-block", type=int, default=0, help="chunk_scan launch shape (0 = built-in)")
     ap.add_argument("--scan-variant", type=int, default=0,
                     help="chunk_scan decomposition: 1 = 64-row blocks, 2 = whole chunks, 0 = built-in")
@@ -124,46 +129,60 @@ def main():
     y_dec = torch.empty_like(dd["x"])
     dims = ssd.make_dims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, d["x"].dtype)
     ws = torch.empty(ssd.ssd_fwd_workspace_size(dims, w.chunk), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
 
     K, W = args.steps, args.warmup
+    use_graph = not args.no_graph
+    hev = HipEvents()
     nev = 7   # 5 around the forward's kernels, 2 around ssd_step
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(max(K, 1))]
-    for evs in events:          # create the underlying HIP events
-        for e in evs:
-            e.record(stream)
-    torch.cuda.synchronize()
+    events = [[hev.create() for _ in range(nev)] for _ in range(max(K, 1))]
+    t_start, t_end = hev.create(), hev.create()
 
     def step(evs=None):
-        handles = None if evs is None else [e.cuda_event for e in evs[:5]]
+        # launches go to the current stream (the capture stream while a graph is captured)
         ssd.ssd_fwd(d["x"], d["dt"], d["dt_bias"], d["A"], d["B"], d["C"], d["D"], chunk_size=w.chunk,
-                    y=y, final_state=state, workspace=ws, stream=stream, stage_events=handles)
+                    y=y, final_state=state, workspace=ws, stage_events=None if evs is None else evs[:5])
         if evs is not None:
-            evs[5].record(stream)
-        ssd.ssd_step(state, dd["x"], dd["dt"], d["dt_bias"], d["A"], dd["B"], dd["C"], d["D"], y=y_dec,
-                     stream=stream)
+            hev.record(evs[5])
+        ssd.ssd_step(state, dd["x"], dd["dt"], d["dt_bias"], d["A"], dd["B"], dd["C"], d["D"], y=y_dec)
         if evs is not None:
-            evs[6].record(stream)
+            hev.record(evs[6])
 
     for _ in range(W):
         step()
     torch.cuda.synchronize()
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if use_graph:
+        # the K steps are captured once into a HIP graph; the timed region is one replay
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(graph, stream=cap):
+            for _ in range(K):
+                step()
+        torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t_start.record(stream)
-    for i in range(K):
-        step(events[i])
-    t_end.record(stream)
+    hev.record(t_start)
+    if use_graph:
+        graph.replay()
+    else:
+        for _ in range(K):
+            step()
+    hev.record(t_end)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
+    total_ms = hev.elapsed_ms(t_start, t_end)
     ms_per_step = total_ms / K
+
+    # Per-kernel durations: the same K steps launched eagerly with HIP events between the
+    # kernels (timing events cannot live inside a captured graph on this runtime).
+    for i in range(K):
+        step(events[i])
+    torch.cuda.synchronize()
 
     per_kernel_ms = {k: 0.0 for k in KERNELS}
     pairs = [(0, 1), (1, 2), (2, 3), (3, 4), (5, 6)]
     for evs in events[:K]:
         for k, (a, b) in zip(KERNELS, pairs):
-            per_kernel_ms[k] += evs[a].elapsed_time(evs[b]) / K
+            per_kernel_ms[k] += hev.elapsed_ms(evs[a], evs[b]) / K
 
     cost = algorithmic_cost(w)
     kernels = {}
@@ -179,8 +198,10 @@ def main():
                       "alg_bytes": c["bytes"], "alg_flops": c["flops"]}
     dom = max(KERNELS, key=lambda k: per_kernel_ms[k])
     kd = kernels[dom]
+    # measured HBM bytes per launch of the dominant kernel (FETCH_SIZE + WRITE_SIZE runs,
+    # calibrated on a plain copy); None when absent or taken on different kernel sources
     roofline = {"kernel": dom, "bound": kd["bound"], "achieved": kd["achieved"], "peak": kd["peak"],
-                "unit": kd["unit"], "frac": kd["frac"], "traffic": None}
+                "unit": kd["unit"], "frac": kd["frac"], "traffic": load_traffic(workload_slug(w.name), dom)}
 
     tokens = w.batch * (w.seqlen + 1)
     out = {
@@ -201,10 +222,18 @@ def main():
                    "chunk_size": w.chunk, "tokens_per_step": tokens},
         "roofline": roofline,
         "kernels": kernels,
+        "launch": ("hip_graph (per-kernel times from an eager pass of the same K steps)" if use_graph
+                   else "eager"),
         "wall_s_timed_region": round(wall, 4),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, dec, args.cpu_budget)
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb * 1024 * 1024
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
     print(json.dumps(out), flush=True)
 
 

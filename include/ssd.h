@@ -97,8 +97,10 @@ ssd_status_t ssd_fwd(const ssd_dims_t* dims,
 /* ssd_fwd with per-kernel timing: identical arguments and results, plus `stage_events`,
  * an array of 5 events created by the caller (hipEventCreate).  stage_events[k] is
  * recorded on `stream` just before kernel k (0 chunk_cumsum, 1 chunk_state,
- * 2 state_passing, 3 chunk_scan) and stage_events[4] after the last one.  For
- * measurement tools; NULL stage_events behaves exactly like ssd_fwd. */
+ * 2 state_passing, 3 chunk_scan) and stage_events[4] after the last one.  Event records
+ * cannot be captured into a graph: with non-NULL stage_events on a stream under capture the
+ * call returns SSD_ERR_UNSUPPORTED and launches nothing.  For measurement tools; NULL
+ * stage_events behaves exactly like ssd_fwd (which may be captured). */
 ssd_status_t ssd_fwd_timed(const ssd_dims_t* dims,
                            const void* x, const void* dt, const float* dt_bias, const float* A,
                            const void* B, const void* C, const float* D, int chunk_size,

@@ -12,8 +12,8 @@
 extern "C" {
 #endif
 
-/* key 0: heads per chunk_scan workgroup (heads of one group sharing one C B^T evaluation);
- *        0 restores the built-in choice; ignored unless it divides nheads / ngroups.
+/* key 0: heads per chunk_scan workgroup (heads of one group sharing one C B^T evaluation):
+ *        1 or 2; 0 restores the built-in choice; ignored unless it divides nheads / ngroups.
  * key 1: minimum chunk_scan workgroup count the built-in choice aims for (default 512).
  * key 2: chunk_scan decomposition: 1 = one workgroup per 64-row block of a chunk,
  *        2 = one workgroup per whole chunk, 0 = built-in choice (1 for fp32, 2 for bf16).

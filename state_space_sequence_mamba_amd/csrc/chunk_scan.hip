@@ -209,76 +209,85 @@ __device__ __forceinline__ void carried_term(f32x4 (&acc)[TPof<P>::v], const typ
     for (int e = 0; e < 4; ++e) acc[pt][e] += t[pt][e] * sc[e];
 }
 
-// Diagonal-block contributions of staged tile J to one strip, for every head of the block,
-// plus the skip term on the strip's own (diagonal) sub-tile.
+// One causal 16x16 sub-tile (column tile jt, local index js in the staged tile) of one strip,
+// for every head of the block.  EDGE: the sub-tile may be the diagonal one, whose columns past
+// the diagonal are masked and which adds the skip term.
+template <typename T, int P, int N, int HB, int BP, int XP, bool EDGE>
+__device__ __forceinline__ void sub_tile(f32x4 (&acc)[HB][TPof<P>::v], const typename NDot<T, N>::frag& cf,
+                                         const float (&dco)[HB][TPof<P>::v], const T* s_b, const T* s_x,
+                                         const float (*s_da)[256], const float (*s_dt)[256], int strip, int jt,
+                                         int js, int r, int qd) {
+  typedef NDot<T, N> ND;
+  constexpr int TP = P / 16;
+  constexpr bool F32 = sizeof(T) == 4;
+  const int i_row = 16 * strip + r;
+  const bool diag = EDGE && jt == strip;
+  // CB^T sub-tile: lane holds CB[i = 16 strip + r][j = 16 jt + 4 qd + e]
+  typename ND::frag bfr;
+  ND::load(bfr, &s_b[(js * 16 + r) * BP], qd);
+  const f32x4 cbt = ND::dot(bfr, cf, zero4());
+  const int j0 = 16 * jt + 4 * qd;
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) {
+    const float da_i = s_da[hh][i_row];
+    const float4 daj = *reinterpret_cast<const float4*>(&s_da[hh][j0]);
+    const float4 dtj = *reinterpret_cast<const float4*>(&s_dt[hh][j0]);
+    float lw[4];
+    lw[0] = cbt[0] * __builtin_amdgcn_exp2f(da_i - daj.x) * dtj.x;
+    lw[1] = cbt[1] * __builtin_amdgcn_exp2f(da_i - daj.y) * dtj.y;
+    lw[2] = cbt[2] * __builtin_amdgcn_exp2f(da_i - daj.z) * dtj.z;
+    lw[3] = cbt[3] * __builtin_amdgcn_exp2f(da_i - daj.w) * dtj.w;
+    if (EDGE) {  // causal mask (select, so an overflowed factor above the diagonal is dropped)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) lw[e] = (j0 + e <= i_row) ? lw[e] : 0.f;
+    }
+    const T* xt = &s_x[(hh * P + r) * XP + js * 16 + 4 * qd];
+    if (F32) {
+#pragma unroll
+      for (int pt = 0; pt < TP; ++pt) {
+        const float4 xv = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(xt) + pt * 16 * XP);
+        acc[hh][pt] = mfma_16x16x4_f32(lw[0], xv.x, acc[hh][pt]);
+        acc[hh][pt] = mfma_16x16x4_f32(lw[1], xv.y, acc[hh][pt]);
+        acc[hh][pt] = mfma_16x16x4_f32(lw[2], xv.z, acc[hh][pt]);
+        acc[hh][pt] = mfma_16x16x4_f32(lw[3], xv.w, acc[hh][pt]);
+        if (diag) {  // x rows 16 jt + 4 qd + e are this lane's output rows
+          acc[hh][pt][0] += dco[hh][pt] * xv.x;
+          acc[hh][pt][1] += dco[hh][pt] * xv.y;
+          acc[hh][pt][2] += dco[hh][pt] * xv.z;
+          acc[hh][pt][3] += dco[hh][pt] * xv.w;
+        }
+      }
+    } else {
+      bf16x4 a;
+      a[0] = static_cast<__bf16>(lw[0]);
+      a[1] = static_cast<__bf16>(lw[1]);
+      a[2] = static_cast<__bf16>(lw[2]);
+      a[3] = static_cast<__bf16>(lw[3]);
+#pragma unroll
+      for (int pt = 0; pt < TP; ++pt) {
+        const bf16x4 xv = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const __bf16*>(xt) + pt * 16 * XP);
+        acc[hh][pt] = mfma_16x16x16_bf16(a, xv, acc[hh][pt]);
+        if (diag) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[hh][pt][e] += dco[hh][pt] * static_cast<float>(xv[e]);
+        }
+      }
+    }
+  }
+}
+
+// Diagonal-block contributions of staged tile J to one strip: its causal sub-tiles, the one
+// on the diagonal masked and carrying the skip term.
 template <typename T, int P, int N, int HB, int BP, int XP>
 __device__ __forceinline__ void diag_tile(f32x4 (&acc)[HB][TPof<P>::v], const typename NDot<T, N>::frag& cf,
                                           const float (&dco)[HB][TPof<P>::v], const T* s_b, const T* s_x,
                                           const float (*s_da)[256], const float (*s_dt)[256], int strip, int J,
                                           int r, int qd) {
-  typedef NDot<T, N> ND;
-  constexpr int TP = P / 16;
-  constexpr bool F32 = sizeof(T) == 4;
-  const int i_row = 16 * strip + r;
 #pragma unroll
   for (int js = 0; js < 4; ++js) {
     const int jt = 4 * J + js;
-    if (jt > strip) break;                               // causal: sub-tiles past the diagonal
-    const bool diag = jt == strip;
-    // CB^T sub-tile: lane holds CB[i = 16 strip + r][j = 16 jt + 4 qd + e]
-    typename ND::frag bfr;
-    ND::load(bfr, &s_b[(js * 16 + r) * BP], qd);
-    const f32x4 cbt = ND::dot(bfr, cf, zero4());
-    const int j0 = 16 * jt + 4 * qd;
-#pragma unroll
-    for (int hh = 0; hh < HB; ++hh) {
-      const float da_i = s_da[hh][i_row];
-      const float4 daj = *reinterpret_cast<const float4*>(&s_da[hh][j0]);
-      const float4 dtj = *reinterpret_cast<const float4*>(&s_dt[hh][j0]);
-      const float w0 = cbt[0] * __builtin_amdgcn_exp2f(da_i - daj.x) * dtj.x;
-      const float w1 = cbt[1] * __builtin_amdgcn_exp2f(da_i - daj.y) * dtj.y;
-      const float w2 = cbt[2] * __builtin_amdgcn_exp2f(da_i - daj.z) * dtj.z;
-      const float w3 = cbt[3] * __builtin_amdgcn_exp2f(da_i - daj.w) * dtj.w;
-      float lw[4];
-      lw[0] = (j0 + 0 <= i_row) ? w0 : 0.f;
-      lw[1] = (j0 + 1 <= i_row) ? w1 : 0.f;
-      lw[2] = (j0 + 2 <= i_row) ? w2 : 0.f;
-      lw[3] = (j0 + 3 <= i_row) ? w3 : 0.f;
-      const T* xt = &s_x[(hh * P + r) * XP + js * 16 + 4 * qd];
-      if (F32) {
-#pragma unroll
-        for (int pt = 0; pt < TP; ++pt) {
-          const float4 xv =
-              *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(xt) + pt * 16 * XP);
-          acc[hh][pt] = mfma_16x16x4_f32(lw[0], xv.x, acc[hh][pt]);
-          acc[hh][pt] = mfma_16x16x4_f32(lw[1], xv.y, acc[hh][pt]);
-          acc[hh][pt] = mfma_16x16x4_f32(lw[2], xv.z, acc[hh][pt]);
-          acc[hh][pt] = mfma_16x16x4_f32(lw[3], xv.w, acc[hh][pt]);
-          if (diag) {  // x rows 16 jt + 4 qd + e are this lane's output rows
-            acc[hh][pt][0] += dco[hh][pt] * xv.x;
-            acc[hh][pt][1] += dco[hh][pt] * xv.y;
-            acc[hh][pt][2] += dco[hh][pt] * xv.z;
-            acc[hh][pt][3] += dco[hh][pt] * xv.w;
-          }
-        }
-      } else {
-        bf16x4 a;
-        a[0] = static_cast<__bf16>(lw[0]);
-        a[1] = static_cast<__bf16>(lw[1]);
-        a[2] = static_cast<__bf16>(lw[2]);
-        a[3] = static_cast<__bf16>(lw[3]);
-#pragma unroll
-        for (int pt = 0; pt < TP; ++pt) {
-          const bf16x4 xv =
-              *reinterpret_cast<const bf16x4*>(reinterpret_cast<const __bf16*>(xt) + pt * 16 * XP);
-          acc[hh][pt] = mfma_16x16x16_bf16(a, xv, acc[hh][pt]);
-          if (diag) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[hh][pt][e] += dco[hh][pt] * static_cast<float>(xv[e]);
-          }
-        }
-      }
-    }
+    if (jt > strip) break;
+    sub_tile<T, P, N, HB, BP, XP, true>(acc, cf, dco, s_b, s_x, s_da, s_dt, strip, jt, js, r, qd);
   }
 }
 
@@ -539,12 +548,8 @@ static hipError_t launch_scan_hb(const FwdArgs& a, hipStream_t s) {
 
 template <typename T, int P, int N>
 static hipError_t launch_scan_impl(const FwdArgs& a, hipStream_t s) {
-  switch (a.heads_per_block) {
-    case 4: return launch_scan_hb<T, P, N, 4>(a, s);
-    case 3: return launch_scan_hb<T, P, N, 3>(a, s);
-    case 2: return launch_scan_hb<T, P, N, 2>(a, s);
-    default: return launch_scan_hb<T, P, N, 1>(a, s);
-  }
+  // instantiated head-block sizes: 1 and 2 (larger blocks need more registers than they save)
+  return a.heads_per_block == 2 ? launch_scan_hb<T, P, N, 2>(a, s) : launch_scan_hb<T, P, N, 1>(a, s);
 }
 
 hipError_t launch_chunk_scan(const FwdArgs& a, hipStream_t s) {

@@ -78,7 +78,7 @@ int pick_scan_variant(int dtype) {
 }
 
 int pick_heads_per_block(int B, int nc, int H, int G, int Q, int variant) {
-  static const int kChoices[] = {4, 3, 2, 1};  // instantiated head-block sizes
+  static const int kChoices[] = {2, 1};  // instantiated head-block sizes
   const int hpg = H / G;
   if (g_tune_heads_per_block > 0) {
     for (int hb : kChoices)
@@ -123,6 +123,13 @@ ssd_status_t fwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   for (const void* p : ptrs)
     if (p && !device_ptr_ok(p)) return SSD_ERR_DEVICE_PTR;
 
+  // timing events cannot be recorded into a graph capture on this runtime: refuse up front
+  if (ev) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return SSD_ERR_HIP;
+    if (cs != hipStreamCaptureStatusNone) return SSD_ERR_UNSUPPORTED;
+  }
+
   ssd::FwdArgs a;
   a.B = (int)dims->batch;
   a.L = (int)dims->seqlen;
@@ -156,20 +163,12 @@ ssd_status_t fwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
     return ssd::launch_state_passing(a, stream) == hipSuccess ? SSD_OK : SSD_ERR_HIP;
   }
 
-  hipError_t e = hipSuccess;
-  if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return SSD_ERR_HIP;
-  e = ssd::launch_chunk_cumsum(a, stream);
-  if (e != hipSuccess) return SSD_ERR_HIP;
-  if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return SSD_ERR_HIP;
-  e = ssd::launch_chunk_state(a, stream);
-  if (e != hipSuccess) return SSD_ERR_HIP;
-  if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return SSD_ERR_HIP;
-  e = ssd::launch_state_passing(a, stream);
-  if (e != hipSuccess) return SSD_ERR_HIP;
-  if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return SSD_ERR_HIP;
-  e = ssd::launch_chunk_scan(a, stream);
-  if (e != hipSuccess) return SSD_ERR_HIP;
-  if (ev && hipEventRecord(ev[4], stream) != hipSuccess) return SSD_ERR_HIP;
+  auto record = [&](int k) { return !ev || hipEventRecord(ev[k], stream) == hipSuccess; };
+  if (!record(0) || ssd::launch_chunk_cumsum(a, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (!record(1) || ssd::launch_chunk_state(a, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (!record(2) || ssd::launch_state_passing(a, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (!record(3) || ssd::launch_chunk_scan(a, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (!record(4)) return SSD_ERR_HIP;
   return SSD_OK;
 }
 

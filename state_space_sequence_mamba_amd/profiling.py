@@ -1,0 +1,151 @@
+"""Summaries of rocprofv3 runs of the benchmark (measurement tooling, not part of the scan).
+
+  python -m state_space_sequence_mamba_amd.profiling traffic \\
+      --fetch DIR --write DIR --copy-mb 1024 --workload NAME --command "..." --out profiles/X.json
+
+reads the counter CSVs of a FETCH_SIZE run and of a WRITE_SIZE run of `bench.py
+--copy-probe-mb N`, calibrates each counter on the plain device copy of N MiB that the
+benchmark ran in the same process (known bytes read and written), and writes, per SSD
+kernel, the HBM bytes per launch.  The JSON carries a digest of the HIP sources, so the
+benchmark reports the figure only while the kernels are unchanged.
+
+  python -m state_space_sequence_mamba_amd.profiling stats --trace DIR
+
+prints per-kernel average durations of a --kernel-trace --stats run.
+"""
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SSD_KERNELS = ["chunk_cumsum", "chunk_state", "state_passing", "chunk_scan", "ssd_step"]
+
+
+def source_digest():
+    """sha256 over the HIP sources and headers the library is built from."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(PKG, "csrc", "*"))) + sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def kernel_key(name):
+    """Map a dispatch's kernel name to an SSD stage, 'copy' for copy kernels, else None."""
+    if "chunk_scan" in name:
+        return "chunk_scan"
+    for k in ("chunk_cumsum", "chunk_state", "state_passing", "ssd_step"):
+        if k + "_kernel" in name:
+            return k
+    if "copyBuffer" in name or "copy_kernel" in name:
+        return "copy"
+    return None
+
+
+def _rows(d):
+    out = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            out.extend(csv.DictReader(fh))
+    if not out:
+        raise FileNotFoundError(f"no counter_collection.csv under {d}")
+    return out
+
+
+def counter_per_dispatch(d, counter):
+    """{kernel key: [value per dispatch]} for one counter (values summed over its instances)."""
+    per = {}
+    for r in _rows(d):
+        if r["Counter_Name"] != counter:
+            continue
+        key = kernel_key(r["Kernel_Name"])
+        if key is None:
+            continue
+        disp = (r["Dispatch_Id"], key)
+        per.setdefault(disp, 0.0)
+        per[disp] += float(r["Counter_Value"])
+    res = {}
+    for (disp, key), v in per.items():
+        res.setdefault(key, []).append(v)
+    return res
+
+
+def traffic(args):
+    copy_bytes = args.copy_mb * 1024 * 1024
+    fetch = counter_per_dispatch(args.fetch, "FETCH_SIZE")
+    write = counter_per_dispatch(args.write, "WRITE_SIZE")
+    # the probe copy is the largest "copy" dispatch (other copies are tiny staging copies)
+    f_copy = max(fetch.get("copy", [0.0]))
+    w_copy = max(write.get("copy", [0.0]))
+    if f_copy <= 0 or w_copy <= 0:
+        sys.exit("probe copy not found in the counter runs")
+    f_scale = copy_bytes / f_copy          # bytes per counter unit (counters report KiB)
+    w_scale = copy_bytes / w_copy
+    kernels = {}
+    for k in SSD_KERNELS:
+        if k in fetch and k in write:
+            fb = sum(fetch[k]) / len(fetch[k]) * f_scale
+            wb = sum(write[k]) / len(write[k]) * w_scale
+            kernels[k] = {"fetch_bytes": fb, "write_bytes": wb, "bytes": fb + wb,
+                          "dispatches": len(fetch[k])}
+    out = {"workload": args.workload, "source_digest": source_digest(),
+           "copy_probe_bytes": copy_bytes,
+           "copy_probe_counter_kib": {"FETCH_SIZE": f_copy, "WRITE_SIZE": w_copy},
+           "scale_bytes_per_unit": {"FETCH_SIZE": f_scale, "WRITE_SIZE": w_scale},
+           "kernels": kernels, "command": args.command}
+    with open(args.out, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def stats(args):
+    files = glob.glob(os.path.join(args.trace, "**", "*kernel_stats.csv"), recursive=True)
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                name = r["Name"].split("(")[0].replace("void ", "")
+                print(f"{name:70s} calls {r['Calls']:>5s}  avg {float(r['AverageNs']) / 1000:9.2f} us  "
+                      f"{float(r['Percentage']):6.2f} %")
+
+
+def workload_slug(name):
+    return "_".join(name.lower().split())
+
+
+def load_traffic(workload_slug, kernel):
+    """HBM bytes per launch of `kernel` from the committed summary, or None (missing/stale)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload_slug}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("source_digest") != source_digest() or kernel not in t.get("kernels", {}):
+        return None
+    return t["kernels"][kernel]["bytes"]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--copy-mb", type=int, required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--command", default="")
+    t.add_argument("--out", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("--trace", required=True)
+    a = ap.parse_args()
+    {"traffic": traffic, "stats": stats}[a.cmd](a)
+
+
+if __name__ == "__main__":
+    main()
