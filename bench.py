@@ -90,6 +90,50 @@ def cpu_baseline(w, inp, dec, budget_s):
                       f"{w.seqlen + 1} tokens (prefill + decode token), {secs:.2f} s, numpy, 1 thread"}
 
 
+def run_decode(w, args, dev):
+    """The decode workload: `w.steps` consecutive ssd_step calls from a random state (one token
+    per sequence per call), timed as one region; inputs for every step are resident in HBM."""
+    inp = I.make_step_inputs(w.batch, w.nheads, w.headdim, w.dstate, w.ngroups, w.steps, w.dtype, w.seed,
+                             w.d_init, device=dev)
+    state = inp["state0"].clone()
+    y = torch.empty_like(inp["x"][0])
+    W = min(args.warmup, w.steps)
+    for t in range(W):
+        ssd.ssd_step(state, inp["x"][t], inp["dt"][t], inp["dt_bias"], inp["A"], inp["B"][t], inp["C"][t],
+                     inp["D"], y=y)
+    state.copy_(inp["state0"])
+    torch.cuda.synchronize()
+    hev = HipEvents()
+    t0, t1 = hev.create(), hev.create()
+    wall0 = time.perf_counter()
+    hev.record(t0)
+    for t in range(w.steps):
+        ssd.ssd_step(state, inp["x"][t], inp["dt"][t], inp["dt_bias"], inp["A"], inp["B"][t], inp["C"][t],
+                     inp["D"], y=y)
+    hev.record(t1)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = hev.elapsed_ms(t0, t1)
+    e = 2 if w.dtype == "bf16" else 4
+    B, H, P, N, G = w.batch, w.nheads, w.headdim, w.dstate, w.ngroups
+    alg_bytes = 8 * B * H * P * N + 2 * B * H * P * e + B * H * e + 2 * B * G * N * e
+    per_step_s = ms * 1e-3 / w.steps
+    ach = alg_bytes / per_step_s / 1e9
+    out = {
+        "metric": "SSD decode tokens/sec at 1 MI355X + % of HBM roofline", "value": round(B * w.steps / (ms * 1e-3), 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": w.steps, "warmup": W, "ms_per_step": round(ms / w.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) state/x/B/C/dt per step)",
+        "config": {"workload": w.name, "batch": B, "nheads": H, "headdim": P, "dstate": N, "ngroups": G},
+        "roofline": {"kernel": "ssd_step", "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                     "alg_bytes_per_launch": alg_bytes},
+        "wall_s_timed_region": round(wall, 4),
+    }
+    hev.close()
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,10 +154,11 @@ def main():
               f"(see the sharding design for more GPUs)", file=sys.stderr)
         sys.exit(2)
     w = I.WORKLOADS[args.workload]
-    if w.entry != "fwd":
-        sys.exit("bench.py times forward workloads (prefill + one decode token)")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if w.entry == "step":
+        run_decode(w, args, dev)
+        return
     if args.heads_per_block:
         ssd.tune_set(0, args.heads_per_block)
     if args.scan_variant:

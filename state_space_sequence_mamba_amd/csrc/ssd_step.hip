@@ -6,6 +6,8 @@
 // Comparison"; D skip from Gap 4 of "Agent 228: MAMBA-2 Implementation Gaps").
 //
 // Bandwidth bound: the fp32 state is read and written once; everything else is small.
+// The state is streamed with non-temporal loads and stores: it is touched once per step and
+// a large decode batch does not fit the last-level cache, so caching it only evicts others.
 // One 256-thread workgroup per (b, h).  A row of N floats is covered by N/4 consecutive
 // lanes (one float4 each), so the state tile streams with fully coalesced 16-byte accesses
 // and the reduction over n is a butterfly of N/4 lanes inside a wavefront.  All state loads
@@ -47,13 +49,13 @@ __global__ __launch_bounds__(256) void ssd_step_kernel(float* __restrict__ state
   }
 
   float* st = state + (size_t)bh * P * N;
-  float4 s[NPASS];
+  f32x4 s[NPASS];
   float xv[NPASS];
 #pragma unroll
   for (int u = 0; u < NPASS; ++u) {
     const int p = row0 + u * RPP;
     if (p < P) {
-      s[u] = *reinterpret_cast<const float4*>(st + (size_t)p * N + col);
+      s[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(st + (size_t)p * N + col));
       xv[u] = to_f32(x[(size_t)bh * P + p]);
     }
   }
@@ -62,13 +64,11 @@ __global__ __launch_bounds__(256) void ssd_step_kernel(float* __restrict__ state
     const int p = row0 + u * RPP;
     if (p < P) {
       const float dx = d * xv[u];
-      float4 v = s[u];
-      v.x = a * v.x + dx * bv[0];
-      v.y = a * v.y + dx * bv[1];
-      v.z = a * v.z + dx * bv[2];
-      v.w = a * v.w + dx * bv[3];
-      *reinterpret_cast<float4*>(st + (size_t)p * N + col) = v;
-      float part = v.x * cv[0] + v.y * cv[1] + v.z * cv[2] + v.w * cv[3];
+      f32x4 v = s[u];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = a * v[e] + dx * bv[e];
+      __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(st + (size_t)p * N + col));
+      float part = v[0] * cv[0] + v[1] * cv[1] + v[2] * cv[2] + v[3] * cv[3];
 #pragma unroll
       for (int off = TPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
       if ((tid % TPR) == 0) {
