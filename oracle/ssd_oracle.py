@@ -24,8 +24,13 @@ Sources (the five pages of the foxhunt Mamba-2 notes):
   * "MAMBA2 Inference Optimization Report", Step 4: the last state is kept as
     the hidden state for stateful inference (here: final_state / ssd_step).
 
+Optional terms: an output gate y * silu(z) ("Agent 228: MAMBA-2 Reference
+Implementations Comparison", section 3.1 forward pass and section 6.1, output
+gating, applied to the scan output including the D term), and a clamp of dt' to
+[dt_min, dt_max] after the softplus (section 5.2 of the same page; Gap 3).
+
 Readings taken where the pages are silent or disagree (each listed in the
-design notes): no dt clamp; the bias is always added; A is used exactly as
+design notes): no dt clamp unless asked for; the bias is always added; A is used exactly as
 given (callers pass negative values); B is discretised by Euler (B * dt'),
 not exact zero-order hold; D has one value per (head, channel); head h uses
 group h // (H / G); the partial last chunk is processed; C is per token.
@@ -38,6 +43,7 @@ import numpy as np
 
 __all__ = [
     "softplus",
+    "silu",
     "head_groups",
     "ssd_recurrence",
     "ssd_step_ref",
@@ -62,6 +68,18 @@ def softplus(v):
     return np.logaddexp(0.0, v)
 
 
+def silu(v):
+    """v * sigmoid(v) = v / (1 + e^-v), the gate nonlinearity (float64)."""
+    return v / (1.0 + np.exp(-v))
+
+
+def _step_size(dt_raw, bias, dt_limit):
+    d = softplus(dt_raw + bias)
+    if dt_limit is not None:
+        d = np.clip(d, dt_limit[0], dt_limit[1])
+    return d
+
+
 def head_groups(H, G):
     """Group index of each head: contiguous blocks of H/G heads share B and C."""
     if G < 1 or H % G != 0:
@@ -69,13 +87,14 @@ def head_groups(H, G):
     return np.arange(H) // (H // G)
 
 
-def ssd_recurrence(x, dt, dt_bias, A, B, C, D=None, initial_state=None):
+def ssd_recurrence(x, dt, dt_bias, A, B, C, D=None, initial_state=None, z=None, dt_limit=None):
     """Sequential float64 evaluation of the SSD recurrence, one time step at a time.
 
+    z (Bt,L,H,P) or None: output gate, y <- y * silu(z).  dt_limit (lo, hi) or None: clamp of dt'.
     Returns (y (Bt,L,H,P), final_state (Bt,H,P,N)), both float64.
     """
     x, dt, dt_bias, A, B, C = map(_f64, (x, dt, dt_bias, A, B, C))
-    D = _f64(D)
+    D, z = _f64(D), _f64(z)
     Bt, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     g = head_groups(H, G)
@@ -85,7 +104,7 @@ def ssd_recurrence(x, dt, dt_bias, A, B, C, D=None, initial_state=None):
         h = _f64(initial_state).copy()
     y = np.zeros((Bt, L, H, P))
     for t in range(L):
-        d = softplus(dt[:, t, :] + dt_bias[None, :])          # (Bt, H)
+        d = _step_size(dt[:, t, :], dt_bias[None, :], dt_limit)  # (Bt, H)
         a = np.exp(d * A[None, :])                              # (Bt, H)
         Bt_h = B[:, t][:, g, :]                                 # (Bt, H, N)
         Ct_h = C[:, t][:, g, :]                                 # (Bt, H, N)
@@ -94,25 +113,28 @@ def ssd_recurrence(x, dt, dt_bias, A, B, C, D=None, initial_state=None):
         yt = (h * Ct_h[:, :, None, :]).sum(axis=-1)             # (Bt, H, P)
         if D is not None:
             yt = yt + D[None, :, :] * xt
+        if z is not None:
+            yt = yt * silu(z[:, t])
         y[:, t] = yt
     return y, h
 
 
-def ssd_step_ref(state, x, dt, dt_bias, A, B, C, D=None):
+def ssd_step_ref(state, x, dt, dt_bias, A, B, C, D=None, z=None, dt_limit=None):
     """One step of the recurrence on a given state (single-token decode).
 
-    state (Bt,H,P,N), x (Bt,H,P), dt (Bt,H), B and C (Bt,G,N).
+    state (Bt,H,P,N), x (Bt,H,P), dt (Bt,H), B and C (Bt,G,N), z (Bt,H,P) or None.
     Returns (y (Bt,H,P), new_state (Bt,H,P,N)), float64; y reads the updated state.
     """
     y, new_state = ssd_recurrence(
         _f64(x)[:, None], _f64(dt)[:, None], dt_bias, A,
         _f64(B)[:, None], _f64(C)[:, None], D, initial_state=state,
+        z=None if z is None else _f64(z)[:, None], dt_limit=dt_limit,
     )
     return y[:, 0], new_state
 
 
-def ssd_quadratic(x, dt, dt_bias, A, B, C, D=None):
-    """Brute-force materialised form y = (L o C B^T) X + D x, zero initial state.
+def ssd_quadratic(x, dt, dt_bias, A, B, C, D=None, z=None, dt_limit=None):
+    """Brute-force materialised form y = ((L o C B^T) X + D x) * silu(z), zero initial state.
 
     For every (b, h) it builds the L x L matrix
         M[t, s] = (C_t . B_s) * exp(sum_{k=s+1..t} d_k A) * d_s   for s <= t, else 0
@@ -122,14 +144,14 @@ def ssd_quadratic(x, dt, dt_bias, A, B, C, D=None):
     Small inputs only: O(L^2 (N + P + L)) per head.
     """
     x, dt, dt_bias, A, B, C = map(_f64, (x, dt, dt_bias, A, B, C))
-    D = _f64(D)
+    D, z = _f64(D), _f64(z)
     Bt, L, H, P = x.shape
     G = B.shape[2]
     g = head_groups(H, G)
     y = np.zeros((Bt, L, H, P))
     for b in range(Bt):
         for hh in range(H):
-            d = softplus(dt[b, :, hh] + dt_bias[hh])           # (L,)
+            d = _step_size(dt[b, :, hh], dt_bias[hh], dt_limit)    # (L,)
             dA = d * A[hh]
             M = np.zeros((L, L))
             for t in range(L):
@@ -139,4 +161,6 @@ def ssd_quadratic(x, dt, dt_bias, A, B, C, D=None):
             y[b, :, hh, :] = M @ x[b, :, hh, :]
             if D is not None:
                 y[b, :, hh, :] += D[hh][None, :] * x[b, :, hh, :]
+            if z is not None:
+                y[b, :, hh, :] *= silu(z[b, :, hh, :])
     return y

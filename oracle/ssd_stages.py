@@ -11,14 +11,14 @@ workspace (dt', segment cumsum, chunk states) stage by stage.
 
 Conventions (Q = chunk size, nc = ceil(L / Q); positions past L in the last
 chunk are padding):
-  dtp  (Bt, H, nc, Q)   softplus(dt + dt_bias); 0 on padding
+  dtp  (Bt, H, nc, Q)   softplus(dt + dt_bias), clamped if asked; 0 on padding
   dAcs (Bt, H, nc, Q)   inclusive in-chunk cumsum of dtp * A (flat on padding)
   S    (Bt, nc, H, P, N) state contributed by chunk c alone, decayed to its end
   prev (Bt, nc, H, P, N) state entering chunk c;  final (Bt, H, P, N)
 """
 import numpy as np
 
-from .ssd_oracle import _f64, head_groups, softplus
+from .ssd_oracle import _f64, _step_size, head_groups, silu
 
 __all__ = ["chunk_cumsum", "chunk_state", "state_passing", "chunk_scan", "ssd_chunked"]
 
@@ -27,7 +27,7 @@ def _nchunks(L, Q):
     return (L + Q - 1) // Q
 
 
-def chunk_cumsum(dt, dt_bias, A, Q):
+def chunk_cumsum(dt, dt_bias, A, Q, dt_limit=None):
     dt, dt_bias, A = map(_f64, (dt, dt_bias, A))
     Bt, L, H = dt.shape
     nc = _nchunks(L, Q)
@@ -35,7 +35,7 @@ def chunk_cumsum(dt, dt_bias, A, Q):
     dAcs = np.zeros((Bt, H, nc, Q))
     for c in range(nc):
         n = min(Q, L - c * Q)
-        d = softplus(dt[:, c * Q:c * Q + n, :] + dt_bias[None, None, :])   # (Bt, n, H)
+        d = _step_size(dt[:, c * Q:c * Q + n, :], dt_bias[None, None, :], dt_limit)   # (Bt, n, H)
         dtp[:, :, c, :n] = d.transpose(0, 2, 1)
         run = np.zeros((Bt, H))
         for i in range(Q):
@@ -71,9 +71,9 @@ def state_passing(S, dAcs, initial_state=None):
     return prev, h
 
 
-def chunk_scan(x, B, C, dtp, dAcs, prev, D=None):
+def chunk_scan(x, B, C, dtp, dAcs, prev, D=None, z=None):
     x, B, C = map(_f64, (x, B, C))
-    D = _f64(D)
+    D, z = _f64(D), _f64(z)
     Bt, L, H, P = x.shape
     G = B.shape[2]
     nc, Q = dtp.shape[2], dtp.shape[3]
@@ -94,14 +94,16 @@ def chunk_scan(x, B, C, dtp, dAcs, prev, D=None):
                 acc = acc + w[:, :, None] * x[:, s]
             if D is not None:
                 acc = acc + D[None] * x[:, t]
+            if z is not None:
+                acc = acc * silu(z[:, t])
             y[:, t] = acc
     return y
 
 
-def ssd_chunked(x, dt, dt_bias, A, B, C, D=None, chunk_size=64, initial_state=None):
+def ssd_chunked(x, dt, dt_bias, A, B, C, D=None, chunk_size=64, initial_state=None, z=None, dt_limit=None):
     """All four stages in order; returns (y, final_state, intermediates dict)."""
-    dtp, dAcs = chunk_cumsum(dt, dt_bias, A, chunk_size)
+    dtp, dAcs = chunk_cumsum(dt, dt_bias, A, chunk_size, dt_limit)
     S = chunk_state(x, B, dtp, dAcs)
     prev, final = state_passing(S, dAcs, initial_state)
-    y = chunk_scan(x, B, C, dtp, dAcs, prev, D)
+    y = chunk_scan(x, B, C, dtp, dAcs, prev, D, z)
     return y, final, {"dtp": dtp, "dAcs": dAcs, "S": S, "prev": prev}

@@ -310,3 +310,65 @@ def test_staged_chunk_size_invariance_at_workload_scale():
     for Q in (64, 128, 256):
         ys, fs, _ = ssd_stages.ssd_chunked(**inp, chunk_size=Q)
         assert _rel(ys, y) < 1e-12 and _rel(fs, fin) < 1e-12
+
+
+# --------------------------------------------------------------------------- gate and dt clamp
+
+def test_silu_against_library_sigmoid():
+    import scipy.special
+    from oracle import silu
+    v = np.linspace(-40.0, 40.0, 161)
+    np.testing.assert_allclose(silu(v), v * scipy.special.expit(v), rtol=1e-14, atol=1e-300)
+    assert silu(np.float64(0.0)) == 0.0
+
+
+def test_gate_multiplies_the_full_output():
+    """y_gated = (scan + D x) * silu(z): z = 0 silences every output, and the gated output is the
+    ungated one times v * sigmoid(v) (library sigmoid), in all four oracle forms."""
+    import scipy.special
+    inp = _np_inputs(seed=31, batch=2, seqlen=21, nheads=4, headdim=3, dstate=2, ngroups=2)
+    z = np.random.default_rng(5).standard_normal(inp["x"].shape) * 3.0
+    y0, f0 = ssd_recurrence(**inp)
+    yz, fz = ssd_recurrence(**inp, z=z)
+    np.testing.assert_allclose(yz, y0 * z * scipy.special.expit(z), rtol=1e-13, atol=1e-15)
+    assert np.array_equal(f0, fz)                          # the gate never touches the state
+    yq = ssd_quadratic(**inp, z=z)
+    assert _rel(yq, yz) < 1e-12
+    ys, fs, _ = ssd_stages.ssd_chunked(**inp, z=z, chunk_size=8)
+    assert _rel(ys, yz) < 1e-12 and _rel(fs, fz) < 1e-12
+    y_off, _ = ssd_recurrence(**inp, z=np.zeros_like(z))
+    assert np.all(y_off == 0.0)
+    st = np.zeros_like(f0)
+    for t in range(21):
+        yt, st = ssd_step_ref(st, inp["x"][:, t], inp["dt"][:, t], inp["dt_bias"], inp["A"], inp["B"][:, t],
+                              inp["C"][:, t], inp["D"], z=z[:, t])
+        assert _rel(yt, yz[:, t]) < 1e-13
+
+
+def test_dt_clamp_saturated_is_constant_step_filter():
+    """With every softplus(dt + bias) above dt_max the step is dt_max everywhere: the scalar
+    channel becomes the IIR filter with d = dt_max (library lfilter); below dt_min, d = dt_min."""
+    L = 50
+    xs = np.random.default_rng(8).standard_normal(L)
+    A = -3.0
+    for dt_raw, (lo, hi), d in ((5.0, (1e-3, 0.1), 0.1), (-30.0, (0.02, 0.1), 0.02)):
+        a = math.exp(d * A)
+        ref = scipy.signal.lfilter([d], [1.0, -a], xs)
+        y, _ = ssd_recurrence(xs.reshape(1, L, 1, 1), np.full((1, L, 1), dt_raw), np.zeros(1), np.array([A]),
+                              np.ones((1, L, 1, 1)), np.ones((1, L, 1, 1)), None, dt_limit=(lo, hi))
+        assert _rel(y[0, :, 0, 0], ref) < 1e-12
+
+
+def test_dt_clamp_inactive_and_staged():
+    inp = _np_inputs(seed=32, batch=1, seqlen=40, nheads=3, headdim=2, dstate=3, ngroups=1)
+    y0, f0 = ssd_recurrence(**inp)
+    yw, fw = ssd_recurrence(**inp, dt_limit=(0.0, 1e9))         # wide limits change nothing
+    assert np.array_equal(y0, yw) and np.array_equal(f0, fw)
+    yc, fc = ssd_recurrence(**inp, dt_limit=(1e-2, 5e-2))
+    assert _rel(yc, y0) > 1e-3                                   # a binding clamp does change results
+    ys, fs, mid = ssd_stages.ssd_chunked(**inp, chunk_size=16, dt_limit=(1e-2, 5e-2))
+    assert _rel(ys, yc) < 1e-12 and _rel(fs, fc) < 1e-12
+    valid = mid["dtp"][:, :, :, :][mid["dtp"] > 0]
+    assert valid.min() >= 1e-2 and valid.max() <= 5e-2
+    yq = ssd_quadratic(**inp, dt_limit=(1e-2, 5e-2))
+    assert _rel(yq, yc) < 1e-12
