@@ -3,15 +3,18 @@
  *
  * The operation.  For every batch row b and head h (group g = h / (H / G)):
  *     dt'_t = softplus(dt[b,t,h] + dt_bias[h])          softplus(v) = log(1 + e^v)
+ *             (then clamped to [dt_min, dt_max] when the dims ask for it)
  *     h_t   = exp(dt'_t * A[h]) * h_{t-1} + dt'_t * x[b,t,h,:]^T B[b,t,g,:]     (P x N state)
- *     y_t   = h_t C[b,t,g,:]^T + D[h,:] * x[b,t,h,:]
- * with h_{-1} = initial_state (zeros when NULL) and final_state = h_{L-1}.
+ *     y_t   = (h_t C[b,t,g,:]^T + D[h,:] * x[b,t,h,:]) * silu(z[b,t,h,:])    (gate only if z given)
+ * with h_{-1} = initial_state (zeros when NULL) and final_state = h_{L-1}; silu(v) = v / (1 + e^-v).
  * Sources: "Agent 228: MAMBA-2 Reference Implementations Comparison", section 2.2 (SSD as a
  * 1-semiseparable masked form, A scalar per head) and section 3.2 (softplus(dt + dt_bias),
  * decay exp(A dt'), input term B dt', chunked evaluation); "Agent 228: MAMBA-2 Implementation
  * Gaps", Gap 1 (diagonal blocks within a chunk plus the carried inter-chunk state), Gap 3
  * (softplus), Gap 4 (D skip term); "MAMBA2 Inference Optimization Report", Step 4 (the last
- * state is kept for stateful inference).
+ * state is kept for stateful inference); the optional gate is the output gating of the
+ * reference-comparison page (section 3.1 forward pass, section 6.1) and the optional clamp its
+ * dt limits (section 5.2; Implementation Gaps, Gap 3).
  *
  * Conventions shared by every entry point:
  *  - All tensor pointers are caller-owned DEVICE pointers on the current HIP device, row-major
@@ -51,7 +54,9 @@ typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype_t;
 
 /* Problem sizes.  batch >= 0, seqlen >= 0 (ssd_step ignores it), nheads >= 1,
  * ngroups >= 1 with nheads % ngroups == 0.  Supported (else SSD_ERR_UNSUPPORTED):
- * headdim in {16, 32, 64}; dstate in {16, 32, 64} for SSD_F32 and {32, 64, 128} for SSD_BF16. */
+ * headdim in {16, 32, 64}; dstate in {16, 32, 64} for SSD_F32 and {32, 64, 128} for SSD_BF16.
+ * dt_max > 0 clamps dt' = softplus(dt + dt_bias) to [dt_min, dt_max] (requires
+ * 0 <= dt_min <= dt_max, else SSD_ERR_INVALID_ARG); dt_max == 0 means no clamp. */
 typedef struct {
   int64_t batch;     /* B */
   int64_t seqlen;    /* L */
@@ -60,6 +65,8 @@ typedef struct {
   int64_t dstate;    /* N */
   int64_t ngroups;   /* G */
   int32_t dtype;     /* ssd_dtype_t */
+  float dt_min;      /* lower clamp of dt' (used when dt_max > 0) */
+  float dt_max;      /* upper clamp of dt'; 0 = no clamp */
 } ssd_dims_t;
 
 /* Bytes of device workspace ssd_fwd needs for these sizes and chunk size; 0 when the
@@ -82,6 +89,7 @@ size_t ssd_fwd_workspace_size(const ssd_dims_t* dims, int chunk_size);
  *   dt_bias, A    (H)           fp32        A is used as given (pass negative values)
  *   B, C          (B, L, G, N)  dtype
  *   D             (H, P)        fp32        NULL means no skip term
+ *   z             (B, L, H, P)  dtype       gate; NULL means no gate
  *   chunk_size    64, 128 or 256; the result does not depend on it beyond rounding
  *   initial_state (B, H, P, N)  fp32        NULL means zeros
  *   y             (B, L, H, P)  dtype       output (may not alias an input)
@@ -90,7 +98,7 @@ size_t ssd_fwd_workspace_size(const ssd_dims_t* dims, int chunk_size);
  * batch == 0 is a no-op.  seqlen == 0 writes only final_state (= initial_state or zeros). */
 ssd_status_t ssd_fwd(const ssd_dims_t* dims,
                      const void* x, const void* dt, const float* dt_bias, const float* A,
-                     const void* B, const void* C, const float* D, int chunk_size,
+                     const void* B, const void* C, const float* D, const void* z, int chunk_size,
                      const float* initial_state, void* y, float* final_state,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
@@ -103,7 +111,7 @@ ssd_status_t ssd_fwd(const ssd_dims_t* dims,
  * stage_events behaves exactly like ssd_fwd (which may be captured). */
 ssd_status_t ssd_fwd_timed(const ssd_dims_t* dims,
                            const void* x, const void* dt, const float* dt_bias, const float* A,
-                           const void* B, const void* C, const float* D, int chunk_size,
+                           const void* B, const void* C, const float* D, const void* z, int chunk_size,
                            const float* initial_state, void* y, float* final_state,
                            void* workspace, size_t workspace_bytes, hipStream_t stream,
                            hipEvent_t* stage_events);
@@ -112,12 +120,12 @@ ssd_status_t ssd_fwd_timed(const ssd_dims_t* dims,
  * the carried hidden state; same discretisation as ssd_fwd).  dims->seqlen is ignored.
  *   state  (B, H, P, N) fp32    read and overwritten in place with h_t
  *   x      (B, H, P)    dtype   dt (B, H) dtype   dt_bias, A (H) fp32
- *   B, C   (B, G, N)    dtype   D (H, P) fp32 or NULL
+ *   B, C   (B, G, N)    dtype   D (H, P) fp32 or NULL   z (B, H, P) dtype or NULL (gate)
  *   y      (B, H, P)    dtype   output, computed from the UPDATED state
  * One kernel; no workspace.  batch == 0 is a no-op. */
 ssd_status_t ssd_step(const ssd_dims_t* dims, float* state,
                       const void* x, const void* dt, const float* dt_bias, const float* A,
-                      const void* B, const void* C, const float* D,
+                      const void* B, const void* C, const float* D, const void* z,
                       void* y, hipStream_t stream);
 
 /* Static English description of a status code; never NULL. */

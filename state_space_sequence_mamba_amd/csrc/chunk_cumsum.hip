@@ -8,7 +8,9 @@
 //
 // One wavefront per (b, c, h); four heads per 256-thread workgroup, grid (ceil(H/4), nc, B).
 // Every lane issues its Q/64 loads before any arithmetic, so one memory latency is exposed.
-// Positions past the end of the sequence get dt' = 0, so the cumsum stays flat there.
+// dt' is optionally clamped to [lo, hi] (the dt limits of section 5.2 of the reference-
+// comparison page).  Positions past the end of the sequence get dt' = 0, so the cumsum
+// stays flat there.
 #include "ssd_common.h"
 #include "ssd_launch.h"
 
@@ -20,7 +22,8 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(const T* __restrict__
                                                            const float* __restrict__ A,
                                                            float* __restrict__ dtp,
                                                            float* __restrict__ dAcs,
-                                                           int L, int H, int nc, int Q) {
+                                                           int L, int H, int nc, int Q, int clamp,
+                                                           float lo, float hi) {
   const int lane = threadIdx.x & 63;
   const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int c = blockIdx.y, b = blockIdx.z;
@@ -42,7 +45,9 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(const T* __restrict__
   float run = 0.f;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const float v = (k < epl && i0 + k < len) ? softplus(raw[k] + bias) : 0.f;
+    float v = softplus(raw[k] + bias);
+    if (clamp) v = fminf(fmaxf(v, lo), hi);
+    v = (k < epl && i0 + k < len) ? v : 0.f;
     d[k] = v;
     run += v * a;
     cs[k] = run;
@@ -70,10 +75,10 @@ hipError_t launch_chunk_cumsum(const FwdArgs& a, hipStream_t s) {
   dim3 grid((a.H + 3) / 4, a.nc, a.B);
   if (a.dtype == DT_F32) {
     chunk_cumsum_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(a.dt), a.dt_bias, a.A,
-                                                    a.dtp, a.dAcs, a.L, a.H, a.nc, a.Q);
+                                                    a.dtp, a.dAcs, a.L, a.H, a.nc, a.Q, a.clamp, a.dt_lo, a.dt_hi);
   } else {
     chunk_cumsum_kernel<__bf16><<<grid, 256, 0, s>>>(static_cast<const __bf16*>(a.dt), a.dt_bias, a.A,
-                                                     a.dtp, a.dAcs, a.L, a.H, a.nc, a.Q);
+                                                     a.dtp, a.dAcs, a.L, a.H, a.nc, a.Q, a.clamp, a.dt_lo, a.dt_hi);
   }
   return hipGetLastError();
 }

@@ -2,12 +2,13 @@
 //   y[i,p] = sum_{j<=i} CB[i,j] exp(dAcs[i] - dAcs[j]) dt'_j x[j,p]        (diagonal block)
 //          + exp(dAcs[i]) sum_n C[i,n] Hprev[p,n]                            (carried state)
 //          + D[p] x[i,p]                                                     (skip term)
-// with CB[i,j] = sum_n C[i,n] B[j,n] and Hprev the state entering the chunk.
+// times silu(z[i,p]) when a gate is given, with CB[i,j] = sum_n C[i,n] B[j,n] and Hprev the
+// state entering the chunk.
 // Sources: "Agent 228: MAMBA-2 Reference Implementations Comparison", section 2.2 (the SSD
 // output as a 1-semiseparable causal mask applied to attention-like C B^T scores) and
 // section 3.2 (chunked evaluation: diagonal blocks plus the inter-chunk carry); "Agent 228:
 // MAMBA-2 Implementation Gaps", Gap 1 (off-diagonal block from the previous state) and
-// Gap 4 (D skip).
+// Gap 4 (D skip); the gate is the output gating of the reference-comparison page, 3.1.
 //
 // Per 16-row strip and 16-column causal sub-tile, CB^T (16x16) is contracted on MFMA and
 // consumed at once by every head of the workgroup's head block: each head applies its decay
@@ -291,6 +292,31 @@ __device__ __forceinline__ void diag_tile(f32x4 (&acc)[HB][TPof<P>::v], const ty
   }
 }
 
+// Output gate y * silu(z) on one strip's registers (rows 16 strip + 4 qd + e, column 16 pt + r).
+// All z loads are issued before use; rows past the sequence read a clamped address.
+template <typename T, int P, int HB>
+__device__ __forceinline__ void apply_gate(f32x4 (&acc)[HB][TPof<P>::v], const T* z, size_t row0, size_t x_tok,
+                                           int h0, int strip, int len, int r, int qd) {
+  constexpr int TP = P / 16;
+  float zv[HB][TP][4];
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh)
+#pragma unroll
+    for (int pt = 0; pt < TP; ++pt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * strip + 4 * qd + e;
+        const size_t o = (row0 + (i < len ? i : 0)) * x_tok + (size_t)(h0 + hh) * P + pt * 16 + r;
+        zv[hh][pt][e] = to_f32(z[o]);
+      }
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh)
+#pragma unroll
+    for (int pt = 0; pt < TP; ++pt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[hh][pt][e] *= zv[hh][pt][e] / (1.f + expf(-zv[hh][pt][e]));
+}
+
 // Write one strip's (16 x P) results of head hh into the y staging rows.
 template <typename T, int P, int HB, int YP>
 __device__ __forceinline__ void put_strip(T* s_y, const f32x4 (&acc)[HB][TPof<P>::v], int hh, int lstrip, int r,
@@ -334,6 +360,7 @@ __global__ __launch_bounds__(256, 2) void chunk_scan_rows_kernel(const T* __rest
                                                                  const float* __restrict__ dAcs,
                                                                  const float* __restrict__ states,
                                                                  const float* __restrict__ Dw,
+                                                                 const T* __restrict__ Z,
                                                                  T* __restrict__ y,
                                                                  int L, int H, int G, int nc, int Q, int B) {
   constexpr int NTHR = 256;
@@ -416,6 +443,7 @@ __global__ __launch_bounds__(256, 2) void chunk_scan_rows_kernel(const T* __rest
     __syncthreads();
     if (strip_ok) diag_tile<T, P, N, HB, SL::BP, SL::XP>(acc, cf, dco, s_b, s_xu, s_da, s_dt, s, J, r, qd);
   }
+  if (Z && strip_ok) apply_gate<T, P, HB>(acc, Z, (size_t)b * L + t0, x_tok, h0, s, len, r, qd);
   const int rows = min(kKT, len - rb * kKT);
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) {
@@ -435,6 +463,7 @@ __global__ __launch_bounds__(512) void chunk_scan_chunk_kernel(const T* __restri
                                                                const float* __restrict__ dAcs,
                                                                const float* __restrict__ states,
                                                                const float* __restrict__ Dw,
+                                                               const T* __restrict__ Z,
                                                                T* __restrict__ y,
                                                                int L, int H, int G, int nc, int Q, uint32_t nblocks) {
   constexpr int NTHR = 512;
@@ -519,6 +548,11 @@ __global__ __launch_bounds__(512) void chunk_scan_chunk_kernel(const T* __restri
       if (ok[st] && 4 * J <= strip[st])
         diag_tile<T, P, N, HB, SL::BP, SL::XP>(acc[st], cf[st], dco, s_b, s_xu, s_da, s_dt, strip[st], J, r, qd);
   }
+  if (Z) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+      if (ok[st]) apply_gate<T, P, HB>(acc[st], Z, (size_t)b * L + t0, x_tok, h0, strip[st], len, r, qd);
+  }
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) {
     __syncthreads();
@@ -536,12 +570,12 @@ static hipError_t launch_scan_hb(const FwdArgs& a, hipStream_t s) {
     const uint32_t nblocks = (uint32_t)a.B * a.nc * (a.H / HB);
     chunk_scan_chunk_kernel<T, P, N, HB><<<nblocks, 512, 0, s>>>(
         static_cast<const T*>(a.x), static_cast<const T*>(a.Bm), static_cast<const T*>(a.Cm), a.dtp, a.dAcs,
-        a.states, a.D, static_cast<T*>(a.y), a.L, a.H, a.G, a.nc, a.Q, nblocks);
+        a.states, a.D, static_cast<const T*>(a.z), static_cast<T*>(a.y), a.L, a.H, a.G, a.nc, a.Q, nblocks);
   } else {
     const uint32_t nblocks = (uint32_t)a.B * a.nc * (a.H / HB) * (a.Q / kKT);
     chunk_scan_rows_kernel<T, P, N, HB><<<nblocks, 256, 0, s>>>(
         static_cast<const T*>(a.x), static_cast<const T*>(a.Bm), static_cast<const T*>(a.Cm), a.dtp, a.dAcs,
-        a.states, a.D, static_cast<T*>(a.y), a.L, a.H, a.G, a.nc, a.Q, a.B);
+        a.states, a.D, static_cast<const T*>(a.z), static_cast<T*>(a.y), a.L, a.H, a.G, a.nc, a.Q, a.B);
   }
   return hipGetLastError();
 }

@@ -25,6 +25,9 @@ ssd_status_t check_dims(const ssd_dims_t* d, bool need_seqlen) {
   if (d->batch < 0 || d->nheads < 1 || d->headdim < 1 || d->dstate < 1 || d->ngroups < 1) return SSD_ERR_INVALID_ARG;
   if (need_seqlen && d->seqlen < 0) return SSD_ERR_INVALID_ARG;
   if (d->nheads % d->ngroups != 0) return SSD_ERR_INVALID_ARG;
+  // dt clamp: off when both bounds are 0, else 0 <= dt_min <= dt_max with dt_max > 0 (NaN fails)
+  if (!(d->dt_min >= 0.f) || !(d->dt_max >= d->dt_min)) return SSD_ERR_INVALID_ARG;
+  if (d->dt_max == 0.f && d->dt_min != 0.f) return SSD_ERR_INVALID_ARG;
   if (d->dtype != SSD_F32 && d->dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
   if (!ssd::shape_supported(d->dtype, (int)d->headdim, (int)d->dstate)) return SSD_ERR_UNSUPPORTED;
   // 32-bit index arithmetic bounds of the launchers (grid sizes, per-sequence offsets)
@@ -94,8 +97,8 @@ int pick_heads_per_block(int B, int nc, int H, int G, int Q, int variant) {
 }
 
 ssd_status_t fwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, const float* dt_bias,
-                      const float* A, const void* B, const void* C, const float* D, int chunk_size,
-                      const float* initial_state, void* y, float* final_state, void* workspace,
+                      const float* A, const void* B, const void* C, const float* D, const void* z,
+                      int chunk_size, const float* initial_state, void* y, float* final_state, void* workspace,
                       size_t workspace_bytes, hipStream_t stream, hipEvent_t* ev) {
   ssd_status_t st = check_dims(dims, true);
   if (st != SSD_OK) return st;
@@ -108,7 +111,8 @@ ssd_status_t fwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   if (has_seq) {
     if (!x || !dt || !dt_bias || !A || !B || !C || !y) return SSD_ERR_INVALID_ARG;
     if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16)) return SSD_ERR_INVALID_ARG;
-    if (!aligned(dt, eb) || !aligned(dt_bias, 4) || !aligned(A, 4) || (D && !aligned(D, 4)))
+    if (!aligned(dt, eb) || !aligned(dt_bias, 4) || !aligned(A, 4) || (D && !aligned(D, 4)) ||
+        (z && !aligned(z, eb)))
       return SSD_ERR_INVALID_ARG;
   }
   if ((initial_state && !aligned(initial_state, 16)) || (final_state && !aligned(final_state, 16)))
@@ -119,7 +123,8 @@ ssd_status_t fwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
     if (!aligned(workspace, 16)) return SSD_ERR_INVALID_ARG;
   }
   // every pointer must be device memory of the current device
-  const void* ptrs[] = {x, dt, dt_bias, A, B, C, D, initial_state, y, final_state, has_seq ? workspace : nullptr};
+  const void* ptrs[] = {x,  dt, dt_bias, A, B, C, D, has_seq ? z : nullptr, initial_state, y, final_state,
+                        has_seq ? workspace : nullptr};
   for (const void* p : ptrs)
     if (p && !device_ptr_ok(p)) return SSD_ERR_DEVICE_PTR;
 
@@ -147,6 +152,10 @@ ssd_status_t fwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   a.Bm = B;
   a.Cm = C;
   a.D = D;
+  a.z = z;
+  a.clamp = dims->dt_max > 0.f;
+  a.dt_lo = dims->dt_min;
+  a.dt_hi = dims->dt_max;
   a.init = initial_state;
   a.y = y;
   a.final_state = final_state;
@@ -192,31 +201,34 @@ size_t ssd_fwd_workspace_size(const ssd_dims_t* dims, int chunk_size) {
 }
 
 ssd_status_t ssd_fwd(const ssd_dims_t* dims, const void* x, const void* dt, const float* dt_bias, const float* A,
-                     const void* B, const void* C, const float* D, int chunk_size, const float* initial_state,
-                     void* y, float* final_state, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return fwd_impl(dims, x, dt, dt_bias, A, B, C, D, chunk_size, initial_state, y, final_state, workspace,
+                     const void* B, const void* C, const float* D, const void* z, int chunk_size,
+                     const float* initial_state, void* y, float* final_state, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  return fwd_impl(dims, x, dt, dt_bias, A, B, C, D, z, chunk_size, initial_state, y, final_state, workspace,
                   workspace_bytes, stream, nullptr);
 }
 
 ssd_status_t ssd_fwd_timed(const ssd_dims_t* dims, const void* x, const void* dt, const float* dt_bias,
-                           const float* A, const void* B, const void* C, const float* D, int chunk_size,
-                           const float* initial_state, void* y, float* final_state, void* workspace,
-                           size_t workspace_bytes, hipStream_t stream, hipEvent_t* stage_events) {
-  return fwd_impl(dims, x, dt, dt_bias, A, B, C, D, chunk_size, initial_state, y, final_state, workspace,
+                           const float* A, const void* B, const void* C, const float* D, const void* z,
+                           int chunk_size, const float* initial_state, void* y, float* final_state,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream,
+                           hipEvent_t* stage_events) {
+  return fwd_impl(dims, x, dt, dt_bias, A, B, C, D, z, chunk_size, initial_state, y, final_state, workspace,
                   workspace_bytes, stream, stage_events);
 }
 
 ssd_status_t ssd_step(const ssd_dims_t* dims, float* state, const void* x, const void* dt, const float* dt_bias,
-                      const float* A, const void* B, const void* C, const float* D, void* y, hipStream_t stream) {
+                      const float* A, const void* B, const void* C, const float* D, const void* z, void* y,
+                      hipStream_t stream) {
   ssd_status_t st = check_dims(dims, false);
   if (st != SSD_OK) return st;
   if (dims->batch == 0) return SSD_OK;
   const size_t eb = elem_bytes(dims->dtype);
   if (!state || !x || !dt || !dt_bias || !A || !B || !C || !y) return SSD_ERR_INVALID_ARG;
   if (!aligned(state, 16) || !aligned(x, eb) || !aligned(dt, eb) || !aligned(B, eb) || !aligned(C, eb) ||
-      !aligned(y, eb) || !aligned(dt_bias, 4) || !aligned(A, 4) || (D && !aligned(D, 4)))
+      !aligned(y, eb) || !aligned(dt_bias, 4) || !aligned(A, 4) || (D && !aligned(D, 4)) || (z && !aligned(z, eb)))
     return SSD_ERR_INVALID_ARG;
-  const void* ptrs[] = {state, x, dt, dt_bias, A, B, C, D, y};
+  const void* ptrs[] = {state, x, dt, dt_bias, A, B, C, D, z, y};
   for (const void* p : ptrs)
     if (p && !device_ptr_ok(p)) return SSD_ERR_DEVICE_PTR;
   ssd::StepArgs a;
@@ -234,6 +246,10 @@ ssd_status_t ssd_step(const ssd_dims_t* dims, float* state, const void* x, const
   a.Bm = B;
   a.Cm = C;
   a.D = D;
+  a.z = z;
+  a.clamp = dims->dt_max > 0.f;
+  a.dt_lo = dims->dt_min;
+  a.dt_hi = dims->dt_max;
   a.y = y;
   return ssd::launch_ssd_step(a, stream) == hipSuccess ? SSD_OK : SSD_ERR_HIP;
 }

@@ -20,6 +20,9 @@ struct FwdArgs {
   const void* Bm;
   const void* Cm;
   const float* D;          // may be null
+  const void* z;           // gate, may be null
+  float dt_lo, dt_hi;      // clamp of dt' when clamp != 0
+  int clamp;
   const float* init;       // may be null
   void* y;
   float* final_state;      // may be null
@@ -41,6 +44,9 @@ struct StepArgs {
   const void* Bm;
   const void* Cm;
   const float* D;
+  const void* z;
+  float dt_lo, dt_hi;
+  int clamp;
   void* y;
 };
 

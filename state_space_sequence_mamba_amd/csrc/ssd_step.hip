@@ -3,7 +3,8 @@
 //     state[p,n] <- a * state[p,n] + dt' x[p] B[n],   y[p] = sum_n state[p,n] C[n] + D[p] x[p]
 // (the carried hidden state of stateful inference: "MAMBA2 Inference Optimization Report",
 // Step 4; the discretisation of section 3.2 of "Agent 228: MAMBA-2 Reference Implementations
-// Comparison"; D skip from Gap 4 of "Agent 228: MAMBA-2 Implementation Gaps").
+// Comparison", optionally clamped as in its section 5.2; D skip from Gap 4 of "Agent 228:
+// MAMBA-2 Implementation Gaps"; optional output gate y * silu(z) of its section 3.1).
 //
 // Bandwidth bound: the fp32 state is read and written once; everything else is small.
 // The state is streamed with non-temporal loads and stores: it is touched once per step and
@@ -26,7 +27,9 @@ __global__ __launch_bounds__(256) void ssd_step_kernel(float* __restrict__ state
                                                        const T* __restrict__ Bm,
                                                        const T* __restrict__ Cm,
                                                        const float* __restrict__ Dw,
-                                                       T* __restrict__ y, int H, int G) {
+                                                       const T* __restrict__ Z,
+                                                       T* __restrict__ y, int H, int G, int clamp,
+                                                       float lo, float hi) {
   constexpr int TPR = N / 4;           // lanes per state row
   constexpr int RPP = 256 / TPR;       // rows per pass
   constexpr int NPASS = (P + RPP - 1) / RPP;
@@ -37,7 +40,8 @@ __global__ __launch_bounds__(256) void ssd_step_kernel(float* __restrict__ state
   const int col = (tid % TPR) * 4;
   const int row0 = tid / TPR;
 
-  const float d = softplus(to_f32(dt[bh]) + dt_bias[h]);
+  float d = softplus(to_f32(dt[bh]) + dt_bias[h]);
+  if (clamp) d = fminf(fmaxf(d, lo), hi);
   const float a = expf(d * A[h]);
   float bv[4], cv[4];
   const T* Bp = Bm + ((size_t)b * G + g) * N + col;
@@ -73,7 +77,12 @@ __global__ __launch_bounds__(256) void ssd_step_kernel(float* __restrict__ state
       for (int off = TPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
       if ((tid % TPR) == 0) {
         const float dw = Dw ? Dw[(size_t)h * P + p] : 0.f;
-        y[(size_t)bh * P + p] = from_f32<T>(part + dw * xv[u]);
+        float out = part + dw * xv[u];
+        if (Z) {
+          const float zv = to_f32(Z[(size_t)bh * P + p]);
+          out *= zv / (1.f + expf(-zv));  // silu gate
+        }
+        y[(size_t)bh * P + p] = from_f32<T>(out);
       }
     }
   }
@@ -84,7 +93,8 @@ static hipError_t launch_step_impl(const StepArgs& a, hipStream_t s) {
   const unsigned nblocks = (unsigned)a.B * a.H;
   ssd_step_kernel<T, P, N><<<nblocks, 256, 0, s>>>(
       a.state, static_cast<const T*>(a.x), static_cast<const T*>(a.dt), a.dt_bias, a.A,
-      static_cast<const T*>(a.Bm), static_cast<const T*>(a.Cm), a.D, static_cast<T*>(a.y), a.H, a.G);
+      static_cast<const T*>(a.Bm), static_cast<const T*>(a.Cm), a.D, static_cast<const T*>(a.z),
+      static_cast<T*>(a.y), a.H, a.G, a.clamp, a.dt_lo, a.dt_hi);
   return hipGetLastError();
 }
 

@@ -103,6 +103,12 @@ def make_fwd_inputs(batch, seqlen, nheads, headdim, dstate, ngroups, dtype="f32"
     return {k: v.to(device) for k, v in out.items()}
 
 
+def make_gate(shape, dtype="f32", seed=0, device="cpu"):
+    """Output-gate input z ~ N(0, 1) of `shape`, from its own CPU generator."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    return torch.randn(*shape, generator=g).to(_torch_dtype(dtype)).to(device)
+
+
 def make_workload_inputs(w, device="cpu"):
     if w.entry != "fwd":
         raise ValueError("use make_step_inputs for decode workloads")

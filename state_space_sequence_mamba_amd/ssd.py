@@ -21,7 +21,7 @@ _DTYPES = {torch.float32: SSD_F32, torch.bfloat16: SSD_BF16}
 class ssd_dims_t(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
                 ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("dt_min", ctypes.c_float), ("dt_max", ctypes.c_float)]
 
 
 class SsdError(RuntimeError):
@@ -45,12 +45,12 @@ def load_library():
     dims_p = ctypes.POINTER(ssd_dims_t)
     lib.ssd_fwd_workspace_size.argtypes = [dims_p, i32]
     lib.ssd_fwd_workspace_size.restype = sz
-    fwd_args = [dims_p, vp, vp, f32p, f32p, vp, vp, f32p, i32, f32p, vp, f32p, vp, sz, vp]
+    fwd_args = [dims_p, vp, vp, f32p, f32p, vp, vp, f32p, vp, i32, f32p, vp, f32p, vp, sz, vp]
     lib.ssd_fwd.argtypes = fwd_args
     lib.ssd_fwd.restype = i32
     lib.ssd_fwd_timed.argtypes = fwd_args + [vp]
     lib.ssd_fwd_timed.restype = i32
-    lib.ssd_step.argtypes = [dims_p, f32p, vp, vp, f32p, f32p, vp, vp, f32p, vp, vp]
+    lib.ssd_step.argtypes = [dims_p, f32p, vp, vp, f32p, f32p, vp, vp, f32p, vp, vp, vp]
     lib.ssd_step.restype = i32
     lib.ssd_status_string.argtypes = [i32]
     lib.ssd_status_string.restype = ctypes.c_char_p
@@ -74,16 +74,18 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, dtype):
+def make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, dtype, dt_limit=None):
+    """dt_limit = (dt_min, dt_max) clamps dt' = softplus(dt + dt_bias); None = no clamp."""
     code = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
-    return ssd_dims_t(batch, seqlen, nheads, headdim, dstate, ngroups, code)
+    lo, hi = (0.0, 0.0) if dt_limit is None else (float(dt_limit[0]), float(dt_limit[1]))
+    return ssd_dims_t(batch, seqlen, nheads, headdim, dstate, ngroups, code, lo, hi)
 
 
 def ssd_fwd_workspace_size(dims, chunk_size):
     return int(load_library().ssd_fwd_workspace_size(ctypes.byref(dims), int(chunk_size)))
 
 
-def _check_fwd_shapes(x, dt, dt_bias, A, B, C, D, initial_state):
+def _check_fwd_shapes(x, dt, dt_bias, A, B, C, D, initial_state, z=None):
     if x.dim() != 4 or dt.dim() != 3 or B.dim() != 4 or C.dim() != 4:
         raise ValueError("x (B,L,H,P), dt (B,L,H), B and C (B,L,G,N) expected")
     b, L, H, P = x.shape
@@ -96,27 +98,31 @@ def _check_fwd_shapes(x, dt, dt_bias, A, B, C, D, initial_state):
         raise ValueError("D must have shape (H, P)")
     if initial_state is not None and tuple(initial_state.shape) != (b, H, P, N):
         raise ValueError("initial_state must have shape (B, H, P, N)")
-    for t in (dt, B, C):
-        if t.dtype != x.dtype:
-            raise ValueError("x, dt, B and C must share one dtype")
+    if z is not None and tuple(z.shape) != tuple(x.shape):
+        raise ValueError("z must have the shape of x")
+    for t in (dt, B, C, z):
+        if t is not None and t.dtype != x.dtype:
+            raise ValueError("x, dt, B, C and z must share one dtype")
     for t in (dt_bias, A, D, initial_state):
         if t is not None and t.dtype != torch.float32:
             raise ValueError("dt_bias, A, D and initial_state must be float32")
-    for t in (x, dt, dt_bias, A, B, C, D, initial_state):
+    for t in (x, dt, dt_bias, A, B, C, D, initial_state, z):
         if t is not None and not t.is_contiguous():
             raise ValueError("all tensors must be contiguous")
     return b, L, H, P, N, G
 
 
 def ssd_fwd(x, dt, dt_bias, A, B, C, D=None, chunk_size=256, initial_state=None, y=None,
-            final_state=None, return_final_state=True, workspace=None, stream=None, stage_events=None):
+            final_state=None, return_final_state=True, workspace=None, stream=None, stage_events=None,
+            z=None, dt_limit=None):
     """Chunked SSD forward.  Returns (y, final_state) (final_state is None if not requested).
 
+    `z` (shape of x) gates the output, y * silu(z); `dt_limit` = (dt_min, dt_max) clamps dt'.
     Output and workspace tensors are allocated with torch when not given.  `stage_events`
     (5 raw hipEvent_t handles as ints) selects the timed entry point.
     """
-    b, L, H, P, N, G = _check_fwd_shapes(x, dt, dt_bias, A, B, C, D, initial_state)
-    dims = make_dims(b, L, H, P, N, G, x.dtype)
+    b, L, H, P, N, G = _check_fwd_shapes(x, dt, dt_bias, A, B, C, D, initial_state, z)
+    dims = make_dims(b, L, H, P, N, G, x.dtype, dt_limit)
     lib = load_library()
     if y is None:
         y = torch.empty_like(x)
@@ -126,7 +132,7 @@ def ssd_fwd(x, dt, dt_bias, A, B, C, D=None, chunk_size=256, initial_state=None,
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
     args = [ctypes.byref(dims), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-            int(chunk_size), _ptr(initial_state), _ptr(y), _ptr(final_state), _ptr(workspace),
+            _ptr(z), int(chunk_size), _ptr(initial_state), _ptr(y), _ptr(final_state), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(stream)]
     if stage_events is None:
         st = lib.ssd_fwd(*args)
@@ -138,8 +144,11 @@ def ssd_fwd(x, dt, dt_bias, A, B, C, D=None, chunk_size=256, initial_state=None,
     return y, final_state
 
 
-def ssd_step(state, x, dt, dt_bias, A, B, C, D=None, y=None, stream=None):
-    """One decode step: updates `state` (B,H,P,N) fp32 in place and returns y (B,H,P)."""
+def ssd_step(state, x, dt, dt_bias, A, B, C, D=None, y=None, stream=None, z=None, dt_limit=None):
+    """One decode step: updates `state` (B,H,P,N) fp32 in place and returns y (B,H,P).
+
+    `z` (B,H,P) gates the output, y * silu(z); `dt_limit` = (dt_min, dt_max) clamps dt'.
+    """
     if state.dim() != 4 or x.dim() != 3 or dt.dim() != 2 or B.dim() != 3 or C.dim() != 3:
         raise ValueError("state (B,H,P,N), x (B,H,P), dt (B,H), B and C (B,G,N) expected")
     b, H, P, N = state.shape
@@ -147,16 +156,21 @@ def ssd_step(state, x, dt, dt_bias, A, B, C, D=None, y=None, stream=None):
     if tuple(x.shape) != (b, H, P) or tuple(dt.shape) != (b, H) or tuple(B.shape) != (b, G, N) \
             or tuple(C.shape) != (b, G, N):
         raise ValueError("inconsistent state / x / dt / B / C shapes")
+    if z is not None and tuple(z.shape) != (b, H, P):
+        raise ValueError("z must have the shape of x")
     if state.dtype != torch.float32:
         raise ValueError("state must be float32")
-    for t in (state, x, dt, dt_bias, A, B, C, D):
+    for t in (dt, B, C, z):
+        if t is not None and t.dtype != x.dtype:
+            raise ValueError("x, dt, B, C and z must share one dtype")
+    for t in (state, x, dt, dt_bias, A, B, C, D, z):
         if t is not None and not t.is_contiguous():
             raise ValueError("all tensors must be contiguous")
-    dims = make_dims(b, 1, H, P, N, G, x.dtype)
+    dims = make_dims(b, 1, H, P, N, G, x.dtype, dt_limit)
     if y is None:
         y = torch.empty_like(x)
     st = load_library().ssd_step(ctypes.byref(dims), _ptr(state), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A),
-                                 _ptr(B), _ptr(C), _ptr(D), _ptr(y), _stream(stream))
+                                 _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y), _stream(stream))
     if st != SSD_OK:
         raise SsdError(st, "ssd_step")
     return y

@@ -76,19 +76,20 @@ def test_workspace_size_layout(lib):
 @pytest.mark.parametrize("kw,q", [
     (dict(headdim=48), 64), (dict(dstate=128, dtype=0), 64), (dict(dstate=16, dtype=1), 64),
     (dict(dtype=5), 64), ({}, 32), ({}, 512), (dict(nheads=6, ngroups=4), 64), (dict(seqlen=-1), 64),
-    (dict(nheads=0), 64),
+    (dict(nheads=0), 64), (dict(dt_min=-0.1, dt_max=1.0), 64), (dict(dt_min=0.5, dt_max=0.1), 64),
+    (dict(dt_min=0.1, dt_max=0.0), 64), (dict(dt_min=0.0, dt_max=float("nan")), 64),
 ])
 def test_workspace_size_rejects(lib, kw, q):
     assert ssd.ssd_fwd_workspace_size(_dims(**kw), q) == 0
 
 
 def _fwd_status(lib, dims, chunk=64, ptr=0x100000, **over):
-    p = dict(x=ptr, dt=ptr, dt_bias=ptr, A=ptr, B=ptr, C=ptr, D=None, init=None, y=ptr, fin=None,
+    p = dict(x=ptr, dt=ptr, dt_bias=ptr, A=ptr, B=ptr, C=ptr, D=None, z=None, init=None, y=ptr, fin=None,
              ws=ptr, ws_bytes=1 << 30)
     p.update(over)
     vp = ctypes.c_void_p
     return lib.ssd_fwd(None if dims is None else ctypes.byref(dims), vp(p["x"]), vp(p["dt"]), vp(p["dt_bias"]),
-                       vp(p["A"]), vp(p["B"]), vp(p["C"]), vp(p["D"]), chunk, vp(p["init"]), vp(p["y"]),
+                       vp(p["A"]), vp(p["B"]), vp(p["C"]), vp(p["D"]), vp(p["z"]), chunk, vp(p["init"]), vp(p["y"]),
                        vp(p["fin"]), vp(p["ws"]), p["ws_bytes"], None)
 
 
@@ -104,17 +105,26 @@ def test_fwd_host_validation_returns_before_any_launch(lib):
     assert _fwd_status(lib, _dims(dtype=1, dstate=32), dt=0x100001) == ssd.SSD_ERR_INVALID_ARG
     assert _fwd_status(lib, _dims(), ws=None) == ssd.SSD_ERR_WORKSPACE
     assert _fwd_status(lib, _dims(), ws_bytes=100) == ssd.SSD_ERR_WORKSPACE
+    assert _fwd_status(lib, _dims(dtype=1, dstate=32), z=0x100001) == ssd.SSD_ERR_INVALID_ARG
+    assert _fwd_status(lib, _dims(dt_min=0.2, dt_max=0.1)) == ssd.SSD_ERR_INVALID_ARG
+    assert _fwd_status(lib, _dims(dt_min=-1.0, dt_max=0.1)) == ssd.SSD_ERR_INVALID_ARG
 
 
 def test_step_host_validation(lib):
     vp = ctypes.c_void_p
     p = vp(0x100000)
     d = _dims()
-    assert lib.ssd_step(None, p, p, p, p, p, p, p, None, p, None) == ssd.SSD_ERR_INVALID_ARG
-    assert lib.ssd_step(ctypes.byref(_dims(dstate=24)), p, p, p, p, p, p, p, None, p, None) == ssd.SSD_ERR_UNSUPPORTED
-    assert lib.ssd_step(ctypes.byref(d), None, p, p, p, p, p, p, None, p, None) == ssd.SSD_ERR_INVALID_ARG
-    assert lib.ssd_step(ctypes.byref(d), vp(0x100008), p, p, p, p, p, p, None, p, None) == ssd.SSD_ERR_INVALID_ARG
-    assert lib.ssd_step(ctypes.byref(_dims(batch=0)), p, p, p, p, p, p, p, None, p, None) == ssd.SSD_OK
+    assert lib.ssd_step(None, p, p, p, p, p, p, p, None, None, p, None) == ssd.SSD_ERR_INVALID_ARG
+    assert lib.ssd_step(ctypes.byref(_dims(dstate=24)), p, p, p, p, p, p, p, None, None, p,
+                        None) == ssd.SSD_ERR_UNSUPPORTED
+    assert lib.ssd_step(ctypes.byref(d), None, p, p, p, p, p, p, None, None, p, None) == ssd.SSD_ERR_INVALID_ARG
+    assert lib.ssd_step(ctypes.byref(d), vp(0x100008), p, p, p, p, p, p, None, None, p,
+                        None) == ssd.SSD_ERR_INVALID_ARG
+    assert lib.ssd_step(ctypes.byref(d), p, p, p, p, p, p, p, None, vp(0x100002), p,
+                        None) == ssd.SSD_ERR_INVALID_ARG                   # z misaligned for fp32
+    assert lib.ssd_step(ctypes.byref(_dims(dt_min=0.3, dt_max=0.2)), p, p, p, p, p, p, p, None, None, p,
+                        None) == ssd.SSD_ERR_INVALID_ARG
+    assert lib.ssd_step(ctypes.byref(_dims(batch=0)), p, p, p, p, p, p, p, None, None, p, None) == ssd.SSD_OK
 
 
 def test_binding_raises_without_library(monkeypatch, tmp_path):

@@ -1,0 +1,148 @@
+"""GPU parity of the optional output gate y * silu(z) and the dt clamp.
+
+Both against the float64 oracle (ssd_recurrence / ssd_step_ref with z and dt_limit), to the
+same bar as the ungated path: rel_err <= 1e-4 (fp32 inputs), <= 2e-2 (bf16 inputs).
+The clamp bounds are chosen inside the range of the drawn steps, so both ends bind.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from helpers import TOL, rel_err, to64
+from oracle import ssd_recurrence, ssd_step_ref
+from state_space_sequence_mamba_amd import inputs as I
+from state_space_sequence_mamba_amd import ssd
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+LIMIT = (0.004, 0.04)
+
+
+def _say(msg):
+    print(f"\n[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _oracle(inp, z=None, dt_limit=None, initial_state=None):
+    return ssd_recurrence(to64(inp["x"]), to64(inp["dt"]), to64(inp["dt_bias"]), to64(inp["A"]),
+                          to64(inp["B"]), to64(inp["C"]), None if inp.get("D") is None else to64(inp["D"]),
+                          initial_state=initial_state, z=None if z is None else to64(z), dt_limit=dt_limit)
+
+
+def _fwd(inp, Q, z=None, dt_limit=None, initial_state=None):
+    dev = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
+    y, fin = ssd.ssd_fwd(dev["x"], dev["dt"], dev["dt_bias"], dev["A"], dev["B"], dev["C"], dev.get("D"),
+                         chunk_size=Q, z=None if z is None else z.to(DEV), dt_limit=dt_limit,
+                         initial_state=None if initial_state is None else initial_state.to(DEV))
+    torch.cuda.synchronize()
+    return to64(y), to64(fin)
+
+
+def test_clamp_bounds_bind_on_these_inputs():
+    """Host-only sanity of the test inputs: some steps fall below and some above the clamp."""
+    inp = I.make_fwd_inputs(2, 300, 6, 32, 32, 2, "f32", seed=40)
+    d = np.logaddexp(0.0, to64(inp["dt"]) + to64(inp["dt_bias"])[None, None, :])
+    assert (d < LIMIT[0]).mean() > 0.02 and (d > LIMIT[1]).mean() > 0.02
+
+
+CASES = [("f32", 64, 64, 1), ("f32", 32, 16, 2), ("f32", 16, 32, 4), ("bf16", 64, 128, 1), ("bf16", 32, 64, 2)]
+
+
+@pytest.mark.parametrize("dtype,P,N,G", CASES)
+@pytest.mark.parametrize("gate,clamp", [(True, False), (False, True), (True, True)])
+@pytest.mark.parametrize("variant", [1, 2])
+def test_fwd_gate_and_clamp(dtype, P, N, G, gate, clamp, variant):
+    L, Q = 333, (64, 128, 256)[(P + N) % 3]
+    _say(f"fwd gate={gate} clamp={clamp} dtype={dtype} P={P} N={N} G={G} L={L} Q={Q} variant={variant}")
+    inp = I.make_fwd_inputs(2, L, 4, P, N, G, dtype, seed=41 + P + N, d_init="normal")
+    z = I.make_gate((2, L, 4, P), dtype, seed=42) if gate else None
+    lim = LIMIT if clamp else None
+    try:
+        ssd.tune_set(2, variant)
+        y, fin = _fwd(inp, Q, z, lim)
+    finally:
+        ssd.tune_set(2, 0)
+    yr, fr = _oracle(inp, z, lim)
+    assert np.all(np.isfinite(y)) and np.all(np.isfinite(fin))
+    assert rel_err(y, yr) <= TOL[dtype], f"y rel_err {rel_err(y, yr):.3e}"
+    assert rel_err(fin, fr) <= TOL[dtype], f"final rel_err {rel_err(fin, fr):.3e}"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gate_zero_gives_zero_output_and_leaves_state(dtype):
+    _say(f"z = 0 {dtype}")
+    N = 64 if dtype == "f32" else 128
+    inp = I.make_fwd_inputs(1, 200, 4, 64, N, 1, dtype, seed=43)
+    y0, f0 = _fwd(inp, 128, z=torch.zeros(1, 200, 4, 64, dtype=inp["x"].dtype))
+    y1, f1 = _fwd(inp, 128)
+    assert np.count_nonzero(y0) == 0
+    assert np.array_equal(f0, f1)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_then_decode_with_gate_and_clamp(dtype):
+    """fwd over a prompt with z and the clamp, then ssd_step from its final state, equals the
+    oracle recurrence over prompt + decoded tokens."""
+    _say(f"prefill -> decode gate+clamp {dtype}")
+    L, T = 290, 4
+    N = 32 if dtype == "f32" else 64
+    inp = I.make_fwd_inputs(2, L + T, 6, 32, N, 3, dtype, seed=44, d_init="normal")
+    z = I.make_gate((2, L + T, 6, 32), dtype, seed=45)
+    dev = {k: v.to(DEV) for k, v in inp.items()}
+    zd = z.to(DEV)
+    sl = lambda t, a, b: t[:, a:b].contiguous()  # noqa: E731
+    y1, f1 = ssd.ssd_fwd(sl(dev["x"], 0, L), sl(dev["dt"], 0, L), dev["dt_bias"], dev["A"], sl(dev["B"], 0, L),
+                         sl(dev["C"], 0, L), dev["D"], chunk_size=128, z=sl(zd, 0, L), dt_limit=LIMIT)
+    state = f1.clone()
+    ys = []
+    for t in range(L, L + T):
+        col = lambda v: v[:, t].contiguous()  # noqa: E731
+        ys.append(ssd.ssd_step(state, col(dev["x"]), col(dev["dt"]), dev["dt_bias"], dev["A"], col(dev["B"]),
+                               col(dev["C"]), dev["D"], z=col(zd), dt_limit=LIMIT))
+    torch.cuda.synchronize()
+    got = np.concatenate([to64(y1), np.stack([to64(v) for v in ys], axis=1)], axis=1)
+    yr, fr = _oracle(inp, z, LIMIT)
+    assert rel_err(got, yr) <= TOL[dtype]
+    assert rel_err(to64(state), fr) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,P,N", [("f32", 16, 16), ("f32", 64, 64), ("bf16", 64, 128), ("bf16", 32, 32)])
+def test_step_gate_and_clamp(dtype, P, N):
+    _say(f"step gate+clamp {dtype} P={P} N={N}")
+    Bt, H, G, steps = 5, 6, 2, 6
+    inp = I.make_step_inputs(Bt, H, P, N, G, steps, dtype, seed=46, d_init="normal")
+    z = I.make_gate((steps, Bt, H, P), dtype, seed=47)
+    dev = {k: v.to(DEV) for k, v in inp.items()}
+    zd = z.to(DEV)
+    state = dev["state0"].clone()
+    st = to64(inp["state0"])
+    for t in range(steps):
+        y = ssd.ssd_step(state, dev["x"][t], dev["dt"][t], dev["dt_bias"], dev["A"], dev["B"][t], dev["C"][t],
+                         dev["D"], z=zd[t], dt_limit=LIMIT)
+        yr, st = ssd_step_ref(st, to64(inp["x"][t]), to64(inp["dt"][t]), to64(inp["dt_bias"]), to64(inp["A"]),
+                              to64(inp["B"][t]), to64(inp["C"][t]), to64(inp["D"]), z=to64(z[t]), dt_limit=LIMIT)
+        assert rel_err(to64(y), yr) <= TOL[dtype], f"step {t}"
+    torch.cuda.synchronize()
+    assert rel_err(to64(state), st) <= TOL[dtype]
+
+
+def test_full_size_bf16_gated_sampled():
+    """The B8 L4096 H32 P64 N128 workload with a gate and the clamp, on sampled (b, h) slices."""
+    w = I.WORKLOAD_LIST[2]
+    _say(f"{w.name} gated+clamped")
+    inp = I.make_workload_inputs(w)
+    z = I.make_gate((w.batch, w.seqlen, w.nheads, w.headdim), w.dtype, seed=48)
+    y, fin = _fwd(inp, w.chunk, z, LIMIT)
+    assert np.all(np.isfinite(y)) and np.all(np.isfinite(fin))
+    H, G = w.nheads, w.ngroups
+    for b, h in [(0, 0), (w.batch - 1, H - 1), (3, 17)]:
+        g = h // (H // G)
+        sub = {k: inp[k][b:b + 1, :, h:h + 1] for k in ("x", "dt")}
+        sub.update({k: inp[k][b:b + 1, :, g:g + 1] for k in ("B", "C")})
+        sub.update(dt_bias=inp["dt_bias"][h:h + 1], A=inp["A"][h:h + 1], D=inp["D"][h:h + 1])
+        yr, fr = _oracle(sub, z[b:b + 1, :, h:h + 1], LIMIT)
+        assert rel_err(y[b, :, h], yr[0, :, 0]) <= TOL[w.dtype], (b, h)
+        assert rel_err(fin[b, h], fr[0, 0]) <= TOL[w.dtype], (b, h)
