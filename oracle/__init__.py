@@ -4,4 +4,4 @@ Only the tests, the smoke check and the benchmark's CPU-baseline leg may
 import anything from this package; the product path never does.
 """
 from .ssd_oracle import softplus, silu, head_groups, ssd_recurrence, ssd_step_ref, ssd_quadratic  # noqa: F401
-from . import ssd_stages  # noqa: F401
+from . import ssd_stages, conv1d  # noqa: F401
