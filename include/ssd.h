@@ -128,6 +128,35 @@ ssd_status_t ssd_step(const ssd_dims_t* dims, float* state,
                       const void* B, const void* C, const float* D, const void* z,
                       void* y, hipStream_t stream);
 
+/* Causal depthwise conv1d + SiLU that produces the scan's x, B and C ("Agent 228: MAMBA-2
+ * Implementation Gaps", Gap 2: one filter of width K = conv_width per channel, causal padding
+ * K - 1; SiLU after it as in section 3.1 of "Agent 228: MAMBA-2 Reference Implementations
+ * Comparison").  Over the Dc = H*P + 2*G*N channels of xbc = [x | B | C]:
+ *     u[t, c] = bias[c] + sum_{k<K} weight[c, k] * xbc[t - (K-1) + k, c],   out = u / (1 + e^-u)
+ * and out's channels are written to x, B and C.  Inputs before t = 0 come from conv_state_in.
+ *   xbc             (B, L, Dc)    dtype   input (16-byte aligned)
+ *   weight          (Dc, K)       fp32    weight[c, K-1] multiplies the current token
+ *   bias            (Dc)          fp32    NULL means no bias
+ *   conv_state_in   (B, K-1, Dc)  dtype   inputs at times -(K-1) .. -1, oldest first; NULL = zeros
+ *   conv_state_out  (B, K-1, Dc)  dtype   NULL = not wanted; receives the inputs at times
+ *                                         L-(K-1) .. L-1 (older ones from conv_state_in when
+ *                                         L < K-1).  Either conv_state_in itself (updated in
+ *                                         place) or disjoint from it
+ *   x (B, L, H, P), B and C (B, L, G, N)  dtype   outputs, 16-byte aligned, disjoint from the inputs
+ * dims->dt_min/dt_max are not used (must still be valid).  conv_width in 1..4 (else
+ * SSD_ERR_UNSUPPORTED).  batch == 0 is a no-op; seqlen == 0 writes only conv_state_out.
+ * One kernel. */
+ssd_status_t ssd_conv1d_silu(const ssd_dims_t* dims, int conv_width, const void* xbc,
+                             const float* weight, const float* bias, const void* conv_state_in,
+                             void* conv_state_out, void* x, void* B, void* C, hipStream_t stream);
+
+/* One decode token of ssd_conv1d_silu per sequence: xbc (B, Dc) dtype; conv_state
+ * (B, K-1, Dc) dtype is read and shifted in place (required when conv_width > 1); outputs
+ * x (B, H, P), B and C (B, G, N) dtype.  dims->seqlen is ignored.  One kernel. */
+ssd_status_t ssd_conv1d_silu_step(const ssd_dims_t* dims, int conv_width, void* conv_state,
+                                  const void* xbc, const float* weight, const float* bias,
+                                  void* x, void* B, void* C, hipStream_t stream);
+
 /* Static English description of a status code; never NULL. */
 const char* ssd_status_string(ssd_status_t status);
 

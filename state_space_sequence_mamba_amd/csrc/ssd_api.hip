@@ -181,6 +181,61 @@ ssd_status_t fwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   return SSD_OK;
 }
 
+// Both conv entry points.  `step`: one token per sequence, state updated in place.
+ssd_status_t conv_impl(const ssd_dims_t* dims, int K, const void* xbc, const float* weight, const float* bias,
+                       const void* state_in, void* state_out, void* x, void* B, void* C, hipStream_t stream,
+                       bool step) {
+  ssd_status_t st = check_dims(dims, !step);
+  if (st != SSD_OK) return st;
+  if (K < 1 || K > 4) return SSD_ERR_UNSUPPORTED;
+  if (dims->batch == 0) return SSD_OK;
+  const bool has_seq = step || dims->seqlen > 0;
+  const size_t eb = elem_bytes(dims->dtype);
+  const int64_t dx = dims->nheads * dims->headdim, dbc = dims->ngroups * dims->dstate;
+  const int64_t Dc = dx + 2 * dbc;
+  if (Dc > (int64_t)1 << 24) return SSD_ERR_UNSUPPORTED;
+  if (has_seq) {
+    if (!xbc || !weight || !x || !B || !C) return SSD_ERR_INVALID_ARG;
+    if (!aligned(xbc, 16) || !aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(weight, 4) ||
+        (bias && !aligned(bias, 4)))
+      return SSD_ERR_INVALID_ARG;
+  }
+  if (step && K > 1 && !state_out) return SSD_ERR_INVALID_ARG;       // decoding needs the state
+  if ((state_in && !aligned(state_in, 16)) || (state_out && !aligned(state_out, 16))) return SSD_ERR_INVALID_ARG;
+  // the incoming and outgoing states are either the same buffer or disjoint
+  if (K > 1 && state_in && state_out && state_in != state_out) {
+    const size_t bytes = (size_t)dims->batch * (K - 1) * Dc * eb;
+    const char* a = static_cast<const char*>(state_in);
+    const char* o = static_cast<const char*>(state_out);
+    if (a < o + bytes && o < a + bytes) return SSD_ERR_INVALID_ARG;
+  }
+  const void* ptrs[] = {has_seq ? xbc : nullptr, has_seq ? weight : nullptr, has_seq ? bias : nullptr,
+                        K > 1 ? state_in : nullptr, K > 1 ? state_out : nullptr,
+                        has_seq ? x : nullptr, has_seq ? B : nullptr, has_seq ? C : nullptr};
+  for (const void* p : ptrs)
+    if (p && !device_ptr_ok(p)) return SSD_ERR_DEVICE_PTR;
+  if (!has_seq && (K == 1 || !state_out)) return SSD_OK;              // no tokens and no state to write
+
+  ssd::ConvArgs a;
+  a.B = (int)dims->batch;
+  a.L = step ? 1 : (int)dims->seqlen;
+  a.Dc = (int)Dc;
+  a.dx = (int)dx;
+  a.dbc = (int)dbc;
+  a.K = K;
+  a.dtype = dims->dtype;
+  a.xbc = xbc;
+  a.w = weight;
+  a.bias = bias;
+  a.state_in = state_in;
+  a.state_out = state_out;
+  a.x = x;
+  a.Bo = B;
+  a.Co = C;
+  const hipError_t e = step ? ssd::launch_conv1d_silu_step(a, stream) : ssd::launch_conv1d_silu(a, stream);
+  return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
 }  // namespace
 
 namespace ssd {
@@ -252,6 +307,18 @@ ssd_status_t ssd_step(const ssd_dims_t* dims, float* state, const void* x, const
   a.dt_hi = dims->dt_max;
   a.y = y;
   return ssd::launch_ssd_step(a, stream) == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
+ssd_status_t ssd_conv1d_silu(const ssd_dims_t* dims, int conv_width, const void* xbc, const float* weight,
+                             const float* bias, const void* conv_state_in, void* conv_state_out, void* x, void* B,
+                             void* C, hipStream_t stream) {
+  return conv_impl(dims, conv_width, xbc, weight, bias, conv_state_in, conv_state_out, x, B, C, stream, false);
+}
+
+ssd_status_t ssd_conv1d_silu_step(const ssd_dims_t* dims, int conv_width, void* conv_state, const void* xbc,
+                                  const float* weight, const float* bias, void* x, void* B, void* C,
+                                  hipStream_t stream) {
+  return conv_impl(dims, conv_width, xbc, weight, bias, conv_state, conv_state, x, B, C, stream, true);
 }
 
 const char* ssd_status_string(ssd_status_t s) {

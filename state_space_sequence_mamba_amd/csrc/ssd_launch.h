@@ -50,6 +50,20 @@ struct StepArgs {
   void* y;
 };
 
+// Causal depthwise conv1d + SiLU over xBC = [x | B | C] channels (Dc = dx + 2 dbc).
+struct ConvArgs {
+  int B, L, Dc, dx, dbc, K;
+  int dtype;
+  const void* xbc;         // (B, L, Dc), or (B, Dc) for the decode step
+  const float* w;          // (Dc, K)
+  const float* bias;       // (Dc) or null
+  const void* state_in;    // (B, K-1, Dc) or null (zeros); the decode step updates it in place
+  void* state_out;         // (B, K-1, Dc) or null; may equal state_in
+  void* x;                 // (B, L, dx)
+  void* Bo;                // (B, L, dbc)
+  void* Co;                // (B, L, dbc)
+};
+
 // true when a kernel instantiation exists for (dtype, P, N)
 bool shape_supported(int dtype, int P, int N);
 
@@ -58,6 +72,8 @@ hipError_t launch_chunk_state(const FwdArgs& a, hipStream_t s);
 hipError_t launch_state_passing(const FwdArgs& a, hipStream_t s);
 hipError_t launch_chunk_scan(const FwdArgs& a, hipStream_t s);
 hipError_t launch_ssd_step(const StepArgs& a, hipStream_t s);
+hipError_t launch_conv1d_silu(const ConvArgs& a, hipStream_t s);
+hipError_t launch_conv1d_silu_step(const ConvArgs& a, hipStream_t s);
 
 }  // namespace ssd
 

@@ -109,6 +109,26 @@ def make_gate(shape, dtype="f32", seed=0, device="cpu"):
     return torch.randn(*shape, generator=g).to(_torch_dtype(dtype)).to(device)
 
 
+def make_conv_inputs(batch, seqlen, nheads, headdim, dstate, ngroups, width=4, dtype="f32", seed=0,
+                     with_state=False, device="cpu"):
+    """Inputs of one conv1d_silu call, drawn on the CPU and moved to `device`.
+
+    xbc (B, L, H*P + 2*G*N) ~ N(0, 1) in `dtype`; weight (Dc, K) and bias (Dc) fp32 ~
+    U(-1/sqrt(K), 1/sqrt(K)) (the default initialisation of a depthwise conv layer, fan-in K);
+    conv_state (B, K-1, Dc) ~ N(0, 1) in `dtype` when asked for, else None.
+    """
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    Dc = nheads * headdim + 2 * ngroups * dstate
+    td = _torch_dtype(dtype)
+    bound = 1.0 / math.sqrt(width)
+    xbc = torch.randn(batch, seqlen, Dc, generator=g).to(td)
+    weight = (2.0 * torch.rand(Dc, width, generator=g) - 1.0) * bound
+    bias = (2.0 * torch.rand(Dc, generator=g) - 1.0) * bound
+    state = torch.randn(batch, width - 1, Dc, generator=g).to(td) if with_state else None
+    out = dict(xbc=xbc, weight=weight.float(), bias=bias.float(), conv_state=state)
+    return {k: (None if v is None else v.to(device)) for k, v in out.items()}
+
+
 def make_workload_inputs(w, device="cpu"):
     if w.entry != "fwd":
         raise ValueError("use make_step_inputs for decode workloads")

@@ -52,6 +52,10 @@ def load_library():
     lib.ssd_fwd_timed.restype = i32
     lib.ssd_step.argtypes = [dims_p, f32p, vp, vp, f32p, f32p, vp, vp, f32p, vp, vp, vp]
     lib.ssd_step.restype = i32
+    lib.ssd_conv1d_silu.argtypes = [dims_p, i32, vp, f32p, f32p, vp, vp, vp, vp, vp, vp]
+    lib.ssd_conv1d_silu.restype = i32
+    lib.ssd_conv1d_silu_step.argtypes = [dims_p, i32, vp, vp, f32p, f32p, vp, vp, vp, vp]
+    lib.ssd_conv1d_silu_step.restype = i32
     lib.ssd_status_string.argtypes = [i32]
     lib.ssd_status_string.restype = ctypes.c_char_p
     lib.ssd_tune_set.argtypes = [i32, i32]
@@ -174,6 +178,82 @@ def ssd_step(state, x, dt, dt_bias, A, B, C, D=None, y=None, stream=None, z=None
     if st != SSD_OK:
         raise SsdError(st, "ssd_step")
     return y
+
+
+def _check_conv(xbc, weight, bias, lead, nheads, headdim, dstate, ngroups):
+    Dc = nheads * headdim + 2 * ngroups * dstate
+    if xbc.shape[-1] != Dc:
+        raise ValueError(f"xbc has {xbc.shape[-1]} channels, H*P + 2*G*N = {Dc}")
+    if weight.dim() != 2 or weight.shape[0] != Dc:
+        raise ValueError("weight must have shape (Dc, K)")
+    if bias is not None and tuple(bias.shape) != (Dc,):
+        raise ValueError("bias must have shape (Dc,)")
+    for t in (weight, bias):
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError("weight and bias must be float32")
+    for t in (xbc, weight, bias):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    return Dc, weight.shape[1]
+
+
+def _conv_outputs(xbc, lead, nheads, headdim, dstate, ngroups, x, B, C):
+    kw = dict(dtype=xbc.dtype, device=xbc.device)
+    if x is None:
+        x = torch.empty(*lead, nheads, headdim, **kw)
+    if B is None:
+        B = torch.empty(*lead, ngroups, dstate, **kw)
+    if C is None:
+        C = torch.empty(*lead, ngroups, dstate, **kw)
+    for t, shp in ((x, (*lead, nheads, headdim)), (B, (*lead, ngroups, dstate)), (C, (*lead, ngroups, dstate))):
+        if tuple(t.shape) != shp or t.dtype != xbc.dtype or not t.is_contiguous():
+            raise ValueError("x / B / C outputs: wrong shape, dtype or layout")
+    return x, B, C
+
+
+def conv1d_silu(xbc, weight, bias, nheads, headdim, dstate, ngroups, conv_state=None, conv_state_out=None,
+                return_conv_state=True, x=None, B=None, C=None, stream=None):
+    """Causal depthwise conv1d + SiLU over xbc (B, L, H*P + 2*G*N), split into x, B, C.
+
+    weight (Dc, K) and bias (Dc,) are float32; conv_state (B, K-1, Dc) in xbc's dtype holds the
+    K-1 inputs before the sequence.  Returns (x, B, C, conv_state_out); conv_state_out may be
+    `conv_state` itself (in-place update).
+    """
+    if xbc.dim() != 3:
+        raise ValueError("xbc (B, L, Dc) expected")
+    b, L, _ = xbc.shape
+    Dc, K = _check_conv(xbc, weight, bias, (b, L), nheads, headdim, dstate, ngroups)
+    for t in (conv_state, conv_state_out):
+        if t is not None and (tuple(t.shape) != (b, K - 1, Dc) or t.dtype != xbc.dtype or not t.is_contiguous()):
+            raise ValueError("conv state must be a contiguous (B, K-1, Dc) tensor of xbc's dtype")
+    x, B, C = _conv_outputs(xbc, (b, L), nheads, headdim, dstate, ngroups, x, B, C)
+    if conv_state_out is None and return_conv_state:
+        conv_state_out = torch.empty(b, K - 1, Dc, dtype=xbc.dtype, device=xbc.device)
+    dims = make_dims(b, L, nheads, headdim, dstate, ngroups, xbc.dtype)
+    st = load_library().ssd_conv1d_silu(ctypes.byref(dims), int(K), _ptr(xbc), _ptr(weight), _ptr(bias),
+                                        _ptr(conv_state), _ptr(conv_state_out), _ptr(x), _ptr(B), _ptr(C),
+                                        _stream(stream))
+    if st != SSD_OK:
+        raise SsdError(st, "ssd_conv1d_silu")
+    return x, B, C, conv_state_out
+
+
+def conv1d_silu_step(conv_state, xbc, weight, bias, nheads, headdim, dstate, ngroups, x=None, B=None, C=None,
+                     stream=None):
+    """One decode token: xbc (B, Dc); conv_state (B, K-1, Dc) is shifted in place.  Returns (x, B, C)."""
+    if xbc.dim() != 2:
+        raise ValueError("xbc (B, Dc) expected")
+    b = xbc.shape[0]
+    Dc, K = _check_conv(xbc, weight, bias, (b,), nheads, headdim, dstate, ngroups)
+    if tuple(conv_state.shape) != (b, K - 1, Dc) or conv_state.dtype != xbc.dtype or not conv_state.is_contiguous():
+        raise ValueError("conv state must be a contiguous (B, K-1, Dc) tensor of xbc's dtype")
+    x, B, C = _conv_outputs(xbc, (b,), nheads, headdim, dstate, ngroups, x, B, C)
+    dims = make_dims(b, 1, nheads, headdim, dstate, ngroups, xbc.dtype)
+    st = load_library().ssd_conv1d_silu_step(ctypes.byref(dims), int(K), _ptr(conv_state), _ptr(xbc), _ptr(weight),
+                                             _ptr(bias), _ptr(x), _ptr(B), _ptr(C), _stream(stream))
+    if st != SSD_OK:
+        raise SsdError(st, "ssd_conv1d_silu_step")
+    return x, B, C
 
 
 def tune_set(key, value):

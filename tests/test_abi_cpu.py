@@ -127,6 +127,34 @@ def test_step_host_validation(lib):
     assert lib.ssd_step(ctypes.byref(_dims(batch=0)), p, p, p, p, p, p, p, None, None, p, None) == ssd.SSD_OK
 
 
+def test_conv_host_validation(lib):
+    vp = ctypes.c_void_p
+    p = vp(0x100000)
+    d = _dims()
+    # fwd: (dims, K, xbc, weight, bias, state_in, state_out, x, B, C, stream)
+    assert lib.ssd_conv1d_silu(None, 4, p, p, None, None, None, p, p, p, None) == ssd.SSD_ERR_INVALID_ARG
+    assert lib.ssd_conv1d_silu(ctypes.byref(d), 5, p, p, None, None, None, p, p, p, None) == ssd.SSD_ERR_UNSUPPORTED
+    assert lib.ssd_conv1d_silu(ctypes.byref(d), 0, p, p, None, None, None, p, p, p, None) == ssd.SSD_ERR_UNSUPPORTED
+    assert lib.ssd_conv1d_silu(ctypes.byref(d), 4, None, p, None, None, None, p, p, p, None) == ssd.SSD_ERR_INVALID_ARG
+    assert lib.ssd_conv1d_silu(ctypes.byref(d), 4, p, None, None, None, None, p, p, p, None) == ssd.SSD_ERR_INVALID_ARG
+    assert lib.ssd_conv1d_silu(ctypes.byref(d), 4, p, p, None, None, None, vp(0x100008), p, p,
+                               None) == ssd.SSD_ERR_INVALID_ARG                # output not 16-byte aligned
+    # states that overlap without being the same buffer
+    assert lib.ssd_conv1d_silu(ctypes.byref(d), 4, p, p, None, vp(0x200000), vp(0x200010), p, p, p,
+                               None) == ssd.SSD_ERR_INVALID_ARG
+    assert lib.ssd_conv1d_silu(ctypes.byref(_dims(batch=0)), 4, p, p, None, None, None, p, p, p, None) == ssd.SSD_OK
+    assert lib.ssd_conv1d_silu(ctypes.byref(_dims(headdim=24)), 4, p, p, None, None, None, p, p, p,
+                               None) == ssd.SSD_ERR_UNSUPPORTED
+    # seqlen 0 without a state to write: nothing to do
+    assert lib.ssd_conv1d_silu(ctypes.byref(_dims(seqlen=0)), 4, None, None, None, None, None, None, None, None,
+                               None) == ssd.SSD_OK
+    # step: (dims, K, state, xbc, weight, bias, x, B, C, stream); the state is required for K > 1
+    assert lib.ssd_conv1d_silu_step(ctypes.byref(d), 4, None, p, p, None, p, p, p, None) == ssd.SSD_ERR_INVALID_ARG
+    assert lib.ssd_conv1d_silu_step(ctypes.byref(d), 4, vp(0x100004), p, p, None, p, p, p,
+                                    None) == ssd.SSD_ERR_INVALID_ARG
+    assert lib.ssd_conv1d_silu_step(ctypes.byref(_dims(batch=0)), 4, p, p, p, None, p, p, p, None) == ssd.SSD_OK
+
+
 def test_binding_raises_without_library(monkeypatch, tmp_path):
     """The product path has no fallback: a missing library is an error, not a CPU detour."""
     monkeypatch.setattr(ssd, "_lib", None)
