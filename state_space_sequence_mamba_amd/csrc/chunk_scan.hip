@@ -314,7 +314,7 @@ __device__ __forceinline__ void apply_gate(f32x4 (&acc)[HB][TPof<P>::v], const T
 #pragma unroll
     for (int pt = 0; pt < TP; ++pt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[hh][pt][e] *= zv[hh][pt][e] / (1.f + expf(-zv[hh][pt][e]));
+      for (int e = 0; e < 4; ++e) acc[hh][pt][e] *= silu(zv[hh][pt][e]);
 }
 
 // Write one strip's (16 x P) results of head hh into the y staging rows.

@@ -7,25 +7,30 @@
 // state (the last K - 1 inputs of the previous call, oldest first), zeros when none is given.
 //
 // Bandwidth bound: every input is read once from HBM and every output written once.
-// One thread owns one 16-byte channel vector (4 fp32 / 8 bf16 channels) over a run of kT
-// consecutive tokens; consecutive threads take consecutive vectors, so each token row is read
-// and written as long contiguous segments.  The K - 1 tokens before the run (the halo, an
-// L2 hit: the neighbouring run reads them too) and the run itself are loaded up front; the
-// window then slides in registers.  Vectors never straddle the x / B / C boundaries
-// (H*P and G*N are multiples of 16 channels), so the split is a per-thread pointer choice.
+// One thread owns one 16-byte channel vector (4 fp32 / 8 bf16 channels) over a segment of
+// consecutive tokens; consecutive lanes take consecutive vectors of a group of up to 64, so
+// each token row is read and written as contiguous segments.  Segments are sized so that a
+// 64-token segment per thread on large inputs (shorter ones when that leaves too few
+// threads).  Each thread streams its segment 4 rows at a time with two register buffers, the
+// loads of the next rows in flight while the current ones are convolved and stored, and the
+// window sliding in registers; the K - 1 rows before a segment (its halo) are the only
+// re-read (K-1 in 64).  Vectors never straddle the x / B / C boundaries (H*P and G*N are multiples of 16
+// channels), so the split is a per-thread pointer choice.
 //
 // The conv state is written by the threads of the first run of each sequence, which are
 // the only ones that read the incoming state, after they have read it: the state may be
 // updated in place (state_out == state_in).
+#include <algorithm>
+
 #include "ssd_common.h"
 #include "ssd_launch.h"
 
 namespace ssd {
 
 namespace {
-constexpr int kT = 16;  // tokens per thread
-
-__device__ __forceinline__ float silu(float u) { return u / (1.f + expf(-u)); }
+constexpr int kRun = 4;            // rows per load batch of one thread (two batches in flight)
+constexpr int kSegment = 64;       // tokens per thread on large inputs (measured best)
+constexpr int64_t kMinThreads = 65536;   // below this, segments shrink to keep the chip busy
 
 template <typename T>
 __device__ __forceinline__ void to_floats(const Vec16<T>& v, float* f) {
@@ -66,90 +71,125 @@ __device__ __forceinline__ T* split_dst(T* xo, T* bo, T* co, int c0, int dx, int
 }
 }  // namespace
 
+// Rows r .. r+TT-1 of one channel vector, rows past `last` clamped to it (cache hits, never stored).
+template <typename T, int TT>
+__device__ __forceinline__ void load_rows(Vec16<T> (&raw)[TT], const T* src, int r, int last, int Dc) {
+#pragma unroll
+  for (int i = 0; i < TT; ++i) raw[i] = load16(src + (size_t)min(r + i, last) * Dc);
+}
+
+// Convolve, activate and store rows r .. min(r+TT, end)-1; the window slides through them.
+template <typename T, int K, int TT>
+__device__ __forceinline__ void conv_rows(const Vec16<T> (&raw)[TT], float (&win)[K > 1 ? K - 1 : 1][Vec16<T>::n],
+                                          const float (&wk)[K][Vec16<T>::n], const float (&bv)[Vec16<T>::n],
+                                          T* dst, int ld, int r, int end) {
+  constexpr int V = Vec16<T>::n;
+  constexpr int KH = K - 1;
+#pragma unroll
+  for (int i = 0; i < TT; ++i) {
+    float cur[V], out[V];
+    to_floats(raw[i], cur);
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      float u = bv[e] + wk[KH][e] * cur[e];
+#pragma unroll
+      for (int j = 0; j < KH; ++j) u += wk[j][e] * win[j][e];
+      out[e] = silu(u);
+    }
+#pragma unroll
+    for (int j = 0; j + 1 < KH; ++j)
+#pragma unroll
+      for (int e = 0; e < V; ++e) win[j][e] = win[j + 1][e];
+    if constexpr (KH > 0) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) win[KH - 1][e] = cur[e];
+    }
+    if (r + i < end) store_vec(dst + (size_t)(r + i) * ld, out);
+  }
+}
+
 template <typename T, int K>
 __global__ __launch_bounds__(256) void conv1d_silu_kernel(const T* __restrict__ xbc, const float* __restrict__ w,
                                                           const float* __restrict__ bias, const T* st_in,
                                                           T* st_out, T* __restrict__ xo, T* __restrict__ bo,
                                                           T* __restrict__ co, int L, int Dc, int dx, int dbc,
-                                                          int NV, int ntb, uint32_t total) {
+                                                          int NV, int VG, int seg, int nseg, uint32_t total,
+                                                          uint32_t nblocks) {
   constexpr int V = Vec16<T>::n;
   constexpr int KH = K - 1;                         // halo / state rows
-  const uint32_t gid = blockIdx.x * 256u + threadIdx.x;
+  constexpr int TT = kRun;
+  // thread -> (batch, vector group, segment, vector in group)
+  const uint32_t gid = xcd_swizzle(blockIdx.x, nblocks) * 256u + threadIdx.x;
   if (gid >= total) return;
-  const int vec = (int)(gid % (uint32_t)NV);
-  const uint32_t rest = gid / (uint32_t)NV;
-  const int tb = (int)(rest % (uint32_t)ntb);
-  const int b = (int)(rest / (uint32_t)ntb);
+  const int vin = (int)(gid % (uint32_t)VG);
+  uint32_t rest = gid / (uint32_t)VG;
+  const int sg = (int)(rest % (uint32_t)nseg);
+  rest /= (uint32_t)nseg;
+  const int ngrp = NV / VG;
+  const int vec = (int)(rest % (uint32_t)ngrp) * VG + vin;
+  const int b = (int)(rest / (uint32_t)ngrp);
   const int c0 = vec * V;
-  const int t0 = tb * kT;
+  const int t0 = sg * seg;
+  const int t1 = min(L, t0 + seg);
   const T* src = xbc + (size_t)b * L * Dc + c0;
 
-  float wk[K][V], bv[V];
-  load_taps<K, V>(w, bias, c0, wk, bv);
-
-  // halo: the KH inputs before t0 (from the sequence, else the carried state, else zero)
-  float halo[KH > 0 ? KH : 1][V];
+  if (t0 < t1) {
+    // halo: the KH inputs before t0 (from the sequence, else the carried state, else zero),
+    // loaded branch-free (a dummy in-bounds address where the value is zero) so that they
+    // overlap the first rows' loads
+    Vec16<T> hraw[KH > 0 ? KH : 1];
 #pragma unroll
-  for (int j = 0; j < KH; ++j) {
-    const int s = t0 - KH + j;
-    Vec16<T> v;
-    if (s >= 0)
-      v = load16(src + (size_t)s * Dc);
-    else if (st_in)
-      v = load16(st_in + ((size_t)b * KH + KH + s) * Dc + c0);
-    else
-      v = zero16<T>();
-    to_floats(v, halo[j]);
-  }
-
-  if (L > 0) {
-    Vec16<T> raw[kT];
-#pragma unroll
-    for (int i = 0; i < kT; ++i) raw[i] = load16(src + (size_t)min(t0 + i, L - 1) * Dc);  // clamped rows unused
+    for (int j = 0; j < KH; ++j) {
+      const int s = t0 - KH + j;
+      const bool in_seq = s >= 0, in_state = !in_seq && st_in != nullptr;
+      const T* p = in_seq ? src + (size_t)s * Dc
+                          : (in_state ? st_in + ((size_t)b * KH + KH + s) * Dc + c0 : src);
+      hraw[j] = load16_if(p, in_seq || in_state);
+    }
+    // ping-pong: the next TT rows are in flight while the current ones are convolved and stored
+    Vec16<T> ra[TT], rb[TT];
+    const int last = t1 - 1;
+    int r = t0;
+    load_rows<T, TT>(ra, src, r, last, Dc);
+    float wk[K][V], bv[V];
+    load_taps<K, V>(w, bias, c0, wk, bv);
     int ld;
     T* dst = split_dst(xo, bo, co, c0, dx, dbc, (size_t)b * L, ld);
     float win[KH > 0 ? KH : 1][V];
 #pragma unroll
-    for (int j = 0; j < KH; ++j)
-#pragma unroll
-      for (int e = 0; e < V; ++e) win[j][e] = halo[j][e];
-#pragma unroll
-    for (int i = 0; i < kT; ++i) {
-      float cur[V], out[V];
-      to_floats(raw[i], cur);
-#pragma unroll
-      for (int e = 0; e < V; ++e) {
-        float u = bv[e] + wk[KH][e] * cur[e];
-#pragma unroll
-        for (int j = 0; j < KH; ++j) u += wk[j][e] * win[j][e];
-        out[e] = silu(u);
-      }
-#pragma unroll
-      for (int j = 0; j + 1 < KH; ++j)
-#pragma unroll
-        for (int e = 0; e < V; ++e) win[j][e] = win[j + 1][e];
-      if constexpr (KH > 0) {
-#pragma unroll
-        for (int e = 0; e < V; ++e) win[KH - 1][e] = cur[e];
-      }
-      if (t0 + i < L) store_vec(dst + (size_t)(t0 + i) * ld, out);
+    for (int j = 0; j < KH; ++j) to_floats(hraw[j], win[j]);
+    while (true) {
+      load_rows<T, TT>(rb, src, r + TT, last, Dc);
+      conv_rows<T, K, TT>(ra, win, wk, bv, dst, ld, r, t1);
+      r += TT;
+      if (r >= t1) break;
+      load_rows<T, TT>(ra, src, r + TT, last, Dc);
+      conv_rows<T, K, TT>(rb, win, wk, bv, dst, ld, r, t1);
+      r += TT;
+      if (r >= t1) break;
     }
   }
 
-  // new conv state: the inputs at times L-KH .. L-1 (older ones from the incoming state)
-  if (st_out && tb == 0) {
+  // New conv state: the inputs at times L-KH .. L-1, older ones (L < KH) from the incoming
+  // state, whose row L + j feeds row j.  Written by the first segment of each sequence, the
+  // only reader of the incoming state, after all its reads (every source row is loaded before
+  // the first store): in-place updates are safe.
+  if (st_out && sg == 0) {
+    Vec16<T> nraw[KH > 0 ? KH : 1];
 #pragma unroll
     for (int j = 0; j < KH; ++j) {
       const int s = L - KH + j;
-      float f[V];
-      if (s >= 0) {
-        to_floats(load16(src + (size_t)s * Dc), f);
-      } else {
-#pragma unroll
-        for (int e = 0; e < V; ++e) f[e] = halo[KH + s][e];   // t0 = 0: halo[j] holds time j - KH
-      }
-      store_vec(st_out + ((size_t)b * KH + j) * Dc + c0, f);
+      const bool in_seq = s >= 0, in_state = !in_seq && st_in != nullptr;
+      if (in_seq)
+        nraw[j] = load16(src + (size_t)s * Dc);
+      else if (in_state)
+        nraw[j] = load16(st_in + ((size_t)b * KH + KH + s) * Dc + c0);
+      else
+        nraw[j] = zero16<T>();
     }
+#pragma unroll
+    for (int j = 0; j < KH; ++j)
+      *reinterpret_cast<uint4*>(st_out + ((size_t)b * KH + j) * Dc + c0) = *reinterpret_cast<const uint4*>(&nraw[j]);
   }
 }
 
@@ -194,12 +234,26 @@ __global__ __launch_bounds__(256) void conv1d_silu_step_kernel(const T* __restri
 template <typename T, int K>
 static hipError_t launch_conv_impl(const ConvArgs& a, hipStream_t s) {
   const int NV = a.Dc / Vec16<T>::n;
-  const int ntb = a.L > 0 ? (a.L + kT - 1) / kT : 1;
-  const uint32_t total = (uint32_t)a.B * ntb * NV;
+  int VG = 64;                                       // vectors per group: the largest power of
+  while (NV % VG) VG >>= 1;                          // two up to 64 that divides NV
+  // segment length (a multiple of the run): kSegment tokens, fewer when that would leave
+  // fewer than kMinThreads threads; or as set explicitly
+  int seg = a.segment;
+  if (seg <= 0) {
+    const int64_t cols = (int64_t)a.B * NV;
+    const int64_t rows = ((int64_t)a.L * cols + kMinThreads - 1) / kMinThreads;
+    seg = (int)std::min<int64_t>(std::max<int64_t>(rows, kRun), kSegment);
+  }
+  seg = (seg + kRun - 1) / kRun * kRun;
+  const int nseg = a.L > 0 ? (a.L + seg - 1) / seg : 1;
+  const uint64_t total = (uint64_t)a.B * nseg * NV;
   if (total == 0) return hipSuccess;
-  conv1d_silu_kernel<T, K><<<(total + 255) / 256, 256, 0, s>>>(
+  if (total > 0xffffff00ull) return hipErrorInvalidValue;
+  const uint32_t nblocks = (uint32_t)((total + 255) / 256);
+  conv1d_silu_kernel<T, K><<<nblocks, 256, 0, s>>>(
       static_cast<const T*>(a.xbc), a.w, a.bias, static_cast<const T*>(a.state_in), static_cast<T*>(a.state_out),
-      static_cast<T*>(a.x), static_cast<T*>(a.Bo), static_cast<T*>(a.Co), a.L, a.Dc, a.dx, a.dbc, NV, ntb, total);
+      static_cast<T*>(a.x), static_cast<T*>(a.Bo), static_cast<T*>(a.Co), a.L, a.Dc, a.dx, a.dbc, NV, VG, seg, nseg,
+      (uint32_t)total, nblocks);
   return hipGetLastError();
 }
 

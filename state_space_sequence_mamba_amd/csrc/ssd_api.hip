@@ -74,6 +74,7 @@ bool device_ptr_ok(const void* p) {
 int g_tune_heads_per_block = 0;  // 0 = heuristic
 int g_tune_min_blocks = 512;
 int g_tune_scan_variant = 0;     // 0 = by dtype
+int g_tune_conv_segment = 0;     // 0 = sized to the chip
 
 int pick_scan_variant(int dtype) {
   if (g_tune_scan_variant == 1 || g_tune_scan_variant == 2) return g_tune_scan_variant;
@@ -194,6 +195,9 @@ ssd_status_t conv_impl(const ssd_dims_t* dims, int K, const void* xbc, const flo
   const int64_t dx = dims->nheads * dims->headdim, dbc = dims->ngroups * dims->dstate;
   const int64_t Dc = dx + 2 * dbc;
   if (Dc > (int64_t)1 << 24) return SSD_ERR_UNSUPPORTED;
+  // thread count of the prefill launch at its shortest segment (16 tokens) and vector (4 channels)
+  if (!step && dims->batch * ((dims->seqlen + 15) / 16 + 1) * (Dc / 4) > ((int64_t)1 << 32) - 256)
+    return SSD_ERR_UNSUPPORTED;
   if (has_seq) {
     if (!xbc || !weight || !x || !B || !C) return SSD_ERR_INVALID_ARG;
     if (!aligned(xbc, 16) || !aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(weight, 4) ||
@@ -232,6 +236,7 @@ ssd_status_t conv_impl(const ssd_dims_t* dims, int K, const void* xbc, const flo
   a.x = x;
   a.Bo = B;
   a.Co = C;
+  a.segment = g_tune_conv_segment;
   const hipError_t e = step ? ssd::launch_conv1d_silu_step(a, stream) : ssd::launch_conv1d_silu(a, stream);
   return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
 }
@@ -336,6 +341,7 @@ const char* ssd_status_string(ssd_status_t s) {
 void ssd_tune_set(int key, int value) {
   if (key == 0) g_tune_heads_per_block = value;
   if (key == 1) g_tune_min_blocks = value > 0 ? value : 512;
+  if (key == 3) g_tune_conv_segment = value > 0 ? value : 0;
   if (key == 2) g_tune_scan_variant = value;
 }
 

@@ -75,6 +75,12 @@ __device__ __forceinline__ Vec16<T> load16_if(const T* p, bool ok) {
 // fp32 resolution of v, so v itself is returned (and e^v never overflows).
 __device__ __forceinline__ float softplus(float v) { return v > 20.f ? v : log1pf(expf(v)); }
 
+// silu(u) = u / (1 + e^-u) with the hardware exp2 and reciprocal (each within ~1 ulp; the
+// result is within a few ulp).  Saturates cleanly: u -> -inf gives -0, u -> +inf gives u.
+__device__ __forceinline__ float silu(float u) {
+  return u * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-u * 1.4426950408889634f));
+}
+
 // ---------------------------------------------------------------- block order
 // Workgroups are dispatched round-robin over the 8 XCDs (id % 8), each with its own L2.
 // Map the hardware id to a logical id so that consecutive logical ids run on the same

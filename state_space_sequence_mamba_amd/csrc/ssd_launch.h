@@ -62,6 +62,7 @@ struct ConvArgs {
   void* x;                 // (B, L, dx)
   void* Bo;                // (B, L, dbc)
   void* Co;                // (B, L, dbc)
+  int segment;             // conv1d_silu tokens per thread (multiple of 16); 0 = sized to the chip
 };
 
 // true when a kernel instantiation exists for (dtype, P, N)

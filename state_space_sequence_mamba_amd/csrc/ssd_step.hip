@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void ssd_step_kernel(float* __restrict__ state
         float out = part + dw * xv[u];
         if (Z) {
           const float zv = to_f32(Z[(size_t)bh * P + p]);
-          out *= zv / (1.f + expf(-zv));  // silu gate
+          out *= silu(zv);  // output gate
         }
         y[(size_t)bh * P + p] = from_f32<T>(out);
       }

@@ -30,7 +30,7 @@ DT_MAX = 1e-1
 @dataclass(frozen=True)
 class Workload:
     name: str
-    entry: str            # "fwd" or "step"
+    entry: str            # "fwd", "step" or "conv"
     dtype: str            # "f32" or "bf16" (x, dt, B, C, y)
     batch: int
     nheads: int
@@ -39,13 +39,14 @@ class Workload:
     ngroups: int
     seed: int
     d_init: str           # "ones" or "normal"
-    seqlen: int = 0       # fwd only
+    seqlen: int = 0       # fwd and conv
     chunk: int = 0        # fwd only
     steps: int = 0        # step only
+    width: int = 0        # conv only (kernel width)
 
     @property
     def tokens(self):
-        return self.batch * (self.seqlen if self.entry == "fwd" else self.steps)
+        return self.batch * (self.steps if self.entry == "step" else self.seqlen)
 
 
 # The five workloads the scan is specified on: three forward sizes in the two
@@ -61,6 +62,9 @@ WORKLOADS = {w.name: w for w in [
              steps=1000),
     Workload("ssd_fwd bf16 B2 L16384 H80 P64 N128 G8 Q256", "fwd", "bf16", 2, 80, 64, 128, 8, 4, "normal",
              seqlen=16384, chunk=256),
+    # the conv in front of the scan, on the channels of the B8 L4096 bf16 forward (Dc 2304)
+    Workload("conv1d_silu bf16 B8 L4096 H32 P64 N128 G1 K4", "conv", "bf16", 8, 32, 64, 128, 1, 5, "ones",
+             seqlen=4096, width=4),
 ]}
 WORKLOAD_LIST = list(WORKLOADS.values())
 

@@ -23,25 +23,31 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SSD_KERNELS = ["chunk_cumsum", "chunk_state", "state_passing", "chunk_scan", "ssd_step"]
+SSD_KERNELS = ["chunk_cumsum", "chunk_state", "state_passing", "chunk_scan", "ssd_step", "conv1d_silu",
+               "conv1d_silu_step"]
+# source file of each kernel; every kernel also depends on the shared headers and the API layer
+# (which picks launch shapes)
+KERNEL_SOURCE = {"chunk_cumsum": "chunk_cumsum.hip", "chunk_state": "chunk_state.hip",
+                 "state_passing": "state_passing.hip", "chunk_scan": "chunk_scan.hip", "ssd_step": "ssd_step.hip",
+                 "conv1d_silu": "conv1d.hip", "conv1d_silu_step": "conv1d.hip"}
+SHARED_SOURCES = ["ssd_common.h", "ssd_launch.h", "ssd_api.hip"]
 
 
-def source_digest():
-    """sha256 over the HIP sources and headers the library is built from."""
+def source_digest(kernel):
+    """sha256 over the sources one kernel is built and launched from."""
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(PKG, "csrc", "*"))) + sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
-    for f in files:
-        h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
+    for name in [KERNEL_SOURCE[kernel]] + SHARED_SOURCES:
+        h.update(name.encode())
+        with open(os.path.join(PKG, "csrc", name), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
 def kernel_key(name):
-    """Map a dispatch's kernel name to an SSD stage, 'copy' for copy kernels, else None."""
+    """Map a dispatch's kernel name to a kernel key, 'copy' for copy kernels, else None."""
     if "chunk_scan" in name:
         return "chunk_scan"
-    for k in ("chunk_cumsum", "chunk_state", "state_passing", "ssd_step"):
+    for k in ("chunk_cumsum", "chunk_state", "state_passing", "ssd_step", "conv1d_silu_step", "conv1d_silu"):
         if k + "_kernel" in name:
             return k
     if "copyBuffer" in name or "copy_kernel" in name:
@@ -94,8 +100,8 @@ def traffic(args):
             fb = sum(fetch[k]) / len(fetch[k]) * f_scale
             wb = sum(write[k]) / len(write[k]) * w_scale
             kernels[k] = {"fetch_bytes": fb, "write_bytes": wb, "bytes": fb + wb,
-                          "dispatches": len(fetch[k])}
-    out = {"workload": args.workload, "source_digest": source_digest(),
+                          "dispatches": len(fetch[k]), "source_digest": source_digest(k)}
+    out = {"workload": args.workload,
            "copy_probe_bytes": copy_bytes,
            "copy_probe_counter_kib": {"FETCH_SIZE": f_copy, "WRITE_SIZE": w_copy},
            "scale_bytes_per_unit": {"FETCH_SIZE": f_scale, "WRITE_SIZE": w_scale},
@@ -126,9 +132,10 @@ def load_traffic(workload_slug, kernel):
         return None
     with open(path) as fh:
         t = json.load(fh)
-    if t.get("source_digest") != source_digest() or kernel not in t.get("kernels", {}):
+    k = t.get("kernels", {}).get(kernel)
+    if k is None or k.get("source_digest") != source_digest(kernel):
         return None
-    return t["kernels"][kernel]["bytes"]
+    return k["bytes"]
 
 
 def main():

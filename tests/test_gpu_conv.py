@@ -62,6 +62,29 @@ def test_conv_matches_oracle(dtype, H, P, N, G, K, L):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_conv_launch_shapes_do_not_change_results(dtype):
+    """Every tokens-per-thread launch shape gives bit-identical outputs and state."""
+    _say(f"conv launch shapes {dtype}")
+    H, P, N, G, K = 3, 64, 64, 1, 4           # 320 channel vectors (bf16): groups of 64, ragged runs
+    inp = I.make_conv_inputs(2, 301, H, P, N, G, K, dtype, seed=67, with_state=True)
+    d = _dev(inp)
+    ref = None
+    try:
+        for tt in (4, 16, 36, 64, 320):
+            ssd.tune_set(3, tt)
+            got = ssd.conv1d_silu(d["xbc"], d["weight"], d["bias"], H, P, N, G, conv_state=d["conv_state"])
+            torch.cuda.synchronize()
+            if ref is None:
+                ref = got
+            else:
+                for a, b in zip(got, ref):
+                    assert torch.equal(a, b), tt
+    finally:
+        ssd.tune_set(3, 0)
+    _check_conv(inp, H, P, N, G, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_conv_state_in_place_and_seqlen_zero(dtype):
     _say(f"conv in-place state {dtype}")
     H, P, N, G, K = 4, 32, 32, 1, 4
