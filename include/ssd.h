@@ -128,6 +128,38 @@ ssd_status_t ssd_step(const ssd_dims_t* dims, float* state,
                       const void* B, const void* C, const float* D, const void* z,
                       void* y, hipStream_t stream);
 
+/* Workspace bytes ssd_bwd needs for these sizes and chunk size, with or without a gate
+ * (with_gate != 0 adds room for the pre-gate output and the gated gradient).  0 if the sizes
+ * are invalid or unsupported.  The workspace holds the recomputed forward intermediates, the
+ * state gradients of every chunk (2 * B * nc * H * P * N fp32), per-head dB and dC
+ * (2 * B * L * H * N fp32) and small per-token and per-chunk partials. */
+size_t ssd_bwd_workspace_size(const ssd_dims_t* dims, int chunk_size, int with_gate);
+
+/* Gradients of ssd_fwd (y and final_state) with respect to every input: the exact gradient
+ * of the recurrence (section 3.2 of "Agent 228: MAMBA-2 Reference Implementations
+ * Comparison", D skip of Gap 4 of "Agent 228: MAMBA-2 Implementation Gaps", optional gate and
+ * dt clamp), evaluated chunk by chunk as in Gap 1.  Inputs are ssd_fwd's (same dims, chunk
+ * size and pointers; the forward intermediates are recomputed, nothing from the forward call
+ * is needed) plus:
+ *   dout            (B, L, H, P)  dtype   dL/dy (y as ssd_fwd returns it, gate included)
+ *   dfinal_state    (B, H, P, N)  fp32    dL/dfinal_state; NULL means zero
+ * Outputs (all written, none accumulated into):
+ *   dx (B, L, H, P), ddt (B, L, H), dB and dC (B, L, G, N)   dtype
+ *   ddt_bias, dA (H)   fp32     dD (H, P) fp32 or NULL (not wanted)
+ *   dz (B, L, H, P) dtype: required exactly when z is given
+ *   dinitial_state (B, H, P, N) fp32 or NULL (not wanted)
+ * ddt is the gradient with respect to the raw dt (before bias and softplus); it is zero where
+ * the clamp binds.  Results are deterministic (fixed-order reductions, no atomics).
+ * batch == 0 is a no-op; seqlen == 0 writes dinitial_state = dfinal_state (or zeros) and zero
+ * ddt_bias, dA, dD.  Thirteen kernels (fifteen with a gate). */
+ssd_status_t ssd_bwd(const ssd_dims_t* dims,
+                     const void* x, const void* dt, const float* dt_bias, const float* A,
+                     const void* B, const void* C, const float* D, const void* z, int chunk_size,
+                     const float* initial_state, const void* dout, const float* dfinal_state,
+                     void* dx, void* ddt, float* ddt_bias, float* dA, void* dB, void* dC, float* dD,
+                     void* dz, float* dinitial_state,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Causal depthwise conv1d + SiLU that produces the scan's x, B and C ("Agent 228: MAMBA-2
  * Implementation Gaps", Gap 2: one filter of width K = conv_width per channel, causal padding
  * K - 1; SiLU after it as in section 3.1 of "Agent 228: MAMBA-2 Reference Implementations

@@ -5,6 +5,8 @@
 // Implementation Gaps" and section 3.2 of "Agent 228: MAMBA-2 Reference Implementations
 // Comparison"; the decay of the carried state from position i to the chunk end is the
 // product of the per-step decays exp(dt' A), i.e. exp of the cumsum difference).
+// The backward pass reuses it with (dy, C) in place of (x, B) and w_i = exp(dAcs[i]): the
+// gradient that chunk c's outputs send into the state entering the chunk.
 //
 // One workgroup (4 wavefronts) per (b, c, h).  A (P x Q) . (Q x N) product on MFMA with
 // fp32 accumulation.  The contraction runs over tokens, the slow axis of x and B in HBM, so
@@ -26,7 +28,7 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const T* __restrict__ 
                                                           const float* __restrict__ dAcs,
                                                           float* __restrict__ states,
                                                           int L, int H, int G, int nc, int Q,
-                                                          uint32_t nblocks) {
+                                                          uint32_t nblocks, int from_start) {
   constexpr bool F32 = sizeof(T) == 4;
   constexpr int KT = 64;                                 // tokens per LDS tile
   constexpr int PITCH = KT + (F32 ? 4 : 8);              // 16-byte aligned rows
@@ -59,7 +61,9 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const T* __restrict__ 
   const float* dtp_c = dtp + (((size_t)b * H + h) * nc + c) * Q;
   const float* dA_c = dAcs + (((size_t)b * H + h) * nc + c) * Q;
   const float last = dA_c[Q - 1];
-  for (int i = tid; i < Q; i += 256) s_w[i] = expf(last - dA_c[i]) * dtp_c[i];
+  // forward: decay to the chunk's end times the step; backward (from_start): decay from the
+  // chunk's start, exp(dAcs_i), which weighs each output's gradient into the entering state
+  for (int i = tid; i < Q; i += 256) s_w[i] = from_start ? expf(dA_c[i]) : expf(last - dA_c[i]) * dtp_c[i];
 
   const size_t xs = (size_t)H * P, bs = (size_t)G * N;    // token strides
   const T* xb = x + ((size_t)b * L + t0) * xs + (size_t)h * P;
@@ -208,7 +212,7 @@ static hipError_t launch_state_impl(const FwdArgs& a, hipStream_t s) {
   const uint32_t nblocks = (uint32_t)a.B * a.nc * a.H;
   chunk_state_kernel<T, P, N><<<nblocks, 256, 0, s>>>(
       static_cast<const T*>(a.x), static_cast<const T*>(a.Bm), a.dtp, a.dAcs, a.states, a.L, a.H, a.G,
-      a.nc, a.Q, nblocks);
+      a.nc, a.Q, nblocks, a.state_from_start);
   return hipGetLastError();
 }
 

@@ -166,6 +166,8 @@ ssd_status_t fwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   a.states = has_seq ? reinterpret_cast<float*>(ws + wl.states_off) : nullptr;
   a.scan_variant = pick_scan_variant(a.dtype);
   a.heads_per_block = pick_heads_per_block(a.B, a.nc, a.H, a.G, a.Q, a.scan_variant);
+  a.state_from_start = 0;
+  a.passing_reverse = 0;
 
   if (!has_seq) {
     // no tokens: final_state = initial_state (or zeros); state_passing with zero chunks
@@ -179,6 +181,168 @@ ssd_status_t fwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   if (!record(2) || ssd::launch_state_passing(a, stream) != hipSuccess) return SSD_ERR_HIP;
   if (!record(3) || ssd::launch_chunk_scan(a, stream) != hipSuccess) return SSD_ERR_HIP;
   if (!record(4)) return SSD_ERR_HIP;
+  return SSD_OK;
+}
+
+// Backward workspace: the forward's regions, the state gradients, per-head dB / dC, per-token
+// and per-chunk partials, and (with a gate) the pre-gate output and the gated gradient.
+struct BwdLayout {
+  size_t dtp, dacs, states, gstates, dBh, dCh, ddir, dSa, dSc, Ub, pA, pbias, pD, ypre, dyg, total;
+};
+
+BwdLayout bwd_layout(const ssd_dims_t* d, int Q, bool gate) {
+  const int64_t nc = (d->seqlen + Q - 1) / Q;
+  const size_t cum = align_up((size_t)d->batch * d->nheads * nc * Q * sizeof(float));
+  const size_t st = align_up((size_t)d->batch * nc * d->nheads * d->headdim * d->dstate * sizeof(float));
+  const size_t perh = align_up((size_t)d->batch * d->seqlen * d->nheads * d->dstate * sizeof(float));
+  const size_t par = align_up((size_t)d->batch * nc * d->nheads * sizeof(float));
+  const size_t pd = align_up((size_t)d->batch * nc * (Q / 64) * d->nheads * d->headdim * sizeof(float));
+  const size_t act = gate ? align_up((size_t)d->batch * d->seqlen * d->nheads * d->headdim * elem_bytes(d->dtype)) : 0;
+  BwdLayout w;
+  size_t o = 0;
+  w.dtp = o; o += cum;
+  w.dacs = o; o += cum;
+  w.states = o; o += st;
+  w.gstates = o; o += st;
+  w.dBh = o; o += perh;
+  w.dCh = o; o += perh;
+  w.ddir = o; o += cum;
+  w.dSa = o; o += cum;
+  w.dSc = o; o += cum;
+  w.Ub = o; o += cum;
+  w.pA = o; o += par;
+  w.pbias = o; o += par;
+  w.pD = o; o += pd;
+  w.ypre = o; o += act;
+  w.dyg = o; o += act;
+  w.total = o;
+  return w;
+}
+
+ssd_status_t bwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, const float* dt_bias, const float* A,
+                      const void* B, const void* C, const float* D, const void* z, int chunk_size,
+                      const float* initial_state, const void* dout, const float* dfinal_state, void* dx, void* ddt,
+                      float* ddt_bias, float* dA, void* dB, void* dC, float* dD, void* dz, float* dinitial_state,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  ssd_status_t st = check_dims(dims, true);
+  if (st != SSD_OK) return st;
+  if (!chunk_ok(chunk_size)) return SSD_ERR_UNSUPPORTED;
+  if (!dt_bias || !A || !ddt_bias || !dA) return SSD_ERR_INVALID_ARG;
+  if ((z == nullptr) != (dz == nullptr)) return SSD_ERR_INVALID_ARG;   // dz exactly when gated
+  if (dims->batch == 0) return SSD_OK;
+  const bool has_seq = dims->seqlen > 0;
+  const size_t eb = elem_bytes(dims->dtype);
+  if (has_seq) {
+    if (!x || !dt || !B || !C || !dout || !dx || !ddt || !dB || !dC) return SSD_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(dout, 16)) return SSD_ERR_INVALID_ARG;
+    if (!aligned(dt, eb) || !aligned(dx, eb) || !aligned(ddt, eb) || !aligned(dB, eb) || !aligned(dC, eb) ||
+        (z && (!aligned(z, eb) || !aligned(dz, eb))) || (D && !aligned(D, 4)))
+      return SSD_ERR_INVALID_ARG;
+  }
+  if (!aligned(dt_bias, 4) || !aligned(A, 4) || !aligned(ddt_bias, 4) || !aligned(dA, 4) || (dD && !aligned(dD, 4)))
+    return SSD_ERR_INVALID_ARG;
+  if ((initial_state && !aligned(initial_state, 16)) || (dfinal_state && !aligned(dfinal_state, 16)) ||
+      (dinitial_state && !aligned(dinitial_state, 16)))
+    return SSD_ERR_INVALID_ARG;
+  const BwdLayout wl = bwd_layout(dims, chunk_size, z != nullptr);
+  if (!workspace || workspace_bytes < wl.total) return SSD_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return SSD_ERR_INVALID_ARG;
+  const void* ptrs[] = {x,  dt, dt_bias, A,  B,  C,   D,  z,  initial_state, dout, dfinal_state, dx,
+                        ddt, ddt_bias, dA, dB, dC, dD, dz, dinitial_state, workspace};
+  for (const void* p : ptrs)
+    if (p && !device_ptr_ok(p)) return SSD_ERR_DEVICE_PTR;
+
+  char* ws = static_cast<char*>(workspace);
+  ssd::BwdArgs a;
+  ssd::FwdArgs& f = a.f;
+  f.B = (int)dims->batch;
+  f.L = (int)dims->seqlen;
+  f.H = (int)dims->nheads;
+  f.P = (int)dims->headdim;
+  f.N = (int)dims->dstate;
+  f.G = (int)dims->ngroups;
+  f.Q = chunk_size;
+  f.nc = (int)((dims->seqlen + chunk_size - 1) / chunk_size);
+  f.dtype = dims->dtype;
+  f.x = x;
+  f.dt = dt;
+  f.dt_bias = dt_bias;
+  f.A = A;
+  f.Bm = B;
+  f.Cm = C;
+  f.D = D;
+  f.z = nullptr;                                      // the recomputed output is the pre-gate one
+  f.clamp = dims->dt_max > 0.f;
+  f.dt_lo = dims->dt_min;
+  f.dt_hi = dims->dt_max;
+  f.init = initial_state;
+  f.y = ws + wl.ypre;
+  f.final_state = nullptr;
+  f.dtp = reinterpret_cast<float*>(ws + wl.dtp);
+  f.dAcs = reinterpret_cast<float*>(ws + wl.dacs);
+  f.states = reinterpret_cast<float*>(ws + wl.states);
+  f.scan_variant = pick_scan_variant(f.dtype);
+  f.heads_per_block = pick_heads_per_block(f.B, f.nc, f.H, f.G, f.Q, f.scan_variant);
+  f.state_from_start = 0;
+  f.passing_reverse = 0;
+  a.dy = z ? static_cast<const void*>(ws + wl.dyg) : dout;
+  a.gstates = reinterpret_cast<float*>(ws + wl.gstates);
+  a.dBh = reinterpret_cast<float*>(ws + wl.dBh);
+  a.dCh = reinterpret_cast<float*>(ws + wl.dCh);
+  a.ddir = reinterpret_cast<float*>(ws + wl.ddir);
+  a.dSa = reinterpret_cast<float*>(ws + wl.dSa);
+  a.dSc = reinterpret_cast<float*>(ws + wl.dSc);
+  a.Ub = reinterpret_cast<float*>(ws + wl.Ub);
+  a.pA = reinterpret_cast<float*>(ws + wl.pA);
+  a.pbias = reinterpret_cast<float*>(ws + wl.pbias);
+  a.pD = reinterpret_cast<float*>(ws + wl.pD);
+  a.dx = dx;
+  a.ddt = ddt;
+  a.dB = dB;
+  a.dC = dC;
+  a.ddt_bias = ddt_bias;
+  a.dA = dA;
+  a.dD = dD;
+
+  // the state gradients, run backwards over the chunks from dL/dfinal_state
+  ssd::FwdArgs gp = f;
+  gp.states = a.gstates;
+  gp.init = dfinal_state;
+  gp.final_state = dinitial_state;
+  gp.passing_reverse = 1;
+  if (!has_seq) {
+    if (dinitial_state && ssd::launch_state_passing(gp, stream) != hipSuccess) return SSD_ERR_HIP;
+    return ssd::launch_bwd_reduce(a, stream) == hipSuccess ? SSD_OK : SSD_ERR_HIP;   // zero dA, d dt_bias, dD
+  }
+  // forward intermediates: dt', its cumsum, the states entering each chunk
+  if (ssd::launch_chunk_cumsum(f, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (ssd::launch_chunk_state(f, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (ssd::launch_state_passing(f, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (z) {
+    // pre-gate output, then dy = dout silu(z) and dz = dout y~ silu'(z)
+    if (ssd::launch_chunk_scan(f, stream) != hipSuccess) return SSD_ERR_HIP;
+    ssd::GateArgs ga;
+    ga.n = dims->batch * dims->seqlen * dims->nheads * dims->headdim;
+    ga.dtype = dims->dtype;
+    ga.dout = dout;
+    ga.z = z;
+    ga.ypre = f.y;
+    ga.dy = ws + wl.dyg;
+    ga.dz = dz;
+    if (ssd::launch_gate_bwd(ga, stream) != hipSuccess) return SSD_ERR_HIP;
+  }
+  // per-chunk gradient into the entering state: sum_i exp(dAcs_i) dy_i^T C_i
+  ssd::FwdArgs gs = f;
+  gs.x = a.dy;
+  gs.Bm = C;
+  gs.states = a.gstates;
+  gs.state_from_start = 1;
+  if (ssd::launch_chunk_state(gs, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (ssd::launch_state_passing(gp, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (ssd::launch_bwd_dxdb(a, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (ssd::launch_bwd_dc(a, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (ssd::launch_bwd_finalize(a, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (ssd::launch_bwd_reduce(a, stream) != hipSuccess) return SSD_ERR_HIP;
   return SSD_OK;
 }
 
@@ -312,6 +476,20 @@ ssd_status_t ssd_step(const ssd_dims_t* dims, float* state, const void* x, const
   a.dt_hi = dims->dt_max;
   a.y = y;
   return ssd::launch_ssd_step(a, stream) == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
+size_t ssd_bwd_workspace_size(const ssd_dims_t* dims, int chunk_size, int with_gate) {
+  if (check_dims(dims, true) != SSD_OK || !chunk_ok(chunk_size)) return 0;
+  return bwd_layout(dims, chunk_size, with_gate != 0).total;
+}
+
+ssd_status_t ssd_bwd(const ssd_dims_t* dims, const void* x, const void* dt, const float* dt_bias, const float* A,
+                     const void* B, const void* C, const float* D, const void* z, int chunk_size,
+                     const float* initial_state, const void* dout, const float* dfinal_state, void* dx, void* ddt,
+                     float* ddt_bias, float* dA, void* dB, void* dC, float* dD, void* dz, float* dinitial_state,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return bwd_impl(dims, x, dt, dt_bias, A, B, C, D, z, chunk_size, initial_state, dout, dfinal_state, dx, ddt,
+                  ddt_bias, dA, dB, dC, dD, dz, dinitial_state, workspace, workspace_bytes, stream);
 }
 
 ssd_status_t ssd_conv1d_silu(const ssd_dims_t* dims, int conv_width, const void* xbc, const float* weight,

@@ -31,6 +31,41 @@ struct FwdArgs {
   float* states;           // workspace (B, nc, H, P, N)
   int heads_per_block;     // chunk_scan: heads sharing one C B^T evaluation (divides H / G)
   int scan_variant;        // chunk_scan decomposition: 1 = 64-row blocks, 2 = whole chunks
+  int state_from_start;    // chunk_state weights exp(dAcs_i) instead of exp(last - dAcs_i) dt'_i
+  int passing_reverse;     // state_passing from the last chunk to the first
+};
+
+// Backward pass (ssd_bwd): the forward's workspace regions plus the gradient buffers.
+struct BwdArgs {
+  FwdArgs f;               // forward sizes, inputs and recomputed intermediates
+  const void* dy;          // (B, L, H, P) dtype: gradient of the pre-gate output
+  float* gstates;          // (B, nc, H, P, N): gradient of the state leaving each chunk
+  float* dBh;              // (B, L, H, N) per-head dB
+  float* dCh;              // (B, L, H, N) per-head dC
+  float* ddir;             // (B, H, nc, Q) direct d(dt') term
+  float* dSa;              // (B, H, nc, Q) anti-causal part of d(dAcs)
+  float* dSc;              // (B, H, nc, Q) causal part of d(dAcs)
+  float* Ub;               // (B, H, nc, Q) state-input term
+  float* pA;               // (B, nc, H) partial dA
+  float* pbias;            // (B, nc, H) partial d dt_bias
+  float* pD;               // (B, nc * Q/64, H, P) partial dD
+  void* dx;
+  void* ddt;
+  void* dB;
+  void* dC;
+  float* ddt_bias;
+  float* dA;
+  float* dD;               // may be null
+};
+
+struct GateArgs {
+  int64_t n;               // elements
+  int dtype;
+  const void* dout;
+  const void* z;
+  const void* ypre;
+  void* dy;
+  void* dz;
 };
 
 struct StepArgs {
@@ -73,6 +108,11 @@ hipError_t launch_chunk_state(const FwdArgs& a, hipStream_t s);
 hipError_t launch_state_passing(const FwdArgs& a, hipStream_t s);
 hipError_t launch_chunk_scan(const FwdArgs& a, hipStream_t s);
 hipError_t launch_ssd_step(const StepArgs& a, hipStream_t s);
+hipError_t launch_bwd_dxdb(const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_dc(const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_finalize(const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_reduce(const BwdArgs& a, hipStream_t s);
+hipError_t launch_gate_bwd(const GateArgs& a, hipStream_t s);
 hipError_t launch_conv1d_silu(const ConvArgs& a, hipStream_t s);
 hipError_t launch_conv1d_silu_step(const ConvArgs& a, hipStream_t s);
 

@@ -6,6 +6,11 @@
 // phase of the block-parallel scan in "Agent 230: Comprehensive MAMBA-2 Implementation
 // Comparison", section 2).
 //
+// The backward pass runs the same recurrence from the last chunk to the first (reverse != 0)
+// on the per-chunk output gradients: G_c = exp(dAcs[c, last]) * G_{c+1} + dS_c, leaving in
+// slot c the gradient of the state leaving chunk c and in final_state that of the initial
+// state.
+//
 // Sequential over chunks, parallel over (b, h, p, n): each thread owns 4 consecutive state
 // elements (one 16-byte load and store per chunk, fully coalesced: a (b, c, h) state block
 // is P*N contiguous floats) and keeps its carry in registers.  Loads of up to 8 chunks are
@@ -19,7 +24,7 @@ __global__ __launch_bounds__(256) void state_passing_kernel(float* __restrict__ 
                                                             const float* __restrict__ dAcs,
                                                             const float* init,
                                                             float* final_state,
-                                                            int H, int nc, int Q, int PN) {
+                                                            int H, int nc, int Q, int PN, int reverse) {
   constexpr int U = 8;
   const int h = blockIdx.y, b = blockIdx.z;
   const int e4 = (blockIdx.x * 256 + threadIdx.x) * 4;
@@ -37,14 +42,16 @@ __global__ __launch_bounds__(256) void state_passing_kernel(float* __restrict__ 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (c0 + u < nc) {
-        buf[u] = *reinterpret_cast<const float4*>(s + (size_t)(c0 + u) * cstride);
-        dec[u] = expf(dA[(size_t)(c0 + u) * Q]);
+        const int cc = reverse ? nc - 1 - (c0 + u) : c0 + u;
+        buf[u] = *reinterpret_cast<const float4*>(s + (size_t)cc * cstride);
+        dec[u] = expf(dA[(size_t)cc * Q]);
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (c0 + u < nc) {
-        *reinterpret_cast<float4*>(s + (size_t)(c0 + u) * cstride) = hs;
+        const int cc = reverse ? nc - 1 - (c0 + u) : c0 + u;
+        *reinterpret_cast<float4*>(s + (size_t)cc * cstride) = hs;
         hs.x = dec[u] * hs.x + buf[u].x;
         hs.y = dec[u] * hs.y + buf[u].y;
         hs.z = dec[u] * hs.z + buf[u].z;
@@ -58,7 +65,8 @@ __global__ __launch_bounds__(256) void state_passing_kernel(float* __restrict__ 
 hipError_t launch_state_passing(const FwdArgs& a, hipStream_t s) {
   const int PN = a.P * a.N;
   dim3 grid((PN / 4 + 255) / 256, a.H, a.B);
-  state_passing_kernel<<<grid, 256, 0, s>>>(a.states, a.dAcs, a.init, a.final_state, a.H, a.nc, a.Q, PN);
+  state_passing_kernel<<<grid, 256, 0, s>>>(a.states, a.dAcs, a.init, a.final_state, a.H, a.nc, a.Q, PN,
+                                            a.passing_reverse);
   return hipGetLastError();
 }
 

@@ -127,6 +127,38 @@ def test_step_host_validation(lib):
     assert lib.ssd_step(ctypes.byref(_dims(batch=0)), p, p, p, p, p, p, p, None, None, p, None) == ssd.SSD_OK
 
 
+def test_bwd_workspace_size_and_validation(lib):
+    # 1 x 256 tokens, H=4, P=N=16, Q=64: cum regions 4096 B, states 16384 B, per-head dB/dC
+    # 256*4*16*4 = 65536 B, per-chunk partials 64 -> 256 B, dD partials 4*4*16*4 = 1024 B
+    base = 2 * 4096 + 2 * 16384 + 2 * 65536 + 4 * 4096 + 2 * 256 + 1024
+    assert ssd.ssd_bwd_workspace_size(_dims(), 64, 0) == base
+    # the gate adds the pre-gate output and the gated gradient: 2 * 256 * 4 * 16 * 4 B
+    assert ssd.ssd_bwd_workspace_size(_dims(), 64, 1) == base + 2 * 65536
+    assert ssd.ssd_bwd_workspace_size(_dims(headdim=24), 64, 0) == 0
+    vp = ctypes.c_void_p
+    p = vp(0x100000)
+    d = _dims()
+
+    def call(dims=d, chunk=64, z=None, dz=None, ws=p, ws_bytes=1 << 30, **over):
+        a = dict(x=p, dt=p, dt_bias=p, A=p, B=p, C=p, D=None, init=None, dout=p, dfinal=None, dx=p, ddt=p,
+                 ddt_bias=p, dA=p, dB=p, dC=p, dD=None, dinit=None)
+        a.update(over)
+        return lib.ssd_bwd(None if dims is None else ctypes.byref(dims), a["x"], a["dt"], a["dt_bias"], a["A"],
+                           a["B"], a["C"], a["D"], z, chunk, a["init"], a["dout"], a["dfinal"], a["dx"], a["ddt"],
+                           a["ddt_bias"], a["dA"], a["dB"], a["dC"], a["dD"], dz, a["dinit"], ws, ws_bytes, None)
+
+    assert call(dims=None) == ssd.SSD_ERR_INVALID_ARG
+    assert call(chunk=32) == ssd.SSD_ERR_UNSUPPORTED
+    assert call(z=p) == ssd.SSD_ERR_INVALID_ARG                  # gate without dz
+    assert call(dz=p) == ssd.SSD_ERR_INVALID_ARG                 # dz without gate
+    assert call(dout=None) == ssd.SSD_ERR_INVALID_ARG
+    assert call(dA=None) == ssd.SSD_ERR_INVALID_ARG
+    assert call(dout=vp(0x100004)) == ssd.SSD_ERR_INVALID_ARG    # not 16-byte aligned
+    assert call(ws=None) == ssd.SSD_ERR_WORKSPACE
+    assert call(ws_bytes=100) == ssd.SSD_ERR_WORKSPACE
+    assert call(dims=_dims(batch=0)) == ssd.SSD_OK
+
+
 def test_conv_host_validation(lib):
     vp = ctypes.c_void_p
     p = vp(0x100000)
