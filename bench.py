@@ -143,6 +143,134 @@ def run_decode(w, args, dev):
     print(json.dumps(out), flush=True)
 
 
+BWD_STAGES = ["chunk_cumsum", "chunk_state", "state_passing", "gate_fwd", "gate_bwd", "chunk_state_grad",
+              "state_passing_rev", "bwd_dxdb", "bwd_dc", "bwd_finalize", "bwd_reduce"]
+
+
+def backward_cost(w):
+    """Algorithmic bytes and flops of each backward kernel per launch.  C B^T and dy x^T are
+    counted once (in bwd_dxdb; bwd_dc recomputes them, which is not algorithmic work)."""
+    e = 4 if w.dtype == "f32" else 2
+    B, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
+    nc = (L + Q - 1) // Q
+    lens = [min(Q, L - c * Q) for c in range(nc)]
+    tri = sum(n * (n + 1) // 2 for n in lens)
+    cum = B * H * nc * Q * 4
+    st = B * nc * H * P * N * 4
+    fin = B * H * P * N * 4
+    x = B * L * H * P * e
+    bc = B * L * G * N * e
+    perh = B * L * H * N * 4
+    fwd = algorithmic_cost(w)
+    cost = {
+        "chunk_cumsum": fwd["chunk_cumsum"],
+        "chunk_state": fwd["chunk_state"],
+        "state_passing": dict(bytes=2 * st + B * H * nc * 4, flops=2 * B * nc * H * P * N),
+        "gate_fwd": dict(bytes=0, flops=0),
+        "gate_bwd": dict(bytes=0, flops=0),
+        "chunk_state_grad": dict(bytes=x + bc + cum + st, flops=2 * B * H * L * P * N),
+        "state_passing_rev": dict(bytes=2 * st + 2 * fin + B * H * nc * 4, flops=2 * B * nc * H * P * N),
+        "bwd_dxdb": dict(bytes=2 * x + 2 * bc + 2 * cum + st + x + perh + 3 * B * H * L * 4,
+                         flops=2 * N * tri * B * G + 2 * P * tri * B * H * 2 + 2 * N * tri * B * H
+                         + 4 * B * H * L * P * N),
+        "bwd_dc": dict(bytes=2 * x + 2 * bc + 2 * cum + st + perh + B * H * L * 4,
+                       flops=2 * N * tri * B * H + 2 * B * H * L * P * N),
+        "bwd_finalize": dict(bytes=2 * st + 5 * cum + B * L * H * e * 2, flops=2 * B * nc * H * P * N),
+        "bwd_reduce": dict(bytes=2 * perh + 2 * bc, flops=2 * B * L * H * N),
+    }
+    for k, v in cost.items():
+        # chunk_state contracts on MFMA in the input dtype; the backward kernels' products run
+        # on fp32 MFMA whatever the input dtype
+        v["peak"] = MFMA_PEAK_TFLOPS[w.dtype] if k.startswith("chunk_state") else MFMA_PEAK_TFLOPS["f32"]
+        t_f = v["flops"] / (v["peak"] * 1e12)
+        t_b = v["bytes"] / (HBM_PEAK_GBS * 1e9)
+        v["bound"] = "mfma" if t_f > t_b else "hbm"
+    return cost
+
+
+def run_bwd(w, args, dev):
+    """The backward workload: K ssd_bwd calls over one resident batch (HIP graph replay);
+    per-kernel durations from an eager pass with the library's stage events."""
+    inp = {k: v.to(dev) for k, v in I.make_workload_inputs(w).items()}
+    dout, dfin = I.make_upstream_grads(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.dtype,
+                                       seed=500 + w.seed, device=dev)
+    out = ssd.ssd_bwd(inp["x"], inp["dt"], inp["dt_bias"], inp["A"], inp["B"], inp["C"], dout, D=inp["D"],
+                      chunk_size=w.chunk, dfinal_state=dfin)
+    dims = ssd.make_dims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, inp["x"].dtype)
+    ws = torch.empty(ssd.ssd_bwd_workspace_size(dims, w.chunk), dtype=torch.uint8, device=dev)
+
+    def step(evs=None):
+        ssd.ssd_bwd(inp["x"], inp["dt"], inp["dt_bias"], inp["A"], inp["B"], inp["C"], dout, D=inp["D"],
+                    chunk_size=w.chunk, dfinal_state=dfin, workspace=ws, out=out, stage_events=evs)
+
+    K, W = args.steps, args.warmup
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    use_graph = not args.no_graph
+    if use_graph:
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(graph, stream=cap):
+            for _ in range(K):
+                step()
+        torch.cuda.synchronize()
+    hev = HipEvents()
+    t0, t1 = hev.create(), hev.create()
+    wall0 = time.perf_counter()
+    hev.record(t0)
+    if use_graph:
+        graph.replay()
+    else:
+        for _ in range(K):
+            step()
+    hev.record(t1)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = hev.elapsed_ms(t0, t1) / K
+    events = [[hev.create() for _ in range(12)] for _ in range(K)]
+    for i in range(K):
+        step(events[i])
+    torch.cuda.synchronize()
+    per_kernel_ms = {k: sum(hev.elapsed_ms(ev[i], ev[i + 1]) for ev in events) / K
+                     for i, k in enumerate(BWD_STAGES)}
+    cost = backward_cost(w)
+    kernels = {}
+    for k in BWD_STAGES:
+        if k.startswith("gate"):
+            continue
+        t = per_kernel_ms[k] * 1e-3
+        c = cost[k]
+        if c["bound"] == "mfma":
+            ach, peak, unit = c["flops"] / t / 1e12, c["peak"], "TFLOP/s"
+        else:
+            ach, peak, unit = c["bytes"] / t / 1e9, HBM_PEAK_GBS, "GB/s"
+        kernels[k] = {"us": round(per_kernel_ms[k] * 1e3, 3), "bound": c["bound"], "achieved": round(ach, 2),
+                      "peak": peak, "unit": unit, "frac": round(ach / peak, 4), "alg_bytes": c["bytes"],
+                      "alg_flops": c["flops"]}
+    dom = max(kernels, key=lambda k: kernels[k]["us"])
+    kd = kernels[dom]
+    res = {
+        "metric": "SSD backward tokens/sec at 1 MI355X + % of MFMA/HBM roofline",
+        "value": round(w.batch * w.seqlen / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) x/B/C/dt/dout/dfinal, log-uniform dt bias, A=-U[1,16])",
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads,
+                   "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups, "chunk_size": w.chunk},
+        "roofline": {"kernel": dom, "bound": kd["bound"], "achieved": kd["achieved"], "peak": kd["peak"],
+                     "unit": kd["unit"], "frac": kd["frac"], "traffic": load_traffic(workload_slug(w.name), dom)},
+        "kernels": kernels,
+        "launch": ("hip_graph (per-kernel times from an eager pass of the same K steps)" if use_graph
+                   else "eager"),
+        "wall_s_timed_region": round(wall, 4),
+    }
+    hev.close()
+    copy_probe(args, dev)
+    print(json.dumps(res), flush=True)
+
+
 def copy_probe(args, dev):
     """A plain device copy of --copy-probe-mb MiB: the known-size reference of counter runs."""
     if args.copy_probe_mb:
@@ -242,6 +370,9 @@ def main():
     torch.cuda.set_device(dev)
     if w.entry == "step":
         run_decode(w, args, dev)
+        return
+    if w.entry == "bwd":
+        run_bwd(w, args, dev)
         return
     if w.entry == "conv":
         if args.conv_tokens:

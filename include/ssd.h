@@ -160,6 +160,22 @@ ssd_status_t ssd_bwd(const ssd_dims_t* dims,
                      void* dz, float* dinitial_state,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ssd_bwd with per-kernel timing: identical arguments and results, plus `stage_events`, an
+ * array of 12 caller-created events recorded on `stream` before each stage: 0 chunk_cumsum,
+ * 1 chunk_state, 2 state_passing (forward recompute), 3 chunk_scan of the pre-gate output and
+ * 4 the gate's backward (both empty without a gate), 5 chunk_state of the output gradients,
+ * 6 reverse state_passing, 7 the anti-causal kernel, 8 the causal kernel, 9 finalize,
+ * 10 reductions, and 11 after the last.  Like ssd_fwd_timed it refuses a stream under graph
+ * capture (SSD_ERR_UNSUPPORTED, nothing launched). */
+ssd_status_t ssd_bwd_timed(const ssd_dims_t* dims,
+                           const void* x, const void* dt, const float* dt_bias, const float* A,
+                           const void* B, const void* C, const float* D, const void* z, int chunk_size,
+                           const float* initial_state, const void* dout, const float* dfinal_state,
+                           void* dx, void* ddt, float* ddt_bias, float* dA, void* dB, void* dC, float* dD,
+                           void* dz, float* dinitial_state,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream,
+                           hipEvent_t* stage_events);
+
 /* Causal depthwise conv1d + SiLU that produces the scan's x, B and C ("Agent 228: MAMBA-2
  * Implementation Gaps", Gap 2: one filter of width K = conv_width per channel, causal padding
  * K - 1; SiLU after it as in section 3.1 of "Agent 228: MAMBA-2 Reference Implementations

@@ -223,7 +223,7 @@ ssd_status_t bwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
                       const void* B, const void* C, const float* D, const void* z, int chunk_size,
                       const float* initial_state, const void* dout, const float* dfinal_state, void* dx, void* ddt,
                       float* ddt_bias, float* dA, void* dB, void* dC, float* dD, void* dz, float* dinitial_state,
-                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                      void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* ev) {
   ssd_status_t st = check_dims(dims, true);
   if (st != SSD_OK) return st;
   if (!chunk_ok(chunk_size)) return SSD_ERR_UNSUPPORTED;
@@ -251,6 +251,11 @@ ssd_status_t bwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
                         ddt, ddt_bias, dA, dB, dC, dD, dz, dinitial_state, workspace};
   for (const void* p : ptrs)
     if (p && !device_ptr_ok(p)) return SSD_ERR_DEVICE_PTR;
+  if (ev) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return SSD_ERR_HIP;
+    if (cs != hipStreamCaptureStatusNone) return SSD_ERR_UNSUPPORTED;
+  }
 
   char* ws = static_cast<char*>(workspace);
   ssd::BwdArgs a;
@@ -310,17 +315,23 @@ ssd_status_t bwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   gp.init = dfinal_state;
   gp.final_state = dinitial_state;
   gp.passing_reverse = 1;
+  auto record = [&](int k) { return !ev || hipEventRecord(ev[k], stream) == hipSuccess; };
   if (!has_seq) {
+    for (int k = 0; k < 11; ++k)
+      if (!record(k)) return SSD_ERR_HIP;
     if (dinitial_state && ssd::launch_state_passing(gp, stream) != hipSuccess) return SSD_ERR_HIP;
-    return ssd::launch_bwd_reduce(a, stream) == hipSuccess ? SSD_OK : SSD_ERR_HIP;   // zero dA, d dt_bias, dD
+    if (ssd::launch_bwd_reduce(a, stream) != hipSuccess) return SSD_ERR_HIP;   // zero dA, d dt_bias, dD
+    return record(11) ? SSD_OK : SSD_ERR_HIP;
   }
   // forward intermediates: dt', its cumsum, the states entering each chunk
-  if (ssd::launch_chunk_cumsum(f, stream) != hipSuccess) return SSD_ERR_HIP;
-  if (ssd::launch_chunk_state(f, stream) != hipSuccess) return SSD_ERR_HIP;
-  if (ssd::launch_state_passing(f, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (!record(0) || ssd::launch_chunk_cumsum(f, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (!record(1) || ssd::launch_chunk_state(f, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (!record(2) || ssd::launch_state_passing(f, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (!record(3)) return SSD_ERR_HIP;
   if (z) {
     // pre-gate output, then dy = dout silu(z) and dz = dout y~ silu'(z)
     if (ssd::launch_chunk_scan(f, stream) != hipSuccess) return SSD_ERR_HIP;
+    if (!record(4)) return SSD_ERR_HIP;
     ssd::GateArgs ga;
     ga.n = dims->batch * dims->seqlen * dims->nheads * dims->headdim;
     ga.dtype = dims->dtype;
@@ -330,6 +341,8 @@ ssd_status_t bwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
     ga.dy = ws + wl.dyg;
     ga.dz = dz;
     if (ssd::launch_gate_bwd(ga, stream) != hipSuccess) return SSD_ERR_HIP;
+  } else if (!record(4)) {
+    return SSD_ERR_HIP;
   }
   // per-chunk gradient into the entering state: sum_i exp(dAcs_i) dy_i^T C_i
   ssd::FwdArgs gs = f;
@@ -337,13 +350,13 @@ ssd_status_t bwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   gs.Bm = C;
   gs.states = a.gstates;
   gs.state_from_start = 1;
-  if (ssd::launch_chunk_state(gs, stream) != hipSuccess) return SSD_ERR_HIP;
-  if (ssd::launch_state_passing(gp, stream) != hipSuccess) return SSD_ERR_HIP;
-  if (ssd::launch_bwd_dxdb(a, stream) != hipSuccess) return SSD_ERR_HIP;
-  if (ssd::launch_bwd_dc(a, stream) != hipSuccess) return SSD_ERR_HIP;
-  if (ssd::launch_bwd_finalize(a, stream) != hipSuccess) return SSD_ERR_HIP;
-  if (ssd::launch_bwd_reduce(a, stream) != hipSuccess) return SSD_ERR_HIP;
-  return SSD_OK;
+  if (!record(5) || ssd::launch_chunk_state(gs, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (!record(6) || ssd::launch_state_passing(gp, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (!record(7) || ssd::launch_bwd_dxdb(a, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (!record(8) || ssd::launch_bwd_dc(a, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (!record(9) || ssd::launch_bwd_finalize(a, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (!record(10) || ssd::launch_bwd_reduce(a, stream) != hipSuccess) return SSD_ERR_HIP;
+  return record(11) ? SSD_OK : SSD_ERR_HIP;
 }
 
 // Both conv entry points.  `step`: one token per sequence, state updated in place.
@@ -489,7 +502,17 @@ ssd_status_t ssd_bwd(const ssd_dims_t* dims, const void* x, const void* dt, cons
                      float* ddt_bias, float* dA, void* dB, void* dC, float* dD, void* dz, float* dinitial_state,
                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return bwd_impl(dims, x, dt, dt_bias, A, B, C, D, z, chunk_size, initial_state, dout, dfinal_state, dx, ddt,
-                  ddt_bias, dA, dB, dC, dD, dz, dinitial_state, workspace, workspace_bytes, stream);
+                  ddt_bias, dA, dB, dC, dD, dz, dinitial_state, workspace, workspace_bytes, stream, nullptr);
+}
+
+ssd_status_t ssd_bwd_timed(const ssd_dims_t* dims, const void* x, const void* dt, const float* dt_bias,
+                           const float* A, const void* B, const void* C, const float* D, const void* z,
+                           int chunk_size, const float* initial_state, const void* dout,
+                           const float* dfinal_state, void* dx, void* ddt, float* ddt_bias, float* dA, void* dB,
+                           void* dC, float* dD, void* dz, float* dinitial_state, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream, hipEvent_t* stage_events) {
+  return bwd_impl(dims, x, dt, dt_bias, A, B, C, D, z, chunk_size, initial_state, dout, dfinal_state, dx, ddt,
+                  ddt_bias, dA, dB, dC, dD, dz, dinitial_state, workspace, workspace_bytes, stream, stage_events);
 }
 
 ssd_status_t ssd_conv1d_silu(const ssd_dims_t* dims, int conv_width, const void* xbc, const float* weight,

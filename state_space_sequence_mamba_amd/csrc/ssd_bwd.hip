@@ -36,9 +36,9 @@ namespace ssd {
 
 namespace {
 constexpr int KT = 64;   // tokens per tile (row block)
-constexpr int KP = KT + 1;
 
-// Stage `nvalid` token rows of width W (row stride `stride` elements) as fp32, zero rows after.
+// Stage `nvalid` token rows of width W (row stride `stride` elements) as fp32 rows of pitch
+// W + 4 (16-byte aligned), zero rows after.
 template <typename T, int W>
 __device__ __forceinline__ void stage_rows(float* dst, const T* src, size_t stride, int nvalid, int tid) {
   constexpr int VEC = Vec16<T>::n, WV = W / VEC, UNITS = KT * WV, NIT = (UNITS + 255) / 256;
@@ -54,13 +54,17 @@ __device__ __forceinline__ void stage_rows(float* dst, const T* src, size_t stri
     const int u = tid + 256 * k;
     if (u < UNITS) {
       const int tok = u / WV, cv = (u % WV) * VEC;
+      float f[VEC];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) dst[tok * (W + 1) + cv + e] = to_f32(v[k].v[e]);
+      for (int e = 0; e < VEC; ++e) f[e] = to_f32(v[k].v[e]);
+#pragma unroll
+      for (int e = 0; e < VEC; e += 4)
+        *reinterpret_cast<float4*>(dst + tok * (W + 4) + cv + e) = make_float4(f[e], f[e + 1], f[e + 2], f[e + 3]);
     }
   }
 }
 
-// Stage a (P x N) fp32 state as rows of pitch N + 1.
+// Stage a (P x N) fp32 state as rows of pitch N + 4.
 template <int P, int N>
 __device__ __forceinline__ void stage_state(float* dst, const float* src, int tid) {
   constexpr int UNITS = P * N / 4, NIT = (UNITS + 255) / 256;
@@ -70,82 +74,72 @@ __device__ __forceinline__ void stage_state(float* dst, const float* src, int ti
 #pragma unroll
   for (int k = 0; k < NIT; ++k) {
     const int u = tid + 256 * k;
-    if (u < UNITS) {
-      const int p = (4 * u) / N, n = (4 * u) % N;
-      float* d = dst + p * (N + 1) + n;
-      d[0] = v[k].x;
-      d[1] = v[k].y;
-      d[2] = v[k].z;
-      d[3] = v[k].w;
-    }
+    if (u < UNITS) *reinterpret_cast<float4*>(dst + ((4 * u) / N) * (N + 4) + (4 * u) % N) = v[k];
   }
 }
 
-// Sum over the 16 lanes of a row group (lanes 16 tr .. 16 tr + 15 of a wavefront).
-__device__ __forceinline__ float sum16(float v) {
+// One 16 x 16 tile of A Bt^T over a contraction of length K along both operands' rows:
+//   out[i][j] += sum_k A[i][k] * Bt[j][k]     (A, Bt: 16 rows each, pitch PA / PB)
+// Lane (r, qd) feeds A row r and Bt row r with k = (K/4) qd + 4 m + c, one 128-bit LDS read
+// each per four MFMAs; it receives out[4 qd + e][r].
+template <int K, int PA, int PB>
+__device__ __forceinline__ f32x4 mm_rows(f32x4 acc, const float* A, const float* Bt, int r, int qd) {
+#pragma unroll
+  for (int m = 0; m < K / 16; ++m) {
+    const float4 a = *reinterpret_cast<const float4*>(A + r * PA + (K / 4) * qd + 4 * m);
+    const float4 b = *reinterpret_cast<const float4*>(Bt + r * PB + (K / 4) * qd + 4 * m);
+    acc = mfma_16x16x4_f32(a.x, b.x, acc);
+    acc = mfma_16x16x4_f32(a.y, b.y, acc);
+    acc = mfma_16x16x4_f32(a.z, b.z, acc);
+    acc = mfma_16x16x4_f32(a.w, b.w, acc);
+  }
+  return acc;
+}
+
+// out[i][c] += sum_k M[k][i] * V[k][c] over the 16 k of one tile, where lane (r, qd) holds
+// M[k = 4 qd + e][i = r] in m[e] (the result layout of mm_rows, used directly as the A
+// operand), and V rows k (pitch PV) are read from LDS at column c0 + r.
+template <int PV>
+__device__ __forceinline__ f32x4 mm_regs(f32x4 acc, const f32x4& m, const float* V, int c0, int r, int qd) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = mfma_16x16x4_f32(m[e], V[(4 * qd + e) * PV + c0 + r], acc);
+  return acc;
+}
+
+// out[i][c] += sum_k A[i][k] * V[k][c] over K, A rows i (pitch PA) and V rows k (pitch PV) in
+// LDS; lane (r, qd) reads A row r as 128-bit runs and V column c0 + r.
+template <int K, int PA, int PV>
+__device__ __forceinline__ f32x4 mm_cols(f32x4 acc, const float* A, const float* V, int c0, int r, int qd) {
+#pragma unroll
+  for (int m = 0; m < K / 16; ++m) {
+    const int k0 = (K / 4) * qd + 4 * m;
+    const float4 a = *reinterpret_cast<const float4*>(A + r * PA + k0);
+    acc = mfma_16x16x4_f32(a.x, V[(k0 + 0) * PV + c0 + r], acc);
+    acc = mfma_16x16x4_f32(a.y, V[(k0 + 1) * PV + c0 + r], acc);
+    acc = mfma_16x16x4_f32(a.z, V[(k0 + 2) * PV + c0 + r], acc);
+    acc = mfma_16x16x4_f32(a.w, V[(k0 + 3) * PV + c0 + r], acc);
+  }
+  return acc;
+}
+
+// Sum over the 16 lanes r of one qd group.
+__device__ __forceinline__ float sum_r(float v) {
 #pragma unroll
   for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
-
-// 4 x 4 block of the product of two row sets over a shared width W:
-// out[r][m] = sum_k A[(4 tr + r)][k] * Bt[(tc + 16 m)][k]   (both row-major, pitch W + 1)
-template <int W>
-__device__ __forceinline__ void rows_dot(float (&out)[4][4], const float* A, const float* Bt, int tr, int tc) {
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int m = 0; m < 4; ++m) out[r][m] = 0.f;
-#pragma unroll 4
-  for (int k = 0; k < W; ++k) {
-    float a[4], b[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) a[r] = A[(4 * tr + r) * (W + 1) + k];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) b[m] = Bt[(tc + 16 * m) * (W + 1) + k];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int m = 0; m < 4; ++m) out[r][m] += a[r] * b[m];
-  }
-}
-
-// acc[r][m] += sum_k M[k][4 tr + r] * V[k][tc + 16 m]   (M pitch KP, V pitch W + 1), k < KT
-template <int W>
-__device__ __forceinline__ void acc_tn(float (&acc)[4][W / 16], const float* M, const float* V, int tr, int tc) {
-#pragma unroll 4
-  for (int k = 0; k < KT; ++k) {
-    float a[4], b[W / 16];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) a[r] = M[k * KP + 4 * tr + r];
-#pragma unroll
-    for (int m = 0; m < W / 16; ++m) b[m] = V[k * (W + 1) + tc + 16 * m];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int m = 0; m < W / 16; ++m) acc[r][m] += a[r] * b[m];
-  }
-}
-
-// acc[r][m] += sum_k M[4 tr + r][k] * V[k][tc + 16 m]   (M pitch MP, V pitch W + 1), k < K
-template <int K, int MP, int W>
-__device__ __forceinline__ void acc_nn(float (&acc)[4][W / 16], const float* M, const float* V, int tr, int tc) {
-#pragma unroll 4
-  for (int k = 0; k < K; ++k) {
-    float a[4], b[W / 16];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) a[r] = M[(4 * tr + r) * MP + k];
-#pragma unroll
-    for (int m = 0; m < W / 16; ++m) b[m] = V[k * (W + 1) + tc + 16 * m];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int m = 0; m < W / 16; ++m) acc[r][m] += a[r] * b[m];
-  }
+// Sum over the 4 qd groups of one lane r.
+__device__ __forceinline__ float sum_qd(float v) {
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
 }
 }  // namespace
 
 // ------------------------------------------------------------------ anti-causal: dx, dB
+// Wavefront w owns the 16 columns j = 16 w .. 16 w + 15 of the row block R: it computes the
+// (i, j) tiles of C B^T and dy x^T for every i of the block I, weights them in registers,
+// and feeds them straight into xi[j][:] and dB[j][:] as MFMA A operands.
 template <typename T, int P, int N>
 __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, const T* __restrict__ Bm,
                                                        const T* __restrict__ Cm, const T* __restrict__ dy,
@@ -156,15 +150,13 @@ __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, 
                                                        float* __restrict__ dSa, float* __restrict__ Ub,
                                                        float* __restrict__ pD, int L, int H, int G, int nc, int Q,
                                                        uint32_t nblocks) {
-  constexpr int PP = P + 1, NP = N + 1, TPm = P / 16, TNm = N / 16;
-  __shared__ float s_b[KT * NP];                 // B of the own block R
-  __shared__ float s_x[KT * PP];                 // x of R
-  __shared__ float s_c[KT * NP];                 // C of block I; later Gnext (P x N)
-  __shared__ float s_dy[KT * PP];                // dy of block I
-  __shared__ float s_m1[KT * KP];                // e^(S_i - S_j) CB_ij   [i][j]
-  __shared__ float s_m2[KT * KP];                // e^(S_i - S_j) DX_ij   [i][j]
-  __shared__ float s_red[16 * KT];
+  constexpr int PP = P + 4, NP = N + 4, TPm = P / 16, TNm = N / 16;
+  __shared__ __attribute__((aligned(16))) float s_b[KT * NP];   // B of the own block R
+  __shared__ __attribute__((aligned(16))) float s_x[KT * PP];   // x of R
+  __shared__ __attribute__((aligned(16))) float s_c[KT * NP];   // C of block I; later Gnext (P x N)
+  __shared__ __attribute__((aligned(16))) float s_dy[KT * PP];  // dy of block I
   __shared__ float s_SR[KT], s_dR[KT], s_SI[KT];
+  __shared__ float s_red[4][P];
 
   const int nrb = Q / KT;
   uint32_t id = xcd_swizzle(blockIdx.x, nblocks);
@@ -175,7 +167,8 @@ __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, 
   const int c = id % nc, b = id / nc;
   const int g = h / (H / G);
   const int t0 = c * Q, len = min(Q, L - t0);
-  const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r = lane & 15, qd = lane >> 4;
   if (R * KT >= len) {                 // a row block past the end of the sequence: no rows,
     if (tid < P)                       // but its dD partial is still summed
       pD[(((size_t)b * nc + c) * nrb + R) * (size_t)(H * P) + (size_t)h * P + tid] = 0.f;
@@ -193,15 +186,13 @@ __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, 
     s_dR[tid] = dtp[cq + R * KT + tid];
   }
 
-  float xi[4][TPm], db[4][TNm], cs[4];
+  f32x4 xi[TPm], db[TNm];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    cs[r] = 0.f;
+  for (int m = 0; m < TPm; ++m) xi[m] = zero4();
 #pragma unroll
-    for (int m = 0; m < TPm; ++m) xi[r][m] = 0.f;
-#pragma unroll
-    for (int m = 0; m < TNm; ++m) db[r][m] = 0.f;
-  }
+  for (int m = 0; m < TNm; ++m) db[m] = zero4();
+  float cs = 0.f;                                  // column j = 16 w + r: sum_i M1 DX (partial over qd)
+  const int jl = 16 * w + r;                       // this lane's column of R
 
   const int nI = (len + KT - 1) / KT;
   for (int I = R; I < nI; ++I) {
@@ -211,136 +202,124 @@ __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, 
     stage_rows<T, P>(s_dy, dy + ((size_t)b * L + t0 + I * KT) * xs + (size_t)h * P, xs, lenI, tid);
     if (tid < KT) s_SI[tid] = dAcs[cq + I * KT + tid];
     __syncthreads();
-    float cb[4][4], dxv[4][4];
-    rows_dot<N>(cb, s_c, s_b, tr, tc);      // rows i of I, columns j of R
-    rows_dot<P>(dxv, s_dy, s_x, tr, tc);
+    const float sj = s_SR[jl];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 4 * tr + r;
+    for (int ti = 0; ti < 4; ++ti) {
+      if (I == R && ti < w) continue;              // tile entirely above the diagonal (i < j)
+      f32x4 cb = mm_rows<N, NP, NP>(zero4(), s_c + 16 * ti * NP, s_b + 16 * w * NP, r, qd);
+      f32x4 dxv = mm_rows<P, PP, PP>(zero4(), s_dy + 16 * ti * PP, s_x + 16 * w * PP, r, qd);
+      f32x4 m1, m2;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int j = tc + 16 * m;
-        const bool ok = (I * KT + i >= R * KT + j) && i < lenI && j < lenR;
-        const float e = ok ? expf(s_SI[i] - s_SR[j]) : 0.f;
-        const float m1 = e * cb[r][m];
-        cs[m] += m1 * dxv[r][m];
-        s_m1[i * KP + j] = m1;
-        s_m2[i * KP + j] = e * dxv[r][m];
+      for (int e = 0; e < 4; ++e) {
+        const int il = 16 * ti + 4 * qd + e;
+        const bool ok = (I * KT + il >= R * KT + jl) && il < lenI && jl < lenR;
+        const float ev = ok ? expf(s_SI[il] - sj) : 0.f;
+        m1[e] = ev * cb[e];
+        m2[e] = ev * dxv[e];
+        cs += m1[e] * dxv[e];
       }
+#pragma unroll
+      for (int m = 0; m < TPm; ++m) xi[m] = mm_regs<PP>(xi[m], m1, s_dy + 16 * ti * PP, 16 * m, r, qd);
+#pragma unroll
+      for (int m = 0; m < TNm; ++m) db[m] = mm_regs<NP>(db[m], m2, s_c + 16 * ti * NP, 16 * m, r, qd);
     }
-    __syncthreads();
-    acc_tn<P>(xi, s_m1, s_dy, tr, tc);      // xi[j][p] += sum_i m1[i][j] dy[i][p]
-    acc_tn<N>(db, s_m2, s_c, tr, tc);       // db[j][n] += sum_i m2[i][j] C[i][n]
   }
 
   // carried terms through the gradient of the state leaving the chunk
   __syncthreads();
   stage_state<P, N>(s_c, gstates + (((size_t)b * nc + c) * H + h) * (size_t)(P * N), tid);
-  // column partial sums of T (over this thread's rows i) -> per column j
-#pragma unroll
-  for (int m = 0; m < 4; ++m) s_red[tr * KT + tc + 16 * m] = cs[m];
   __syncthreads();
-  float tmp[4][TPm];
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int m = 0; m < TPm; ++m) tmp[r][m] = 0.f;
-  // tmp[j][p] = sum_n B[j][n] Gnext[p][n]
-#pragma unroll 4
-  for (int n = 0; n < N; ++n) {
-    float a[4], gv[TPm];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) a[r] = s_b[(4 * tr + r) * NP + n];
-#pragma unroll
-    for (int m = 0; m < TPm; ++m) gv[m] = s_c[(tc + 16 * m) * NP + n];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int m = 0; m < TPm; ++m) tmp[r][m] += a[r] * gv[m];
-  }
+  // lane rows j = 16 w + 4 qd + e from here on
   float f[4], dj[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    f[r] = expf(Slast - s_SR[4 * tr + r]);
-    dj[r] = s_dR[4 * tr + r];
+  for (int e = 0; e < 4; ++e) {
+    const int j = 16 * w + 4 * qd + e;
+    f[e] = expf(Slast - s_SR[j]);
+    dj[e] = s_dR[j];
   }
-  // db[j][n] += f_j sum_p x[j][p] Gnext[p][n]
-  {
-    float xg[4][TNm];
+  float u[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+  for (int m = 0; m < TPm; ++m) {
+    // tmp[j][p] = sum_n B[j][n] Gnext[p][n]
+    const f32x4 tmp = mm_rows<N, NP, NP>(zero4(), s_b + 16 * w * NP, s_c + 16 * m * NP, r, qd);
 #pragma unroll
-      for (int m = 0; m < TNm; ++m) xg[r][m] = 0.f;
-    acc_nn<P, PP, N>(xg, s_x, s_c, tr, tc);
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int m = 0; m < TNm; ++m) db[r][m] += f[r] * xg[r][m];
+    for (int e = 0; e < 4; ++e) {
+      u[e] += s_x[(16 * w + 4 * qd + e) * PP + 16 * m + r] * tmp[e];
+      xi[m][e] += f[e] * tmp[e];
+    }
   }
-  float U[4], dd[4], dDp[TPm];
+#pragma unroll
+  for (int m = 0; m < TNm; ++m) {
+    // xg[j][n] = sum_p x[j][p] Gnext[p][n]
+    const f32x4 xg = mm_cols<P, PP, NP>(zero4(), s_x + 16 * w * PP, s_c, 16 * m, r, qd);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) db[m][e] += f[e] * xg[e];
+  }
+  float U[4], dd[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int j = 16 * w + 4 * qd + e;
+    float q = 0.f;
+#pragma unroll
+    for (int m = 0; m < TPm; ++m) q += s_x[j * PP + 16 * m + r] * xi[m][e];
+    U[e] = f[e] * dj[e] * sum_r(u[e]);
+    dd[e] = sum_r(q);
+  }
+  const float colsum = s_dR[jl] * sum_qd(cs);
+
+  // outputs of the own block R
+  const size_t row0 = (size_t)b * L + t0 + R * KT;
+  float dDp[TPm];
 #pragma unroll
   for (int m = 0; m < TPm; ++m) dDp[m] = 0.f;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int j = 4 * tr + r;
-    float u = 0.f, q = 0.f;
-#pragma unroll
-    for (int m = 0; m < TPm; ++m) {
-      const float xv = s_x[j * PP + tc + 16 * m];
-      u += xv * tmp[r][m];
-      xi[r][m] += f[r] * tmp[r][m];
-      q += xv * xi[r][m];
-    }
-    U[r] = f[r] * dj[r] * sum16(u);
-    dd[r] = sum16(q);
-  }
-  // outputs of the own block R
-  const size_t row0 = (size_t)b * L + t0 + R * KT;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int j = 4 * tr + r;
+  for (int e = 0; e < 4; ++e) {
+    const int j = 16 * w + 4 * qd + e;
     const bool ok = j < lenR;
     const size_t tok = row0 + (ok ? j : 0);
 #pragma unroll
     for (int m = 0; m < TPm; ++m) {
-      const int p = tc + 16 * m;
+      const int p = 16 * m + r;
       const float dyv = ok ? to_f32(dy[tok * xs + (size_t)h * P + p]) : 0.f;
       const float dw = Dw ? Dw[(size_t)h * P + p] : 0.f;
-      if (ok) dx[tok * xs + (size_t)h * P + p] = from_f32<T>(dw * dyv + dj[r] * xi[r][m]);
+      if (ok) dx[tok * xs + (size_t)h * P + p] = from_f32<T>(dw * dyv + dj[e] * xi[m][e]);
       dDp[m] += dyv * s_x[j * PP + p];
     }
     if (ok) {
 #pragma unroll
-      for (int m = 0; m < TNm; ++m) dBh[(tok * H + h) * (size_t)N + tc + 16 * m] = dj[r] * db[r][m];
-    }
-  }
-  if (tc == 0) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int j = 4 * tr + r;
-      if (j < lenR) {
-        float colsum = 0.f;
-        for (int q = 0; q < 16; ++q) colsum += s_red[q * KT + j];
-        colsum *= dj[r];
-        ddir[cq + R * KT + j] = dd[r];
-        dSa[cq + R * KT + j] = -colsum - U[r];
-        Ub[cq + R * KT + j] = U[r];
+      for (int m = 0; m < TNm; ++m) dBh[(tok * H + h) * (size_t)N + 16 * m + r] = dj[e] * db[m][e];
+      if (r == 0) {
+        ddir[cq + R * KT + j] = dd[e];
+        Ub[cq + R * KT + j] = U[e];
       }
     }
   }
-  // dD partial of this block: sum over the block's rows, per channel p
+  // the column sums belong to column j = 16 w + r; its U was computed by the lane holding row j
   __syncthreads();
+  float* s_u = s_c;                                  // Gnext no longer needed
+  if (r == 0) {
 #pragma unroll
-  for (int m = 0; m < TPm; ++m) s_red[tr * KT + tc + 16 * m] = dDp[m];
-  __syncthreads();
-  if (tid < P) {
-    float sD = 0.f;
-    for (int q = 0; q < 16; ++q) sD += s_red[q * KT + tid];
-    pD[(((size_t)b * nc + c) * nrb + R) * (size_t)(H * P) + (size_t)h * P + tid] = sD;
+    for (int e = 0; e < 4; ++e) s_u[16 * w + 4 * qd + e] = U[e];
   }
+  // dD partial of this block: per channel p, summed over the block's rows
+#pragma unroll
+  for (int m = 0; m < TPm; ++m) {
+    float v = dDp[m];
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    if (qd == 0) s_red[w][16 * m + r] = v;
+  }
+  __syncthreads();
+  if (qd == 0 && jl < lenR) dSa[cq + R * KT + jl] = -colsum - s_u[jl];
+  if (tid < P)
+    pD[(((size_t)b * nc + c) * nrb + R) * (size_t)(H * P) + (size_t)h * P + tid] =
+        s_red[0][tid] + s_red[1][tid] + s_red[2][tid] + s_red[3][tid];
 }
 
 // ------------------------------------------------------------------ causal: dC
+// Wavefront w owns the 16 rows i = 16 w .. 16 w + 15 of the row block R.  It computes the
+// transposed tiles (j, i) of B C^T and x dy^T for every j of block J, so that the weighted
+// tile feeds dC[i][:] directly as an MFMA A operand.
 template <typename T, int P, int N>
 __global__ __launch_bounds__(256) void bwd_dc_kernel(const T* __restrict__ x, const T* __restrict__ Bm,
                                                      const T* __restrict__ Cm, const T* __restrict__ dy,
@@ -348,12 +327,11 @@ __global__ __launch_bounds__(256) void bwd_dc_kernel(const T* __restrict__ x, co
                                                      const float* __restrict__ states, float* __restrict__ dCh,
                                                      float* __restrict__ dSc, int L, int H, int G, int nc, int Q,
                                                      uint32_t nblocks) {
-  constexpr int PP = P + 1, NP = N + 1, TNm = N / 16;
-  __shared__ float s_c[KT * NP];                 // C of the own block R
-  __shared__ float s_dy[KT * PP];                // dy of R
-  __shared__ float s_b[KT * NP];                 // B of block J; later Hprev (P x N)
-  __shared__ float s_x[KT * PP];                 // x of J
-  __shared__ float s_w[KT * KP];                 // e^(S_i - S_j) d_j DX_ij   [i][j]
+  constexpr int PP = P + 4, NP = N + 4, TNm = N / 16;
+  __shared__ __attribute__((aligned(16))) float s_c[KT * NP];   // C of the own block R
+  __shared__ __attribute__((aligned(16))) float s_dy[KT * PP];  // dy of R
+  __shared__ __attribute__((aligned(16))) float s_b[KT * NP];   // B of block J; later Hprev (P x N)
+  __shared__ __attribute__((aligned(16))) float s_x[KT * PP];   // x of J
   __shared__ float s_SR[KT], s_SJ[KT], s_dJ[KT];
 
   const int nrb = Q / KT;
@@ -367,7 +345,8 @@ __global__ __launch_bounds__(256) void bwd_dc_kernel(const T* __restrict__ x, co
   const int t0 = c * Q, len = min(Q, L - t0);
   if (R * KT >= len) return;
   const int lenR = min(KT, len - R * KT);
-  const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r = lane & 15, qd = lane >> 4;
   const size_t xs = (size_t)H * P, bs = (size_t)G * N;
   const size_t cq = (((size_t)b * H + h) * nc + c) * Q;
 
@@ -375,13 +354,11 @@ __global__ __launch_bounds__(256) void bwd_dc_kernel(const T* __restrict__ x, co
   stage_rows<T, P>(s_dy, dy + ((size_t)b * L + t0 + R * KT) * xs + (size_t)h * P, xs, lenR, tid);
   if (tid < KT) s_SR[tid] = dAcs[cq + R * KT + tid];
 
-  float dc[4][TNm], rs[4];
+  f32x4 dc[TNm];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    rs[r] = 0.f;
-#pragma unroll
-    for (int m = 0; m < TNm; ++m) dc[r][m] = 0.f;
-  }
+  for (int m = 0; m < TNm; ++m) dc[m] = zero4();
+  float rs = 0.f;                                  // row i = 16 w + r: sum_j T_ij (partial over qd)
+  const int il = 16 * w + r;
   for (int J = 0; J <= R; ++J) {
     const int lenJ = min(KT, len - J * KT);
     __syncthreads();
@@ -392,50 +369,59 @@ __global__ __launch_bounds__(256) void bwd_dc_kernel(const T* __restrict__ x, co
       s_dJ[tid] = dtp[cq + J * KT + tid];
     }
     __syncthreads();
-    float cb[4][4], dxv[4][4];
-    rows_dot<N>(cb, s_c, s_b, tr, tc);       // rows i of R, columns j of J
-    rows_dot<P>(dxv, s_dy, s_x, tr, tc);
+    const float si = s_SR[il];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 4 * tr + r;
+    for (int tj = 0; tj < 4; ++tj) {
+      if (J == R && tj > w) continue;              // tile entirely after the diagonal (j > i)
+      const f32x4 cbt = mm_rows<N, NP, NP>(zero4(), s_b + 16 * tj * NP, s_c + 16 * w * NP, r, qd);
+      const f32x4 dxt = mm_rows<P, PP, PP>(zero4(), s_x + 16 * tj * PP, s_dy + 16 * w * PP, r, qd);
+      f32x4 wt;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int j = tc + 16 * m;
-        const bool ok = (R * KT + i >= J * KT + j) && i < lenR && j < lenJ;
-        const float w = ok ? expf(s_SR[i] - s_SJ[j]) * s_dJ[j] * dxv[r][m] : 0.f;
-        rs[r] += w * cb[r][m];
-        s_w[i * KP + j] = w;
+      for (int e = 0; e < 4; ++e) {
+        const int jl = 16 * tj + 4 * qd + e;
+        const bool ok = (R * KT + il >= J * KT + jl) && il < lenR && jl < lenJ;
+        wt[e] = ok ? expf(si - s_SJ[jl]) * s_dJ[jl] * dxt[e] : 0.f;
+        rs += wt[e] * cbt[e];
       }
+#pragma unroll
+      for (int m = 0; m < TNm; ++m) dc[m] = mm_regs<NP>(dc[m], wt, s_b + 16 * tj * NP, 16 * m, r, qd);
     }
-    __syncthreads();
-    acc_nn<KT, KP, N>(dc, s_w, s_b, tr, tc);  // dc[i][n] += sum_j w[i][j] B[j][n]
   }
   __syncthreads();
   stage_state<P, N>(s_b, states + (((size_t)b * nc + c) * H + h) * (size_t)(P * N), tid);
   __syncthreads();
-  float cr[4][TNm];
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int m = 0; m < TNm; ++m) cr[r][m] = 0.f;
-  acc_nn<P, PP, N>(cr, s_dy, s_b, tr, tc);   // cr[i][n] = sum_p dy[i][p] Hprev[p][n]
+  // lane rows i = 16 w + 4 qd + e from here on
   const size_t row0 = (size_t)b * L + t0 + R * KT;
+  float rr[4] = {0.f, 0.f, 0.f, 0.f}, ei[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int i = 4 * tr + r;
-    const float ei = expf(s_SR[i]);
-    float rr = 0.f;
+  for (int e = 0; e < 4; ++e) ei[e] = expf(s_SR[16 * w + 4 * qd + e]);
 #pragma unroll
-    for (int m = 0; m < TNm; ++m) rr += cr[r][m] * s_c[i * NP + tc + 16 * m];
-    rr = ei * sum16(rr);
-    const float rsum = sum16(rs[r]);
+  for (int m = 0; m < TNm; ++m) {
+    // cr[i][n] = sum_p dy[i][p] Hprev[p][n]
+    const f32x4 cr = mm_cols<P, PP, NP>(zero4(), s_dy + 16 * w * PP, s_b, 16 * m, r, qd);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * w + 4 * qd + e;
+      rr[e] += cr[e] * s_c[i * NP + 16 * m + r];
+      dc[m][e] += ei[e] * cr[e];
+    }
+  }
+  const float rsum = sum_qd(rs);                   // row il
+  float* s_rr = s_x;                               // x of J no longer needed
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = 16 * w + 4 * qd + e;
+    const float rv = ei[e] * sum_r(rr[e]);
+    if (r == 0) s_rr[i] = rv;
     if (i < lenR) {
       const size_t tok = row0 + i;
 #pragma unroll
-      for (int m = 0; m < TNm; ++m) dCh[(tok * H + h) * (size_t)N + tc + 16 * m] = dc[r][m] + ei * cr[r][m];
-      if (tc == 0) dSc[cq + R * KT + i] = rsum + rr;
+      for (int m = 0; m < TNm; ++m) dCh[(tok * H + h) * (size_t)N + 16 * m + r] = dc[m][e];
     }
   }
+  __syncthreads();
+  if (qd == 0 && il < lenR) dSc[cq + R * KT + il] = rsum + s_rr[il];
 }
 
 // ------------------------------------------------------------------ per-chunk finalize

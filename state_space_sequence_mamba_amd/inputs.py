@@ -30,7 +30,7 @@ DT_MAX = 1e-1
 @dataclass(frozen=True)
 class Workload:
     name: str
-    entry: str            # "fwd", "step" or "conv"
+    entry: str            # "fwd", "bwd", "step" or "conv"
     dtype: str            # "f32" or "bf16" (x, dt, B, C, y)
     batch: int
     nheads: int
@@ -62,6 +62,11 @@ WORKLOADS = {w.name: w for w in [
              steps=1000),
     Workload("ssd_fwd bf16 B2 L16384 H80 P64 N128 G8 Q256", "fwd", "bf16", 2, 80, 64, 128, 8, 4, "normal",
              seqlen=16384, chunk=256),
+    # the backward of the two forward workloads above (same inputs, seeded upstream gradients)
+    Workload("ssd_bwd f32 B4 L1024 H24 P64 N64 G1 Q256", "bwd", "f32", 4, 24, 64, 64, 1, 1, "ones",
+             seqlen=1024, chunk=256),
+    Workload("ssd_bwd bf16 B8 L4096 H32 P64 N128 G1 Q256", "bwd", "bf16", 8, 32, 64, 128, 1, 2, "normal",
+             seqlen=4096, chunk=256),
     # the conv in front of the scan, on the channels of the B8 L4096 bf16 forward (Dc 2304)
     Workload("conv1d_silu bf16 B8 L4096 H32 P64 N128 G1 K4", "conv", "bf16", 8, 32, 64, 128, 1, 5, "ones",
              seqlen=4096, width=4),
@@ -133,8 +138,17 @@ def make_conv_inputs(batch, seqlen, nheads, headdim, dstate, ngroups, width=4, d
     return {k: (None if v is None else v.to(device)) for k, v in out.items()}
 
 
+def make_upstream_grads(batch, seqlen, nheads, headdim, dstate, dtype="f32", seed=0, device="cpu"):
+    """Upstream gradients of one ssd_fwd call: dout (B, L, H, P) in `dtype` and dfinal
+    (B, H, P, N) fp32, both N(0, 1), from their own CPU generator."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    dout = torch.randn(batch, seqlen, nheads, headdim, generator=g).to(_torch_dtype(dtype))
+    dfin = torch.randn(batch, nheads, headdim, dstate, generator=g)
+    return dout.to(device), dfin.to(device)
+
+
 def make_workload_inputs(w, device="cpu"):
-    if w.entry != "fwd":
+    if w.entry not in ("fwd", "bwd"):
         raise ValueError("use make_step_inputs for decode workloads")
     return make_fwd_inputs(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups,
                            w.dtype, w.seed, w.d_init, device)

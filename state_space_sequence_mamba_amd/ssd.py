@@ -54,9 +54,12 @@ def load_library():
     lib.ssd_step.restype = i32
     lib.ssd_bwd_workspace_size.argtypes = [dims_p, i32, i32]
     lib.ssd_bwd_workspace_size.restype = sz
-    lib.ssd_bwd.argtypes = [dims_p, vp, vp, f32p, f32p, vp, vp, f32p, vp, i32, f32p, vp, f32p,
-                            vp, vp, f32p, f32p, vp, vp, f32p, vp, f32p, vp, sz, vp]
+    bwd_args = [dims_p, vp, vp, f32p, f32p, vp, vp, f32p, vp, i32, f32p, vp, f32p,
+                vp, vp, f32p, f32p, vp, vp, f32p, vp, f32p, vp, sz, vp]
+    lib.ssd_bwd.argtypes = bwd_args
     lib.ssd_bwd.restype = i32
+    lib.ssd_bwd_timed.argtypes = bwd_args + [vp]
+    lib.ssd_bwd_timed.restype = i32
     lib.ssd_conv1d_silu.argtypes = [dims_p, i32, vp, f32p, f32p, vp, vp, vp, vp, vp, vp]
     lib.ssd_conv1d_silu.restype = i32
     lib.ssd_conv1d_silu_step.argtypes = [dims_p, i32, vp, vp, f32p, f32p, vp, vp, vp, vp]
@@ -190,9 +193,12 @@ def ssd_bwd_workspace_size(dims, chunk_size, with_gate=False):
 
 
 def ssd_bwd(x, dt, dt_bias, A, B, C, dout, D=None, chunk_size=256, initial_state=None, dfinal_state=None,
-            z=None, dt_limit=None, want_dD=True, want_dinitial_state=True, workspace=None, stream=None):
+            z=None, dt_limit=None, want_dD=True, want_dinitial_state=True, workspace=None, stream=None,
+            out=None, stage_events=None):
     """Gradients of ssd_fwd.  Returns a dict: dx, ddt, ddt_bias, dA, dB, dC, dD, dz, dinitial_state
-    (dD / dz / dinitial_state are None when not requested or not applicable)."""
+    (dD / dz / dinitial_state are None when not requested or not applicable).  `out` reuses a
+    previous call's dict as the output buffers; `stage_events` (12 raw hipEvent_t handles as
+    ints) selects the timed entry point."""
     b, L, H, P, N, G = _check_fwd_shapes(x, dt, dt_bias, A, B, C, D, initial_state, z)
     if tuple(dout.shape) != tuple(x.shape) or dout.dtype != x.dtype or not dout.is_contiguous():
         raise ValueError("dout must be a contiguous tensor shaped and typed like x")
@@ -201,19 +207,25 @@ def ssd_bwd(x, dt, dt_bias, A, B, C, dout, D=None, chunk_size=256, initial_state
         raise ValueError("dfinal_state must be a contiguous (B, H, P, N) float32 tensor")
     dims = make_dims(b, L, H, P, N, G, x.dtype, dt_limit)
     f32 = dict(dtype=torch.float32, device=x.device)
-    out = {"dx": torch.empty_like(x), "ddt": torch.empty_like(dt), "ddt_bias": torch.empty(H, **f32),
-           "dA": torch.empty(H, **f32), "dB": torch.empty_like(B), "dC": torch.empty_like(C),
-           "dD": torch.empty(H, P, **f32) if want_dD else None,
-           "dz": torch.empty_like(z) if z is not None else None,
-           "dinitial_state": torch.empty(b, H, P, N, **f32) if want_dinitial_state else None}
+    if out is None:
+        out = {"dx": torch.empty_like(x), "ddt": torch.empty_like(dt), "ddt_bias": torch.empty(H, **f32),
+               "dA": torch.empty(H, **f32), "dB": torch.empty_like(B), "dC": torch.empty_like(C),
+               "dD": torch.empty(H, P, **f32) if want_dD else None,
+               "dz": torch.empty_like(z) if z is not None else None,
+               "dinitial_state": torch.empty(b, H, P, N, **f32) if want_dinitial_state else None}
     ws_bytes = ssd_bwd_workspace_size(dims, chunk_size, z is not None)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
-    st = load_library().ssd_bwd(
+    lib = load_library()
+    args = [
         ctypes.byref(dims), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
         int(chunk_size), _ptr(initial_state), _ptr(dout), _ptr(dfinal_state), _ptr(out["dx"]), _ptr(out["ddt"]),
         _ptr(out["ddt_bias"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]),
-        _ptr(out["dinitial_state"]), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+        _ptr(out["dinitial_state"]), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)]
+    if stage_events is None:
+        st = lib.ssd_bwd(*args)
+    else:
+        st = lib.ssd_bwd_timed(*args, (ctypes.c_void_p * 12)(*stage_events))
     if st != SSD_OK:
         raise SsdError(st, "ssd_bwd")
     return out

@@ -163,3 +163,49 @@ def test_bwd_full_length_bf16_one_row():
     dout, dfin = _upstream(1, w.seqlen, H, w.headdim, w.dstate, "bf16", seed=241)
     got = _run(inp, w.chunk, dout, dfin)
     _compare(got, _oracle(inp, dout, dfin), TOL["bf16"])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_graph_replay_and_timed_entry_match_eager(dtype):
+    """ssd_bwd captured into a HIP graph gives the eager result on every replay; the timed entry
+    point gives the same result and refuses a capturing stream."""
+    from state_space_sequence_mamba_amd.timing import HipEvents
+    _say(f"bwd graph + timed {dtype}")
+    N = 64 if dtype == "f32" else 128
+    inp = {k: v.to(DEV) for k, v in I.make_fwd_inputs(2, 500, 8, 64, N, 2, dtype, seed=250).items()}
+    dout, dfin = (t.to(DEV) for t in _upstream(2, 500, 8, 64, N, dtype, seed=251))
+    args = (inp["x"], inp["dt"], inp["dt_bias"], inp["A"], inp["B"], inp["C"], dout)
+    ref = ssd.ssd_bwd(*args, D=inp["D"], chunk_size=128, dfinal_state=dfin)
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in ref.items() if v is not None}
+    out = ssd.ssd_bwd(*args, D=inp["D"], chunk_size=128, dfinal_state=dfin)
+    dims = ssd.make_dims(2, 500, 8, 64, N, 2, inp["x"].dtype)
+    ws = torch.empty(ssd.ssd_bwd_workspace_size(dims, 128), dtype=torch.uint8, device=DEV)
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=cap):
+        ssd.ssd_bwd(*args, D=inp["D"], chunk_size=128, dfinal_state=dfin, workspace=ws, out=out)
+    for rep in range(3):
+        for v in out.values():
+            if v is not None:
+                v.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, v in ref.items():
+            assert torch.equal(out[k], v), (rep, k)
+    hev = HipEvents()
+    evs = [hev.create() for _ in range(12)]
+    timed = ssd.ssd_bwd(*args, D=inp["D"], chunk_size=128, dfinal_state=dfin, stage_events=evs)
+    torch.cuda.synchronize()
+    for k, v in ref.items():
+        assert torch.equal(timed[k], v), k
+    assert all(hev.elapsed_ms(evs[i], evs[i + 1]) >= 0.0 for i in range(11))
+    g2 = torch.cuda.CUDAGraph()
+    with pytest.raises(ssd.SsdError) as ei:
+        with torch.cuda.graph(g2, stream=cap):
+            ssd.ssd_bwd(*args, D=inp["D"], chunk_size=128, dfinal_state=dfin, workspace=ws, out=out,
+                        stage_events=evs)
+    assert ei.value.status == ssd.SSD_ERR_UNSUPPORTED
+    hev.close()
