@@ -1,8 +1,10 @@
 """Benchmark of the SSD hot path on one MI355X.
 
 One step = one pass of the whole path over one batch: ssd_fwd over the prefill batch
-(chunk_cumsum -> chunk_state -> state_passing -> chunk_scan), writing final_state, then
-one ssd_step decode token per sequence continuing from that state.  Workload: the fp32
+(chunk_state with the dt' cumsum and, for fp32, C B^T once per group -> state_passing ->
+chunk_scan), writing final_state, then one ssd_step decode token per sequence continuing
+from that state.  Other workloads (--workload): the backward (ssd_bwd), the decode loop and
+the conv1d + SiLU in front of the scan.  Workload: the fp32
 forward of batch 4 x 1024 tokens, 24 heads, headdim 64, dstate 64, 1 group, chunk 256
 (plus its decode token).  Inputs are seeded synthetic tensors resident in HBM before the
 timed region.  Prints ONE JSON line.
@@ -29,7 +31,7 @@ from state_space_sequence_mamba_amd.timing import HipEvents  # noqa: E402
 HBM_PEAK_GBS = 8000.0                         # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}   # dense matrix peaks, TFLOP/s
 DEFAULT_WORKLOAD = "ssd_fwd f32 B4 L1024 H24 P64 N64 G1 Q256"
-KERNELS = ["chunk_cumsum", "chunk_state", "state_passing", "chunk_scan", "ssd_step"]
+KERNELS = ["chunk_state", "state_passing", "chunk_scan", "ssd_step"]
 
 
 def algorithmic_cost(w):
@@ -45,12 +47,19 @@ def algorithmic_cost(w):
     x = B * L * H * P * e
     bc = B * L * G * N * e
     tri = sum(n * (n + 1) // 2 for n in lens)           # causal (i, j) pairs per (b, h) sequence
+    pre = w.dtype == "f32"
+    nrb = Q // 64
+    cbw = B * nc * G * (nrb * (nrb + 1) // 2) * 16 * 1024     # C B^T blocks written (16 KB each)
+    cbr = cbw * (H // G)                                        # ... and read once per head
     cost = {
-        "chunk_cumsum": dict(bytes=B * L * H * e + cum + 8 * H, flops=0),
-        "chunk_state": dict(bytes=x + bc + cum + st, flops=2 * B * H * L * P * N),
+        # dt' and its cumsum (dt in, both out), the chunk states; fp32 adds C B^T once per group
+        # (C in, 16 KB blocks out, one per row block and causal column block)
+        "chunk_state": dict(bytes=B * L * H * e + 8 * H + cum + x + bc + st + ((bc + cbw) if pre else 0),
+                            flops=2 * B * H * L * P * N + (2 * B * G * N * tri if pre else 0)),
         "state_passing": dict(bytes=2 * st + fin + B * H * nc * 4, flops=2 * B * nc * H * P * N),
-        "chunk_scan": dict(bytes=2 * x + 2 * bc + cum + st + H * P * 4,
-                           flops=2 * B * H * P * tri + 2 * B * H * L * N * P + 2 * B * G * N * tri),
+        # fp32 reads the C B^T blocks back once per head; bf16 forms C B^T inside chunk_scan
+        "chunk_scan": dict(bytes=2 * x + (cbr if pre else 2 * bc) + cum + st + H * P * 4,
+                           flops=2 * B * H * P * tri + 2 * B * H * L * N * P + (0 if pre else 2 * B * G * N * tri)),
         # decode: state read + write, x, y, dt, B, C
         "ssd_step": dict(bytes=2 * fin + 2 * B * H * P * e + B * H * e + 2 * B * G * N * e,
                          flops=4 * B * H * P * N),
@@ -143,7 +152,7 @@ def run_decode(w, args, dev):
     print(json.dumps(out), flush=True)
 
 
-BWD_STAGES = ["chunk_cumsum", "chunk_state", "state_passing", "gate_fwd", "gate_bwd", "chunk_state_grad",
+BWD_STAGES = ["chunk_state", "state_passing", "gate_fwd", "gate_bwd", "chunk_state_grad",
               "state_passing_rev", "bwd_dxdb", "bwd_dc", "bwd_finalize", "bwd_reduce"]
 
 
@@ -161,10 +170,8 @@ def backward_cost(w):
     x = B * L * H * P * e
     bc = B * L * G * N * e
     perh = B * L * H * N * 4
-    fwd = algorithmic_cost(w)
     cost = {
-        "chunk_cumsum": fwd["chunk_cumsum"],
-        "chunk_state": fwd["chunk_state"],
+        "chunk_state": dict(bytes=B * L * H * e + 8 * H + cum + x + bc + st, flops=2 * B * H * L * P * N),
         "state_passing": dict(bytes=2 * st + B * H * nc * 4, flops=2 * B * nc * H * P * N),
         "gate_fwd": dict(bytes=0, flops=0),
         "gate_bwd": dict(bytes=0, flops=0),
@@ -229,7 +236,7 @@ def run_bwd(w, args, dev):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms = hev.elapsed_ms(t0, t1) / K
-    events = [[hev.create() for _ in range(12)] for _ in range(K)]
+    events = [[hev.create() for _ in range(11)] for _ in range(K)]
     for i in range(K):
         step(events[i])
     torch.cuda.synchronize()
@@ -398,19 +405,19 @@ def main():
     K, W = args.steps, args.warmup
     use_graph = not args.no_graph
     hev = HipEvents()
-    nev = 7   # 5 around the forward's kernels, 2 around ssd_step
+    nev = 6   # 4 around the forward's kernels, 2 around ssd_step
     events = [[hev.create() for _ in range(nev)] for _ in range(max(K, 1))]
     t_start, t_end = hev.create(), hev.create()
 
     def step(evs=None):
         # launches go to the current stream (the capture stream while a graph is captured)
         ssd.ssd_fwd(d["x"], d["dt"], d["dt_bias"], d["A"], d["B"], d["C"], d["D"], chunk_size=w.chunk,
-                    y=y, final_state=state, workspace=ws, stage_events=None if evs is None else evs[:5])
+                    y=y, final_state=state, workspace=ws, stage_events=None if evs is None else evs[:4])
         if evs is not None:
-            hev.record(evs[5])
+            hev.record(evs[4])
         ssd.ssd_step(state, dd["x"], dd["dt"], d["dt_bias"], d["A"], dd["B"], dd["C"], d["D"], y=y_dec)
         if evs is not None:
-            hev.record(evs[6])
+            hev.record(evs[5])
 
     for _ in range(W):
         step()
@@ -444,7 +451,7 @@ def main():
     torch.cuda.synchronize()
 
     per_kernel_ms = {k: 0.0 for k in KERNELS}
-    pairs = [(0, 1), (1, 2), (2, 3), (3, 4), (5, 6)]
+    pairs = [(0, 1), (1, 2), (2, 3), (4, 5)]
     for evs in events[:K]:
         for k, (a, b) in zip(KERNELS, pairs):
             per_kernel_ms[k] += hev.elapsed_ms(evs[a], evs[b]) / K
@@ -454,6 +461,8 @@ def main():
     for k in KERNELS:
         t = per_kernel_ms[k] * 1e-3
         c = cost[k]
+        if c["bytes"] == 0 and c["flops"] == 0:       # not launched for this dtype
+            continue
         if c["bound"] == "mfma":
             ach, peak, unit = c["flops"] / t / 1e12, MFMA_PEAK_TFLOPS[w.dtype], "TFLOP/s"
         else:
@@ -461,7 +470,7 @@ def main():
         kernels[k] = {"us": round(per_kernel_ms[k] * 1e3, 3), "bound": c["bound"], "achieved": round(ach, 2),
                       "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
                       "alg_bytes": c["bytes"], "alg_flops": c["flops"]}
-    dom = max(KERNELS, key=lambda k: per_kernel_ms[k])
+    dom = max(kernels, key=lambda k: per_kernel_ms[k])
     kd = kernels[dom]
     # measured HBM bytes per launch of the dominant kernel (FETCH_SIZE + WRITE_SIZE runs,
     # calibrated on a plain copy); None when absent or taken on different kernel sources

@@ -72,18 +72,22 @@ typedef struct {
 /* Bytes of device workspace ssd_fwd needs for these sizes and chunk size; 0 when the
  * arguments are invalid or unsupported.  Pure host arithmetic.  Layout (each region
  * 256-byte aligned, nc = ceil(L / chunk_size)):
- *   [0] dt'  (B, H, nc, chunk_size) fp32   softplus(dt + dt_bias); 0 past the end of the sequence
+ *   [0] dt'  (B, H, nc, chunk_size) fp32   softplus(dt + dt_bias) (clamped if asked); 0 past the end
  *   [1] dAcs (B, H, nc, chunk_size) fp32   inclusive in-chunk cumulative sum of dt' * A
  *   [2] states (B, nc, H, P, N) fp32       first the state each chunk contributes (decayed to
  *                                          the chunk end), then overwritten in place by the
  *                                          state entering each chunk
+ *   [3] SSD_F32 only: C B^T, computed once per group, (B, nc, G, nrb (nrb + 1) / 2) blocks of
+ *       16 x 256 fp32, nrb = chunk_size / 64: the causal 16 x 16 sub-tiles of each pair of
+ *       64-row blocks (row block rb, column block J <= rb), in the scan's register order
  * The contents after a call are those intermediates and may be inspected. */
 size_t ssd_fwd_workspace_size(const ssd_dims_t* dims, int chunk_size);
 
 /* Chunked SSD forward over a whole sequence (the chunked diagonal-block / carried-state
  * evaluation of the reference-comparison page, section 3.2, and of Gap 1 of the
- * implementation-gaps page).  Four kernels run in order on `stream`: chunk_cumsum,
- * chunk_state, state_passing, chunk_scan.
+ * implementation-gaps page).  Three kernels run in order on `stream`: chunk_state (dt', its
+ * in-chunk cumsum and the chunk states; for SSD_F32 also C B^T once per group),
+ * state_passing, chunk_scan.
  *   x             (B, L, H, P)  dtype       input sequence
  *   dt            (B, L, H)     dtype       raw step, before bias and softplus
  *   dt_bias, A    (H)           fp32        A is used as given (pass negative values)
@@ -103,9 +107,9 @@ ssd_status_t ssd_fwd(const ssd_dims_t* dims,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ssd_fwd with per-kernel timing: identical arguments and results, plus `stage_events`,
- * an array of 5 events created by the caller (hipEventCreate).  stage_events[k] is
- * recorded on `stream` just before kernel k (0 chunk_cumsum, 1 chunk_state,
- * 2 state_passing, 3 chunk_scan) and stage_events[4] after the last one.  Event records
+ * an array of 4 events created by the caller (hipEventCreate).  stage_events[k] is
+ * recorded on `stream` just before kernel k (0 chunk_state, 1 state_passing, 2 chunk_scan)
+ * and stage_events[3] after the last one.  Event records
  * cannot be captured into a graph: with non-NULL stage_events on a stream under capture the
  * call returns SSD_ERR_UNSUPPORTED and launches nothing.  For measurement tools; NULL
  * stage_events behaves exactly like ssd_fwd (which may be captured). */
@@ -151,7 +155,7 @@ size_t ssd_bwd_workspace_size(const ssd_dims_t* dims, int chunk_size, int with_g
  * ddt is the gradient with respect to the raw dt (before bias and softplus); it is zero where
  * the clamp binds.  Results are deterministic (fixed-order reductions, no atomics).
  * batch == 0 is a no-op; seqlen == 0 writes dinitial_state = dfinal_state (or zeros) and zero
- * ddt_bias, dA, dD.  Thirteen kernels (fifteen with a gate). */
+ * ddt_bias, dA, dD.  Nine kernels (two more with a gate). */
 ssd_status_t ssd_bwd(const ssd_dims_t* dims,
                      const void* x, const void* dt, const float* dt_bias, const float* A,
                      const void* B, const void* C, const float* D, const void* z, int chunk_size,
@@ -161,11 +165,11 @@ ssd_status_t ssd_bwd(const ssd_dims_t* dims,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ssd_bwd with per-kernel timing: identical arguments and results, plus `stage_events`, an
- * array of 12 caller-created events recorded on `stream` before each stage: 0 chunk_cumsum,
- * 1 chunk_state, 2 state_passing (forward recompute), 3 chunk_scan of the pre-gate output and
- * 4 the gate's backward (both empty without a gate), 5 chunk_state of the output gradients,
- * 6 reverse state_passing, 7 the anti-causal kernel, 8 the causal kernel, 9 finalize,
- * 10 reductions, and 11 after the last.  Like ssd_fwd_timed it refuses a stream under graph
+ * array of 11 caller-created events recorded on `stream` before each stage: 0 chunk_state,
+ * 1 state_passing (forward recompute), 2 chunk_scan of the pre-gate output and 3 the gate's
+ * backward (both empty without a gate), 4 chunk_state of the output gradients, 5 reverse
+ * state_passing, 6 the anti-causal kernel, 7 the causal kernel, 8 finalize, 9 reductions,
+ * and 10 after the last.  Like ssd_fwd_timed it refuses a stream under graph
  * capture (SSD_ERR_UNSUPPORTED, nothing launched). */
 ssd_status_t ssd_bwd_timed(const ssd_dims_t* dims,
                            const void* x, const void* dt, const float* dt_bias, const float* A,

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libssd.so")
 
-SOURCES = ["ssd_api.hip", "chunk_cumsum.hip", "chunk_state.hip", "state_passing.hip", "chunk_scan.hip",
+SOURCES = ["ssd_api.hip", "chunk_state.hip", "state_passing.hip", "chunk_scan.hip",
            "ssd_step.hip", "conv1d.hip", "ssd_bwd.hip"]
 ARCH = "gfx950"
 FLAGS = [

@@ -33,6 +33,7 @@
 // MFMA: fp32 inputs -> v_mfma_f32_16x16x4_f32 for all three products; bf16 inputs ->
 // 16x16x32 bf16 for C B^T and C Hprev^T, 16x16x16 bf16 for (L o CB) X.  Decay factors use
 // the hardware base-2 exponential on log2(e)-scaled cumsums; factors below 2^-126 become 0.
+#include "cb_tiles.h"
 #include "ssd_common.h"
 #include "ssd_launch.h"
 
@@ -49,7 +50,8 @@ struct ScanLds {
   static constexpr int BP = N + (F32 ? 4 : 8);   // B tile / Hprev rows (n-contiguous), 16-byte rows
   static constexpr int XP = kKT + 4;              // x^T rows (token-contiguous)
   static constexpr int YP = P + (F32 ? 4 : 8);   // y staging rows
-  static constexpr int B_ELEMS = kKT * BP;
+  // B tile, or (fp32) the 16 KB block of precomputed C B^T sub-tiles that replaces it
+  static constexpr int B_ELEMS = (F32 && 16 * 256 > kKT * BP) ? 16 * 256 : kKT * BP;
   static constexpr int X_ELEMS = HB * P * XP;
   static constexpr int PREV_ELEMS = P * BP;
   static constexpr int XU_ELEMS = X_ELEMS > PREV_ELEMS ? X_ELEMS : PREV_ELEMS;  // x tiles alias Hprev
@@ -58,58 +60,18 @@ struct ScanLds {
   static constexpr int TOTAL = MAIN > Y_ELEMS ? MAIN : Y_ELEMS;
 };
 
-// Contraction over dstate of two n-contiguous rows.
-template <typename T, int N> struct NDot;
-template <int N> struct NDot<float, N> {
-  static constexpr int NF = N / 4;                // k values per lane: n = (N/4) qd + kk
-  typedef float frag[NF];
-  __device__ static __forceinline__ void load(frag f, const float* row, int qd, bool ok = true) {
-    const float* p = row + (N / 4) * qd;
-#pragma unroll
-    for (int m = 0; m < NF / 4; ++m) {
-      const float4 v = *reinterpret_cast<const float4*>(p + 4 * m);
-      f[4 * m + 0] = ok ? v.x : 0.f;
-      f[4 * m + 1] = ok ? v.y : 0.f;
-      f[4 * m + 2] = ok ? v.z : 0.f;
-      f[4 * m + 3] = ok ? v.w : 0.f;
-    }
-  }
-  __device__ static __forceinline__ f32x4 dot(const frag a, const frag b, f32x4 c) {
-#pragma unroll
-    for (int k = 0; k < NF; ++k) c = mfma_16x16x4_f32(a[k], b[k], c);
-    return c;
-  }
-};
-template <int N> struct NDot<__bf16, N> {
-  static constexpr int NF = N / 32;               // 16x16x32 instructions: n = 32 k + 8 qd + e
-  typedef bf16x8 frag[NF];
-  __device__ static __forceinline__ void load(frag f, const __bf16* row, int qd, bool ok = true) {
-#pragma unroll
-    for (int k = 0; k < NF; ++k) {
-      uint4 v = *reinterpret_cast<const uint4*>(row + 32 * k + 8 * qd);
-      v.x = ok ? v.x : 0u;
-      v.y = ok ? v.y : 0u;
-      v.z = ok ? v.z : 0u;
-      v.w = ok ? v.w : 0u;
-      f[k] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
-  __device__ static __forceinline__ f32x4 dot(const frag a, const frag b, f32x4 c) {
-#pragma unroll
-    for (int k = 0; k < NF; ++k) c = mfma_16x16x32_bf16(a[k], b[k], c);
-    return c;
-  }
-};
-
 // One 64-token tile of B rows and of x for every head of the block, held in registers
 // between its global loads and its LDS stores.  Loads read clamped in-bounds addresses and
 // only record which tokens are real; the zeroing selects happen at store time, so nothing
 // waits for the loads until the tile is written to LDS (after the current tile's MFMAs).
-template <typename T, int P, int N, int HB, int NTHR>
+// PRECB: instead of B rows, the tile is the 16 KB block of precomputed C B^T sub-tiles of
+// (row block, column tile J), copied as is (cb_block writes it in the lane order used here).
+
+template <typename T, int P, int N, int HB, int NTHR, bool PRECB = false>
 struct TileRegs {
   static constexpr int VEC = Vec16<T>::n;
   static constexpr int NVR = N / VEC, PV = P / VEC;
-  static constexpr int BU = kKT * NVR;                 // 16-byte vectors of B
+  static constexpr int BU = PRECB ? kCbBlock / 4 : kKT * NVR;   // 16-byte vectors of B (or C B^T)
   static constexpr int XU = HB * (kKT / 2) * PV;       // token-pair units of x
   static constexpr int BPT = (BU + NTHR - 1) / NTHR, XPT = (XU + NTHR - 1) / NTHR;
   static_assert(BPT + 2 * XPT <= 32, "validity mask");
@@ -123,11 +85,16 @@ struct TileRegs {
 #pragma unroll
     for (int u = 0; u < BPT; ++u) {
       const int v = min(tid + NTHR * u, BU - 1);
-      const int i = v / NVR, nv = (v % NVR) * VEC;
-      const int tok = J * kKT + i;
-      const bool ok = tok < len;
-      b[u] = load16(Bb + (uint32_t)(ok ? tok : 0) * bc_tok + nv);
-      okm |= (uint32_t)ok << u;
+      if (PRECB) {
+        b[u] = load16(Bb + (size_t)J * kCbBlock + 4 * v);
+        okm |= 1u << u;
+      } else {
+        const int i = v / NVR, nv = (v % NVR) * VEC;
+        const int tok = J * kKT + i;
+        const bool ok = tok < len;
+        b[u] = load16(Bb + (uint32_t)(ok ? tok : 0) * bc_tok + nv);
+        okm |= (uint32_t)ok << u;
+      }
     }
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {
@@ -149,8 +116,12 @@ struct TileRegs {
     for (int u = 0; u < BPT; ++u) {
       const int v = tid + NTHR * u;
       if (v < BU) {
-        const int i = v / NVR, nv = (v % NVR) * VEC;
-        *reinterpret_cast<Vec16<T>*>(&s_b[i * BP + nv]) = keep_if(b[u], (okm >> u) & 1u);
+        if (PRECB) {
+          *reinterpret_cast<Vec16<T>*>(&s_b[4 * v]) = b[u];
+        } else {
+          const int i = v / NVR, nv = (v % NVR) * VEC;
+          *reinterpret_cast<Vec16<T>*>(&s_b[i * BP + nv]) = keep_if(b[u], (okm >> u) & 1u);
+        }
       }
     }
 #pragma unroll
@@ -213,20 +184,26 @@ __device__ __forceinline__ void carried_term(f32x4 (&acc)[TPof<P>::v], const typ
 // One causal 16x16 sub-tile (column tile jt, local index js in the staged tile) of one strip,
 // for every head of the block.  EDGE: the sub-tile may be the diagonal one, whose columns past
 // the diagonal are masked and which adds the skip term.
-template <typename T, int P, int N, int HB, int BP, int XP, bool EDGE>
+template <typename T, int P, int N, int HB, int BP, int XP, bool EDGE, bool PRECB>
 __device__ __forceinline__ void sub_tile(f32x4 (&acc)[HB][TPof<P>::v], const typename NDot<T, N>::frag& cf,
                                          const float (&dco)[HB][TPof<P>::v], const T* s_b, const T* s_x,
                                          const float (*s_da)[256], const float (*s_dt)[256], int strip, int jt,
-                                         int js, int r, int qd) {
+                                         int js, int lstrip, int r, int qd) {
   typedef NDot<T, N> ND;
   constexpr int TP = P / 16;
   constexpr bool F32 = sizeof(T) == 4;
   const int i_row = 16 * strip + r;
   const bool diag = EDGE && jt == strip;
   // CB^T sub-tile: lane holds CB[i = 16 strip + r][j = 16 jt + 4 qd + e]
-  typename ND::frag bfr;
-  ND::load(bfr, &s_b[(js * 16 + r) * BP], qd);
-  const f32x4 cbt = ND::dot(bfr, cf, zero4());
+  f32x4 cbt;
+  if constexpr (PRECB) {
+    cbt = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(s_b) +
+                                          ((lstrip * 4 + js) * 64 + r + 16 * qd) * 4);
+  } else {
+    typename ND::frag bfr;
+    ND::load(bfr, &s_b[(js * 16 + r) * BP], qd);
+    cbt = ND::dot(bfr, cf, zero4());
+  }
   const int j0 = 16 * jt + 4 * qd;
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) {
@@ -279,16 +256,16 @@ __device__ __forceinline__ void sub_tile(f32x4 (&acc)[HB][TPof<P>::v], const typ
 
 // Diagonal-block contributions of staged tile J to one strip: its causal sub-tiles, the one
 // on the diagonal masked and carrying the skip term.
-template <typename T, int P, int N, int HB, int BP, int XP>
+template <typename T, int P, int N, int HB, int BP, int XP, bool PRECB = false>
 __device__ __forceinline__ void diag_tile(f32x4 (&acc)[HB][TPof<P>::v], const typename NDot<T, N>::frag& cf,
                                           const float (&dco)[HB][TPof<P>::v], const T* s_b, const T* s_x,
                                           const float (*s_da)[256], const float (*s_dt)[256], int strip, int J,
-                                          int r, int qd) {
+                                          int lstrip, int r, int qd) {
 #pragma unroll
   for (int js = 0; js < 4; ++js) {
     const int jt = 4 * J + js;
     if (jt > strip) break;
-    sub_tile<T, P, N, HB, BP, XP, true>(acc, cf, dco, s_b, s_x, s_da, s_dt, strip, jt, js, r, qd);
+    sub_tile<T, P, N, HB, BP, XP, true, PRECB>(acc, cf, dco, s_b, s_x, s_da, s_dt, strip, jt, js, lstrip, r, qd);
   }
 }
 
@@ -355,6 +332,7 @@ __device__ __forceinline__ void load_chunk_scalars(float (*s_da)[256], float (*s
 template <typename T, int P, int N, int HB>
 __global__ __launch_bounds__(256, 2) void chunk_scan_rows_kernel(const T* __restrict__ x,
                                                                  const T* __restrict__ Bm,
+                                                                 const float* __restrict__ cbp,
                                                                  const T* __restrict__ Cm,
                                                                  const float* __restrict__ dtp,
                                                                  const float* __restrict__ dAcs,
@@ -406,10 +384,15 @@ __global__ __launch_bounds__(256, 2) void chunk_scan_rows_kernel(const T* __rest
 
   const size_t bc_tok = (size_t)G * N, x_tok = (size_t)H * P;
   const T* Cb = Cm + ((size_t)b * L + t0) * bc_tok + (size_t)g * N;
-  const T* Bb = Bm + ((size_t)b * L + t0) * bc_tok + (size_t)g * N;
+  // fp32: the C B^T sub-tiles of this row block come precomputed (once per group) by cb_block
+  constexpr bool PRECB = sizeof(T) == 4;
+  const T* Bb = PRECB ? reinterpret_cast<const T*>(cbp + (((size_t)b * nc + c) * G + g) *
+                                                             (size_t)(nrb * (nrb + 1) / 2) * kCbBlock +
+                                                   (size_t)(rb * (rb + 1) / 2) * kCbBlock)
+                      : Bm + ((size_t)b * L + t0) * bc_tok + (size_t)g * N;
   const T* xb = x + ((size_t)b * L + t0) * x_tok + (size_t)h0 * P;
 
-  TileRegs<T, P, N, HB, NTHR> tr;
+  TileRegs<T, P, N, HB, NTHR, PRECB> tr;
   tr.load(Bb, xb, (uint32_t)bc_tok, (uint32_t)x_tok, 0, len, tid);
   load_chunk_scalars<HB>(s_da, s_dt, dtp, dAcs, b, H, h0, nc, c, Q, tid, NTHR);
   typename ND::frag cf;
@@ -441,7 +424,8 @@ __global__ __launch_bounds__(256, 2) void chunk_scan_rows_kernel(const T* __rest
     tr.template store<SL::BP, SL::XP>(s_b, s_xu, tid);
     if (J < rb) tr.load(Bb, xb, (uint32_t)bc_tok, (uint32_t)x_tok, J + 1, len, tid);
     __syncthreads();
-    if (strip_ok) diag_tile<T, P, N, HB, SL::BP, SL::XP>(acc, cf, dco, s_b, s_xu, s_da, s_dt, s, J, r, qd);
+    if (strip_ok)
+      diag_tile<T, P, N, HB, SL::BP, SL::XP, PRECB>(acc, cf, dco, s_b, s_xu, s_da, s_dt, s, J, wave, r, qd);
   }
   if (Z && strip_ok) apply_gate<T, P, HB>(acc, Z, (size_t)b * L + t0, x_tok, h0, s, len, r, qd);
   const int rows = min(kKT, len - rb * kKT);
@@ -546,7 +530,7 @@ __global__ __launch_bounds__(512) void chunk_scan_chunk_kernel(const T* __restri
 #pragma unroll
     for (int st = 0; st < 2; ++st)
       if (ok[st] && 4 * J <= strip[st])
-        diag_tile<T, P, N, HB, SL::BP, SL::XP>(acc[st], cf[st], dco, s_b, s_xu, s_da, s_dt, strip[st], J, r, qd);
+        diag_tile<T, P, N, HB, SL::BP, SL::XP>(acc[st], cf[st], dco, s_b, s_xu, s_da, s_dt, strip[st], J, 0, r, qd);
   }
   if (Z) {
 #pragma unroll
@@ -574,7 +558,7 @@ static hipError_t launch_scan_hb(const FwdArgs& a, hipStream_t s) {
   } else {
     const uint32_t nblocks = (uint32_t)a.B * a.nc * (a.H / HB) * (a.Q / kKT);
     chunk_scan_rows_kernel<T, P, N, HB><<<nblocks, 256, 0, s>>>(
-        static_cast<const T*>(a.x), static_cast<const T*>(a.Bm), static_cast<const T*>(a.Cm), a.dtp, a.dAcs,
+        static_cast<const T*>(a.x), static_cast<const T*>(a.Bm), a.cb, static_cast<const T*>(a.Cm), a.dtp, a.dAcs,
         a.states, a.D, static_cast<const T*>(a.z), static_cast<T*>(a.y), a.L, a.H, a.G, a.nc, a.Q, a.B);
   }
   return hipGetLastError();

@@ -8,27 +8,96 @@
 // The backward pass reuses it with (dy, C) in place of (x, B) and w_i = exp(dAcs[i]): the
 // gradient that chunk c's outputs send into the state entering the chunk.
 //
-// One workgroup (4 wavefronts) per (b, c, h).  A (P x Q) . (Q x N) product on MFMA with
-// fp32 accumulation.  The contraction runs over tokens, the slow axis of x and B in HBM, so
+// One workgroup (4 wavefronts) per (b, c, h); its wavefront 0 first computes the chunk's dt'
+// and their cumsum (chunk_cumsum_wave below), which the other kernels read from the
+// workspace.  A (P x Q) . (Q x N) product on MFMA with fp32 accumulation.  The contraction runs over tokens, the slow axis of x and B in HBM, so
 // 64-token tiles are staged transposed in LDS (token-contiguous rows): each thread loads
 // the same 16-byte column slice of two consecutive tokens and writes them as one packed
 // pair, which keeps the transposed LDS writes free of bank conflicts.  The next tile's
 // global loads are issued into registers before the current tile's MFMAs.  The per-token
 // weight w_i is folded into x while staging.  Tokens past the end of the sequence are zero.
 // fp32 fragments use the token permutation k = 16*qd + kk so that each lane reads 128 bits.
+#include "cb_tiles.h"
 #include "ssd_common.h"
 #include "ssd_launch.h"
 
 namespace ssd {
 
+// dt' = softplus(dt + dt_bias) (optionally clamped to [lo, hi], the dt limits of section 5.2
+// of the reference-comparison page) and the inclusive in-chunk cumulative sum of dt' A, for
+// one (b, c, h), by one wavefront: each lane scans Q/64 consecutive positions serially, then
+// the 64 lane totals are combined by a log-step shuffle scan (the up-sweep idea of the
+// parallel-scan section of "Agent 230: Comprehensive MAMBA-2 Implementation Comparison", on
+// 64-wide wavefronts).  Positions past the end of the sequence get dt' = 0, so the cumsum
+// stays flat there.  Results go to the workspace (for state_passing and chunk_scan) and to LDS.
+template <typename T>
+__device__ __forceinline__ void chunk_cumsum_wave(const T* __restrict__ dt, float bias, float a, size_t tok0,
+                                                  int H, int h, int len, int Q, int clamp, float lo, float hi,
+                                                  float* __restrict__ dtp_c, float* __restrict__ dA_c,
+                                                  float* s_d, float* s_cs, int lane) {
+  const int epl = Q >> 6;                      // positions per lane: 1, 2 or 4
+  const int i0 = lane * epl;
+  float raw[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    raw[k] = 0.f;
+    if (k < epl && i0 + k < len) raw[k] = to_f32(dt[(tok0 + i0 + k) * H + h]);
+  }
+  float d[4], cs[4];
+  float run = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float v = softplus(raw[k] + bias);
+    if (clamp) v = fminf(fmaxf(v, lo), hi);
+    v = (k < epl && i0 + k < len) ? v : 0.f;
+    d[k] = v;
+    run += v * a;
+    cs[k] = run;
+  }
+  // inclusive scan of the lane totals, then shift by one lane for the exclusive prefix
+  float incl = run;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float t = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += t;
+  }
+  float excl = __shfl_up(incl, 1, 64);
+  if (lane == 0) excl = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (k < epl) {
+      dtp_c[i0 + k] = d[k];
+      dA_c[i0 + k] = cs[k] + excl;
+      s_d[i0 + k] = d[k];
+      s_cs[i0 + k] = cs[k] + excl;
+    }
+  }
+}
+
+// Forward: workgroups [0, nblocks) compute the chunk states (each first the dt' cumsum of its
+// own (b, c, h)); fp32 launches add workgroups [nblocks, ...) that compute the C B^T blocks
+// the scan reads (cb_block), filling the tail of the grid.  Backward (from_start): dt' and the
+// cumsum are read from the workspace.
 template <typename T, int P, int N>
 __global__ __launch_bounds__(256) void chunk_state_kernel(const T* __restrict__ x,
                                                           const T* __restrict__ Bm,
-                                                          const float* __restrict__ dtp,
-                                                          const float* __restrict__ dAcs,
+                                                          const T* __restrict__ Cm,
+                                                          const T* __restrict__ dt,
+                                                          const float* __restrict__ dt_bias,
+                                                          const float* __restrict__ A,
+                                                          float* __restrict__ dtp,
+                                                          float* __restrict__ dAcs,
                                                           float* __restrict__ states,
+                                                          float* __restrict__ cb,
                                                           int L, int H, int G, int nc, int Q,
-                                                          uint32_t nblocks, int from_start) {
+                                                          uint32_t nblocks, int from_start, int clamp,
+                                                          float lo, float hi) {
+  if (blockIdx.x >= nblocks) {
+    if constexpr (sizeof(T) == 4) cb_block<N>(reinterpret_cast<const float*>(Bm),
+                                              reinterpret_cast<const float*>(Cm), cb, L, G, nc, Q,
+                                              blockIdx.x - nblocks);
+    return;
+  }
   constexpr bool F32 = sizeof(T) == 4;
   constexpr int KT = 64;                                 // tokens per LDS tile
   constexpr int PITCH = KT + (F32 ? 4 : 8);              // 16-byte aligned rows
@@ -46,6 +115,7 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const T* __restrict__ 
   __shared__ __attribute__((aligned(16))) T s_x[P * PITCH];   // (x * w)^T
   __shared__ __attribute__((aligned(16))) T s_b[N * PITCH];   // B^T
   __shared__ float s_w[256];
+  __shared__ float s_d[256], s_cs[256];
 
   uint32_t id = xcd_swizzle(blockIdx.x, nblocks);
   const int h = id % H;
@@ -58,12 +128,21 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const T* __restrict__ 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, qd = lane >> 4;
 
-  const float* dtp_c = dtp + (((size_t)b * H + h) * nc + c) * Q;
-  const float* dA_c = dAcs + (((size_t)b * H + h) * nc + c) * Q;
-  const float last = dA_c[Q - 1];
-  // forward: decay to the chunk's end times the step; backward (from_start): decay from the
-  // chunk's start, exp(dAcs_i), which weighs each output's gradient into the entering state
-  for (int i = tid; i < Q; i += 256) s_w[i] = from_start ? expf(dA_c[i]) : expf(last - dA_c[i]) * dtp_c[i];
+  float* dtp_c = dtp + (((size_t)b * H + h) * nc + c) * Q;
+  float* dA_c = dAcs + (((size_t)b * H + h) * nc + c) * Q;
+  if (from_start) {
+    // backward: decay from the chunk's start, exp(dAcs_i), which weighs each output's
+    // gradient into the state entering the chunk
+    for (int i = tid; i < Q; i += 256) s_w[i] = expf(dA_c[i]);
+  } else {
+    // forward: decay to the chunk's end times the step
+    if (wave == 0)
+      chunk_cumsum_wave<T>(dt, dt_bias[h], A[h], (size_t)b * L + t0, H, h, len, Q, clamp, lo, hi, dtp_c, dA_c,
+                           s_d, s_cs, lane);
+    __syncthreads();
+    const float last = s_cs[Q - 1];
+    for (int i = tid; i < Q; i += 256) s_w[i] = expf(last - s_cs[i]) * s_d[i];
+  }
 
   const size_t xs = (size_t)H * P, bs = (size_t)G * N;    // token strides
   const T* xb = x + ((size_t)b * L + t0) * xs + (size_t)h * P;
@@ -210,9 +289,14 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const T* __restrict__ 
 template <typename T, int P, int N>
 static hipError_t launch_state_impl(const FwdArgs& a, hipStream_t s) {
   const uint32_t nblocks = (uint32_t)a.B * a.nc * a.H;
-  chunk_state_kernel<T, P, N><<<nblocks, 256, 0, s>>>(
-      static_cast<const T*>(a.x), static_cast<const T*>(a.Bm), a.dtp, a.dAcs, a.states, a.L, a.H, a.G,
-      a.nc, a.Q, nblocks, a.state_from_start);
+  const int nrb = a.Q / kCbKT;
+  const uint32_t ncb = (sizeof(T) == 4 && a.cb && !a.state_from_start)
+                           ? (uint32_t)a.B * a.nc * a.G * (nrb * (nrb + 1) / 2) : 0u;
+  if (nblocks + ncb == 0) return hipSuccess;
+  chunk_state_kernel<T, P, N><<<nblocks + ncb, 256, 0, s>>>(
+      static_cast<const T*>(a.x), static_cast<const T*>(a.Bm), static_cast<const T*>(a.Cm),
+      static_cast<const T*>(a.dt), a.dt_bias, a.A, a.dtp, a.dAcs, a.states, a.cb, a.L, a.H, a.G, a.nc, a.Q,
+      nblocks, a.state_from_start, a.clamp, a.dt_lo, a.dt_hi);
   return hipGetLastError();
 }
 

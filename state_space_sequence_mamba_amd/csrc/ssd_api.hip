@@ -38,8 +38,15 @@ ssd_status_t check_dims(const ssd_dims_t* d, bool need_seqlen) {
 bool chunk_ok(int q) { return q == 64 || q == 128 || q == 256; }
 
 struct WsLayout {
-  size_t dtp_off, dacs_off, states_off, total;
+  size_t dtp_off, dacs_off, states_off, cb_off, total;
 };
+
+// fp32 only: the C B^T sub-tile blocks cb_block writes, (B, nc, G, nrb (nrb + 1) / 2) x 16 KB
+size_t cb_bytes(const ssd_dims_t* d, int Q) {
+  if (d->dtype != SSD_F32) return 0;
+  const int64_t nc = (d->seqlen + Q - 1) / Q, nrb = Q / 64;
+  return align_up((size_t)d->batch * nc * d->ngroups * (nrb * (nrb + 1) / 2) * 16 * 256 * sizeof(float));
+}
 
 WsLayout ws_layout(const ssd_dims_t* d, int Q) {
   const int64_t nc = (d->seqlen + Q - 1) / Q;
@@ -49,7 +56,8 @@ WsLayout ws_layout(const ssd_dims_t* d, int Q) {
   w.dtp_off = 0;
   w.dacs_off = cum;
   w.states_off = 2 * cum;
-  w.total = 2 * cum + st;
+  w.cb_off = 2 * cum + st;
+  w.total = 2 * cum + st + cb_bytes(d, Q);
   return w;
 }
 
@@ -164,6 +172,7 @@ ssd_status_t fwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   a.dtp = has_seq ? reinterpret_cast<float*>(ws + wl.dtp_off) : nullptr;
   a.dAcs = has_seq ? reinterpret_cast<float*>(ws + wl.dacs_off) : nullptr;
   a.states = has_seq ? reinterpret_cast<float*>(ws + wl.states_off) : nullptr;
+  a.cb = has_seq && dims->dtype == SSD_F32 ? reinterpret_cast<float*>(ws + wl.cb_off) : nullptr;
   a.scan_variant = pick_scan_variant(a.dtype);
   a.heads_per_block = pick_heads_per_block(a.B, a.nc, a.H, a.G, a.Q, a.scan_variant);
   a.state_from_start = 0;
@@ -176,18 +185,17 @@ ssd_status_t fwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   }
 
   auto record = [&](int k) { return !ev || hipEventRecord(ev[k], stream) == hipSuccess; };
-  if (!record(0) || ssd::launch_chunk_cumsum(a, stream) != hipSuccess) return SSD_ERR_HIP;
-  if (!record(1) || ssd::launch_chunk_state(a, stream) != hipSuccess) return SSD_ERR_HIP;
-  if (!record(2) || ssd::launch_state_passing(a, stream) != hipSuccess) return SSD_ERR_HIP;
-  if (!record(3) || ssd::launch_chunk_scan(a, stream) != hipSuccess) return SSD_ERR_HIP;
-  if (!record(4)) return SSD_ERR_HIP;
+  if (!record(0) || ssd::launch_chunk_state(a, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (!record(1) || ssd::launch_state_passing(a, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (!record(2) || ssd::launch_chunk_scan(a, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (!record(3)) return SSD_ERR_HIP;
   return SSD_OK;
 }
 
 // Backward workspace: the forward's regions, the state gradients, per-head dB / dC, per-token
 // and per-chunk partials, and (with a gate) the pre-gate output and the gated gradient.
 struct BwdLayout {
-  size_t dtp, dacs, states, gstates, dBh, dCh, ddir, dSa, dSc, Ub, pA, pbias, pD, ypre, dyg, total;
+  size_t dtp, dacs, states, gstates, dBh, dCh, ddir, dSa, dSc, Ub, pA, pbias, pD, ypre, dyg, cb, total;
 };
 
 BwdLayout bwd_layout(const ssd_dims_t* d, int Q, bool gate) {
@@ -215,6 +223,7 @@ BwdLayout bwd_layout(const ssd_dims_t* d, int Q, bool gate) {
   w.pD = o; o += pd;
   w.ypre = o; o += act;
   w.dyg = o; o += act;
+  w.cb = o; o += gate ? cb_bytes(d, Q) : 0;
   w.total = o;
   return w;
 }
@@ -286,6 +295,7 @@ ssd_status_t bwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   f.dtp = reinterpret_cast<float*>(ws + wl.dtp);
   f.dAcs = reinterpret_cast<float*>(ws + wl.dacs);
   f.states = reinterpret_cast<float*>(ws + wl.states);
+  f.cb = z && dims->dtype == SSD_F32 ? reinterpret_cast<float*>(ws + wl.cb) : nullptr;   // only the gate needs y~
   f.scan_variant = pick_scan_variant(f.dtype);
   f.heads_per_block = pick_heads_per_block(f.B, f.nc, f.H, f.G, f.Q, f.scan_variant);
   f.state_from_start = 0;
@@ -317,21 +327,21 @@ ssd_status_t bwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   gp.passing_reverse = 1;
   auto record = [&](int k) { return !ev || hipEventRecord(ev[k], stream) == hipSuccess; };
   if (!has_seq) {
-    for (int k = 0; k < 11; ++k)
+    for (int k = 0; k < 10; ++k)
       if (!record(k)) return SSD_ERR_HIP;
     if (dinitial_state && ssd::launch_state_passing(gp, stream) != hipSuccess) return SSD_ERR_HIP;
     if (ssd::launch_bwd_reduce(a, stream) != hipSuccess) return SSD_ERR_HIP;   // zero dA, d dt_bias, dD
-    return record(11) ? SSD_OK : SSD_ERR_HIP;
+    return record(10) ? SSD_OK : SSD_ERR_HIP;
   }
-  // forward intermediates: dt', its cumsum, the states entering each chunk
-  if (!record(0) || ssd::launch_chunk_cumsum(f, stream) != hipSuccess) return SSD_ERR_HIP;
-  if (!record(1) || ssd::launch_chunk_state(f, stream) != hipSuccess) return SSD_ERR_HIP;
-  if (!record(2) || ssd::launch_state_passing(f, stream) != hipSuccess) return SSD_ERR_HIP;
-  if (!record(3)) return SSD_ERR_HIP;
+  // forward intermediates: dt', its cumsum, the states entering each chunk (and, with a gate
+  // in fp32, the C B^T blocks of the pre-gate output)
+  if (!record(0) || ssd::launch_chunk_state(f, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (!record(1) || ssd::launch_state_passing(f, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (!record(2)) return SSD_ERR_HIP;
   if (z) {
     // pre-gate output, then dy = dout silu(z) and dz = dout y~ silu'(z)
     if (ssd::launch_chunk_scan(f, stream) != hipSuccess) return SSD_ERR_HIP;
-    if (!record(4)) return SSD_ERR_HIP;
+    if (!record(3)) return SSD_ERR_HIP;
     ssd::GateArgs ga;
     ga.n = dims->batch * dims->seqlen * dims->nheads * dims->headdim;
     ga.dtype = dims->dtype;
@@ -341,7 +351,7 @@ ssd_status_t bwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
     ga.dy = ws + wl.dyg;
     ga.dz = dz;
     if (ssd::launch_gate_bwd(ga, stream) != hipSuccess) return SSD_ERR_HIP;
-  } else if (!record(4)) {
+  } else if (!record(3)) {
     return SSD_ERR_HIP;
   }
   // per-chunk gradient into the entering state: sum_i exp(dAcs_i) dy_i^T C_i
@@ -350,13 +360,13 @@ ssd_status_t bwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   gs.Bm = C;
   gs.states = a.gstates;
   gs.state_from_start = 1;
-  if (!record(5) || ssd::launch_chunk_state(gs, stream) != hipSuccess) return SSD_ERR_HIP;
-  if (!record(6) || ssd::launch_state_passing(gp, stream) != hipSuccess) return SSD_ERR_HIP;
-  if (!record(7) || ssd::launch_bwd_dxdb(a, stream) != hipSuccess) return SSD_ERR_HIP;
-  if (!record(8) || ssd::launch_bwd_dc(a, stream) != hipSuccess) return SSD_ERR_HIP;
-  if (!record(9) || ssd::launch_bwd_finalize(a, stream) != hipSuccess) return SSD_ERR_HIP;
-  if (!record(10) || ssd::launch_bwd_reduce(a, stream) != hipSuccess) return SSD_ERR_HIP;
-  return record(11) ? SSD_OK : SSD_ERR_HIP;
+  if (!record(4) || ssd::launch_chunk_state(gs, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (!record(5) || ssd::launch_state_passing(gp, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (!record(6) || ssd::launch_bwd_dxdb(a, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (!record(7) || ssd::launch_bwd_dc(a, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (!record(8) || ssd::launch_bwd_finalize(a, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (!record(9) || ssd::launch_bwd_reduce(a, stream) != hipSuccess) return SSD_ERR_HIP;
+  return record(10) ? SSD_OK : SSD_ERR_HIP;
 }
 
 // Both conv entry points.  `step`: one token per sequence, state updated in place.

@@ -29,9 +29,12 @@ struct FwdArgs {
   float* dtp;              // workspace (B, H, nc, Q)
   float* dAcs;             // workspace (B, H, nc, Q)
   float* states;           // workspace (B, nc, H, P, N)
+  float* cb;               // workspace, fp32 only: C B^T sub-tiles per (b, c, g), see cb_block;
+                           // null: chunk_state does not compute them
   int heads_per_block;     // chunk_scan: heads sharing one C B^T evaluation (divides H / G)
   int scan_variant;        // chunk_scan decomposition: 1 = 64-row blocks, 2 = whole chunks
-  int state_from_start;    // chunk_state weights exp(dAcs_i) instead of exp(last - dAcs_i) dt'_i
+  int state_from_start;    // chunk_state weights exp(dAcs_i) instead of exp(last - dAcs_i) dt'_i,
+                           // reading dt' and the cumsum instead of computing them
   int passing_reverse;     // state_passing from the last chunk to the first
 };
 
@@ -103,7 +106,6 @@ struct ConvArgs {
 // true when a kernel instantiation exists for (dtype, P, N)
 bool shape_supported(int dtype, int P, int N);
 
-hipError_t launch_chunk_cumsum(const FwdArgs& a, hipStream_t s);
 hipError_t launch_chunk_state(const FwdArgs& a, hipStream_t s);
 hipError_t launch_state_passing(const FwdArgs& a, hipStream_t s);
 hipError_t launch_chunk_scan(const FwdArgs& a, hipStream_t s);

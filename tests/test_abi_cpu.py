@@ -62,15 +62,21 @@ def _dims(**kw):
 
 def test_workspace_size_layout(lib):
     # 1 x 256 tokens, H=4, Q=64 -> nc=4; dt' and cumsum: 4*4*64 floats = 4096 B each (256-aligned);
-    # states: 4 chunks * 4 heads * 16 * 16 floats = 16384 B
-    assert ssd.ssd_fwd_workspace_size(_dims(), 64) == 2 * 4096 + 16384
+    # states: 4 chunks * 4 heads * 16 * 16 floats = 16384 B; fp32 adds C B^T once per group:
+    # 4 chunks * 1 group * 1 block pair (Q/64 = 1) * 16 KB = 65536 B
+    assert ssd.ssd_fwd_workspace_size(_dims(), 64) == 2 * 4096 + 16384 + 65536
     # ragged: L=300, Q=128 -> nc=3; 2*4*3*128*4 = 12288 B each; states 2*3*4*64*128*4 = 786432 B
     d = _dims(batch=2, seqlen=300, headdim=64, dstate=128, dtype=1)
     assert ssd.ssd_fwd_workspace_size(d, 128) == 2 * 12288 + 786432
-    # 1 x 5 tokens, H=3, Q=64: 3*64*4 = 768 B (already 256-aligned); states 3*16*16*4 = 3072
-    assert ssd.ssd_fwd_workspace_size(_dims(seqlen=5, nheads=3), 64) == 2 * 768 + 3072
+    # 1 x 5 tokens, H=3, Q=64: 3*64*4 = 768 B (already 256-aligned); states 3*16*16*4 = 3072; C B^T 16 KB
+    assert ssd.ssd_fwd_workspace_size(_dims(seqlen=5, nheads=3), 64) == 2 * 768 + 3072 + 16384
     # alignment padding: H=1, L=1, Q=64 -> 256 B regions
-    assert ssd.ssd_fwd_workspace_size(_dims(seqlen=1, nheads=1, headdim=16, dstate=16), 64) == 2 * 256 + 1024
+    assert ssd.ssd_fwd_workspace_size(_dims(seqlen=1, nheads=1, headdim=16, dstate=16), 64) == \
+        2 * 256 + 1024 + 16384
+    # Q=256 -> 4 row blocks, 10 (rb, J <= rb) block pairs of 16 KB per chunk and group;
+    # L=300 -> 2 chunks (cumsums 4*2*256*4 B, states 2*4*16*16*4 B), G=2: 2 * 2 * 10 * 16384 B
+    d = _dims(seqlen=300, ngroups=2)
+    assert ssd.ssd_fwd_workspace_size(d, 256) == 2 * 8192 + 2 * 4 * 16 * 16 * 4 + 2 * 2 * 10 * 16384
 
 
 @pytest.mark.parametrize("kw,q", [
@@ -132,8 +138,9 @@ def test_bwd_workspace_size_and_validation(lib):
     # 256*4*16*4 = 65536 B, per-chunk partials 64 -> 256 B, dD partials 4*4*16*4 = 1024 B
     base = 2 * 4096 + 2 * 16384 + 2 * 65536 + 4 * 4096 + 2 * 256 + 1024
     assert ssd.ssd_bwd_workspace_size(_dims(), 64, 0) == base
-    # the gate adds the pre-gate output and the gated gradient: 2 * 256 * 4 * 16 * 4 B
-    assert ssd.ssd_bwd_workspace_size(_dims(), 64, 1) == base + 2 * 65536
+    # the gate adds the pre-gate output and the gated gradient (2 * 256 * 4 * 16 * 4 B) and, for
+    # fp32, the C B^T blocks of the recomputed forward output (4 chunks * 16 KB)
+    assert ssd.ssd_bwd_workspace_size(_dims(), 64, 1) == base + 2 * 65536 + 65536
     assert ssd.ssd_bwd_workspace_size(_dims(headdim=24), 64, 0) == 0
     vp = ctypes.c_void_p
     p = vp(0x100000)

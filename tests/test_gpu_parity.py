@@ -353,12 +353,12 @@ def test_stage_events_time_each_kernel_and_refuse_capture():
     _say("stage events")
     from state_space_sequence_mamba_amd.timing import HipEvents
     hev = HipEvents()
-    evs = [hev.create() for _ in range(5)]
+    evs = [hev.create() for _ in range(4)]
     inp = {k: v.to(DEV) for k, v in I.make_fwd_inputs(2, 1000, 8, 64, 64, 1, "f32", seed=24).items()}
     y, _ = ssd.ssd_fwd(inp["x"], inp["dt"], inp["dt_bias"], inp["A"], inp["B"], inp["C"], inp["D"],
                        chunk_size=256, stage_events=evs)
     torch.cuda.synchronize()
-    assert all(hev.elapsed_ms(evs[k], evs[k + 1]) > 0 for k in range(4))
+    assert all(hev.elapsed_ms(evs[k], evs[k + 1]) > 0 for k in range(3))
     y_ref, _ = ssd.ssd_fwd(inp["x"], inp["dt"], inp["dt_bias"], inp["A"], inp["B"], inp["C"], inp["D"],
                            chunk_size=256)
     torch.cuda.synchronize()
