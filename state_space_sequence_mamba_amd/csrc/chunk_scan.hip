@@ -115,7 +115,7 @@ struct TileRegs {
 #pragma unroll
     for (int u = 0; u < BPT; ++u) {
       const int v = tid + NTHR * u;
-      if (v < BU) {
+      if (BU % NTHR == 0 || v < BU) {
         if (PRECB) {
           *reinterpret_cast<Vec16<T>*>(&s_b[4 * v]) = b[u];
         } else {
@@ -127,7 +127,7 @@ struct TileRegs {
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {
       const int v = tid + NTHR * u;
-      if (v < XU) {
+      if (XU % NTHR == 0 || v < XU) {
         const int m = v % (kKT / 2), rest = v / (kKT / 2);
         const int pv = (rest % PV) * VEC, hh = rest / PV;
         const Vec16<T> x0 = keep_if(x[u][0], (okm >> (BPT + 2 * u)) & 1u);
@@ -316,17 +316,68 @@ __device__ __forceinline__ void flush_rows(T* y, const T* s_y, size_t row0, size
   }
 }
 
-template <int HB>
-__device__ __forceinline__ void load_chunk_scalars(float (*s_da)[256], float (*s_dt)[256], const float* dtp,
-                                                   const float* dAcs, int b, int H, int h0, int nc, int c, int Q,
-                                                   int tid, int nthr) {
-  for (int idx = tid; idx < HB * Q; idx += nthr) {
-    const int hh = idx / Q, i = idx % Q;
-    const size_t off = (((size_t)b * H + h0 + hh) * nc + c) * Q + i;
-    s_dt[hh][i] = dtp[off];
-    s_da[hh][i] = dAcs[off] * kLog2e;
+// The chunk's dt' and (log2e-scaled) cumsum of HB heads, and head 0's entering state, held in
+// registers from their loads to their LDS stores, so that every global load of a workgroup's
+// prologue is in flight at once (one memory latency instead of one per phase).
+// Every slot i < 256 of every head is written (positions past Q repeat position Q - 1 and are
+// never read), so neither the loads nor the stores sit behind a branch: a conditional store
+// lets the compiler sink its load into the branch and wait for it there.
+template <int HB, int NTHR>
+struct ScalarRegs {
+  static constexpr int K = (256 + NTHR - 1) / NTHR;
+  float da[HB][K], dt[HB][K];
+  __device__ __forceinline__ void load(const float* dtp, const float* dAcs, int b, int H, int h0, int nc, int c,
+                                       int Q, int tid) {
+#pragma unroll
+    for (int hh = 0; hh < HB; ++hh)
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int i = min(tid + NTHR * k, Q - 1);
+        const size_t off = (((size_t)b * H + h0 + hh) * nc + c) * Q + i;
+        dt[hh][k] = dtp[off];
+        da[hh][k] = dAcs[off];
+      }
   }
-}
+  __device__ __forceinline__ void store(float (*s_da)[256], float (*s_dt)[256], int tid) const {
+#pragma unroll
+    for (int hh = 0; hh < HB; ++hh)
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int i = tid + NTHR * k;
+        if (NTHR * K == 256 || i < 256) {
+          s_dt[hh][i] = dt[hh][k];
+          s_da[hh][i] = da[hh][k] * kLog2e;
+        }
+      }
+  }
+};
+
+template <typename T, int P, int N, int NTHR>
+struct PrevRegs {
+  static constexpr int U = P * N / 4, K = (U + NTHR - 1) / NTHR;
+  float4 v[K];
+  __device__ __forceinline__ void load(const float* hp, int tid) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) v[k] = reinterpret_cast<const float4*>(hp)[min(tid + NTHR * k, U - 1)];
+  }
+  template <int BP>
+  __device__ __forceinline__ void store(T* s_prev, int tid) const {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int u = tid + NTHR * k;
+      if (U % NTHR == 0 || u < U) {              // compile-time true for every instantiated shape
+        const int p = (4 * u) / N, n = (4 * u) % N;
+        T* dst = &s_prev[p * BP + n];
+        if (sizeof(T) == 4) {
+          __builtin_memcpy(dst, &v[k], sizeof(float4));
+        } else {
+          T q[4] = {from_f32<T>(v[k].x), from_f32<T>(v[k].y), from_f32<T>(v[k].z), from_f32<T>(v[k].w)};
+          __builtin_memcpy(dst, q, sizeof(q));
+        }
+      }
+    }
+  }
+};
 
 // ---------------------------------------------------------------- row-block decomposition
 template <typename T, int P, int N, int HB>
@@ -392,9 +443,13 @@ __global__ __launch_bounds__(256, 2) void chunk_scan_rows_kernel(const T* __rest
                       : Bm + ((size_t)b * L + t0) * bc_tok + (size_t)g * N;
   const T* xb = x + ((size_t)b * L + t0) * x_tok + (size_t)h0 * P;
 
+  // prologue: every global load in flight before the first wait
   TileRegs<T, P, N, HB, NTHR, PRECB> tr;
   tr.load(Bb, xb, (uint32_t)bc_tok, (uint32_t)x_tok, 0, len, tid);
-  load_chunk_scalars<HB>(s_da, s_dt, dtp, dAcs, b, H, h0, nc, c, Q, tid, NTHR);
+  ScalarRegs<HB, NTHR> sr;
+  sr.load(dtp, dAcs, b, H, h0, nc, c, Q, tid);
+  PrevRegs<T, P, N, NTHR> pr;
+  pr.load(states + (((size_t)b * nc + c) * H + h0) * (size_t)(P * N), tid);
   typename ND::frag cf;
   {
     const int i = 16 * s + r;
@@ -412,8 +467,12 @@ __global__ __launch_bounds__(256, 2) void chunk_scan_rows_kernel(const T* __rest
 #pragma unroll
     for (int pt = 0; pt < TP; ++pt) acc[hh][pt] = zero4();
 
+  sr.store(s_da, s_dt, tid);
+  pr.template store<SL::BP>(s_xu, tid);
+  __syncthreads();
+  if (strip_ok) carried_term<T, P, N, SL::BP>(acc[0], cf, s_xu, s_da[0], s, r, qd);
 #pragma unroll
-  for (int hh = 0; hh < HB; ++hh) {
+  for (int hh = 1; hh < HB; ++hh) {
     __syncthreads();
     stage_prev<T, P, N, SL::BP>(s_xu, states + (((size_t)b * nc + c) * H + h0 + hh) * (size_t)(P * N), tid, NTHR);
     __syncthreads();
@@ -488,9 +547,13 @@ __global__ __launch_bounds__(512) void chunk_scan_chunk_kernel(const T* __restri
   const T* Bb = Bm + ((size_t)b * L + t0) * bc_tok + (size_t)g * N;
   const T* xb = x + ((size_t)b * L + t0) * x_tok + (size_t)h0 * P;
 
+  // prologue: every global load in flight before the first wait
   TileRegs<T, P, N, HB, NTHR> tr;
   tr.load(Bb, xb, (uint32_t)bc_tok, (uint32_t)x_tok, 0, len, tid);
-  load_chunk_scalars<HB>(s_da, s_dt, dtp, dAcs, b, H, h0, nc, c, Q, tid, NTHR);
+  ScalarRegs<HB, NTHR> sr;
+  sr.load(dtp, dAcs, b, H, h0, nc, c, Q, tid);
+  PrevRegs<T, P, N, NTHR> pr;
+  pr.load(states + (((size_t)b * nc + c) * H + h0) * (size_t)(P * N), tid);
   typename ND::frag cf[2];
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
@@ -512,8 +575,14 @@ __global__ __launch_bounds__(512) void chunk_scan_chunk_kernel(const T* __restri
 #pragma unroll
       for (int pt = 0; pt < TP; ++pt) acc[st][hh][pt] = zero4();
 
+  sr.store(s_da, s_dt, tid);
+  pr.template store<SL::BP>(s_xu, tid);
+  __syncthreads();
 #pragma unroll
-  for (int hh = 0; hh < HB; ++hh) {
+  for (int st = 0; st < 2; ++st)
+    if (ok[st]) carried_term<T, P, N, SL::BP>(acc[st][0], cf[st], s_xu, s_da[0], strip[st], r, qd);
+#pragma unroll
+  for (int hh = 1; hh < HB; ++hh) {
     __syncthreads();
     stage_prev<T, P, N, SL::BP>(s_xu, states + (((size_t)b * nc + c) * H + h0 + hh) * (size_t)(P * N), tid, NTHR);
     __syncthreads();

@@ -128,22 +128,6 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const T* __restrict__ 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, qd = lane >> 4;
 
-  float* dtp_c = dtp + (((size_t)b * H + h) * nc + c) * Q;
-  float* dA_c = dAcs + (((size_t)b * H + h) * nc + c) * Q;
-  if (from_start) {
-    // backward: decay from the chunk's start, exp(dAcs_i), which weighs each output's
-    // gradient into the state entering the chunk
-    for (int i = tid; i < Q; i += 256) s_w[i] = expf(dA_c[i]);
-  } else {
-    // forward: decay to the chunk's end times the step
-    if (wave == 0)
-      chunk_cumsum_wave<T>(dt, dt_bias[h], A[h], (size_t)b * L + t0, H, h, len, Q, clamp, lo, hi, dtp_c, dA_c,
-                           s_d, s_cs, lane);
-    __syncthreads();
-    const float last = s_cs[Q - 1];
-    for (int i = tid; i < Q; i += 256) s_w[i] = expf(last - s_cs[i]) * s_d[i];
-  }
-
   const size_t xs = (size_t)H * P, bs = (size_t)G * N;    // token strides
   const T* xb = x + ((size_t)b * L + t0) * xs + (size_t)h * P;
   const T* bb = Bm + ((size_t)b * L + t0) * bs + (size_t)g * N;
@@ -216,7 +200,23 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const T* __restrict__ 
 #pragma unroll
     for (int j = 0; j < WN; ++j) acc[i][j] = zero4();
 
-  load_tile(0);
+  load_tile(0);                            // in flight while the weights are computed
+  float* dtp_c = dtp + (((size_t)b * H + h) * nc + c) * Q;
+  float* dA_c = dAcs + (((size_t)b * H + h) * nc + c) * Q;
+  if (from_start) {
+    // backward: decay from the chunk's start, exp(dAcs_i), which weighs each output's
+    // gradient into the state entering the chunk
+    for (int i = tid; i < Q; i += 256) s_w[i] = expf(dA_c[i]);
+  } else {
+    // forward: decay to the chunk's end times the step
+    if (wave == 0)
+      chunk_cumsum_wave<T>(dt, dt_bias[h], A[h], (size_t)b * L + t0, H, h, len, Q, clamp, lo, hi, dtp_c, dA_c,
+                           s_d, s_cs, lane);
+    __syncthreads();
+    const float last = s_cs[Q - 1];
+    for (int i = tid; i < Q; i += 256) s_w[i] = expf(last - s_cs[i]) * s_d[i];
+  }
+
   for (int k0 = 0; k0 < len; k0 += KT) {
     __syncthreads();                       // previous tile consumed; s_w written
     store_tile(k0);
