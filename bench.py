@@ -236,11 +236,11 @@ def run_bwd(w, args, dev):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms = hev.elapsed_ms(t0, t1) / K
-    events = [[hev.create() for _ in range(11)] for _ in range(K)]
+    events = [[hev.create() for _ in range(20)] for _ in range(K)]
     for i in range(K):
         step(events[i])
     torch.cuda.synchronize()
-    per_kernel_ms = {k: sum(hev.elapsed_ms(ev[i], ev[i + 1]) for ev in events) / K
+    per_kernel_ms = {k: sum(hev.elapsed_ms(ev[2 * i], ev[2 * i + 1]) for ev in events) / K
                      for i, k in enumerate(BWD_STAGES)}
     cost = backward_cost(w)
     kernels = {}
@@ -405,19 +405,19 @@ def main():
     K, W = args.steps, args.warmup
     use_graph = not args.no_graph
     hev = HipEvents()
-    nev = 6   # 4 around the forward's kernels, 2 around ssd_step
+    nev = 8   # start / stop of the forward's three kernels (from their dispatches), 2 around ssd_step
     events = [[hev.create() for _ in range(nev)] for _ in range(max(K, 1))]
     t_start, t_end = hev.create(), hev.create()
 
     def step(evs=None):
         # launches go to the current stream (the capture stream while a graph is captured)
         ssd.ssd_fwd(d["x"], d["dt"], d["dt_bias"], d["A"], d["B"], d["C"], d["D"], chunk_size=w.chunk,
-                    y=y, final_state=state, workspace=ws, stage_events=None if evs is None else evs[:4])
+                    y=y, final_state=state, workspace=ws, stage_events=None if evs is None else evs[:6])
         if evs is not None:
-            hev.record(evs[4])
+            hev.record(evs[6])
         ssd.ssd_step(state, dd["x"], dd["dt"], d["dt_bias"], d["A"], dd["B"], dd["C"], d["D"], y=y_dec)
         if evs is not None:
-            hev.record(evs[5])
+            hev.record(evs[7])
 
     for _ in range(W):
         step()
@@ -444,14 +444,15 @@ def main():
     total_ms = hev.elapsed_ms(t_start, t_end)
     ms_per_step = total_ms / K
 
-    # Per-kernel durations: the same K steps launched eagerly with HIP events between the
-    # kernels (timing events cannot live inside a captured graph on this runtime).
+    # Per-kernel durations: the same K steps launched eagerly, each forward kernel timed by a
+    # start / stop event pair recorded by its own dispatch (ssd_fwd_timed); ssd_step between
+    # two stream events.  Timing events cannot live inside a captured graph on this runtime.
     for i in range(K):
         step(events[i])
     torch.cuda.synchronize()
 
     per_kernel_ms = {k: 0.0 for k in KERNELS}
-    pairs = [(0, 1), (1, 2), (2, 3), (4, 5)]
+    pairs = [(0, 1), (2, 3), (4, 5), (6, 7)]
     for evs in events[:K]:
         for k, (a, b) in zip(KERNELS, pairs):
             per_kernel_ms[k] += hev.elapsed_ms(evs[a], evs[b]) / K

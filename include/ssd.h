@@ -107,9 +107,10 @@ ssd_status_t ssd_fwd(const ssd_dims_t* dims,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ssd_fwd with per-kernel timing: identical arguments and results, plus `stage_events`,
- * an array of 4 events created by the caller (hipEventCreate).  stage_events[k] is
- * recorded on `stream` just before kernel k (0 chunk_state, 1 state_passing, 2 chunk_scan)
- * and stage_events[3] after the last one.  Event records
+ * an array of 6 events created by the caller (hipEventCreate): stage_events[2k] and
+ * [2k + 1] are the start and stop of kernel k (0 chunk_state, 1 state_passing, 2 chunk_scan),
+ * recorded by the kernel's own dispatch (hipExtLaunchKernelGGL), so hipEventElapsedTime of a
+ * pair is that kernel's execution time alone, as in a profiler's kernel trace.  Event records
  * cannot be captured into a graph: with non-NULL stage_events on a stream under capture the
  * call returns SSD_ERR_UNSUPPORTED and launches nothing.  For measurement tools; NULL
  * stage_events behaves exactly like ssd_fwd (which may be captured). */
@@ -165,11 +166,12 @@ ssd_status_t ssd_bwd(const ssd_dims_t* dims,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ssd_bwd with per-kernel timing: identical arguments and results, plus `stage_events`, an
- * array of 11 caller-created events recorded on `stream` before each stage: 0 chunk_state,
- * 1 state_passing (forward recompute), 2 chunk_scan of the pre-gate output and 3 the gate's
- * backward (both empty without a gate), 4 chunk_state of the output gradients, 5 reverse
- * state_passing, 6 the anti-causal kernel, 7 the causal kernel, 8 finalize, 9 reductions,
- * and 10 after the last.  Like ssd_fwd_timed it refuses a stream under graph
+ * array of 20 caller-created events: [2k] and [2k + 1] are the start and stop of stage k,
+ * recorded by the dispatches themselves: 0 chunk_state, 1 state_passing (forward
+ * recompute), 2 chunk_scan of the pre-gate output and 3 the gate's backward (both recorded
+ * back to back, i.e. empty, without a gate), 4 chunk_state of the output gradients,
+ * 5 reverse state_passing, 6 the anti-causal kernel, 7 the causal kernel, 8 finalize,
+ * 9 the two reduction kernels.  Like ssd_fwd_timed it refuses a stream under graph
  * capture (SSD_ERR_UNSUPPORTED, nothing launched). */
 ssd_status_t ssd_bwd_timed(const ssd_dims_t* dims,
                            const void* x, const void* dt, const float* dt_bias, const float* A,

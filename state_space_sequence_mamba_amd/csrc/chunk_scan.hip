@@ -621,12 +621,12 @@ template <typename T, int P, int N, int HB>
 static hipError_t launch_scan_hb(const FwdArgs& a, hipStream_t s) {
   if (a.scan_variant == 2) {
     const uint32_t nblocks = (uint32_t)a.B * a.nc * (a.H / HB);
-    chunk_scan_chunk_kernel<T, P, N, HB><<<nblocks, 512, 0, s>>>(
+    hipExtLaunchKernelGGL(chunk_scan_chunk_kernel<T, P, N, HB>, dim3(nblocks), dim3(512), 0, s, a.ev0, a.ev1, 0,
         static_cast<const T*>(a.x), static_cast<const T*>(a.Bm), static_cast<const T*>(a.Cm), a.dtp, a.dAcs,
         a.states, a.D, static_cast<const T*>(a.z), static_cast<T*>(a.y), a.L, a.H, a.G, a.nc, a.Q, nblocks);
   } else {
     const uint32_t nblocks = (uint32_t)a.B * a.nc * (a.H / HB) * (a.Q / kKT);
-    chunk_scan_rows_kernel<T, P, N, HB><<<nblocks, 256, 0, s>>>(
+    hipExtLaunchKernelGGL(chunk_scan_rows_kernel<T, P, N, HB>, dim3(nblocks), dim3(256), 0, s, a.ev0, a.ev1, 0,
         static_cast<const T*>(a.x), static_cast<const T*>(a.Bm), a.cb, static_cast<const T*>(a.Cm), a.dtp, a.dAcs,
         a.states, a.D, static_cast<const T*>(a.z), static_cast<T*>(a.y), a.L, a.H, a.G, a.nc, a.Q, a.B);
   }

@@ -293,7 +293,7 @@ static hipError_t launch_state_impl(const FwdArgs& a, hipStream_t s) {
   const uint32_t ncb = (sizeof(T) == 4 && a.cb && !a.state_from_start)
                            ? (uint32_t)a.B * a.nc * a.G * (nrb * (nrb + 1) / 2) : 0u;
   if (nblocks + ncb == 0) return hipSuccess;
-  chunk_state_kernel<T, P, N><<<nblocks + ncb, 256, 0, s>>>(
+  hipExtLaunchKernelGGL(chunk_state_kernel<T, P, N>, dim3(nblocks + ncb), dim3(256), 0, s, a.ev0, a.ev1, 0,
       static_cast<const T*>(a.x), static_cast<const T*>(a.Bm), static_cast<const T*>(a.Cm),
       static_cast<const T*>(a.dt), a.dt_bias, a.A, a.dtp, a.dAcs, a.states, a.cb, a.L, a.H, a.G, a.nc, a.Q,
       nblocks, a.state_from_start, a.clamp, a.dt_lo, a.dt_hi);

@@ -177,18 +177,28 @@ ssd_status_t fwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   a.heads_per_block = pick_heads_per_block(a.B, a.nc, a.H, a.G, a.Q, a.scan_variant);
   a.state_from_start = 0;
   a.passing_reverse = 0;
+  a.ev0 = a.ev1 = nullptr;
 
   if (!has_seq) {
     // no tokens: final_state = initial_state (or zeros); state_passing with zero chunks
+    if (ev)
+      for (int k = 0; k < 6; ++k)
+        if (hipEventRecord(ev[k], stream) != hipSuccess) return SSD_ERR_HIP;
     if (!final_state) return SSD_OK;
     return ssd::launch_state_passing(a, stream) == hipSuccess ? SSD_OK : SSD_ERR_HIP;
   }
 
-  auto record = [&](int k) { return !ev || hipEventRecord(ev[k], stream) == hipSuccess; };
-  if (!record(0) || ssd::launch_chunk_state(a, stream) != hipSuccess) return SSD_ERR_HIP;
-  if (!record(1) || ssd::launch_state_passing(a, stream) != hipSuccess) return SSD_ERR_HIP;
-  if (!record(2) || ssd::launch_chunk_scan(a, stream) != hipSuccess) return SSD_ERR_HIP;
-  if (!record(3)) return SSD_ERR_HIP;
+  // kernel k is timed by ev[2k] (start) and ev[2k + 1] (stop), recorded by its own dispatch
+  auto stage = [&](int k) {
+    a.ev0 = ev ? ev[2 * k] : nullptr;
+    a.ev1 = ev ? ev[2 * k + 1] : nullptr;
+  };
+  stage(0);
+  if (ssd::launch_chunk_state(a, stream) != hipSuccess) return SSD_ERR_HIP;
+  stage(1);
+  if (ssd::launch_state_passing(a, stream) != hipSuccess) return SSD_ERR_HIP;
+  stage(2);
+  if (ssd::launch_chunk_scan(a, stream) != hipSuccess) return SSD_ERR_HIP;
   return SSD_OK;
 }
 
@@ -300,6 +310,7 @@ ssd_status_t bwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   f.heads_per_block = pick_heads_per_block(f.B, f.nc, f.H, f.G, f.Q, f.scan_variant);
   f.state_from_start = 0;
   f.passing_reverse = 0;
+  f.ev0 = f.ev1 = nullptr;
   a.dy = z ? static_cast<const void*>(ws + wl.dyg) : dout;
   a.gstates = reinterpret_cast<float*>(ws + wl.gstates);
   a.dBh = reinterpret_cast<float*>(ws + wl.dBh);
@@ -325,23 +336,32 @@ ssd_status_t bwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   gp.init = dfinal_state;
   gp.final_state = dinitial_state;
   gp.passing_reverse = 1;
-  auto record = [&](int k) { return !ev || hipEventRecord(ev[k], stream) == hipSuccess; };
+  // stage k is timed by ev[2k] (start) and ev[2k + 1] (stop), recorded by the dispatches
+  // themselves; stages that launch nothing record both events back to back
+  auto timing = [&](ssd::FwdArgs& args, int k) {
+    args.ev0 = ev ? ev[2 * k] : nullptr;
+    args.ev1 = ev ? ev[2 * k + 1] : nullptr;
+  };
+  auto empty_stage = [&](int k) {
+    return !ev || (hipEventRecord(ev[2 * k], stream) == hipSuccess && hipEventRecord(ev[2 * k + 1], stream) == hipSuccess);
+  };
   if (!has_seq) {
     for (int k = 0; k < 10; ++k)
-      if (!record(k)) return SSD_ERR_HIP;
+      if (!empty_stage(k)) return SSD_ERR_HIP;
     if (dinitial_state && ssd::launch_state_passing(gp, stream) != hipSuccess) return SSD_ERR_HIP;
     if (ssd::launch_bwd_reduce(a, stream) != hipSuccess) return SSD_ERR_HIP;   // zero dA, d dt_bias, dD
-    return record(10) ? SSD_OK : SSD_ERR_HIP;
+    return SSD_OK;
   }
   // forward intermediates: dt', its cumsum, the states entering each chunk (and, with a gate
   // in fp32, the C B^T blocks of the pre-gate output)
-  if (!record(0) || ssd::launch_chunk_state(f, stream) != hipSuccess) return SSD_ERR_HIP;
-  if (!record(1) || ssd::launch_state_passing(f, stream) != hipSuccess) return SSD_ERR_HIP;
-  if (!record(2)) return SSD_ERR_HIP;
+  timing(f, 0);
+  if (ssd::launch_chunk_state(f, stream) != hipSuccess) return SSD_ERR_HIP;
+  timing(f, 1);
+  if (ssd::launch_state_passing(f, stream) != hipSuccess) return SSD_ERR_HIP;
   if (z) {
     // pre-gate output, then dy = dout silu(z) and dz = dout y~ silu'(z)
+    timing(f, 2);
     if (ssd::launch_chunk_scan(f, stream) != hipSuccess) return SSD_ERR_HIP;
-    if (!record(3)) return SSD_ERR_HIP;
     ssd::GateArgs ga;
     ga.n = dims->batch * dims->seqlen * dims->nheads * dims->headdim;
     ga.dtype = dims->dtype;
@@ -350,8 +370,10 @@ ssd_status_t bwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
     ga.ypre = f.y;
     ga.dy = ws + wl.dyg;
     ga.dz = dz;
+    ga.ev0 = ev ? ev[6] : nullptr;
+    ga.ev1 = ev ? ev[7] : nullptr;
     if (ssd::launch_gate_bwd(ga, stream) != hipSuccess) return SSD_ERR_HIP;
-  } else if (!record(3)) {
+  } else if (!empty_stage(2) || !empty_stage(3)) {
     return SSD_ERR_HIP;
   }
   // per-chunk gradient into the entering state: sum_i exp(dAcs_i) dy_i^T C_i
@@ -360,13 +382,19 @@ ssd_status_t bwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   gs.Bm = C;
   gs.states = a.gstates;
   gs.state_from_start = 1;
-  if (!record(4) || ssd::launch_chunk_state(gs, stream) != hipSuccess) return SSD_ERR_HIP;
-  if (!record(5) || ssd::launch_state_passing(gp, stream) != hipSuccess) return SSD_ERR_HIP;
-  if (!record(6) || ssd::launch_bwd_dxdb(a, stream) != hipSuccess) return SSD_ERR_HIP;
-  if (!record(7) || ssd::launch_bwd_dc(a, stream) != hipSuccess) return SSD_ERR_HIP;
-  if (!record(8) || ssd::launch_bwd_finalize(a, stream) != hipSuccess) return SSD_ERR_HIP;
-  if (!record(9) || ssd::launch_bwd_reduce(a, stream) != hipSuccess) return SSD_ERR_HIP;
-  return record(10) ? SSD_OK : SSD_ERR_HIP;
+  timing(gs, 4);
+  if (ssd::launch_chunk_state(gs, stream) != hipSuccess) return SSD_ERR_HIP;
+  timing(gp, 5);
+  if (ssd::launch_state_passing(gp, stream) != hipSuccess) return SSD_ERR_HIP;
+  timing(f, 6);
+  if (ssd::launch_bwd_dxdb(a, stream) != hipSuccess) return SSD_ERR_HIP;
+  timing(f, 7);
+  if (ssd::launch_bwd_dc(a, stream) != hipSuccess) return SSD_ERR_HIP;
+  timing(f, 8);
+  if (ssd::launch_bwd_finalize(a, stream) != hipSuccess) return SSD_ERR_HIP;
+  timing(f, 9);
+  if (ssd::launch_bwd_reduce(a, stream) != hipSuccess) return SSD_ERR_HIP;
+  return SSD_OK;
 }
 
 // Both conv entry points.  `step`: one token per sequence, state updated in place.

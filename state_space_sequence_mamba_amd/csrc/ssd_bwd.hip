@@ -582,7 +582,7 @@ template <typename T, int P, int N>
 static hipError_t launch_dxdb_impl(const BwdArgs& a, hipStream_t s) {
   const FwdArgs& f = a.f;
   const uint32_t nblocks = (uint32_t)f.B * f.nc * (f.Q / KT) * f.H;
-  bwd_dxdb_kernel<T, P, N><<<nblocks, 256, 0, s>>>(
+  hipExtLaunchKernelGGL(bwd_dxdb_kernel<T, P, N>, dim3(nblocks), dim3(256), 0, s, f.ev0, f.ev1, 0,
       static_cast<const T*>(f.x), static_cast<const T*>(f.Bm), static_cast<const T*>(f.Cm),
       static_cast<const T*>(a.dy), f.dtp, f.dAcs, a.gstates, f.D, static_cast<T*>(a.dx), a.dBh, a.ddir, a.dSa, a.Ub,
       a.pD, f.L, f.H, f.G, f.nc, f.Q, nblocks);
@@ -593,7 +593,7 @@ template <typename T, int P, int N>
 static hipError_t launch_dc_impl(const BwdArgs& a, hipStream_t s) {
   const FwdArgs& f = a.f;
   const uint32_t nblocks = (uint32_t)f.B * f.nc * (f.Q / KT) * f.H;
-  bwd_dc_kernel<T, P, N><<<nblocks, 256, 0, s>>>(
+  hipExtLaunchKernelGGL(bwd_dc_kernel<T, P, N>, dim3(nblocks), dim3(256), 0, s, f.ev0, f.ev1, 0,
       static_cast<const T*>(f.x), static_cast<const T*>(f.Bm), static_cast<const T*>(f.Cm),
       static_cast<const T*>(a.dy), f.dtp, f.dAcs, f.states, a.dCh, a.dSc, f.L, f.H, f.G, f.nc, f.Q, nblocks);
   return hipGetLastError();
@@ -603,7 +603,7 @@ template <typename T, int P, int N>
 static hipError_t launch_finalize_impl(const BwdArgs& a, hipStream_t s) {
   const FwdArgs& f = a.f;
   const uint32_t nblocks = (uint32_t)f.B * f.nc * f.H;
-  bwd_finalize_kernel<T, P, N><<<nblocks, 256, 0, s>>>(
+  hipExtLaunchKernelGGL(bwd_finalize_kernel<T, P, N>, dim3(nblocks), dim3(256), 0, s, f.ev0, f.ev1, 0,
       static_cast<const T*>(f.dt), f.dt_bias, f.A, f.dtp, f.dAcs, f.states, a.gstates, a.ddir, a.dSa, a.dSc, a.Ub,
       static_cast<T*>(a.ddt), a.pA, a.pbias, f.L, f.H, f.nc, f.Q, f.clamp, f.dt_lo, f.dt_hi);
   return hipGetLastError();
@@ -613,11 +613,16 @@ template <typename T>
 static hipError_t launch_reduce_impl(const BwdArgs& a, hipStream_t s) {
   const FwdArgs& f = a.f;
   const size_t total = (size_t)f.B * f.L * f.G * f.N;
-  if (total > 0)
-    bwd_reduce_bc_kernel<T><<<(unsigned)((total + 255) / 256), 256, 0, s>>>(
-        a.dBh, a.dCh, static_cast<T*>(a.dB), static_cast<T*>(a.dC), f.H, f.G, f.N, total);
-  bwd_reduce_params_kernel<<<f.H, 256, 0, s>>>(a.pA, a.pbias, a.pD, a.dA, a.ddt_bias, a.dD, f.H, f.P, f.B * f.nc,
-                                               f.B * f.nc * (f.Q / KT));
+  // the start event goes with the first launch and the stop event with the second
+  hipEvent_t start = f.ev0;
+  if (total > 0) {
+    hipExtLaunchKernelGGL(bwd_reduce_bc_kernel<T>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, start,
+                          nullptr, 0, a.dBh, a.dCh, static_cast<T*>(a.dB), static_cast<T*>(a.dC), f.H, f.G, f.N,
+                          total);
+    start = nullptr;
+  }
+  hipExtLaunchKernelGGL(bwd_reduce_params_kernel, dim3(f.H), dim3(256), 0, s, start, f.ev1, 0, a.pA, a.pbias, a.pD,
+                        a.dA, a.ddt_bias, a.dD, f.H, f.P, f.B * f.nc, f.B * f.nc * (f.Q / KT));
   return hipGetLastError();
 }
 
@@ -650,16 +655,18 @@ hipError_t launch_bwd_reduce(const BwdArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_gate_bwd(const GateArgs& a, hipStream_t s) {
-  if (a.n == 0) return hipSuccess;
+  if (a.n == 0) return hipSuccess;   // unreachable with a gate: a sequence has at least one token
   const unsigned nb = (unsigned)((a.n + 255) / 256);
   if (a.dtype == DT_F32)
-    gate_bwd_kernel<float><<<nb, 256, 0, s>>>(static_cast<const float*>(a.dout), static_cast<const float*>(a.z),
-                                              static_cast<const float*>(a.ypre), static_cast<float*>(a.dy),
-                                              static_cast<float*>(a.dz), a.n);
+    hipExtLaunchKernelGGL(gate_bwd_kernel<float>, dim3(nb), dim3(256), 0, s, a.ev0, a.ev1, 0,
+                          static_cast<const float*>(a.dout), static_cast<const float*>(a.z),
+                          static_cast<const float*>(a.ypre), static_cast<float*>(a.dy), static_cast<float*>(a.dz),
+                          a.n);
   else
-    gate_bwd_kernel<__bf16><<<nb, 256, 0, s>>>(static_cast<const __bf16*>(a.dout), static_cast<const __bf16*>(a.z),
-                                               static_cast<const __bf16*>(a.ypre), static_cast<__bf16*>(a.dy),
-                                               static_cast<__bf16*>(a.dz), a.n);
+    hipExtLaunchKernelGGL(gate_bwd_kernel<__bf16>, dim3(nb), dim3(256), 0, s, a.ev0, a.ev1, 0,
+                          static_cast<const __bf16*>(a.dout), static_cast<const __bf16*>(a.z),
+                          static_cast<const __bf16*>(a.ypre), static_cast<__bf16*>(a.dy), static_cast<__bf16*>(a.dz),
+                          a.n);
   return hipGetLastError();
 }
 

@@ -2,6 +2,7 @@
 // Every launcher assumes its arguments were validated by the API layer.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -33,6 +34,9 @@ struct FwdArgs {
                            // null: chunk_state does not compute them
   int heads_per_block;     // chunk_scan: heads sharing one C B^T evaluation (divides H / G)
   int scan_variant;        // chunk_scan decomposition: 1 = 64-row blocks, 2 = whole chunks
+  hipEvent_t ev0, ev1;     // timing: start / stop events of the next launch (or null), recorded
+                           // by the dispatch itself (hipExtLaunchKernelGGL), so they time the
+                           // kernel alone, as a profiler's kernel trace does
   int state_from_start;    // chunk_state weights exp(dAcs_i) instead of exp(last - dAcs_i) dt'_i,
                            // reading dt' and the cumsum instead of computing them
   int passing_reverse;     // state_passing from the last chunk to the first
@@ -69,6 +73,7 @@ struct GateArgs {
   const void* ypre;
   void* dy;
   void* dz;
+  hipEvent_t ev0, ev1;
 };
 
 struct StepArgs {

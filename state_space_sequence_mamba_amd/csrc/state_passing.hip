@@ -65,7 +65,8 @@ __global__ __launch_bounds__(256) void state_passing_kernel(float* __restrict__ 
 hipError_t launch_state_passing(const FwdArgs& a, hipStream_t s) {
   const int PN = a.P * a.N;
   dim3 grid((PN / 4 + 255) / 256, a.H, a.B);
-  state_passing_kernel<<<grid, 256, 0, s>>>(a.states, a.dAcs, a.init, a.final_state, a.H, a.nc, a.Q, PN,
+  hipExtLaunchKernelGGL(state_passing_kernel, grid, dim3(256), 0, s, a.ev0, a.ev1, 0, a.states, a.dAcs, a.init,
+                        a.final_state, a.H, a.nc, a.Q, PN,
                                             a.passing_reverse);
   return hipGetLastError();
 }

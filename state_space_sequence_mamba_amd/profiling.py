@@ -123,6 +123,56 @@ def stats(args):
                       f"{float(r['Percentage']):6.2f} %")
 
 
+def _bench_line(log):
+    """The JSON line bench.py printed in a profiled run's log, or None."""
+    if not log or not os.path.exists(log):
+        return None
+    with open(log) as fh:
+        for line in fh:
+            line = line.strip()
+            if line.startswith("{") and '"metric"' in line:
+                return json.loads(line)
+    return None
+
+
+def summary(args):
+    """Markdown summary of one kernel-trace run: per-kernel calls and average duration, next to
+    the per-kernel durations bench.py measured with HIP events in the same process."""
+    files = glob.glob(os.path.join(args.trace, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        sys.exit(f"no kernel_stats.csv under {args.trace}")
+    rows = []
+    with open(files[0]) as fh:
+        for r in csv.DictReader(fh):
+            name = r["Name"].split("(")[0].replace("void ", "")
+            rows.append((name, int(r["Calls"]), float(r["AverageNs"]) / 1000.0, float(r["Percentage"])))
+    bench = _bench_line(args.log)
+    events = {}
+    if bench:
+        for k, v in bench.get("kernels", {}).items():
+            events[k] = v["us"]
+        rl = bench.get("roofline", {})
+        if rl.get("kernel"):
+            events.setdefault(rl["kernel"], None)
+    out = [f"# Kernel trace: {args.workload} (MI355X, gfx950)", "",
+           "Command (from the repository root, TMPDIR=/tmp):", "", f"    {args.command}", "",
+           f"Summarised with `python -m state_space_sequence_mamba_amd.profiling summary` from the run's "
+           f"kernel_stats.csv and the JSON line bench.py printed in the same process.", "",
+           "| kernel | calls | rocprofv3 average (us) | share of GPU time | bench.py HIP-event average (us) |",
+           "|---|---|---|---|---|"]
+    for name, calls, avg, pct in rows:
+        key = kernel_key(name)
+        ev = events.get(key) if key else None
+        out.append(f"| `{name}` | {calls} | {avg:.2f} | {pct:.1f} % | {'' if ev is None else f'{ev:.2f}'} |")
+    if bench:
+        out += ["", f"bench.py line of this run: `{bench['ms_per_step']}` ms per step, value {bench['value']:.4g} "
+                f"{bench['unit']}, roofline {json.dumps(bench.get('roofline'))}."]
+    text = "\n".join(out) + "\n"
+    with open(args.out, "w") as fh:
+        fh.write(text)
+    print(text)
+
+
 def workload_slug(name):
     return "_".join(name.lower().split())
 
@@ -152,8 +202,14 @@ def main():
     t.add_argument("--out", required=True)
     s = sub.add_parser("stats")
     s.add_argument("--trace", required=True)
+    m = sub.add_parser("summary")
+    m.add_argument("--trace", required=True)
+    m.add_argument("--log", default="")
+    m.add_argument("--workload", required=True)
+    m.add_argument("--command", required=True)
+    m.add_argument("--out", required=True)
     a = ap.parse_args()
-    {"traffic": traffic, "stats": stats}[a.cmd](a)
+    {"traffic": traffic, "stats": stats, "summary": summary}[a.cmd](a)
 
 
 if __name__ == "__main__":

@@ -131,7 +131,8 @@ def ssd_fwd(x, dt, dt_bias, A, B, C, D=None, chunk_size=256, initial_state=None,
 
     `z` (shape of x) gates the output, y * silu(z); `dt_limit` = (dt_min, dt_max) clamps dt'.
     Output and workspace tensors are allocated with torch when not given.  `stage_events`
-    (4 raw hipEvent_t handles as ints) selects the timed entry point.
+    (6 raw hipEvent_t handles as ints: start and stop of each of the three kernels) selects the
+    timed entry point.
     """
     b, L, H, P, N, G = _check_fwd_shapes(x, dt, dt_bias, A, B, C, D, initial_state, z)
     dims = make_dims(b, L, H, P, N, G, x.dtype, dt_limit)
@@ -149,7 +150,7 @@ def ssd_fwd(x, dt, dt_bias, A, B, C, D=None, chunk_size=256, initial_state=None,
     if stage_events is None:
         st = lib.ssd_fwd(*args)
     else:
-        arr = (ctypes.c_void_p * 4)(*stage_events)
+        arr = (ctypes.c_void_p * 6)(*stage_events)
         st = lib.ssd_fwd_timed(*args, arr)
     if st != SSD_OK:
         raise SsdError(st, "ssd_fwd")
@@ -197,8 +198,8 @@ def ssd_bwd(x, dt, dt_bias, A, B, C, dout, D=None, chunk_size=256, initial_state
             out=None, stage_events=None):
     """Gradients of ssd_fwd.  Returns a dict: dx, ddt, ddt_bias, dA, dB, dC, dD, dz, dinitial_state
     (dD / dz / dinitial_state are None when not requested or not applicable).  `out` reuses a
-    previous call's dict as the output buffers; `stage_events` (11 raw hipEvent_t handles as
-    ints) selects the timed entry point."""
+    previous call's dict as the output buffers; `stage_events` (20 raw hipEvent_t handles as
+    ints: start and stop of each of the ten stages) selects the timed entry point."""
     b, L, H, P, N, G = _check_fwd_shapes(x, dt, dt_bias, A, B, C, D, initial_state, z)
     if tuple(dout.shape) != tuple(x.shape) or dout.dtype != x.dtype or not dout.is_contiguous():
         raise ValueError("dout must be a contiguous tensor shaped and typed like x")
@@ -225,7 +226,7 @@ def ssd_bwd(x, dt, dt_bias, A, B, C, dout, D=None, chunk_size=256, initial_state
     if stage_events is None:
         st = lib.ssd_bwd(*args)
     else:
-        st = lib.ssd_bwd_timed(*args, (ctypes.c_void_p * 11)(*stage_events))
+        st = lib.ssd_bwd_timed(*args, (ctypes.c_void_p * 20)(*stage_events))
     if st != SSD_OK:
         raise SsdError(st, "ssd_bwd")
     return out

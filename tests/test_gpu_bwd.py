@@ -196,12 +196,13 @@ def test_bwd_graph_replay_and_timed_entry_match_eager(dtype):
         for k, v in ref.items():
             assert torch.equal(out[k], v), (rep, k)
     hev = HipEvents()
-    evs = [hev.create() for _ in range(11)]
+    evs = [hev.create() for _ in range(20)]
     timed = ssd.ssd_bwd(*args, D=inp["D"], chunk_size=128, dfinal_state=dfin, stage_events=evs)
     torch.cuda.synchronize()
     for k, v in ref.items():
         assert torch.equal(timed[k], v), k
-    assert all(hev.elapsed_ms(evs[i], evs[i + 1]) >= 0.0 for i in range(10))
+    assert all(hev.elapsed_ms(evs[2 * k], evs[2 * k + 1]) >= 0.0 for k in range(10))
+    assert all(hev.elapsed_ms(evs[2 * k], evs[2 * k + 1]) > 0.0 for k in (0, 1, 4, 5, 6, 7, 8, 9))
     g2 = torch.cuda.CUDAGraph()
     with pytest.raises(ssd.SsdError) as ei:
         with torch.cuda.graph(g2, stream=cap):

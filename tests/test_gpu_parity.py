@@ -348,17 +348,19 @@ def test_graph_capture_replays_match_eager(dtype):
 
 
 def test_stage_events_time_each_kernel_and_refuse_capture():
-    """ssd_fwd_timed records one event before each kernel and one after the last; on a
+    """ssd_fwd_timed records a start and a stop event with each kernel's dispatch; on a
     capturing stream it refuses (nothing launched) instead of breaking the capture."""
     _say("stage events")
     from state_space_sequence_mamba_amd.timing import HipEvents
     hev = HipEvents()
-    evs = [hev.create() for _ in range(4)]
+    evs = [hev.create() for _ in range(6)]
     inp = {k: v.to(DEV) for k, v in I.make_fwd_inputs(2, 1000, 8, 64, 64, 1, "f32", seed=24).items()}
     y, _ = ssd.ssd_fwd(inp["x"], inp["dt"], inp["dt_bias"], inp["A"], inp["B"], inp["C"], inp["D"],
                        chunk_size=256, stage_events=evs)
     torch.cuda.synchronize()
-    assert all(hev.elapsed_ms(evs[k], evs[k + 1]) > 0 for k in range(3))
+    # each kernel's own start / stop pair, and the kernels in launch order
+    assert all(hev.elapsed_ms(evs[2 * k], evs[2 * k + 1]) > 0 for k in range(3))
+    assert all(hev.elapsed_ms(evs[2 * k + 1], evs[2 * k + 2]) >= 0 for k in range(2))
     y_ref, _ = ssd.ssd_fwd(inp["x"], inp["dt"], inp["dt_bias"], inp["A"], inp["B"], inp["C"], inp["D"],
                            chunk_size=256)
     torch.cuda.synchronize()
