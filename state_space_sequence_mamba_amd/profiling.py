@@ -156,8 +156,10 @@ def summary(args):
             events.setdefault(rl["kernel"], None)
     out = [f"# Kernel trace: {args.workload} (MI355X, gfx950)", "",
            "Command (from the repository root, TMPDIR=/tmp):", "", f"    {args.command}", "",
-           f"Summarised with `python -m state_space_sequence_mamba_amd.profiling summary` from the run's "
-           f"kernel_stats.csv and the JSON line bench.py printed in the same process.", "",
+           "Summarised with `python -m state_space_sequence_mamba_amd.profiling summary` from the run's "
+           "kernel_stats.csv.  The last column is the per-kernel duration bench.py measured with "
+           "dispatch-recorded HIP events in a separate, unprofiled run of the same bench.py command "
+           "on the same box (the profiler's dispatch interception distorts those events).", "",
            "| kernel | calls | rocprofv3 average (us) | share of GPU time | bench.py HIP-event average (us) |",
            "|---|---|---|---|---|"]
     for name, calls, avg, pct in rows:
@@ -165,7 +167,7 @@ def summary(args):
         ev = events.get(key) if key else None
         out.append(f"| `{name}` | {calls} | {avg:.2f} | {pct:.1f} % | {'' if ev is None else f'{ev:.2f}'} |")
     if bench:
-        out += ["", f"bench.py line of this run: `{bench['ms_per_step']}` ms per step, value {bench['value']:.4g} "
+        out += ["", f"Unprofiled bench.py line: `{bench['ms_per_step']}` ms per step, value {bench['value']:.4g} "
                 f"{bench['unit']}, roofline {json.dumps(bench.get('roofline'))}."]
     text = "\n".join(out) + "\n"
     with open(args.out, "w") as fh:
