@@ -56,9 +56,11 @@ def algorithmic_cost(w):
         # (C in, 16 KB blocks out, one per row block and causal column block)
         "chunk_state": dict(bytes=B * L * H * e + 8 * H + cum + x + bc + st + ((bc + cbw) if pre else 0),
                             flops=2 * B * H * L * P * N + (2 * B * G * N * tri if pre else 0)),
-        "state_passing": dict(bytes=2 * st + fin + B * H * nc * 4, flops=2 * B * nc * H * P * N),
+        # bf16 writes the entering states once, rounded to bf16, for the scan
+        "state_passing": dict(bytes=st + (st // 2 if not pre else st) + fin + B * H * nc * 4,
+                              flops=2 * B * nc * H * P * N),
         # fp32 reads the C B^T blocks back once per head; bf16 forms C B^T inside chunk_scan
-        "chunk_scan": dict(bytes=2 * x + (cbr if pre else 2 * bc) + cum + st + H * P * 4,
+        "chunk_scan": dict(bytes=2 * x + (cbr if pre else 2 * bc) + cum + (st if pre else st // 2) + H * P * 4,
                            flops=2 * B * H * P * tri + 2 * B * H * L * N * P + (0 if pre else 2 * B * G * N * tri)),
         # decode: state read + write, x, y, dt, B, C
         "ssd_step": dict(bytes=2 * fin + 2 * B * H * P * e + B * H * e + 2 * B * G * N * e,

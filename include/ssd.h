@@ -80,6 +80,9 @@ typedef struct {
  *   [3] SSD_F32 only: C B^T, computed once per group, (B, nc, G, nrb (nrb + 1) / 2) blocks of
  *       16 x 256 fp32, nrb = chunk_size / 64: the causal 16 x 16 sub-tiles of each pair of
  *       64-row blocks (row block rb, column block J <= rb), in the scan's register order
+ *   [4] SSD_BF16 only: the states entering each chunk rounded to bf16, (B, nc, H, P, N); for
+ *       bf16 inputs region [2] keeps the per-chunk contributions (state_passing writes the
+ *       entering states here instead)
  * The contents after a call are those intermediates and may be inspected. */
 size_t ssd_fwd_workspace_size(const ssd_dims_t* dims, int chunk_size);
 

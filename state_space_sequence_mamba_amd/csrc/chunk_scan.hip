@@ -143,19 +143,14 @@ struct TileRegs {
   }
 };
 
-// Stage the (P x N) fp32 state entering the chunk into LDS as T, n-contiguous rows.
+// Stage the (P x N) state entering the chunk (already in T: fp32 states, or the bf16 copy
+// state_passing writes for bf16 inputs) into LDS, n-contiguous rows.
 template <typename T, int P, int N, int BP>
-__device__ __forceinline__ void stage_prev(T* s_prev, const float* hp, int tid, int nthr) {
-  for (int v = tid; v < P * N / 4; v += nthr) {
-    const int p = (v * 4) / N, n = (v * 4) % N;
-    const float4 f = *reinterpret_cast<const float4*>(hp + (size_t)p * N + n);
-    T* dst = &s_prev[p * BP + n];
-    if (sizeof(T) == 4) {
-      __builtin_memcpy(dst, &f, sizeof(f));
-    } else {
-      T q[4] = {from_f32<T>(f.x), from_f32<T>(f.y), from_f32<T>(f.z), from_f32<T>(f.w)};
-      __builtin_memcpy(dst, q, sizeof(q));
-    }
+__device__ __forceinline__ void stage_prev(T* s_prev, const T* hp, int tid, int nthr) {
+  constexpr int VEC = Vec16<T>::n;
+  for (int v = tid; v < P * N / VEC; v += nthr) {
+    const int p = (v * VEC) / N, n = (v * VEC) % N;
+    *reinterpret_cast<Vec16<T>*>(&s_prev[p * BP + n]) = load16(hp + (size_t)p * N + n);
   }
 }
 
@@ -354,26 +349,21 @@ struct ScalarRegs {
 
 template <typename T, int P, int N, int NTHR>
 struct PrevRegs {
-  static constexpr int U = P * N / 4, K = (U + NTHR - 1) / NTHR;
-  float4 v[K];
-  __device__ __forceinline__ void load(const float* hp, int tid) {
+  static constexpr int VEC = Vec16<T>::n;
+  static constexpr int U = P * N / VEC, K = (U + NTHR - 1) / NTHR;
+  Vec16<T> v[K];
+  __device__ __forceinline__ void load(const T* hp, int tid) {
 #pragma unroll
-    for (int k = 0; k < K; ++k) v[k] = reinterpret_cast<const float4*>(hp)[min(tid + NTHR * k, U - 1)];
+    for (int k = 0; k < K; ++k) v[k] = load16(hp + (size_t)min(tid + NTHR * k, U - 1) * VEC);
   }
   template <int BP>
   __device__ __forceinline__ void store(T* s_prev, int tid) const {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const int u = tid + NTHR * k;
-      if (U % NTHR == 0 || u < U) {              // compile-time true for every instantiated shape
-        const int p = (4 * u) / N, n = (4 * u) % N;
-        T* dst = &s_prev[p * BP + n];
-        if (sizeof(T) == 4) {
-          __builtin_memcpy(dst, &v[k], sizeof(float4));
-        } else {
-          T q[4] = {from_f32<T>(v[k].x), from_f32<T>(v[k].y), from_f32<T>(v[k].z), from_f32<T>(v[k].w)};
-          __builtin_memcpy(dst, q, sizeof(q));
-        }
+      if (U % NTHR == 0 || u < U) {              // compile-time true for most instantiated shapes
+        const int p = (VEC * u) / N, n = (VEC * u) % N;
+        *reinterpret_cast<Vec16<T>*>(&s_prev[p * BP + n]) = v[k];
       }
     }
   }
@@ -387,7 +377,7 @@ __global__ __launch_bounds__(256, 2) void chunk_scan_rows_kernel(const T* __rest
                                                                  const T* __restrict__ Cm,
                                                                  const float* __restrict__ dtp,
                                                                  const float* __restrict__ dAcs,
-                                                                 const float* __restrict__ states,
+                                                                 const T* __restrict__ states,
                                                                  const float* __restrict__ Dw,
                                                                  const T* __restrict__ Z,
                                                                  T* __restrict__ y,
@@ -504,7 +494,7 @@ __global__ __launch_bounds__(512) void chunk_scan_chunk_kernel(const T* __restri
                                                                const T* __restrict__ Cm,
                                                                const float* __restrict__ dtp,
                                                                const float* __restrict__ dAcs,
-                                                               const float* __restrict__ states,
+                                                               const T* __restrict__ states,
                                                                const float* __restrict__ Dw,
                                                                const T* __restrict__ Z,
                                                                T* __restrict__ y,
@@ -619,16 +609,17 @@ __global__ __launch_bounds__(512) void chunk_scan_chunk_kernel(const T* __restri
 
 template <typename T, int P, int N, int HB>
 static hipError_t launch_scan_hb(const FwdArgs& a, hipStream_t s) {
+  const T* prevT = sizeof(T) == 4 ? reinterpret_cast<const T*>(a.states) : static_cast<const T*>(a.prev16);
   if (a.scan_variant == 2) {
     const uint32_t nblocks = (uint32_t)a.B * a.nc * (a.H / HB);
     hipExtLaunchKernelGGL(chunk_scan_chunk_kernel<T, P, N, HB>, dim3(nblocks), dim3(512), 0, s, a.ev0, a.ev1, 0,
         static_cast<const T*>(a.x), static_cast<const T*>(a.Bm), static_cast<const T*>(a.Cm), a.dtp, a.dAcs,
-        a.states, a.D, static_cast<const T*>(a.z), static_cast<T*>(a.y), a.L, a.H, a.G, a.nc, a.Q, nblocks);
+        prevT, a.D, static_cast<const T*>(a.z), static_cast<T*>(a.y), a.L, a.H, a.G, a.nc, a.Q, nblocks);
   } else {
     const uint32_t nblocks = (uint32_t)a.B * a.nc * (a.H / HB) * (a.Q / kKT);
     hipExtLaunchKernelGGL(chunk_scan_rows_kernel<T, P, N, HB>, dim3(nblocks), dim3(256), 0, s, a.ev0, a.ev1, 0,
         static_cast<const T*>(a.x), static_cast<const T*>(a.Bm), a.cb, static_cast<const T*>(a.Cm), a.dtp, a.dAcs,
-        a.states, a.D, static_cast<const T*>(a.z), static_cast<T*>(a.y), a.L, a.H, a.G, a.nc, a.Q, a.B);
+        prevT, a.D, static_cast<const T*>(a.z), static_cast<T*>(a.y), a.L, a.H, a.G, a.nc, a.Q, a.B);
   }
   return hipGetLastError();
 }

@@ -16,7 +16,7 @@
 // pair, which keeps the transposed LDS writes free of bank conflicts.  The next tile's
 // global loads are issued into registers before the current tile's MFMAs.  The per-token
 // weight w_i is folded into x while staging.  Tokens past the end of the sequence are zero.
-// fp32 fragments use the token permutation k = 16*qd + kk so that each lane reads 128 bits.
+// fp32 fragments use the token permutation k = (KT/4) qd + kk so that each lane reads 128 bits.
 #include "cb_tiles.h"
 #include "ssd_common.h"
 #include "ssd_launch.h"
@@ -224,20 +224,20 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const T* __restrict__ 
     __syncthreads();
     if (F32) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
+      for (int m = 0; m < KT / 16; ++m) {
         float4 af[WP], bf[WN];
 #pragma unroll
         for (int i = 0; i < WP; ++i) {
           const int tp = wp * WP + i;
           const int tpc = tp < TP ? tp : TP - 1;  // clamped read, zeroed by select
           const float4 v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(s_x) +
-                                                            (tpc * 16 + r) * PITCH + 16 * qd + 4 * m);
+                                                            (tpc * 16 + r) * PITCH + (KT / 4) * qd + 4 * m);
           af[i] = (tp < TP) ? v : make_float4(0.f, 0.f, 0.f, 0.f);
         }
 #pragma unroll
         for (int j = 0; j < WN; ++j)
           bf[j] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(s_b) +
-                                                   ((wn * WN + j) * 16 + r) * PITCH + 16 * qd + 4 * m);
+                                                   ((wn * WN + j) * 16 + r) * PITCH + (KT / 4) * qd + 4 * m);
 #pragma unroll
         for (int i = 0; i < WP; ++i)
 #pragma unroll

@@ -38,8 +38,15 @@ ssd_status_t check_dims(const ssd_dims_t* d, bool need_seqlen) {
 bool chunk_ok(int q) { return q == 64 || q == 128 || q == 256; }
 
 struct WsLayout {
-  size_t dtp_off, dacs_off, states_off, cb_off, total;
+  size_t dtp_off, dacs_off, states_off, cb_off, prev16_off, total;
 };
+
+// bf16 only: the states entering each chunk rounded to bf16, (B, nc, H, P, N)
+size_t prev16_bytes(const ssd_dims_t* d, int Q) {
+  if (d->dtype != SSD_BF16) return 0;
+  const int64_t nc = (d->seqlen + Q - 1) / Q;
+  return align_up((size_t)d->batch * nc * d->nheads * d->headdim * d->dstate * 2);
+}
 
 // fp32 only: the C B^T sub-tile blocks cb_block writes, (B, nc, G, nrb (nrb + 1) / 2) x 16 KB
 size_t cb_bytes(const ssd_dims_t* d, int Q) {
@@ -57,7 +64,8 @@ WsLayout ws_layout(const ssd_dims_t* d, int Q) {
   w.dacs_off = cum;
   w.states_off = 2 * cum;
   w.cb_off = 2 * cum + st;
-  w.total = 2 * cum + st + cb_bytes(d, Q);
+  w.prev16_off = w.cb_off + cb_bytes(d, Q);
+  w.total = w.prev16_off + prev16_bytes(d, Q);
   return w;
 }
 
@@ -173,6 +181,8 @@ ssd_status_t fwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   a.dAcs = has_seq ? reinterpret_cast<float*>(ws + wl.dacs_off) : nullptr;
   a.states = has_seq ? reinterpret_cast<float*>(ws + wl.states_off) : nullptr;
   a.cb = has_seq && dims->dtype == SSD_F32 ? reinterpret_cast<float*>(ws + wl.cb_off) : nullptr;
+  a.prev16 = has_seq && dims->dtype == SSD_BF16 ? static_cast<void*>(ws + wl.prev16_off) : nullptr;
+  a.keep_f32_states = 0;
   a.scan_variant = pick_scan_variant(a.dtype);
   a.heads_per_block = pick_heads_per_block(a.B, a.nc, a.H, a.G, a.Q, a.scan_variant);
   a.state_from_start = 0;
@@ -205,7 +215,7 @@ ssd_status_t fwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
 // Backward workspace: the forward's regions, the state gradients, per-head dB / dC, per-token
 // and per-chunk partials, and (with a gate) the pre-gate output and the gated gradient.
 struct BwdLayout {
-  size_t dtp, dacs, states, gstates, dBh, dCh, ddir, dSa, dSc, Ub, pA, pbias, pD, ypre, dyg, cb, total;
+  size_t dtp, dacs, states, gstates, dBh, dCh, ddir, dSa, dSc, Ub, pA, pbias, pD, ypre, dyg, cb, prev16, total;
 };
 
 BwdLayout bwd_layout(const ssd_dims_t* d, int Q, bool gate) {
@@ -234,6 +244,7 @@ BwdLayout bwd_layout(const ssd_dims_t* d, int Q, bool gate) {
   w.ypre = o; o += act;
   w.dyg = o; o += act;
   w.cb = o; o += gate ? cb_bytes(d, Q) : 0;
+  w.prev16 = o; o += gate ? prev16_bytes(d, Q) : 0;
   w.total = o;
   return w;
 }
@@ -306,6 +317,8 @@ ssd_status_t bwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   f.dAcs = reinterpret_cast<float*>(ws + wl.dacs);
   f.states = reinterpret_cast<float*>(ws + wl.states);
   f.cb = z && dims->dtype == SSD_F32 ? reinterpret_cast<float*>(ws + wl.cb) : nullptr;   // only the gate needs y~
+  f.prev16 = z && dims->dtype == SSD_BF16 ? static_cast<void*>(ws + wl.prev16) : nullptr;
+  f.keep_f32_states = 1;                              // the backward kernels read the fp32 states
   f.scan_variant = pick_scan_variant(f.dtype);
   f.heads_per_block = pick_heads_per_block(f.B, f.nc, f.H, f.G, f.Q, f.scan_variant);
   f.state_from_start = 0;
@@ -336,6 +349,7 @@ ssd_status_t bwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   gp.init = dfinal_state;
   gp.final_state = dinitial_state;
   gp.passing_reverse = 1;
+  gp.prev16 = nullptr;
   // stage k is timed by ev[2k] (start) and ev[2k + 1] (stop), recorded by the dispatches
   // themselves; stages that launch nothing record both events back to back
   auto timing = [&](ssd::FwdArgs& args, int k) {

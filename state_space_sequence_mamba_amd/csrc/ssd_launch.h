@@ -30,6 +30,9 @@ struct FwdArgs {
   float* dtp;              // workspace (B, H, nc, Q)
   float* dAcs;             // workspace (B, H, nc, Q)
   float* states;           // workspace (B, nc, H, P, N)
+  void* prev16;            // bf16 only: the states entering each chunk rounded to bf16, (B, nc, H, P, N),
+                           // written by state_passing and read by chunk_scan; null: fp32 states
+  int keep_f32_states;     // with prev16: also keep the fp32 states entering each chunk (backward)
   float* cb;               // workspace, fp32 only: C B^T sub-tiles per (b, c, g), see cb_block;
                            // null: chunk_state does not compute them
   int heads_per_block;     // chunk_scan: heads sharing one C B^T evaluation (divides H / G)

@@ -1,6 +1,8 @@
 // state_passing: the inter-chunk recurrence on the chunk states,
 //     H_0 = initial_state (or 0),   H_{c+1} = exp(dAcs[c, last]) * H_c + S_c,
-// writing H_c (the state entering chunk c) over S_c in place and H_nc to final_state.
+// writing H_c (the state entering chunk c) over S_c in place and H_nc to final_state.  For
+// bf16 inputs H_c goes instead (or, for the backward, also) to a bf16 copy, which is all the
+// scan reads: it halves the largest stream of the bf16 forward (P N values per chunk and head).
 // This is the carry step of the chunked scan ("Agent 228: MAMBA-2 Implementation Gaps",
 // Gap 1: the last state of each chunk is carried into the next; the scan-of-block-carries
 // phase of the block-parallel scan in "Agent 230: Comprehensive MAMBA-2 Implementation
@@ -24,6 +26,7 @@ __global__ __launch_bounds__(256) void state_passing_kernel(float* __restrict__ 
                                                             const float* __restrict__ dAcs,
                                                             const float* init,
                                                             float* final_state,
+                                                            __bf16* __restrict__ prev16, int keep_f32,
                                                             int H, int nc, int Q, int PN, int reverse) {
   constexpr int U = 8;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -51,7 +54,16 @@ __global__ __launch_bounds__(256) void state_passing_kernel(float* __restrict__ 
     for (int u = 0; u < U; ++u) {
       if (c0 + u < nc) {
         const int cc = reverse ? nc - 1 - (c0 + u) : c0 + u;
-        *reinterpret_cast<float4*>(s + (size_t)cc * cstride) = hs;
+        if (prev16) {
+          // the scan's bf16 copy: the same rounding it would apply when staging fp32 states
+          bf16x4 q;
+          q[0] = static_cast<__bf16>(hs.x);
+          q[1] = static_cast<__bf16>(hs.y);
+          q[2] = static_cast<__bf16>(hs.z);
+          q[3] = static_cast<__bf16>(hs.w);
+          *reinterpret_cast<bf16x4*>(prev16 + ((size_t)b * nc * H + h) * PN + e4 + (size_t)cc * cstride) = q;
+        }
+        if (!prev16 || keep_f32) *reinterpret_cast<float4*>(s + (size_t)cc * cstride) = hs;
         hs.x = dec[u] * hs.x + buf[u].x;
         hs.y = dec[u] * hs.y + buf[u].y;
         hs.z = dec[u] * hs.z + buf[u].z;
@@ -66,7 +78,7 @@ hipError_t launch_state_passing(const FwdArgs& a, hipStream_t s) {
   const int PN = a.P * a.N;
   dim3 grid((PN / 4 + 255) / 256, a.H, a.B);
   hipExtLaunchKernelGGL(state_passing_kernel, grid, dim3(256), 0, s, a.ev0, a.ev1, 0, a.states, a.dAcs, a.init,
-                        a.final_state, a.H, a.nc, a.Q, PN,
+                        a.final_state, static_cast<__bf16*>(a.prev16), a.keep_f32_states, a.H, a.nc, a.Q, PN,
                                             a.passing_reverse);
   return hipGetLastError();
 }

@@ -65,9 +65,10 @@ def test_workspace_size_layout(lib):
     # states: 4 chunks * 4 heads * 16 * 16 floats = 16384 B; fp32 adds C B^T once per group:
     # 4 chunks * 1 group * 1 block pair (Q/64 = 1) * 16 KB = 65536 B
     assert ssd.ssd_fwd_workspace_size(_dims(), 64) == 2 * 4096 + 16384 + 65536
-    # ragged: L=300, Q=128 -> nc=3; 2*4*3*128*4 = 12288 B each; states 2*3*4*64*128*4 = 786432 B
+    # ragged: L=300, Q=128 -> nc=3; 2*4*3*128*4 = 12288 B each; states 2*3*4*64*128*4 = 786432 B;
+    # bf16 adds the entering states rounded to bf16: 786432 / 2 B
     d = _dims(batch=2, seqlen=300, headdim=64, dstate=128, dtype=1)
-    assert ssd.ssd_fwd_workspace_size(d, 128) == 2 * 12288 + 786432
+    assert ssd.ssd_fwd_workspace_size(d, 128) == 2 * 12288 + 786432 + 393216
     # 1 x 5 tokens, H=3, Q=64: 3*64*4 = 768 B (already 256-aligned); states 3*16*16*4 = 3072; C B^T 16 KB
     assert ssd.ssd_fwd_workspace_size(_dims(seqlen=5, nheads=3), 64) == 2 * 768 + 3072 + 16384
     # alignment padding: H=1, L=1, Q=64 -> 256 B regions
