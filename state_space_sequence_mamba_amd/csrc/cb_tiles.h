@@ -59,10 +59,12 @@ template <int N> struct NDot<__bf16, N> {
 // order of the scan's A operand: sub-tile (w, js), lane l, element e at ((4 w + js) 64 + l) 4 + e,
 // i.e. lane (r, qd) holds CB[i = 16 (4 rb + w) + r][j = 16 (4 J + js) + 4 qd + e].  The MFMA
 // sequence is the scan's own, so results are bit-identical to computing in place.  Sub-tiles
-// past the diagonal and rows past the sequence are zeros.  Four wavefronts, one per strip.
+// past the diagonal and rows past the sequence are zeros.  Four wavefronts (tid in [0, 256)),
+// one per strip.
 template <int N>
 __device__ __forceinline__ void cb_block(const float* __restrict__ Bm, const float* __restrict__ Cm,
-                                         float* __restrict__ cb, int L, int G, int nc, int Q, uint32_t id) {
+                                         float* __restrict__ cb, int L, int G, int nc, int Q, uint32_t id,
+                                         int tid) {
   typedef NDot<float, N> ND;
   const int nrb = Q / kCbKT, nblk = nrb * (nrb + 1) / 2;
   const int blk = id % nblk;
@@ -74,7 +76,7 @@ __device__ __forceinline__ void cb_block(const float* __restrict__ Bm, const flo
   while ((rb + 1) * (rb + 2) / 2 <= blk) ++rb;
   const int J = blk - rb * (rb + 1) / 2;
   const int t0 = c * Q, len = min(Q, L - t0);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63, w = tid >> 6;
   const int r = lane & 15, qd = lane >> 4;
   const int strip = 4 * rb + w;
   const size_t bc_tok = (size_t)G * N;

@@ -264,6 +264,20 @@ __device__ __forceinline__ void diag_tile(f32x4 (&acc)[HB][TPof<P>::v], const ty
   }
 }
 
+// Staged tile J entirely below the diagonal of one strip (4 J + 3 < strip): four unmasked
+// sub-tiles in one straight-line block, so the LDS reads of one sub-tile overlap the MFMAs of
+// the one before.
+template <typename T, int P, int N, int HB, int BP, int XP, bool PRECB = false>
+__device__ __forceinline__ void full_tile(f32x4 (&acc)[HB][TPof<P>::v], const typename NDot<T, N>::frag& cf,
+                                          const float (&dco)[HB][TPof<P>::v], const T* s_b, const T* s_x,
+                                          const float (*s_da)[256], const float (*s_dt)[256], int strip, int J,
+                                          int lstrip, int r, int qd) {
+#pragma unroll
+  for (int js = 0; js < 4; ++js)
+    sub_tile<T, P, N, HB, BP, XP, false, PRECB>(acc, cf, dco, s_b, s_x, s_da, s_dt, strip, 4 * J + js, js, lstrip,
+                                                r, qd);
+}
+
 // Output gate y * silu(z) on one strip's registers (rows 16 strip + 4 qd + e, column 16 pt + r).
 // All z loads are issued before use; rows past the sequence read a clamped address.
 template <typename T, int P, int HB>
@@ -371,7 +385,7 @@ struct PrevRegs {
 
 // ---------------------------------------------------------------- row-block decomposition
 template <typename T, int P, int N, int HB>
-__global__ __launch_bounds__(256, 2) void chunk_scan_rows_kernel(const T* __restrict__ x,
+__global__ __launch_bounds__(256, (sizeof(T) == 4 && HB == 1) ? 4 : 2) void chunk_scan_rows_kernel(const T* __restrict__ x,
                                                                  const T* __restrict__ Bm,
                                                                  const float* __restrict__ cbp,
                                                                  const T* __restrict__ Cm,
@@ -473,8 +487,12 @@ __global__ __launch_bounds__(256, 2) void chunk_scan_rows_kernel(const T* __rest
     tr.template store<SL::BP, SL::XP>(s_b, s_xu, tid);
     if (J < rb) tr.load(Bb, xb, (uint32_t)bc_tok, (uint32_t)x_tok, J + 1, len, tid);
     __syncthreads();
-    if (strip_ok)
-      diag_tile<T, P, N, HB, SL::BP, SL::XP, PRECB>(acc, cf, dco, s_b, s_xu, s_da, s_dt, s, J, wave, r, qd);
+    if (strip_ok) {
+      if (J < rb)
+        full_tile<T, P, N, HB, SL::BP, SL::XP, PRECB>(acc, cf, dco, s_b, s_xu, s_da, s_dt, s, J, wave, r, qd);
+      else
+        diag_tile<T, P, N, HB, SL::BP, SL::XP, PRECB>(acc, cf, dco, s_b, s_xu, s_da, s_dt, s, J, wave, r, qd);
+    }
   }
   if (Z && strip_ok) apply_gate<T, P, HB>(acc, Z, (size_t)b * L + t0, x_tok, h0, s, len, r, qd);
   const int rows = min(kKT, len - rb * kKT);
@@ -587,9 +605,12 @@ __global__ __launch_bounds__(512) void chunk_scan_chunk_kernel(const T* __restri
     if (J + 1 < ntiles) tr.load(Bb, xb, (uint32_t)bc_tok, (uint32_t)x_tok, J + 1, len, tid);
     __syncthreads();
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
-      if (ok[st] && 4 * J <= strip[st])
+    for (int st = 0; st < 2; ++st) {
+      if (ok[st] && 4 * J + 3 < strip[st])
+        full_tile<T, P, N, HB, SL::BP, SL::XP>(acc[st], cf[st], dco, s_b, s_xu, s_da, s_dt, strip[st], J, 0, r, qd);
+      else if (ok[st] && 4 * J <= strip[st])
         diag_tile<T, P, N, HB, SL::BP, SL::XP>(acc[st], cf[st], dco, s_b, s_xu, s_da, s_dt, strip[st], J, 0, r, qd);
+    }
   }
   if (Z) {
 #pragma unroll

@@ -8,9 +8,10 @@
 // The backward pass reuses it with (dy, C) in place of (x, B) and w_i = exp(dAcs[i]): the
 // gradient that chunk c's outputs send into the state entering the chunk.
 //
-// One workgroup (4 wavefronts) per (b, c, h); its wavefront 0 first computes the chunk's dt'
-// and their cumsum (chunk_cumsum_wave below), which the other kernels read from the
-// workspace.  A (P x Q) . (Q x N) product on MFMA with fp32 accumulation.  The contraction runs over tokens, the slow axis of x and B in HBM, so
+// One workgroup (8 wavefronts, two 16x16 output tiles each at P = N = 64) per (b, c, h);
+// its wavefront 0 first computes the chunk's dt' and their cumsum (chunk_cumsum_wave
+// below), which the other kernels read from the workspace.  A (P x Q) . (Q x N) product on
+// MFMA with fp32 accumulation.  The contraction runs over tokens, the slow axis of x and B in HBM, so
 // 64-token tiles are staged transposed in LDS (token-contiguous rows): each thread loads
 // the same 16-byte column slice of two consecutive tokens and writes them as one packed
 // pair, which keeps the transposed LDS writes free of bank conflicts.  The next tile's
@@ -78,8 +79,8 @@ __device__ __forceinline__ void chunk_cumsum_wave(const T* __restrict__ dt, floa
 // own (b, c, h)); fp32 launches add workgroups [nblocks, ...) that compute the C B^T blocks
 // the scan reads (cb_block), filling the tail of the grid.  Backward (from_start): dt' and the
 // cumsum are read from the workspace.
-template <typename T, int P, int N>
-__global__ __launch_bounds__(256) void chunk_state_kernel(const T* __restrict__ x,
+template <typename T, int P, int N, int NTHR>
+__global__ __launch_bounds__(NTHR) void chunk_state_kernel(const T* __restrict__ x,
                                                           const T* __restrict__ Bm,
                                                           const T* __restrict__ Cm,
                                                           const T* __restrict__ dt,
@@ -90,12 +91,14 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const T* __restrict__ 
                                                           float* __restrict__ states,
                                                           float* __restrict__ cb,
                                                           int L, int H, int G, int nc, int Q,
-                                                          uint32_t nblocks, int from_start, int clamp,
+                                                          uint32_t nblocks, uint32_t ncb, int from_start, int clamp,
                                                           float lo, float hi) {
   if (blockIdx.x >= nblocks) {
-    if constexpr (sizeof(T) == 4) cb_block<N>(reinterpret_cast<const float*>(Bm),
-                                              reinterpret_cast<const float*>(Cm), cb, L, G, nc, Q,
-                                              blockIdx.x - nblocks);
+    // NTHR / 256 blocks per workgroup, four wavefronts each
+    const uint32_t id = (blockIdx.x - nblocks) * (NTHR / 256) + threadIdx.x / 256;
+    if constexpr (sizeof(T) == 4)
+      if (id < ncb) cb_block<N>(reinterpret_cast<const float*>(Bm), reinterpret_cast<const float*>(Cm), cb, L, G,
+                                nc, Q, id, threadIdx.x & 255);
     return;
   }
   constexpr bool F32 = sizeof(T) == 4;
@@ -104,11 +107,12 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const T* __restrict__ 
   constexpr int VEC = Vec16<T>::n;
   constexpr int PV = P / VEC, NV = N / VEC;
   constexpr int XU = (KT / 2) * PV, BU = (KT / 2) * NV;  // token-pair units per tile
-  constexpr int XPT = (XU + 255) / 256, BPT = (BU + 255) / 256;
+  constexpr int XPT = (XU + NTHR - 1) / NTHR, BPT = (BU + NTHR - 1) / NTHR;
   constexpr int TP = P / 16, TN = N / 16;
   // wavefront layout over the (TP x TN) grid of 16x16 output tiles
-  constexpr int WAVES_N = TN < 4 ? TN : 4;
-  constexpr int WAVES_P = 4 / WAVES_N;
+  constexpr int NW = NTHR / 64;
+  constexpr int WAVES_N = TN < NW ? TN : NW;
+  constexpr int WAVES_P = NW / WAVES_N;
   constexpr int WN = TN / WAVES_N;
   constexpr int WP = (TP + WAVES_P - 1) / WAVES_P;
 
@@ -142,7 +146,7 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const T* __restrict__ 
     okm = 0;
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {
-      const int v = min(tid + 256 * u, XU - 1);
+      const int v = min(tid + NTHR * u, XU - 1);
       const int m = v % (KT / 2), pv = (v / (KT / 2)) * VEC;
       const int tok = k0 + 2 * m;
       const bool ok0 = tok < len, ok1 = tok + 1 < len;
@@ -152,7 +156,7 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const T* __restrict__ 
     }
 #pragma unroll
     for (int u = 0; u < BPT; ++u) {
-      const int v = min(tid + 256 * u, BU - 1);
+      const int v = min(tid + NTHR * u, BU - 1);
       const int m = v % (KT / 2), nv = (v / (KT / 2)) * VEC;
       const int tok = k0 + 2 * m;
       const bool ok0 = tok < len, ok1 = tok + 1 < len;
@@ -164,8 +168,8 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const T* __restrict__ 
   auto store_tile = [&](int k0) {
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {
-      const int v = tid + 256 * u;
-      if (v < XU) {
+      const int v = tid + NTHR * u;
+      if (XU % NTHR == 0 || v < XU) {
         const int m = v % (KT / 2), pv = (v / (KT / 2)) * VEC;
         const float w0 = s_w[k0 + 2 * m], w1 = s_w[k0 + 2 * m + 1];
         const Vec16<T> x0 = keep_if(xr[u][0], (okm >> (2 * u)) & 1u);
@@ -179,8 +183,8 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const T* __restrict__ 
     }
 #pragma unroll
     for (int u = 0; u < BPT; ++u) {
-      const int v = tid + 256 * u;
-      if (v < BU) {
+      const int v = tid + NTHR * u;
+      if (BU % NTHR == 0 || v < BU) {
         const int m = v % (KT / 2), nv = (v / (KT / 2)) * VEC;
         const Vec16<T> b0 = keep_if(br[u][0], (okm >> (2 * XPT + 2 * u)) & 1u);
         const Vec16<T> b1 = keep_if(br[u][1], (okm >> (2 * XPT + 2 * u + 1)) & 1u);
@@ -206,7 +210,7 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const T* __restrict__ 
   if (from_start) {
     // backward: decay from the chunk's start, exp(dAcs_i), which weighs each output's
     // gradient into the state entering the chunk
-    for (int i = tid; i < Q; i += 256) s_w[i] = expf(dA_c[i]);
+    for (int i = tid; i < Q; i += NTHR) s_w[i] = expf(dA_c[i]);
   } else {
     // forward: decay to the chunk's end times the step
     if (wave == 0)
@@ -214,7 +218,7 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const T* __restrict__ 
                            s_d, s_cs, lane);
     __syncthreads();
     const float last = s_cs[Q - 1];
-    for (int i = tid; i < Q; i += 256) s_w[i] = expf(last - s_cs[i]) * s_d[i];
+    for (int i = tid; i < Q; i += NTHR) s_w[i] = expf(last - s_cs[i]) * s_d[i];
   }
 
   for (int k0 = 0; k0 < len; k0 += KT) {
@@ -293,10 +297,12 @@ static hipError_t launch_state_impl(const FwdArgs& a, hipStream_t s) {
   const uint32_t ncb = (sizeof(T) == 4 && a.cb && !a.state_from_start)
                            ? (uint32_t)a.B * a.nc * a.G * (nrb * (nrb + 1) / 2) : 0u;
   if (nblocks + ncb == 0) return hipSuccess;
-  hipExtLaunchKernelGGL(chunk_state_kernel<T, P, N>, dim3(nblocks + ncb), dim3(256), 0, s, a.ev0, a.ev1, 0,
-      static_cast<const T*>(a.x), static_cast<const T*>(a.Bm), static_cast<const T*>(a.Cm),
+  constexpr int NTHR = 512;
+  const uint32_t ncb_wg = (ncb + NTHR / 256 - 1) / (NTHR / 256);
+  hipExtLaunchKernelGGL(chunk_state_kernel<T, P, N, NTHR>, dim3(nblocks + ncb_wg), dim3(NTHR), 0, s, a.ev0, a.ev1,
+      0, static_cast<const T*>(a.x), static_cast<const T*>(a.Bm), static_cast<const T*>(a.Cm),
       static_cast<const T*>(a.dt), a.dt_bias, a.A, a.dtp, a.dAcs, a.states, a.cb, a.L, a.H, a.G, a.nc, a.Q,
-      nblocks, a.state_from_start, a.clamp, a.dt_lo, a.dt_hi);
+      nblocks, ncb, a.state_from_start, a.clamp, a.dt_lo, a.dt_hi);
   return hipGetLastError();
 }
 
