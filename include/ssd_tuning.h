@@ -16,7 +16,7 @@ extern "C" {
  *        1 or 2; 0 restores the built-in choice; ignored unless it divides nheads / ngroups.
  * key 1: minimum chunk_scan workgroup count the built-in choice aims for (default 512).
  * key 2: chunk_scan decomposition: 1 = one workgroup per 64-row block of a chunk,
- *        2 = one workgroup per whole chunk, 0 = built-in choice (1 for fp32, 2 for bf16).
+ *        2 = one workgroup per whole chunk, 0 = built-in choice (1).
  * key 3: tokens per thread of ssd_conv1d_silu (rounded up to a multiple of 4); 0 restores
  *        the built-in choice (64, fewer on small inputs).
  * Unknown keys are ignored. */

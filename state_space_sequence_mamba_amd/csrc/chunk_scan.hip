@@ -22,11 +22,12 @@
 //
 // Two decompositions share these pieces:
 //  * rows : one workgroup (4 wavefronts, one strip each) per 64-row block of a chunk and
-//           head block; row blocks with more causal tiles are dispatched first.  Many small
-//           workgroups: suits compute-bound (fp32) problems.
+//           head; row blocks with more causal tiles are dispatched first.  Many small
+//           workgroups, four per CU; x tiles are re-read by later row blocks (mostly from L2).
+//           The default for both dtypes.
 //  * chunk: one workgroup (8 wavefronts) per whole chunk and head block; wavefront w owns
 //           the strip pair (w, S-1-w), S+1 sub-tiles each.  x, the carried state and y move
-//           exactly once: suits memory-bound (bf16) problems.
+//           exactly once, but the register footprint allows one workgroup per CU.
 // Token tiles (64 tokens of B and of x for every head) are loaded into registers one tile
 // ahead of the MFMA work, then written to LDS.  y leaves through LDS as 16-byte row stores.
 //
@@ -385,7 +386,7 @@ struct PrevRegs {
 
 // ---------------------------------------------------------------- row-block decomposition
 template <typename T, int P, int N, int HB>
-__global__ __launch_bounds__(256, (sizeof(T) == 4 && HB == 1) ? 4 : 2) void chunk_scan_rows_kernel(const T* __restrict__ x,
+__global__ __launch_bounds__(256, HB == 1 ? 4 : 2) void chunk_scan_rows_kernel(const T* __restrict__ x,
                                                                  const T* __restrict__ Bm,
                                                                  const float* __restrict__ cbp,
                                                                  const T* __restrict__ Cm,
@@ -415,6 +416,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && HB == 1) ? 4 : 2) void chun
   const uint32_t hw = blockIdx.x;
   uint32_t cls, unit;
   if ((U & 7u) == 0) {
+    // heaviest row blocks first, every XCD an equal share of each class
     const uint32_t per = U >> 3, seq = hw >> 3;
     cls = seq / per;
     unit = (hw & 7u) * per + seq % per;

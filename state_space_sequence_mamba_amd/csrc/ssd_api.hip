@@ -89,12 +89,16 @@ bool device_ptr_ok(const void* p) {
 // further but leave fewer workgroups to fill 256 CUs.
 int g_tune_heads_per_block = 0;  // 0 = heuristic
 int g_tune_min_blocks = 512;
-int g_tune_scan_variant = 0;     // 0 = by dtype
+int g_tune_scan_variant = 0;     // 0 = built-in (row blocks)
 int g_tune_conv_segment = 0;     // 0 = sized to the chip
 
+// Row blocks for both dtypes: measured on MI355X, fp32 B4 L1024 H24 39 us against 68 us for
+// whole chunks; bf16 B8 L4096 H32 N128 191 us against 208 us (bf16 B2 L16384 H80 G8: 545 us
+// against 519 us, the one shape measured where whole chunks win).
 int pick_scan_variant(int dtype) {
+  (void)dtype;
   if (g_tune_scan_variant == 1 || g_tune_scan_variant == 2) return g_tune_scan_variant;
-  return dtype == SSD_F32 ? 1 : 2;
+  return 1;
 }
 
 int pick_heads_per_block(int B, int nc, int H, int G, int Q, int variant) {
@@ -104,12 +108,12 @@ int pick_heads_per_block(int B, int nc, int H, int G, int Q, int variant) {
     for (int hb : kChoices)
       if (hb == g_tune_heads_per_block && hpg % hb == 0) return hb;
   }
-  // workgroups per head of a group; the row-block kernel needs more of them (its units are
-  // small and uneven), so it aims for twice the target
-  const long per_head = (long)B * nc * G * (variant == 1 ? Q / 64 : 1);
-  const long target = (long)g_tune_min_blocks * (variant == 1 ? 2 : 1);
+  // row blocks: one head per workgroup (a second head's accumulators would halve occupancy)
+  if (variant == 1) return 1;
+  // whole chunks: the largest head block that still leaves enough workgroups
+  const long per_head = (long)B * nc * G;
   for (int hb : kChoices)
-    if (hpg % hb == 0 && per_head * (hpg / hb) >= target) return hb;
+    if (hpg % hb == 0 && per_head * (hpg / hb) >= g_tune_min_blocks) return hb;
   return 1;
 }
 
