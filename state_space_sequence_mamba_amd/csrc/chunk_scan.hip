@@ -449,9 +449,10 @@ __global__ __launch_bounds__(256, HB == 1 ? 4 : 2) void chunk_scan_rows_kernel(c
                       : Bm + ((size_t)b * L + t0) * bc_tok + (size_t)g * N;
   const T* xb = x + ((size_t)b * L + t0) * x_tok + (size_t)h0 * P;
 
-  // prologue: every global load in flight before the first wait
-  TileRegs<T, P, N, HB, NTHR, PRECB> tr;
-  tr.load(Bb, xb, (uint32_t)bc_tok, (uint32_t)x_tok, 0, len, tid);
+  // prologue: every global load in flight before the first wait, those of the carried term
+  // first: loads complete in order, so the carried term's MFMAs need not wait for tile 0.
+  // C rows past the sequence read row 0 unmasked: they only reach output rows that are
+  // never stored.
   ScalarRegs<HB, NTHR> sr;
   sr.load(dtp, dAcs, b, H, h0, nc, c, Q, tid);
   PrevRegs<T, P, N, NTHR> pr;
@@ -459,13 +460,15 @@ __global__ __launch_bounds__(256, HB == 1 ? 4 : 2) void chunk_scan_rows_kernel(c
   typename ND::frag cf;
   {
     const int i = 16 * s + r;
-    ND::load(cf, Cb + (size_t)(i < len ? i : 0) * bc_tok, qd, i < len);
+    ND::load(cf, Cb + (size_t)(i < len ? i : 0) * bc_tok, qd);
   }
   float dco[HB][TP];
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh)
 #pragma unroll
     for (int pt = 0; pt < TP; ++pt) dco[hh][pt] = Dw ? Dw[(size_t)(h0 + hh) * P + pt * 16 + r] : 0.f;
+  TileRegs<T, P, N, HB, NTHR, PRECB> tr;
+  tr.load(Bb, xb, (uint32_t)bc_tok, (uint32_t)x_tok, 0, len, tid);
 
   f32x4 acc[HB][TP];
 #pragma unroll
@@ -557,9 +560,8 @@ __global__ __launch_bounds__(512) void chunk_scan_chunk_kernel(const T* __restri
   const T* Bb = Bm + ((size_t)b * L + t0) * bc_tok + (size_t)g * N;
   const T* xb = x + ((size_t)b * L + t0) * x_tok + (size_t)h0 * P;
 
-  // prologue: every global load in flight before the first wait
-  TileRegs<T, P, N, HB, NTHR> tr;
-  tr.load(Bb, xb, (uint32_t)bc_tok, (uint32_t)x_tok, 0, len, tid);
+  // prologue: every global load in flight before the first wait, those of the carried term
+  // first (as in the row-block kernel)
   ScalarRegs<HB, NTHR> sr;
   sr.load(dtp, dAcs, b, H, h0, nc, c, Q, tid);
   PrevRegs<T, P, N, NTHR> pr;
@@ -569,13 +571,15 @@ __global__ __launch_bounds__(512) void chunk_scan_chunk_kernel(const T* __restri
   for (int st = 0; st < 2; ++st) {
     const int i = 16 * strip[st] + r;
     const bool in = active && i < len;
-    ND::load(cf[st], Cb + (size_t)(in ? i : 0) * bc_tok, qd, in);
+    ND::load(cf[st], Cb + (size_t)(in ? i : 0) * bc_tok, qd);
   }
   float dco[HB][TP];
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh)
 #pragma unroll
     for (int pt = 0; pt < TP; ++pt) dco[hh][pt] = Dw ? Dw[(size_t)(h0 + hh) * P + pt * 16 + r] : 0.f;
+  TileRegs<T, P, N, HB, NTHR> tr;
+  tr.load(Bb, xb, (uint32_t)bc_tok, (uint32_t)x_tok, 0, len, tid);
 
   f32x4 acc[2][HB][TP];
 #pragma unroll
