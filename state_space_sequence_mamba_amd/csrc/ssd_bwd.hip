@@ -25,10 +25,10 @@
 //   bwd_reduce_*: per-head dB, dC summed over the heads of each group; parameter partials
 //                 summed in a fixed order (results are run-to-run deterministic)
 //   gate_bwd:  dy = dout silu(z) and dz = dout y~ silu'(z)
-// Tiles are staged in LDS as fp32 with an odd row pitch, so that both the row-broadcast
-// and the column-stride reads of the 64 x 64 products are free of bank conflicts.  A
-// thread (tr, tc) = (tid / 16, tid % 16) owns rows 4 tr .. 4 tr + 3 and the columns
-// tc + 16 m of every 64-row product.
+// Token tiles are staged in LDS in the input dtype (bf16 -> fp32 is exact, so the fp32 MFMA
+// arithmetic is the same either way and bf16 tiles take half the LDS), with row pitches that
+// start consecutive rows on different banks; the fp32 state tiles (Hprev, Gnext) reuse the
+// space of the token tiles once those are consumed.
 #include "ssd_common.h"
 #include "ssd_launch.h"
 
@@ -36,33 +36,55 @@ namespace ssd {
 
 namespace {
 constexpr int KT = 64;   // tokens per tile (row block)
+constexpr float kLog2e = 1.4426950408889634f;
 
-// Stage `nvalid` token rows of width W (row stride `stride` elements) as fp32 rows of pitch
-// W + 4 (16-byte aligned), zero rows after.
+// LDS row pitch (elements) of a W-wide tile of S: 16-byte aligned rows whose start banks
+// differ from row to row.
+template <typename S, int W> struct Pitch { static constexpr int v = W + (sizeof(S) == 4 ? 4 : 8); };
+
+// Four consecutive tile elements, or one, as fp32 (bf16 -> fp32 is exact).
+__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 ld4(const __bf16* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xffff0000u));
+}
+__device__ __forceinline__ float ld1(const float* p) { return *p; }
+__device__ __forceinline__ float ld1(const __bf16* p) { return static_cast<float>(*p); }
+
+// KT token rows of width W (row stride `stride` elements), held in registers between their
+// global loads and their LDS stores (pitch Pitch<T, W>), so that the next tile's loads are in
+// flight during the current tile's MFMAs.  Rows past `nvalid` read row 0 and are zeroed at
+// store time (a select at load time would wait for the data there).
 template <typename T, int W>
-__device__ __forceinline__ void stage_rows(float* dst, const T* src, size_t stride, int nvalid, int tid) {
-  constexpr int VEC = Vec16<T>::n, WV = W / VEC, UNITS = KT * WV, NIT = (UNITS + 255) / 256;
+struct RowTile {
+  static constexpr int VEC = Vec16<T>::n, WV = W / VEC, UNITS = KT * WV, NIT = (UNITS + 255) / 256;
+  static_assert(NIT <= 32, "validity mask");
   Vec16<T> v[NIT];
+  uint32_t okm;
+  __device__ __forceinline__ void load(const T* src, size_t stride, int nvalid, int tid) {
+    okm = 0;
 #pragma unroll
-  for (int k = 0; k < NIT; ++k) {
-    const int u = min(tid + 256 * k, UNITS - 1);
-    const int tok = u / WV, cv = (u % WV) * VEC;
-    v[k] = load16_if(src + (size_t)(tok < nvalid ? tok : 0) * stride + cv, tok < nvalid);
-  }
-#pragma unroll
-  for (int k = 0; k < NIT; ++k) {
-    const int u = tid + 256 * k;
-    if (u < UNITS) {
+    for (int k = 0; k < NIT; ++k) {
+      const int u = min(tid + 256 * k, UNITS - 1);
       const int tok = u / WV, cv = (u % WV) * VEC;
-      float f[VEC];
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) f[e] = to_f32(v[k].v[e]);
-#pragma unroll
-      for (int e = 0; e < VEC; e += 4)
-        *reinterpret_cast<float4*>(dst + tok * (W + 4) + cv + e) = make_float4(f[e], f[e + 1], f[e + 2], f[e + 3]);
+      const bool ok = tok < nvalid;
+      v[k] = load16(src + (size_t)(ok ? tok : 0) * stride + cv);
+      okm |= (uint32_t)ok << k;
     }
   }
-}
+  __device__ __forceinline__ void store(T* dst, int tid) const {
+    constexpr int PW = Pitch<T, W>::v;
+#pragma unroll
+    for (int k = 0; k < NIT; ++k) {
+      const int u = tid + 256 * k;
+      if (UNITS % 256 == 0 || u < UNITS) {
+        const int tok = u / WV, cv = (u % WV) * VEC;
+        *reinterpret_cast<Vec16<T>*>(dst + tok * PW + cv) = keep_if(v[k], (okm >> k) & 1u);
+      }
+    }
+  }
+};
 
 // Stage a (P x N) fp32 state as rows of pitch N + 4.
 template <int P, int N>
@@ -80,14 +102,14 @@ __device__ __forceinline__ void stage_state(float* dst, const float* src, int ti
 
 // One 16 x 16 tile of A Bt^T over a contraction of length K along both operands' rows:
 //   out[i][j] += sum_k A[i][k] * Bt[j][k]     (A, Bt: 16 rows each, pitch PA / PB)
-// Lane (r, qd) feeds A row r and Bt row r with k = (K/4) qd + 4 m + c, one 128-bit LDS read
-// each per four MFMAs; it receives out[4 qd + e][r].
-template <int K, int PA, int PB>
-__device__ __forceinline__ f32x4 mm_rows(f32x4 acc, const float* A, const float* Bt, int r, int qd) {
+// Lane (r, qd) feeds A row r and Bt row r with k = (K/4) qd + 4 m + c, one LDS read each per
+// four MFMAs; it receives out[4 qd + e][r].
+template <int K, int PA, int PB, typename SA, typename SB>
+__device__ __forceinline__ f32x4 mm_rows(f32x4 acc, const SA* A, const SB* Bt, int r, int qd) {
 #pragma unroll
   for (int m = 0; m < K / 16; ++m) {
-    const float4 a = *reinterpret_cast<const float4*>(A + r * PA + (K / 4) * qd + 4 * m);
-    const float4 b = *reinterpret_cast<const float4*>(Bt + r * PB + (K / 4) * qd + 4 * m);
+    const float4 a = ld4(A + r * PA + (K / 4) * qd + 4 * m);
+    const float4 b = ld4(Bt + r * PB + (K / 4) * qd + 4 * m);
     acc = mfma_16x16x4_f32(a.x, b.x, acc);
     acc = mfma_16x16x4_f32(a.y, b.y, acc);
     acc = mfma_16x16x4_f32(a.z, b.z, acc);
@@ -99,21 +121,21 @@ __device__ __forceinline__ f32x4 mm_rows(f32x4 acc, const float* A, const float*
 // out[i][c] += sum_k M[k][i] * V[k][c] over the 16 k of one tile, where lane (r, qd) holds
 // M[k = 4 qd + e][i = r] in m[e] (the result layout of mm_rows, used directly as the A
 // operand), and V rows k (pitch PV) are read from LDS at column c0 + r.
-template <int PV>
-__device__ __forceinline__ f32x4 mm_regs(f32x4 acc, const f32x4& m, const float* V, int c0, int r, int qd) {
+template <int PV, typename SV>
+__device__ __forceinline__ f32x4 mm_regs(f32x4 acc, const f32x4& m, const SV* V, int c0, int r, int qd) {
 #pragma unroll
-  for (int e = 0; e < 4; ++e) acc = mfma_16x16x4_f32(m[e], V[(4 * qd + e) * PV + c0 + r], acc);
+  for (int e = 0; e < 4; ++e) acc = mfma_16x16x4_f32(m[e], ld1(V + (4 * qd + e) * PV + c0 + r), acc);
   return acc;
 }
 
-// out[i][c] += sum_k A[i][k] * V[k][c] over K, A rows i (pitch PA) and V rows k (pitch PV) in
-// LDS; lane (r, qd) reads A row r as 128-bit runs and V column c0 + r.
-template <int K, int PA, int PV>
-__device__ __forceinline__ f32x4 mm_cols(f32x4 acc, const float* A, const float* V, int c0, int r, int qd) {
+// out[i][c] += sum_k A[i][k] * V[k][c] over K, A rows i (pitch PA) and fp32 V rows k (pitch PV)
+// in LDS; lane (r, qd) reads A row r as runs of four and V column c0 + r.
+template <int K, int PA, int PV, typename SA>
+__device__ __forceinline__ f32x4 mm_cols(f32x4 acc, const SA* A, const float* V, int c0, int r, int qd) {
 #pragma unroll
   for (int m = 0; m < K / 16; ++m) {
     const int k0 = (K / 4) * qd + 4 * m;
-    const float4 a = *reinterpret_cast<const float4*>(A + r * PA + k0);
+    const float4 a = ld4(A + r * PA + k0);
     acc = mfma_16x16x4_f32(a.x, V[(k0 + 0) * PV + c0 + r], acc);
     acc = mfma_16x16x4_f32(a.y, V[(k0 + 1) * PV + c0 + r], acc);
     acc = mfma_16x16x4_f32(a.z, V[(k0 + 2) * PV + c0 + r], acc);
@@ -139,7 +161,8 @@ __device__ __forceinline__ float sum_qd(float v) {
 // ------------------------------------------------------------------ anti-causal: dx, dB
 // Wavefront w owns the 16 columns j = 16 w .. 16 w + 15 of the row block R: it computes the
 // (i, j) tiles of C B^T and dy x^T for every i of the block I, weights them in registers,
-// and feeds them straight into xi[j][:] and dB[j][:] as MFMA A operands.
+// and feeds them straight into xi[j][:] and dB[j][:] as MFMA A operands.  The tiles of block
+// I + 1 are loaded into registers while block I is computed.
 template <typename T, int P, int N>
 __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, const T* __restrict__ Bm,
                                                        const T* __restrict__ Cm, const T* __restrict__ dy,
@@ -150,13 +173,17 @@ __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, 
                                                        float* __restrict__ dSa, float* __restrict__ Ub,
                                                        float* __restrict__ pD, int L, int H, int G, int nc, int Q,
                                                        uint32_t nblocks) {
-  constexpr int PP = P + 4, NP = N + 4, TPm = P / 16, TNm = N / 16;
-  __shared__ __attribute__((aligned(16))) float s_b[KT * NP];   // B of the own block R
-  __shared__ __attribute__((aligned(16))) float s_x[KT * PP];   // x of R
-  __shared__ __attribute__((aligned(16))) float s_c[KT * NP];   // C of block I; later Gnext (P x N)
-  __shared__ __attribute__((aligned(16))) float s_dy[KT * PP];  // dy of block I
+  constexpr int PP = Pitch<T, P>::v, NP = Pitch<T, N>::v, NPF = N + 4, TPm = P / 16, TNm = N / 16;
+  constexpr int C_BYTES = KT * NP * (int)sizeof(T), DY_BYTES = KT * PP * (int)sizeof(T), G_BYTES = P * NPF * 4;
+  constexpr int U_BYTES = C_BYTES + DY_BYTES > G_BYTES ? C_BYTES + DY_BYTES : G_BYTES;
+  __shared__ __attribute__((aligned(16))) T s_b[KT * NP];       // B of the own block R
+  __shared__ __attribute__((aligned(16))) T s_x[KT * PP];       // x of R
+  __shared__ __attribute__((aligned(16))) char s_un[U_BYTES];   // C and dy of block I; later Gnext
   __shared__ float s_SR[KT], s_dR[KT], s_SI[KT];
   __shared__ float s_red[4][P];
+  T* s_c = reinterpret_cast<T*>(s_un);
+  T* s_dy = reinterpret_cast<T*>(s_un + C_BYTES);
+  float* s_g = reinterpret_cast<float*>(s_un);
 
   const int nrb = Q / KT;
   uint32_t id = xcd_swizzle(blockIdx.x, nblocks);
@@ -177,13 +204,25 @@ __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, 
   const int lenR = min(KT, len - R * KT);
   const size_t xs = (size_t)H * P, bs = (size_t)G * N;
   const size_t cq = (((size_t)b * H + h) * nc + c) * Q;
-  const float Slast = dAcs[cq + Q - 1];
+  const int tk = min(tid, KT - 1);
+  const T* Cg = Cm + ((size_t)b * L + t0) * bs + (size_t)g * N;
+  const T* dyg = dy + ((size_t)b * L + t0) * xs + (size_t)h * P;
 
-  stage_rows<T, N>(s_b, Bm + ((size_t)b * L + t0 + R * KT) * bs + (size_t)g * N, bs, lenR, tid);
-  stage_rows<T, P>(s_x, x + ((size_t)b * L + t0 + R * KT) * xs + (size_t)h * P, xs, lenR, tid);
+  // prologue: the own block's B and x, block I = R's C and dy, and the cumsums, all in flight
+  RowTile<T, N> tb, tc;
+  RowTile<T, P> tx, tdy;
+  tb.load(Bm + ((size_t)b * L + t0 + R * KT) * bs + (size_t)g * N, bs, lenR, tid);
+  tx.load(x + ((size_t)b * L + t0 + R * KT) * xs + (size_t)h * P, xs, lenR, tid);
+  tc.load(Cg + (size_t)(R * KT) * bs, bs, lenR, tid);
+  tdy.load(dyg + (size_t)(R * KT) * xs, xs, lenR, tid);
+  const float sR = dAcs[cq + R * KT + tk], dR = dtp[cq + R * KT + tk];
+  float sI = sR;
+  const float Slast = dAcs[cq + Q - 1];
+  tb.store(s_b, tid);
+  tx.store(s_x, tid);
   if (tid < KT) {
-    s_SR[tid] = dAcs[cq + R * KT + tid];
-    s_dR[tid] = dtp[cq + R * KT + tid];
+    s_SR[tid] = sR;
+    s_dR[tid] = dR;
   }
 
   f32x4 xi[TPm], db[TNm];
@@ -198,9 +237,15 @@ __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, 
   for (int I = R; I < nI; ++I) {
     const int lenI = min(KT, len - I * KT);
     __syncthreads();
-    stage_rows<T, N>(s_c, Cm + ((size_t)b * L + t0 + I * KT) * bs + (size_t)g * N, bs, lenI, tid);
-    stage_rows<T, P>(s_dy, dy + ((size_t)b * L + t0 + I * KT) * xs + (size_t)h * P, xs, lenI, tid);
-    if (tid < KT) s_SI[tid] = dAcs[cq + I * KT + tid];
+    tc.store(s_c, tid);
+    tdy.store(s_dy, tid);
+    if (tid < KT) s_SI[tid] = sI;
+    if (I + 1 < nI) {
+      const int lenN = min(KT, len - (I + 1) * KT);
+      tc.load(Cg + (size_t)((I + 1) * KT) * bs, bs, lenN, tid);
+      tdy.load(dyg + (size_t)((I + 1) * KT) * xs, xs, lenN, tid);
+      sI = dAcs[cq + (I + 1) * KT + tk];
+    }
     __syncthreads();
     const float sj = s_SR[jl];
 #pragma unroll
@@ -213,7 +258,7 @@ __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, 
       for (int e = 0; e < 4; ++e) {
         const int il = 16 * ti + 4 * qd + e;
         const bool ok = (I * KT + il >= R * KT + jl) && il < lenI && jl < lenR;
-        const float ev = ok ? expf(s_SI[il] - sj) : 0.f;
+        const float ev = ok ? __builtin_amdgcn_exp2f((s_SI[il] - sj) * kLog2e) : 0.f;
         m1[e] = ev * cb[e];
         m2[e] = ev * dxv[e];
         cs += m1[e] * dxv[e];
@@ -227,31 +272,31 @@ __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, 
 
   // carried terms through the gradient of the state leaving the chunk
   __syncthreads();
-  stage_state<P, N>(s_c, gstates + (((size_t)b * nc + c) * H + h) * (size_t)(P * N), tid);
+  stage_state<P, N>(s_g, gstates + (((size_t)b * nc + c) * H + h) * (size_t)(P * N), tid);
   __syncthreads();
   // lane rows j = 16 w + 4 qd + e from here on
   float f[4], dj[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int j = 16 * w + 4 * qd + e;
-    f[e] = expf(Slast - s_SR[j]);
+    f[e] = __builtin_amdgcn_exp2f((Slast - s_SR[j]) * kLog2e);
     dj[e] = s_dR[j];
   }
   float u[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int m = 0; m < TPm; ++m) {
     // tmp[j][p] = sum_n B[j][n] Gnext[p][n]
-    const f32x4 tmp = mm_rows<N, NP, NP>(zero4(), s_b + 16 * w * NP, s_c + 16 * m * NP, r, qd);
+    const f32x4 tmp = mm_rows<N, NP, NPF>(zero4(), s_b + 16 * w * NP, s_g + 16 * m * NPF, r, qd);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      u[e] += s_x[(16 * w + 4 * qd + e) * PP + 16 * m + r] * tmp[e];
+      u[e] += ld1(s_x + (16 * w + 4 * qd + e) * PP + 16 * m + r) * tmp[e];
       xi[m][e] += f[e] * tmp[e];
     }
   }
 #pragma unroll
   for (int m = 0; m < TNm; ++m) {
     // xg[j][n] = sum_p x[j][p] Gnext[p][n]
-    const f32x4 xg = mm_cols<P, PP, NP>(zero4(), s_x + 16 * w * PP, s_c, 16 * m, r, qd);
+    const f32x4 xg = mm_cols<P, PP, NPF>(zero4(), s_x + 16 * w * PP, s_g, 16 * m, r, qd);
 #pragma unroll
     for (int e = 0; e < 4; ++e) db[m][e] += f[e] * xg[e];
   }
@@ -261,7 +306,7 @@ __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, 
     const int j = 16 * w + 4 * qd + e;
     float q = 0.f;
 #pragma unroll
-    for (int m = 0; m < TPm; ++m) q += s_x[j * PP + 16 * m + r] * xi[m][e];
+    for (int m = 0; m < TPm; ++m) q += ld1(s_x + j * PP + 16 * m + r) * xi[m][e];
     U[e] = f[e] * dj[e] * sum_r(u[e]);
     dd[e] = sum_r(q);
   }
@@ -283,7 +328,7 @@ __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, 
       const float dyv = ok ? to_f32(dy[tok * xs + (size_t)h * P + p]) : 0.f;
       const float dw = Dw ? Dw[(size_t)h * P + p] : 0.f;
       if (ok) dx[tok * xs + (size_t)h * P + p] = from_f32<T>(dw * dyv + dj[e] * xi[m][e]);
-      dDp[m] += dyv * s_x[j * PP + p];
+      dDp[m] += dyv * ld1(s_x + j * PP + p);
     }
     if (ok) {
 #pragma unroll
@@ -296,7 +341,7 @@ __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, 
   }
   // the column sums belong to column j = 16 w + r; its U was computed by the lane holding row j
   __syncthreads();
-  float* s_u = s_c;                                  // Gnext no longer needed
+  float* s_u = s_g;                                  // Gnext no longer needed
   if (r == 0) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) s_u[16 * w + 4 * qd + e] = U[e];
@@ -319,7 +364,8 @@ __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, 
 // ------------------------------------------------------------------ causal: dC
 // Wavefront w owns the 16 rows i = 16 w .. 16 w + 15 of the row block R.  It computes the
 // transposed tiles (j, i) of B C^T and x dy^T for every j of block J, so that the weighted
-// tile feeds dC[i][:] directly as an MFMA A operand.
+// tile feeds dC[i][:] directly as an MFMA A operand.  The tiles of block J + 1 are loaded
+// into registers while block J is computed.
 template <typename T, int P, int N>
 __global__ __launch_bounds__(256) void bwd_dc_kernel(const T* __restrict__ x, const T* __restrict__ Bm,
                                                      const T* __restrict__ Cm, const T* __restrict__ dy,
@@ -327,12 +373,16 @@ __global__ __launch_bounds__(256) void bwd_dc_kernel(const T* __restrict__ x, co
                                                      const float* __restrict__ states, float* __restrict__ dCh,
                                                      float* __restrict__ dSc, int L, int H, int G, int nc, int Q,
                                                      uint32_t nblocks) {
-  constexpr int PP = P + 4, NP = N + 4, TNm = N / 16;
-  __shared__ __attribute__((aligned(16))) float s_c[KT * NP];   // C of the own block R
-  __shared__ __attribute__((aligned(16))) float s_dy[KT * PP];  // dy of R
-  __shared__ __attribute__((aligned(16))) float s_b[KT * NP];   // B of block J; later Hprev (P x N)
-  __shared__ __attribute__((aligned(16))) float s_x[KT * PP];   // x of J
-  __shared__ float s_SR[KT], s_SJ[KT], s_dJ[KT];
+  constexpr int PP = Pitch<T, P>::v, NP = Pitch<T, N>::v, NPF = N + 4, TNm = N / 16;
+  constexpr int B_BYTES = KT * NP * (int)sizeof(T), X_BYTES = KT * PP * (int)sizeof(T), H_BYTES = P * NPF * 4;
+  constexpr int U_BYTES = B_BYTES + X_BYTES > H_BYTES ? B_BYTES + X_BYTES : H_BYTES;
+  __shared__ __attribute__((aligned(16))) T s_c[KT * NP];       // C of the own block R
+  __shared__ __attribute__((aligned(16))) T s_dy[KT * PP];      // dy of R
+  __shared__ __attribute__((aligned(16))) char s_un[U_BYTES];   // B and x of block J; later Hprev
+  __shared__ float s_SR[KT], s_SJ[KT], s_dJ[KT], s_rr[KT];
+  T* s_b = reinterpret_cast<T*>(s_un);
+  T* s_x = reinterpret_cast<T*>(s_un + B_BYTES);
+  float* s_h = reinterpret_cast<float*>(s_un);
 
   const int nrb = Q / KT;
   uint32_t id = xcd_swizzle(blockIdx.x, nblocks);
@@ -349,10 +399,23 @@ __global__ __launch_bounds__(256) void bwd_dc_kernel(const T* __restrict__ x, co
   const int r = lane & 15, qd = lane >> 4;
   const size_t xs = (size_t)H * P, bs = (size_t)G * N;
   const size_t cq = (((size_t)b * H + h) * nc + c) * Q;
+  const int tk = min(tid, KT - 1);
+  const T* Bg = Bm + ((size_t)b * L + t0) * bs + (size_t)g * N;
+  const T* xg = x + ((size_t)b * L + t0) * xs + (size_t)h * P;
 
-  stage_rows<T, N>(s_c, Cm + ((size_t)b * L + t0 + R * KT) * bs + (size_t)g * N, bs, lenR, tid);
-  stage_rows<T, P>(s_dy, dy + ((size_t)b * L + t0 + R * KT) * xs + (size_t)h * P, xs, lenR, tid);
-  if (tid < KT) s_SR[tid] = dAcs[cq + R * KT + tid];
+  // prologue: the own block's C and dy, block J = 0's B and x, and the cumsums, all in flight
+  RowTile<T, N> tc, tb;
+  RowTile<T, P> tdy, tx;
+  tc.load(Cm + ((size_t)b * L + t0 + R * KT) * bs + (size_t)g * N, bs, lenR, tid);
+  tdy.load(dy + ((size_t)b * L + t0 + R * KT) * xs + (size_t)h * P, xs, lenR, tid);
+  const int len0 = min(KT, len);
+  tb.load(Bg, bs, len0, tid);
+  tx.load(xg, xs, len0, tid);
+  const float sR = dAcs[cq + R * KT + tk];
+  float sJ = dAcs[cq + tk], dJ = dtp[cq + tk];
+  tc.store(s_c, tid);
+  tdy.store(s_dy, tid);
+  if (tid < KT) s_SR[tid] = sR;
 
   f32x4 dc[TNm];
 #pragma unroll
@@ -362,11 +425,18 @@ __global__ __launch_bounds__(256) void bwd_dc_kernel(const T* __restrict__ x, co
   for (int J = 0; J <= R; ++J) {
     const int lenJ = min(KT, len - J * KT);
     __syncthreads();
-    stage_rows<T, N>(s_b, Bm + ((size_t)b * L + t0 + J * KT) * bs + (size_t)g * N, bs, lenJ, tid);
-    stage_rows<T, P>(s_x, x + ((size_t)b * L + t0 + J * KT) * xs + (size_t)h * P, xs, lenJ, tid);
+    tb.store(s_b, tid);
+    tx.store(s_x, tid);
     if (tid < KT) {
-      s_SJ[tid] = dAcs[cq + J * KT + tid];
-      s_dJ[tid] = dtp[cq + J * KT + tid];
+      s_SJ[tid] = sJ;
+      s_dJ[tid] = dJ;
+    }
+    if (J < R) {
+      const int lenN = min(KT, len - (J + 1) * KT);
+      tb.load(Bg + (size_t)((J + 1) * KT) * bs, bs, lenN, tid);
+      tx.load(xg + (size_t)((J + 1) * KT) * xs, xs, lenN, tid);
+      sJ = dAcs[cq + (J + 1) * KT + tk];
+      dJ = dtp[cq + (J + 1) * KT + tk];
     }
     __syncthreads();
     const float si = s_SR[il];
@@ -380,7 +450,7 @@ __global__ __launch_bounds__(256) void bwd_dc_kernel(const T* __restrict__ x, co
       for (int e = 0; e < 4; ++e) {
         const int jl = 16 * tj + 4 * qd + e;
         const bool ok = (R * KT + il >= J * KT + jl) && il < lenR && jl < lenJ;
-        wt[e] = ok ? expf(si - s_SJ[jl]) * s_dJ[jl] * dxt[e] : 0.f;
+        wt[e] = ok ? __builtin_amdgcn_exp2f((si - s_SJ[jl]) * kLog2e) * s_dJ[jl] * dxt[e] : 0.f;
         rs += wt[e] * cbt[e];
       }
 #pragma unroll
@@ -388,27 +458,25 @@ __global__ __launch_bounds__(256) void bwd_dc_kernel(const T* __restrict__ x, co
     }
   }
   __syncthreads();
-  stage_state<P, N>(s_b, states + (((size_t)b * nc + c) * H + h) * (size_t)(P * N), tid);
+  stage_state<P, N>(s_h, states + (((size_t)b * nc + c) * H + h) * (size_t)(P * N), tid);
   __syncthreads();
   // lane rows i = 16 w + 4 qd + e from here on
   const size_t row0 = (size_t)b * L + t0 + R * KT;
   float rr[4] = {0.f, 0.f, 0.f, 0.f}, ei[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) ei[e] = expf(s_SR[16 * w + 4 * qd + e]);
+  for (int e = 0; e < 4; ++e) ei[e] = __builtin_amdgcn_exp2f(s_SR[16 * w + 4 * qd + e] * kLog2e);
 #pragma unroll
   for (int m = 0; m < TNm; ++m) {
     // cr[i][n] = sum_p dy[i][p] Hprev[p][n]
-    const f32x4 cr = mm_cols<P, PP, NP>(zero4(), s_dy + 16 * w * PP, s_b, 16 * m, r, qd);
+    const f32x4 cr = mm_cols<P, PP, NPF>(zero4(), s_dy + 16 * w * PP, s_h, 16 * m, r, qd);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 16 * w + 4 * qd + e;
-      rr[e] += cr[e] * s_c[i * NP + 16 * m + r];
+      rr[e] += cr[e] * ld1(s_c + i * NP + 16 * m + r);
       dc[m][e] += ei[e] * cr[e];
     }
   }
   const float rsum = sum_qd(rs);                   // row il
-  float* s_rr = s_x;                               // x of J no longer needed
-  __syncthreads();
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int i = 16 * w + 4 * qd + e;
