@@ -104,16 +104,27 @@ __device__ __forceinline__ void stage_state(float* dst, const float* src, int ti
 //   out[i][j] += sum_k A[i][k] * Bt[j][k]     (A, Bt: 16 rows each, pitch PA / PB)
 // Lane (r, qd) feeds A row r and Bt row r with k = (K/4) qd + 4 m + c, one LDS read each per
 // four MFMAs; it receives out[4 qd + e][r].
+// Both operands bf16 (input tiles, K a multiple of 32): 16x16x32 bf16 MFMAs with
+// k = 32 m + 8 qd + e, the same products (exact in fp32) summed in fp32 in another order.
 template <int K, int PA, int PB, typename SA, typename SB>
 __device__ __forceinline__ f32x4 mm_rows(f32x4 acc, const SA* A, const SB* Bt, int r, int qd) {
+  if constexpr (sizeof(SA) == 2 && sizeof(SB) == 2 && K % 32 == 0) {
 #pragma unroll
-  for (int m = 0; m < K / 16; ++m) {
-    const float4 a = ld4(A + r * PA + (K / 4) * qd + 4 * m);
-    const float4 b = ld4(Bt + r * PB + (K / 4) * qd + 4 * m);
-    acc = mfma_16x16x4_f32(a.x, b.x, acc);
-    acc = mfma_16x16x4_f32(a.y, b.y, acc);
-    acc = mfma_16x16x4_f32(a.z, b.z, acc);
-    acc = mfma_16x16x4_f32(a.w, b.w, acc);
+    for (int m = 0; m < K / 32; ++m) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(A + r * PA + 32 * m + 8 * qd);
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(Bt + r * PB + 32 * m + 8 * qd);
+      acc = mfma_16x16x32_bf16(a, b, acc);
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < K / 16; ++m) {
+      const float4 a = ld4(A + r * PA + (K / 4) * qd + 4 * m);
+      const float4 b = ld4(Bt + r * PB + (K / 4) * qd + 4 * m);
+      acc = mfma_16x16x4_f32(a.x, b.x, acc);
+      acc = mfma_16x16x4_f32(a.y, b.y, acc);
+      acc = mfma_16x16x4_f32(a.z, b.z, acc);
+      acc = mfma_16x16x4_f32(a.w, b.w, acc);
+    }
   }
   return acc;
 }
