@@ -179,9 +179,12 @@ def backward_cost(w):
         "gate_bwd": dict(bytes=0, flops=0),
         "chunk_state_grad": dict(bytes=x + bc + cum + st, flops=2 * B * H * L * P * N),
         "state_passing_rev": dict(bytes=2 * st + 2 * fin + B * H * nc * 4, flops=2 * B * nc * H * P * N),
+        # C B^T and dy x^T contract the input tiles (MFMA in the input dtype); the weighted
+        # products and the carried terms run on fp32 MFMA
         "bwd_dxdb": dict(bytes=2 * x + 2 * bc + 2 * cum + st + x + perh + 3 * B * H * L * 4,
                          flops=2 * N * tri * B * G + 2 * P * tri * B * H * 2 + 2 * N * tri * B * H
-                         + 4 * B * H * L * P * N),
+                         + 4 * B * H * L * P * N,
+                         flops_in=2 * N * tri * B * G + 2 * P * tri * B * H),
         "bwd_dc": dict(bytes=2 * x + 2 * bc + 2 * cum + st + perh + B * H * L * 4,
                        flops=2 * N * tri * B * H + 2 * B * H * L * P * N),
         "bwd_finalize": dict(bytes=2 * st + 5 * cum + B * L * H * e * 2, flops=2 * B * nc * H * P * N),
@@ -189,8 +192,15 @@ def backward_cost(w):
     }
     for k, v in cost.items():
         # chunk_state contracts on MFMA in the input dtype; the backward kernels' products run
-        # on fp32 MFMA whatever the input dtype
-        v["peak"] = MFMA_PEAK_TFLOPS[w.dtype] if k.startswith("chunk_state") else MFMA_PEAK_TFLOPS["f32"]
+        # on fp32 MFMA except the flops_in share (input-dtype MFMA): the peak is the blend that
+        # the split implies, flops / (flops_in / peak_in + rest / peak_f32)
+        p_in, p_32 = MFMA_PEAK_TFLOPS[w.dtype], MFMA_PEAK_TFLOPS["f32"]
+        if k.startswith("chunk_state"):
+            v["peak"] = p_in
+        else:
+            f_in = v.pop("flops_in", 0)
+            t = f_in / p_in + (v["flops"] - f_in) / p_32
+            v["peak"] = round(v["flops"] / t, 1) if t > 0 else p_32
         t_f = v["flops"] / (v["peak"] * 1e12)
         t_b = v["bytes"] / (HBM_PEAK_GBS * 1e9)
         v["bound"] = "mfma" if t_f > t_b else "hbm"
