@@ -589,25 +589,57 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(const T* __restrict__
 }
 
 // ------------------------------------------------------------------ reductions
+// dB, dC of each group: the per-head partials summed over the heads of the group in head
+// order.  Each thread owns four consecutive n (16-byte loads and stores) and keeps the loads
+// of four heads in flight; the order of the additions is the sequential one.
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restrict__ dBh,
                                                             const float* __restrict__ dCh, T* __restrict__ dB,
-                                                            T* __restrict__ dC, int H, int G, int N, size_t total) {
-  const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;   // index into (B, L, G, N)
-  if (e >= total) return;
-  const int n = (int)(e % N);
-  const size_t bg = e / N;
+                                                            T* __restrict__ dC, int H, int G, int N, size_t total4) {
+  const size_t e4 = (size_t)blockIdx.x * 256 + threadIdx.x;   // index into (B, L, G, N / 4)
+  if (e4 >= total4) return;
+  const int N4 = N / 4;
+  const int n = (int)(e4 % N4) * 4;
+  const size_t bg = e4 / N4;
   const int g = (int)(bg % G);
   const size_t bl = bg / G;
   const int hpg = H / G;
-  float sb = 0.f, sc = 0.f;
-  for (int k = 0; k < hpg; ++k) {
-    const size_t o = (bl * H + (size_t)g * hpg + k) * N + n;
-    sb += dBh[o];
-    sc += dCh[o];
+  const float* pb = dBh + (bl * H + (size_t)g * hpg) * N + n;
+  const float* pc = dCh + (bl * H + (size_t)g * hpg) * N + n;
+  float4 sb = make_float4(0.f, 0.f, 0.f, 0.f), sc = sb;
+  auto add = [](float4& acc, const float4& v) {
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  };
+  int k = 0;
+  for (; k + 4 <= hpg; k += 4) {
+    float4 vb[4], vc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      vb[u] = *reinterpret_cast<const float4*>(pb + (size_t)(k + u) * N);
+      vc[u] = *reinterpret_cast<const float4*>(pc + (size_t)(k + u) * N);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      add(sb, vb[u]);
+      add(sc, vc[u]);
+    }
   }
-  dB[e] = from_f32<T>(sb);
-  dC[e] = from_f32<T>(sc);
+  for (; k < hpg; ++k) {
+    add(sb, *reinterpret_cast<const float4*>(pb + (size_t)k * N));
+    add(sc, *reinterpret_cast<const float4*>(pc + (size_t)k * N));
+  }
+  const size_t e = e4 * 4;
+  dB[e + 0] = from_f32<T>(sb.x);
+  dB[e + 1] = from_f32<T>(sb.y);
+  dB[e + 2] = from_f32<T>(sb.z);
+  dB[e + 3] = from_f32<T>(sb.w);
+  dC[e + 0] = from_f32<T>(sc.x);
+  dC[e + 1] = from_f32<T>(sc.y);
+  dC[e + 2] = from_f32<T>(sc.z);
+  dC[e + 3] = from_f32<T>(sc.w);
 }
 
 __global__ __launch_bounds__(256) void bwd_reduce_params_kernel(const float* __restrict__ pA,
@@ -695,9 +727,10 @@ static hipError_t launch_reduce_impl(const BwdArgs& a, hipStream_t s) {
   // the start event goes with the first launch and the stop event with the second
   hipEvent_t start = f.ev0;
   if (total > 0) {
-    hipExtLaunchKernelGGL(bwd_reduce_bc_kernel<T>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, start,
+    const size_t total4 = total / 4;                // N is a multiple of 16
+    hipExtLaunchKernelGGL(bwd_reduce_bc_kernel<T>, dim3((unsigned)((total4 + 255) / 256)), dim3(256), 0, s, start,
                           nullptr, 0, a.dBh, a.dCh, static_cast<T*>(a.dB), static_cast<T*>(a.dC), f.H, f.G, f.N,
-                          total);
+                          total4);
     start = nullptr;
   }
   hipExtLaunchKernelGGL(bwd_reduce_params_kernel, dim3(f.H), dim3(256), 0, s, start, f.ev1, 0, a.pA, a.pbias, a.pD,
