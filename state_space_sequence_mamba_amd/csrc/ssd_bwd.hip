@@ -668,10 +668,28 @@ __global__ __launch_bounds__(256) void bwd_reduce_params_kernel(const float* __r
     dA[h] = s_a[0];
     dbias[h] = s_b[0];
   }
-  if (dD && tid < P) {
+  if (dD) {
+    // thread (slice sl, channel p) sums the partial rows k = sl (mod S), four loads in flight;
+    // the S slice sums are then added in slice order
+    const int S = 256 / P, p = tid % P, sl = tid / P;
     float sD = 0.f;
-    for (int k = 0; k < nbr; ++k) sD += pD[((size_t)k * H + h) * P + tid];
-    dD[(size_t)h * P + tid] = sD;
+    int k = sl;
+    for (; k + 3 * S < nbr; k += 4 * S) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = pD[((size_t)(k + u * S) * H + h) * P + p];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) sD += v[u];
+    }
+    for (; k < nbr; k += S) sD += pD[((size_t)k * H + h) * P + p];
+    __syncthreads();
+    s_a[tid] = sD;
+    __syncthreads();
+    if (tid < P) {
+      float t = 0.f;
+      for (int j = 0; j < S; ++j) t += s_a[j * P + tid];
+      dD[(size_t)h * P + tid] = t;
+    }
   }
 }
 
