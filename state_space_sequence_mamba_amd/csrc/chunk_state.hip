@@ -80,7 +80,7 @@ __device__ __forceinline__ void chunk_cumsum_wave(const T* __restrict__ dt, floa
 // the scan reads (cb_block), filling the tail of the grid.  Backward (from_start): dt' and the
 // cumsum are read from the workspace.
 template <typename T, int P, int N, int NTHR>
-__global__ __launch_bounds__(NTHR) void chunk_state_kernel(const T* __restrict__ x,
+__global__ __launch_bounds__(NTHR, sizeof(T) == 2 ? 6 : 1) void chunk_state_kernel(const T* __restrict__ x,
                                                           const T* __restrict__ Bm,
                                                           const T* __restrict__ Cm,
                                                           const T* __restrict__ dt,
