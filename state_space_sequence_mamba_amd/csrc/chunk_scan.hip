@@ -34,6 +34,8 @@
 // MFMA: fp32 inputs -> v_mfma_f32_16x16x4_f32 for all three products; bf16 inputs ->
 // 16x16x32 bf16 for C B^T and C Hprev^T, 16x16x16 bf16 for (L o CB) X.  Decay factors use
 // the hardware base-2 exponential on log2(e)-scaled cumsums; factors below 2^-126 become 0.
+// Below the diagonal the decay is split at each column tile's last position into a row
+// factor and a per-column weight (both <= 1), so a lane takes one exponential per sub-tile.
 #include "cb_tiles.h"
 #include "ssd_common.h"
 #include "ssd_launch.h"
@@ -44,6 +46,11 @@ constexpr int kKT = 64;                       // tokens per staged tile == rows 
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int P> struct TPof { static constexpr int v = P / 16; };
+
+// Split decay below the diagonal (one exponential per lane and sub-tile) for bf16, where the
+// exponentials weigh against short MFMAs; fp32 keeps one per element (the split's extra
+// registers would spill there, and its sub-tiles are MFMA-bound).
+template <typename T> constexpr bool kSplitDecay = sizeof(T) == 2;
 
 template <typename T, int P, int N, int HB, int ROWS>
 struct ScanLds {
@@ -183,8 +190,9 @@ __device__ __forceinline__ void carried_term(f32x4 (&acc)[TPof<P>::v], const typ
 template <typename T, int P, int N, int HB, int BP, int XP, bool EDGE, bool PRECB>
 __device__ __forceinline__ void sub_tile(f32x4 (&acc)[HB][TPof<P>::v], const typename NDot<T, N>::frag& cf,
                                          const float (&dco)[HB][TPof<P>::v], const T* s_b, const T* s_x,
-                                         const float (*s_da)[256], const float (*s_dt)[256], int strip, int jt,
-                                         int js, int lstrip, int r, int qd) {
+                                         const float (*s_da)[256], const float (*s_dt)[256],
+                                         const float (*s_w)[256], int strip, int jt, int js, int lstrip, int r,
+                                         int qd) {
   typedef NDot<T, N> ND;
   constexpr int TP = P / 16;
   constexpr bool F32 = sizeof(T) == 4;
@@ -203,17 +211,33 @@ __device__ __forceinline__ void sub_tile(f32x4 (&acc)[HB][TPof<P>::v], const typ
   const int j0 = 16 * jt + 4 * qd;
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) {
-    const float da_i = s_da[hh][i_row];
-    const float4 daj = *reinterpret_cast<const float4*>(&s_da[hh][j0]);
-    const float4 dtj = *reinterpret_cast<const float4*>(&s_dt[hh][j0]);
     float lw[4];
-    lw[0] = cbt[0] * __builtin_amdgcn_exp2f(da_i - daj.x) * dtj.x;
-    lw[1] = cbt[1] * __builtin_amdgcn_exp2f(da_i - daj.y) * dtj.y;
-    lw[2] = cbt[2] * __builtin_amdgcn_exp2f(da_i - daj.z) * dtj.z;
-    lw[3] = cbt[3] * __builtin_amdgcn_exp2f(da_i - daj.w) * dtj.w;
-    if (EDGE) {  // causal mask (select, so an overflowed factor above the diagonal is dropped)
+    if (diag || !kSplitDecay<T>) {
+      // the diagonal sub-tile (and every sub-tile for fp32): the decay of each (i, j) on its
+      // own, then the causal mask on the diagonal (a select, so an overflowed factor above the
+      // diagonal is dropped)
+      const float da_i = s_da[hh][i_row];
+      const float4 daj = *reinterpret_cast<const float4*>(&s_da[hh][j0]);
+      const float4 dtj = *reinterpret_cast<const float4*>(&s_dt[hh][j0]);
+      lw[0] = cbt[0] * __builtin_amdgcn_exp2f(da_i - daj.x) * dtj.x;
+      lw[1] = cbt[1] * __builtin_amdgcn_exp2f(da_i - daj.y) * dtj.y;
+      lw[2] = cbt[2] * __builtin_amdgcn_exp2f(da_i - daj.z) * dtj.z;
+      lw[3] = cbt[3] * __builtin_amdgcn_exp2f(da_i - daj.w) * dtj.w;
+      if (EDGE) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) lw[e] = (j0 + e <= i_row) ? lw[e] : 0.f;
+        for (int e = 0; e < 4; ++e) lw[e] = (j0 + e <= i_row) ? lw[e] : 0.f;
+      }
+    } else {
+      // below the diagonal every j precedes every i: the decay splits at c, the tile's last
+      // column, into a row factor exp2(dAcs_i - dAcs_c) and the column weight
+      // W_j = exp2(dAcs_c - dAcs_j) dt'_j (both factors <= 1: no overflow), one exponential per
+      // lane instead of four
+      const float ri = __builtin_amdgcn_exp2f(s_da[hh][i_row] - s_da[hh][16 * jt + 15]);
+      const float4 wj = *reinterpret_cast<const float4*>(&s_w[hh][j0]);
+      lw[0] = cbt[0] * wj.x * ri;
+      lw[1] = cbt[1] * wj.y * ri;
+      lw[2] = cbt[2] * wj.z * ri;
+      lw[3] = cbt[3] * wj.w * ri;
     }
     const T* xt = &s_x[(hh * P + r) * XP + js * 16 + 4 * qd];
     if (F32) {
@@ -255,13 +279,14 @@ __device__ __forceinline__ void sub_tile(f32x4 (&acc)[HB][TPof<P>::v], const typ
 template <typename T, int P, int N, int HB, int BP, int XP, bool PRECB = false>
 __device__ __forceinline__ void diag_tile(f32x4 (&acc)[HB][TPof<P>::v], const typename NDot<T, N>::frag& cf,
                                           const float (&dco)[HB][TPof<P>::v], const T* s_b, const T* s_x,
-                                          const float (*s_da)[256], const float (*s_dt)[256], int strip, int J,
-                                          int lstrip, int r, int qd) {
+                                          const float (*s_da)[256], const float (*s_dt)[256],
+                                          const float (*s_w)[256], int strip, int J, int lstrip, int r, int qd) {
 #pragma unroll
   for (int js = 0; js < 4; ++js) {
     const int jt = 4 * J + js;
     if (jt > strip) break;
-    sub_tile<T, P, N, HB, BP, XP, true, PRECB>(acc, cf, dco, s_b, s_x, s_da, s_dt, strip, jt, js, lstrip, r, qd);
+    sub_tile<T, P, N, HB, BP, XP, true, PRECB>(acc, cf, dco, s_b, s_x, s_da, s_dt, s_w, strip, jt, js, lstrip, r,
+                                               qd);
   }
 }
 
@@ -271,12 +296,12 @@ __device__ __forceinline__ void diag_tile(f32x4 (&acc)[HB][TPof<P>::v], const ty
 template <typename T, int P, int N, int HB, int BP, int XP, bool PRECB = false>
 __device__ __forceinline__ void full_tile(f32x4 (&acc)[HB][TPof<P>::v], const typename NDot<T, N>::frag& cf,
                                           const float (&dco)[HB][TPof<P>::v], const T* s_b, const T* s_x,
-                                          const float (*s_da)[256], const float (*s_dt)[256], int strip, int J,
-                                          int lstrip, int r, int qd) {
+                                          const float (*s_da)[256], const float (*s_dt)[256],
+                                          const float (*s_w)[256], int strip, int J, int lstrip, int r, int qd) {
 #pragma unroll
   for (int js = 0; js < 4; ++js)
-    sub_tile<T, P, N, HB, BP, XP, false, PRECB>(acc, cf, dco, s_b, s_x, s_da, s_dt, strip, 4 * J + js, js, lstrip,
-                                                r, qd);
+    sub_tile<T, P, N, HB, BP, XP, false, PRECB>(acc, cf, dco, s_b, s_x, s_da, s_dt, s_w, strip, 4 * J + js, js,
+                                                lstrip, r, qd);
 }
 
 // Output gate y * silu(z) on one strip's registers (rows 16 strip + 4 qd + e, column 16 pt + r).
@@ -332,6 +357,18 @@ __device__ __forceinline__ void flush_rows(T* y, const T* s_y, size_t row0, size
 // Every slot i < 256 of every head is written (positions past Q repeat position Q - 1 and are
 // never read), so neither the loads nor the stores sit behind a branch: a conditional store
 // lets the compiler sink its load into the branch and wait for it there.
+// Column weights of the below-diagonal sub-tiles, W_j = exp2(dAcs_c - dAcs_j) dt'_j with c the
+// last column of j's 16-column tile (c = j | 15), for every slot of every head of the block.
+template <typename T, int HB, int NTHR>
+__device__ __forceinline__ void column_weights(float (*s_w)[256], const float (*s_da)[256],
+                                               const float (*s_dt)[256], int tid) {
+  if constexpr (!kSplitDecay<T>) return;
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh)
+    for (int i = tid; i < 256; i += NTHR)
+      s_w[hh][i] = __builtin_amdgcn_exp2f(s_da[hh][i | 15] - s_da[hh][i]) * s_dt[hh][i];
+}
+
 template <int HB, int NTHR>
 struct ScalarRegs {
   static constexpr int K = (256 + NTHR - 1) / NTHR;
@@ -405,6 +442,7 @@ __global__ __launch_bounds__(256, HB == 1 ? 4 : 2) void chunk_scan_rows_kernel(c
   __shared__ __attribute__((aligned(16))) T s_mem[SL::TOTAL];
   __shared__ __attribute__((aligned(16))) float s_da[HB][256];     // dAcs * log2(e)
   __shared__ __attribute__((aligned(16))) float s_dt[HB][256];
+  __shared__ __attribute__((aligned(16))) float s_w[kSplitDecay<T> ? HB : 1][256];   // column weights (bf16)
   T* s_b = s_mem;
   T* s_xu = s_mem + SL::B_ELEMS;                                   // Hprev, then x^T tiles
   T* s_y = s_mem;                                                  // y staging, at the end
@@ -479,6 +517,7 @@ __global__ __launch_bounds__(256, HB == 1 ? 4 : 2) void chunk_scan_rows_kernel(c
   sr.store(s_da, s_dt, tid);
   pr.template store<SL::BP>(s_xu, tid);
   __syncthreads();
+  column_weights<T, HB, NTHR>(s_w, s_da, s_dt, tid);          // read after the J loop's first barrier
   if (strip_ok) carried_term<T, P, N, SL::BP>(acc[0], cf, s_xu, s_da[0], s, r, qd);
 #pragma unroll
   for (int hh = 1; hh < HB; ++hh) {
@@ -494,9 +533,9 @@ __global__ __launch_bounds__(256, HB == 1 ? 4 : 2) void chunk_scan_rows_kernel(c
     __syncthreads();
     if (strip_ok) {
       if (J < rb)
-        full_tile<T, P, N, HB, SL::BP, SL::XP, PRECB>(acc, cf, dco, s_b, s_xu, s_da, s_dt, s, J, wave, r, qd);
+        full_tile<T, P, N, HB, SL::BP, SL::XP, PRECB>(acc, cf, dco, s_b, s_xu, s_da, s_dt, s_w, s, J, wave, r, qd);
       else
-        diag_tile<T, P, N, HB, SL::BP, SL::XP, PRECB>(acc, cf, dco, s_b, s_xu, s_da, s_dt, s, J, wave, r, qd);
+        diag_tile<T, P, N, HB, SL::BP, SL::XP, PRECB>(acc, cf, dco, s_b, s_xu, s_da, s_dt, s_w, s, J, wave, r, qd);
     }
   }
   if (Z && strip_ok) apply_gate<T, P, HB>(acc, Z, (size_t)b * L + t0, x_tok, h0, s, len, r, qd);
@@ -530,6 +569,7 @@ __global__ __launch_bounds__(512) void chunk_scan_chunk_kernel(const T* __restri
   __shared__ __attribute__((aligned(16))) T s_mem[SL::TOTAL];
   __shared__ __attribute__((aligned(16))) float s_da[HB][256];
   __shared__ __attribute__((aligned(16))) float s_dt[HB][256];
+  __shared__ __attribute__((aligned(16))) float s_w[kSplitDecay<T> ? HB : 1][256];
   T* s_b = s_mem;
   T* s_xu = s_mem + SL::B_ELEMS;
   T* s_y = s_mem;
@@ -592,6 +632,7 @@ __global__ __launch_bounds__(512) void chunk_scan_chunk_kernel(const T* __restri
   sr.store(s_da, s_dt, tid);
   pr.template store<SL::BP>(s_xu, tid);
   __syncthreads();
+  column_weights<T, HB, NTHR>(s_w, s_da, s_dt, tid);          // read after the J loop's first barrier
 #pragma unroll
   for (int st = 0; st < 2; ++st)
     if (ok[st]) carried_term<T, P, N, SL::BP>(acc[st][0], cf[st], s_xu, s_da[0], strip[st], r, qd);
@@ -613,9 +654,11 @@ __global__ __launch_bounds__(512) void chunk_scan_chunk_kernel(const T* __restri
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       if (ok[st] && 4 * J + 3 < strip[st])
-        full_tile<T, P, N, HB, SL::BP, SL::XP>(acc[st], cf[st], dco, s_b, s_xu, s_da, s_dt, strip[st], J, 0, r, qd);
+        full_tile<T, P, N, HB, SL::BP, SL::XP>(acc[st], cf[st], dco, s_b, s_xu, s_da, s_dt, s_w, strip[st], J, 0, r,
+                                               qd);
       else if (ok[st] && 4 * J <= strip[st])
-        diag_tile<T, P, N, HB, SL::BP, SL::XP>(acc[st], cf[st], dco, s_b, s_xu, s_da, s_dt, strip[st], J, 0, r, qd);
+        diag_tile<T, P, N, HB, SL::BP, SL::XP>(acc[st], cf[st], dco, s_b, s_xu, s_da, s_dt, s_w, strip[st], J, 0, r,
+                                               qd);
     }
   }
   if (Z) {
