@@ -228,6 +228,19 @@ def test_special_values_A_zero_and_large_dt():
     _check_full(inp, 64, TOL["f32"])
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_strong_decay_stays_finite(dtype):
+    """A = -16 and dt' = 3 over 80 tokens: decays across one 16-token tile reach e^-768, far
+    past fp32 range; every factor the kernels form must stay finite (outputs match the oracle)."""
+    _say(f"strong decay {dtype}")
+    N = 64 if dtype == "f32" else 128
+    inp = I.make_fwd_inputs(2, 300, 4, 64, N, 1, dtype, seed=15)
+    inp["A"] = torch.full((4,), -16.0)
+    inp["dt"][:, 100:180] = 3.0
+    for Q in (64, 256):
+        _check_full(inp, Q, TOL[dtype])
+
+
 def test_no_D_term():
     _say("D = NULL")
     inp = I.make_fwd_inputs(1, 130, 4, 32, 32, 1, "f32", seed=13)
