@@ -179,14 +179,15 @@ def backward_cost(w):
         "gate_bwd": dict(bytes=0, flops=0),
         "chunk_state_grad": dict(bytes=x + bc + cum + st, flops=2 * B * H * L * P * N),
         "state_passing_rev": dict(bytes=2 * st + 2 * fin + B * H * nc * 4, flops=2 * B * nc * H * P * N),
-        # C B^T and dy x^T contract the input tiles (MFMA in the input dtype); the weighted
-        # products and the carried terms run on fp32 MFMA
+        # C B^T, dy x^T and the weighted products contract tiles of the input dtype (MFMA in
+        # that dtype); the carried terms through the fp32 state gradients run on fp32 MFMA
         "bwd_dxdb": dict(bytes=2 * x + 2 * bc + 2 * cum + st + x + perh + 3 * B * H * L * 4,
                          flops=2 * N * tri * B * G + 2 * P * tri * B * H * 2 + 2 * N * tri * B * H
                          + 4 * B * H * L * P * N,
-                         flops_in=2 * N * tri * B * G + 2 * P * tri * B * H),
+                         flops_in=2 * N * tri * B * G + 2 * P * tri * B * H * 2 + 2 * N * tri * B * H),
         "bwd_dc": dict(bytes=2 * x + 2 * bc + 2 * cum + st + perh + B * H * L * 4,
-                       flops=2 * N * tri * B * H + 2 * B * H * L * P * N),
+                       flops=2 * N * tri * B * H + 2 * B * H * L * P * N,
+                       flops_in=2 * N * tri * B * H),
         "bwd_finalize": dict(bytes=2 * st + 5 * cum + B * L * H * e * 2, flops=2 * B * nc * H * P * N),
         "bwd_reduce": dict(bytes=2 * perh + 2 * bc, flops=2 * B * L * H * N),
     }

@@ -132,10 +132,22 @@ __device__ __forceinline__ f32x4 mm_rows(f32x4 acc, const SA* A, const SB* Bt, i
 // out[i][c] += sum_k M[k][i] * V[k][c] over the 16 k of one tile, where lane (r, qd) holds
 // M[k = 4 qd + e][i = r] in m[e] (the result layout of mm_rows, used directly as the A
 // operand), and V rows k (pitch PV) are read from LDS at column c0 + r.
+// bf16 tiles: one 16x16x16 bf16 MFMA with M rounded to bf16 (the A operand layout is the same:
+// lane (r, qd) holds k = 4 qd + e), as the forward rounds its weighted C B^T for (L o CB) X.
 template <int PV, typename SV>
 __device__ __forceinline__ f32x4 mm_regs(f32x4 acc, const f32x4& m, const SV* V, int c0, int r, int qd) {
+  if constexpr (sizeof(SV) == 2) {
+    bf16x4 a, b;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) acc = mfma_16x16x4_f32(m[e], ld1(V + (4 * qd + e) * PV + c0 + r), acc);
+    for (int e = 0; e < 4; ++e) {
+      a[e] = static_cast<__bf16>(m[e]);
+      b[e] = V[(4 * qd + e) * PV + c0 + r];
+    }
+    acc = mfma_16x16x16_bf16(a, b, acc);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = mfma_16x16x4_f32(m[e], ld1(V + (4 * qd + e) * PV + c0 + r), acc);
+  }
   return acc;
 }
 
