@@ -86,17 +86,30 @@ struct RowTile {
   }
 };
 
-// Stage a (P x N) fp32 state as rows of pitch N + 4.
-template <int P, int N>
-__device__ __forceinline__ void stage_state(float* dst, const float* src, int tid) {
-  constexpr int UNITS = P * N / 4, NIT = (UNITS + 255) / 256;
+// Stage a (P x N) fp32 state as rows of pitch Pitch<S, N>, in S (fp32, or bf16 rounded to
+// nearest even for the bf16 path, as the forward's carried term reads the entering states).
+template <typename S, int P, int N>
+__device__ __forceinline__ void stage_state(S* dst, const float* src, int tid) {
+  constexpr int UNITS = P * N / 4, NIT = (UNITS + 255) / 256, PN = Pitch<S, N>::v;
   float4 v[NIT];
 #pragma unroll
   for (int k = 0; k < NIT; ++k) v[k] = reinterpret_cast<const float4*>(src)[min(tid + 256 * k, UNITS - 1)];
 #pragma unroll
   for (int k = 0; k < NIT; ++k) {
     const int u = tid + 256 * k;
-    if (u < UNITS) *reinterpret_cast<float4*>(dst + ((4 * u) / N) * (N + 4) + (4 * u) % N) = v[k];
+    if (u < UNITS) {
+      S* d = dst + ((4 * u) / N) * PN + (4 * u) % N;
+      if constexpr (sizeof(S) == 4) {
+        *reinterpret_cast<float4*>(d) = v[k];
+      } else {
+        bf16x4 q;
+        q[0] = static_cast<__bf16>(v[k].x);
+        q[1] = static_cast<__bf16>(v[k].y);
+        q[2] = static_cast<__bf16>(v[k].z);
+        q[3] = static_cast<__bf16>(v[k].w);
+        *reinterpret_cast<bf16x4*>(d) = q;
+      }
+    }
   }
 }
 
@@ -151,18 +164,27 @@ __device__ __forceinline__ f32x4 mm_regs(f32x4 acc, const f32x4& m, const SV* V,
   return acc;
 }
 
-// out[i][c] += sum_k A[i][k] * V[k][c] over K, A rows i (pitch PA) and fp32 V rows k (pitch PV)
-// in LDS; lane (r, qd) reads A row r as runs of four and V column c0 + r.
-template <int K, int PA, int PV, typename SA>
-__device__ __forceinline__ f32x4 mm_cols(f32x4 acc, const SA* A, const float* V, int c0, int r, int qd) {
+// out[i][c] += sum_k A[i][k] * V[k][c] over K, A rows i (pitch PA) and V rows k (pitch PV) in
+// LDS; lane (r, qd) reads A row r as runs of four and V column c0 + r.  Both bf16: one
+// 16x16x16 bf16 MFMA per run of four k.
+template <int K, int PA, int PV, typename SA, typename SV>
+__device__ __forceinline__ f32x4 mm_cols(f32x4 acc, const SA* A, const SV* V, int c0, int r, int qd) {
 #pragma unroll
   for (int m = 0; m < K / 16; ++m) {
     const int k0 = (K / 4) * qd + 4 * m;
-    const float4 a = ld4(A + r * PA + k0);
-    acc = mfma_16x16x4_f32(a.x, V[(k0 + 0) * PV + c0 + r], acc);
-    acc = mfma_16x16x4_f32(a.y, V[(k0 + 1) * PV + c0 + r], acc);
-    acc = mfma_16x16x4_f32(a.z, V[(k0 + 2) * PV + c0 + r], acc);
-    acc = mfma_16x16x4_f32(a.w, V[(k0 + 3) * PV + c0 + r], acc);
+    if constexpr (sizeof(SA) == 2 && sizeof(SV) == 2) {
+      const bf16x4 a = *reinterpret_cast<const bf16x4*>(A + r * PA + k0);
+      bf16x4 b;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) b[e] = V[(k0 + e) * PV + c0 + r];
+      acc = mfma_16x16x16_bf16(a, b, acc);
+    } else {
+      const float4 a = ld4(A + r * PA + k0);
+      acc = mfma_16x16x4_f32(a.x, ld1(V + (k0 + 0) * PV + c0 + r), acc);
+      acc = mfma_16x16x4_f32(a.y, ld1(V + (k0 + 1) * PV + c0 + r), acc);
+      acc = mfma_16x16x4_f32(a.z, ld1(V + (k0 + 2) * PV + c0 + r), acc);
+      acc = mfma_16x16x4_f32(a.w, ld1(V + (k0 + 3) * PV + c0 + r), acc);
+    }
   }
   return acc;
 }
@@ -197,7 +219,8 @@ __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, 
                                                        float* __restrict__ pD, int L, int H, int G, int nc, int Q,
                                                        uint32_t nblocks) {
   constexpr int PP = Pitch<T, P>::v, NP = Pitch<T, N>::v, NPF = N + 4, TPm = P / 16, TNm = N / 16;
-  constexpr int C_BYTES = KT * NP * (int)sizeof(T), DY_BYTES = KT * PP * (int)sizeof(T), G_BYTES = P * NPF * 4;
+  constexpr int C_BYTES = KT * NP * (int)sizeof(T), DY_BYTES = KT * PP * (int)sizeof(T);
+  constexpr int G_BYTES = P * NPF * 4;                             // Gnext staged in fp32
   constexpr int U_BYTES = C_BYTES + DY_BYTES > G_BYTES ? C_BYTES + DY_BYTES : G_BYTES;
   __shared__ __attribute__((aligned(16))) T s_b[KT * NP];       // B of the own block R
   __shared__ __attribute__((aligned(16))) T s_x[KT * PP];       // x of R
@@ -295,7 +318,7 @@ __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, 
 
   // carried terms through the gradient of the state leaving the chunk
   __syncthreads();
-  stage_state<P, N>(s_g, gstates + (((size_t)b * nc + c) * H + h) * (size_t)(P * N), tid);
+  stage_state<float, P, N>(s_g, gstates + (((size_t)b * nc + c) * H + h) * (size_t)(P * N), tid);
   __syncthreads();
   // lane rows j = 16 w + 4 qd + e from here on
   float f[4], dj[4];
@@ -396,8 +419,9 @@ __global__ __launch_bounds__(256) void bwd_dc_kernel(const T* __restrict__ x, co
                                                      const float* __restrict__ states, float* __restrict__ dCh,
                                                      float* __restrict__ dSc, int L, int H, int G, int nc, int Q,
                                                      uint32_t nblocks) {
-  constexpr int PP = Pitch<T, P>::v, NP = Pitch<T, N>::v, NPF = N + 4, TNm = N / 16;
-  constexpr int B_BYTES = KT * NP * (int)sizeof(T), X_BYTES = KT * PP * (int)sizeof(T), H_BYTES = P * NPF * 4;
+  constexpr int PP = Pitch<T, P>::v, NP = Pitch<T, N>::v, TNm = N / 16;
+  constexpr int B_BYTES = KT * NP * (int)sizeof(T), X_BYTES = KT * PP * (int)sizeof(T);
+  constexpr int H_BYTES = P * NP * (int)sizeof(T);                // Hprev staged in T
   constexpr int U_BYTES = B_BYTES + X_BYTES > H_BYTES ? B_BYTES + X_BYTES : H_BYTES;
   __shared__ __attribute__((aligned(16))) T s_c[KT * NP];       // C of the own block R
   __shared__ __attribute__((aligned(16))) T s_dy[KT * PP];      // dy of R
@@ -405,7 +429,7 @@ __global__ __launch_bounds__(256) void bwd_dc_kernel(const T* __restrict__ x, co
   __shared__ float s_SR[KT], s_SJ[KT], s_dJ[KT], s_rr[KT];
   T* s_b = reinterpret_cast<T*>(s_un);
   T* s_x = reinterpret_cast<T*>(s_un + B_BYTES);
-  float* s_h = reinterpret_cast<float*>(s_un);
+  T* s_h = reinterpret_cast<T*>(s_un);
 
   const int nrb = Q / KT;
   uint32_t id = xcd_swizzle(blockIdx.x, nblocks);
@@ -481,7 +505,7 @@ __global__ __launch_bounds__(256) void bwd_dc_kernel(const T* __restrict__ x, co
     }
   }
   __syncthreads();
-  stage_state<P, N>(s_h, states + (((size_t)b * nc + c) * H + h) * (size_t)(P * N), tid);
+  stage_state<T, P, N>(s_h, states + (((size_t)b * nc + c) * H + h) * (size_t)(P * N), tid);
   __syncthreads();
   // lane rows i = 16 w + 4 qd + e from here on
   const size_t row0 = (size_t)b * L + t0 + R * KT;
@@ -491,7 +515,7 @@ __global__ __launch_bounds__(256) void bwd_dc_kernel(const T* __restrict__ x, co
 #pragma unroll
   for (int m = 0; m < TNm; ++m) {
     // cr[i][n] = sum_p dy[i][p] Hprev[p][n]
-    const f32x4 cr = mm_cols<P, PP, NPF>(zero4(), s_dy + 16 * w * PP, s_h, 16 * m, r, qd);
+    const f32x4 cr = mm_cols<P, PP, NP>(zero4(), s_dy + 16 * w * PP, s_h, 16 * m, r, qd);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 16 * w + 4 * qd + e;
