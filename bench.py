@@ -378,6 +378,8 @@ def main():
     ap.add_argument("--heads-per-block", type=int, default=0, help="chunk_scan launch shape (0 = built-in)")
     ap.add_argument("--scan-variant", type=int, default=0,
                     help="chunk_scan decomposition: 1 = 64-row blocks, 2 = whole chunks, 0 = built-in")
+    ap.add_argument("--rows-group", type=int, default=0,
+                    help="chunk_scan row blocks: units per dispatch group on an XCD (0 = built-in, 16)")
     ap.add_argument("--conv-tokens", type=int, default=0,
                     help="conv1d_silu tokens per thread, a multiple of 4 (0 = built-in)")
     args = ap.parse_args()
@@ -403,6 +405,8 @@ def main():
         ssd.tune_set(0, args.heads_per_block)
     if args.scan_variant:
         ssd.tune_set(2, args.scan_variant)
+    if args.rows_group:
+        ssd.tune_set(4, args.rows_group)
 
     inp = I.make_workload_inputs(w)
     dec = I.make_step_inputs(w.batch, w.nheads, w.headdim, w.dstate, w.ngroups, 1, w.dtype,

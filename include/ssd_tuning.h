@@ -19,6 +19,8 @@ extern "C" {
  *        2 = one workgroup per whole chunk, 0 = built-in choice (1).
  * key 3: tokens per thread of ssd_conv1d_silu (rounded up to a multiple of 4); 0 restores
  *        the built-in choice (64, fewer on small inputs).
+ * key 4: chunk_scan row blocks: units (b, c, head) per dispatch group on one XCD, whose row
+ *        blocks run together (heaviest first within the group); 0 restores the built-in 16.
  * Unknown keys are ignored. */
 void ssd_tune_set(int key, int value);
 

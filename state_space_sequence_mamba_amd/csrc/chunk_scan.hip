@@ -22,12 +22,12 @@
 //
 // Two decompositions share these pieces:
 //  * rows : one workgroup (4 wavefronts, one strip each) per 64-row block of a chunk and
-//           head; row blocks with more causal tiles are dispatched first.  Many small
-//           workgroups, four per CU; x tiles are re-read by later row blocks (mostly from L2).
-//           The default for both dtypes.
+//           head; each XCD takes a contiguous run of units in groups whose row blocks are
+//           dispatched together (heaviest first), so that their re-reads of x and of the
+//           entering state hit L2.  The default for both dtypes.
 //  * chunk: one workgroup (8 wavefronts) per whole chunk and head block; wavefront w owns
 //           the strip pair (w, S-1-w), S+1 sub-tiles each.  x, the carried state and y move
-//           exactly once, but the register footprint allows one workgroup per CU.
+//           exactly once, but its registers allow one workgroup per CU.
 // Token tiles (64 tokens of B and of x for every head) are loaded into registers one tile
 // ahead of the MFMA work, then written to LDS.  y leaves through LDS as 16-byte row stores.
 //
@@ -433,7 +433,8 @@ __global__ __launch_bounds__(256, HB == 1 ? 4 : 2) void chunk_scan_rows_kernel(c
                                                                  const float* __restrict__ Dw,
                                                                  const T* __restrict__ Z,
                                                                  T* __restrict__ y,
-                                                                 int L, int H, int G, int nc, int Q, int B) {
+                                                                 int L, int H, int G, int nc, int Q, int B,
+                                                                 int group_units) {
   constexpr int NTHR = 256;
   typedef ScanLds<T, P, N, HB, kKT> SL;
   typedef NDot<T, N> ND;
@@ -453,7 +454,15 @@ __global__ __launch_bounds__(256, HB == 1 ? 4 : 2) void chunk_scan_rows_kernel(c
   const uint32_t U = (uint32_t)B * nc * nhb;          // units per row-block class
   const uint32_t hw = blockIdx.x;
   uint32_t cls, unit;
-  if ((U & 7u) == 0) {
+  if ((U & 7u) == 0 && group_units > 0) {
+    // every XCD a contiguous run of units, taken in groups of group_units whose row blocks
+    // are dispatched together (heaviest class first within the group): the group's row blocks
+    // share their x tiles and entering states in that XCD's L2
+    const uint32_t per = U >> 3, seq = hw >> 3, k = (uint32_t)group_units;
+    const uint32_t gi = seq / (nrb * k), gsize = min(k, per - gi * k), pos = seq - gi * nrb * k;
+    cls = pos / gsize;
+    unit = (hw & 7u) * per + gi * k + pos % gsize;
+  } else if ((U & 7u) == 0) {
     // heaviest row blocks first, every XCD an equal share of each class
     const uint32_t per = U >> 3, seq = hw >> 3;
     cls = seq / per;
@@ -689,7 +698,8 @@ static hipError_t launch_scan_hb(const FwdArgs& a, hipStream_t s) {
     const uint32_t nblocks = (uint32_t)a.B * a.nc * (a.H / HB) * (a.Q / kKT);
     hipExtLaunchKernelGGL(chunk_scan_rows_kernel<T, P, N, HB>, dim3(nblocks), dim3(256), 0, s, a.ev0, a.ev1, 0,
         static_cast<const T*>(a.x), static_cast<const T*>(a.Bm), a.cb, static_cast<const T*>(a.Cm), a.dtp, a.dAcs,
-        prevT, a.D, static_cast<const T*>(a.z), static_cast<T*>(a.y), a.L, a.H, a.G, a.nc, a.Q, a.B);
+        prevT, a.D, static_cast<const T*>(a.z), static_cast<T*>(a.y), a.L, a.H, a.G, a.nc, a.Q, a.B,
+        a.rows_group);
   }
   return hipGetLastError();
 }

@@ -91,6 +91,12 @@ int g_tune_heads_per_block = 0;  // 0 = heuristic
 int g_tune_min_blocks = 512;
 int g_tune_scan_variant = 0;     // 0 = built-in (row blocks)
 int g_tune_conv_segment = 0;     // 0 = sized to the chip
+int g_tune_rows_group = 0;       // units per row-block dispatch group (0 = built-in, 16)
+
+// Row-block dispatch groups of 16 units per XCD: measured on MI355X, bf16 B2 L16384 H80 G8
+// chunk_scan 514 -> 432 us (the row blocks of a unit re-read its x tiles and entering state
+// from L2 instead of HBM); B8 L4096 H32 and fp32 B4 L1024 unchanged within noise.
+int pick_rows_group() { return g_tune_rows_group > 0 ? g_tune_rows_group : 16; }
 
 // Row blocks for both dtypes: measured on MI355X, fp32 B4 L1024 H24 39 us against 68 us for
 // whole chunks; bf16 B8 L4096 H32 N128 191 us against 208 us (bf16 B2 L16384 H80 G8: 545 us
@@ -188,6 +194,7 @@ ssd_status_t fwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   a.prev16 = has_seq && dims->dtype == SSD_BF16 ? static_cast<void*>(ws + wl.prev16_off) : nullptr;
   a.keep_f32_states = 0;
   a.scan_variant = pick_scan_variant(a.dtype);
+  a.rows_group = pick_rows_group();
   a.heads_per_block = pick_heads_per_block(a.B, a.nc, a.H, a.G, a.Q, a.scan_variant);
   a.state_from_start = 0;
   a.passing_reverse = 0;
@@ -324,6 +331,7 @@ ssd_status_t bwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   f.prev16 = z && dims->dtype == SSD_BF16 ? static_cast<void*>(ws + wl.prev16) : nullptr;
   f.keep_f32_states = 1;                              // the backward kernels read the fp32 states
   f.scan_variant = pick_scan_variant(f.dtype);
+  f.rows_group = pick_rows_group();
   f.heads_per_block = pick_heads_per_block(f.B, f.nc, f.H, f.G, f.Q, f.scan_variant);
   f.state_from_start = 0;
   f.passing_reverse = 0;
@@ -599,6 +607,7 @@ void ssd_tune_set(int key, int value) {
   if (key == 0) g_tune_heads_per_block = value;
   if (key == 1) g_tune_min_blocks = value > 0 ? value : 512;
   if (key == 3) g_tune_conv_segment = value > 0 ? value : 0;
+  if (key == 4) g_tune_rows_group = value > 0 ? value : 0;
   if (key == 2) g_tune_scan_variant = value;
 }
 

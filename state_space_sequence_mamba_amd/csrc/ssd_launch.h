@@ -37,6 +37,7 @@ struct FwdArgs {
                            // null: chunk_state does not compute them
   int heads_per_block;     // chunk_scan: heads sharing one C B^T evaluation (divides H / G)
   int scan_variant;        // chunk_scan decomposition: 1 = 64-row blocks, 2 = whole chunks
+  int rows_group;          // row blocks: units per dispatch group on an XCD (0: all of one class first)
   hipEvent_t ev0, ev1;     // timing: start / stop events of the next launch (or null), recorded
                            // by the dispatch itself (hipExtLaunchKernelGGL), so they time the
                            // kernel alone, as a profiler's kernel trace does
