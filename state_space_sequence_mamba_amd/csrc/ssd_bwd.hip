@@ -29,6 +29,8 @@
 // arithmetic is the same either way and bf16 tiles take half the LDS), with row pitches that
 // start consecutive rows on different banks; the fp32 state tiles (Hprev, Gnext) reuse the
 // space of the token tiles once those are consumed.
+#include <type_traits>
+
 #include "ssd_common.h"
 #include "ssd_launch.h"
 
@@ -294,26 +296,36 @@ __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, 
     }
     __syncthreads();
     const float sj = s_SR[jl];
+    // MASK: the diagonal block or a block that crosses the end of the sequence; other blocks
+    // (every i after every j, all rows real) run as straight-line code without the mask
+    auto block = [&](auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti) {
-      if (I == R && ti < w) continue;              // tile entirely above the diagonal (i < j)
-      f32x4 cb = mm_rows<N, NP, NP>(zero4(), s_c + 16 * ti * NP, s_b + 16 * w * NP, r, qd);
-      f32x4 dxv = mm_rows<P, PP, PP>(zero4(), s_dy + 16 * ti * PP, s_x + 16 * w * PP, r, qd);
-      f32x4 m1, m2;
+      for (int ti = 0; ti < 4; ++ti) {
+        if (MASK && I == R && ti < w) continue;    // tile entirely above the diagonal (i < j)
+        f32x4 cb = mm_rows<N, NP, NP>(zero4(), s_c + 16 * ti * NP, s_b + 16 * w * NP, r, qd);
+        f32x4 dxv = mm_rows<P, PP, PP>(zero4(), s_dy + 16 * ti * PP, s_x + 16 * w * PP, r, qd);
+        f32x4 m1, m2;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int il = 16 * ti + 4 * qd + e;
-        const bool ok = (I * KT + il >= R * KT + jl) && il < lenI && jl < lenR;
-        const float ev = ok ? __builtin_amdgcn_exp2f((s_SI[il] - sj) * kLog2e) : 0.f;
-        m1[e] = ev * cb[e];
-        m2[e] = ev * dxv[e];
-        cs += m1[e] * dxv[e];
+        for (int e = 0; e < 4; ++e) {
+          const int il = 16 * ti + 4 * qd + e;
+          const bool ok = !MASK || ((I * KT + il >= R * KT + jl) && il < lenI && jl < lenR);
+          const float ev = ok ? __builtin_amdgcn_exp2f((s_SI[il] - sj) * kLog2e) : 0.f;
+          m1[e] = ev * cb[e];
+          m2[e] = ev * dxv[e];
+          cs += m1[e] * dxv[e];
+        }
+#pragma unroll
+        for (int m = 0; m < TPm; ++m) xi[m] = mm_regs<PP>(xi[m], m1, s_dy + 16 * ti * PP, 16 * m, r, qd);
+#pragma unroll
+        for (int m = 0; m < TNm; ++m) db[m] = mm_regs<NP>(db[m], m2, s_c + 16 * ti * NP, 16 * m, r, qd);
       }
-#pragma unroll
-      for (int m = 0; m < TPm; ++m) xi[m] = mm_regs<PP>(xi[m], m1, s_dy + 16 * ti * PP, 16 * m, r, qd);
-#pragma unroll
-      for (int m = 0; m < TNm; ++m) db[m] = mm_regs<NP>(db[m], m2, s_c + 16 * ti * NP, 16 * m, r, qd);
-    }
+    };
+    // (fp32 only: for bf16 tiles the second copy of the block was slower, 936 -> 1325 us)
+    if (sizeof(T) == 4 && I > R && lenI == KT && lenR == KT)
+      block(std::false_type());
+    else
+      block(std::true_type());
   }
 
   // carried terms through the gradient of the state leaving the chunk
@@ -487,22 +499,30 @@ __global__ __launch_bounds__(256) void bwd_dc_kernel(const T* __restrict__ x, co
     }
     __syncthreads();
     const float si = s_SR[il];
+    // MASK as in bwd_dxdb: blocks before the diagonal with all rows real run unmasked
+    auto block = [&](auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
-    for (int tj = 0; tj < 4; ++tj) {
-      if (J == R && tj > w) continue;              // tile entirely after the diagonal (j > i)
-      const f32x4 cbt = mm_rows<N, NP, NP>(zero4(), s_b + 16 * tj * NP, s_c + 16 * w * NP, r, qd);
-      const f32x4 dxt = mm_rows<P, PP, PP>(zero4(), s_x + 16 * tj * PP, s_dy + 16 * w * PP, r, qd);
-      f32x4 wt;
+      for (int tj = 0; tj < 4; ++tj) {
+        if (MASK && J == R && tj > w) continue;    // tile entirely after the diagonal (j > i)
+        const f32x4 cbt = mm_rows<N, NP, NP>(zero4(), s_b + 16 * tj * NP, s_c + 16 * w * NP, r, qd);
+        const f32x4 dxt = mm_rows<P, PP, PP>(zero4(), s_x + 16 * tj * PP, s_dy + 16 * w * PP, r, qd);
+        f32x4 wt;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int jl = 16 * tj + 4 * qd + e;
-        const bool ok = (R * KT + il >= J * KT + jl) && il < lenR && jl < lenJ;
-        wt[e] = ok ? __builtin_amdgcn_exp2f((si - s_SJ[jl]) * kLog2e) * s_dJ[jl] * dxt[e] : 0.f;
-        rs += wt[e] * cbt[e];
+        for (int e = 0; e < 4; ++e) {
+          const int jl = 16 * tj + 4 * qd + e;
+          const bool ok = !MASK || ((R * KT + il >= J * KT + jl) && il < lenR && jl < lenJ);
+          wt[e] = ok ? __builtin_amdgcn_exp2f((si - s_SJ[jl]) * kLog2e) * s_dJ[jl] * dxt[e] : 0.f;
+          rs += wt[e] * cbt[e];
+        }
+#pragma unroll
+        for (int m = 0; m < TNm; ++m) dc[m] = mm_regs<NP>(dc[m], wt, s_b + 16 * tj * NP, 16 * m, r, qd);
       }
-#pragma unroll
-      for (int m = 0; m < TNm; ++m) dc[m] = mm_regs<NP>(dc[m], wt, s_b + 16 * tj * NP, 16 * m, r, qd);
-    }
+    };
+    if (J < R && lenJ == KT && lenR == KT)
+      block(std::false_type());
+    else
+      block(std::true_type());
   }
   __syncthreads();
   stage_state<T, P, N>(s_h, states + (((size_t)b * nc + c) * H + h) * (size_t)(P * N), tid);
