@@ -144,23 +144,27 @@ def test_run_to_run_bitwise_determinism(dtype):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_launch_shapes_do_not_change_results(dtype):
-    """Both chunk_scan decompositions and every head-block size give bit-identical results."""
+    """Both chunk_scan decompositions, every head-block size and every row-block dispatch
+    grouping give bit-identical results."""
     _say(f"launch shape invariance {dtype}")
     inp = I.make_fwd_inputs(2, 700, 12, 64, 64, 1, dtype, seed=9)
     ref = None
     try:
         for variant in (1, 2):
             for hb in (1, 2):
-                ssd.tune_set(2, variant)
-                ssd.tune_set(0, hb)
-                y, f = _fwd_gpu(inp, 256)
-                if ref is None:
-                    ref = (y, f)
-                else:
-                    assert torch.equal(y, ref[0]) and torch.equal(f, ref[1]), (variant, hb)
+                for group in ((1, 16, 1000) if variant == 1 else (0,)):
+                    ssd.tune_set(2, variant)
+                    ssd.tune_set(0, hb)
+                    ssd.tune_set(4, group)          # row-block dispatch groups: order only
+                    y, f = _fwd_gpu(inp, 256)
+                    if ref is None:
+                        ref = (y, f)
+                    else:
+                        assert torch.equal(y, ref[0]) and torch.equal(f, ref[1]), (variant, hb, group)
     finally:
         ssd.tune_set(0, 0)
         ssd.tune_set(2, 0)
+        ssd.tune_set(4, 0)
     _check_full(inp, 256, TOL[dtype])
 
 
