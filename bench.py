@@ -218,14 +218,22 @@ def run_bwd(w, args, dev):
                       chunk_size=w.chunk, dfinal_state=dfin)
     dims = ssd.make_dims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, inp["x"].dtype)
     ws = torch.empty(ssd.ssd_bwd_workspace_size(dims, w.chunk), dtype=torch.uint8, device=dev)
+    # rotating copies of the per-token inputs and of the outputs, as in the forward benchmark
+    per_copy = sum(t.numel() * t.element_size() for t in (inp["x"], inp["dt"], inp["B"], inp["C"], dout))
+    per_copy += sum(t.numel() * t.element_size() for t in out.values() if t is not None)
+    R = max(1, -(-2 * args.rotate_mb * 2**20 // per_copy)) if args.rotate_mb > 0 else 1
+    copies = [(inp, dout, out)] + [({**inp, **{k: inp[k].clone() for k in ("x", "dt", "B", "C")}}, dout.clone(),
+                                    {k: (None if t is None else torch.empty_like(t)) for k, t in out.items()})
+                                   for _ in range(R - 1)]
 
-    def step(evs=None):
-        ssd.ssd_bwd(inp["x"], inp["dt"], inp["dt_bias"], inp["A"], inp["B"], inp["C"], dout, D=inp["D"],
-                    chunk_size=w.chunk, dfinal_state=dfin, workspace=ws, out=out, stage_events=evs)
+    def step(i, evs=None):
+        c, dy, o = copies[i % R]
+        ssd.ssd_bwd(c["x"], c["dt"], c["dt_bias"], c["A"], c["B"], c["C"], dy, D=c["D"],
+                    chunk_size=w.chunk, dfinal_state=dfin, workspace=ws, out=o, stage_events=evs)
 
     K, W = args.steps, args.warmup
-    for _ in range(W):
-        step()
+    for i in range(W):
+        step(i)
     torch.cuda.synchronize()
     use_graph = not args.no_graph
     if use_graph:
@@ -233,8 +241,8 @@ def run_bwd(w, args, dev):
         cap = torch.cuda.Stream()
         cap.wait_stream(torch.cuda.current_stream())
         with torch.cuda.graph(graph, stream=cap):
-            for _ in range(K):
-                step()
+            for i in range(K):
+                step(W + i)
         torch.cuda.synchronize()
     hev = HipEvents()
     t0, t1 = hev.create(), hev.create()
@@ -243,15 +251,15 @@ def run_bwd(w, args, dev):
     if use_graph:
         graph.replay()
     else:
-        for _ in range(K):
-            step()
+        for i in range(K):
+            step(W + i)
     hev.record(t1)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms = hev.elapsed_ms(t0, t1) / K
     events = [[hev.create() for _ in range(20)] for _ in range(K)]
     for i in range(K):
-        step(events[i])
+        step(W + i, events[i])
     torch.cuda.synchronize()
     per_kernel_ms = {k: sum(hev.elapsed_ms(ev[2 * i], ev[2 * i + 1]) for ev in events) / K
                      for i, k in enumerate(BWD_STAGES)}
@@ -284,6 +292,7 @@ def run_bwd(w, args, dev):
         "kernels": kernels,
         "launch": ("hip_graph (per-kernel times from an eager pass of the same K steps)" if use_graph
                    else "eager"),
+        "input_copies": R,
         "wall_s_timed_region": round(wall, 4),
     }
     hev.close()
@@ -373,6 +382,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch the timed steps eagerly, not as a HIP graph")
+    ap.add_argument("--rotate-mb", type=int, default=256,
+                    help="forward steps rotate over copies of x, dt, B, C, y totalling at least twice "
+                         "this many MiB, so inputs come from HBM, not the last-level cache (0 = one copy)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--heads-per-block", type=int, default=0, help="chunk_scan launch shape (0 = built-in)")
@@ -414,6 +426,13 @@ def main():
     d = {k: v.to(dev) for k, v in inp.items()}
     dd = {k: v[0].contiguous().to(dev) for k, v in dec.items() if k in ("x", "dt", "B", "C")}
     y = torch.empty_like(d["x"])
+    # Consecutive steps read and write rotating copies of the per-token tensors (x, dt, B, C,
+    # y), enough of them to exceed the 256 MB last-level cache twice, so that every step reads
+    # its inputs from HBM as a fresh batch would
+    per_copy = sum(d[k].numel() * d[k].element_size() for k in ("x", "dt", "B", "C")) + y.numel() * y.element_size()
+    R = max(1, -(-2 * args.rotate_mb * 2**20 // per_copy)) if args.rotate_mb > 0 else 1
+    copies = [{**d, "y": y}] + [{**d, **{k: d[k].clone() for k in ("x", "dt", "B", "C")}, "y": torch.empty_like(y)}
+                               for _ in range(R - 1)]
     state = torch.empty(w.batch, w.nheads, w.headdim, w.dstate, dtype=torch.float32, device=dev)
     y_dec = torch.empty_like(dd["x"])
     dims = ssd.make_dims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, d["x"].dtype)
@@ -426,18 +445,19 @@ def main():
     events = [[hev.create() for _ in range(nev)] for _ in range(max(K, 1))]
     t_start, t_end = hev.create(), hev.create()
 
-    def step(evs=None):
+    def step(i, evs=None):
         # launches go to the current stream (the capture stream while a graph is captured)
-        ssd.ssd_fwd(d["x"], d["dt"], d["dt_bias"], d["A"], d["B"], d["C"], d["D"], chunk_size=w.chunk,
-                    y=y, final_state=state, workspace=ws, stage_events=None if evs is None else evs[:6])
+        c = copies[i % R]
+        ssd.ssd_fwd(c["x"], c["dt"], c["dt_bias"], c["A"], c["B"], c["C"], c["D"], chunk_size=w.chunk,
+                    y=c["y"], final_state=state, workspace=ws, stage_events=None if evs is None else evs[:6])
         if evs is not None:
             hev.record(evs[6])
         ssd.ssd_step(state, dd["x"], dd["dt"], d["dt_bias"], d["A"], dd["B"], dd["C"], d["D"], y=y_dec)
         if evs is not None:
             hev.record(evs[7])
 
-    for _ in range(W):
-        step()
+    for i in range(W):
+        step(i)
     torch.cuda.synchronize()
     if use_graph:
         # the K steps are captured once into a HIP graph; the timed region is one replay
@@ -445,16 +465,16 @@ def main():
         cap = torch.cuda.Stream()
         cap.wait_stream(torch.cuda.current_stream())
         with torch.cuda.graph(graph, stream=cap):
-            for _ in range(K):
-                step()
+            for i in range(K):
+                step(W + i)
         torch.cuda.synchronize()
     wall0 = time.perf_counter()
     hev.record(t_start)
     if use_graph:
         graph.replay()
     else:
-        for _ in range(K):
-            step()
+        for i in range(K):
+            step(W + i)
     hev.record(t_end)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -465,7 +485,7 @@ def main():
     # start / stop event pair recorded by its own dispatch (ssd_fwd_timed); ssd_step between
     # two stream events.  Timing events cannot live inside a captured graph on this runtime.
     for i in range(K):
-        step(events[i])
+        step(W + i, events[i])
     torch.cuda.synchronize()
 
     per_kernel_ms = {k: 0.0 for k in KERNELS}
@@ -516,6 +536,7 @@ def main():
         "kernels": kernels,
         "launch": ("hip_graph (per-kernel times from an eager pass of the same K steps)" if use_graph
                    else "eager"),
+        "input_copies": R,
         "wall_s_timed_region": round(wall, 4),
     }
     if not args.no_cpu_baseline:
