@@ -9,10 +9,10 @@
 // Bandwidth bound: the fp32 state is read and written once; everything else is small.
 // The state is streamed with non-temporal loads and stores: it is touched once per step and
 // a large decode batch does not fit the last-level cache, so caching it only evicts others.
-// One 256-thread workgroup per (b, h).  A row of N floats is covered by N/4 consecutive
-// lanes (one float4 each), so the state tile streams with fully coalesced 16-byte accesses
-// and the reduction over n is a butterfly of N/4 lanes inside a wavefront.  All state loads
-// of a thread are issued before any use.
+// One 256-thread workgroup per (b, h), or per half or quarter of its rows for small batches.
+// A row of N floats is covered by N/4 consecutive lanes (one float4 each), so the state tile
+// streams with fully coalesced 16-byte accesses and the reduction over n is a butterfly of
+// N/4 lanes inside a wavefront.  All state loads of a thread are issued before any use.
 #include "ssd_common.h"
 #include "ssd_launch.h"
 
@@ -29,11 +29,12 @@ __global__ __launch_bounds__(256) void ssd_step_kernel(float* __restrict__ state
                                                        const float* __restrict__ Dw,
                                                        const T* __restrict__ Z,
                                                        T* __restrict__ y, int H, int G, int clamp,
-                                                       float lo, float hi) {
+                                                       float lo, float hi, int split) {
   constexpr int TPR = N / 4;           // lanes per state row
   constexpr int RPP = 256 / TPR;       // rows per pass
   constexpr int NPASS = (P + RPP - 1) / RPP;
-  const int bh = blockIdx.x;
+  const int bh = blockIdx.x / split;
+  const int prows = P / split, pbase = (blockIdx.x % split) * prows;   // this workgroup's rows
   const int h = bh % H, b = bh / H;
   const int g = h / (H / G);
   const int tid = threadIdx.x;
@@ -55,18 +56,20 @@ __global__ __launch_bounds__(256) void ssd_step_kernel(float* __restrict__ state
   float* st = state + (size_t)bh * P * N;
   f32x4 s[NPASS];
   float xv[NPASS];
+  // every load is issued (rows past the workgroup's share read its first row again) before
+  // any use
 #pragma unroll
   for (int u = 0; u < NPASS; ++u) {
-    const int p = row0 + u * RPP;
-    if (p < P) {
-      s[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(st + (size_t)p * N + col));
-      xv[u] = to_f32(x[(size_t)bh * P + p]);
-    }
+    const int pl = row0 + u * RPP;
+    const int p = pbase + (pl < prows ? pl : 0);
+    s[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(st + (size_t)p * N + col));
+    xv[u] = to_f32(x[(size_t)bh * P + p]);
   }
 #pragma unroll
   for (int u = 0; u < NPASS; ++u) {
-    const int p = row0 + u * RPP;
-    if (p < P) {
+    const int pl = row0 + u * RPP;
+    const int p = pbase + pl;
+    if (pl < prows) {
       const float dx = d * xv[u];
       f32x4 v = s[u];
 #pragma unroll
@@ -90,11 +93,17 @@ __global__ __launch_bounds__(256) void ssd_step_kernel(float* __restrict__ state
 
 template <typename T, int P, int N>
 static hipError_t launch_step_impl(const StepArgs& a, hipStream_t s) {
-  const unsigned nblocks = (unsigned)a.B * a.H;
+  // small batches: the rows of a (b, h) state over up to 4 workgroups (whole passes of
+  // 256 / (N / 4) rows each), so that the launch still spreads over the chip
+  constexpr int RPP = 256 / (N / 4);
+  int split = 1;
+  while (split < 4 && (long)a.B * a.H * split < 1024 && P % (2 * split) == 0 && (P / (2 * split)) % RPP == 0)
+    split *= 2;
+  const unsigned nblocks = (unsigned)a.B * a.H * split;
   ssd_step_kernel<T, P, N><<<nblocks, 256, 0, s>>>(
       a.state, static_cast<const T*>(a.x), static_cast<const T*>(a.dt), a.dt_bias, a.A,
       static_cast<const T*>(a.Bm), static_cast<const T*>(a.Cm), a.D, static_cast<const T*>(a.z),
-      static_cast<T*>(a.y), a.H, a.G, a.clamp, a.dt_lo, a.dt_hi);
+      static_cast<T*>(a.y), a.H, a.G, a.clamp, a.dt_lo, a.dt_hi, split);
   return hipGetLastError();
 }
 
