@@ -296,8 +296,61 @@ def run_bwd(w, args, dev):
         "wall_s_timed_region": round(wall, 4),
     }
     hev.close()
+    emit(args, dev, res)
+
+
+def peak_probe(dev):
+    """Attainable rates measured on this GPU, to set beside the published peaks the rooflines use:
+    register-resident MFMA loops (libssd_peak.so) for the two matrix shapes the kernels issue,
+    and a 1 GiB device-to-device copy (read + write bytes per second)."""
+    import ctypes
+    from state_space_sequence_mamba_amd import build as B
+    if not os.path.exists(B.LIB_PEAK):
+        raise RuntimeError(f"{B.LIB_PEAK} not found: build it with `python -m state_space_sequence_mamba_amd.build`")
+    lib = ctypes.CDLL(B.LIB_PEAK)
+    lib.ssd_peak_mfma_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.ssd_peak_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.ssd_peak_mfma_flops.restype = ctypes.c_double
+    blocks = 2048
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {}
+    for kind, name, iters in ((0, "fp32_mfma_16x16x4_tflops", 10000), (1, "bf16_mfma_16x16x32_tflops", 20000)):
+        best = None
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            rc = lib.ssd_peak_mfma_launch(kind, blocks, iters, ctypes.c_void_p(out.data_ptr()),
+                                          ctypes.c_void_p(stream))
+            e1.record()
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"ssd_peak_mfma_launch({kind}) failed: {rc}")
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        res[name] = round(lib.ssd_peak_mfma_flops(kind, blocks, iters) / (best * 1e-3) / 1e12, 1)
+    n = 1024 * 1024 * 1024
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = None
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        best = e0.elapsed_time(e1) if best is None else min(best, e0.elapsed_time(e1))
+    res["copy_1gib_gbs"] = round(2 * n / (best * 1e-3) / 1e9, 1)
+    del src, dst
+    return res
+
+
+def emit(args, dev, out):
     copy_probe(args, dev)
-    print(json.dumps(res), flush=True)
+    if args.peak_probe:
+        out["measured_peaks"] = peak_probe(dev)
+    print(json.dumps(out), flush=True)
 
 
 def copy_probe(args, dev):
@@ -369,8 +422,7 @@ def run_conv(w, args, dev):
         "launch": "hip_graph" if use_graph else "eager",
         "wall_s_timed_region": round(wall, 4),
     }
-    copy_probe(args, dev)
-    print(json.dumps(out), flush=True)
+    emit(args, dev, out)
 
 
 def main():
@@ -387,6 +439,8 @@ def main():
                          "this many MiB, so inputs come from HBM, not the last-level cache (0 = one copy)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--peak-probe", action="store_true",
+                    help="after timing, measure attainable MFMA rates and copy bandwidth (measured_peaks)")
     ap.add_argument("--heads-per-block", type=int, default=0, help="chunk_scan launch shape (0 = built-in)")
     ap.add_argument("--scan-variant", type=int, default=0,
                     help="chunk_scan decomposition: 1 = 64-row blocks, 2 = whole chunks, 0 = built-in")
@@ -541,8 +595,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, dec, args.cpu_budget)
-    copy_probe(args, dev)
-    print(json.dumps(out), flush=True)
+    emit(args, dev, out)
 
 
 if __name__ == "__main__":

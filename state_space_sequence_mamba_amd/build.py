@@ -3,7 +3,8 @@
     python -m state_space_sequence_mamba_amd.build        # or build() from Python
 
 Each .hip file is compiled to an object in _build/ (in parallel), then linked into
-state_space_sequence_mamba_amd/libssd.so.  Always recompiles.
+state_space_sequence_mamba_amd/libssd.so (and the measurement-only libssd_peak.so).  Always
+recompiles.
 """
 import concurrent.futures
 import os
@@ -20,6 +21,9 @@ LIB = os.path.join(PKG, "libssd.so")
 
 SOURCES = ["ssd_api.hip", "chunk_state.hip", "state_passing.hip", "chunk_scan.hip",
            "ssd_step.hip", "conv1d.hip", "ssd_bwd.hip"]
+# measurement only (bench.py --peak-probe): register-resident MFMA loops, a library of its own
+PEAK_SOURCES = ["peak_probe.hip"]
+LIB_PEAK = os.path.join(PKG, "libssd_peak.so")
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -48,20 +52,20 @@ def _run(cmd):
 def build(verbose=False, jobs=None):
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
-    objs = []
     cmds = []
-    for src in SOURCES:
+    for src in SOURCES + PEAK_SOURCES:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        objs.append(obj)
         cmds.append([cc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
     jobs = jobs or min(len(cmds), os.cpu_count() or 4, 8)
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
         for cmd, err in zip(cmds, ex.map(_run, cmds)):
             if verbose or err.strip():
                 print(" ".join(os.path.basename(c) for c in cmd[-3:]), err, file=sys.stderr)
-    tmp = LIB + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
+    for lib, srcs in ((LIB, SOURCES), (LIB_PEAK, PEAK_SOURCES)):
+        objs = [os.path.join(BUILD, os.path.splitext(src)[0] + ".o") for src in srcs]
+        tmp = lib + ".tmp"
+        _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -14,9 +14,13 @@ from state_space_sequence_mamba_amd import ssd
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _declared_functions():
+def _declared_functions(peak=False):
+    """Functions declared by include/*.h: those of ssd_peak.h (the measurement-only
+    libssd_peak.so) with peak=True, the others (libssd.so) without."""
     names = set()
     for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        if (os.path.basename(h) == "ssd_peak.h") != peak:
+            continue
         text = open(h).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         for m in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b(ssd_\w+)\s*\(", text, flags=re.M):
@@ -40,6 +44,24 @@ def test_every_declared_symbol_is_exported(lib):
     out = subprocess.run(["nm", "-D", "--defined-only", ssd.LIB_PATH], capture_output=True, text=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
     assert set(names) <= exported
+
+
+def test_peak_probe_library_exports_its_declared_symbols():
+    from state_space_sequence_mamba_amd import build as B
+    if not os.path.exists(B.LIB_PEAK):
+        pytest.fail("libssd_peak.so is not built (run __graft_entry__.build())")
+    names = _declared_functions(peak=True)
+    assert names == ["ssd_peak_mfma_flops", "ssd_peak_mfma_launch"]
+    peak = ctypes.CDLL(B.LIB_PEAK)
+    peak.ssd_peak_mfma_flops.restype = ctypes.c_double
+    peak.ssd_peak_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    assert peak.ssd_peak_mfma_flops(0, 2, 3) == 2048.0 * 4 * 3 * 4 * 2
+    assert peak.ssd_peak_mfma_flops(1, 1, 1) == 16384.0 * 16
+    # invalid arguments return 1 before any HIP call
+    peak.ssd_peak_mfma_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                          ctypes.c_void_p]
+    assert peak.ssd_peak_mfma_launch(0, 0, 1, None, None) == 1
+    assert peak.ssd_peak_mfma_launch(5, 1, 1, ctypes.c_void_p(16), None) == 1
 
 
 def test_library_is_built_for_gfx950():
