@@ -56,7 +56,8 @@ template <int N> struct NDot<__bf16, N> {
 // block pair (rb, J <= rb) numbered blk = rb (rb + 1) / 2 + J, the 16 causal 16 x 16
 // sub-tiles (strip 4 rb + w, column tile 4 J + js) that the scan's rows decomposition
 // consumes, computed once per group instead of once per head.  Stored as 16 KB in the lane
-// order of the scan's A operand: sub-tile (w, js), lane l, element e at ((4 w + js) 64 + l) 4 + e,
+// order of the scan's A operand (each scan wavefront loads its four sub-tiles with one
+// 16-byte load per lane each): sub-tile (w, js), lane l, element e at ((4 w + js) 64 + l) 4 + e,
 // i.e. lane (r, qd) holds CB[i = 16 (4 rb + w) + r][j = 16 (4 J + js) + 4 qd + e].  The MFMA
 // sequence is the scan's own, so results are bit-identical to computing in place.  Sub-tiles
 // past the diagonal and rows past the sequence are zeros.  Four wavefronts (tid in [0, 256)),

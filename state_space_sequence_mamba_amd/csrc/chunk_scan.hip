@@ -30,6 +30,9 @@
 //           exactly once, but its registers allow one workgroup per CU.
 // Token tiles (64 tokens of B and of x for every head) are loaded into registers one tile
 // ahead of the MFMA work, then written to LDS.  y leaves through LDS as 16-byte row stores.
+// fp32 row blocks read C B^T precomputed once per group (cb_block, in the A-operand lane
+// order): each wavefront loads its own four sub-tiles of a column tile straight into
+// registers, one tile ahead, with no LDS copy.
 //
 // MFMA: fp32 inputs -> v_mfma_f32_16x16x4_f32 for all three products; bf16 inputs ->
 // 16x16x32 bf16 for C B^T and C Hprev^T, 16x16x16 bf16 for (L o CB) X.  Decay factors use
@@ -52,14 +55,14 @@ template <int P> struct TPof { static constexpr int v = P / 16; };
 // registers would spill there, and its sub-tiles are MFMA-bound).
 template <typename T> constexpr bool kSplitDecay = sizeof(T) == 2;
 
-template <typename T, int P, int N, int HB, int ROWS>
+template <typename T, int P, int N, int HB, int ROWS, bool NOB = false>
 struct ScanLds {
   static constexpr bool F32 = sizeof(T) == 4;
   static constexpr int BP = N + (F32 ? 4 : 8);   // B tile / Hprev rows (n-contiguous), 16-byte rows
   static constexpr int XP = kKT + 4;              // x^T rows (token-contiguous)
   static constexpr int YP = P + (F32 ? 4 : 8);   // y staging rows
-  // B tile, or (fp32) the 16 KB block of precomputed C B^T sub-tiles that replaces it
-  static constexpr int B_ELEMS = (F32 && 16 * 256 > kKT * BP) ? 16 * 256 : kKT * BP;
+  // B tile (none when C B^T comes precomputed)
+  static constexpr int B_ELEMS = NOB ? 0 : kKT * BP;
   static constexpr int X_ELEMS = HB * P * XP;
   static constexpr int PREV_ELEMS = P * BP;
   static constexpr int XU_ELEMS = X_ELEMS > PREV_ELEMS ? X_ELEMS : PREV_ELEMS;  // x tiles alias Hprev
@@ -72,14 +75,14 @@ struct ScanLds {
 // between its global loads and its LDS stores.  Loads read clamped in-bounds addresses and
 // only record which tokens are real; the zeroing selects happen at store time, so nothing
 // waits for the loads until the tile is written to LDS (after the current tile's MFMAs).
-// PRECB: instead of B rows, the tile is the 16 KB block of precomputed C B^T sub-tiles of
-// (row block, column tile J), copied as is (cb_block writes it in the lane order used here).
+// PRECB: C B^T comes precomputed (each wavefront loads its own sub-tiles into registers), and
+// the tile is x alone.
 
 template <typename T, int P, int N, int HB, int NTHR, bool PRECB = false>
 struct TileRegs {
   static constexpr int VEC = Vec16<T>::n;
   static constexpr int NVR = N / VEC, PV = P / VEC;
-  static constexpr int BU = PRECB ? kCbBlock / 4 : kKT * NVR;   // 16-byte vectors of B (or C B^T)
+  static constexpr int BU = PRECB ? 0 : kKT * NVR;      // 16-byte vectors of B (none with PRECB)
   static constexpr int XU = HB * (kKT / 2) * PV;       // token-pair units of x
   // x unit order: for bf16 the 16-byte vectors of one token row sit on consecutive lanes, so
   // every load instruction reads whole rows (the transposing LDS stores then meet two-way bank
@@ -89,7 +92,7 @@ struct TileRegs {
   static constexpr bool kXRows = sizeof(T) == 2;
   static constexpr int BPT = (BU + NTHR - 1) / NTHR, XPT = (XU + NTHR - 1) / NTHR;
   static_assert(BPT + 2 * XPT <= 32, "validity mask");
-  Vec16<T> b[BPT];
+  Vec16<T> b[BPT > 0 ? BPT : 1];
   Vec16<T> x[XPT][2];
   uint32_t okm;
 
@@ -99,16 +102,11 @@ struct TileRegs {
 #pragma unroll
     for (int u = 0; u < BPT; ++u) {
       const int v = min(tid + NTHR * u, BU - 1);
-      if (PRECB) {
-        b[u] = load16(Bb + (size_t)J * kCbBlock + 4 * v);
-        okm |= 1u << u;
-      } else {
-        const int i = v / NVR, nv = (v % NVR) * VEC;
-        const int tok = J * kKT + i;
-        const bool ok = tok < len;
-        b[u] = load16(Bb + (uint32_t)(ok ? tok : 0) * bc_tok + nv);
-        okm |= (uint32_t)ok << u;
-      }
+      const int i = v / NVR, nv = (v % NVR) * VEC;
+      const int tok = J * kKT + i;
+      const bool ok = tok < len;
+      b[u] = load16(Bb + (uint32_t)(ok ? tok : 0) * bc_tok + nv);
+      okm |= (uint32_t)ok << u;
     }
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {
@@ -131,12 +129,8 @@ struct TileRegs {
     for (int u = 0; u < BPT; ++u) {
       const int v = tid + NTHR * u;
       if (BU % NTHR == 0 || v < BU) {
-        if (PRECB) {
-          *reinterpret_cast<Vec16<T>*>(&s_b[4 * v]) = b[u];
-        } else {
-          const int i = v / NVR, nv = (v % NVR) * VEC;
-          *reinterpret_cast<Vec16<T>*>(&s_b[i * BP + nv]) = keep_if(b[u], (okm >> u) & 1u);
-        }
+        const int i = v / NVR, nv = (v % NVR) * VEC;
+        *reinterpret_cast<Vec16<T>*>(&s_b[i * BP + nv]) = keep_if(b[u], (okm >> u) & 1u);
       }
     }
 #pragma unroll
@@ -200,7 +194,7 @@ __device__ __forceinline__ void sub_tile(f32x4 (&acc)[HB][TPof<P>::v], const typ
                                          const float (&dco)[HB][TPof<P>::v], const T* s_b, const T* s_x,
                                          const float (*s_da)[256], const float (*s_dt)[256],
                                          const float (*s_w)[256], int strip, int jt, int js, int lstrip, int r,
-                                         int qd) {
+                                         int qd, const f32x4& cbr) {
   typedef NDot<T, N> ND;
   constexpr int TP = P / 16;
   constexpr bool F32 = sizeof(T) == 4;
@@ -209,8 +203,7 @@ __device__ __forceinline__ void sub_tile(f32x4 (&acc)[HB][TPof<P>::v], const typ
   // CB^T sub-tile: lane holds CB[i = 16 strip + r][j = 16 jt + 4 qd + e]
   f32x4 cbt;
   if constexpr (PRECB) {
-    cbt = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(s_b) +
-                                          ((lstrip * 4 + js) * 64 + r + 16 * qd) * 4);
+    cbt = cbr;                                   // lane (r, qd) of sub-tile (lstrip, js)
   } else {
     typename ND::frag bfr;
     ND::load(bfr, &s_b[(js * 16 + r) * BP], qd);
@@ -288,13 +281,14 @@ template <typename T, int P, int N, int HB, int BP, int XP, bool PRECB = false>
 __device__ __forceinline__ void diag_tile(f32x4 (&acc)[HB][TPof<P>::v], const typename NDot<T, N>::frag& cf,
                                           const float (&dco)[HB][TPof<P>::v], const T* s_b, const T* s_x,
                                           const float (*s_da)[256], const float (*s_dt)[256],
-                                          const float (*s_w)[256], int strip, int J, int lstrip, int r, int qd) {
+                                          const float (*s_w)[256], int strip, int J, int lstrip, int r, int qd,
+                                          const f32x4 (&cbr)[4]) {
 #pragma unroll
   for (int js = 0; js < 4; ++js) {
     const int jt = 4 * J + js;
     if (jt > strip) break;
     sub_tile<T, P, N, HB, BP, XP, true, PRECB>(acc, cf, dco, s_b, s_x, s_da, s_dt, s_w, strip, jt, js, lstrip, r,
-                                               qd);
+                                               qd, cbr[js]);
   }
 }
 
@@ -305,11 +299,15 @@ template <typename T, int P, int N, int HB, int BP, int XP, bool PRECB = false>
 __device__ __forceinline__ void full_tile(f32x4 (&acc)[HB][TPof<P>::v], const typename NDot<T, N>::frag& cf,
                                           const float (&dco)[HB][TPof<P>::v], const T* s_b, const T* s_x,
                                           const float (*s_da)[256], const float (*s_dt)[256],
-                                          const float (*s_w)[256], int strip, int J, int lstrip, int r, int qd) {
+                                          const float (*s_w)[256], int strip, int J, int lstrip, int r, int qd,
+                                          f32x4 (&cbr)[4], const float* cb_next) {
 #pragma unroll
-  for (int js = 0; js < 4; ++js)
+  for (int js = 0; js < 4; ++js) {
     sub_tile<T, P, N, HB, BP, XP, false, PRECB>(acc, cf, dco, s_b, s_x, s_da, s_dt, s_w, strip, 4 * J + js, js,
-                                                lstrip, r, qd);
+                                                lstrip, r, qd, cbr[js]);
+    // the next block's sub-tile into the register this one has just released
+    if constexpr (PRECB) cbr[js] = *reinterpret_cast<const f32x4*>(cb_next + 256 * js);
+  }
 }
 
 // Output gate y * silu(z) on one strip's registers (rows 16 strip + 4 qd + e, column 16 pt + r).
@@ -444,7 +442,8 @@ __global__ __launch_bounds__(256, HB == 1 ? 4 : 2) void chunk_scan_rows_kernel(c
                                                                  int L, int H, int G, int nc, int Q, int B,
                                                                  int group_units) {
   constexpr int NTHR = 256;
-  typedef ScanLds<T, P, N, HB, kKT> SL;
+  // fp32: C B^T sub-tiles come precomputed, straight into each wavefront's registers
+  typedef ScanLds<T, P, N, HB, kKT, sizeof(T) == 4> SL;
   typedef NDot<T, N> ND;
   constexpr int TP = P / 16;
 
@@ -524,6 +523,13 @@ __global__ __launch_bounds__(256, HB == 1 ? 4 : 2) void chunk_scan_rows_kernel(c
     for (int pt = 0; pt < TP; ++pt) dco[hh][pt] = Dw ? Dw[(size_t)(h0 + hh) * P + pt * 16 + r] : 0.f;
   TileRegs<T, P, N, HB, NTHR, PRECB> tr;
   tr.load(Bb, xb, (uint32_t)bc_tok, (uint32_t)x_tok, 0, len, tid);
+  // this wavefront's four C B^T sub-tiles of block (rb, 0), in the lane order cb_block wrote
+  const float* cb_lane = reinterpret_cast<const float*>(Bb) + ((size_t)(wave * 4) * 64 + lane) * 4;
+  f32x4 cbr[4] = {};
+  if constexpr (PRECB) {
+#pragma unroll
+    for (int js = 0; js < 4; ++js) cbr[js] = *reinterpret_cast<const f32x4*>(cb_lane + 256 * js);
+  }
 
   f32x4 acc[HB][TP];
 #pragma unroll
@@ -550,9 +556,11 @@ __global__ __launch_bounds__(256, HB == 1 ? 4 : 2) void chunk_scan_rows_kernel(c
     __syncthreads();
     if (strip_ok) {
       if (J < rb)
-        full_tile<T, P, N, HB, SL::BP, SL::XP, PRECB>(acc, cf, dco, s_b, s_xu, s_da, s_dt, s_w, s, J, wave, r, qd);
+        full_tile<T, P, N, HB, SL::BP, SL::XP, PRECB>(acc, cf, dco, s_b, s_xu, s_da, s_dt, s_w, s, J, wave, r, qd,
+                                                      cbr, cb_lane + (size_t)(J + 1) * kCbBlock);
       else
-        diag_tile<T, P, N, HB, SL::BP, SL::XP, PRECB>(acc, cf, dco, s_b, s_xu, s_da, s_dt, s_w, s, J, wave, r, qd);
+        diag_tile<T, P, N, HB, SL::BP, SL::XP, PRECB>(acc, cf, dco, s_b, s_xu, s_da, s_dt, s_w, s, J, wave, r, qd,
+                                                      cbr);
     }
   }
   if (Z && strip_ok) apply_gate<T, P, HB>(acc, Z, (size_t)b * L + t0, x_tok, h0, s, len, r, qd);
@@ -663,6 +671,7 @@ __global__ __launch_bounds__(512) void chunk_scan_chunk_kernel(const T* __restri
       if (ok[st]) carried_term<T, P, N, SL::BP>(acc[st][hh], cf[st], s_xu, s_da[hh], strip[st], r, qd);
   }
   const int ntiles = (len + kKT - 1) / kKT;
+  f32x4 no_cb[4] = {};                                  // (C B^T is formed here, not read)
   for (int J = 0; J < ntiles; ++J) {
     __syncthreads();
     tr.template store<SL::BP, SL::XP>(s_b, s_xu, tid);
@@ -672,10 +681,10 @@ __global__ __launch_bounds__(512) void chunk_scan_chunk_kernel(const T* __restri
     for (int st = 0; st < 2; ++st) {
       if (ok[st] && 4 * J + 3 < strip[st])
         full_tile<T, P, N, HB, SL::BP, SL::XP>(acc[st], cf[st], dco, s_b, s_xu, s_da, s_dt, s_w, strip[st], J, 0, r,
-                                               qd);
+                                               qd, no_cb, nullptr);
       else if (ok[st] && 4 * J <= strip[st])
         diag_tile<T, P, N, HB, SL::BP, SL::XP>(acc[st], cf[st], dco, s_b, s_xu, s_da, s_dt, s_w, strip[st], J, 0, r,
-                                               qd);
+                                               qd, no_cb);
     }
   }
   if (Z) {
