@@ -52,7 +52,7 @@ template <int N> struct NDot<__bf16, N> {
   }
 };
 
-// One block of C B^T sub-tiles (fp32): for (batch, chunk, group) and the row block / column
+// One block of C B^T sub-tiles (fp32 values, from fp32 or bf16 B and C): for (batch, chunk, group) and the row block / column
 // block pair (rb, J <= rb) numbered blk = rb (rb + 1) / 2 + J, the 16 causal 16 x 16
 // sub-tiles (strip 4 rb + w, column tile 4 J + js) that the scan's rows decomposition
 // consumes, computed once per group instead of once per head.  Stored as 16 KB in the lane
@@ -62,11 +62,11 @@ template <int N> struct NDot<__bf16, N> {
 // sequence is the scan's own, so results are bit-identical to computing in place.  Sub-tiles
 // past the diagonal and rows past the sequence are zeros.  Four wavefronts (tid in [0, 256)),
 // one per strip.
-template <int N>
-__device__ __forceinline__ void cb_block(const float* __restrict__ Bm, const float* __restrict__ Cm,
+template <typename T, int N>
+__device__ __forceinline__ void cb_block(const T* __restrict__ Bm, const T* __restrict__ Cm,
                                          float* __restrict__ cb, int L, int G, int nc, int Q, uint32_t id,
                                          int tid) {
-  typedef NDot<float, N> ND;
+  typedef NDot<T, N> ND;
   const int nrb = Q / kCbKT, nblk = nrb * (nrb + 1) / 2;
   const int blk = id % nblk;
   id /= nblk;
@@ -81,22 +81,28 @@ __device__ __forceinline__ void cb_block(const float* __restrict__ Bm, const flo
   const int r = lane & 15, qd = lane >> 4;
   const int strip = 4 * rb + w;
   const size_t bc_tok = (size_t)G * N;
-  const float* Cb = Cm + ((size_t)b * L + t0) * bc_tok + (size_t)g * N;
-  const float* Bb = Bm + ((size_t)b * L + t0) * bc_tok + (size_t)g * N;
+  const T* Cb = Cm + ((size_t)b * L + t0) * bc_tok + (size_t)g * N;
+  const T* Bb = Bm + ((size_t)b * L + t0) * bc_tok + (size_t)g * N;
   float* out = cb + ((((size_t)b * nc + c) * G + g) * nblk + blk) * (size_t)kCbBlock;
-  // every fragment load is issued before the first MFMA
-  typename ND::frag cf, bfr[4];
+  // the fragment loads of JB column tiles are issued before their MFMAs (all four at once
+  // where the registers allow it, two by two for bf16, whose caller keeps fewer)
+  constexpr int JB = sizeof(T) == 4 ? 4 : 2;
+  typename ND::frag cf, bfr[JB];
   const int i = 16 * strip + r;
   ND::load(cf, Cb + (size_t)(i < len ? i : 0) * bc_tok, qd, i < len);
 #pragma unroll
-  for (int js = 0; js < 4; ++js) {
-    const int j = 16 * (4 * J + js) + r;
-    ND::load(bfr[js], Bb + (size_t)(j < len ? j : 0) * bc_tok, qd, j < len);
-  }
+  for (int j0 = 0; j0 < 4; j0 += JB) {
 #pragma unroll
-  for (int js = 0; js < 4; ++js) {
-    const f32x4 cbt = (4 * J + js <= strip) ? ND::dot(bfr[js], cf, zero4()) : zero4();
-    *reinterpret_cast<f32x4*>(out + ((w * 4 + js) * 64 + lane) * 4) = cbt;
+    for (int u = 0; u < JB; ++u) {
+      const int j = 16 * (4 * J + j0 + u) + r;
+      ND::load(bfr[u], Bb + (size_t)(j < len ? j : 0) * bc_tok, qd, j < len);
+    }
+#pragma unroll
+    for (int u = 0; u < JB; ++u) {
+      const int js = j0 + u;
+      const f32x4 cbt = (4 * J + js <= strip) ? ND::dot(bfr[u], cf, zero4()) : zero4();
+      *reinterpret_cast<f32x4*>(out + ((w * 4 + js) * 64 + lane) * 4) = cbt;
+    }
   }
 }
 

@@ -428,8 +428,8 @@ struct PrevRegs {
 };
 
 // ---------------------------------------------------------------- row-block decomposition
-template <typename T, int P, int N, int HB>
-__global__ __launch_bounds__(256, HB == 1 ? 4 : 2) void chunk_scan_rows_kernel(const T* __restrict__ x,
+template <typename T, int P, int N, int HB, bool PRECB>
+__global__ __launch_bounds__(256, HB == 1 ? (sizeof(T) == 2 && PRECB && N >= 128 ? 5 : 4) : 2) void chunk_scan_rows_kernel(const T* __restrict__ x,
                                                                  const T* __restrict__ Bm,
                                                                  const float* __restrict__ cbp,
                                                                  const T* __restrict__ Cm,
@@ -442,8 +442,8 @@ __global__ __launch_bounds__(256, HB == 1 ? 4 : 2) void chunk_scan_rows_kernel(c
                                                                  int L, int H, int G, int nc, int Q, int B,
                                                                  int group_units) {
   constexpr int NTHR = 256;
-  // fp32: C B^T sub-tiles come precomputed, straight into each wavefront's registers
-  typedef ScanLds<T, P, N, HB, kKT, sizeof(T) == 4> SL;
+  // PRECB: C B^T sub-tiles come precomputed, straight into each wavefront's registers
+  typedef ScanLds<T, P, N, HB, kKT, PRECB> SL;
   typedef NDot<T, N> ND;
   constexpr int TP = P / 16;
 
@@ -495,8 +495,7 @@ __global__ __launch_bounds__(256, HB == 1 ? 4 : 2) void chunk_scan_rows_kernel(c
 
   const size_t bc_tok = (size_t)G * N, x_tok = (size_t)H * P;
   const T* Cb = Cm + ((size_t)b * L + t0) * bc_tok + (size_t)g * N;
-  // fp32: the C B^T sub-tiles of this row block come precomputed (once per group) by cb_block
-  constexpr bool PRECB = sizeof(T) == 4;
+  // PRECB: the C B^T sub-tiles of this row block come precomputed (once per group) by cb_block
   const T* Bb = PRECB ? reinterpret_cast<const T*>(cbp + (((size_t)b * nc + c) * G + g) *
                                                              (size_t)(nrb * (nrb + 1) / 2) * kCbBlock +
                                                    (size_t)(rb * (rb + 1) / 2) * kCbBlock)
@@ -713,7 +712,14 @@ static hipError_t launch_scan_hb(const FwdArgs& a, hipStream_t s) {
         prevT, a.D, static_cast<const T*>(a.z), static_cast<T*>(a.y), a.L, a.H, a.G, a.nc, a.Q, nblocks);
   } else {
     const uint32_t nblocks = (uint32_t)a.B * a.nc * (a.H / HB) * (a.Q / kKT);
-    hipExtLaunchKernelGGL(chunk_scan_rows_kernel<T, P, N, HB>, dim3(nblocks), dim3(256), 0, s, a.ev0, a.ev1, 0,
+    // C B^T precomputed whenever chunk_state formed it (always for fp32)
+    auto kern = chunk_scan_rows_kernel<T, P, N, HB, true>;
+    if constexpr (sizeof(T) == 4) {
+      if (!a.cb) return hipErrorInvalidValue;
+    } else {
+      if (!a.cb) kern = chunk_scan_rows_kernel<T, P, N, HB, false>;
+    }
+    hipExtLaunchKernelGGL(kern, dim3(nblocks), dim3(256), 0, s, a.ev0, a.ev1, 0,
         static_cast<const T*>(a.x), static_cast<const T*>(a.Bm), a.cb, static_cast<const T*>(a.Cm), a.dtp, a.dAcs,
         prevT, a.D, static_cast<const T*>(a.z), static_cast<T*>(a.y), a.L, a.H, a.G, a.nc, a.Q, a.B,
         a.rows_group);

@@ -75,10 +75,11 @@ __device__ __forceinline__ void chunk_cumsum_wave(const T* __restrict__ dt, floa
   }
 }
 
-// Forward: workgroups [0, nblocks) compute the chunk states (each first the dt' cumsum of its
-// own (b, c, h)); fp32 launches add workgroups [nblocks, ...) that compute the C B^T blocks
-// the scan reads (cb_block), filling the tail of the grid.  Backward (from_start): dt' and the
-// cumsum are read from the workspace.
+// Forward: workgroups [ncb_wg, ncb_wg + nblocks) compute the chunk states (each first the dt'
+// cumsum of its own (b, c, h)); when the scan reads C B^T formed once per group (fp32, and bf16
+// with many heads per group), the first ncb_wg workgroups compute those blocks (cb_block):
+// dispatched ahead of the state workgroups, they overlap them instead of forming a tail behind
+// the last ones.  Backward (from_start): dt' and the cumsum are read from the workspace.
 template <typename T, int P, int N, int NTHR>
 __global__ __launch_bounds__(NTHR, sizeof(T) == 2 ? 6 : 1) void chunk_state_kernel(const T* __restrict__ x,
                                                           const T* __restrict__ Bm,
@@ -91,14 +92,13 @@ __global__ __launch_bounds__(NTHR, sizeof(T) == 2 ? 6 : 1) void chunk_state_kern
                                                           float* __restrict__ states,
                                                           float* __restrict__ cb,
                                                           int L, int H, int G, int nc, int Q,
-                                                          uint32_t nblocks, uint32_t ncb, int from_start, int clamp,
-                                                          float lo, float hi) {
-  if (blockIdx.x >= nblocks) {
-    // NTHR / 256 blocks per workgroup, four wavefronts each
-    const uint32_t id = (blockIdx.x - nblocks) * (NTHR / 256) + threadIdx.x / 256;
-    if constexpr (sizeof(T) == 4)
-      if (id < ncb) cb_block<N>(reinterpret_cast<const float*>(Bm), reinterpret_cast<const float*>(Cm), cb, L, G,
-                                nc, Q, id, threadIdx.x & 255);
+                                                          uint32_t nblocks, uint32_t ncb, uint32_t ncb_wg,
+                                                          int from_start, int clamp, float lo, float hi) {
+  if (blockIdx.x < ncb_wg) {
+    // the C B^T blocks first (dispatched with the first state workgroups rather than as a
+    // tail behind the last ones); NTHR / 256 blocks per workgroup, four wavefronts each
+    const uint32_t id = blockIdx.x * (NTHR / 256) + threadIdx.x / 256;
+    if (id < ncb) cb_block<T, N>(Bm, Cm, cb, L, G, nc, Q, id, threadIdx.x & 255);
     return;
   }
   constexpr bool F32 = sizeof(T) == 4;
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(NTHR, sizeof(T) == 2 ? 6 : 1) void chunk_state_kern
   __shared__ float s_w[256];
   __shared__ float s_d[256], s_cs[256];
 
-  uint32_t id = xcd_swizzle(blockIdx.x, nblocks);
+  uint32_t id = xcd_swizzle(blockIdx.x - ncb_wg, nblocks);   // ncb_wg % 8 == 0: XCDs unchanged
   const int h = id % H;
   id /= H;
   const int c = id % nc;
@@ -294,15 +294,15 @@ template <typename T, int P, int N>
 static hipError_t launch_state_impl(const FwdArgs& a, hipStream_t s) {
   const uint32_t nblocks = (uint32_t)a.B * a.nc * a.H;
   const int nrb = a.Q / kCbKT;
-  const uint32_t ncb = (sizeof(T) == 4 && a.cb && !a.state_from_start)
+  const uint32_t ncb = (a.cb && !a.state_from_start)
                            ? (uint32_t)a.B * a.nc * a.G * (nrb * (nrb + 1) / 2) : 0u;
   if (nblocks + ncb == 0) return hipSuccess;
   constexpr int NTHR = 512;
-  const uint32_t ncb_wg = (ncb + NTHR / 256 - 1) / (NTHR / 256);
+  const uint32_t ncb_wg = ((ncb + NTHR / 256 - 1) / (NTHR / 256) + 7) / 8 * 8;
   hipExtLaunchKernelGGL(chunk_state_kernel<T, P, N, NTHR>, dim3(nblocks + ncb_wg), dim3(NTHR), 0, s, a.ev0, a.ev1,
       0, static_cast<const T*>(a.x), static_cast<const T*>(a.Bm), static_cast<const T*>(a.Cm),
       static_cast<const T*>(a.dt), a.dt_bias, a.A, a.dtp, a.dAcs, a.states, a.cb, a.L, a.H, a.G, a.nc, a.Q,
-      nblocks, ncb, a.state_from_start, a.clamp, a.dt_lo, a.dt_hi);
+      nblocks, ncb, ncb_wg, a.state_from_start, a.clamp, a.dt_lo, a.dt_hi);
   return hipGetLastError();
 }
 

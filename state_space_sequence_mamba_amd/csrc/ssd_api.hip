@@ -48,9 +48,17 @@ size_t prev16_bytes(const ssd_dims_t* d, int Q) {
   return align_up((size_t)d->batch * nc * d->nheads * d->headdim * d->dstate * 2);
 }
 
-// fp32 only: the C B^T sub-tile blocks cb_block writes, (B, nc, G, nrb (nrb + 1) / 2) x 16 KB
+// C B^T formed once per group by chunk_state (cb_block) and read by every head's scan: always
+// for fp32; for bf16 when a group has at least 20 heads.  For bf16 the scan can also form it
+// itself from the bf16 rows, and the blocks (16 KB of fp32 per 64 x 64 block) cost chunk_state
+// more than they save the scan below that: measured on MI355X, 32 heads per group (B8 L4096
+// H32 N128) 0.341 -> 0.320 ms per forward, 10 heads per group (B2 L16384 H80 G8) 0.795 ->
+// 0.819 ms.
+bool cb_shared(const ssd_dims_t* d) { return d->dtype == SSD_F32 || d->nheads / d->ngroups >= 20; }
+
+// the C B^T sub-tile blocks cb_block writes, (B, nc, G, nrb (nrb + 1) / 2) x 16 KB (fp32)
 size_t cb_bytes(const ssd_dims_t* d, int Q) {
-  if (d->dtype != SSD_F32) return 0;
+  if (!cb_shared(d)) return 0;
   const int64_t nc = (d->seqlen + Q - 1) / Q, nrb = Q / 64;
   return align_up((size_t)d->batch * nc * d->ngroups * (nrb * (nrb + 1) / 2) * 16 * 256 * sizeof(float));
 }
@@ -190,7 +198,7 @@ ssd_status_t fwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   a.dtp = has_seq ? reinterpret_cast<float*>(ws + wl.dtp_off) : nullptr;
   a.dAcs = has_seq ? reinterpret_cast<float*>(ws + wl.dacs_off) : nullptr;
   a.states = has_seq ? reinterpret_cast<float*>(ws + wl.states_off) : nullptr;
-  a.cb = has_seq && dims->dtype == SSD_F32 ? reinterpret_cast<float*>(ws + wl.cb_off) : nullptr;
+  a.cb = has_seq && cb_shared(dims) ? reinterpret_cast<float*>(ws + wl.cb_off) : nullptr;
   a.prev16 = has_seq && dims->dtype == SSD_BF16 ? static_cast<void*>(ws + wl.prev16_off) : nullptr;
   a.keep_f32_states = 0;
   a.scan_variant = pick_scan_variant(a.dtype);
@@ -327,7 +335,7 @@ ssd_status_t bwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   f.dtp = reinterpret_cast<float*>(ws + wl.dtp);
   f.dAcs = reinterpret_cast<float*>(ws + wl.dacs);
   f.states = reinterpret_cast<float*>(ws + wl.states);
-  f.cb = z && dims->dtype == SSD_F32 ? reinterpret_cast<float*>(ws + wl.cb) : nullptr;   // only the gate needs y~
+  f.cb = z && cb_shared(dims) ? reinterpret_cast<float*>(ws + wl.cb) : nullptr;   // only the gate needs y~
   f.prev16 = z && dims->dtype == SSD_BF16 ? static_cast<void*>(ws + wl.prev16) : nullptr;
   f.keep_f32_states = 1;                              // the backward kernels read the fp32 states
   f.scan_variant = pick_scan_variant(f.dtype);

@@ -96,6 +96,18 @@ def test_bwd_gate_clamp_initial_state(dtype, gate, clamp, init):
     _compare(got, _oracle(inp, dout, dfin, init=h0, z=z, dt_limit=lim), TOL[dtype])
 
 
+def test_bwd_gate_with_shared_cb_blocks():
+    """bf16 with 20 heads per group and a gate: the backward's forward recompute forms C B^T
+    once per group for the pre-gate output."""
+    _say("bwd bf16 gate H=20 G=1")
+    Bt, L, H, P, N, G = 1, 200, 20, 32, 64, 1
+    inp = I.make_fwd_inputs(Bt, L, H, P, N, G, "bf16", seed=220, d_init="normal")
+    dout, dfin = _upstream(Bt, L, H, P, N, "bf16", seed=221)
+    z = I.make_gate((Bt, L, H, P), "bf16", seed=222)
+    got = _run(inp, 64, dout, dfin, z=z)
+    _compare(got, _oracle(inp, dout, dfin, z=z), TOL["bf16"])
+
+
 def test_bwd_no_D_no_upstream_state():
     _say("bwd D=None dfinal=None")
     inp = I.make_fwd_inputs(2, 200, 4, 32, 32, 1, "f32", seed=220)

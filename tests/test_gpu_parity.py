@@ -142,6 +142,32 @@ def test_run_to_run_bitwise_determinism(dtype):
     assert torch.equal(y1, y2) and torch.equal(f1, f2)
 
 
+@pytest.mark.parametrize("L,Q,G", [(700, 256, 1), (300, 128, 1), (130, 64, 2), (64, 256, 1)])
+def test_bf16_shared_cb_blocks_match_in_kernel_cb(L, Q, G):
+    """bf16 with at least 20 heads per group: the row blocks read C B^T formed once per group by
+    chunk_state; the whole-chunk decomposition forms it itself from the bf16 rows.  Same MFMA
+    sequence, so the results agree bit for bit (ragged last chunks, every chunk size, with a
+    gate), and both match the oracle."""
+    _say(f"bf16 shared C B^T L={L} Q={Q} G={G}")
+    H = 20 * G
+    inp = I.make_fwd_inputs(2, L, H, 64, 128, G, "bf16", seed=31 + L, d_init="normal")
+    z = I.make_gate(tuple(inp["x"].shape), "bf16", seed=32)
+    dev = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
+    try:
+        for gate in (None, z.to(DEV)):
+            outs = []
+            for variant in (1, 2):
+                ssd.tune_set(2, variant)
+                y, f = ssd.ssd_fwd(dev["x"], dev["dt"], dev["dt_bias"], dev["A"], dev["B"], dev["C"], dev["D"],
+                                   chunk_size=Q, z=gate)
+                torch.cuda.synchronize()
+                outs.append((y, f))
+            assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1]), gate is None
+    finally:
+        ssd.tune_set(2, 0)
+    _check_full(inp, Q, TOL["bf16"])
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_launch_shapes_do_not_change_results(dtype):
     """Both chunk_scan decompositions, every head-block size and every row-block dispatch
