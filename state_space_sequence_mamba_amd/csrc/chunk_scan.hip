@@ -30,9 +30,10 @@
 //           exactly once, but its registers allow one workgroup per CU.
 // Token tiles (64 tokens of B and of x for every head) are loaded into registers one tile
 // ahead of the MFMA work, then written to LDS.  y leaves through LDS as 16-byte row stores.
-// fp32 row blocks read C B^T precomputed once per group (cb_block, in the A-operand lane
-// order): each wavefront loads its own four sub-tiles of a column tile straight into
-// registers, one tile ahead, with no LDS copy.
+// Row blocks read C B^T precomputed once per group when chunk_state formed it (cb_block, in
+// the A-operand lane order; always for fp32, for bf16 with many heads per group): each
+// wavefront loads its own four sub-tiles of a column tile straight into registers, one tile
+// ahead, with no LDS copy; the B tile is then not staged at all.
 //
 // MFMA: fp32 inputs -> v_mfma_f32_16x16x4_f32 for all three products; bf16 inputs ->
 // 16x16x32 bf16 for C B^T and C Hprev^T, 16x16x16 bf16 for (L o CB) X.  Decay factors use
