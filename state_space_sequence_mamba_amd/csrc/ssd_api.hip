@@ -262,7 +262,7 @@ BwdLayout bwd_layout(const ssd_dims_t* d, int Q, bool gate) {
   w.pD = o; o += pd;
   w.ypre = o; o += act;
   w.dyg = o; o += act;
-  w.cb = o; o += gate ? cb_bytes(d, Q) : 0;
+  w.cb = o; o += (gate || d->dtype == SSD_F32) ? cb_bytes(d, Q) : 0;
   w.prev16 = o; o += gate ? prev16_bytes(d, Q) : 0;
   w.total = o;
   return w;
@@ -335,7 +335,10 @@ ssd_status_t bwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   f.dtp = reinterpret_cast<float*>(ws + wl.dtp);
   f.dAcs = reinterpret_cast<float*>(ws + wl.dacs);
   f.states = reinterpret_cast<float*>(ws + wl.states);
-  f.cb = z && cb_shared(dims) ? reinterpret_cast<float*>(ws + wl.cb) : nullptr;   // only the gate needs y~
+  // C B^T once per group (when shared): read by the scan for the pre-gate output and, for fp32,
+  // by bwd_dc (fp32 B4 L1024 H24: bwd_dc 86.5 -> 69.1 us; for bf16 forming C B^T from the bf16
+  // rows in bwd_dc measured as fast as reading the blocks, which then only cost chunk_state)
+  f.cb = cb_shared(dims) && (z || dims->dtype == SSD_F32) ? reinterpret_cast<float*>(ws + wl.cb) : nullptr;
   f.prev16 = z && dims->dtype == SSD_BF16 ? static_cast<void*>(ws + wl.prev16) : nullptr;
   f.keep_f32_states = 1;                              // the backward kernels read the fp32 states
   f.scan_variant = pick_scan_variant(f.dtype);
@@ -386,8 +389,8 @@ ssd_status_t bwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
     if (ssd::launch_bwd_reduce(a, stream) != hipSuccess) return SSD_ERR_HIP;   // zero dA, d dt_bias, dD
     return SSD_OK;
   }
-  // forward intermediates: dt', its cumsum, the states entering each chunk (and, with a gate
-  // in fp32, the C B^T blocks of the pre-gate output)
+  // forward intermediates: dt', its cumsum, the states entering each chunk, and (when shared)
+  // the C B^T blocks
   timing(f, 0);
   if (ssd::launch_chunk_state(f, stream) != hipSuccess) return SSD_ERR_HIP;
   timing(f, 1);

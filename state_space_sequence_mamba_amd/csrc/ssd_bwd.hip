@@ -20,7 +20,8 @@
 //
 // Kernels here, each one workgroup of 256 threads:
 //   bwd_dxdb   per (b, c, 64-row block R, h): the anti-causal sums over row blocks I >= R
-//   bwd_dc     per (b, c, R, h): the causal sums over row blocks J <= R
+//   bwd_dc     per (b, c, R, h): the causal sums over row blocks J <= R (fp32: C B^T read from
+//              the blocks the forward recompute formed once per group)
 //   bwd_finalize per (b, c, h): dS, its reverse cumsum, d(dt), and the dA / d dt_bias partials
 //   bwd_reduce_*: per-head dB, dC summed over the heads of each group; parameter partials
 //                 summed in a fixed order (results are run-to-run deterministic)
@@ -31,6 +32,7 @@
 // space of the token tiles once those are consumed.
 #include <type_traits>
 
+#include "cb_tiles.h"
 #include "ssd_common.h"
 #include "ssd_launch.h"
 
@@ -424,11 +426,12 @@ __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, 
 // transposed tiles (j, i) of B C^T and x dy^T for every j of block J, so that the weighted
 // tile feeds dC[i][:] directly as an MFMA A operand.  The tiles of block J + 1 are loaded
 // into registers while block J is computed.
-template <typename T, int P, int N>
+template <typename T, int P, int N, bool PRECB>
 __global__ __launch_bounds__(256) void bwd_dc_kernel(const T* __restrict__ x, const T* __restrict__ Bm,
                                                      const T* __restrict__ Cm, const T* __restrict__ dy,
                                                      const float* __restrict__ dtp, const float* __restrict__ dAcs,
-                                                     const float* __restrict__ states, float* __restrict__ dCh,
+                                                     const float* __restrict__ states,
+                                                     const float* __restrict__ cbp, float* __restrict__ dCh,
                                                      float* __restrict__ dSc, int L, int H, int G, int nc, int Q,
                                                      uint32_t nblocks) {
   constexpr int PP = Pitch<T, P>::v, NP = Pitch<T, N>::v, TNm = N / 16;
@@ -472,6 +475,16 @@ __global__ __launch_bounds__(256) void bwd_dc_kernel(const T* __restrict__ x, co
   tx.load(xg, xs, len0, tid);
   const float sR = dAcs[cq + R * KT + tk];
   float sJ = dAcs[cq + tk], dJ = dtp[cq + tk];
+  // PRECB: the C B^T sub-tiles (own strip w, column tiles of block J) come from the blocks the
+  // forward recompute formed once per group (cb_block: the same MFMA sequence as mm_rows here,
+  // so the same values), one 16-byte load per lane and sub-tile
+  const float* cb_lane = cbp + ((((size_t)b * nc + c) * G + g) * (size_t)(nrb * (nrb + 1) / 2) +
+                                (size_t)(R * (R + 1) / 2)) * kCbBlock + ((size_t)(w * 4) * 64 + lane) * 4;
+  f32x4 cbr[4] = {};
+  if constexpr (PRECB) {
+#pragma unroll
+    for (int tj = 0; tj < 4; ++tj) cbr[tj] = *reinterpret_cast<const f32x4*>(cb_lane + 256 * tj);
+  }
   tc.store(s_c, tid);
   tdy.store(s_dy, tid);
   if (tid < KT) s_SR[tid] = sR;
@@ -505,7 +518,14 @@ __global__ __launch_bounds__(256) void bwd_dc_kernel(const T* __restrict__ x, co
 #pragma unroll
       for (int tj = 0; tj < 4; ++tj) {
         if (MASK && J == R && tj > w) continue;    // tile entirely after the diagonal (j > i)
-        const f32x4 cbt = mm_rows<N, NP, NP>(zero4(), s_b + 16 * tj * NP, s_c + 16 * w * NP, r, qd);
+        f32x4 cbt;
+        if constexpr (PRECB) {
+          cbt = cbr[tj];
+          // block J + 1's sub-tile into the register this one releases
+          if (J < R) cbr[tj] = *reinterpret_cast<const f32x4*>(cb_lane + (size_t)(J + 1) * kCbBlock + 256 * tj);
+        } else {
+          cbt = mm_rows<N, NP, NP>(zero4(), s_b + 16 * tj * NP, s_c + 16 * w * NP, r, qd);
+        }
         const f32x4 dxt = mm_rows<P, PP, PP>(zero4(), s_x + 16 * tj * PP, s_dy + 16 * w * PP, r, qd);
         f32x4 wt;
 #pragma unroll
@@ -778,9 +798,14 @@ template <typename T, int P, int N>
 static hipError_t launch_dc_impl(const BwdArgs& a, hipStream_t s) {
   const FwdArgs& f = a.f;
   const uint32_t nblocks = (uint32_t)f.B * f.nc * (f.Q / KT) * f.H;
-  hipExtLaunchKernelGGL(bwd_dc_kernel<T, P, N>, dim3(nblocks), dim3(256), 0, s, f.ev0, f.ev1, 0,
+  auto kern = bwd_dc_kernel<T, P, N, false>;
+  if constexpr (sizeof(T) == 4)
+    if (f.cb) kern = bwd_dc_kernel<T, P, N, true>;     // fp32: C B^T read from the shared blocks
+  hipExtLaunchKernelGGL(kern, dim3(nblocks),
+      dim3(256), 0, s, f.ev0, f.ev1, 0,
       static_cast<const T*>(f.x), static_cast<const T*>(f.Bm), static_cast<const T*>(f.Cm),
-      static_cast<const T*>(a.dy), f.dtp, f.dAcs, f.states, a.dCh, a.dSc, f.L, f.H, f.G, f.nc, f.Q, nblocks);
+      static_cast<const T*>(a.dy), f.dtp, f.dAcs, f.states, f.cb, a.dCh, a.dSc, f.L, f.H, f.G, f.nc, f.Q,
+      nblocks);
   return hipGetLastError();
 }
 
