@@ -62,7 +62,11 @@ template <int N> struct NDot<__bf16, N> {
 // sequence is the scan's own, so results are bit-identical to computing in place.  Sub-tiles
 // past the diagonal and rows past the sequence are zeros.  Four wavefronts (tid in [0, 256)),
 // one per strip.
-template <typename T, int N>
+// TRANS: the layout the backward's anti-causal kernel (bwd_dxdb) consumes: lane (r, qd) of
+// sub-tile (w, js) holds CB[i = 16 (4 rb + w) + 4 qd + e][j = 16 (4 J + js) + r] (the MFMA with
+// C as its A operand, as bwd_dxdb forms it), stored at ((4 js + w) 64 + l) 4 + e so that the
+// wavefront owning column tile js reads its four row tiles contiguously.
+template <typename T, int N, bool TRANS = false>
 __device__ __forceinline__ void cb_block(const T* __restrict__ Bm, const T* __restrict__ Cm,
                                          float* __restrict__ cb, int L, int G, int nc, int Q, uint32_t id,
                                          int tid) {
@@ -100,8 +104,13 @@ __device__ __forceinline__ void cb_block(const T* __restrict__ Bm, const T* __re
 #pragma unroll
     for (int u = 0; u < JB; ++u) {
       const int js = j0 + u;
-      const f32x4 cbt = (4 * J + js <= strip) ? ND::dot(bfr[u], cf, zero4()) : zero4();
-      *reinterpret_cast<f32x4*>(out + ((w * 4 + js) * 64 + lane) * 4) = cbt;
+      if constexpr (TRANS) {
+        const f32x4 cbt = (4 * J + js <= strip) ? ND::dot(cf, bfr[u], zero4()) : zero4();
+        *reinterpret_cast<f32x4*>(out + ((js * 4 + w) * 64 + lane) * 4) = cbt;
+      } else {
+        const f32x4 cbt = (4 * J + js <= strip) ? ND::dot(bfr[u], cf, zero4()) : zero4();
+        *reinterpret_cast<f32x4*>(out + ((w * 4 + js) * 64 + lane) * 4) = cbt;
+      }
     }
   }
 }

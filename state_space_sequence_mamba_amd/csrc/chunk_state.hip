@@ -90,7 +90,7 @@ __global__ __launch_bounds__(NTHR, sizeof(T) == 2 ? 6 : 1) void chunk_state_kern
                                                           float* __restrict__ dtp,
                                                           float* __restrict__ dAcs,
                                                           float* __restrict__ states,
-                                                          float* __restrict__ cb,
+                                                          float* __restrict__ cb, float* __restrict__ cbT,
                                                           int L, int H, int G, int nc, int Q,
                                                           uint32_t nblocks, uint32_t ncb, uint32_t ncb_wg,
                                                           int from_start, int clamp, float lo, float hi) {
@@ -98,7 +98,10 @@ __global__ __launch_bounds__(NTHR, sizeof(T) == 2 ? 6 : 1) void chunk_state_kern
     // the C B^T blocks first (dispatched with the first state workgroups rather than as a
     // tail behind the last ones); NTHR / 256 blocks per workgroup, four wavefronts each
     const uint32_t id = blockIdx.x * (NTHR / 256) + threadIdx.x / 256;
-    if (id < ncb) cb_block<T, N>(Bm, Cm, cb, L, G, nc, Q, id, threadIdx.x & 255);
+    if (id < ncb)
+      cb_block<T, N>(Bm, Cm, cb, L, G, nc, Q, id, threadIdx.x & 255);
+    else if (cbT && id < 2 * ncb)       // the backward's transposed copy
+      cb_block<T, N, true>(Bm, Cm, cbT, L, G, nc, Q, id - ncb, threadIdx.x & 255);
     return;
   }
   constexpr bool F32 = sizeof(T) == 4;
@@ -298,10 +301,11 @@ static hipError_t launch_state_impl(const FwdArgs& a, hipStream_t s) {
                            ? (uint32_t)a.B * a.nc * a.G * (nrb * (nrb + 1) / 2) : 0u;
   if (nblocks + ncb == 0) return hipSuccess;
   constexpr int NTHR = 512;
-  const uint32_t ncb_wg = ((ncb + NTHR / 256 - 1) / (NTHR / 256) + 7) / 8 * 8;
+  const uint32_t ncb_all = a.cbT && ncb ? 2 * ncb : ncb;
+  const uint32_t ncb_wg = ((ncb_all + NTHR / 256 - 1) / (NTHR / 256) + 7) / 8 * 8;
   hipExtLaunchKernelGGL(chunk_state_kernel<T, P, N, NTHR>, dim3(nblocks + ncb_wg), dim3(NTHR), 0, s, a.ev0, a.ev1,
       0, static_cast<const T*>(a.x), static_cast<const T*>(a.Bm), static_cast<const T*>(a.Cm),
-      static_cast<const T*>(a.dt), a.dt_bias, a.A, a.dtp, a.dAcs, a.states, a.cb, a.L, a.H, a.G, a.nc, a.Q,
+      static_cast<const T*>(a.dt), a.dt_bias, a.A, a.dtp, a.dAcs, a.states, a.cb, a.cbT, a.L, a.H, a.G, a.nc, a.Q,
       nblocks, ncb, ncb_wg, a.state_from_start, a.clamp, a.dt_lo, a.dt_hi);
   return hipGetLastError();
 }

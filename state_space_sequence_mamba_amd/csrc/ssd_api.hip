@@ -199,6 +199,7 @@ ssd_status_t fwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   a.dAcs = has_seq ? reinterpret_cast<float*>(ws + wl.dacs_off) : nullptr;
   a.states = has_seq ? reinterpret_cast<float*>(ws + wl.states_off) : nullptr;
   a.cb = has_seq && cb_shared(dims) ? reinterpret_cast<float*>(ws + wl.cb_off) : nullptr;
+  a.cbT = nullptr;
   a.prev16 = has_seq && dims->dtype == SSD_BF16 ? static_cast<void*>(ws + wl.prev16_off) : nullptr;
   a.keep_f32_states = 0;
   a.scan_variant = pick_scan_variant(a.dtype);
@@ -234,7 +235,7 @@ ssd_status_t fwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
 // Backward workspace: the forward's regions, the state gradients, per-head dB / dC, per-token
 // and per-chunk partials, and (with a gate) the pre-gate output and the gated gradient.
 struct BwdLayout {
-  size_t dtp, dacs, states, gstates, dBh, dCh, ddir, dSa, dSc, Ub, pA, pbias, pD, ypre, dyg, cb, prev16, total;
+  size_t dtp, dacs, states, gstates, dBh, dCh, ddir, dSa, dSc, Ub, pA, pbias, pD, ypre, dyg, cb, cbT, prev16, total;
 };
 
 BwdLayout bwd_layout(const ssd_dims_t* d, int Q, bool gate) {
@@ -263,6 +264,7 @@ BwdLayout bwd_layout(const ssd_dims_t* d, int Q, bool gate) {
   w.ypre = o; o += act;
   w.dyg = o; o += act;
   w.cb = o; o += (gate || d->dtype == SSD_F32) ? cb_bytes(d, Q) : 0;
+  w.cbT = o; o += d->dtype == SSD_F32 ? cb_bytes(d, Q) : 0;
   w.prev16 = o; o += gate ? prev16_bytes(d, Q) : 0;
   w.total = o;
   return w;
@@ -339,6 +341,8 @@ ssd_status_t bwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   // by bwd_dc (fp32 B4 L1024 H24: bwd_dc 86.5 -> 69.1 us; for bf16 forming C B^T from the bf16
   // rows in bwd_dc measured as fast as reading the blocks, which then only cost chunk_state)
   f.cb = cb_shared(dims) && (z || dims->dtype == SSD_F32) ? reinterpret_cast<float*>(ws + wl.cb) : nullptr;
+  // fp32: the same blocks transposed for bwd_dxdb
+  f.cbT = dims->dtype == SSD_F32 ? reinterpret_cast<float*>(ws + wl.cbT) : nullptr;
   f.prev16 = z && dims->dtype == SSD_BF16 ? static_cast<void*>(ws + wl.prev16) : nullptr;
   f.keep_f32_states = 1;                              // the backward kernels read the fp32 states
   f.scan_variant = pick_scan_variant(f.dtype);

@@ -20,6 +20,7 @@
 //
 // Kernels here, each one workgroup of 256 threads:
 //   bwd_dxdb   per (b, c, 64-row block R, h): the anti-causal sums over row blocks I >= R
+//              (fp32: C B^T read from transposed blocks the forward recompute formed)
 //   bwd_dc     per (b, c, R, h): the causal sums over row blocks J <= R (fp32: C B^T read from
 //              the blocks the forward recompute formed once per group)
 //   bwd_finalize per (b, c, h): dS, its reverse cumsum, d(dt), and the dA / d dt_bias partials
@@ -212,11 +213,12 @@ __device__ __forceinline__ float sum_qd(float v) {
 // (i, j) tiles of C B^T and dy x^T for every i of the block I, weights them in registers,
 // and feeds them straight into xi[j][:] and dB[j][:] as MFMA A operands.  The tiles of block
 // I + 1 are loaded into registers while block I is computed.
-template <typename T, int P, int N>
+template <typename T, int P, int N, bool PRECB>
 __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, const T* __restrict__ Bm,
                                                        const T* __restrict__ Cm, const T* __restrict__ dy,
                                                        const float* __restrict__ dtp, const float* __restrict__ dAcs,
                                                        const float* __restrict__ gstates,
+                                                       const float* __restrict__ cbT,
                                                        const float* __restrict__ Dw, T* __restrict__ dx,
                                                        float* __restrict__ dBh, float* __restrict__ ddir,
                                                        float* __restrict__ dSa, float* __restrict__ Ub,
@@ -284,6 +286,19 @@ __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, 
   const int jl = 16 * w + r;                       // this lane's column of R
 
   const int nI = (len + KT - 1) / KT;
+  // PRECB: the C B^T sub-tiles (row tiles of block I, own column tile w of R) come from the
+  // transposed blocks the forward recompute formed once per group (cb_block TRANS: the same
+  // MFMA sequence as mm_rows here, so the same values), one 16-byte load per lane and sub-tile
+  const float* cb_grp = cbT + (((size_t)b * nc + c) * G + g) * (size_t)(nrb * (nrb + 1) / 2) * kCbBlock +
+                        ((size_t)(w * 4) * 64 + lane) * 4;
+  auto cb_at = [&](int I, int ti) {
+    return *reinterpret_cast<const f32x4*>(cb_grp + (size_t)(I * (I + 1) / 2 + R) * kCbBlock + 256 * ti);
+  };
+  f32x4 cbr[4] = {};
+  if constexpr (PRECB) {
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) cbr[ti] = cb_at(R, ti);
+  }
   for (int I = R; I < nI; ++I) {
     const int lenI = min(KT, len - I * KT);
     __syncthreads();
@@ -304,8 +319,13 @@ __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, 
       constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
       for (int ti = 0; ti < 4; ++ti) {
+        f32x4 cb;
+        if constexpr (PRECB) {
+          cb = cbr[ti];
+          if (I + 1 < nI) cbr[ti] = cb_at(I + 1, ti);  // block I + 1's, into the released register
+        }
         if (MASK && I == R && ti < w) continue;    // tile entirely above the diagonal (i < j)
-        f32x4 cb = mm_rows<N, NP, NP>(zero4(), s_c + 16 * ti * NP, s_b + 16 * w * NP, r, qd);
+        if constexpr (!PRECB) cb = mm_rows<N, NP, NP>(zero4(), s_c + 16 * ti * NP, s_b + 16 * w * NP, r, qd);
         f32x4 dxv = mm_rows<P, PP, PP>(zero4(), s_dy + 16 * ti * PP, s_x + 16 * w * PP, r, qd);
         f32x4 m1, m2;
 #pragma unroll
@@ -787,10 +807,13 @@ template <typename T, int P, int N>
 static hipError_t launch_dxdb_impl(const BwdArgs& a, hipStream_t s) {
   const FwdArgs& f = a.f;
   const uint32_t nblocks = (uint32_t)f.B * f.nc * (f.Q / KT) * f.H;
-  hipExtLaunchKernelGGL(bwd_dxdb_kernel<T, P, N>, dim3(nblocks), dim3(256), 0, s, f.ev0, f.ev1, 0,
+  auto kern = bwd_dxdb_kernel<T, P, N, false>;
+  if constexpr (sizeof(T) == 4)
+    if (f.cbT) kern = bwd_dxdb_kernel<T, P, N, true>;  // fp32: C B^T read from the transposed blocks
+  hipExtLaunchKernelGGL(kern, dim3(nblocks), dim3(256), 0, s, f.ev0, f.ev1, 0,
       static_cast<const T*>(f.x), static_cast<const T*>(f.Bm), static_cast<const T*>(f.Cm),
-      static_cast<const T*>(a.dy), f.dtp, f.dAcs, a.gstates, f.D, static_cast<T*>(a.dx), a.dBh, a.ddir, a.dSa, a.Ub,
-      a.pD, f.L, f.H, f.G, f.nc, f.Q, nblocks);
+      static_cast<const T*>(a.dy), f.dtp, f.dAcs, a.gstates, f.cbT, f.D, static_cast<T*>(a.dx), a.dBh, a.ddir,
+      a.dSa, a.Ub, a.pD, f.L, f.H, f.G, f.nc, f.Q, nblocks);
   return hipGetLastError();
 }
 

@@ -33,8 +33,10 @@ struct FwdArgs {
   void* prev16;            // bf16 only: the states entering each chunk rounded to bf16, (B, nc, H, P, N),
                            // written by state_passing and read by chunk_scan; null: fp32 states
   int keep_f32_states;     // with prev16: also keep the fp32 states entering each chunk (backward)
-  float* cb;               // workspace, fp32 only: C B^T sub-tiles per (b, c, g), see cb_block;
-                           // null: chunk_state does not compute them
+  float* cb;               // workspace: C B^T sub-tiles per (b, c, g), see cb_block (fp32, and
+                           // bf16 with many heads per group); null: chunk_state does not form them
+  float* cbT;              // backward (fp32): the same blocks in bwd_dxdb's layout (cb_block TRANS);
+                           // null: not formed
   int heads_per_block;     // chunk_scan: heads sharing one C B^T evaluation (divides H / G)
   int scan_variant;        // chunk_scan decomposition: 1 = 64-row blocks, 2 = whole chunks
   int rows_group;          // row blocks: units per dispatch group on an XCD (0: all of one class first)

@@ -159,8 +159,9 @@ def test_step_host_validation(lib):
 def test_bwd_workspace_size_and_validation(lib):
     # 1 x 256 tokens, H=4, P=N=16, Q=64: cum regions 4096 B, states 16384 B, per-head dB/dC
     # 256*4*16*4 = 65536 B, per-chunk partials 64 -> 256 B, dD partials 4*4*16*4 = 1024 B, and
-    # (fp32) the C B^T blocks of the recomputed forward (4 chunks * 16 KB), which bwd_dc reads
-    base = 2 * 4096 + 2 * 16384 + 2 * 65536 + 4 * 4096 + 2 * 256 + 1024 + 65536
+    # (fp32) the C B^T blocks of the recomputed forward (4 chunks * 16 KB), which bwd_dc reads,
+    # and their transposed copy for bwd_dxdb
+    base = 2 * 4096 + 2 * 16384 + 2 * 65536 + 4 * 4096 + 2 * 256 + 1024 + 2 * 65536
     assert ssd.ssd_bwd_workspace_size(_dims(), 64, 0) == base
     # the gate adds the pre-gate output and the gated gradient (2 * 256 * 4 * 16 * 4 B)
     assert ssd.ssd_bwd_workspace_size(_dims(), 64, 1) == base + 2 * 65536
