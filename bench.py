@@ -146,12 +146,13 @@ def run_decode(w, args, dev):
         "data": "synthetic (seeded N(0,1) state/x/B/C/dt per step)",
         "config": {"workload": w.name, "batch": B, "nheads": H, "headdim": P, "dstate": N, "ngroups": G},
         "roofline": {"kernel": "ssd_step", "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic(workload_slug(w.name), "ssd_step"),
                      "alg_bytes_per_launch": alg_bytes},
         "wall_s_timed_region": round(wall, 4),
     }
     hev.close()
-    print(json.dumps(out), flush=True)
+    emit(args, dev, out)
 
 
 BWD_STAGES = ["chunk_state", "state_passing", "gate_fwd", "gate_bwd", "chunk_state_grad",
