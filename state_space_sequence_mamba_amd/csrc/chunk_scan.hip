@@ -51,10 +51,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 template <int P> struct TPof { static constexpr int v = P / 16; };
 
-// Split decay below the diagonal (one exponential per lane and sub-tile) for bf16, where the
-// exponentials weigh against short MFMAs; fp32 keeps one per element (the split's extra
-// registers would spill there, and its sub-tiles are MFMA-bound).
-template <typename T> constexpr bool kSplitDecay = sizeof(T) == 2;
 
 template <typename T, int P, int N, int HB, int ROWS, bool NOB = false>
 struct ScanLds {
@@ -214,10 +210,9 @@ __device__ __forceinline__ void sub_tile(f32x4 (&acc)[HB][TPof<P>::v], const typ
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) {
     float lw[4];
-    if (diag || !kSplitDecay<T>) {
-      // the diagonal sub-tile (and every sub-tile for fp32): the decay of each (i, j) on its
-      // own, then the causal mask on the diagonal (a select, so an overflowed factor above the
-      // diagonal is dropped)
+    if (diag) {
+      // the diagonal sub-tile: the decay of each (i, j) on its own, then the causal mask (a
+      // select, so an overflowed factor above the diagonal is dropped)
       const float da_i = s_da[hh][i_row];
       const float4 daj = *reinterpret_cast<const float4*>(&s_da[hh][j0]);
       const float4 dtj = *reinterpret_cast<const float4*>(&s_dt[hh][j0]);
@@ -369,7 +364,6 @@ __device__ __forceinline__ void flush_rows(T* y, const T* s_y, size_t row0, size
 template <typename T, int HB, int NTHR>
 __device__ __forceinline__ void column_weights(float (*s_w)[256], const float (*s_da)[256],
                                                const float (*s_dt)[256], int tid) {
-  if constexpr (!kSplitDecay<T>) return;
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh)
     for (int i = tid; i < 256; i += NTHR)
@@ -451,7 +445,7 @@ __global__ __launch_bounds__(256, HB == 1 ? (sizeof(T) == 2 && PRECB && N >= 128
   __shared__ __attribute__((aligned(16))) T s_mem[SL::TOTAL];
   __shared__ __attribute__((aligned(16))) float s_da[HB][256];     // dAcs * log2(e)
   __shared__ __attribute__((aligned(16))) float s_dt[HB][256];
-  __shared__ __attribute__((aligned(16))) float s_w[kSplitDecay<T> ? HB : 1][256];   // column weights (bf16)
+  __shared__ __attribute__((aligned(16))) float s_w[HB][256];     // column weights
   T* s_b = s_mem;
   T* s_xu = s_mem + SL::B_ELEMS;                                   // Hprev, then x^T tiles
   T* s_y = s_mem;                                                  // y staging, at the end
@@ -594,7 +588,7 @@ __global__ __launch_bounds__(512) void chunk_scan_chunk_kernel(const T* __restri
   __shared__ __attribute__((aligned(16))) T s_mem[SL::TOTAL];
   __shared__ __attribute__((aligned(16))) float s_da[HB][256];
   __shared__ __attribute__((aligned(16))) float s_dt[HB][256];
-  __shared__ __attribute__((aligned(16))) float s_w[kSplitDecay<T> ? HB : 1][256];
+  __shared__ __attribute__((aligned(16))) float s_w[HB][256];
   T* s_b = s_mem;
   T* s_xu = s_mem + SL::B_ELEMS;
   T* s_y = s_mem;
