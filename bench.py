@@ -2,7 +2,9 @@
 
 One step = one pass of the whole path over one batch: ssd_fwd over the prefill batch
 (chunk_state with the dt' cumsum and, for fp32, C B^T once per group -> state_passing ->
-chunk_scan), writing final_state, then one ssd_step decode token per sequence continuing
+chunk_scan; for large bf16 batches chunk_state_seq, one pass over the chunks with the state
+carried in registers, in place of the first two), writing final_state, then one ssd_step
+decode token per sequence continuing
 from that state.  Other workloads (--workload): the backward (ssd_bwd), the decode loop and
 the conv1d + SiLU in front of the scan.  Workload: the fp32
 forward of batch 4 x 1024 tokens, 24 heads, headdim 64, dstate 64, 1 group, chunk 256
@@ -56,6 +58,11 @@ def algorithmic_cost(w):
         # (C in, 16 KB blocks out, one per row block and causal column block)
         "chunk_state": dict(bytes=B * L * H * e + 8 * H + cum + x + bc + st + ((bc + cbw) if pre else 0),
                             flops=2 * B * H * L * P * N + (2 * B * G * N * tri if pre else 0)),
+        # one pass over the chunks: dt in, dt' and its cumsum out, x and B once, the entering
+        # states out once (bf16: rounded to bf16) and the final state; fp32 adds C B^T as above
+        "chunk_state_seq": dict(bytes=B * L * H * e + 8 * H + cum + x + bc + (st if pre else st // 2) + fin
+                                + ((bc + cbw) if pre else 0),
+                                flops=2 * B * H * L * P * N + (2 * B * G * N * tri if pre else 0)),
         # bf16 writes the entering states once, rounded to bf16, for the scan
         "state_passing": dict(bytes=st + (st // 2 if not pre else st) + fin + B * H * nc * 4,
                               flops=2 * B * nc * H * P * N),
@@ -68,7 +75,7 @@ def algorithmic_cost(w):
     }
     for k, v in cost.items():
         peak_f = MFMA_PEAK_TFLOPS[w.dtype] * 1e12
-        t_f = v["flops"] / peak_f if k in ("chunk_state", "chunk_scan") else 0.0
+        t_f = v["flops"] / peak_f if k in ("chunk_state", "chunk_state_seq", "chunk_scan") else 0.0
         t_b = v["bytes"] / (HBM_PEAK_GBS * 1e9)
         v["bound"] = "mfma" if t_f > t_b else "hbm"
     return cost
@@ -447,6 +454,11 @@ def main():
                     help="chunk_scan decomposition: 1 = 64-row blocks, 2 = whole chunks, 0 = built-in")
     ap.add_argument("--rows-group", type=int, default=0,
                     help="chunk_scan row blocks: units per dispatch group on an XCD (0 = built-in, 16)")
+    ap.add_argument("--state-path", type=int, default=0,
+                    help="chunk states: 1 = chunk_state + state_passing, 2 = one pass over the chunks, "
+                         "0 = built-in")
+    ap.add_argument("--state-slice", type=int, default=0,
+                    help="one-pass chunk states: headdim rows per workgroup (0 = built-in)")
     ap.add_argument("--conv-tokens", type=int, default=0,
                     help="conv1d_silu tokens per thread, a multiple of 4 (0 = built-in)")
     args = ap.parse_args()
@@ -454,7 +466,7 @@ def main():
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               f"(see the sharding design for more GPUs)", file=sys.stderr)
         sys.exit(2)
-    w = I.WORKLOADS[args.workload]
+    w = I.workload(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if w.entry == "step":
@@ -474,6 +486,10 @@ def main():
         ssd.tune_set(2, args.scan_variant)
     if args.rows_group:
         ssd.tune_set(4, args.rows_group)
+    if args.state_path:
+        ssd.tune_set(5, args.state_path)
+    if args.state_slice:
+        ssd.tune_set(6, args.state_slice)
 
     inp = I.make_workload_inputs(w)
     dec = I.make_step_inputs(w.batch, w.nheads, w.headdim, w.dstate, w.ngroups, 1, w.dtype,
@@ -543,15 +559,19 @@ def main():
         step(W + i, events[i])
     torch.cuda.synchronize()
 
-    per_kernel_ms = {k: 0.0 for k in KERNELS}
+    # the one-pass chunk-state path launches no state_passing (its event pair brackets nothing)
+    one_pass = ssd.fwd_state_path(dims, w.chunk) == 2
+    names = ["chunk_state_seq", None, "chunk_scan", "ssd_step"] if one_pass else KERNELS
+    per_kernel_ms = {k: 0.0 for k in names if k}
     pairs = [(0, 1), (2, 3), (4, 5), (6, 7)]
     for evs in events[:K]:
-        for k, (a, b) in zip(KERNELS, pairs):
-            per_kernel_ms[k] += hev.elapsed_ms(evs[a], evs[b]) / K
+        for k, (a, b) in zip(names, pairs):
+            if k:
+                per_kernel_ms[k] += hev.elapsed_ms(evs[a], evs[b]) / K
 
     cost = algorithmic_cost(w)
     kernels = {}
-    for k in KERNELS:
+    for k in per_kernel_ms:
         t = per_kernel_ms[k] * 1e-3
         c = cost[k]
         if c["bytes"] == 0 and c["flops"] == 0:       # not launched for this dtype

@@ -76,10 +76,14 @@ typedef struct {
  *   [1] dAcs (B, H, nc, chunk_size) fp32   inclusive in-chunk cumulative sum of dt' * A
  *   [2] states (B, nc, H, P, N) fp32       first the state each chunk contributes (decayed to
  *                                          the chunk end), then overwritten in place by the
- *                                          state entering each chunk
- *   [3] SSD_F32 only: C B^T, computed once per group, (B, nc, G, nrb (nrb + 1) / 2) blocks of
- *       16 x 256 fp32, nrb = chunk_size / 64: the causal 16 x 16 sub-tiles of each pair of
- *       64-row blocks (row block rb, column block J <= rb), in the scan's register order
+ *                                          state entering each chunk; on the one-pass path
+ *                                          (ssd_tuning.h, ssd_fwd_state_path) fp32 inputs get
+ *                                          the entering states only and bf16 inputs leave it
+ *                                          unwritten
+ *   [3] SSD_F32, and SSD_BF16 with at least 20 heads per group: C B^T, computed once per
+ *       group, (B, nc, G, nrb (nrb + 1) / 2) blocks of 16 x 256 fp32, nrb = chunk_size / 64:
+ *       the causal 16 x 16 sub-tiles of each pair of 64-row blocks (row block rb, column
+ *       block J <= rb), in the scan's register order; 0 bytes otherwise
  *   [4] SSD_BF16 only: the states entering each chunk rounded to bf16, (B, nc, H, P, N); for
  *       bf16 inputs region [2] keeps the per-chunk contributions (state_passing writes the
  *       entering states here instead)
@@ -89,8 +93,10 @@ size_t ssd_fwd_workspace_size(const ssd_dims_t* dims, int chunk_size);
 /* Chunked SSD forward over a whole sequence (the chunked diagonal-block / carried-state
  * evaluation of the reference-comparison page, section 3.2, and of Gap 1 of the
  * implementation-gaps page).  Three kernels run in order on `stream`: chunk_state (dt', its
- * in-chunk cumsum and the chunk states; for SSD_F32 also C B^T once per group),
- * state_passing, chunk_scan.
+ * in-chunk cumsum and the chunk states; where region [3] exists also C B^T once per group),
+ * state_passing, chunk_scan.  For SSD_BF16 with P = 64, N = 128 and batch x nheads >= 256 the
+ * first two are one kernel instead (chunk_state_seq: one pass over the chunks per (b, h) with
+ * the carried state in registers); ssd_fwd_state_path in ssd_tuning.h tells which.
  *   x             (B, L, H, P)  dtype       input sequence
  *   dt            (B, L, H)     dtype       raw step, before bias and softplus
  *   dt_bias, A    (H)           fp32        A is used as given (pass negative values)
@@ -113,7 +119,9 @@ ssd_status_t ssd_fwd(const ssd_dims_t* dims,
  * an array of 6 events created by the caller (hipEventCreate): stage_events[2k] and
  * [2k + 1] are the start and stop of kernel k (0 chunk_state, 1 state_passing, 2 chunk_scan),
  * recorded by the kernel's own dispatch (hipExtLaunchKernelGGL), so hipEventElapsedTime of a
- * pair is that kernel's execution time alone, as in a profiler's kernel trace.  Event records
+ * pair is that kernel's execution time alone, as in a profiler's kernel trace.  On the one-pass
+ * path kernel 0 is chunk_state_seq and the state_passing pair is recorded back to back around
+ * no kernel.  Event records
  * cannot be captured into a graph: with non-NULL stage_events on a stream under capture the
  * call returns SSD_ERR_UNSUPPORTED and launches nothing.  For measurement tools; NULL
  * stage_events behaves exactly like ssd_fwd (which may be captured). */

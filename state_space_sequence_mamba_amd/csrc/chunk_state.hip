@@ -22,6 +22,10 @@
 #include "ssd_common.h"
 #include "ssd_launch.h"
 
+// (dtype, P, N, PS) of the one-pass chunk-state kernel
+#define SSD_FOR_EACH_SEQ_SHAPE(X) \
+  X(float, 64, 64, 32) X(float, 64, 64, 64) X(__bf16, 64, 128, 64)
+
 namespace ssd {
 
 // dt' = softplus(dt + dt_bias) (optionally clamped to [lo, hi], the dt limits of section 5.2
@@ -293,6 +297,338 @@ __global__ __launch_bounds__(NTHR, sizeof(T) == 2 ? 6 : 1) void chunk_state_kern
   }
 }
 
+// Forward, chunk states and their recurrence in one pass: one workgroup per (b, h, slice of PS
+// headdim rows) walks the chunks in order, keeping the running state H in its MFMA
+// accumulators.  At the start of chunk c it writes H_c (the state entering the chunk: fp32 for
+// fp32 inputs, rounded to bf16 for bf16 inputs, the copy the scan reads), scales H by the
+// chunk's total decay exp(dAcs[last]) and then accumulates that chunk's x^T diag(w) B tiles
+// into it, which is H_{c+1} = exp(dAcs_c[last]) H_c + S_c with S_c summed straight into the
+// carried state; after the last chunk H is the final state.  Each chunk's own state never goes
+// to memory, and no separate state_passing launch is needed.
+// The loop is chunk-major with the TPC tiles of a chunk unrolled; tile loads run one chunk
+// (TPC tiles) ahead through a ring of register sets, and the dt of the next chunk is loaded at
+// the start of the current one.  Every global load is unconditional (addresses clamped in
+// bounds, tokens past the end zeroed by flags), so the compiler's wait counts stay exact and
+// no wait drains the ring.  When the scan reads C B^T formed once per group, the first ncb_wg
+// workgroups form those blocks.
+template <typename T, int P, int N, int PS, int NTHR, int TPC>
+__global__ __launch_bounds__(NTHR) void chunk_state_seq_kernel(
+    const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ Cm, const T* __restrict__ dt,
+    const float* __restrict__ dt_bias, const float* __restrict__ A, float* __restrict__ dtp,
+    float* __restrict__ dAcs, float* __restrict__ states, __bf16* __restrict__ prev16,
+    const float* __restrict__ init, float* __restrict__ final_state, float* __restrict__ cb, int L, int H,
+    int G, int nc, uint32_t nseq, uint32_t ncb, uint32_t ncb_wg, int clamp, float lo, float hi) {
+  constexpr int KT = 64;                                 // tokens per LDS tile
+  constexpr int Q = TPC * KT;
+  if (blockIdx.x < ncb_wg) {
+    const uint32_t id = blockIdx.x * (NTHR / 256) + threadIdx.x / 256;
+    if (id < ncb) cb_block<T, N>(Bm, Cm, cb, L, G, nc, Q, id, threadIdx.x & 255);
+    return;
+  }
+  constexpr bool F32 = sizeof(T) == 4;
+  constexpr int PITCH = KT + (F32 ? 4 : 8);
+  constexpr int VEC = Vec16<T>::n;
+  constexpr int PV = PS / VEC, NV = N / VEC;
+  constexpr int XU = (KT / 2) * PV, BU = (KT / 2) * NV;  // token-pair units per tile
+  constexpr int XPT = (XU + NTHR - 1) / NTHR, BPT = (BU + NTHR - 1) / NTHR;
+  constexpr int TP = PS / 16, TN = N / 16;
+  constexpr int NW = NTHR / 64;
+  constexpr int WAVES_N = TN < NW ? TN : NW;
+  constexpr int WAVES_P = NW / WAVES_N;
+  constexpr int WN = TN / WAVES_N;
+  constexpr int WP = (TP + WAVES_P - 1) / WAVES_P;
+  constexpr int NS = P / PS;
+  constexpr int EPL = Q / 64;                            // cumsum positions per lane
+
+  __shared__ __attribute__((aligned(16))) T s_x[PS * PITCH];   // (x * w)^T, this slice's rows
+  __shared__ __attribute__((aligned(16))) T s_b[N * PITCH];    // B^T
+  __shared__ float s_d[Q], s_w[Q];
+  __shared__ float s_last;
+
+  uint32_t id = xcd_swizzle(blockIdx.x - ncb_wg, nseq);   // consecutive ids share b (and B)
+  const int sl = id % NS;
+  id /= NS;
+  const int h = id % H;
+  const int b = id / H;
+  const int g = h / (H / G);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, qd = lane >> 4;
+  const int wn = wave % WAVES_N, wp = wave / WAVES_N;
+
+  const size_t xs = (size_t)H * P, bs = (size_t)G * N;    // token strides
+  const uint32_t xs32 = (uint32_t)xs, bs32 = (uint32_t)bs;
+  const T* xb = x + (size_t)b * L * xs + (size_t)h * P + sl * PS;
+  const T* bb = Bm + (size_t)b * L * bs + (size_t)g * N;
+  const size_t PN = (size_t)P * N;
+  const size_t bh = (size_t)b * H + h;
+
+  // ---- tile ring
+  Vec16<T> xr[TPC][XPT][2], br[TPC][BPT][2];
+  uint32_t okm[TPC];
+  auto load_tile = [&](Vec16<T> (&xq)[XPT][2], Vec16<T> (&bq)[BPT][2], uint32_t& ok, int tb) {
+    const int rem = L - tb;                                // real tokens from tb on (may be <= 0)
+    const size_t base = rem > 0 ? (size_t)tb : 0;          // past the end: read token 0, zeroed
+    const T* xt = xb + base * xs;
+    const T* bt = bb + base * bs;
+    ok = 0;
+#pragma unroll
+    for (int u = 0; u < XPT; ++u) {
+      const int v = min(tid + NTHR * u, XU - 1);
+      const int m = v % (KT / 2), pv = (v / (KT / 2)) * VEC;
+      const int tok = 2 * m;
+      const bool ok0 = tok < rem, ok1 = tok + 1 < rem;
+      xq[u][0] = load16(xt + (uint32_t)(ok0 ? tok : 0) * xs32 + pv);
+      xq[u][1] = load16(xt + (uint32_t)(ok1 ? tok + 1 : 0) * xs32 + pv);
+      ok |= ((uint32_t)ok0 << (2 * u)) | ((uint32_t)ok1 << (2 * u + 1));
+    }
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+      const int v = min(tid + NTHR * u, BU - 1);
+      const int m = v % (KT / 2), nv = (v / (KT / 2)) * VEC;
+      const int tok = 2 * m;
+      const bool ok0 = tok < rem, ok1 = tok + 1 < rem;
+      bq[u][0] = load16(bt + (uint32_t)(ok0 ? tok : 0) * bs32 + nv);
+      bq[u][1] = load16(bt + (uint32_t)(ok1 ? tok + 1 : 0) * bs32 + nv);
+      ok |= ((uint32_t)ok0 << (2 * XPT + 2 * u)) | ((uint32_t)ok1 << (2 * XPT + 2 * u + 1));
+    }
+  };
+  // a loaded register made opaque where it is stored, so that no work on it (the bf16 pair
+  // packing) is hoisted up to its load, which would wait for the load there
+  auto opaque = [](const Vec16<T>& q) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 t;
+    __builtin_memcpy(&t, &q, 16);
+    asm volatile("" : "+v"(t));
+    Vec16<T> o;
+    __builtin_memcpy(&o, &t, 16);
+    return o;
+  };
+  auto store_tile = [&](const Vec16<T> (&xq)[XPT][2], const Vec16<T> (&bq)[BPT][2], uint32_t ok, int k0) {
+#pragma unroll
+    for (int u = 0; u < XPT; ++u) {
+      const int v = tid + NTHR * u;
+      if (XU % NTHR == 0 || v < XU) {
+        const int m = v % (KT / 2), pv = (v / (KT / 2)) * VEC;
+        const float w0 = s_w[k0 + 2 * m], w1 = s_w[k0 + 2 * m + 1];
+        const Vec16<T> x0 = keep_if(opaque(xq[u][0]), (ok >> (2 * u)) & 1u);
+        const Vec16<T> x1 = keep_if(opaque(xq[u][1]), (ok >> (2 * u + 1)) & 1u);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          T pair[2] = {from_f32<T>(to_f32(x0.v[e]) * w0), from_f32<T>(to_f32(x1.v[e]) * w1)};
+          __builtin_memcpy(&s_x[(pv + e) * PITCH + 2 * m], pair, sizeof(pair));
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+      const int v = tid + NTHR * u;
+      if (BU % NTHR == 0 || v < BU) {
+        const int m = v % (KT / 2), nv = (v / (KT / 2)) * VEC;
+        const Vec16<T> b0 = keep_if(opaque(bq[u][0]), (ok >> (2 * XPT + 2 * u)) & 1u);
+        const Vec16<T> b1 = keep_if(opaque(bq[u][1]), (ok >> (2 * XPT + 2 * u + 1)) & 1u);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          T pair[2] = {b0.v[e], b1.v[e]};
+          __builtin_memcpy(&s_b[(nv + e) * PITCH + 2 * m], pair, sizeof(pair));
+        }
+      }
+    }
+  };
+
+  // ---- dt: one position of the next chunk per thread (clamped in-bounds read)
+  const int dpos = tid % Q;
+  auto load_dt = [&](int c) {
+    return dt[((size_t)b * L + min(c * Q + dpos, L - 1)) * H + h];
+  };
+  const float bias = dt_bias[h], av = A[h];
+
+  // ---- the carried state (initial state read and waited for before the ring's loads)
+  f32x4 acc[WP][WN];
+#pragma unroll
+  for (int i = 0; i < WP; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j) acc[i][j] = zero4();
+  if (init) {
+#pragma unroll
+    for (int i = 0; i < WP; ++i) {
+      const int tp = wp * WP + i;
+      if (tp >= TP) continue;
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        const int n = (wn * WN + j) * 16 + r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][j][e] = init[bh * PN + (size_t)(sl * PS + tp * 16 + qd * 4 + e) * N + n];
+        asm volatile("" : "+v"(acc[i][j]));              // wait here, not inside the loop
+      }
+    }
+  }
+  auto write_state = [&](float* f32dst, __bf16* bf16dst) {
+#pragma unroll
+    for (int i = 0; i < WP; ++i) {
+      const int tp = wp * WP + i;
+      if (tp >= TP) continue;
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        const int n = (wn * WN + j) * 16 + r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const size_t o = (size_t)(sl * PS + tp * 16 + qd * 4 + e) * N + n;
+          if (f32dst) f32dst[o] = acc[i][j][e];
+          else bf16dst[o] = static_cast<__bf16>(acc[i][j][e]);
+        }
+      }
+    }
+  };
+
+  T dtv = load_dt(0);
+  // issued in the order the loop reissues them (slot 0 first), so that the waits the compiler
+  // derives for the loop hold for the first chunk too and do not drain the ring
+#pragma unroll
+  for (int k = 0; k < TPC; ++k) {
+    load_tile(xr[k], br[k], okm[k], k * KT);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  for (int c = 0; c < nc; ++c) {
+    // chunk prologue: dt' of this chunk into LDS, the next chunk's dt on its way
+    {
+      const int len = min(Q, L - c * Q);
+      float d = softplus(to_f32(dtv) + bias);
+      if (clamp) d = fminf(fmaxf(d, lo), hi);
+      if (tid < Q) s_d[dpos] = dpos < len ? d : 0.f;
+    }
+    dtv = load_dt(c + 1 < nc ? c + 1 : c);
+    __syncthreads();                     // s_d complete; the previous tile's MFMAs are done
+    if (wave == 0) {
+      // inclusive cumsum of dt' A (as chunk_cumsum_wave), weights and the total decay exponent
+      float d[EPL], cs[EPL];
+      float run = 0.f;
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) {
+        d[k] = s_d[lane * EPL + k];
+        run += d[k] * av;
+        cs[k] = run;
+      }
+      float incl = run;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float t = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += t;
+      }
+      float excl = __shfl_up(incl, 1, 64);
+      if (lane == 0) excl = 0.f;
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) cs[k] += excl;
+      const float last = __shfl(cs[EPL - 1], 63, 64);      // the stored dAcs[Q - 1]
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) s_w[lane * EPL + k] = expf(last - cs[k]) * d[k];
+      if (lane == 0) s_last = last;
+      if (sl == 0) {
+        float* dtp_c = dtp + (bh * nc + c) * Q + lane * EPL;
+        float* dA_c = dAcs + (bh * nc + c) * Q + lane * EPL;
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) {
+          dtp_c[k] = d[k];
+          dA_c[k] = cs[k];
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < TPC; ++k) {
+      __syncthreads();                   // previous tile consumed; s_w and s_last written
+      if (k == 0) {
+        // H_c leaves for the scan, then the decay over chunk c
+        const size_t o = (((size_t)b * nc + c) * H + h) * PN;
+        if (F32) write_state(states + o, nullptr);
+        else write_state(nullptr, prev16 + o);
+        const float dec = expf(s_last);
+#pragma unroll
+        for (int i = 0; i < WP; ++i)
+#pragma unroll
+          for (int j = 0; j < WN; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][e] *= dec;
+      }
+      store_tile(xr[k], br[k], okm[k], k * KT);
+      load_tile(xr[k], br[k], okm[k], (c + 1) * Q + k * KT);   // the same tile of the next chunk
+      __syncthreads();
+      if (F32) {
+#pragma unroll
+        for (int m = 0; m < KT / 16; ++m) {
+          float4 af[WP], bf[WN];
+#pragma unroll
+          for (int i = 0; i < WP; ++i) {
+            const int tp = wp * WP + i;
+            const int tpc = tp < TP ? tp : TP - 1;
+            const float4 v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(s_x) +
+                                                              (tpc * 16 + r) * PITCH + (KT / 4) * qd + 4 * m);
+            af[i] = (tp < TP) ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+          }
+#pragma unroll
+          for (int j = 0; j < WN; ++j)
+            bf[j] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(s_b) +
+                                                     ((wn * WN + j) * 16 + r) * PITCH + (KT / 4) * qd + 4 * m);
+#pragma unroll
+          for (int i = 0; i < WP; ++i)
+#pragma unroll
+            for (int j = 0; j < WN; ++j) {
+              acc[i][j] = mfma_16x16x4_f32(af[i].x, bf[j].x, acc[i][j]);
+              acc[i][j] = mfma_16x16x4_f32(af[i].y, bf[j].y, acc[i][j]);
+              acc[i][j] = mfma_16x16x4_f32(af[i].z, bf[j].z, acc[i][j]);
+              acc[i][j] = mfma_16x16x4_f32(af[i].w, bf[j].w, acc[i][j]);
+            }
+        }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < KT / 32; ++kk) {
+          bf16x8 af[WP], bf[WN];
+#pragma unroll
+          for (int i = 0; i < WP; ++i) {
+            const int tp = wp * WP + i;
+            const int tpc = tp < TP ? tp : TP - 1;
+            const bf16x8 v = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(s_x) +
+                                                              (tpc * 16 + r) * PITCH + 32 * kk + 8 * qd);
+            af[i] = (tp < TP) ? v : KMma<__bf16>::zero();
+          }
+#pragma unroll
+          for (int j = 0; j < WN; ++j)
+            bf[j] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(s_b) +
+                                                     ((wn * WN + j) * 16 + r) * PITCH + 32 * kk + 8 * qd);
+#pragma unroll
+          for (int i = 0; i < WP; ++i)
+#pragma unroll
+            for (int j = 0; j < WN; ++j) acc[i][j] = mfma_16x16x32_bf16(af[i], bf[j], acc[i][j]);
+        }
+      }
+    }
+  }
+  if (final_state) write_state(final_state + bh * PN, nullptr);
+}
+
+template <typename T, int P, int N, int PS>
+static hipError_t launch_state_seq_impl(const FwdArgs& a, hipStream_t s) {
+  constexpr int NTHR = (PS / 16) * (N / 16) >= 32 ? 512 : 256;
+  const uint32_t nseq = (uint32_t)a.B * a.H * (P / PS);
+  const int nrb = a.Q / kCbKT;
+  const uint32_t ncb = a.cb ? (uint32_t)a.B * a.nc * a.G * (nrb * (nrb + 1) / 2) : 0u;
+  const uint32_t ncb_wg = ((ncb + NTHR / 256 - 1) / (NTHR / 256) + 7) / 8 * 8;
+  if (nseq == 0 || a.nc == 0) return hipErrorInvalidValue;
+#define SSD_SEQ_LAUNCH(TPC_)                                                                                    \
+  hipExtLaunchKernelGGL(chunk_state_seq_kernel<T, P, N, PS, NTHR, TPC_>, dim3(nseq + ncb_wg), dim3(NTHR), 0, s,  \
+                        a.ev0, a.ev1, 0, static_cast<const T*>(a.x), static_cast<const T*>(a.Bm),               \
+                        static_cast<const T*>(a.Cm), static_cast<const T*>(a.dt), a.dt_bias, a.A, a.dtp, a.dAcs,  \
+                        a.states, static_cast<__bf16*>(a.prev16), a.init, a.final_state, a.cb, a.L, a.H, a.G,   \
+                        a.nc, nseq, ncb, ncb_wg, a.clamp, a.dt_lo, a.dt_hi)
+  if (a.Q == 256)
+    SSD_SEQ_LAUNCH(4);
+  else if (a.Q == 128)
+    SSD_SEQ_LAUNCH(2);
+  else
+    return hipErrorInvalidValue;
+#undef SSD_SEQ_LAUNCH
+  return hipGetLastError();
+}
+
 template <typename T, int P, int N>
 static hipError_t launch_state_impl(const FwdArgs& a, hipStream_t s) {
   const uint32_t nblocks = (uint32_t)a.B * a.nc * a.H;
@@ -315,6 +651,24 @@ hipError_t launch_chunk_state(const FwdArgs& a, hipStream_t s) {
   if (a.dtype == SSD_DTYPE_CODE_##T && a.P == P_ && a.N == N_) return launch_state_impl<T, P_, N_>(a, s);
   SSD_FOR_EACH_SHAPE(SSD_CASE)
 #undef SSD_CASE
+  return hipErrorInvalidValue;
+}
+
+bool chunk_state_seq_supported(const FwdArgs& a, int ps) {
+  if (a.Q != 256 && a.Q != 128) return false;
+#define SSD_SEQ_CASE(T, P_, N_, PS_) \
+  if (a.dtype == SSD_DTYPE_CODE_##T && a.P == P_ && a.N == N_ && ps == PS_) return true;
+  SSD_FOR_EACH_SEQ_SHAPE(SSD_SEQ_CASE)
+#undef SSD_SEQ_CASE
+  return false;
+}
+
+hipError_t launch_chunk_state_seq(const FwdArgs& a, int ps, hipStream_t s) {
+#define SSD_SEQ_CASE(T, P_, N_, PS_) \
+  if (a.dtype == SSD_DTYPE_CODE_##T && a.P == P_ && a.N == N_ && ps == PS_) \
+    return launch_state_seq_impl<T, P_, N_, PS_>(a, s);
+  SSD_FOR_EACH_SEQ_SHAPE(SSD_SEQ_CASE)
+#undef SSD_SEQ_CASE
   return hipErrorInvalidValue;
 }
 

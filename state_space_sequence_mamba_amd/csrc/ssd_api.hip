@@ -100,6 +100,32 @@ int g_tune_min_blocks = 512;
 int g_tune_scan_variant = 0;     // 0 = built-in (row blocks)
 int g_tune_conv_segment = 0;     // 0 = sized to the chip
 int g_tune_rows_group = 0;       // units per row-block dispatch group (0 = built-in, 16)
+int g_tune_state_seq = 0;        // 0 = built-in, 1 = chunk_state + state_passing, 2 = one pass
+int g_tune_state_seq_ps = 0;     // headdim rows per one-pass workgroup (0 = built-in)
+
+// Chunk states: either per (b, c, h) in parallel followed by the sequential state_passing
+// launch, or one pass per (b, h, headdim slice) walking the chunks in order with the state in
+// registers (no per-chunk states in memory).  Returns the slice rows of the one-pass kernel, or
+// 0 for the two-launch path.  Built-in choice, measured on MI355X (bf16 P64 N128): one pass from
+// B H >= 256 (B8 L4096 H32 forward 0.320 -> 0.277 ms, B16 L2048 0.338 -> 0.299, B8 L1024
+// 0.092 -> 0.082, B8 L4096 chunk 128 0.378 -> 0.344), two launches below (B4 L4096 H32 0.163
+// against 0.172 ms; B2 L16384 H80 G8 0.793 against 0.823: too few workgroups for 256 CUs, each
+// with a long chain of chunks); fp32 keeps two launches (B4 L1024 H24 0.0695 against 0.0765 ms
+// at 32-row slices, B16 L1024 H24 0.230 against 0.228 at whole rows).
+int pick_state_seq(int dtype, int64_t B, int64_t H, int P, int N, int Q, bool forward_only) {
+  if (g_tune_state_seq == 1 || !forward_only) return 0;
+  ssd::FwdArgs a{};
+  a.dtype = dtype;
+  a.P = P;
+  a.N = N;
+  a.Q = Q;
+  if (g_tune_state_seq == 2) {
+    const int ps = g_tune_state_seq_ps > 0 ? g_tune_state_seq_ps : P;
+    return ssd::chunk_state_seq_supported(a, ps) ? ps : 0;
+  }
+  if (dtype != ssd::DT_BF16 || P != 64 || N != 128 || B * H < 256) return 0;
+  return ssd::chunk_state_seq_supported(a, 64) ? 64 : 0;
+}
 
 // Row-block dispatch groups of 16 units per XCD: measured on MI355X, bf16 B2 L16384 H80 G8
 // chunk_scan 514 -> 432 us (the row blocks of a unit re-read its x tiles and entering state
@@ -223,10 +249,18 @@ ssd_status_t fwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
     a.ev0 = ev ? ev[2 * k] : nullptr;
     a.ev1 = ev ? ev[2 * k + 1] : nullptr;
   };
-  stage(0);
-  if (ssd::launch_chunk_state(a, stream) != hipSuccess) return SSD_ERR_HIP;
-  stage(1);
-  if (ssd::launch_state_passing(a, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (const int ps = pick_state_seq(a.dtype, a.B, a.H, a.P, a.N, a.Q, !a.keep_f32_states && !a.state_from_start)) {
+    stage(0);
+    if (ssd::launch_chunk_state_seq(a, ps, stream) != hipSuccess) return SSD_ERR_HIP;
+    // no state_passing launch: its event pair brackets nothing
+    if (ev && (hipEventRecord(ev[2], stream) != hipSuccess || hipEventRecord(ev[3], stream) != hipSuccess))
+      return SSD_ERR_HIP;
+  } else {
+    stage(0);
+    if (ssd::launch_chunk_state(a, stream) != hipSuccess) return SSD_ERR_HIP;
+    stage(1);
+    if (ssd::launch_state_passing(a, stream) != hipSuccess) return SSD_ERR_HIP;
+  }
   stage(2);
   if (ssd::launch_chunk_scan(a, stream) != hipSuccess) return SSD_ERR_HIP;
   return SSD_OK;
@@ -618,12 +652,21 @@ const char* ssd_status_string(ssd_status_t s) {
   return "unknown status";
 }
 
+int ssd_fwd_state_path(const ssd_dims_t* dims, int chunk_size) {
+  if (check_dims(dims, true) != SSD_OK || !chunk_ok(chunk_size) || dims->seqlen == 0 || dims->batch == 0) return 0;
+  const int dtype = dims->dtype == SSD_F32 ? ssd::DT_F32 : ssd::DT_BF16;
+  return pick_state_seq(dtype, dims->batch, dims->nheads, (int)dims->headdim, (int)dims->dstate, chunk_size, true)
+             ? 2 : 1;
+}
+
 void ssd_tune_set(int key, int value) {
   if (key == 0) g_tune_heads_per_block = value;
   if (key == 1) g_tune_min_blocks = value > 0 ? value : 512;
   if (key == 3) g_tune_conv_segment = value > 0 ? value : 0;
   if (key == 4) g_tune_rows_group = value > 0 ? value : 0;
   if (key == 2) g_tune_scan_variant = value;
+  if (key == 5) g_tune_state_seq = value;
+  if (key == 6) g_tune_state_seq_ps = value > 0 ? value : 0;
 }
 
 }  // extern "C"

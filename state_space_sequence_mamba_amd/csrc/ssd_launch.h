@@ -119,6 +119,10 @@ bool shape_supported(int dtype, int P, int N);
 
 hipError_t launch_chunk_state(const FwdArgs& a, hipStream_t s);
 hipError_t launch_state_passing(const FwdArgs& a, hipStream_t s);
+// forward only: chunk states and state passing in one launch, one workgroup per (b, h, ps
+// headdim rows); supported(a, ps): an instantiation exists for (dtype, P, N, ps)
+bool chunk_state_seq_supported(const FwdArgs& a, int ps);
+hipError_t launch_chunk_state_seq(const FwdArgs& a, int ps, hipStream_t s);
 hipError_t launch_chunk_scan(const FwdArgs& a, hipStream_t s);
 hipError_t launch_ssd_step(const StepArgs& a, hipStream_t s);
 hipError_t launch_bwd_dxdb(const BwdArgs& a, hipStream_t s);

@@ -74,6 +74,22 @@ WORKLOADS = {w.name: w for w in [
 WORKLOAD_LIST = list(WORKLOADS.values())
 
 
+def workload(name):
+    """One of WORKLOADS, or a forward / backward of another size named the same way, e.g.
+    "ssd_fwd bf16 B4 L4096 H32 P64 N128 G1 Q256" (seed 0; D ones for f32, normal for bf16)."""
+    if name in WORKLOADS:
+        return WORKLOADS[name]
+    parts = name.split()
+    if len(parts) != 9 or parts[0] not in ("ssd_fwd", "ssd_bwd") or parts[1] not in ("f32", "bf16"):
+        raise KeyError(f"unknown workload {name!r}")
+    try:
+        v = {p[0]: int(p[1:]) for p in parts[2:]}
+        return Workload(name, parts[0][4:], parts[1], v["B"], v["H"], v["P"], v["N"], v["G"], 0,
+                        "ones" if parts[1] == "f32" else "normal", seqlen=v["L"], chunk=v["Q"])
+    except (KeyError, ValueError):
+        raise KeyError(f"unknown workload {name!r}") from None
+
+
 def _torch_dtype(dtype):
     return {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
 

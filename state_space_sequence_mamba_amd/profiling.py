@@ -23,11 +23,12 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SSD_KERNELS = ["chunk_state", "state_passing", "chunk_scan", "ssd_step", "conv1d_silu",
+SSD_KERNELS = ["chunk_state", "chunk_state_seq", "state_passing", "chunk_scan", "ssd_step", "conv1d_silu",
                "conv1d_silu_step", "bwd_dxdb", "bwd_dc", "bwd_finalize"]
 # source file of each kernel; every kernel also depends on the shared headers and the API layer
 # (which picks launch shapes)
-KERNEL_SOURCE = {"chunk_state": "chunk_state.hip", "state_passing": "state_passing.hip",
+KERNEL_SOURCE = {"chunk_state": "chunk_state.hip", "chunk_state_seq": "chunk_state.hip",
+                 "state_passing": "state_passing.hip",
                  "chunk_scan": "chunk_scan.hip", "ssd_step": "ssd_step.hip",
                  "conv1d_silu": "conv1d.hip", "conv1d_silu_step": "conv1d.hip", "bwd_dxdb": "ssd_bwd.hip",
                  "bwd_dc": "ssd_bwd.hip", "bwd_finalize": "ssd_bwd.hip"}
@@ -48,7 +49,7 @@ def kernel_key(name):
     """Map a dispatch's kernel name to a kernel key, 'copy' for copy kernels, else None."""
     if "chunk_scan" in name:
         return "chunk_scan"
-    for k in ("chunk_state", "state_passing", "ssd_step", "conv1d_silu_step", "conv1d_silu",
+    for k in ("chunk_state_seq", "chunk_state", "state_passing", "ssd_step", "conv1d_silu_step", "conv1d_silu",
               "bwd_dxdb", "bwd_dc", "bwd_finalize"):
         if k + "_kernel" in name:
             return k

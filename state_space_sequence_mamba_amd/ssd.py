@@ -68,6 +68,8 @@ def load_library():
     lib.ssd_status_string.restype = ctypes.c_char_p
     lib.ssd_tune_set.argtypes = [i32, i32]
     lib.ssd_tune_set.restype = None
+    lib.ssd_fwd_state_path.argtypes = [dims_p, i32]
+    lib.ssd_fwd_state_path.restype = i32
     _lib = lib
     return lib
 
@@ -309,5 +311,10 @@ def conv1d_silu_step(conv_state, xbc, weight, bias, nheads, headdim, dstate, ngr
 
 
 def tune_set(key, value):
-    """Launch-shape knob (include/ssd_tuning.h); results never depend on it."""
+    """Launch-shape knob (include/ssd_tuning.h); results depend on it at most by rounding."""
     load_library().ssd_tune_set(int(key), int(value))
+
+
+def fwd_state_path(dims, chunk_size):
+    """1: chunk_state then state_passing; 2: one pass over the chunks; 0: invalid or empty."""
+    return int(load_library().ssd_fwd_state_path(ctypes.byref(dims), int(chunk_size)))

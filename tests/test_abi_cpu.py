@@ -232,3 +232,31 @@ def test_product_package_never_imports_the_oracle():
         if f.endswith((".py", ".hip", ".h", ".cpp")):
             text = open(f).read()
             assert not re.search(r"\boracle\b", text.replace("the oracle", "")) or f.endswith("inputs.py"), f
+
+
+def test_fwd_state_path_choice_is_host_logic():
+    """The chunk-state path ssd_fwd takes (pure host logic, no GPU needed): one pass for bf16
+    P64 N128 from batch x heads >= 256, two launches otherwise; the knob forces either where an
+    instantiation exists; invalid or empty sizes give 0."""
+    import torch
+    bf, f32 = torch.bfloat16, torch.float32
+    cases = [((8, 4096, 32, 64, 128, 1, bf), 256, 2), ((8, 4096, 32, 64, 128, 1, bf), 128, 2),
+             ((8, 4096, 32, 64, 128, 1, bf), 64, 1), ((4, 4096, 32, 64, 128, 1, bf), 256, 1),
+             ((2, 16384, 80, 64, 128, 8, bf), 256, 1), ((8, 4096, 32, 64, 64, 1, bf), 256, 1),
+             ((16, 1024, 24, 64, 64, 1, f32), 256, 1), ((8, 0, 32, 64, 128, 1, bf), 256, 0),
+             ((8, 4096, 32, 64, 128, 1, bf), 100, 0)]
+    for args, q, want in cases:
+        assert ssd.fwd_state_path(ssd.make_dims(*args), q) == want, (args, q)
+    try:
+        ssd.tune_set(5, 2)
+        assert ssd.fwd_state_path(ssd.make_dims(4, 1024, 24, 64, 64, 1, f32), 256) == 2
+        ssd.tune_set(6, 32)
+        assert ssd.fwd_state_path(ssd.make_dims(4, 1024, 24, 64, 64, 1, f32), 256) == 2
+        ssd.tune_set(6, 16)          # no such instantiation: two launches
+        assert ssd.fwd_state_path(ssd.make_dims(4, 1024, 24, 64, 64, 1, f32), 256) == 1
+        ssd.tune_set(6, 0)
+        ssd.tune_set(5, 1)
+        assert ssd.fwd_state_path(ssd.make_dims(8, 4096, 32, 64, 128, 1, bf), 256) == 1
+    finally:
+        ssd.tune_set(5, 0)
+        ssd.tune_set(6, 0)
