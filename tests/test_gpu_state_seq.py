@@ -4,7 +4,8 @@ place of chunk_state + state_passing), through the C ABI, against the float64 or
 
 The path is forced with the launch knob (key 5 = 2, key 6 = slice rows) on small shapes that
 still span several chunks, 64-token tiles and a ragged last chunk; the built-in choice takes it
-for bf16 P64 N128 once batch x heads >= 256, which the last test covers without the knob.
+for bf16 P64 N128 once batch x heads >= 256, which test_built_in_choice_takes_one_pass_for_large_bf16_batches
+covers without the knob.
 Bar as in the other parity tests: rel_err <= 1e-4 (fp32 inputs), <= 2e-2 (bf16 inputs).
 """
 import sys
@@ -169,3 +170,41 @@ def test_built_in_choice_takes_one_pass_for_large_bf16_batches():
     yr, fr = _oracle(inp)
     assert rel_err(to64(y), yr) <= TOL["bf16"]
     assert rel_err(to64(fin), fr) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_one_pass_graph_capture_replays_match_eager(dtype):
+    """The one-pass forward captured into a HIP graph: every replay, with unrelated eager work
+    and synchronisation in between, reproduces the eager outputs bit for bit."""
+    _say(f"one-pass graph capture {dtype}")
+    P, N = (64, 64) if dtype == "f32" else (64, 128)
+    inp = {k: v.to(DEV) for k, v in I.make_fwd_inputs(2, 500, 4, P, N, 1, dtype, seed=87).items()}
+    dims = ssd.make_dims(2, 500, 4, P, N, 1, inp["x"].dtype)
+    ws = torch.empty(ssd.ssd_fwd_workspace_size(dims, 256), dtype=torch.uint8, device=DEV)
+    y = torch.empty_like(inp["x"])
+    st = torch.empty(2, 4, P, N, device=DEV)
+
+    def run():
+        ssd.ssd_fwd(inp["x"], inp["dt"], inp["dt_bias"], inp["A"], inp["B"], inp["C"], inp["D"], chunk_size=256,
+                    y=y, final_state=st, workspace=ws)
+
+    with _one_pass(64):
+        run()
+        torch.cuda.synchronize()
+        ref = (y.clone(), st.clone())
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(graph, stream=cap):
+            run()
+        torch.cuda.synchronize()
+    other = {k: v.to(DEV) for k, v in I.make_fwd_inputs(2, 300, 4, P, N, 1, dtype, seed=88).items()}
+    for rep in range(3):
+        y.fill_(float("nan"))
+        st.fill_(float("nan"))
+        ssd.ssd_fwd(other["x"], other["dt"], other["dt_bias"], other["A"], other["B"], other["C"], other["D"],
+                    chunk_size=64)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref[0]) and torch.equal(st, ref[1]), rep
