@@ -176,6 +176,71 @@ def summary(args):
     print(text)
 
 
+MFMA_COUNTERS = ["SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES",
+                 "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY", "GRBM_GUI_ACTIVE"]
+MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
+
+
+def mfma(args):
+    """Markdown summary of one counter run over MFMA_COUNTERS: per kernel, the matrix-core work
+    the hardware counted (the MOPS counters count MFMA operations in units of 512 flops), its
+    ratio to the kernel's algorithmic flops, and that work's rate over the kernel's duration
+    (dispatch events of the same bench.py run) against the published dense peak."""
+    per = {c: counter_per_dispatch(args.pmc, c) for c in MFMA_COUNTERS}
+    bench = _bench_line(args.log)
+    if not bench:
+        sys.exit(f"no bench.py line in {args.log}")
+    dtype = bench["dtype"]
+    kernels = bench.get("kernels", {})
+    # kernel durations from the kernel-trace summary of the same workload (rocprofv3 averages):
+    # dispatch events inside a counter run are stretched by the collection
+    dur = {}
+    with open(args.trace_md) as fh:
+        for line in fh:
+            cells = [c.strip() for c in line.split("|")]
+            if len(cells) > 4 and cells[1].startswith("`"):
+                key = kernel_key(cells[1].strip("`"))
+                if key and key not in dur:
+                    dur[key] = float(cells[3])
+    out = [f"# MFMA counters: {args.workload} (MI355X, gfx950)", "",
+           "Command (from the repository root, TMPDIR=/tmp):", "", f"    {args.command}", "",
+           "Summarised with `python -m state_space_sequence_mamba_amd.profiling mfma` from the run's "
+           "counter_collection.csv (counter values summed over their instances, averaged over the "
+           "dispatches of each kernel).  Counted MFMA flops = 512 x (SQ_INSTS_VALU_MFMA_MOPS_F32 + "
+           "SQ_INSTS_VALU_MFMA_MOPS_BF16) per dispatch; the ratio column divides it by the kernel's "
+           "algorithmic flops (causal half of the in-chunk products, C B^T once per group), so values "
+           "above 1 are work the kernel spends beyond the algorithm (masked upper halves of diagonal "
+           "tiles, C B^T per head).  The rate column divides the counted flops by the kernel's average "
+           f"duration in the kernel trace `{os.path.basename(args.trace_md)}` (same workload, unprofiled "
+           "by counters; dispatch events inside a counter run are stretched by the collection); the "
+           f"peak is the published dense {dtype} MFMA peak "
+           f"({MFMA_PEAK_TFLOPS[dtype]} TFLOP/s).  Wait share = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (wave "
+           "cycles spent waiting on an s_waitcnt).", "",
+           "| kernel | dispatches | counted MFMA GFLOP | algorithmic GFLOP | ratio | trace duration (us) | "
+           "counted MFMA TFLOP/s | of peak | wait share | SQ_VALU_MFMA_BUSY_CYCLES | SQ_BUSY_CYCLES | "
+           "GRBM_GUI_ACTIVE |",
+           "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    avg = lambda c, k: (sum(per[c][k]) / len(per[c][k])) if k in per[c] else 0.0  # noqa: E731
+    for k in SSD_KERNELS:
+        if k not in per["SQ_WAVE_CYCLES"] or k not in kernels:
+            continue
+        mops = avg("SQ_INSTS_VALU_MFMA_MOPS_F32", k) + avg("SQ_INSTS_VALU_MFMA_MOPS_BF16", k)
+        flops = 512.0 * mops
+        alg = kernels[k].get("alg_flops", 0)
+        us = dur.get(k, 0.0)
+        rate = flops / (us * 1e-6) / 1e12 if us else 0.0
+        wait = avg("SQ_WAIT_INST_ANY", k) / max(avg("SQ_WAVE_CYCLES", k), 1.0)
+        out.append(f"| {k} | {len(per['SQ_WAVE_CYCLES'][k])} | {flops / 1e9:.3f} | {alg / 1e9:.3f} | "
+                   f"{(flops / alg) if alg else float('nan'):.2f} | {us:.2f} | {rate:.1f} | "
+                   f"{rate / MFMA_PEAK_TFLOPS[dtype] * 100:.1f} % | {wait * 100:.0f} % | "
+                   f"{avg('SQ_VALU_MFMA_BUSY_CYCLES', k):.4g} | {avg('SQ_BUSY_CYCLES', k):.4g} | "
+                   f"{avg('GRBM_GUI_ACTIVE', k):.4g} |")
+    text = "\n".join(out) + "\n"
+    with open(args.out, "w") as fh:
+        fh.write(text)
+    print(text)
+
+
 def workload_slug(name):
     return "_".join(name.lower().split())
 
@@ -211,8 +276,15 @@ def main():
     m.add_argument("--workload", required=True)
     m.add_argument("--command", required=True)
     m.add_argument("--out", required=True)
+    f = sub.add_parser("mfma")
+    f.add_argument("--pmc", required=True)
+    f.add_argument("--log", required=True)
+    f.add_argument("--trace-md", required=True)
+    f.add_argument("--workload", required=True)
+    f.add_argument("--command", required=True)
+    f.add_argument("--out", required=True)
     a = ap.parse_args()
-    {"traffic": traffic, "stats": stats, "summary": summary}[a.cmd](a)
+    {"traffic": traffic, "stats": stats, "summary": summary, "mfma": mfma}[a.cmd](a)
 
 
 if __name__ == "__main__":
