@@ -1,17 +1,17 @@
 """Benchmark of the SSD hot path on one MI355X.
 
-One step = one pass of the whole path over one batch: ssd_fwd over the prefill batch
-(chunk_state with the dt' cumsum and, for fp32, C B^T once per group -> state_passing ->
-chunk_scan; for large bf16 batches chunk_state_seq, one pass over the chunks with the state
-carried in registers, in place of the first two), writing final_state, then one ssd_step
-decode token per sequence continuing
-from that state.  Other workloads (--workload): the backward (ssd_bwd), the decode loop and
-the conv1d + SiLU in front of the scan.  Workload: the fp32
-forward of batch 4 x 1024 tokens, 24 heads, headdim 64, dstate 64, 1 group, chunk 256
-(plus its decode token).  Inputs are seeded synthetic tensors resident in HBM before the
-timed region.  Prints ONE JSON line.
+Headline (default): one step = one ssd_fwd call (chunk_state with the dt' cumsum, or the one-pass
+chunk_state_seq for large bf16 batches; state_passing; chunk_scan) over the bf16 batch of
+2 sequences x 16384 tokens, 80 heads in 8 groups, headdim 64, dstate 128, chunk 256 (the largest
+of the five workloads the scan is specified on), writing y and final_state.  tokens/s = B L / the
+time of one call.  The same JSON line carries `configs`: the other four workloads (the fp32
+B1 L256 and B4 L1024 forwards, the bf16 B8 L4096 forward, and 1000 consecutive ssd_step decode
+calls over B256 H80), each with its tokens/s and its dominant kernel's roofline fraction.
+Other workloads alone (--workload): any forward or backward size, the decode loop, the conv1d +
+SiLU in front of the scan.  Inputs are seeded synthetic tensors resident in HBM before the timed
+region.  Prints ONE JSON line.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload NAME]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME] [--no-configs]
 """
 import argparse
 import json
@@ -32,8 +32,9 @@ from state_space_sequence_mamba_amd.timing import HipEvents  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0                         # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}   # dense matrix peaks, TFLOP/s
-DEFAULT_WORKLOAD = "ssd_fwd f32 B4 L1024 H24 P64 N64 G1 Q256"
-KERNELS = ["chunk_state", "state_passing", "chunk_scan", "ssd_step"]
+DEFAULT_WORKLOAD = "ssd_fwd bf16 B2 L16384 H80 P64 N128 G8 Q256"
+KERNELS = ["chunk_state", "state_passing", "chunk_scan"]
+MAX_WORKERS = 16          # the host's CPU share per GPU
 
 
 def algorithmic_cost(w):
@@ -69,9 +70,6 @@ def algorithmic_cost(w):
         # fp32 reads the C B^T blocks back once per head; bf16 forms C B^T inside chunk_scan
         "chunk_scan": dict(bytes=2 * x + (cbr if pre else 2 * bc) + cum + (st if pre else st // 2) + H * P * 4,
                            flops=2 * B * H * P * tri + 2 * B * H * L * N * P + (0 if pre else 2 * B * G * N * tri)),
-        # decode: state read + write, x, y, dt, B, C
-        "ssd_step": dict(bytes=2 * fin + 2 * B * H * P * e + B * H * e + 2 * B * G * N * e,
-                         flops=4 * B * H * P * N),
     }
     for k, v in cost.items():
         peak_f = MFMA_PEAK_TFLOPS[w.dtype] * 1e12
@@ -81,53 +79,95 @@ def algorithmic_cost(w):
     return cost
 
 
-def cpu_baseline(w, inp, dec, budget_s):
-    """The float64 oracle (as it stands) on a bounded sample of the same step, single thread."""
-    import numpy as np
-    from threadpoolctl import threadpool_limits
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
+
+def _oracle_heads(inp, b, heads, T):
+    """Oracle y over the first T tokens of batch row b for the listed heads (each head its own
+    group in one vectorised oracle call: heads are independent)."""
+    import numpy as np
     from oracle import ssd_recurrence
 
     f64 = lambda t: t.detach().cpu().double().numpy()  # noqa: E731
-    rows = w.batch
-    with threadpool_limits(1):
-        # one pass over as many whole sequences as fit the budget, then repeat passes until
-        # the budget is spent (or a cap of 30 s), so the rate rests on 10-30 s of work
-        while True:
-            x = np.concatenate([f64(inp["x"][:rows]), f64(dec["x"][0, :rows])[:, None]], axis=1)
-            dt = np.concatenate([f64(inp["dt"][:rows]), f64(dec["dt"][0, :rows])[:, None]], axis=1)
-            Bm = np.concatenate([f64(inp["B"][:rows]), f64(dec["B"][0, :rows])[:, None]], axis=1)
-            Cm = np.concatenate([f64(inp["C"][:rows]), f64(dec["C"][0, :rows])[:, None]], axis=1)
-            t0 = time.perf_counter()
-            ssd_recurrence(x, dt, f64(inp["dt_bias"]), f64(inp["A"]), Bm, Cm, f64(inp["D"]))
-            secs = time.perf_counter() - t0
-            if secs <= budget_s or rows == 1:
-                break
-            rows = max(1, rows // 2)
-        passes = 1
-        while secs < budget_s and secs * (passes + 1) / passes < 30.0:
-            t0 = time.perf_counter()
-            ssd_recurrence(x, dt, f64(inp["dt_bias"]), f64(inp["A"]), Bm, Cm, f64(inp["D"]))
-            secs += time.perf_counter() - t0
-            passes += 1
-    tokens = passes * rows * (w.seqlen + 1)
-    return {"value": tokens / secs, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"float64 sequential recurrence over {rows} of {w.batch} sequences x "
-                      f"{w.seqlen + 1} tokens (prefill + decode token), {passes} passes, {secs:.2f} s, "
-                      f"numpy, 1 thread"}
+    H, G = inp["x"].shape[2], inp["B"].shape[2]
+    gs = [h // (H // G) for h in heads]
+    x = f64(inp["x"][b:b + 1, :T][:, :, heads])
+    dt = f64(inp["dt"][b:b + 1, :T][:, :, heads])
+    Bm = np.stack([f64(inp["B"][b, :T, g]) for g in gs], axis=1)[None]
+    Cm = np.stack([f64(inp["C"][b, :T, g]) for g in gs], axis=1)[None]
+    D = None if inp.get("D") is None else f64(inp["D"])[heads]
+    y, _ = ssd_recurrence(x, dt, f64(inp["dt_bias"])[heads], f64(inp["A"])[heads], Bm, Cm, D)
+    return y[0]
+
+
+def cpu_baseline(w, inp, y_gpu, budget_s):
+    """The float64 oracle (as it stands) on a bounded sample of the same forward: the first T
+    tokens of batch row 0 with every head, the heads split over a thread pool of the host's cores
+    (numpy releases the GIL inside its array operations).  T is sized from a short calibration
+    run so that the timed run takes about `budget_s`.  The sample's oracle output is also
+    compared with the GPU output (a parity check of the timed workload)."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+
+    workers = max(1, min(len(os.sched_getaffinity(0)), MAX_WORKERS, w.nheads))
+    slices = [list(range(w.nheads))[k::workers] for k in range(workers)]
+
+    def run(T):
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(workers) as ex:
+            ys = list(ex.map(lambda hs: _oracle_heads(inp, 0, hs, T), slices))
+        return time.perf_counter() - t0, ys
+
+    T0 = min(w.seqlen, 128)
+    secs, _ = run(T0)
+    T = int(min(w.seqlen, max(T0, T0 * budget_s / max(secs, 1e-3))))
+    secs, ys = run(T)
+    ref = np.zeros((T, w.nheads, w.headdim))
+    for hs, yk in zip(slices, ys):
+        ref[:, hs] = yk
+    got = y_gpu[0, :T].float().cpu().double().numpy()
+    scale = float(np.max(np.abs(ref)))
+    err = float(np.max(np.abs(got - ref)) / scale)
+    p999 = float(np.percentile(np.abs(got - ref) / (np.abs(ref) + 1e-3 * scale), 99.9))
+    base = {"value": round(T / secs, 1), "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"float64 sequential recurrence over the first {T} of {w.seqlen} tokens of batch row 0 "
+                      f"(all {w.nheads} heads, {workers} threads of numpy), {secs:.2f} s",
+            "cpu_model": cpu_model(), "host_cores": len(os.sched_getaffinity(0))}
+    parity = {"tokens": T, "batch_row": 0, "rel_err": err, "p99_9_rel_err": p999,
+              "tolerance": 1e-4 if w.dtype == "f32" else 2e-2}
+    return base, parity
+
+
+def decode_cost(w):
+    e = 2 if w.dtype == "bf16" else 4
+    B, H, P, N, G = w.batch, w.nheads, w.headdim, w.dstate, w.ngroups
+    return 8 * B * H * P * N + 2 * B * H * P * e + B * H * e + 2 * B * G * N * e
 
 
 def run_decode(w, args, dev):
     """The decode workload: `w.steps` consecutive ssd_step calls from a random state (one token
-    per sequence per call), timed as one region; inputs for every step are resident in HBM."""
+    per sequence per call), timed as one region; inputs for every step are resident in HBM.  The
+    kernel's own duration comes from dispatch-recorded events (ssd_step_ex) in a second pass."""
     inp = I.make_step_inputs(w.batch, w.nheads, w.headdim, w.dstate, w.ngroups, w.steps, w.dtype, w.seed,
                              w.d_init, device=dev)
     state = inp["state0"].clone()
     y = torch.empty_like(inp["x"][0])
     W = min(args.warmup, w.steps)
-    for t in range(W):
+
+    def call(t, evs=None):
         ssd.ssd_step(state, inp["x"][t], inp["dt"][t], inp["dt_bias"], inp["A"], inp["B"][t], inp["C"][t],
-                     inp["D"], y=y)
+                     inp["D"], y=y, events=evs)
+
+    for t in range(W):
+        call(t)
     state.copy_(inp["state0"])
     torch.cuda.synchronize()
     hev = HipEvents()
@@ -135,31 +175,35 @@ def run_decode(w, args, dev):
     wall0 = time.perf_counter()
     hev.record(t0)
     for t in range(w.steps):
-        ssd.ssd_step(state, inp["x"][t], inp["dt"][t], inp["dt_bias"], inp["A"], inp["B"][t], inp["C"][t],
-                     inp["D"], y=y)
+        call(t)
     hev.record(t1)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms = hev.elapsed_ms(t0, t1)
-    e = 2 if w.dtype == "bf16" else 4
-    B, H, P, N, G = w.batch, w.nheads, w.headdim, w.dstate, w.ngroups
-    alg_bytes = 8 * B * H * P * N + 2 * B * H * P * e + B * H * e + 2 * B * G * N * e
-    per_step_s = ms * 1e-3 / w.steps
-    ach = alg_bytes / per_step_s / 1e9
-    out = {
-        "metric": "SSD decode tokens/sec at 1 MI355X + % of HBM roofline", "value": round(B * w.steps / (ms * 1e-3), 1),
-        "unit": "tokens/s", "n_gpus": 1, "steps": w.steps, "warmup": W, "ms_per_step": round(ms / w.steps, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+    # per-kernel time: the same calls again, each timed by its own dispatch
+    n_ev = min(w.steps, 200)
+    evs = [(hev.create(), hev.create()) for _ in range(n_ev)]
+    for t in range(n_ev):
+        call(t, evs[t])
+    torch.cuda.synchronize()
+    k_ms = sum(hev.elapsed_ms(a, b) for a, b in evs) / n_ev
+    hev.close()
+    alg_bytes = decode_cost(w)
+    ach = alg_bytes / (k_ms * 1e-3) / 1e9
+    return {
+        "metric": "SSD decode tokens/sec at 1 MI355X + % of HBM roofline",
+        "value": round(w.batch * w.steps / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": w.steps,
+        "warmup": W, "ms_per_step": round(ms / w.steps, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) state/x/B/C/dt per step)",
-        "config": {"workload": w.name, "batch": B, "nheads": H, "headdim": P, "dstate": N, "ngroups": G},
+        "config": {"workload": w.name, "batch": w.batch, "nheads": w.nheads, "headdim": w.headdim,
+                   "dstate": w.dstate, "ngroups": w.ngroups, "calls": w.steps},
         "roofline": {"kernel": "ssd_step", "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
                      "traffic": load_traffic(workload_slug(w.name), "ssd_step"),
-                     "alg_bytes_per_launch": alg_bytes},
+                     "kernel_us": round(k_ms * 1e3, 3), "alg_bytes_per_launch": alg_bytes},
         "wall_s_timed_region": round(wall, 4),
     }
-    hev.close()
-    emit(args, dev, out)
 
 
 BWD_STAGES = ["chunk_state", "state_passing", "gate_fwd", "gate_bwd", "chunk_state_grad",
@@ -216,7 +260,7 @@ def backward_cost(w):
     return cost
 
 
-def run_bwd(w, args, dev):
+def run_bwd(w, args, dev, opts=None):
     """The backward workload: K ssd_bwd calls over one resident batch (HIP graph replay);
     per-kernel durations from an eager pass with the library's stage events."""
     inp = {k: v.to(dev) for k, v in I.make_workload_inputs(w).items()}
@@ -237,7 +281,7 @@ def run_bwd(w, args, dev):
     def step(i, evs=None):
         c, dy, o = copies[i % R]
         ssd.ssd_bwd(c["x"], c["dt"], c["dt_bias"], c["A"], c["B"], c["C"], dy, D=c["D"],
-                    chunk_size=w.chunk, dfinal_state=dfin, workspace=ws, out=o, stage_events=evs)
+                    chunk_size=w.chunk, dfinal_state=dfin, workspace=ws, out=o, stage_events=evs, opts=opts)
 
     K, W = args.steps, args.warmup
     for i in range(W):
@@ -304,7 +348,7 @@ def run_bwd(w, args, dev):
         "wall_s_timed_region": round(wall, 4),
     }
     hev.close()
-    emit(args, dev, res)
+    return res
 
 
 def peak_probe(dev):
@@ -371,7 +415,7 @@ def copy_probe(args, dev):
         torch.cuda.synchronize()
 
 
-def run_conv(w, args, dev):
+def run_conv(w, args, dev, opts=None):
     """The conv workload: K launches of conv1d_silu over one resident batch (HIP graph replay),
     the carried conv state written every launch."""
     c = I.make_conv_inputs(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.width, w.dtype,
@@ -381,7 +425,7 @@ def run_conv(w, args, dev):
 
     def step():
         ssd.conv1d_silu(c["xbc"], c["weight"], c["bias"], H, P, N, G, conv_state=c["conv_state"],
-                        conv_state_out=st_out, x=x, B=B, C=C)
+                        conv_state_out=st_out, x=x, B=B, C=C, opts=opts)
 
     K, W = args.steps, args.warmup
     for _ in range(W):
@@ -430,16 +474,149 @@ def run_conv(w, args, dev):
         "launch": "hip_graph" if use_graph else "eager",
         "wall_s_timed_region": round(wall, 4),
     }
-    emit(args, dev, out)
+    return out
+
+
+def fwd_summary(out):
+    """The fields of a forward or decode line that the configs array keeps."""
+    r = out["roofline"]
+    return {"workload": out["config"]["workload"], "dtype": out["dtype"], "value": out["value"],
+            "unit": out["unit"], "ms_per_step": out["ms_per_step"],
+            "roofline": {k: r[k] for k in ("kernel", "bound", "achieved", "peak", "unit", "frac")}}
+
+
+def run_fwd(w, args, dev, opts, with_cpu):
+    """K ssd_fwd calls over one batch (HIP graph replay), per-kernel durations from an eager pass
+    of the same calls with dispatch-recorded events."""
+    inp = I.make_workload_inputs(w)
+    d = {k: v.to(dev) for k, v in inp.items()}
+    y = torch.empty_like(d["x"])
+    # Consecutive steps read and write rotating copies of the per-token tensors (x, dt, B, C,
+    # y), enough of them to exceed the 256 MB last-level cache twice, so that every step reads
+    # its inputs from HBM as a fresh batch would
+    per_copy = sum(d[k].numel() * d[k].element_size() for k in ("x", "dt", "B", "C")) + y.numel() * y.element_size()
+    R = max(1, -(-2 * args.rotate_mb * 2**20 // per_copy)) if args.rotate_mb > 0 else 1
+    copies = [{**d, "y": y}] + [{**d, **{k: d[k].clone() for k in ("x", "dt", "B", "C")}, "y": torch.empty_like(y)}
+                               for _ in range(R - 1)]
+    state = torch.empty(w.batch, w.nheads, w.headdim, w.dstate, dtype=torch.float32, device=dev)
+    dims = ssd.make_dims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, d["x"].dtype)
+    ws = torch.empty(max(1, ssd.ssd_fwd_workspace_size(dims, w.chunk)), dtype=torch.uint8, device=dev)
+
+    K, W = args.steps, args.warmup
+    use_graph = not args.no_graph
+    hev = HipEvents()
+    events = [[hev.create() for _ in range(6)] for _ in range(max(K, 1))]
+    t_start, t_end = hev.create(), hev.create()
+
+    def step(i, evs=None):
+        # launches go to the current stream (the capture stream while a graph is captured)
+        c = copies[i % R]
+        ssd.ssd_fwd(c["x"], c["dt"], c["dt_bias"], c["A"], c["B"], c["C"], c["D"], chunk_size=w.chunk,
+                    y=c["y"], final_state=state, workspace=ws, stage_events=evs, opts=opts)
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    if use_graph:
+        # the K steps are captured once into a HIP graph; the timed region is one replay
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(K):
+                step(W + i)
+        torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    hev.record(t_start)
+    if use_graph:
+        graph.replay()
+    else:
+        for i in range(K):
+            step(W + i)
+    hev.record(t_end)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = hev.elapsed_ms(t_start, t_end) / K
+
+    # Per-kernel durations: the same K steps launched eagerly, each kernel timed by a start /
+    # stop event pair recorded by its own dispatch (ssd_fwd_ex).  Timing events cannot live
+    # inside a captured graph on this runtime.
+    for i in range(K):
+        step(W + i, events[i])
+    torch.cuda.synchronize()
+
+    # the one-pass chunk-state path launches no state_passing (its event pair brackets nothing)
+    one_pass = ssd.fwd_state_path(dims, w.chunk, opts) == 2
+    names = ["chunk_state_seq", None, "chunk_scan"] if one_pass else KERNELS
+    per_kernel_ms = {k: 0.0 for k in names if k}
+    for evs in events[:K]:
+        for i, k in enumerate(names):
+            if k:
+                per_kernel_ms[k] += hev.elapsed_ms(evs[2 * i], evs[2 * i + 1]) / K
+
+    cost = algorithmic_cost(w)
+    kernels = {}
+    for k in per_kernel_ms:
+        t = per_kernel_ms[k] * 1e-3
+        c = cost[k]
+        if c["bound"] == "mfma":
+            ach, peak, unit = c["flops"] / t / 1e12, MFMA_PEAK_TFLOPS[w.dtype], "TFLOP/s"
+        else:
+            ach, peak, unit = c["bytes"] / t / 1e9, HBM_PEAK_GBS, "GB/s"
+        kernels[k] = {"us": round(per_kernel_ms[k] * 1e3, 3), "bound": c["bound"], "achieved": round(ach, 2),
+                      "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
+                      "alg_bytes": c["bytes"], "alg_flops": c["flops"]}
+    dom = max(kernels, key=lambda k: per_kernel_ms[k])
+    kd = kernels[dom]
+    # measured HBM bytes per launch of the dominant kernel (FETCH_SIZE + WRITE_SIZE runs,
+    # calibrated on a plain copy); None when absent or taken on different kernel sources
+    roofline = {"kernel": dom, "bound": kd["bound"], "achieved": kd["achieved"], "peak": kd["peak"],
+                "unit": kd["unit"], "frac": kd["frac"], "traffic": load_traffic(workload_slug(w.name), dom)}
+    tokens = w.batch * w.seqlen
+    out = {
+        "metric": "SSD scan tokens/sec at 1 MI355X + % of MFMA/HBM roofline",
+        "value": round(tokens / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) x/B/C/dt, log-uniform dt bias, A=-U[1,16])",
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads,
+                   "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups, "chunk_size": w.chunk,
+                   "tokens_per_step": tokens},
+        "roofline": roofline,
+        "kernels": kernels,
+        "launch": ("hip_graph (per-kernel times from an eager pass of the same K steps)" if use_graph
+                   else "eager"),
+        "input_copies": R,
+        "wall_s_timed_region": round(wall, 4),
+    }
+    hev.close()
+    if with_cpu:
+        out["cpu_baseline"], out["parity_sample"] = cpu_baseline(w, inp, copies[(W + K - 1) % R]["y"], args.cpu_budget)
+    return out
+
+
+def launch_options(args):
+    o = {k: getattr(args, k) for k in ("scan_variant", "heads_per_block", "rows_group", "state_path",
+                                       "state_slice", "conv_tokens") if getattr(args, k)}
+    return o or None
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the configs array (the other four workloads) after the headline")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch the timed steps eagerly, not as a HIP graph")
     ap.add_argument("--rotate-mb", type=int, default=256,
@@ -464,158 +641,32 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              f"(see the sharding design for more GPUs)", file=sys.stderr)
+              f"(the sharding across GPUs is a design, not built)", file=sys.stderr)
         sys.exit(2)
     w = I.workload(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    opts = launch_options(args)
     if w.entry == "step":
-        run_decode(w, args, dev)
-        return
-    if w.entry == "bwd":
-        run_bwd(w, args, dev)
-        return
-    if w.entry == "conv":
-        if args.conv_tokens:
-            ssd.tune_set(3, args.conv_tokens)
-        run_conv(w, args, dev)
-        return
-    if args.heads_per_block:
-        ssd.tune_set(0, args.heads_per_block)
-    if args.scan_variant:
-        ssd.tune_set(2, args.scan_variant)
-    if args.rows_group:
-        ssd.tune_set(4, args.rows_group)
-    if args.state_path:
-        ssd.tune_set(5, args.state_path)
-    if args.state_slice:
-        ssd.tune_set(6, args.state_slice)
-
-    inp = I.make_workload_inputs(w)
-    dec = I.make_step_inputs(w.batch, w.nheads, w.headdim, w.dstate, w.ngroups, 1, w.dtype,
-                             seed=1000 + w.seed, d_init=w.d_init, device="cpu")
-    d = {k: v.to(dev) for k, v in inp.items()}
-    dd = {k: v[0].contiguous().to(dev) for k, v in dec.items() if k in ("x", "dt", "B", "C")}
-    y = torch.empty_like(d["x"])
-    # Consecutive steps read and write rotating copies of the per-token tensors (x, dt, B, C,
-    # y), enough of them to exceed the 256 MB last-level cache twice, so that every step reads
-    # its inputs from HBM as a fresh batch would
-    per_copy = sum(d[k].numel() * d[k].element_size() for k in ("x", "dt", "B", "C")) + y.numel() * y.element_size()
-    R = max(1, -(-2 * args.rotate_mb * 2**20 // per_copy)) if args.rotate_mb > 0 else 1
-    copies = [{**d, "y": y}] + [{**d, **{k: d[k].clone() for k in ("x", "dt", "B", "C")}, "y": torch.empty_like(y)}
-                               for _ in range(R - 1)]
-    state = torch.empty(w.batch, w.nheads, w.headdim, w.dstate, dtype=torch.float32, device=dev)
-    y_dec = torch.empty_like(dd["x"])
-    dims = ssd.make_dims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, d["x"].dtype)
-    ws = torch.empty(ssd.ssd_fwd_workspace_size(dims, w.chunk), dtype=torch.uint8, device=dev)
-
-    K, W = args.steps, args.warmup
-    use_graph = not args.no_graph
-    hev = HipEvents()
-    nev = 8   # start / stop of the forward's three kernels (from their dispatches), 2 around ssd_step
-    events = [[hev.create() for _ in range(nev)] for _ in range(max(K, 1))]
-    t_start, t_end = hev.create(), hev.create()
-
-    def step(i, evs=None):
-        # launches go to the current stream (the capture stream while a graph is captured)
-        c = copies[i % R]
-        ssd.ssd_fwd(c["x"], c["dt"], c["dt_bias"], c["A"], c["B"], c["C"], c["D"], chunk_size=w.chunk,
-                    y=c["y"], final_state=state, workspace=ws, stage_events=None if evs is None else evs[:6])
-        if evs is not None:
-            hev.record(evs[6])
-        ssd.ssd_step(state, dd["x"], dd["dt"], d["dt_bias"], d["A"], dd["B"], dd["C"], d["D"], y=y_dec)
-        if evs is not None:
-            hev.record(evs[7])
-
-    for i in range(W):
-        step(i)
-    torch.cuda.synchronize()
-    if use_graph:
-        # the K steps are captured once into a HIP graph; the timed region is one replay
-        graph = torch.cuda.CUDAGraph()
-        cap = torch.cuda.Stream()
-        cap.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.graph(graph, stream=cap):
-            for i in range(K):
-                step(W + i)
-        torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    hev.record(t_start)
-    if use_graph:
-        graph.replay()
+        out = run_decode(w, args, dev)
+    elif w.entry == "bwd":
+        out = run_bwd(w, args, dev, opts)
+    elif w.entry == "conv":
+        out = run_conv(w, args, dev, opts)
     else:
-        for i in range(K):
-            step(W + i)
-    hev.record(t_end)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = hev.elapsed_ms(t_start, t_end)
-    ms_per_step = total_ms / K
-
-    # Per-kernel durations: the same K steps launched eagerly, each forward kernel timed by a
-    # start / stop event pair recorded by its own dispatch (ssd_fwd_timed); ssd_step between
-    # two stream events.  Timing events cannot live inside a captured graph on this runtime.
-    for i in range(K):
-        step(W + i, events[i])
-    torch.cuda.synchronize()
-
-    # the one-pass chunk-state path launches no state_passing (its event pair brackets nothing)
-    one_pass = ssd.fwd_state_path(dims, w.chunk) == 2
-    names = ["chunk_state_seq", None, "chunk_scan", "ssd_step"] if one_pass else KERNELS
-    per_kernel_ms = {k: 0.0 for k in names if k}
-    pairs = [(0, 1), (2, 3), (4, 5), (6, 7)]
-    for evs in events[:K]:
-        for k, (a, b) in zip(names, pairs):
-            if k:
-                per_kernel_ms[k] += hev.elapsed_ms(evs[a], evs[b]) / K
-
-    cost = algorithmic_cost(w)
-    kernels = {}
-    for k in per_kernel_ms:
-        t = per_kernel_ms[k] * 1e-3
-        c = cost[k]
-        if c["bytes"] == 0 and c["flops"] == 0:       # not launched for this dtype
-            continue
-        if c["bound"] == "mfma":
-            ach, peak, unit = c["flops"] / t / 1e12, MFMA_PEAK_TFLOPS[w.dtype], "TFLOP/s"
-        else:
-            ach, peak, unit = c["bytes"] / t / 1e9, HBM_PEAK_GBS, "GB/s"
-        kernels[k] = {"us": round(per_kernel_ms[k] * 1e3, 3), "bound": c["bound"], "achieved": round(ach, 2),
-                      "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
-                      "alg_bytes": c["bytes"], "alg_flops": c["flops"]}
-    dom = max(kernels, key=lambda k: per_kernel_ms[k])
-    kd = kernels[dom]
-    # measured HBM bytes per launch of the dominant kernel (FETCH_SIZE + WRITE_SIZE runs,
-    # calibrated on a plain copy); None when absent or taken on different kernel sources
-    roofline = {"kernel": dom, "bound": kd["bound"], "achieved": kd["achieved"], "peak": kd["peak"],
-                "unit": kd["unit"], "frac": kd["frac"], "traffic": load_traffic(workload_slug(w.name), dom)}
-
-    tokens = w.batch * (w.seqlen + 1)
-    out = {
-        "metric": "SSD scan tokens/sec at 1 MI355X + % of MFMA/HBM roofline",
-        "value": round(tokens / (ms_per_step * 1e-3), 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": w.dtype,
-        "data": "synthetic (seeded N(0,1) x/B/C/dt, log-uniform dt bias, A=-U[1,16])",
-        "config": {"workload": w.name + " + 1 decode token", "batch": w.batch, "seqlen": w.seqlen,
-                   "nheads": w.nheads, "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
-                   "chunk_size": w.chunk, "tokens_per_step": tokens},
-        "roofline": roofline,
-        "kernels": kernels,
-        "launch": ("hip_graph (per-kernel times from an eager pass of the same K steps)" if use_graph
-                   else "eager"),
-        "input_copies": R,
-        "wall_s_timed_region": round(wall, 4),
-    }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, inp, dec, args.cpu_budget)
+        out = run_fwd(w, args, dev, opts, with_cpu=not args.no_cpu_baseline)
+        if w.name == DEFAULT_WORKLOAD and not args.no_configs:
+            # the other four specified workloads, each timed the same way (built-in launch choice)
+            configs = []
+            for cw in I.WORKLOAD_LIST[:5]:
+                if cw.name == w.name:
+                    configs.append(fwd_summary(out))
+                elif cw.entry == "step":
+                    configs.append(fwd_summary(run_decode(cw, args, dev)))
+                else:
+                    configs.append(fwd_summary(run_fwd(cw, args, dev, None, with_cpu=False)))
+                torch.cuda.empty_cache()
+            out["configs"] = configs
     emit(args, dev, out)
 
 

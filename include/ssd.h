@@ -77,7 +77,7 @@ typedef struct {
  *   [2] states (B, nc, H, P, N) fp32       first the state each chunk contributes (decayed to
  *                                          the chunk end), then overwritten in place by the
  *                                          state entering each chunk; on the one-pass path
- *                                          (ssd_tuning.h, ssd_fwd_state_path) fp32 inputs get
+ *                                          (ssd_fwd_state_path in ssd_tuning.h) fp32 inputs get
  *                                          the entering states only and bf16 inputs leave it
  *                                          unwritten
  *   [3] SSD_F32, and SSD_BF16 with at least 20 heads per group: C B^T, computed once per
@@ -96,7 +96,8 @@ size_t ssd_fwd_workspace_size(const ssd_dims_t* dims, int chunk_size);
  * in-chunk cumsum and the chunk states; where region [3] exists also C B^T once per group),
  * state_passing, chunk_scan.  For SSD_BF16 with P = 64, N = 128 and batch x nheads >= 256 the
  * first two are one kernel instead (chunk_state_seq: one pass over the chunks per (b, h) with
- * the carried state in registers); ssd_fwd_state_path in ssd_tuning.h tells which.
+ * the carried state in registers); ssd_fwd_state_path in ssd_tuning.h tells which.  The choice
+ * is a pure function of the arguments (ssd_fwd_ex in ssd_tuning.h takes explicit options).
  *   x             (B, L, H, P)  dtype       input sequence
  *   dt            (B, L, H)     dtype       raw step, before bias and softplus
  *   dt_bias, A    (H)           fp32        A is used as given (pass negative values)
@@ -114,23 +115,6 @@ ssd_status_t ssd_fwd(const ssd_dims_t* dims,
                      const void* B, const void* C, const float* D, const void* z, int chunk_size,
                      const float* initial_state, void* y, float* final_state,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
-
-/* ssd_fwd with per-kernel timing: identical arguments and results, plus `stage_events`,
- * an array of 6 events created by the caller (hipEventCreate): stage_events[2k] and
- * [2k + 1] are the start and stop of kernel k (0 chunk_state, 1 state_passing, 2 chunk_scan),
- * recorded by the kernel's own dispatch (hipExtLaunchKernelGGL), so hipEventElapsedTime of a
- * pair is that kernel's execution time alone, as in a profiler's kernel trace.  On the one-pass
- * path kernel 0 is chunk_state_seq and the state_passing pair is recorded back to back around
- * no kernel.  Event records
- * cannot be captured into a graph: with non-NULL stage_events on a stream under capture the
- * call returns SSD_ERR_UNSUPPORTED and launches nothing.  For measurement tools; NULL
- * stage_events behaves exactly like ssd_fwd (which may be captured). */
-ssd_status_t ssd_fwd_timed(const ssd_dims_t* dims,
-                           const void* x, const void* dt, const float* dt_bias, const float* A,
-                           const void* B, const void* C, const float* D, const void* z, int chunk_size,
-                           const float* initial_state, void* y, float* final_state,
-                           void* workspace, size_t workspace_bytes, hipStream_t stream,
-                           hipEvent_t* stage_events);
 
 /* One recurrent decode step for every (b, h) ("MAMBA2 Inference Optimization Report", Step 4:
  * the carried hidden state; same discretisation as ssd_fwd).  dims->seqlen is ignored.
@@ -166,8 +150,9 @@ size_t ssd_bwd_workspace_size(const ssd_dims_t* dims, int chunk_size, int with_g
  *   dinitial_state (B, H, P, N) fp32 or NULL (not wanted)
  * ddt is the gradient with respect to the raw dt (before bias and softplus); it is zero where
  * the clamp binds.  Results are deterministic (fixed-order reductions, no atomics).
- * batch == 0 is a no-op; seqlen == 0 writes dinitial_state = dfinal_state (or zeros) and zero
- * ddt_bias, dA, dD.  Nine kernels (two more with a gate). */
+ * With no tokens (batch == 0 or seqlen == 0) ddt_bias, dA and dD are written as zeros and
+ * dinitial_state = dfinal_state (or zeros); the per-token tensors may then be NULL, and so may
+ * the workspace when ssd_bwd_workspace_size() is 0.  Nine kernels (two more with a gate). */
 ssd_status_t ssd_bwd(const ssd_dims_t* dims,
                      const void* x, const void* dt, const float* dt_bias, const float* A,
                      const void* B, const void* C, const float* D, const void* z, int chunk_size,
@@ -175,23 +160,6 @@ ssd_status_t ssd_bwd(const ssd_dims_t* dims,
                      void* dx, void* ddt, float* ddt_bias, float* dA, void* dB, void* dC, float* dD,
                      void* dz, float* dinitial_state,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
-
-/* ssd_bwd with per-kernel timing: identical arguments and results, plus `stage_events`, an
- * array of 20 caller-created events: [2k] and [2k + 1] are the start and stop of stage k,
- * recorded by the dispatches themselves: 0 chunk_state, 1 state_passing (forward
- * recompute), 2 chunk_scan of the pre-gate output and 3 the gate's backward (both recorded
- * back to back, i.e. empty, without a gate), 4 chunk_state of the output gradients,
- * 5 reverse state_passing, 6 the anti-causal kernel, 7 the causal kernel, 8 finalize,
- * 9 the two reduction kernels.  Like ssd_fwd_timed it refuses a stream under graph
- * capture (SSD_ERR_UNSUPPORTED, nothing launched). */
-ssd_status_t ssd_bwd_timed(const ssd_dims_t* dims,
-                           const void* x, const void* dt, const float* dt_bias, const float* A,
-                           const void* B, const void* C, const float* D, const void* z, int chunk_size,
-                           const float* initial_state, const void* dout, const float* dfinal_state,
-                           void* dx, void* ddt, float* ddt_bias, float* dA, void* dB, void* dC, float* dD,
-                           void* dz, float* dinitial_state,
-                           void* workspace, size_t workspace_bytes, hipStream_t stream,
-                           hipEvent_t* stage_events);
 
 /* Causal depthwise conv1d + SiLU that produces the scan's x, B and C ("Agent 228: MAMBA-2
  * Implementation Gaps", Gap 2: one filter of width K = conv_width per channel, causal padding

@@ -4,5 +4,5 @@
 """
 from .ssd import (  # noqa: F401
     SsdError, conv1d_silu, conv1d_silu_step, load_library, make_dims, ssd_bwd, ssd_bwd_workspace_size, ssd_fwd,
-    ssd_fwd_workspace_size, ssd_status_string, ssd_step, tune_set,
+    ssd_fwd_workspace_size, ssd_status_string, ssd_step, launch_opts, fwd_state_path,
 )

@@ -90,18 +90,9 @@ bool device_ptr_ok(const void* p) {
   return attr.type == hipMemoryTypeManaged;
 }
 
-// chunk_scan launch shape.  Two decompositions: 64-row blocks (many small workgroups: x
-// tiles and the carried state are re-read per row block, which suits compute-bound fp32)
-// and whole chunks (every input and output moves once: memory-bound bf16).  Heads of one
-// group share each C B^T evaluation inside a workgroup; more heads per workgroup amortise it
-// further but leave fewer workgroups to fill 256 CUs.
-int g_tune_heads_per_block = 0;  // 0 = heuristic
-int g_tune_min_blocks = 512;
-int g_tune_scan_variant = 0;     // 0 = built-in (row blocks)
-int g_tune_conv_segment = 0;     // 0 = sized to the chip
-int g_tune_rows_group = 0;       // units per row-block dispatch group (0 = built-in, 16)
-int g_tune_state_seq = 0;        // 0 = built-in, 1 = chunk_state + state_passing, 2 = one pass
-int g_tune_state_seq_ps = 0;     // headdim rows per one-pass workgroup (0 = built-in)
+// Launch choices: pure functions of the sizes and the caller's options (NULL = built-in).
+const ssd_launch_opts_t kBuiltin{};
+const ssd_launch_opts_t& opts_or_builtin(const ssd_launch_opts_t* o) { return o ? *o : kBuiltin; }
 
 // Chunk states: either per (b, c, h) in parallel followed by the sequential state_passing
 // launch, or one pass per (b, h, headdim slice) walking the chunks in order with the state in
@@ -112,15 +103,16 @@ int g_tune_state_seq_ps = 0;     // headdim rows per one-pass workgroup (0 = bui
 // against 0.172 ms; B2 L16384 H80 G8 0.793 against 0.823: too few workgroups for 256 CUs, each
 // with a long chain of chunks); fp32 keeps two launches (B4 L1024 H24 0.0695 against 0.0765 ms
 // at 32-row slices, B16 L1024 H24 0.230 against 0.228 at whole rows).
-int pick_state_seq(int dtype, int64_t B, int64_t H, int P, int N, int Q, bool forward_only) {
-  if (g_tune_state_seq == 1 || !forward_only) return 0;
+int pick_state_seq(int dtype, int64_t B, int64_t H, int P, int N, int Q, bool forward_only,
+                   const ssd_launch_opts_t& o) {
+  if (o.state_path == 1 || !forward_only) return 0;
   ssd::FwdArgs a{};
   a.dtype = dtype;
   a.P = P;
   a.N = N;
   a.Q = Q;
-  if (g_tune_state_seq == 2) {
-    const int ps = g_tune_state_seq_ps > 0 ? g_tune_state_seq_ps : P;
+  if (o.state_path == 2) {
+    const int ps = o.state_slice > 0 ? o.state_slice : P;
     return ssd::chunk_state_seq_supported(a, ps) ? ps : 0;
   }
   if (dtype != ssd::DT_BF16 || P != 64 || N != 128 || B * H < 256) return 0;
@@ -130,37 +122,44 @@ int pick_state_seq(int dtype, int64_t B, int64_t H, int P, int N, int Q, bool fo
 // Row-block dispatch groups of 16 units per XCD: measured on MI355X, bf16 B2 L16384 H80 G8
 // chunk_scan 514 -> 432 us (the row blocks of a unit re-read its x tiles and entering state
 // from L2 instead of HBM); B8 L4096 H32 and fp32 B4 L1024 unchanged within noise.
-int pick_rows_group() { return g_tune_rows_group > 0 ? g_tune_rows_group : 16; }
+int pick_rows_group(const ssd_launch_opts_t& o) { return o.rows_group > 0 ? o.rows_group : 16; }
 
-// Row blocks for both dtypes: measured on MI355X, fp32 B4 L1024 H24 39 us against 68 us for
-// whole chunks; bf16 B8 L4096 H32 N128 191 us against 208 us (bf16 B2 L16384 H80 G8: 545 us
-// against 519 us, the one shape measured where whole chunks win).
-int pick_scan_variant(int dtype) {
+// chunk_scan decomposition.  Two: 64-row blocks (many small workgroups: x tiles and the
+// carried state are re-read per row block, from L2 when dispatched in groups) and whole chunks
+// (every input and output moves once).  Row blocks for both dtypes: measured on MI355X, fp32
+// B4 L1024 H24 39 us against 68 us for whole chunks; bf16 B8 L4096 H32 N128 191 us against
+// 208 us (bf16 B2 L16384 H80 G8: 545 us against 519 us, the one shape measured where whole
+// chunks win).
+int pick_scan_variant(int dtype, const ssd_launch_opts_t& o) {
   (void)dtype;
-  if (g_tune_scan_variant == 1 || g_tune_scan_variant == 2) return g_tune_scan_variant;
+  if (o.scan_variant == 1 || o.scan_variant == 2) return o.scan_variant;
   return 1;
 }
 
-int pick_heads_per_block(int B, int nc, int H, int G, int Q, int variant) {
+// Heads of one group sharing one C B^T evaluation inside a workgroup; more heads per workgroup
+// amortise it further but leave fewer workgroups to fill 256 CUs.
+int pick_heads_per_block(int B, int nc, int H, int G, int variant, const ssd_launch_opts_t& o) {
   static const int kChoices[] = {2, 1};  // instantiated head-block sizes
   const int hpg = H / G;
-  if (g_tune_heads_per_block > 0) {
+  if (o.heads_per_block > 0) {
     for (int hb : kChoices)
-      if (hb == g_tune_heads_per_block && hpg % hb == 0) return hb;
+      if (hb == o.heads_per_block && hpg % hb == 0) return hb;
   }
   // row blocks: one head per workgroup (a second head's accumulators would halve occupancy)
   if (variant == 1) return 1;
   // whole chunks: the largest head block that still leaves enough workgroups
   const long per_head = (long)B * nc * G;
+  const long min_blocks = o.min_blocks > 0 ? o.min_blocks : 512;
   for (int hb : kChoices)
-    if (hpg % hb == 0 && per_head * (hpg / hb) >= g_tune_min_blocks) return hb;
+    if (hpg % hb == 0 && per_head * (hpg / hb) >= min_blocks) return hb;
   return 1;
 }
 
 ssd_status_t fwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, const float* dt_bias,
                       const float* A, const void* B, const void* C, const float* D, const void* z,
                       int chunk_size, const float* initial_state, void* y, float* final_state, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream, hipEvent_t* ev) {
+                      size_t workspace_bytes, hipStream_t stream, const ssd_launch_opts_t* opts, hipEvent_t* ev) {
+  const ssd_launch_opts_t& o = opts_or_builtin(opts);
   ssd_status_t st = check_dims(dims, true);
   if (st != SSD_OK) return st;
   if (!chunk_ok(chunk_size)) return SSD_ERR_UNSUPPORTED;
@@ -228,9 +227,9 @@ ssd_status_t fwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   a.cbT = nullptr;
   a.prev16 = has_seq && dims->dtype == SSD_BF16 ? static_cast<void*>(ws + wl.prev16_off) : nullptr;
   a.keep_f32_states = 0;
-  a.scan_variant = pick_scan_variant(a.dtype);
-  a.rows_group = pick_rows_group();
-  a.heads_per_block = pick_heads_per_block(a.B, a.nc, a.H, a.G, a.Q, a.scan_variant);
+  a.scan_variant = pick_scan_variant(a.dtype, o);
+  a.rows_group = pick_rows_group(o);
+  a.heads_per_block = pick_heads_per_block(a.B, a.nc, a.H, a.G, a.scan_variant, o);
   a.state_from_start = 0;
   a.passing_reverse = 0;
   a.ev0 = a.ev1 = nullptr;
@@ -249,7 +248,7 @@ ssd_status_t fwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
     a.ev0 = ev ? ev[2 * k] : nullptr;
     a.ev1 = ev ? ev[2 * k + 1] : nullptr;
   };
-  if (const int ps = pick_state_seq(a.dtype, a.B, a.H, a.P, a.N, a.Q, !a.keep_f32_states && !a.state_from_start)) {
+  if (const int ps = pick_state_seq(a.dtype, a.B, a.H, a.P, a.N, a.Q, !a.keep_f32_states && !a.state_from_start, o)) {
     stage(0);
     if (ssd::launch_chunk_state_seq(a, ps, stream) != hipSuccess) return SSD_ERR_HIP;
     // no state_passing launch: its event pair brackets nothing
@@ -308,14 +307,16 @@ ssd_status_t bwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
                       const void* B, const void* C, const float* D, const void* z, int chunk_size,
                       const float* initial_state, const void* dout, const float* dfinal_state, void* dx, void* ddt,
                       float* ddt_bias, float* dA, void* dB, void* dC, float* dD, void* dz, float* dinitial_state,
-                      void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* ev) {
+                      void* workspace, size_t workspace_bytes, hipStream_t stream, const ssd_launch_opts_t* opts,
+                      hipEvent_t* ev) {
+  const ssd_launch_opts_t& o = opts_or_builtin(opts);
   ssd_status_t st = check_dims(dims, true);
   if (st != SSD_OK) return st;
   if (!chunk_ok(chunk_size)) return SSD_ERR_UNSUPPORTED;
   if (!dt_bias || !A || !ddt_bias || !dA) return SSD_ERR_INVALID_ARG;
   if ((z == nullptr) != (dz == nullptr)) return SSD_ERR_INVALID_ARG;   // dz exactly when gated
-  if (dims->batch == 0) return SSD_OK;
-  const bool has_seq = dims->seqlen > 0;
+  // no tokens (seqlen == 0 or batch == 0): only the per-head gradients (zeros) and dinitial_state
+  const bool has_seq = dims->seqlen > 0 && dims->batch > 0;
   const size_t eb = elem_bytes(dims->dtype);
   if (has_seq) {
     if (!x || !dt || !B || !C || !dout || !dx || !ddt || !dB || !dC) return SSD_ERR_INVALID_ARG;
@@ -330,10 +331,14 @@ ssd_status_t bwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
       (dinitial_state && !aligned(dinitial_state, 16)))
     return SSD_ERR_INVALID_ARG;
   const BwdLayout wl = bwd_layout(dims, chunk_size, z != nullptr);
-  if (!workspace || workspace_bytes < wl.total) return SSD_ERR_WORKSPACE;
-  if (!aligned(workspace, 16)) return SSD_ERR_INVALID_ARG;
-  const void* ptrs[] = {x,  dt, dt_bias, A,  B,  C,   D,  z,  initial_state, dout, dfinal_state, dx,
-                        ddt, ddt_bias, dA, dB, dC, dD, dz, dinitial_state, workspace};
+  if (wl.total > 0 && (!workspace || workspace_bytes < wl.total)) return SSD_ERR_WORKSPACE;
+  if (workspace && !aligned(workspace, 16)) return SSD_ERR_INVALID_ARG;
+  const bool has_b = dims->batch > 0;   // per-sequence tensors are empty when batch == 0
+  const void* ptrs[] = {has_seq ? x : nullptr, has_seq ? dt : nullptr, dt_bias, A, has_seq ? B : nullptr,
+                        has_seq ? C : nullptr, D, has_seq ? z : nullptr, has_b ? initial_state : nullptr,
+                        has_seq ? dout : nullptr, has_b ? dfinal_state : nullptr, has_seq ? dx : nullptr,
+                        has_seq ? ddt : nullptr, ddt_bias, dA, has_seq ? dB : nullptr, has_seq ? dC : nullptr, dD,
+                        has_seq ? dz : nullptr, has_b ? dinitial_state : nullptr, wl.total > 0 ? workspace : nullptr};
   for (const void* p : ptrs)
     if (p && !device_ptr_ok(p)) return SSD_ERR_DEVICE_PTR;
   if (ev) {
@@ -379,9 +384,9 @@ ssd_status_t bwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   f.cbT = dims->dtype == SSD_F32 ? reinterpret_cast<float*>(ws + wl.cbT) : nullptr;
   f.prev16 = z && dims->dtype == SSD_BF16 ? static_cast<void*>(ws + wl.prev16) : nullptr;
   f.keep_f32_states = 1;                              // the backward kernels read the fp32 states
-  f.scan_variant = pick_scan_variant(f.dtype);
-  f.rows_group = pick_rows_group();
-  f.heads_per_block = pick_heads_per_block(f.B, f.nc, f.H, f.G, f.Q, f.scan_variant);
+  f.scan_variant = pick_scan_variant(f.dtype, o);
+  f.rows_group = pick_rows_group(o);
+  f.heads_per_block = pick_heads_per_block(f.B, f.nc, f.H, f.G, f.scan_variant, o);
   f.state_from_start = 0;
   f.passing_reverse = 0;
   f.ev0 = f.ev1 = nullptr;
@@ -423,7 +428,7 @@ ssd_status_t bwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   if (!has_seq) {
     for (int k = 0; k < 10; ++k)
       if (!empty_stage(k)) return SSD_ERR_HIP;
-    if (dinitial_state && ssd::launch_state_passing(gp, stream) != hipSuccess) return SSD_ERR_HIP;
+    if (has_b && dinitial_state && ssd::launch_state_passing(gp, stream) != hipSuccess) return SSD_ERR_HIP;
     if (ssd::launch_bwd_reduce(a, stream) != hipSuccess) return SSD_ERR_HIP;   // zero dA, d dt_bias, dD
     return SSD_OK;
   }
@@ -472,10 +477,55 @@ ssd_status_t bwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   return SSD_OK;
 }
 
+// ssd_step (events: start / stop recorded by the kernel's dispatch, or null)
+ssd_status_t step_impl(const ssd_dims_t* dims, float* state, const void* x, const void* dt, const float* dt_bias,
+                       const float* A, const void* B, const void* C, const float* D, const void* z, void* y,
+                       hipStream_t stream, hipEvent_t* ev) {
+  ssd_status_t st = check_dims(dims, false);
+  if (st != SSD_OK) return st;
+  if (dims->batch == 0) return SSD_OK;
+  const size_t eb = elem_bytes(dims->dtype);
+  if (!state || !x || !dt || !dt_bias || !A || !B || !C || !y) return SSD_ERR_INVALID_ARG;
+  if (!aligned(state, 16) || !aligned(x, eb) || !aligned(dt, eb) || !aligned(B, eb) || !aligned(C, eb) ||
+      !aligned(y, eb) || !aligned(dt_bias, 4) || !aligned(A, 4) || (D && !aligned(D, 4)) || (z && !aligned(z, eb)))
+    return SSD_ERR_INVALID_ARG;
+  const void* ptrs[] = {state, x, dt, dt_bias, A, B, C, D, z, y};
+  for (const void* p : ptrs)
+    if (p && !device_ptr_ok(p)) return SSD_ERR_DEVICE_PTR;
+  if (ev) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return SSD_ERR_HIP;
+    if (cs != hipStreamCaptureStatusNone) return SSD_ERR_UNSUPPORTED;
+  }
+  ssd::StepArgs a;
+  a.B = (int)dims->batch;
+  a.H = (int)dims->nheads;
+  a.P = (int)dims->headdim;
+  a.N = (int)dims->dstate;
+  a.G = (int)dims->ngroups;
+  a.dtype = dims->dtype;
+  a.state = state;
+  a.x = x;
+  a.dt = dt;
+  a.dt_bias = dt_bias;
+  a.A = A;
+  a.Bm = B;
+  a.Cm = C;
+  a.D = D;
+  a.z = z;
+  a.clamp = dims->dt_max > 0.f;
+  a.dt_lo = dims->dt_min;
+  a.dt_hi = dims->dt_max;
+  a.y = y;
+  a.ev0 = ev ? ev[0] : nullptr;
+  a.ev1 = ev ? ev[1] : nullptr;
+  return ssd::launch_ssd_step(a, stream) == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
 // Both conv entry points.  `step`: one token per sequence, state updated in place.
 ssd_status_t conv_impl(const ssd_dims_t* dims, int K, const void* xbc, const float* weight, const float* bias,
                        const void* state_in, void* state_out, void* x, void* B, void* C, hipStream_t stream,
-                       bool step) {
+                       bool step, const ssd_launch_opts_t* opts) {
   ssd_status_t st = check_dims(dims, !step);
   if (st != SSD_OK) return st;
   if (K < 1 || K > 4) return SSD_ERR_UNSUPPORTED;
@@ -526,7 +576,7 @@ ssd_status_t conv_impl(const ssd_dims_t* dims, int K, const void* xbc, const flo
   a.x = x;
   a.Bo = B;
   a.Co = C;
-  a.segment = g_tune_conv_segment;
+  a.segment = opts && opts->conv_tokens > 0 ? opts->conv_tokens : 0;
   const hipError_t e = step ? ssd::launch_conv1d_silu_step(a, stream) : ssd::launch_conv1d_silu(a, stream);
   return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
 }
@@ -555,53 +605,28 @@ ssd_status_t ssd_fwd(const ssd_dims_t* dims, const void* x, const void* dt, cons
                      const float* initial_state, void* y, float* final_state, void* workspace,
                      size_t workspace_bytes, hipStream_t stream) {
   return fwd_impl(dims, x, dt, dt_bias, A, B, C, D, z, chunk_size, initial_state, y, final_state, workspace,
-                  workspace_bytes, stream, nullptr);
+                  workspace_bytes, stream, nullptr, nullptr);
 }
 
-ssd_status_t ssd_fwd_timed(const ssd_dims_t* dims, const void* x, const void* dt, const float* dt_bias,
-                           const float* A, const void* B, const void* C, const float* D, const void* z,
-                           int chunk_size, const float* initial_state, void* y, float* final_state,
-                           void* workspace, size_t workspace_bytes, hipStream_t stream,
-                           hipEvent_t* stage_events) {
+ssd_status_t ssd_fwd_ex(const ssd_dims_t* dims, const void* x, const void* dt, const float* dt_bias, const float* A,
+                        const void* B, const void* C, const float* D, const void* z, int chunk_size,
+                        const float* initial_state, void* y, float* final_state, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream, const ssd_launch_opts_t* opts,
+                        hipEvent_t* stage_events) {
   return fwd_impl(dims, x, dt, dt_bias, A, B, C, D, z, chunk_size, initial_state, y, final_state, workspace,
-                  workspace_bytes, stream, stage_events);
+                  workspace_bytes, stream, opts, stage_events);
 }
 
 ssd_status_t ssd_step(const ssd_dims_t* dims, float* state, const void* x, const void* dt, const float* dt_bias,
                       const float* A, const void* B, const void* C, const float* D, const void* z, void* y,
                       hipStream_t stream) {
-  ssd_status_t st = check_dims(dims, false);
-  if (st != SSD_OK) return st;
-  if (dims->batch == 0) return SSD_OK;
-  const size_t eb = elem_bytes(dims->dtype);
-  if (!state || !x || !dt || !dt_bias || !A || !B || !C || !y) return SSD_ERR_INVALID_ARG;
-  if (!aligned(state, 16) || !aligned(x, eb) || !aligned(dt, eb) || !aligned(B, eb) || !aligned(C, eb) ||
-      !aligned(y, eb) || !aligned(dt_bias, 4) || !aligned(A, 4) || (D && !aligned(D, 4)) || (z && !aligned(z, eb)))
-    return SSD_ERR_INVALID_ARG;
-  const void* ptrs[] = {state, x, dt, dt_bias, A, B, C, D, z, y};
-  for (const void* p : ptrs)
-    if (p && !device_ptr_ok(p)) return SSD_ERR_DEVICE_PTR;
-  ssd::StepArgs a;
-  a.B = (int)dims->batch;
-  a.H = (int)dims->nheads;
-  a.P = (int)dims->headdim;
-  a.N = (int)dims->dstate;
-  a.G = (int)dims->ngroups;
-  a.dtype = dims->dtype;
-  a.state = state;
-  a.x = x;
-  a.dt = dt;
-  a.dt_bias = dt_bias;
-  a.A = A;
-  a.Bm = B;
-  a.Cm = C;
-  a.D = D;
-  a.z = z;
-  a.clamp = dims->dt_max > 0.f;
-  a.dt_lo = dims->dt_min;
-  a.dt_hi = dims->dt_max;
-  a.y = y;
-  return ssd::launch_ssd_step(a, stream) == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+  return step_impl(dims, state, x, dt, dt_bias, A, B, C, D, z, y, stream, nullptr);
+}
+
+ssd_status_t ssd_step_ex(const ssd_dims_t* dims, float* state, const void* x, const void* dt, const float* dt_bias,
+                         const float* A, const void* B, const void* C, const float* D, const void* z, void* y,
+                         hipStream_t stream, hipEvent_t* events) {
+  return step_impl(dims, state, x, dt, dt_bias, A, B, C, D, z, y, stream, events);
 }
 
 size_t ssd_bwd_workspace_size(const ssd_dims_t* dims, int chunk_size, int with_gate) {
@@ -615,29 +640,37 @@ ssd_status_t ssd_bwd(const ssd_dims_t* dims, const void* x, const void* dt, cons
                      float* ddt_bias, float* dA, void* dB, void* dC, float* dD, void* dz, float* dinitial_state,
                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return bwd_impl(dims, x, dt, dt_bias, A, B, C, D, z, chunk_size, initial_state, dout, dfinal_state, dx, ddt,
-                  ddt_bias, dA, dB, dC, dD, dz, dinitial_state, workspace, workspace_bytes, stream, nullptr);
+                  ddt_bias, dA, dB, dC, dD, dz, dinitial_state, workspace, workspace_bytes, stream, nullptr, nullptr);
 }
 
-ssd_status_t ssd_bwd_timed(const ssd_dims_t* dims, const void* x, const void* dt, const float* dt_bias,
-                           const float* A, const void* B, const void* C, const float* D, const void* z,
-                           int chunk_size, const float* initial_state, const void* dout,
-                           const float* dfinal_state, void* dx, void* ddt, float* ddt_bias, float* dA, void* dB,
-                           void* dC, float* dD, void* dz, float* dinitial_state, void* workspace,
-                           size_t workspace_bytes, hipStream_t stream, hipEvent_t* stage_events) {
+ssd_status_t ssd_bwd_ex(const ssd_dims_t* dims, const void* x, const void* dt, const float* dt_bias, const float* A,
+                        const void* B, const void* C, const float* D, const void* z, int chunk_size,
+                        const float* initial_state, const void* dout, const float* dfinal_state, void* dx,
+                        void* ddt, float* ddt_bias, float* dA, void* dB, void* dC, float* dD, void* dz,
+                        float* dinitial_state, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                        const ssd_launch_opts_t* opts, hipEvent_t* stage_events) {
   return bwd_impl(dims, x, dt, dt_bias, A, B, C, D, z, chunk_size, initial_state, dout, dfinal_state, dx, ddt,
-                  ddt_bias, dA, dB, dC, dD, dz, dinitial_state, workspace, workspace_bytes, stream, stage_events);
+                  ddt_bias, dA, dB, dC, dD, dz, dinitial_state, workspace, workspace_bytes, stream, opts,
+                  stage_events);
 }
 
 ssd_status_t ssd_conv1d_silu(const ssd_dims_t* dims, int conv_width, const void* xbc, const float* weight,
                              const float* bias, const void* conv_state_in, void* conv_state_out, void* x, void* B,
                              void* C, hipStream_t stream) {
-  return conv_impl(dims, conv_width, xbc, weight, bias, conv_state_in, conv_state_out, x, B, C, stream, false);
+  return conv_impl(dims, conv_width, xbc, weight, bias, conv_state_in, conv_state_out, x, B, C, stream, false,
+                   nullptr);
+}
+
+ssd_status_t ssd_conv1d_silu_ex(const ssd_dims_t* dims, int conv_width, const void* xbc, const float* weight,
+                                const float* bias, const void* conv_state_in, void* conv_state_out, void* x,
+                                void* B, void* C, hipStream_t stream, const ssd_launch_opts_t* opts) {
+  return conv_impl(dims, conv_width, xbc, weight, bias, conv_state_in, conv_state_out, x, B, C, stream, false, opts);
 }
 
 ssd_status_t ssd_conv1d_silu_step(const ssd_dims_t* dims, int conv_width, void* conv_state, const void* xbc,
                                   const float* weight, const float* bias, void* x, void* B, void* C,
                                   hipStream_t stream) {
-  return conv_impl(dims, conv_width, xbc, weight, bias, conv_state, conv_state, x, B, C, stream, true);
+  return conv_impl(dims, conv_width, xbc, weight, bias, conv_state, conv_state, x, B, C, stream, true, nullptr);
 }
 
 const char* ssd_status_string(ssd_status_t s) {
@@ -652,21 +685,12 @@ const char* ssd_status_string(ssd_status_t s) {
   return "unknown status";
 }
 
-int ssd_fwd_state_path(const ssd_dims_t* dims, int chunk_size) {
+int ssd_fwd_state_path(const ssd_dims_t* dims, int chunk_size, const ssd_launch_opts_t* opts) {
   if (check_dims(dims, true) != SSD_OK || !chunk_ok(chunk_size) || dims->seqlen == 0 || dims->batch == 0) return 0;
   const int dtype = dims->dtype == SSD_F32 ? ssd::DT_F32 : ssd::DT_BF16;
-  return pick_state_seq(dtype, dims->batch, dims->nheads, (int)dims->headdim, (int)dims->dstate, chunk_size, true)
+  return pick_state_seq(dtype, dims->batch, dims->nheads, (int)dims->headdim, (int)dims->dstate, chunk_size, true,
+                        opts_or_builtin(opts))
              ? 2 : 1;
-}
-
-void ssd_tune_set(int key, int value) {
-  if (key == 0) g_tune_heads_per_block = value;
-  if (key == 1) g_tune_min_blocks = value > 0 ? value : 512;
-  if (key == 3) g_tune_conv_segment = value > 0 ? value : 0;
-  if (key == 4) g_tune_rows_group = value > 0 ? value : 0;
-  if (key == 2) g_tune_scan_variant = value;
-  if (key == 5) g_tune_state_seq = value;
-  if (key == 6) g_tune_state_seq_ps = value > 0 ? value : 0;
 }
 
 }  // extern "C"

@@ -97,6 +97,7 @@ struct StepArgs {
   float dt_lo, dt_hi;
   int clamp;
   void* y;
+  hipEvent_t ev0, ev1;     // timing events recorded by the dispatch (or null)
 };
 
 // Causal depthwise conv1d + SiLU over xBC = [x | B | C] channels (Dc = dx + 2 dbc).

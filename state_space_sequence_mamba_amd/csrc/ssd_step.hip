@@ -100,7 +100,7 @@ static hipError_t launch_step_impl(const StepArgs& a, hipStream_t s) {
   while (split < 4 && (long)a.B * a.H * split < 1024 && P % (2 * split) == 0 && (P / (2 * split)) % RPP == 0)
     split *= 2;
   const unsigned nblocks = (unsigned)a.B * a.H * split;
-  ssd_step_kernel<T, P, N><<<nblocks, 256, 0, s>>>(
+  hipExtLaunchKernelGGL(ssd_step_kernel<T, P, N>, dim3(nblocks), dim3(256), 0, s, a.ev0, a.ev1, 0,
       a.state, static_cast<const T*>(a.x), static_cast<const T*>(a.dt), a.dt_bias, a.A,
       static_cast<const T*>(a.Bm), static_cast<const T*>(a.Cm), a.D, static_cast<const T*>(a.z),
       static_cast<T*>(a.y), a.H, a.G, a.clamp, a.dt_lo, a.dt_hi, split);

@@ -24,6 +24,31 @@ class ssd_dims_t(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("dt_min", ctypes.c_float), ("dt_max", ctypes.c_float)]
 
 
+class ssd_launch_opts_t(ctypes.Structure):
+    """Launch-shape options of the measurement entry points (include/ssd_tuning.h); 0 = built-in."""
+    _fields_ = [("scan_variant", ctypes.c_int32), ("heads_per_block", ctypes.c_int32),
+                ("min_blocks", ctypes.c_int32), ("rows_group", ctypes.c_int32), ("state_path", ctypes.c_int32),
+                ("state_slice", ctypes.c_int32), ("conv_tokens", ctypes.c_int32)]
+
+
+def launch_opts(**fields):
+    """An ssd_launch_opts_t with the named fields set (every other field 0 = built-in)."""
+    o = ssd_launch_opts_t()
+    for k, v in fields.items():
+        if k not in dict(ssd_launch_opts_t._fields_):
+            raise KeyError(f"unknown launch option {k!r}")
+        setattr(o, k, int(v))
+    return o
+
+
+def _opts_ref(opts):
+    if opts is None:
+        return None
+    if isinstance(opts, dict):
+        opts = launch_opts(**opts)
+    return ctypes.byref(opts)
+
+
 class SsdError(RuntimeError):
     def __init__(self, status, where):
         self.status = status
@@ -48,27 +73,32 @@ def load_library():
     fwd_args = [dims_p, vp, vp, f32p, f32p, vp, vp, f32p, vp, i32, f32p, vp, f32p, vp, sz, vp]
     lib.ssd_fwd.argtypes = fwd_args
     lib.ssd_fwd.restype = i32
-    lib.ssd_fwd_timed.argtypes = fwd_args + [vp]
-    lib.ssd_fwd_timed.restype = i32
-    lib.ssd_step.argtypes = [dims_p, f32p, vp, vp, f32p, f32p, vp, vp, f32p, vp, vp, vp]
+    opts_p = ctypes.POINTER(ssd_launch_opts_t)
+    lib.ssd_fwd_ex.argtypes = fwd_args + [opts_p, vp]
+    lib.ssd_fwd_ex.restype = i32
+    step_args = [dims_p, f32p, vp, vp, f32p, f32p, vp, vp, f32p, vp, vp, vp]
+    lib.ssd_step.argtypes = step_args
     lib.ssd_step.restype = i32
+    lib.ssd_step_ex.argtypes = step_args + [vp]
+    lib.ssd_step_ex.restype = i32
     lib.ssd_bwd_workspace_size.argtypes = [dims_p, i32, i32]
     lib.ssd_bwd_workspace_size.restype = sz
     bwd_args = [dims_p, vp, vp, f32p, f32p, vp, vp, f32p, vp, i32, f32p, vp, f32p,
                 vp, vp, f32p, f32p, vp, vp, f32p, vp, f32p, vp, sz, vp]
     lib.ssd_bwd.argtypes = bwd_args
     lib.ssd_bwd.restype = i32
-    lib.ssd_bwd_timed.argtypes = bwd_args + [vp]
-    lib.ssd_bwd_timed.restype = i32
-    lib.ssd_conv1d_silu.argtypes = [dims_p, i32, vp, f32p, f32p, vp, vp, vp, vp, vp, vp]
+    lib.ssd_bwd_ex.argtypes = bwd_args + [opts_p, vp]
+    lib.ssd_bwd_ex.restype = i32
+    conv_args = [dims_p, i32, vp, f32p, f32p, vp, vp, vp, vp, vp, vp]
+    lib.ssd_conv1d_silu.argtypes = conv_args
     lib.ssd_conv1d_silu.restype = i32
+    lib.ssd_conv1d_silu_ex.argtypes = conv_args + [opts_p]
+    lib.ssd_conv1d_silu_ex.restype = i32
     lib.ssd_conv1d_silu_step.argtypes = [dims_p, i32, vp, vp, f32p, f32p, vp, vp, vp, vp]
     lib.ssd_conv1d_silu_step.restype = i32
     lib.ssd_status_string.argtypes = [i32]
     lib.ssd_status_string.restype = ctypes.c_char_p
-    lib.ssd_tune_set.argtypes = [i32, i32]
-    lib.ssd_tune_set.restype = None
-    lib.ssd_fwd_state_path.argtypes = [dims_p, i32]
+    lib.ssd_fwd_state_path.argtypes = [dims_p, i32, opts_p]
     lib.ssd_fwd_state_path.restype = i32
     _lib = lib
     return lib
@@ -128,13 +158,13 @@ def _check_fwd_shapes(x, dt, dt_bias, A, B, C, D, initial_state, z=None):
 
 def ssd_fwd(x, dt, dt_bias, A, B, C, D=None, chunk_size=256, initial_state=None, y=None,
             final_state=None, return_final_state=True, workspace=None, stream=None, stage_events=None,
-            z=None, dt_limit=None):
+            z=None, dt_limit=None, opts=None):
     """Chunked SSD forward.  Returns (y, final_state) (final_state is None if not requested).
 
     `z` (shape of x) gates the output, y * silu(z); `dt_limit` = (dt_min, dt_max) clamps dt'.
     Output and workspace tensors are allocated with torch when not given.  `stage_events`
-    (6 raw hipEvent_t handles as ints: start and stop of each of the three kernels) selects the
-    timed entry point.
+    (6 raw hipEvent_t handles as ints: start and stop of each of the three kernels) and `opts`
+    (launch options: a dict of ssd_launch_opts_t fields or the struct) select ssd_fwd_ex.
     """
     b, L, H, P, N, G = _check_fwd_shapes(x, dt, dt_bias, A, B, C, D, initial_state, z)
     dims = make_dims(b, L, H, P, N, G, x.dtype, dt_limit)
@@ -149,20 +179,21 @@ def ssd_fwd(x, dt, dt_bias, A, B, C, D=None, chunk_size=256, initial_state=None,
     args = [ctypes.byref(dims), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
             _ptr(z), int(chunk_size), _ptr(initial_state), _ptr(y), _ptr(final_state), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(stream)]
-    if stage_events is None:
+    if stage_events is None and opts is None:
         st = lib.ssd_fwd(*args)
     else:
-        arr = (ctypes.c_void_p * 6)(*stage_events)
-        st = lib.ssd_fwd_timed(*args, arr)
+        arr = None if stage_events is None else (ctypes.c_void_p * 6)(*stage_events)
+        st = lib.ssd_fwd_ex(*args, _opts_ref(opts), arr)
     if st != SSD_OK:
         raise SsdError(st, "ssd_fwd")
     return y, final_state
 
 
-def ssd_step(state, x, dt, dt_bias, A, B, C, D=None, y=None, stream=None, z=None, dt_limit=None):
+def ssd_step(state, x, dt, dt_bias, A, B, C, D=None, y=None, stream=None, z=None, dt_limit=None, events=None):
     """One decode step: updates `state` (B,H,P,N) fp32 in place and returns y (B,H,P).
 
     `z` (B,H,P) gates the output, y * silu(z); `dt_limit` = (dt_min, dt_max) clamps dt'.
+    `events` (2 raw hipEvent_t handles: start and stop of the step's kernel) selects ssd_step_ex.
     """
     if state.dim() != 4 or x.dim() != 3 or dt.dim() != 2 or B.dim() != 3 or C.dim() != 3:
         raise ValueError("state (B,H,P,N), x (B,H,P), dt (B,H), B and C (B,G,N) expected")
@@ -184,8 +215,13 @@ def ssd_step(state, x, dt, dt_bias, A, B, C, D=None, y=None, stream=None, z=None
     dims = make_dims(b, 1, H, P, N, G, x.dtype, dt_limit)
     if y is None:
         y = torch.empty_like(x)
-    st = load_library().ssd_step(ctypes.byref(dims), _ptr(state), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A),
-                                 _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y), _stream(stream))
+    args = [ctypes.byref(dims), _ptr(state), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+            _ptr(z), _ptr(y), _stream(stream)]
+    lib = load_library()
+    if events is None:
+        st = lib.ssd_step(*args)
+    else:
+        st = lib.ssd_step_ex(*args, (ctypes.c_void_p * 2)(*events))
     if st != SSD_OK:
         raise SsdError(st, "ssd_step")
     return y
@@ -197,7 +233,7 @@ def ssd_bwd_workspace_size(dims, chunk_size, with_gate=False):
 
 def ssd_bwd(x, dt, dt_bias, A, B, C, dout, D=None, chunk_size=256, initial_state=None, dfinal_state=None,
             z=None, dt_limit=None, want_dD=True, want_dinitial_state=True, workspace=None, stream=None,
-            out=None, stage_events=None):
+            out=None, stage_events=None, opts=None):
     """Gradients of ssd_fwd.  Returns a dict: dx, ddt, ddt_bias, dA, dB, dC, dD, dz, dinitial_state
     (dD / dz / dinitial_state are None when not requested or not applicable).  `out` reuses a
     previous call's dict as the output buffers; `stage_events` (20 raw hipEvent_t handles as
@@ -225,10 +261,11 @@ def ssd_bwd(x, dt, dt_bias, A, B, C, dout, D=None, chunk_size=256, initial_state
         int(chunk_size), _ptr(initial_state), _ptr(dout), _ptr(dfinal_state), _ptr(out["dx"]), _ptr(out["ddt"]),
         _ptr(out["ddt_bias"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]),
         _ptr(out["dinitial_state"]), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)]
-    if stage_events is None:
+    if stage_events is None and opts is None:
         st = lib.ssd_bwd(*args)
     else:
-        st = lib.ssd_bwd_timed(*args, (ctypes.c_void_p * 20)(*stage_events))
+        arr = None if stage_events is None else (ctypes.c_void_p * 20)(*stage_events)
+        st = lib.ssd_bwd_ex(*args, _opts_ref(opts), arr)
     if st != SSD_OK:
         raise SsdError(st, "ssd_bwd")
     return out
@@ -266,7 +303,7 @@ def _conv_outputs(xbc, lead, nheads, headdim, dstate, ngroups, x, B, C):
 
 
 def conv1d_silu(xbc, weight, bias, nheads, headdim, dstate, ngroups, conv_state=None, conv_state_out=None,
-                return_conv_state=True, x=None, B=None, C=None, stream=None):
+                return_conv_state=True, x=None, B=None, C=None, stream=None, opts=None):
     """Causal depthwise conv1d + SiLU over xbc (B, L, H*P + 2*G*N), split into x, B, C.
 
     weight (Dc, K) and bias (Dc,) are float32; conv_state (B, K-1, Dc) in xbc's dtype holds the
@@ -284,9 +321,10 @@ def conv1d_silu(xbc, weight, bias, nheads, headdim, dstate, ngroups, conv_state=
     if conv_state_out is None and return_conv_state:
         conv_state_out = torch.empty(b, K - 1, Dc, dtype=xbc.dtype, device=xbc.device)
     dims = make_dims(b, L, nheads, headdim, dstate, ngroups, xbc.dtype)
-    st = load_library().ssd_conv1d_silu(ctypes.byref(dims), int(K), _ptr(xbc), _ptr(weight), _ptr(bias),
-                                        _ptr(conv_state), _ptr(conv_state_out), _ptr(x), _ptr(B), _ptr(C),
-                                        _stream(stream))
+    args = [ctypes.byref(dims), int(K), _ptr(xbc), _ptr(weight), _ptr(bias), _ptr(conv_state),
+            _ptr(conv_state_out), _ptr(x), _ptr(B), _ptr(C), _stream(stream)]
+    lib = load_library()
+    st = lib.ssd_conv1d_silu(*args) if opts is None else lib.ssd_conv1d_silu_ex(*args, _opts_ref(opts))
     if st != SSD_OK:
         raise SsdError(st, "ssd_conv1d_silu")
     return x, B, C, conv_state_out
@@ -310,11 +348,6 @@ def conv1d_silu_step(conv_state, xbc, weight, bias, nheads, headdim, dstate, ngr
     return x, B, C
 
 
-def tune_set(key, value):
-    """Launch-shape knob (include/ssd_tuning.h); results depend on it at most by rounding."""
-    load_library().ssd_tune_set(int(key), int(value))
-
-
-def fwd_state_path(dims, chunk_size):
+def fwd_state_path(dims, chunk_size, opts=None):
     """1: chunk_state then state_passing; 2: one pass over the chunks; 0: invalid or empty."""
-    return int(load_library().ssd_fwd_state_path(ctypes.byref(dims), int(chunk_size)))
+    return int(load_library().ssd_fwd_state_path(ctypes.byref(dims), int(chunk_size), _opts_ref(opts)))

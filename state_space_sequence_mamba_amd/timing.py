@@ -1,7 +1,7 @@
 """Raw HIP event handles for the library's per-kernel timing entry point.
 
 The handles are created with the HIP runtime that torch already loaded (same library,
-looked up by its soname) and passed to ssd_fwd_timed.  Measurement plumbing only: nothing
+looked up by its soname) and passed to the *_ex entry points.  Measurement plumbing only: nothing
 here takes part in the scan.
 """
 import ctypes

@@ -37,8 +37,8 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared_functions()
-    assert {"ssd_fwd", "ssd_fwd_timed", "ssd_step", "ssd_fwd_workspace_size", "ssd_status_string",
-            "ssd_tune_set"} <= set(names)
+    assert {"ssd_fwd", "ssd_fwd_ex", "ssd_step", "ssd_step_ex", "ssd_fwd_workspace_size", "ssd_status_string",
+            "ssd_bwd_ex", "ssd_conv1d_silu_ex", "ssd_fwd_state_path"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", ssd.LIB_PATH], capture_output=True, text=True).stdout
@@ -187,7 +187,8 @@ def test_bwd_workspace_size_and_validation(lib):
     assert call(dout=vp(0x100004)) == ssd.SSD_ERR_INVALID_ARG    # not 16-byte aligned
     assert call(ws=None) == ssd.SSD_ERR_WORKSPACE
     assert call(ws_bytes=100) == ssd.SSD_ERR_WORKSPACE
-    assert call(dims=_dims(batch=0)) == ssd.SSD_OK
+    # no tokens: the per-head gradients are still written (zeros), so they must be device memory
+    assert call(dims=_dims(batch=0)) == ssd.SSD_ERR_DEVICE_PTR
 
 
 def test_conv_host_validation(lib):
@@ -236,8 +237,8 @@ def test_product_package_never_imports_the_oracle():
 
 def test_fwd_state_path_choice_is_host_logic():
     """The chunk-state path ssd_fwd takes (pure host logic, no GPU needed): one pass for bf16
-    P64 N128 from batch x heads >= 256, two launches otherwise; the knob forces either where an
-    instantiation exists; invalid or empty sizes give 0."""
+    P64 N128 from batch x heads >= 256, two launches otherwise; per-call options force either where
+    an instantiation exists; invalid or empty sizes give 0."""
     import torch
     bf, f32 = torch.bfloat16, torch.float32
     cases = [((8, 4096, 32, 64, 128, 1, bf), 256, 2), ((8, 4096, 32, 64, 128, 1, bf), 128, 2),
@@ -247,16 +248,12 @@ def test_fwd_state_path_choice_is_host_logic():
              ((8, 4096, 32, 64, 128, 1, bf), 100, 0)]
     for args, q, want in cases:
         assert ssd.fwd_state_path(ssd.make_dims(*args), q) == want, (args, q)
-    try:
-        ssd.tune_set(5, 2)
-        assert ssd.fwd_state_path(ssd.make_dims(4, 1024, 24, 64, 64, 1, f32), 256) == 2
-        ssd.tune_set(6, 32)
-        assert ssd.fwd_state_path(ssd.make_dims(4, 1024, 24, 64, 64, 1, f32), 256) == 2
-        ssd.tune_set(6, 16)          # no such instantiation: two launches
-        assert ssd.fwd_state_path(ssd.make_dims(4, 1024, 24, 64, 64, 1, f32), 256) == 1
-        ssd.tune_set(6, 0)
-        ssd.tune_set(5, 1)
-        assert ssd.fwd_state_path(ssd.make_dims(8, 4096, 32, 64, 128, 1, bf), 256) == 1
-    finally:
-        ssd.tune_set(5, 0)
-        ssd.tune_set(6, 0)
+    p = lambda *a: ssd.make_dims(*a)  # noqa: E731
+    assert ssd.fwd_state_path(p(4, 1024, 24, 64, 64, 1, f32), 256, {"state_path": 2}) == 2
+    assert ssd.fwd_state_path(p(4, 1024, 24, 64, 64, 1, f32), 256, {"state_path": 2, "state_slice": 32}) == 2
+    # no such instantiation: two launches
+    assert ssd.fwd_state_path(p(4, 1024, 24, 64, 64, 1, f32), 256, {"state_path": 2, "state_slice": 16}) == 1
+    assert ssd.fwd_state_path(p(8, 4096, 32, 64, 128, 1, bf), 256, {"state_path": 1}) == 1
+    # options are per call: nothing of the calls above is kept
+    assert ssd.fwd_state_path(p(8, 4096, 32, 64, 128, 1, bf), 256) == 2
+    assert ssd.fwd_state_path(p(4, 1024, 24, 64, 64, 1, f32), 256, ssd.launch_opts()) == 1

@@ -177,6 +177,66 @@ def test_bwd_full_length_bf16_one_row():
     _compare(got, _oracle(inp, dout, dfin), TOL["bf16"])
 
 
+def test_bwd_batch_zero_writes_zero_head_gradients():
+    """No sequences: ddt_bias, dA and dD are still outputs of the call and come back zero."""
+    _say("bwd batch 0")
+    H, P, N = 4, 16, 16
+    x = torch.empty(0, 10, H, P, device=DEV)
+    dt = torch.empty(0, 10, H, device=DEV)
+    Bm = torch.empty(0, 10, 1, N, device=DEV)
+    out = {"dx": torch.empty_like(x), "ddt": torch.empty_like(dt), "dB": torch.empty_like(Bm),
+           "dC": torch.empty_like(Bm), "ddt_bias": torch.full((H,), float("nan"), device=DEV),
+           "dA": torch.full((H,), float("nan"), device=DEV), "dD": torch.full((H, P), float("nan"), device=DEV),
+           "dz": None, "dinitial_state": torch.empty(0, H, P, N, device=DEV)}
+    ssd.ssd_bwd(x, dt, torch.zeros(H, device=DEV), -torch.ones(H, device=DEV), Bm, Bm.clone(), torch.empty_like(x),
+                D=torch.ones(H, P, device=DEV), chunk_size=64, out=out)
+    torch.cuda.synchronize()
+    for k in ("ddt_bias", "dA", "dD"):
+        assert torch.count_nonzero(out[k]) == 0 and not torch.isnan(out[k]).any(), k
+
+
+def test_bwd_bf16_workload_launch_sparse_upstream():
+    """The backward at the bf16 B8 L4096 H32 P64 N128 workload's own sizes and launch shape, with
+    the upstream gradients nonzero only on batch rows R and heads S.  The gradients are linear in
+    the upstream ones, so every output equals the oracle's on the (R, S) slice (dB, dC summed over
+    the heads of S, dA, d dt_bias, dD over the rows of R), and is exactly zero outside it."""
+    w = I.WORKLOAD_LIST[2]
+    R, S = [0, 7], [0, 31]
+    _say(f"bwd {w.name} (upstream gradients on rows {R}, heads {S})")
+    inp = I.make_workload_inputs(w)
+    Bt, L, H, P, N = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate
+    d_s, f_s = _upstream(len(R), L, len(S), P, N, "bf16", seed=242)
+    dout = torch.zeros(Bt, L, H, P, dtype=torch.bfloat16)
+    dfin = torch.zeros(Bt, H, P, N)
+    for i, b in enumerate(R):
+        for j, h in enumerate(S):
+            dout[b, :, h] = d_s[i, :, j]
+            dfin[b, h] = f_s[i, j]
+    got = _run(inp, w.chunk, dout, dfin)
+    sub = {k: (v[R][:, :, S].contiguous() if k in ("x", "dt") else v[R].contiguous() if k in ("B", "C")
+               else v[S].contiguous()) for k, v in inp.items()}
+    ref = _oracle(sub, d_s, f_s)
+    tol = TOL["bf16"]
+    rows, heads = np.array(R), np.array(S)
+    for k in ("dx", "ddt"):
+        e = rel_err(got[k][rows][:, :, heads], ref[k])
+        assert e <= tol, f"{k} rel_err {e:.3e}"
+        mask = np.ones(got[k].shape[:3], dtype=bool)
+        mask[np.ix_(rows, np.arange(L), heads)] = False
+        assert np.count_nonzero(got[k][mask]) == 0, f"{k} nonzero outside the upstream slice"
+    for k in ("dB", "dC"):
+        e = rel_err(got[k][rows], ref[k])
+        assert e <= tol, f"{k} rel_err {e:.3e}"
+        others = np.setdiff1d(np.arange(Bt), rows)
+        assert np.count_nonzero(got[k][others]) == 0, f"{k} nonzero outside rows {R}"
+    for k in ("dA", "ddt_bias", "dD"):
+        e = rel_err(got[k][heads], ref[k])
+        assert e <= tol, f"{k} rel_err {e:.3e}"
+        assert np.count_nonzero(got[k][np.setdiff1d(np.arange(H), heads)]) == 0, k
+    e = rel_err(got["dinitial_state"][rows][:, heads], ref["dinitial_state"])
+    assert e <= tol, f"dinitial_state rel_err {e:.3e}"
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_bwd_graph_replay_and_timed_entry_match_eager(dtype):
     """ssd_bwd captured into a HIP graph gives the eager result on every replay; the timed entry

@@ -69,18 +69,15 @@ def test_conv_launch_shapes_do_not_change_results(dtype):
     inp = I.make_conv_inputs(2, 301, H, P, N, G, K, dtype, seed=67, with_state=True)
     d = _dev(inp)
     ref = None
-    try:
-        for tt in (4, 16, 36, 64, 320):
-            ssd.tune_set(3, tt)
-            got = ssd.conv1d_silu(d["xbc"], d["weight"], d["bias"], H, P, N, G, conv_state=d["conv_state"])
-            torch.cuda.synchronize()
-            if ref is None:
-                ref = got
-            else:
-                for a, b in zip(got, ref):
-                    assert torch.equal(a, b), tt
-    finally:
-        ssd.tune_set(3, 0)
+    for tt in (4, 16, 36, 64, 320):
+        got = ssd.conv1d_silu(d["xbc"], d["weight"], d["bias"], H, P, N, G, conv_state=d["conv_state"],
+                              opts={"conv_tokens": tt})
+        torch.cuda.synchronize()
+        if ref is None:
+            ref = got
+        else:
+            for a, b in zip(got, ref):
+                assert torch.equal(a, b), tt
     _check_conv(inp, H, P, N, G, dtype)
 
 

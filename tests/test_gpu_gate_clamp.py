@@ -32,11 +32,11 @@ def _oracle(inp, z=None, dt_limit=None, initial_state=None):
                           initial_state=initial_state, z=None if z is None else to64(z), dt_limit=dt_limit)
 
 
-def _fwd(inp, Q, z=None, dt_limit=None, initial_state=None):
+def _fwd(inp, Q, z=None, dt_limit=None, initial_state=None, opts=None):
     dev = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
     y, fin = ssd.ssd_fwd(dev["x"], dev["dt"], dev["dt_bias"], dev["A"], dev["B"], dev["C"], dev.get("D"),
                          chunk_size=Q, z=None if z is None else z.to(DEV), dt_limit=dt_limit,
-                         initial_state=None if initial_state is None else initial_state.to(DEV))
+                         initial_state=None if initial_state is None else initial_state.to(DEV), opts=opts)
     torch.cuda.synchronize()
     return to64(y), to64(fin)
 
@@ -60,11 +60,7 @@ def test_fwd_gate_and_clamp(dtype, P, N, G, gate, clamp, variant):
     inp = I.make_fwd_inputs(2, L, 4, P, N, G, dtype, seed=41 + P + N, d_init="normal")
     z = I.make_gate((2, L, 4, P), dtype, seed=42) if gate else None
     lim = LIMIT if clamp else None
-    try:
-        ssd.tune_set(2, variant)
-        y, fin = _fwd(inp, Q, z, lim)
-    finally:
-        ssd.tune_set(2, 0)
+    y, fin = _fwd(inp, Q, z, lim, opts={"scan_variant": variant})
     yr, fr = _oracle(inp, z, lim)
     assert np.all(np.isfinite(y)) and np.all(np.isfinite(fin))
     assert rel_err(y, yr) <= TOL[dtype], f"y rel_err {rel_err(y, yr):.3e}"

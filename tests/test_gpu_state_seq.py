@@ -2,7 +2,7 @@
 headdim slice) walks the chunks in order with the carried state in its MFMA accumulators, in
 place of chunk_state + state_passing), through the C ABI, against the float64 oracle.
 
-The path is forced with the launch knob (key 5 = 2, key 6 = slice rows) on small shapes that
+The path is forced with the launch options (state_path = 2, state_slice = rows) on small shapes that
 still span several chunks, 64-token tiles and a ragged last chunk; the built-in choice takes it
 for bf16 P64 N128 once batch x heads >= 256, which test_built_in_choice_takes_one_pass_for_large_bf16_batches
 covers without the knob.
@@ -29,26 +29,37 @@ def _say(msg):
     sys.stdout.flush()
 
 
-class _one_pass:
-    """Force the one-pass path (slice rows ps) for the duration of a block."""
+_OPTS = None      # launch options _run passes (set by _one_pass / _two_launch)
 
-    def __init__(self, ps):
-        self.ps = ps
+
+class _forced:
+    """Pass the given launch options to every _run call of a block."""
+
+    def __init__(self, **opts):
+        self.opts = opts
 
     def __enter__(self):
-        ssd.tune_set(5, 2)
-        ssd.tune_set(6, self.ps)
+        global _OPTS
+        _OPTS = self.opts
 
     def __exit__(self, *exc):
-        ssd.tune_set(5, 0)
-        ssd.tune_set(6, 0)
+        global _OPTS
+        _OPTS = None
+
+
+def _one_pass(ps):
+    return _forced(state_path=2, state_slice=ps)
+
+
+def _two_launch():
+    return _forced(state_path=1)
 
 
 def _run(inp, Q, init=None, z=None, dt_limit=None, workspace=None):
     dev = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
     y, fin = ssd.ssd_fwd(dev["x"], dev["dt"], dev["dt_bias"], dev["A"], dev["B"], dev["C"], dev.get("D"),
                          chunk_size=Q, initial_state=None if init is None else init.to(DEV),
-                         z=None if z is None else z.to(DEV), dt_limit=dt_limit, workspace=workspace)
+                         z=None if z is None else z.to(DEV), dt_limit=dt_limit, workspace=workspace, opts=_OPTS)
     torch.cuda.synchronize()
     return y, fin
 
@@ -79,7 +90,7 @@ def test_one_pass_matches_oracle(dtype, P, N, ps, L, Q, G):
     H = 4
     inp = I.make_fwd_inputs(2, L, H, P, N, G, dtype, seed=500 + L + Q + G, d_init="normal")
     with _one_pass(ps):
-        assert ssd.fwd_state_path(_dims(inp), Q) == 2
+        assert ssd.fwd_state_path(_dims(inp), Q, _OPTS) == 2
         y, fin = _run(inp, Q)
     yr, fr = _oracle(inp)
     assert np.all(np.isfinite(to64(y))) and np.all(np.isfinite(to64(fin)))
@@ -112,11 +123,8 @@ def test_one_pass_agrees_with_two_launch_path(dtype):
     _say(f"one-pass vs two launches {dtype}")
     P, N = (64, 64) if dtype == "f32" else (64, 128)
     inp = I.make_fwd_inputs(2, 900, 8, P, N, 2, dtype, seed=81, d_init="normal")
-    ssd.tune_set(5, 1)
-    try:
+    with _two_launch():
         y1, f1 = _run(inp, 256)
-    finally:
-        ssd.tune_set(5, 0)
     with _one_pass(64):
         y2, f2 = _run(inp, 256)
         y3, f3 = _run(inp, 256)
