@@ -47,7 +47,8 @@ typedef enum {
   SSD_ERR_UNSUPPORTED = 2,   /* valid but not implemented: chunk size, headdim, dstate, dtype */
   SSD_ERR_DEVICE_PTR = 3,    /* a pointer is not device memory of the current device */
   SSD_ERR_WORKSPACE = 4,     /* workspace NULL or smaller than ssd_fwd_workspace_size() */
-  SSD_ERR_HIP = 5            /* the HIP runtime reported an error when launching */
+  SSD_ERR_HIP = 5,           /* the HIP runtime reported an error when launching */
+  SSD_ERR_SCRATCH_LIMIT = 6  /* ssd_fwd_noalloc: the sizes need more than its fixed scratch */
 } ssd_status_t;
 
 typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype_t;
@@ -115,6 +116,25 @@ ssd_status_t ssd_fwd(const ssd_dims_t* dims,
                      const void* B, const void* C, const float* D, const void* z, int chunk_size,
                      const float* initial_state, void* y, float* final_state,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of the fixed device scratch that ssd_fwd_noalloc uses as its workspace. */
+#define SSD_FWD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* ssd_fwd for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same operation, arguments and results as
+ * ssd_fwd, but the workspace is a fixed array of SSD_FWD_NOALLOC_SCRATCH_BYTES inside the library
+ * (one per device, held until the process ends), so the call allocates nothing; the caller still
+ * passes the inputs and outputs.  Sizes whose ssd_fwd_workspace_size() exceeds the scratch are
+ * refused with SSD_ERR_SCRATCH_LIMIT before anything else (nothing launched, nothing written).
+ * The first call on a device resolves the array's device address (a host query, no allocation;
+ * make that first call outside a graph capture).  Every call on a device shares that device's
+ * array and leaves its intermediates there: calls on one device that may run concurrently (on
+ * different streams, or from different threads without ordering) race on it and must be
+ * serialised by the caller.  Nothing in the scratch needs to start at zero. */
+ssd_status_t ssd_fwd_noalloc(const ssd_dims_t* dims,
+                             const void* x, const void* dt, const float* dt_bias, const float* A,
+                             const void* B, const void* C, const float* D, const void* z, int chunk_size,
+                             const float* initial_state, void* y, float* final_state, hipStream_t stream);
 
 /* One recurrent decode step for every (b, h) ("MAMBA2 Inference Optimization Report", Step 4:
  * the carried hidden state; same discretisation as ssd_fwd).  dims->seqlen is ignored.

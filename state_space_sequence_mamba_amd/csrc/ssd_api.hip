@@ -2,6 +2,7 @@
 // Declarations and the contract live in include/ssd.h.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <stdint.h>
 #include <stdlib.h>
 
@@ -158,7 +159,8 @@ int pick_heads_per_block(int B, int nc, int H, int G, int variant, const ssd_lau
 ssd_status_t fwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, const float* dt_bias,
                       const float* A, const void* B, const void* C, const float* D, const void* z,
                       int chunk_size, const float* initial_state, void* y, float* final_state, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream, const ssd_launch_opts_t* opts, hipEvent_t* ev) {
+                      size_t workspace_bytes, hipStream_t stream, const ssd_launch_opts_t* opts, hipEvent_t* ev,
+                      bool own_scratch = false) {
   const ssd_launch_opts_t& o = opts_or_builtin(opts);
   ssd_status_t st = check_dims(dims, true);
   if (st != SSD_OK) return st;
@@ -183,8 +185,9 @@ ssd_status_t fwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
     if (!aligned(workspace, 16)) return SSD_ERR_INVALID_ARG;
   }
   // every pointer must be device memory of the current device
+  // (the library's own scratch array is a module global, not a runtime allocation: not queried)
   const void* ptrs[] = {x,  dt, dt_bias, A, B, C, D, has_seq ? z : nullptr, initial_state, y, final_state,
-                        has_seq ? workspace : nullptr};
+                        has_seq && !own_scratch ? workspace : nullptr};
   for (const void* p : ptrs)
     if (p && !device_ptr_ok(p)) return SSD_ERR_DEVICE_PTR;
 
@@ -522,6 +525,35 @@ ssd_status_t step_impl(const ssd_dims_t* dims, float* state, const void* x, cons
   return ssd::launch_ssd_step(a, stream) == hipSuccess ? SSD_OK : SSD_ERR_HIP;
 }
 
+// ---------------------------------------------------------------- no-allocation forward
+// The workspace of ssd_fwd_noalloc: a fixed device array of the library (each device that runs
+// the library holds its own copy until the process ends).  Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in for the symbol): the device address is
+// resolved once per device with hipGetSymbolAddress, with that device current, and kept here.
+constexpr size_t kScratchBytes = SSD_FWD_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};   // written once per device, under g_scratch_mu
+
+// Device address of `scratch` on the current device (resolved on the first call there).
+ssd_status_t scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SSD_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return SSD_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SSD_OK;
+}
+
 // Both conv entry points.  `step`: one token per sequence, state updated in place.
 ssd_status_t conv_impl(const ssd_dims_t* dims, int K, const void* xbc, const float* weight, const float* bias,
                        const void* state_in, void* state_out, void* x, void* B, void* C, hipStream_t stream,
@@ -617,6 +649,22 @@ ssd_status_t ssd_fwd_ex(const ssd_dims_t* dims, const void* x, const void* dt, c
                   workspace_bytes, stream, opts, stage_events);
 }
 
+ssd_status_t ssd_fwd_noalloc(const ssd_dims_t* dims, const void* x, const void* dt, const float* dt_bias,
+                             const float* A, const void* B, const void* C, const float* D, const void* z,
+                             int chunk_size, const float* initial_state, void* y, float* final_state,
+                             hipStream_t stream) {
+  ssd_status_t st = check_dims(dims, true);
+  if (st != SSD_OK) return st;
+  if (!chunk_ok(chunk_size)) return SSD_ERR_UNSUPPORTED;
+  // sizes beyond the fixed scratch are refused before anything else happens
+  if (ws_layout(dims, chunk_size).total > kScratchBytes) return SSD_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != SSD_OK) return st;
+  return fwd_impl(dims, x, dt, dt_bias, A, B, C, D, z, chunk_size, initial_state, y, final_state, ws, kScratchBytes,
+                  stream, nullptr, nullptr, true);
+}
+
 ssd_status_t ssd_step(const ssd_dims_t* dims, float* state, const void* x, const void* dt, const float* dt_bias,
                       const float* A, const void* B, const void* C, const float* D, const void* z, void* y,
                       hipStream_t stream) {
@@ -681,6 +729,7 @@ const char* ssd_status_string(ssd_status_t s) {
     case SSD_ERR_DEVICE_PTR: return "pointer is not device memory of the current device";
     case SSD_ERR_WORKSPACE: return "workspace missing or too small";
     case SSD_ERR_HIP: return "HIP runtime error at launch";
+    case SSD_ERR_SCRATCH_LIMIT: return "sizes need more workspace than ssd_fwd_noalloc's fixed scratch holds";
   }
   return "unknown status";
 }

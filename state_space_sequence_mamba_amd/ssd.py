@@ -12,7 +12,9 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libssd.so")
 
-SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_DEVICE_PTR, SSD_ERR_WORKSPACE, SSD_ERR_HIP = range(6)
+(SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_DEVICE_PTR, SSD_ERR_WORKSPACE, SSD_ERR_HIP,
+ SSD_ERR_SCRATCH_LIMIT) = range(7)
+NOALLOC_SCRATCH_BYTES = 64 << 20      # SSD_FWD_NOALLOC_SCRATCH_BYTES of include/ssd.h
 SSD_F32, SSD_BF16 = 0, 1
 
 _DTYPES = {torch.float32: SSD_F32, torch.bfloat16: SSD_BF16}
@@ -73,6 +75,8 @@ def load_library():
     fwd_args = [dims_p, vp, vp, f32p, f32p, vp, vp, f32p, vp, i32, f32p, vp, f32p, vp, sz, vp]
     lib.ssd_fwd.argtypes = fwd_args
     lib.ssd_fwd.restype = i32
+    lib.ssd_fwd_noalloc.argtypes = [dims_p, vp, vp, f32p, f32p, vp, vp, f32p, vp, i32, f32p, vp, f32p, vp]
+    lib.ssd_fwd_noalloc.restype = i32
     opts_p = ctypes.POINTER(ssd_launch_opts_t)
     lib.ssd_fwd_ex.argtypes = fwd_args + [opts_p, vp]
     lib.ssd_fwd_ex.restype = i32
@@ -186,6 +190,23 @@ def ssd_fwd(x, dt, dt_bias, A, B, C, D=None, chunk_size=256, initial_state=None,
         st = lib.ssd_fwd_ex(*args, _opts_ref(opts), arr)
     if st != SSD_OK:
         raise SsdError(st, "ssd_fwd")
+    return y, final_state
+
+
+def ssd_fwd_noalloc(x, dt, dt_bias, A, B, C, D=None, chunk_size=256, initial_state=None, y=None, final_state=None,
+                    stream=None, z=None, dt_limit=None):
+    """ssd_fwd with the library's fixed scratch as its workspace (ssd_fwd_noalloc: no device
+    allocation in the call).  y and final_state must be given (the binding allocates nothing
+    either); returns (y, final_state)."""
+    b, L, H, P, N, G = _check_fwd_shapes(x, dt, dt_bias, A, B, C, D, initial_state, z)
+    if y is None:
+        raise ValueError("ssd_fwd_noalloc: pass y (the call allocates nothing)")
+    dims = make_dims(b, L, H, P, N, G, x.dtype, dt_limit)
+    st = load_library().ssd_fwd_noalloc(ctypes.byref(dims), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B),
+                                        _ptr(C), _ptr(D), _ptr(z), int(chunk_size), _ptr(initial_state), _ptr(y),
+                                        _ptr(final_state), _stream(stream))
+    if st != SSD_OK:
+        raise SsdError(st, "ssd_fwd_noalloc")
     return y, final_state
 
 

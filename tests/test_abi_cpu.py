@@ -257,3 +257,19 @@ def test_fwd_state_path_choice_is_host_logic():
     # options are per call: nothing of the calls above is kept
     assert ssd.fwd_state_path(p(8, 4096, 32, 64, 128, 1, bf), 256) == 2
     assert ssd.fwd_state_path(p(4, 1024, 24, 64, 64, 1, f32), 256, ssd.launch_opts()) == 1
+
+
+def test_noalloc_refuses_oversize_before_any_device_call(lib):
+    """ssd_fwd_noalloc checks the sizes against its fixed scratch first: an oversize problem is
+    refused (no launch, no device query), and invalid sizes keep their usual codes."""
+    import torch
+    big = ssd.make_dims(8, 4096, 32, 64, 128, 1, torch.bfloat16)
+    assert ssd.ssd_fwd_workspace_size(big, 256) > ssd.NOALLOC_SCRATCH_BYTES
+    p = ctypes.c_void_p(0x100000)
+    args = [p, p, p, p, p, p, None, None, 256, None, p, None, None]
+    assert lib.ssd_fwd_noalloc(ctypes.byref(big), *args) == ssd.SSD_ERR_SCRATCH_LIMIT
+    bad = ssd.make_dims(8, 4096, 33, 64, 128, 2, torch.bfloat16)       # heads not a multiple of groups
+    assert lib.ssd_fwd_noalloc(ctypes.byref(bad), *args) == ssd.SSD_ERR_INVALID_ARG
+    args[8] = 100                                                       # chunk size
+    assert lib.ssd_fwd_noalloc(ctypes.byref(big), *args) == ssd.SSD_ERR_UNSUPPORTED
+    assert "scratch" in ssd.ssd_status_string(ssd.SSD_ERR_SCRATCH_LIMIT)
