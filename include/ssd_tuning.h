@@ -22,8 +22,11 @@ extern "C" {
  * call's sizes (no such instantiation) fall back to the built-in choice. */
 typedef struct {
   int32_t scan_variant;     /* chunk_scan decomposition: 1 = one workgroup per 64-row block of a
-                             * chunk, 2 = one workgroup per whole chunk */
+                             * chunk, 2 = one workgroup per whole chunk, 3 = one workgroup per chunk,
+                             * group and slice of the group's heads, C B^T formed once per slice
+                             * (SSD_BF16, chunk 256, headdim 64, dstate 128) */
   int32_t heads_per_block;  /* chunk_scan heads per workgroup sharing one C B^T evaluation: 1 or 2
+                             * for decompositions 1 and 2, any divisor of nheads / ngroups for 3
                              * (ignored unless it divides nheads / ngroups) */
   int32_t min_blocks;       /* whole-chunk decomposition: minimum workgroup count the head-block
                              * choice aims for (built-in 512) */

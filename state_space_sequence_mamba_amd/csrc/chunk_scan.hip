@@ -729,6 +729,7 @@ static hipError_t launch_scan_impl(const FwdArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_chunk_scan(const FwdArgs& a, hipStream_t s) {
+  if (a.scan_variant == 3) return launch_chunk_scan_group(a, a.heads_per_block, s);
 #define SSD_CASE(T, P_, N_) \
   if (a.dtype == SSD_DTYPE_CODE_##T && a.P == P_ && a.N == N_) return launch_scan_impl<T, P_, N_>(a, s);
   SSD_FOR_EACH_SHAPE(SSD_CASE)

@@ -1,0 +1,427 @@
+// chunk_scan, group-shared form for bf16 inputs (chunk 256): the same output as chunk_scan.hip,
+//   y[i,p] = sum_{j<=i} CB[i,j] exp(dAcs[i] - dAcs[j]) dt'_j x[j,p]        (diagonal block)
+//          + exp(dAcs[i]) sum_n C[i,n] Hprev[p,n]                            (carried state)
+//          + D[p] x[i,p]                                                     (skip term)
+// (times silu(z[i,p]) with a gate), CB[i,j] = sum_n C[i,n] B[j,n].  Sources as chunk_scan.hip:
+// "Agent 228: MAMBA-2 Reference Implementations Comparison", sections 2.2 and 3.2; "Agent 228:
+// MAMBA-2 Implementation Gaps", Gaps 1 and 4; the gate of section 3.1 of the first page.
+//
+// CB depends only on the chunk and the group, not on the head, so a workgroup takes one chunk of
+// one group and a slice of that group's heads: it forms the chunk's causal CB once, keeps it in
+// registers, and streams the heads of its slice through it.  Per head it reads x, the entering
+// state and the cumsums once and writes y once, so a launch moves each input and output exactly
+// once (B and C once per slice) and contracts CB once per slice instead of once per head.
+//
+// Eight wavefronts; wavefront w owns the strip pair (w, 15 - w) of the chunk's sixteen 16-row
+// strips, i.e. w + 1 and 16 - w causal 16x16 sub-tiles, 17 for every wavefront.  The CB sub-tiles
+// (16x16x32 bf16 MFMA over dstate, from the chunk's B and C rows staged in LDS) stay in registers
+// for all heads; the C rows stay in LDS for the carried term.  Per head: the carried term C Hprev^T on MFMA (Hprev staged in LDS),
+// then every sub-tile's decay in registers (below the diagonal a row factor times a per-column
+// weight, both <= 1: one exponential per lane; on the diagonal one per element and the causal
+// mask) rounded to bf16 as the A operand of the 16x16x16 bf16 MFMA with the x^T tile in LDS; the
+// skip term on the diagonal sub-tile, whose x values are the lane's own output rows.  The next
+// head's x, entering state and cumsums are loaded into registers while the current head computes
+// (two barriers per head), and y leaves through an LDS staging tile as 16-byte row stores.
+#include "cb_tiles.h"
+#include "ssd_common.h"
+#include "ssd_launch.h"
+
+namespace ssd {
+
+namespace {
+
+constexpr int kGQ = 256;                        // chunk length of this form
+constexpr int kGS = kGQ / 16;                   // 16-row strips per chunk
+constexpr int kGThreads = 512;                  // eight wavefronts
+constexpr int kGSub = kGS + 1;                  // causal sub-tiles per wavefront (strip pair)
+constexpr float kGLog2e = 1.4426950408889634f;
+
+template <int P, int N>
+struct GroupLds {
+  static constexpr int BP = N + 8;              // B rows / Hprev rows, n-contiguous (bf16)
+  static constexpr int XP = kGQ + 4;            // x^T rows, token-contiguous (a 130-dword pitch:
+                                                // the 8-byte operand reads of 16 rows hit 32 banks)
+  static constexpr int YP = P + 8;              // y staging rows
+  static constexpr int X_ELEMS = P * XP;
+  static constexpr int PREV_ELEMS = P * BP;
+  static constexpr int Y_ELEMS = kGQ * YP;
+  static constexpr int HEAD = X_ELEMS + PREV_ELEMS + Y_ELEMS;   // per-head regions, side by side
+  static constexpr int B_ELEMS = kGQ * BP;                      // B rows of the chunk (CB phase only)
+  static constexpr int TOTAL = HEAD > B_ELEMS ? HEAD : B_ELEMS;
+  static constexpr int C_ELEMS = kGQ * BP;                      // C rows of the chunk, kept for every head
+};
+
+// One head's inputs between their global loads and their LDS stores: x as token pairs (each
+// thread two 16-byte vectors of consecutive tokens at the same headdim offset; eight lanes cover
+// one token row, so every load instruction reads whole rows), the bf16 entering state as 16-byte
+// vectors, the chunk's dt' and cumsum (threads 0..255, one position each) and D (threads 0..P-1).
+template <int P, int N>
+struct HeadRegs {
+  static constexpr int PV = P / 8;                          // 16-byte vectors per token row
+  static constexpr int XU = (kGQ / 2) * PV;                 // token-pair units
+  static constexpr int XPT = XU / kGThreads;
+  static constexpr int PU = P * N / 8;                      // 16-byte vectors of the state
+  static constexpr int PPT = PU / kGThreads;
+  static_assert(XU % kGThreads == 0 && PU % kGThreads == 0, "shape");
+  uint4 x[XPT][2];
+  uint4 pv[PPT];
+  float dt, da, dd;
+  uint32_t okm;
+
+  // Per-lane element offsets from the head's (wavefront-uniform) base pointers, 32-bit: the
+  // loads take a scalar base plus a vector offset.  The offsets are made opaque at each call so
+  // the compiler does not keep precomputed 64-bit addresses alive across the head loop.
+  __device__ __forceinline__ void load(const __bf16* xh, const __bf16* ph, const float* dth, const float* dah,
+                                       const float* Dh, uint32_t x_tok, int len, int tid) {
+    uint32_t xo[XPT][2], po[PPT];
+    okm = 0;
+#pragma unroll
+    for (int u = 0; u < XPT; ++u) {
+      const int v = tid + kGThreads * u;
+      const int vec = (v % PV) * 8, m = v / PV;
+      const int tok = 2 * m;
+      const bool ok0 = tok < len, ok1 = tok + 1 < len;
+      xo[u][0] = (uint32_t)(ok0 ? tok : 0) * x_tok + vec;
+      xo[u][1] = (uint32_t)(ok1 ? tok + 1 : 0) * x_tok + vec;
+      okm |= ((uint32_t)ok0 << (2 * u)) | ((uint32_t)ok1 << (2 * u + 1));
+      asm volatile("" : "+v"(xo[u][0]), "+v"(xo[u][1]));
+    }
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      po[u] = (uint32_t)(tid + kGThreads * u) * 8;
+      asm volatile("" : "+v"(po[u]));
+    }
+    uint32_t io = tid & (kGQ - 1), Do = tid & (P - 1);
+    asm volatile("" : "+v"(io), "+v"(Do));
+#pragma unroll
+    for (int u = 0; u < XPT; ++u) {
+      x[u][0] = *reinterpret_cast<const uint4*>(xh + xo[u][0]);
+      x[u][1] = *reinterpret_cast<const uint4*>(xh + xo[u][1]);
+    }
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) pv[u] = *reinterpret_cast<const uint4*>(ph + po[u]);
+    dt = dth[io];
+    da = dah[io];
+    dd = Dh ? Dh[Do] : 0.f;
+  }
+
+  // x^T (token pairs packed into one 32-bit store per headdim row), the state rows, and for
+  // threads 0..255 the log2e-scaled cumsum, dt' and the column weights
+  // W_j = exp2(dAcs_c - dAcs_j) dt'_j, c = j | 15 (the last column of j's 16-column tile)
+  template <typename L>
+  __device__ __forceinline__ void store(__bf16* s_x, __bf16* s_prev, float* s_da, float* s_dt, float* s_w,
+                                        float* s_D, int tid) const {
+#pragma unroll
+    for (int u = 0; u < XPT; ++u) {
+      const int v = tid + kGThreads * u;
+      const int vec = (v % PV) * 8, m = v / PV;
+      uint4 a = x[u][0], b = x[u][1];
+      if (!((okm >> (2 * u)) & 1u)) a = make_uint4(0, 0, 0, 0);
+      if (!((okm >> (2 * u + 1)) & 1u)) b = make_uint4(0, 0, 0, 0);
+      const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        // elements 2q (low halves) and 2q + 1 (high halves) of the two tokens
+        const uint32_t lo = (av[q] & 0xffffu) | (bv[q] << 16);
+        const uint32_t hi = (av[q] >> 16) | (bv[q] & 0xffff0000u);
+        *reinterpret_cast<uint32_t*>(&s_x[(vec + 2 * q) * L::XP + 2 * m]) = lo;
+        *reinterpret_cast<uint32_t*>(&s_x[(vec + 2 * q + 1) * L::XP + 2 * m]) = hi;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int v = tid + kGThreads * u;
+      const int p = (v * 8) / N, n = (v * 8) % N;
+      *reinterpret_cast<uint4*>(&s_prev[p * L::BP + n]) = pv[u];
+    }
+    if (tid < kGQ) {
+      const float d2 = da * kGLog2e;
+      const float dc = __shfl(d2, (tid & 63) | 15, 64);
+      s_da[tid] = d2;
+      s_dt[tid] = dt;
+      s_w[tid] = __builtin_amdgcn_exp2f(dc - d2) * dt;
+    }
+    if (tid < P) s_D[tid] = dd;
+  }
+};
+
+// two fp32 values rounded to bf16 (nearest-even) in one 32-bit word, and back
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const __bf16 l = static_cast<__bf16>(lo), h = static_cast<__bf16>(hi);
+  return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+}
+__device__ __forceinline__ float unpack_lo(uint32_t v) { return __builtin_bit_cast(float, v << 16); }
+__device__ __forceinline__ float unpack_hi(uint32_t v) { return __builtin_bit_cast(float, v & 0xffff0000u); }
+
+}  // namespace
+
+template <int P, int N>
+__global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
+    const __bf16* __restrict__ x, const __bf16* __restrict__ Bm, const __bf16* __restrict__ Cm,
+    const float* __restrict__ dtp, const float* __restrict__ dAcs, const __bf16* __restrict__ prev16,
+    const float* __restrict__ Dw, const __bf16* __restrict__ Z, __bf16* __restrict__ y, int L, int H, int G, int nc,
+    int hs, uint32_t nblocks) {
+  typedef GroupLds<P, N> SL;
+  typedef NDot<__bf16, N> ND;
+  typedef HeadRegs<P, N> HR;
+  constexpr int TP = P / 16;
+
+  __shared__ __attribute__((aligned(16))) __bf16 s_mem[SL::TOTAL];
+  __shared__ __attribute__((aligned(16))) __bf16 s_c[SL::C_ELEMS];   // C rows (carried term)
+  __shared__ __attribute__((aligned(16))) float s_da[kGQ];   // dAcs * log2(e)
+  __shared__ __attribute__((aligned(16))) float s_dt[kGQ];
+  __shared__ __attribute__((aligned(16))) float s_w[kGQ];    // column weights
+  __shared__ __attribute__((aligned(16))) float s_D[P];      // skip weights of the head
+  __bf16* s_b = s_mem;                                       // CB phase: B rows
+  __bf16* s_x = s_mem;                                       // per head: x^T, Hprev, y staging
+  __bf16* s_prev = s_mem + SL::X_ELEMS;
+  __bf16* s_y = s_mem + SL::X_ELEMS + SL::PREV_ELEMS;
+
+  // work unit: (b, c, g, head slice); the slices of one (b, c, g) are consecutive, so they share
+  // B and C in one XCD's L2
+  uint32_t id = xcd_swizzle(blockIdx.x, nblocks);
+  const int hpg = H / G, nsl = hpg / hs;
+  const int sl = id % nsl;
+  id /= nsl;
+  const int g = id % G;
+  id /= G;
+  const int c = id % nc, b = id / nc;
+  const int h0 = g * hpg + sl * hs;
+  const int t0 = c * kGQ;
+  const int len = min(kGQ, L - t0);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);    // wavefront-uniform: scalar branches below
+  const int r = lane & 15, qd = lane >> 4;
+  const int s0 = w, s1 = kGS - 1 - w;                        // this wavefront's strips
+
+  const size_t bc_tok = (size_t)G * N, x_tok = (size_t)H * P;
+  const __bf16* Cb = Cm + ((size_t)b * L + t0) * bc_tok + (size_t)g * N;
+  const __bf16* Bb = Bm + ((size_t)b * L + t0) * bc_tok + (size_t)g * N;
+  auto head_ptrs = [&](int h, const __bf16*& xh, const __bf16*& ph, const float*& dth, const float*& dah,
+                       const float*& Dh) {
+    xh = x + ((size_t)b * L + t0) * x_tok + (size_t)h * P;
+    ph = prev16 + (((size_t)b * nc + c) * H + h) * (size_t)(P * N);
+    const size_t o = (((size_t)b * H + h) * nc + c) * kGQ;
+    dth = dtp + o;
+    dah = dAcs + o;
+    Dh = Dw ? Dw + (size_t)h * P : nullptr;
+  };
+
+  // ---- prologue: B rows of the chunk, this wavefront's C rows, the first head's inputs
+  constexpr int BU = kGQ * N / 8, BPT = BU / kGThreads;       // 16-byte vectors of B
+  uint4 breg[BPT];
+#pragma unroll
+  for (int u = 0; u < BPT; ++u) {
+    const int v = tid + kGThreads * u;
+    const int row = v / (N / 8), nv = (v % (N / 8)) * 8;
+    breg[u] = *reinterpret_cast<const uint4*>(Bb + (size_t)(row < len ? row : 0) * bc_tok + nv);
+  }
+  // C rows past the end read row 0 (they reach only output rows that are never stored)
+  uint4 creg[BPT];
+#pragma unroll
+  for (int u = 0; u < BPT; ++u) {
+    const int v = tid + kGThreads * u;
+    const int row = v / (N / 8), nv = (v % (N / 8)) * 8;
+    creg[u] = *reinterpret_cast<const uint4*>(Cb + (size_t)(row < len ? row : 0) * bc_tok + nv);
+  }
+  HR hr;
+  {
+    const __bf16 *xh, *ph;
+    const float *dth, *dah, *Dh;
+    head_ptrs(h0, xh, ph, dth, dah, Dh);
+    hr.load(xh, ph, dth, dah, Dh, (uint32_t)x_tok, len, tid);
+  }
+#pragma unroll
+  for (int u = 0; u < BPT; ++u) {
+    const int v = tid + kGThreads * u;
+    const int row = v / (N / 8), nv = (v % (N / 8)) * 8;
+    *reinterpret_cast<uint4*>(&s_b[row * SL::BP + nv]) = row < len ? breg[u] : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(&s_c[row * SL::BP + nv]) = creg[u];
+  }
+  __syncthreads();
+
+  // ---- C B^T of this wavefront's 17 causal sub-tiles, kept for every head:
+  // sub-tile k <= w is (strip s0, column tile k), k > w is (strip s1, column tile k - w - 1);
+  // lane (r, qd) holds CB[i = 16 s + r][j = 16 jt + 4 qd + e]
+  f32x4 cb[kGSub];
+  {
+    typename ND::frag cf0, cf1;
+    ND::load(cf0, &s_c[(16 * s0 + r) * SL::BP], qd);
+    ND::load(cf1, &s_c[(16 * s1 + r) * SL::BP], qd);
+#pragma unroll
+    for (int k = 0; k < kGSub; ++k) {
+      const int jt = k <= w ? k : k - w - 1;
+      typename ND::frag bfr;
+      ND::load(bfr, &s_b[(16 * jt + r) * SL::BP], qd);
+      if (k <= w)
+        cb[k] = ND::dot(bfr, cf0, zero4());
+      else
+        cb[k] = ND::dot(bfr, cf1, zero4());
+    }
+  }
+  __syncthreads();                                           // s_b consumed: the head regions reuse it
+  hr.template store<SL>(s_x, s_prev, s_da, s_dt, s_w, s_D, tid);
+  __syncthreads();
+
+  for (int hh = 0; hh < hs; ++hh) {
+    const int h = h0 + hh;
+    // the next head's inputs, in flight during this head's MFMAs
+    const bool more = hh + 1 < hs;
+    if (more) {
+      const __bf16 *xh, *ph;
+      const float *dth, *dah, *Dh;
+      head_ptrs(h + 1, xh, ph, dth, dah, Dh);
+      hr.load(xh, ph, dth, dah, Dh, (uint32_t)x_tok, len, tid);
+    }
+
+    // per-lane LDS offsets, opaque to the compiler at every head: otherwise it hoists the 68
+    // head-independent operand addresses of the sub-tiles out of the head loop and spills them;
+    // this way each read is a base register plus an immediate offset.  Strip s1's column tiles
+    // are jt = k - w - 1, folded into its base.
+    int xo0 = r * SL::XP + 4 * qd, xo1 = xo0 - 16 * (w + 1);
+    int wo0 = 4 * qd, wo1 = wo0 - 16 * (w + 1);
+    asm volatile("" : "+v"(xo0), "+v"(xo1), "+v"(wo0), "+v"(wo1));
+    // likewise C B^T: nothing derived from it is hoisted out of the head loop
+#pragma unroll
+    for (int k = 0; k < kGSub; ++k) asm volatile("" : "+v"(cb[k]));
+
+    // the two strips one after the other (one strip's accumulators live at a time); the first
+    // strip's results wait in registers as bf16 until the y staging tile is free
+    uint32_t ypk[TP][2];
+    f32x4 acc[TP];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int s = st ? s1 : s0;
+      // carried term: exp(dAcs_i) C_i Hprev^T
+      {
+        typename ND::frag cf;
+        ND::load(cf, &s_c[(16 * s + r) * SL::BP], qd);
+#pragma unroll
+        for (int pt = 0; pt < TP; ++pt) {
+          typename ND::frag pf;
+          ND::load(pf, &s_prev[(pt * 16 + r) * SL::BP], qd);
+          acc[pt] = ND::dot(cf, pf, zero4());
+        }
+        float sc[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc[e] = __builtin_amdgcn_exp2f(s_da[16 * s + 4 * qd + e]);
+#pragma unroll
+        for (int pt = 0; pt < TP; ++pt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[pt][e] *= sc[e];
+      }
+      // diagonal-block sub-tiles of this strip: k <= w for the first, k > w for the second
+      const int i_row = 16 * s + r;
+      const float da_row = s_da[i_row];
+#pragma unroll
+      for (int k = 0; k < kGSub; ++k) {
+        const bool mine = st == 0 ? k <= w : k > w;
+        if (!mine) continue;
+        const int jt = st == 0 ? k : k - w - 1;
+        const bool diag = jt == s;
+        const int wo = (st == 0 ? wo0 : wo1) + 16 * k;   // = 16 jt + 4 qd
+        const int xo = (st == 0 ? xo0 : xo1) + 16 * k;   // = r XP + 16 jt + 4 qd
+        float lw[4];
+        if (diag) {
+          const float4 daj = *reinterpret_cast<const float4*>(&s_da[wo]);
+          const float4 dtj = *reinterpret_cast<const float4*>(&s_dt[wo]);
+          lw[0] = (4 * qd + 0 <= r) ? cb[k][0] * __builtin_amdgcn_exp2f(da_row - daj.x) * dtj.x : 0.f;
+          lw[1] = (4 * qd + 1 <= r) ? cb[k][1] * __builtin_amdgcn_exp2f(da_row - daj.y) * dtj.y : 0.f;
+          lw[2] = (4 * qd + 2 <= r) ? cb[k][2] * __builtin_amdgcn_exp2f(da_row - daj.z) * dtj.z : 0.f;
+          lw[3] = (4 * qd + 3 <= r) ? cb[k][3] * __builtin_amdgcn_exp2f(da_row - daj.w) * dtj.w : 0.f;
+        } else {
+          const float ri = __builtin_amdgcn_exp2f(da_row - s_da[16 * jt + 15]);
+          const float4 wj = *reinterpret_cast<const float4*>(&s_w[wo]);
+          lw[0] = cb[k][0] * wj.x * ri;
+          lw[1] = cb[k][1] * wj.y * ri;
+          lw[2] = cb[k][2] * wj.z * ri;
+          lw[3] = cb[k][3] * wj.w * ri;
+        }
+        bf16x4 a;
+        a[0] = static_cast<__bf16>(lw[0]);
+        a[1] = static_cast<__bf16>(lw[1]);
+        a[2] = static_cast<__bf16>(lw[2]);
+        a[3] = static_cast<__bf16>(lw[3]);
+#pragma unroll
+        for (int pt = 0; pt < TP; ++pt) {
+          const bf16x4 xv = *reinterpret_cast<const bf16x4*>(&s_x[xo + pt * 16 * SL::XP]);
+          acc[pt] = mfma_16x16x16_bf16(a, xv, acc[pt]);
+          if (diag)  // x rows 16 jt + 4 qd + e are this lane's output rows
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[pt][e] += s_D[pt * 16 + r] * static_cast<float>(xv[e]);
+        }
+      }
+      if (Z) {
+        // output gate on the lane's elements (rows past the sequence read a clamped address)
+        const __bf16* zh = Z + ((size_t)b * L + t0) * x_tok + (size_t)h * P;
+        float zv[TP][4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * s + 4 * qd + e;
+          uint32_t zo = (uint32_t)(i < len ? i : 0) * (uint32_t)x_tok + r;
+          asm volatile("" : "+v"(zo));
+#pragma unroll
+          for (int pt = 0; pt < TP; ++pt) zv[pt][e] = static_cast<float>(zh[zo + pt * 16]);
+        }
+#pragma unroll
+        for (int pt = 0; pt < TP; ++pt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[pt][e] *= silu(zv[pt][e]);
+      }
+      if (st == 0) {
+#pragma unroll
+        for (int pt = 0; pt < TP; ++pt) {
+          ypk[pt][0] = pack_bf16(acc[pt][0], acc[pt][1]);
+          ypk[pt][1] = pack_bf16(acc[pt][2], acc[pt][3]);
+        }
+      }
+    }
+    __syncthreads();                                         // x^T, Hprev and scalars of head h consumed
+#pragma unroll
+    for (int pt = 0; pt < TP; ++pt) {
+      const float y0[4] = {unpack_lo(ypk[pt][0]), unpack_hi(ypk[pt][0]), unpack_lo(ypk[pt][1]),
+                           unpack_hi(ypk[pt][1])};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s_y[(16 * s0 + 4 * qd + e) * SL::YP + pt * 16 + r] = static_cast<__bf16>(y0[e]);
+        s_y[(16 * s1 + 4 * qd + e) * SL::YP + pt * 16 + r] = static_cast<__bf16>(acc[pt][e]);
+      }
+    }
+    if (more) hr.template store<SL>(s_x, s_prev, s_da, s_dt, s_w, s_D, tid);
+    __syncthreads();                                         // y staged; the next head's inputs in LDS
+    {
+      constexpr int YU = kGQ * P / 8, YPT = YU / kGThreads;
+      __bf16* yh = y + ((size_t)b * L + t0) * x_tok + (size_t)h * P;
+#pragma unroll
+      for (int u = 0; u < YPT; ++u) {
+        const int v = tid + kGThreads * u;
+        const int row = v / (P / 8), cv = (v % (P / 8)) * 8;
+        uint32_t yo = (uint32_t)row * (uint32_t)x_tok + cv;
+        asm volatile("" : "+v"(yo));
+        if (row < len)
+          *reinterpret_cast<uint4*>(yh + yo) = *reinterpret_cast<const uint4*>(&s_y[row * SL::YP + cv]);
+      }
+    }
+    // s_y is rewritten only after the next head's first barrier: the flush above is complete by then
+  }
+}
+
+bool chunk_scan_group_supported(int dtype, int P, int N, int Q) {
+  return dtype == DT_BF16 && Q == kGQ && P == 64 && N == 128;
+}
+
+hipError_t launch_chunk_scan_group(const FwdArgs& a, int hs, hipStream_t s) {
+  if (!chunk_scan_group_supported(a.dtype, a.P, a.N, a.Q) || !a.prev16) return hipErrorInvalidValue;
+  const int hpg = a.H / a.G;
+  if (hs < 1 || hpg % hs != 0) return hipErrorInvalidValue;
+  const uint32_t nblocks = (uint32_t)a.B * a.nc * a.G * (hpg / hs);
+  if (nblocks == 0) return hipSuccess;
+  hipExtLaunchKernelGGL(chunk_scan_group_kernel<64, 128>, dim3(nblocks), dim3(kGThreads), 0, s, a.ev0, a.ev1, 0,
+                        static_cast<const __bf16*>(a.x), static_cast<const __bf16*>(a.Bm),
+                        static_cast<const __bf16*>(a.Cm), a.dtp, a.dAcs, static_cast<const __bf16*>(a.prev16), a.D,
+                        static_cast<const __bf16*>(a.z), static_cast<__bf16*>(a.y), a.L, a.H, a.G, a.nc, hs, nblocks);
+  return hipGetLastError();
+}
+
+}  // namespace ssd

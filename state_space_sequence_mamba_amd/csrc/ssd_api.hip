@@ -131,10 +131,14 @@ int pick_rows_group(const ssd_launch_opts_t& o) { return o.rows_group > 0 ? o.ro
 // B4 L1024 H24 39 us against 68 us for whole chunks; bf16 B8 L4096 H32 N128 191 us against
 // 208 us (bf16 B2 L16384 H80 G8: 545 us against 519 us, the one shape measured where whole
 // chunks win).
-int pick_scan_variant(int dtype, const ssd_launch_opts_t& o) {
-  (void)dtype;
-  if (o.scan_variant == 1 || o.scan_variant == 2) return o.scan_variant;
-  return 1;
+// The group form (a workgroup per chunk, group and slice of heads, C B^T formed once per slice)
+// wherever it is instantiated (bf16, chunk 256, P64 N128): measured on MI355X, bf16 B2 L16384 H80
+// G8 chunk_scan 456 -> 398 us, B8 L4096 H32 on par (162 us) with chunk_state_seq 122 -> 101 us,
+// since no C B^T blocks are formed for the scan to read.
+int pick_scan_variant(const ssd_dims_t* d, int Q, const ssd_launch_opts_t& o) {
+  const bool group = ssd::chunk_scan_group_supported(d->dtype, (int)d->headdim, (int)d->dstate, Q);
+  if (o.scan_variant == 1 || o.scan_variant == 2 || (o.scan_variant == 3 && group)) return o.scan_variant;
+  return group ? 3 : 1;
 }
 
 // Heads of one group sharing one C B^T evaluation inside a workgroup; more heads per workgroup
@@ -142,6 +146,17 @@ int pick_scan_variant(int dtype, const ssd_launch_opts_t& o) {
 int pick_heads_per_block(int B, int nc, int H, int G, int variant, const ssd_launch_opts_t& o) {
   static const int kChoices[] = {2, 1};  // instantiated head-block sizes
   const int hpg = H / G;
+  if (variant == 3) {
+    // a workgroup per (b, c, g, slice of heads): any slice size that divides the group.  Built-in:
+    // the largest slice of at most 16 heads that still leaves a workgroup per CU (C B^T once per
+    // slice; a workgroup fills a CU).  Measured on MI355X: B2 L16384 H80 G8 slices of 10 / 5 / 2
+    // heads 398 / 433 / 533 us; B8 L4096 H32 slices of 16 / 8 / 4 / 2 163 / 162 / 185 / 222 us.
+    if (o.heads_per_block > 0 && hpg % o.heads_per_block == 0) return o.heads_per_block;
+    const long units = (long)B * nc * G;
+    for (int hs = hpg < 16 ? hpg : 16; hs > 1; --hs)
+      if (hpg % hs == 0 && units * (hpg / hs) >= 256) return hs;
+    return 1;
+  }
   if (o.heads_per_block > 0) {
     for (int hb : kChoices)
       if (hb == o.heads_per_block && hpg % hb == 0) return hb;
@@ -226,13 +241,15 @@ ssd_status_t fwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   a.dtp = has_seq ? reinterpret_cast<float*>(ws + wl.dtp_off) : nullptr;
   a.dAcs = has_seq ? reinterpret_cast<float*>(ws + wl.dacs_off) : nullptr;
   a.states = has_seq ? reinterpret_cast<float*>(ws + wl.states_off) : nullptr;
-  a.cb = has_seq && cb_shared(dims) ? reinterpret_cast<float*>(ws + wl.cb_off) : nullptr;
+  a.cb = nullptr;   // set below, once the scan's decomposition is known
   a.cbT = nullptr;
   a.prev16 = has_seq && dims->dtype == SSD_BF16 ? static_cast<void*>(ws + wl.prev16_off) : nullptr;
   a.keep_f32_states = 0;
-  a.scan_variant = pick_scan_variant(a.dtype, o);
+  a.scan_variant = pick_scan_variant(dims, chunk_size, o);
   a.rows_group = pick_rows_group(o);
   a.heads_per_block = pick_heads_per_block(a.B, a.nc, a.H, a.G, a.scan_variant, o);
+  // C B^T blocks for the row blocks and whole chunks to read (the group form forms its own)
+  a.cb = has_seq && cb_shared(dims) && a.scan_variant != 3 ? reinterpret_cast<float*>(ws + wl.cb_off) : nullptr;
   a.state_from_start = 0;
   a.passing_reverse = 0;
   a.ev0 = a.ev1 = nullptr;
@@ -387,9 +404,10 @@ ssd_status_t bwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   f.cbT = dims->dtype == SSD_F32 ? reinterpret_cast<float*>(ws + wl.cbT) : nullptr;
   f.prev16 = z && dims->dtype == SSD_BF16 ? static_cast<void*>(ws + wl.prev16) : nullptr;
   f.keep_f32_states = 1;                              // the backward kernels read the fp32 states
-  f.scan_variant = pick_scan_variant(f.dtype, o);
+  f.scan_variant = pick_scan_variant(dims, chunk_size, o);
   f.rows_group = pick_rows_group(o);
   f.heads_per_block = pick_heads_per_block(f.B, f.nc, f.H, f.G, f.scan_variant, o);
+  if (f.scan_variant == 3 && dims->dtype != SSD_F32) f.cb = nullptr;   // the group form forms its own
   f.state_from_start = 0;
   f.passing_reverse = 0;
   f.ev0 = f.ev1 = nullptr;

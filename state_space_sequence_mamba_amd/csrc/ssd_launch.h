@@ -37,8 +37,10 @@ struct FwdArgs {
                            // bf16 with many heads per group); null: chunk_state does not form them
   float* cbT;              // backward (fp32): the same blocks in bwd_dxdb's layout (cb_block TRANS);
                            // null: not formed
-  int heads_per_block;     // chunk_scan: heads sharing one C B^T evaluation (divides H / G)
-  int scan_variant;        // chunk_scan decomposition: 1 = 64-row blocks, 2 = whole chunks
+  int heads_per_block;     // chunk_scan: heads sharing one C B^T evaluation (divides H / G); for
+                           // scan_variant 3 the heads of a workgroup's slice
+  int scan_variant;        // chunk_scan decomposition: 1 = 64-row blocks, 2 = whole chunks, 3 = a
+                           // chunk of one group and a slice of its heads (bf16, chunk 256, P64 N128)
   int rows_group;          // row blocks: units per dispatch group on an XCD (0: all of one class first)
   hipEvent_t ev0, ev1;     // timing: start / stop events of the next launch (or null), recorded
                            // by the dispatch itself (hipExtLaunchKernelGGL), so they time the
@@ -125,6 +127,9 @@ hipError_t launch_state_passing(const FwdArgs& a, hipStream_t s);
 bool chunk_state_seq_supported(const FwdArgs& a, int ps);
 hipError_t launch_chunk_state_seq(const FwdArgs& a, int ps, hipStream_t s);
 hipError_t launch_chunk_scan(const FwdArgs& a, hipStream_t s);
+// scan_variant 3 (chunk_scan_group.hip): an instantiation exists for these sizes
+bool chunk_scan_group_supported(int dtype, int P, int N, int Q);
+hipError_t launch_chunk_scan_group(const FwdArgs& a, int hs, hipStream_t s);
 hipError_t launch_ssd_step(const StepArgs& a, hipStream_t s);
 hipError_t launch_bwd_dxdb(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dc(const BwdArgs& a, hipStream_t s);

@@ -29,7 +29,7 @@ SSD_KERNELS = ["chunk_state", "chunk_state_seq", "state_passing", "chunk_scan", 
 # (which picks launch shapes)
 KERNEL_SOURCE = {"chunk_state": "chunk_state.hip", "chunk_state_seq": "chunk_state.hip",
                  "state_passing": "state_passing.hip",
-                 "chunk_scan": "chunk_scan.hip", "ssd_step": "ssd_step.hip",
+                 "chunk_scan": ["chunk_scan.hip", "chunk_scan_group.hip"], "ssd_step": "ssd_step.hip",
                  "conv1d_silu": "conv1d.hip", "conv1d_silu_step": "conv1d.hip", "bwd_dxdb": "ssd_bwd.hip",
                  "bwd_dc": "ssd_bwd.hip", "bwd_finalize": "ssd_bwd.hip"}
 SHARED_SOURCES = ["ssd_common.h", "ssd_launch.h", "cb_tiles.h", "ssd_api.hip"]
@@ -38,7 +38,8 @@ SHARED_SOURCES = ["ssd_common.h", "ssd_launch.h", "cb_tiles.h", "ssd_api.hip"]
 def source_digest(kernel):
     """sha256 over the sources one kernel is built and launched from."""
     h = hashlib.sha256()
-    for name in [KERNEL_SOURCE[kernel]] + SHARED_SOURCES:
+    src = KERNEL_SOURCE[kernel]
+    for name in (src if isinstance(src, list) else [src]) + SHARED_SOURCES:
         h.update(name.encode())
         with open(os.path.join(PKG, "csrc", name), "rb") as fh:
             h.update(fh.read())
