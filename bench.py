@@ -37,12 +37,14 @@ KERNELS = ["chunk_state", "state_passing", "chunk_scan"]
 MAX_WORKERS = 16          # the host's CPU share per GPU
 
 
-def algorithmic_cost(w):
+def algorithmic_cost(w, seg_chunks=0):
     """Bytes each kernel must move (its inputs once, its outputs once) and the flops it must
-    do (causal half of the in-chunk products, C B^T once per group), per launch."""
+    do (causal half of the in-chunk products, C B^T once per group), per launch.  seg_chunks:
+    chunks per segment on the segmented chunk-state path (0 = not that path)."""
     e = 4 if w.dtype == "f32" else 2
     B, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
     nc = (L + Q - 1) // Q
+    nseg = -(-nc // seg_chunks) if seg_chunks else 0
     lens = [min(Q, L - c * Q) for c in range(nc)]
     cum = 2 * B * H * nc * Q * 4                       # dt' and its cumsum, fp32
     st = B * nc * H * P * N * 4                        # chunk states, fp32
@@ -68,12 +70,23 @@ def algorithmic_cost(w):
         "state_passing": dict(bytes=st + (st // 2 if not pre else st) + fin + B * H * nc * 4,
                               flops=2 * B * nc * H * P * N),
         # fp32 reads the C B^T blocks back once per head; bf16 forms C B^T inside chunk_scan
-        "chunk_scan": dict(bytes=2 * x + (cbr if pre else 2 * bc) + cum + (st if pre else st // 2) + H * P * 4,
+        # (segmented states: also each segment's incoming state, bf16, once per segment)
+        "chunk_scan": dict(bytes=2 * x + (cbr if pre else 2 * bc) + cum + (st if pre else st // 2) + H * P * 4
+                           + (nseg * B * H * P * N * 2 if seg_chunks else 0),
                            flops=2 * B * H * P * tri + 2 * B * H * L * N * P + (0 if pre else 2 * B * G * N * tri)),
+        # segmented: dt in, dt' and the cumsum out, x and B once, the states each segment carried
+        # into its chunks out (bf16, none for a segment's first chunk), the segments' end states
+        # out (fp32) and the exponents
+        "chunk_state_seg": dict(bytes=B * L * H * e + 8 * H + cum + x + bc + (nc - nseg) * B * H * P * N * 2
+                                + nseg * B * H * P * N * 4 + B * H * (nc + nseg) * 4,
+                                flops=2 * B * H * L * P * N),
+        # the recurrence over segments: end states in (fp32), incoming states out (bf16), final
+        "state_passing_seg": dict(bytes=nseg * B * H * P * N * (4 + 2) + fin + B * H * nseg * 4,
+                                  flops=2 * B * nseg * H * P * N),
     }
     for k, v in cost.items():
         peak_f = MFMA_PEAK_TFLOPS[w.dtype] * 1e12
-        t_f = v["flops"] / peak_f if k in ("chunk_state", "chunk_state_seq", "chunk_scan") else 0.0
+        t_f = v["flops"] / peak_f if k in ("chunk_state", "chunk_state_seq", "chunk_state_seg", "chunk_scan") else 0.0
         t_b = v["bytes"] / (HBM_PEAK_GBS * 1e9)
         v["bound"] = "mfma" if t_f > t_b else "hbm"
     return cost
@@ -546,15 +559,16 @@ def run_fwd(w, args, dev, opts, with_cpu):
     torch.cuda.synchronize()
 
     # the one-pass chunk-state path launches no state_passing (its event pair brackets nothing)
-    one_pass = ssd.fwd_state_path(dims, w.chunk, opts) == 2
-    names = ["chunk_state_seq", None, "chunk_scan"] if one_pass else KERNELS
+    path = ssd.fwd_state_path(dims, w.chunk, opts)
+    names = {2: ["chunk_state_seq", None, "chunk_scan"],
+             3: ["chunk_state_seg", "state_passing_seg", "chunk_scan"]}.get(path, KERNELS)
     per_kernel_ms = {k: 0.0 for k in names if k}
     for evs in events[:K]:
         for i, k in enumerate(names):
             if k:
                 per_kernel_ms[k] += hev.elapsed_ms(evs[2 * i], evs[2 * i + 1]) / K
 
-    cost = algorithmic_cost(w)
+    cost = algorithmic_cost(w, ssd.fwd_state_segment_chunks(dims, w.chunk, opts))
     kernels = {}
     for k in per_kernel_ms:
         t = per_kernel_ms[k] * 1e-3
@@ -604,7 +618,7 @@ def run_fwd(w, args, dev, opts, with_cpu):
 
 def launch_options(args):
     o = {k: getattr(args, k) for k in ("scan_variant", "heads_per_block", "rows_group", "state_path",
-                                       "state_slice", "conv_tokens") if getattr(args, k)}
+                                       "state_slice", "conv_tokens", "state_heads", "state_chunks") if getattr(args, k)}
     return o or None
 
 
@@ -633,9 +647,13 @@ def main():
                     help="chunk_scan row blocks: units per dispatch group on an XCD (0 = built-in, 16)")
     ap.add_argument("--state-path", type=int, default=0,
                     help="chunk states: 1 = chunk_state + state_passing, 2 = one pass over the chunks, "
-                         "0 = built-in")
+                         "3 = segments joined by state_passing, 0 = built-in")
     ap.add_argument("--state-slice", type=int, default=0,
                     help="one-pass chunk states: headdim rows per workgroup (0 = built-in)")
+    ap.add_argument("--state-heads", type=int, default=0,
+                    help="segmented chunk states: heads per workgroup (0 = built-in)")
+    ap.add_argument("--state-chunks", type=int, default=0,
+                    help="segmented chunk states: chunks per segment (0 = built-in)")
     ap.add_argument("--conv-tokens", type=int, default=0,
                     help="conv1d_silu tokens per thread, a multiple of 4 (0 = built-in)")
     args = ap.parse_args()

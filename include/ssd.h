@@ -80,14 +80,21 @@ typedef struct {
  *                                          state entering each chunk; on the one-pass path
  *                                          (ssd_fwd_state_path in ssd_tuning.h) fp32 inputs get
  *                                          the entering states only and bf16 inputs leave it
- *                                          unwritten
+ *                                          unwritten; on the segmented path it holds each
+ *                                          segment's end state from a zero start, (B, nseg, H,
+ *                                          P, N) fp32, then (256-byte aligned) the states
+ *                                          entering the segments in bf16, nseg = ceil(nc / SL)
  *   [3] SSD_F32, and SSD_BF16 with at least 20 heads per group: C B^T, computed once per
  *       group, (B, nc, G, nrb (nrb + 1) / 2) blocks of 16 x 256 fp32, nrb = chunk_size / 64:
  *       the causal 16 x 16 sub-tiles of each pair of 64-row blocks (row block rb, column
  *       block J <= rb), in the scan's register order; 0 bytes otherwise
  *   [4] SSD_BF16 only: the states entering each chunk rounded to bf16, (B, nc, H, P, N); for
  *       bf16 inputs region [2] keeps the per-chunk contributions (state_passing writes the
- *       entering states here instead)
+ *       entering states here instead); on the segmented path, the state each segment alone
+ *       carried into its chunks (slots of a segment's first chunk unwritten)
+ *   [5] SSD_BF16 only: two (B, H, nc) fp32 arrays (each 256-byte aligned), used on the
+ *       segmented path: the segments' total decay exponents (B, H, nseg), then for every chunk
+ *       the exponent summed from its segment's start
  * The contents after a call are those intermediates and may be inspected. */
 size_t ssd_fwd_workspace_size(const ssd_dims_t* dims, int chunk_size);
 

@@ -33,10 +33,15 @@ typedef struct {
   int32_t rows_group;       /* row blocks: units (b, c, head) per dispatch group on one XCD
                              * (built-in 16) */
   int32_t state_path;       /* chunk states: 1 = chunk_state then state_passing, 2 = one pass over
-                             * the chunks per (b, h, headdim slice); changes the order of the
-                             * state sums, so results agree to rounding */
+                             * the chunks per (b, h, headdim slice), 3 = segments of consecutive
+                             * chunks per (b, group, slice of heads), each from a zero state, joined
+                             * by state_passing over the segments (SSD_BF16, chunk 256, headdim 64,
+                             * dstate 128, with chunk_scan decomposition 3); the paths sum the states
+                             * in different orders, so results agree to rounding */
   int32_t state_slice;      /* one-pass chunk states: headdim rows per workgroup (0 = all) */
   int32_t conv_tokens;      /* ssd_conv1d_silu tokens per thread (rounded up to a multiple of 4) */
+  int32_t state_heads;      /* segmented chunk states: heads per workgroup (1, 2, 4 or 5) */
+  int32_t state_chunks;     /* segmented chunk states: chunks per segment (at least 2) */
 } ssd_launch_opts_t;
 
 /* ssd_fwd with options and per-kernel timing.  `opts` may be NULL.  `stage_events` is NULL or
@@ -87,8 +92,14 @@ ssd_status_t ssd_conv1d_silu_ex(const ssd_dims_t* dims, int conv_width, const vo
 /* Which chunk-state path ssd_fwd_ex takes for these sizes and options (NULL = the built-in
  * choice of ssd_fwd): 1 = chunk_state then state_passing (three forward kernels), 2 = one pass
  * over the chunks (two forward kernels: no state_passing launch; the state_passing events of
- * ssd_fwd_ex then bracket no kernel), 0 = invalid or empty arguments.  Pure host logic. */
+ * ssd_fwd_ex then bracket no kernel), 3 = segmented chunk states (chunk_state_seg in place of
+ * chunk_state, state_passing over the segments), 0 = invalid or empty arguments.  Pure host
+ * logic. */
 int ssd_fwd_state_path(const ssd_dims_t* dims, int chunk_size, const ssd_launch_opts_t* opts);
+
+/* Chunks per segment on the segmented path (3) for these sizes and options, 0 on the other paths
+ * or for invalid or empty arguments.  Pure host logic. */
+int ssd_fwd_state_segment_chunks(const ssd_dims_t* dims, int chunk_size, const ssd_launch_opts_t* opts);
 
 #ifdef __cplusplus
 }

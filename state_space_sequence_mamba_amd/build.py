@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libssd.so")
 
-SOURCES = ["ssd_api.hip", "chunk_state.hip", "state_passing.hip", "chunk_scan.hip", "chunk_scan_group.hip",
+SOURCES = ["ssd_api.hip", "chunk_state.hip", "chunk_state_seg.hip", "state_passing.hip", "chunk_scan.hip",
+           "chunk_scan_group.hip",
            "ssd_step.hip", "conv1d.hip", "ssd_bwd.hip"]
 # measurement only (bench.py --peak-probe): register-resident MFMA loops, a library of its own
 PEAK_SOURCES = ["peak_probe.hip"]

@@ -36,6 +36,14 @@ constexpr int kGThreads = 512;                  // eight wavefronts
 constexpr int kGSub = kGS + 1;                  // causal sub-tiles per wavefront (strip pair)
 constexpr float kGLog2e = 1.4426950408889634f;
 
+// two fp32 values rounded to bf16 (nearest-even) in one 32-bit word, and back
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const __bf16 l = static_cast<__bf16>(lo), h = static_cast<__bf16>(hi);
+  return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+}
+__device__ __forceinline__ float unpack_lo(uint32_t v) { return __builtin_bit_cast(float, v << 16); }
+__device__ __forceinline__ float unpack_hi(uint32_t v) { return __builtin_bit_cast(float, v & 0xffff0000u); }
+
 template <int P, int N>
 struct GroupLds {
   static constexpr int BP = N + 8;              // B rows / Hprev rows, n-contiguous (bf16)
@@ -65,14 +73,18 @@ struct HeadRegs {
   static_assert(XU % kGThreads == 0 && PU % kGThreads == 0, "shape");
   uint4 x[XPT][2];
   uint4 pv[PPT];
-  float dt, da, dd;
+  uint4 hv[PPT];           // segmented states: the state entering the segment (else unused)
+  float dt, da, dd, sdec;  // sdec: exp of the decay since the segment start; < 0: no segments
   uint32_t okm;
 
   // Per-lane element offsets from the head's (wavefront-uniform) base pointers, 32-bit: the
   // loads take a scalar base plus a vector offset.  The offsets are made opaque at each call so
   // the compiler does not keep precomputed 64-bit addresses alive across the head loop.
+  // hh: the segment's incoming state (null without segments); first: c opens its segment (no
+  // carried part of its own); ecd: the decay exponent since the segment start
   __device__ __forceinline__ void load(const __bf16* xh, const __bf16* ph, const float* dth, const float* dah,
-                                       const float* Dh, uint32_t x_tok, int len, int tid) {
+                                       const float* Dh, uint32_t x_tok, int len, int tid, const __bf16* hh = nullptr,
+                                       bool first = false, const float* ecd = nullptr) {
     uint32_t xo[XPT][2], po[PPT];
     okm = 0;
 #pragma unroll
@@ -100,6 +112,15 @@ struct HeadRegs {
     }
 #pragma unroll
     for (int u = 0; u < PPT; ++u) pv[u] = *reinterpret_cast<const uint4*>(ph + po[u]);
+    sdec = -1.f;
+    if (hh) {
+#pragma unroll
+      for (int u = 0; u < PPT; ++u) {
+        hv[u] = *reinterpret_cast<const uint4*>(hh + po[u]);
+        if (first) pv[u] = make_uint4(0, 0, 0, 0);   // (that slot holds no state of this segment)
+      }
+      sdec = __expf(*ecd);
+    }
     dt = dth[io];
     da = dah[io];
     dd = Dh ? Dh[Do] : 0.f;
@@ -132,7 +153,21 @@ struct HeadRegs {
     for (int u = 0; u < PPT; ++u) {
       const int v = tid + kGThreads * u;
       const int p = (v * 8) / N, n = (v * 8) % N;
-      *reinterpret_cast<uint4*>(&s_prev[p * L::BP + n]) = pv[u];
+      uint4 o = pv[u];
+      if (sdec >= 0.f) {
+        // segmented states: the entering state is the segment's own carry plus the decayed
+        // state that entered the segment, rounded to bf16 as the scan reads it
+        const uint32_t lv[4] = {pv[u].x, pv[u].y, pv[u].z, pv[u].w}, iv[4] = {hv[u].x, hv[u].y, hv[u].z, hv[u].w};
+        uint32_t ov[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float l0 = __builtin_bit_cast(float, lv[q] << 16), l1 = __builtin_bit_cast(float, lv[q] & 0xffff0000u);
+          const float i0 = __builtin_bit_cast(float, iv[q] << 16), i1 = __builtin_bit_cast(float, iv[q] & 0xffff0000u);
+          ov[q] = pack_bf16(l0 + sdec * i0, l1 + sdec * i1);
+        }
+        o = make_uint4(ov[0], ov[1], ov[2], ov[3]);
+      }
+      *reinterpret_cast<uint4*>(&s_prev[p * L::BP + n]) = o;
     }
     if (tid < kGQ) {
       const float d2 = da * kGLog2e;
@@ -145,14 +180,6 @@ struct HeadRegs {
   }
 };
 
-// two fp32 values rounded to bf16 (nearest-even) in one 32-bit word, and back
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  const __bf16 l = static_cast<__bf16>(lo), h = static_cast<__bf16>(hi);
-  return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
-}
-__device__ __forceinline__ float unpack_lo(uint32_t v) { return __builtin_bit_cast(float, v << 16); }
-__device__ __forceinline__ float unpack_hi(uint32_t v) { return __builtin_bit_cast(float, v & 0xffff0000u); }
-
 }  // namespace
 
 template <int P, int N>
@@ -160,7 +187,7 @@ __global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
     const __bf16* __restrict__ x, const __bf16* __restrict__ Bm, const __bf16* __restrict__ Cm,
     const float* __restrict__ dtp, const float* __restrict__ dAcs, const __bf16* __restrict__ prev16,
     const float* __restrict__ Dw, const __bf16* __restrict__ Z, __bf16* __restrict__ y, int L, int H, int G, int nc,
-    int hs, uint32_t nblocks) {
+    int hs, uint32_t nblocks, const __bf16* __restrict__ hin16, const float* __restrict__ cdec, int seg_len) {
   typedef GroupLds<P, N> SL;
   typedef NDot<__bf16, N> ND;
   typedef HeadRegs<P, N> HR;
@@ -208,6 +235,14 @@ __global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
     Dh = Dw ? Dw + (size_t)h * P : nullptr;
   };
 
+  // segmented chunk states: the state entering c's segment and the decay since its start
+  const bool seg_first = seg_len > 0 && c % seg_len == 0;
+  auto seg_in = [&](int h) -> const __bf16* {
+    return seg_len > 0 ? hin16 + (((size_t)b * ((nc + seg_len - 1) / seg_len) + c / seg_len) * H + h) * (size_t)(P * N)
+                       : nullptr;
+  };
+  auto seg_dec = [&](int h) { return cdec + ((size_t)b * H + h) * nc + c; };
+
   // ---- prologue: B rows of the chunk, this wavefront's C rows, the first head's inputs
   constexpr int BU = kGQ * N / 8, BPT = BU / kGThreads;       // 16-byte vectors of B
   uint4 breg[BPT];
@@ -230,7 +265,7 @@ __global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
     const __bf16 *xh, *ph;
     const float *dth, *dah, *Dh;
     head_ptrs(h0, xh, ph, dth, dah, Dh);
-    hr.load(xh, ph, dth, dah, Dh, (uint32_t)x_tok, len, tid);
+    hr.load(xh, ph, dth, dah, Dh, (uint32_t)x_tok, len, tid, seg_in(h0), seg_first, seg_dec(h0));
   }
 #pragma unroll
   for (int u = 0; u < BPT; ++u) {
@@ -272,7 +307,7 @@ __global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
       const __bf16 *xh, *ph;
       const float *dth, *dah, *Dh;
       head_ptrs(h + 1, xh, ph, dth, dah, Dh);
-      hr.load(xh, ph, dth, dah, Dh, (uint32_t)x_tok, len, tid);
+      hr.load(xh, ph, dth, dah, Dh, (uint32_t)x_tok, len, tid, seg_in(h + 1), seg_first, seg_dec(h + 1));
     }
 
     // per-lane LDS offsets, opaque to the compiler at every head: otherwise it hoists the 68
@@ -420,7 +455,8 @@ hipError_t launch_chunk_scan_group(const FwdArgs& a, int hs, hipStream_t s) {
   hipExtLaunchKernelGGL(chunk_scan_group_kernel<64, 128>, dim3(nblocks), dim3(kGThreads), 0, s, a.ev0, a.ev1, 0,
                         static_cast<const __bf16*>(a.x), static_cast<const __bf16*>(a.Bm),
                         static_cast<const __bf16*>(a.Cm), a.dtp, a.dAcs, static_cast<const __bf16*>(a.prev16), a.D,
-                        static_cast<const __bf16*>(a.z), static_cast<__bf16*>(a.y), a.L, a.H, a.G, a.nc, hs, nblocks);
+                        static_cast<const __bf16*>(a.z), static_cast<__bf16*>(a.y), a.L, a.H, a.G, a.nc, hs, nblocks,
+                        static_cast<const __bf16*>(a.hin16), a.cdec, a.seg_len);
   return hipGetLastError();
 }
 

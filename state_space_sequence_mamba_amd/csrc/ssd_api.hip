@@ -39,8 +39,16 @@ ssd_status_t check_dims(const ssd_dims_t* d, bool need_seqlen) {
 bool chunk_ok(int q) { return q == 64 || q == 128 || q == 256; }
 
 struct WsLayout {
-  size_t dtp_off, dacs_off, states_off, cb_off, prev16_off, total;
+  size_t dtp_off, dacs_off, states_off, cb_off, prev16_off, segs_off, total;
 };
+
+// bf16 only: the segmented chunk-state path's per-(b, h) exponents, segment totals then the
+// exponents from each chunk's segment start, 2 x (B, H, nc) fp32 (at most nc segments)
+size_t segs_bytes(const ssd_dims_t* d, int Q) {
+  if (d->dtype != SSD_BF16) return 0;
+  const int64_t nc = (d->seqlen + Q - 1) / Q;
+  return 2 * align_up((size_t)d->batch * d->nheads * nc * sizeof(float));
+}
 
 // bf16 only: the states entering each chunk rounded to bf16, (B, nc, H, P, N)
 size_t prev16_bytes(const ssd_dims_t* d, int Q) {
@@ -74,7 +82,8 @@ WsLayout ws_layout(const ssd_dims_t* d, int Q) {
   w.states_off = 2 * cum;
   w.cb_off = 2 * cum + st;
   w.prev16_off = w.cb_off + cb_bytes(d, Q);
-  w.total = w.prev16_off + prev16_bytes(d, Q);
+  w.segs_off = w.prev16_off + prev16_bytes(d, Q);
+  w.total = w.segs_off + segs_bytes(d, Q);
   return w;
 }
 
@@ -95,29 +104,91 @@ bool device_ptr_ok(const void* p) {
 const ssd_launch_opts_t kBuiltin{};
 const ssd_launch_opts_t& opts_or_builtin(const ssd_launch_opts_t* o) { return o ? *o : kBuiltin; }
 
-// Chunk states: either per (b, c, h) in parallel followed by the sequential state_passing
-// launch, or one pass per (b, h, headdim slice) walking the chunks in order with the state in
-// registers (no per-chunk states in memory).  Returns the slice rows of the one-pass kernel, or
-// 0 for the two-launch path.  Built-in choice, measured on MI355X (bf16 P64 N128): one pass from
-// B H >= 256 (B8 L4096 H32 forward 0.320 -> 0.277 ms, B16 L2048 0.338 -> 0.299, B8 L1024
-// 0.092 -> 0.082, B8 L4096 chunk 128 0.378 -> 0.344), two launches below (B4 L4096 H32 0.163
-// against 0.172 ms; B2 L16384 H80 G8 0.793 against 0.823: too few workgroups for 256 CUs, each
-// with a long chain of chunks); fp32 keeps two launches (B4 L1024 H24 0.0695 against 0.0765 ms
-// at 32-row slices, B16 L1024 H24 0.230 against 0.228 at whole rows).
-int pick_state_seq(int dtype, int64_t B, int64_t H, int P, int N, int Q, bool forward_only,
-                   const ssd_launch_opts_t& o) {
-  if (o.state_path == 1 || !forward_only) return 0;
+// Chunk states.  Three paths:
+//  1: chunk_state per (b, c, h) in parallel, then the sequential state_passing launch;
+//  2: one pass per (b, h, headdim slice) walking the chunks in order with the state in registers
+//     (no per-chunk states in memory);
+//  3: segments of SL chunks per (b, group, slice of hs heads), each from a zero state, combined
+//     by state_passing over segments, the scan adding each segment's incoming state (needs the
+//     scan's group form, which applies that correction).
+struct StatePath {
+  int path = 1;
+  int ps = 0;            // path 2: headdim rows per workgroup
+  int hs = 0, SL = 0;    // path 3: heads per workgroup, chunks per segment
+};
+
+int seg_heads(int hpg, int want) {
+  if (want > 0) return ssd::chunk_state_seg_supported(ssd::DT_BF16, 64, 128, 256, want) && hpg % want == 0 ? want : 0;
+  for (int hs : {5, 4, 2, 1})
+    if (hpg % hs == 0) return hs;
+  return 0;
+}
+
+// Built-in choice, measured on MI355X (bf16 P64 N128): one pass from B H >= 256 (B8 L4096 H32
+// forward 0.320 -> 0.277 ms, B16 L2048 0.338 -> 0.299, B8 L1024 0.092 -> 0.082, B8 L4096 chunk
+// 128 0.378 -> 0.344); below that the one-pass chains are too few for 256 CUs (B4 L4096 H32 0.163
+// against 0.172 ms for two launches; B2 L16384 H80 G8 0.793 against 0.823), and segments take
+// over where the scan's group form applies (below); fp32 keeps two launches (B4 L1024 H24 0.0695
+// against 0.0765 ms at 32-row slices, B16 L1024 H24 0.230 against 0.228 at whole rows).
+StatePath pick_state_path(int dtype, int64_t B, int64_t H, int64_t G, int P, int N, int Q, int nc, bool forward_only,
+                          int scan_variant, const ssd_launch_opts_t& o) {
+  StatePath sp;
+  if (o.state_path == 1 || !forward_only) return sp;
   ssd::FwdArgs a{};
   a.dtype = dtype;
   a.P = P;
   a.N = N;
   a.Q = Q;
+  if (o.state_path == 3) {
+    // segments: SL chunks each, at least two so that the segment states fit the chunk-state region
+    const int hs = seg_heads((int)(H / G), o.state_heads);
+    if (hs > 0 && scan_variant == 3 && ssd::chunk_state_seg_supported(dtype, P, N, Q, hs)) {
+      const int SL = o.state_chunks > 0 ? o.state_chunks : 8;
+      const int nseg = (nc + SL - 1) / SL;
+      if (SL >= 2 && 3 * nseg <= 2 * nc) {
+        sp.path = 3;
+        sp.hs = hs;
+        sp.SL = SL;
+        return sp;
+      }
+    }
+    return sp;
+  }
   if (o.state_path == 2) {
     const int ps = o.state_slice > 0 ? o.state_slice : P;
-    return ssd::chunk_state_seq_supported(a, ps) ? ps : 0;
+    if (ssd::chunk_state_seq_supported(a, ps)) {
+      sp.path = 2;
+      sp.ps = ps;
+    }
+    return sp;
   }
-  if (dtype != ssd::DT_BF16 || P != 64 || N != 128 || B * H < 256) return 0;
-  return ssd::chunk_state_seq_supported(a, 64) ? 64 : 0;
+  if (dtype != ssd::DT_BF16 || P != 64 || N != 128) return sp;
+  if (B * H >= 256) {
+    if (ssd::chunk_state_seq_supported(a, 64)) {
+      sp.path = 2;
+      sp.ps = 64;
+    }
+    return sp;
+  }
+  // fewer chains than CUs: segments, sized for at least 256 workgroups.  Measured on MI355X, bf16
+  // B2 L16384 H80 G8 (64 chunks, 5 heads per workgroup): segments of 8 / 4 / 2 chunks 0.701 /
+  // 0.724 / 0.752 ms per forward against 0.808 for two launches (chunk_state 256 + state_passing
+  // 85 us -> 209 + 11 us; the scan's correction costs it 404 -> 445 us); the one-pass path keeps
+  // B8 L4096 H32 (0.252 ms against 0.266 with segments of 4)
+  // (segment sizes given in the options apply here too)
+  const int hs = seg_heads((int)(H / G), o.state_heads);
+  if (hs > 0 && scan_variant == 3 && ssd::chunk_state_seg_supported(dtype, P, N, Q, hs) && nc >= 3) {
+    const long per_seg = B * G * ((H / G) / hs);                 // workgroups per segment index
+    const int nseg_want = (int)((256 + per_seg - 1) / per_seg);
+    int SL = o.state_chunks > 0 ? o.state_chunks : (nc + nseg_want - 1) / nseg_want;
+    if (SL < 2) SL = 2;
+    if (3 * ((nc + SL - 1) / SL) <= 2 * nc) {
+      sp.path = 3;
+      sp.hs = hs;
+      sp.SL = SL;
+    }
+  }
+  return sp;
 }
 
 // Row-block dispatch groups of 16 units per XCD: measured on MI355X, bf16 B2 L16384 H80 G8
@@ -252,6 +323,9 @@ ssd_status_t fwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   a.cb = has_seq && cb_shared(dims) && a.scan_variant != 3 ? reinterpret_cast<float*>(ws + wl.cb_off) : nullptr;
   a.state_from_start = 0;
   a.passing_reverse = 0;
+  a.seg_len = 0;
+  a.hin16 = nullptr;
+  a.cdec = nullptr;
   a.ev0 = a.ev1 = nullptr;
 
   if (!has_seq) {
@@ -268,9 +342,39 @@ ssd_status_t fwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
     a.ev0 = ev ? ev[2 * k] : nullptr;
     a.ev1 = ev ? ev[2 * k + 1] : nullptr;
   };
-  if (const int ps = pick_state_seq(a.dtype, a.B, a.H, a.P, a.N, a.Q, !a.keep_f32_states && !a.state_from_start, o)) {
+  const StatePath sp = pick_state_path(a.dtype, a.B, a.H, a.G, a.P, a.N, a.Q, a.nc,
+                                      !a.keep_f32_states && !a.state_from_start, a.scan_variant, o);
+  if (sp.path == 3) {
+    // segment states from zero (into the chunk-state region: end states in fp32, then the
+    // incoming states in bf16), their exponents in the segments region; state_passing over the
+    // segments; the scan adds each segment's incoming state
+    ssd::SegArgs sg;
+    sg.hs = sp.hs;
+    sg.SL = sp.SL;
+    sg.nseg = (a.nc + sp.SL - 1) / sp.SL;
+    const size_t pnh = (size_t)a.B * sg.nseg * a.H * a.P * a.N;
+    sg.E = a.states;
+    __bf16* hin16 = reinterpret_cast<__bf16*>(reinterpret_cast<char*>(a.states) + align_up(pnh * sizeof(float)));
+    sg.segdec = reinterpret_cast<float*>(ws + wl.segs_off);
+    sg.cdec = sg.segdec + align_up((size_t)a.B * a.H * a.nc * sizeof(float)) / sizeof(float);
     stage(0);
-    if (ssd::launch_chunk_state_seq(a, ps, stream) != hipSuccess) return SSD_ERR_HIP;
+    if (ssd::launch_chunk_state_seg(a, sg, stream) != hipSuccess) return SSD_ERR_HIP;
+    ssd::FwdArgs cp = a;   // the recurrence over segments: "chunks" of length 1 with the segments' exponents
+    cp.nc = sg.nseg;
+    cp.Q = 1;
+    cp.dAcs = sg.segdec;
+    cp.states = sg.E;
+    cp.prev16 = hin16;
+    cp.keep_f32_states = 0;
+    cp.ev0 = ev ? ev[2] : nullptr;
+    cp.ev1 = ev ? ev[3] : nullptr;
+    if (ssd::launch_state_passing(cp, stream) != hipSuccess) return SSD_ERR_HIP;
+    a.seg_len = sp.SL;
+    a.hin16 = hin16;
+    a.cdec = sg.cdec;
+  } else if (sp.path == 2) {
+    stage(0);
+    if (ssd::launch_chunk_state_seq(a, sp.ps, stream) != hipSuccess) return SSD_ERR_HIP;
     // no state_passing launch: its event pair brackets nothing
     if (ev && (hipEventRecord(ev[2], stream) != hipSuccess || hipEventRecord(ev[3], stream) != hipSuccess))
       return SSD_ERR_HIP;
@@ -410,6 +514,9 @@ ssd_status_t bwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   if (f.scan_variant == 3 && dims->dtype != SSD_F32) f.cb = nullptr;   // the group form forms its own
   f.state_from_start = 0;
   f.passing_reverse = 0;
+  f.seg_len = 0;
+  f.hin16 = nullptr;
+  f.cdec = nullptr;
   f.ev0 = f.ev1 = nullptr;
   a.dy = z ? static_cast<const void*>(ws + wl.dyg) : dout;
   a.gstates = reinterpret_cast<float*>(ws + wl.gstates);
@@ -755,9 +862,20 @@ const char* ssd_status_string(ssd_status_t s) {
 int ssd_fwd_state_path(const ssd_dims_t* dims, int chunk_size, const ssd_launch_opts_t* opts) {
   if (check_dims(dims, true) != SSD_OK || !chunk_ok(chunk_size) || dims->seqlen == 0 || dims->batch == 0) return 0;
   const int dtype = dims->dtype == SSD_F32 ? ssd::DT_F32 : ssd::DT_BF16;
-  return pick_state_seq(dtype, dims->batch, dims->nheads, (int)dims->headdim, (int)dims->dstate, chunk_size, true,
-                        opts_or_builtin(opts))
-             ? 2 : 1;
+  const ssd_launch_opts_t& o = opts_or_builtin(opts);
+  const int nc = (int)((dims->seqlen + chunk_size - 1) / chunk_size);
+  return pick_state_path(dtype, dims->batch, dims->nheads, dims->ngroups, (int)dims->headdim, (int)dims->dstate,
+                         chunk_size, nc, true, pick_scan_variant(dims, chunk_size, o), o).path;
+}
+
+int ssd_fwd_state_segment_chunks(const ssd_dims_t* dims, int chunk_size, const ssd_launch_opts_t* opts) {
+  if (check_dims(dims, true) != SSD_OK || !chunk_ok(chunk_size) || dims->seqlen == 0 || dims->batch == 0) return 0;
+  const int dtype = dims->dtype == SSD_F32 ? ssd::DT_F32 : ssd::DT_BF16;
+  const ssd_launch_opts_t& o = opts_or_builtin(opts);
+  const int nc = (int)((dims->seqlen + chunk_size - 1) / chunk_size);
+  const StatePath sp = pick_state_path(dtype, dims->batch, dims->nheads, dims->ngroups, (int)dims->headdim,
+                                       (int)dims->dstate, chunk_size, nc, true, pick_scan_variant(dims, chunk_size, o), o);
+  return sp.path == 3 ? sp.SL : 0;
 }
 
 }  // extern "C"

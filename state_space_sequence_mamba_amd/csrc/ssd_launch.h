@@ -48,6 +48,19 @@ struct FwdArgs {
   int state_from_start;    // chunk_state weights exp(dAcs_i) instead of exp(last - dAcs_i) dt'_i,
                            // reading dt' and the cumsum instead of computing them
   int passing_reverse;     // state_passing from the last chunk to the first
+  // segmented chunk states (chunk_state_seg): prev16 holds the states each segment alone carried
+  // into its chunks (none for a segment's first chunk); chunk_scan adds exp(cdec) hin16
+  int seg_len;             // chunks per segment, 0 = no segments
+  const void* hin16;       // (B, nseg, H, P, N) bf16: the state entering each segment
+  const float* cdec;       // (B, H, nc): exponent of the decay from the segment start to chunk c
+};
+
+// The segmented chunk-state launch: heads per workgroup, chunks per segment, and its outputs.
+struct SegArgs {
+  int hs, SL, nseg;
+  float* E;                // (B, nseg, H, P, N) fp32: each segment's end state from a zero start
+  float* segdec;           // (B, H, nseg): the segment's total decay exponent
+  float* cdec;             // (B, H, nc)
 };
 
 // Backward pass (ssd_bwd): the forward's workspace regions plus the gradient buffers.
@@ -129,6 +142,9 @@ hipError_t launch_chunk_state_seq(const FwdArgs& a, int ps, hipStream_t s);
 hipError_t launch_chunk_scan(const FwdArgs& a, hipStream_t s);
 // scan_variant 3 (chunk_scan_group.hip): an instantiation exists for these sizes
 bool chunk_scan_group_supported(int dtype, int P, int N, int Q);
+// segmented chunk states (chunk_state_seg.hip), hs heads per workgroup
+bool chunk_state_seg_supported(int dtype, int P, int N, int Q, int hs);
+hipError_t launch_chunk_state_seg(const FwdArgs& a, const SegArgs& sg, hipStream_t s);
 hipError_t launch_chunk_scan_group(const FwdArgs& a, int hs, hipStream_t s);
 hipError_t launch_ssd_step(const StepArgs& a, hipStream_t s);
 hipError_t launch_bwd_dxdb(const BwdArgs& a, hipStream_t s);

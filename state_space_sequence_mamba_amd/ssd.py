@@ -30,7 +30,8 @@ class ssd_launch_opts_t(ctypes.Structure):
     """Launch-shape options of the measurement entry points (include/ssd_tuning.h); 0 = built-in."""
     _fields_ = [("scan_variant", ctypes.c_int32), ("heads_per_block", ctypes.c_int32),
                 ("min_blocks", ctypes.c_int32), ("rows_group", ctypes.c_int32), ("state_path", ctypes.c_int32),
-                ("state_slice", ctypes.c_int32), ("conv_tokens", ctypes.c_int32)]
+                ("state_slice", ctypes.c_int32), ("conv_tokens", ctypes.c_int32), ("state_heads", ctypes.c_int32),
+                ("state_chunks", ctypes.c_int32)]
 
 
 def launch_opts(**fields):
@@ -103,6 +104,8 @@ def load_library():
     lib.ssd_status_string.argtypes = [i32]
     lib.ssd_status_string.restype = ctypes.c_char_p
     lib.ssd_fwd_state_path.argtypes = [dims_p, i32, opts_p]
+    lib.ssd_fwd_state_segment_chunks.argtypes = [dims_p, i32, opts_p]
+    lib.ssd_fwd_state_segment_chunks.restype = i32
     lib.ssd_fwd_state_path.restype = i32
     _lib = lib
     return lib
@@ -370,5 +373,11 @@ def conv1d_silu_step(conv_state, xbc, weight, bias, nheads, headdim, dstate, ngr
 
 
 def fwd_state_path(dims, chunk_size, opts=None):
-    """1: chunk_state then state_passing; 2: one pass over the chunks; 0: invalid or empty."""
+    """1: chunk_state then state_passing; 2: one pass over the chunks; 3: segmented chunk states;
+    0: invalid or empty."""
     return int(load_library().ssd_fwd_state_path(ctypes.byref(dims), int(chunk_size), _opts_ref(opts)))
+
+
+def fwd_state_segment_chunks(dims, chunk_size, opts=None):
+    """Chunks per segment on the segmented chunk-state path, 0 on the other paths."""
+    return int(load_library().ssd_fwd_state_segment_chunks(ctypes.byref(dims), int(chunk_size), _opts_ref(opts)))

@@ -88,9 +88,10 @@ def test_workspace_size_layout(lib):
     # 4 chunks * 1 group * 1 block pair (Q/64 = 1) * 16 KB = 65536 B
     assert ssd.ssd_fwd_workspace_size(_dims(), 64) == 2 * 4096 + 16384 + 65536
     # ragged: L=300, Q=128 -> nc=3; 2*4*3*128*4 = 12288 B each; states 2*3*4*64*128*4 = 786432 B;
-    # bf16 adds the entering states rounded to bf16: 786432 / 2 B
+    # bf16 adds the entering states rounded to bf16 (786432 / 2 B) and the segmented path's
+    # exponents, 2 x (B, H, nc) floats, each region 256-aligned: 2 * 256 B
     d = _dims(batch=2, seqlen=300, headdim=64, dstate=128, dtype=1)
-    assert ssd.ssd_fwd_workspace_size(d, 128) == 2 * 12288 + 786432 + 393216
+    assert ssd.ssd_fwd_workspace_size(d, 128) == 2 * 12288 + 786432 + 393216 + 2 * 256
     # 1 x 5 tokens, H=3, Q=64: 3*64*4 = 768 B (already 256-aligned); states 3*16*16*4 = 3072; C B^T 16 KB
     assert ssd.ssd_fwd_workspace_size(_dims(seqlen=5, nheads=3), 64) == 2 * 768 + 3072 + 16384
     # alignment padding: H=1, L=1, Q=64 -> 256 B regions
@@ -237,13 +238,15 @@ def test_product_package_never_imports_the_oracle():
 
 def test_fwd_state_path_choice_is_host_logic():
     """The chunk-state path ssd_fwd takes (pure host logic, no GPU needed): one pass for bf16
-    P64 N128 from batch x heads >= 256, two launches otherwise; per-call options force either where
-    an instantiation exists; invalid or empty sizes give 0."""
+    P64 N128 from batch x heads >= 256, segments below that at chunk 256 (three or more chunks),
+    two launches otherwise; per-call options force a path where an instantiation exists; invalid
+    or empty sizes give 0."""
     import torch
     bf, f32 = torch.bfloat16, torch.float32
     cases = [((8, 4096, 32, 64, 128, 1, bf), 256, 2), ((8, 4096, 32, 64, 128, 1, bf), 128, 2),
-             ((8, 4096, 32, 64, 128, 1, bf), 64, 1), ((4, 4096, 32, 64, 128, 1, bf), 256, 1),
-             ((2, 16384, 80, 64, 128, 8, bf), 256, 1), ((8, 4096, 32, 64, 64, 1, bf), 256, 1),
+             ((8, 4096, 32, 64, 128, 1, bf), 64, 1), ((4, 4096, 32, 64, 128, 1, bf), 256, 3),
+             ((2, 16384, 80, 64, 128, 8, bf), 256, 3), ((2, 512, 8, 64, 128, 1, bf), 256, 1),
+             ((4, 4096, 32, 64, 128, 1, bf), 128, 1), ((8, 4096, 32, 64, 64, 1, bf), 256, 1),
              ((16, 1024, 24, 64, 64, 1, f32), 256, 1), ((8, 0, 32, 64, 128, 1, bf), 256, 0),
              ((8, 4096, 32, 64, 128, 1, bf), 100, 0)]
     for args, q, want in cases:
@@ -254,6 +257,11 @@ def test_fwd_state_path_choice_is_host_logic():
     # no such instantiation: two launches
     assert ssd.fwd_state_path(p(4, 1024, 24, 64, 64, 1, f32), 256, {"state_path": 2, "state_slice": 16}) == 1
     assert ssd.fwd_state_path(p(8, 4096, 32, 64, 128, 1, bf), 256, {"state_path": 1}) == 1
+    # segments of 8 chunks for the B2 L16384 H80 G8 shape (at least 256 workgroups), forced sizes
+    assert ssd.fwd_state_segment_chunks(p(2, 16384, 80, 64, 128, 8, bf), 256) == 8
+    assert ssd.fwd_state_segment_chunks(p(2, 16384, 80, 64, 128, 8, bf), 256, {"state_chunks": 4}) == 4
+    assert ssd.fwd_state_segment_chunks(p(8, 4096, 32, 64, 128, 1, bf), 256) == 0
+    assert ssd.fwd_state_path(p(8, 4096, 32, 64, 128, 1, bf), 256, {"state_path": 3, "state_heads": 4}) == 3
     # options are per call: nothing of the calls above is kept
     assert ssd.fwd_state_path(p(8, 4096, 32, 64, 128, 1, bf), 256) == 2
     assert ssd.fwd_state_path(p(4, 1024, 24, 64, 64, 1, f32), 256, ssd.launch_opts()) == 1

@@ -164,7 +164,7 @@ def test_one_pass_stage_intermediates(dtype):
         states = f[2 * cum_al // 4: 2 * cum_al // 4 + n_st].view(Bt, nc, H, P, N)
         assert rel_err(to64(states), r_prev) <= TOL[dtype]
     else:
-        off = ws.numel() - (n_st * 2 + 255) // 256 * 256          # region [4], the last one
+        off = 2 * cum_al + (n_st * 4 + 255) // 256 * 256          # region [4] (no C B^T region: 2 heads per group)
         prev16 = ws[off: off + n_st * 2].view(torch.bfloat16).view(Bt, nc, H, P, N)
         assert rel_err(to64(prev16), r_prev) <= TOL[dtype]
 
