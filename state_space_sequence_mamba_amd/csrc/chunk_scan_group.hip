@@ -15,13 +15,16 @@
 // Eight wavefronts; wavefront w owns the strip pair (w, 15 - w) of the chunk's sixteen 16-row
 // strips, i.e. w + 1 and 16 - w causal 16x16 sub-tiles, 17 for every wavefront.  The CB sub-tiles
 // (16x16x32 bf16 MFMA over dstate, from the chunk's B and C rows staged in LDS) stay in registers
-// for all heads; the C rows stay in LDS for the carried term.  Per head: the carried term C Hprev^T on MFMA (Hprev staged in LDS),
-// then every sub-tile's decay in registers (below the diagonal a row factor times a per-column
+// for all heads; the C rows stay in LDS for the carried term.  Per head: the carried terms
+// C Hprev^T of both strips on MFMA (Hprev staged in LDS), then the 17 sub-tiles as one software
+// pipeline (the next sub-tile's LDS operands in flight during the current one's MFMAs), each
+// sub-tile's decay formed in registers (below the diagonal a row factor times a per-column
 // weight, both <= 1: one exponential per lane; on the diagonal one per element and the causal
-// mask) rounded to bf16 as the A operand of the 16x16x16 bf16 MFMA with the x^T tile in LDS; the
-// skip term on the diagonal sub-tile, whose x values are the lane's own output rows.  The next
-// head's x, entering state and cumsums are loaded into registers while the current head computes
-// (two barriers per head), and y leaves through an LDS staging tile as 16-byte row stores.
+// mask) and rounded to bf16 as the A operand of the 16x16x16 bf16 MFMA with the x^T tile; the
+// skip term on the diagonal sub-tiles, whose x values are the lane's own output rows.  The inputs of
+// head h + 2 are loaded into registers as soon as those of head h + 1 are in LDS, so they are in
+// flight during head h + 1's MFMAs and are issued ahead of head h's y stores (two barriers per
+// head); y leaves through an LDS staging tile as 16-byte row stores.
 #include "cb_tiles.h"
 #include "ssd_common.h"
 #include "ssd_launch.h"
@@ -276,9 +279,10 @@ __global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
   }
   __syncthreads();
 
-  // ---- C B^T of this wavefront's 17 causal sub-tiles, kept for every head:
-  // sub-tile k <= w is (strip s0, column tile k), k > w is (strip s1, column tile k - w - 1);
-  // lane (r, qd) holds CB[i = 16 s + r][j = 16 jt + 4 qd + e]
+  // ---- C B^T of this wavefront's 17 causal sub-tiles, kept for every head, in the order the
+  // head loop takes them: slot 0 is strip s0's diagonal tile, slot k in 1..15 is (strip s0,
+  // column tile k - 1) for k <= w and (strip s1, column tile k - w - 1) after, slot 16 is strip
+  // s1's diagonal tile.  Lane (r, qd) holds CB[i = 16 s + r][j = 16 jt + 4 qd + e].
   f32x4 cb[kGSub];
   {
     typename ND::frag cf0, cf1;
@@ -286,10 +290,11 @@ __global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
     ND::load(cf1, &s_c[(16 * s1 + r) * SL::BP], qd);
 #pragma unroll
     for (int k = 0; k < kGSub; ++k) {
-      const int jt = k <= w ? k : k - w - 1;
+      const bool first = k == 0 || (k < kGSub - 1 && k <= w);
+      const int jt = k == 0 ? w : k == kGSub - 1 ? s1 : k <= w ? k - 1 : k - w - 1;
       typename ND::frag bfr;
       ND::load(bfr, &s_b[(16 * jt + r) * SL::BP], qd);
-      if (k <= w)
+      if (first)
         cb[k] = ND::dot(bfr, cf0, zero4());
       else
         cb[k] = ND::dot(bfr, cf1, zero4());
@@ -297,121 +302,158 @@ __global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
   }
   __syncthreads();                                           // s_b consumed: the head regions reuse it
   hr.template store<SL>(s_x, s_prev, s_da, s_dt, s_w, s_D, tid);
+  // the next head's inputs are loaded as soon as the registers are free, before any y store: a
+  // load into registers that a pending store still reads would wait for that store to complete
+  auto load_next = [&](int hn, int t) {
+    const __bf16 *xh, *ph;
+    const float *dth, *dah, *Dh;
+    head_ptrs(hn, xh, ph, dth, dah, Dh);
+    hr.load(xh, ph, dth, dah, Dh, (uint32_t)x_tok, len, t, seg_in(hn), seg_first, seg_dec(hn));
+  };
+  if (hs > 1) load_next(h0 + 1, tid);
   __syncthreads();
 
   for (int hh = 0; hh < hs; ++hh) {
     const int h = h0 + hh;
-    // the next head's inputs, in flight during this head's MFMAs
     const bool more = hh + 1 < hs;
-    if (more) {
-      const __bf16 *xh, *ph;
-      const float *dth, *dah, *Dh;
-      head_ptrs(h + 1, xh, ph, dth, dah, Dh);
-      hr.load(xh, ph, dth, dah, Dh, (uint32_t)x_tok, len, tid, seg_in(h + 1), seg_first, seg_dec(h + 1));
-    }
 
-    // per-lane LDS offsets, opaque to the compiler at every head: otherwise it hoists the 68
+    // per-lane LDS offsets, opaque to the compiler at every head: otherwise it hoists the
     // head-independent operand addresses of the sub-tiles out of the head loop and spills them;
-    // this way each read is a base register plus an immediate offset.  Strip s1's column tiles
-    // are jt = k - w - 1, folded into its base.
-    int xo0 = r * SL::XP + 4 * qd, xo1 = xo0 - 16 * (w + 1);
-    int wo0 = 4 * qd, wo1 = wo0 - 16 * (w + 1);
-    asm volatile("" : "+v"(xo0), "+v"(xo1), "+v"(wo0), "+v"(wo1));
+    // this way each read is a base register plus an offset.
+    // Every lane-dependent quantity of the loop body is derived from a laundered copy of the
+    // thread index for the same reason.
+    int lt = tid;
+    asm volatile("" : "+v"(lt));
+    const int r = lt & 15, qd = (lt >> 4) & 3;
+    const int xo = r * SL::XP + 4 * qd, wo = 4 * qd;
     // likewise C B^T: nothing derived from it is hoisted out of the head loop
 #pragma unroll
     for (int k = 0; k < kGSub; ++k) asm volatile("" : "+v"(cb[k]));
 
-    // the two strips one after the other (one strip's accumulators live at a time); the first
-    // strip's results wait in registers as bf16 until the y staging tile is free
-    uint32_t ypk[TP][2];
-    f32x4 acc[TP];
+    // carried terms of both strips, exp(dAcs_i) C_i Hprev^T: each state tile is read once for both
+    f32x4 acc[TP], acc1[TP];
+    {
+      typename ND::frag cf0, cf1;
+      ND::load(cf0, &s_c[(16 * s0 + r) * SL::BP], qd);
+      ND::load(cf1, &s_c[(16 * s1 + r) * SL::BP], qd);
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int s = st ? s1 : s0;
-      // carried term: exp(dAcs_i) C_i Hprev^T
-      {
-        typename ND::frag cf;
-        ND::load(cf, &s_c[(16 * s + r) * SL::BP], qd);
-#pragma unroll
-        for (int pt = 0; pt < TP; ++pt) {
-          typename ND::frag pf;
-          ND::load(pf, &s_prev[(pt * 16 + r) * SL::BP], qd);
-          acc[pt] = ND::dot(cf, pf, zero4());
-        }
-        float sc[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sc[e] = __builtin_amdgcn_exp2f(s_da[16 * s + 4 * qd + e]);
-#pragma unroll
-        for (int pt = 0; pt < TP; ++pt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[pt][e] *= sc[e];
+      for (int pt = 0; pt < TP; ++pt) {
+        typename ND::frag pf;
+        ND::load(pf, &s_prev[(pt * 16 + r) * SL::BP], qd);
+        acc[pt] = ND::dot(cf0, pf, zero4());
+        acc1[pt] = ND::dot(cf1, pf, zero4());
       }
-      // diagonal-block sub-tiles of this strip: k <= w for the first, k > w for the second
-      const int i_row = 16 * s + r;
-      const float da_row = s_da[i_row];
+      const float4 e0 = *reinterpret_cast<const float4*>(&s_da[16 * s0 + 4 * qd]);
+      const float4 e1 = *reinterpret_cast<const float4*>(&s_da[16 * s1 + 4 * qd]);
+      const float f0[4] = {__builtin_amdgcn_exp2f(e0.x), __builtin_amdgcn_exp2f(e0.y), __builtin_amdgcn_exp2f(e0.z),
+                           __builtin_amdgcn_exp2f(e0.w)};
+      const float f1[4] = {__builtin_amdgcn_exp2f(e1.x), __builtin_amdgcn_exp2f(e1.y), __builtin_amdgcn_exp2f(e1.z),
+                           __builtin_amdgcn_exp2f(e1.w)};
 #pragma unroll
-      for (int k = 0; k < kGSub; ++k) {
-        const bool mine = st == 0 ? k <= w : k > w;
-        if (!mine) continue;
-        const int jt = st == 0 ? k : k - w - 1;
-        const bool diag = jt == s;
-        const int wo = (st == 0 ? wo0 : wo1) + 16 * k;   // = 16 jt + 4 qd
-        const int xo = (st == 0 ? xo0 : xo1) + 16 * k;   // = r XP + 16 jt + 4 qd
-        float lw[4];
-        if (diag) {
-          const float4 daj = *reinterpret_cast<const float4*>(&s_da[wo]);
-          const float4 dtj = *reinterpret_cast<const float4*>(&s_dt[wo]);
-          lw[0] = (4 * qd + 0 <= r) ? cb[k][0] * __builtin_amdgcn_exp2f(da_row - daj.x) * dtj.x : 0.f;
-          lw[1] = (4 * qd + 1 <= r) ? cb[k][1] * __builtin_amdgcn_exp2f(da_row - daj.y) * dtj.y : 0.f;
-          lw[2] = (4 * qd + 2 <= r) ? cb[k][2] * __builtin_amdgcn_exp2f(da_row - daj.z) * dtj.z : 0.f;
-          lw[3] = (4 * qd + 3 <= r) ? cb[k][3] * __builtin_amdgcn_exp2f(da_row - daj.w) * dtj.w : 0.f;
-        } else {
-          const float ri = __builtin_amdgcn_exp2f(da_row - s_da[16 * jt + 15]);
-          const float4 wj = *reinterpret_cast<const float4*>(&s_w[wo]);
-          lw[0] = cb[k][0] * wj.x * ri;
-          lw[1] = cb[k][1] * wj.y * ri;
-          lw[2] = cb[k][2] * wj.z * ri;
-          lw[3] = cb[k][3] * wj.w * ri;
-        }
-        bf16x4 a;
-        a[0] = static_cast<__bf16>(lw[0]);
-        a[1] = static_cast<__bf16>(lw[1]);
-        a[2] = static_cast<__bf16>(lw[2]);
-        a[3] = static_cast<__bf16>(lw[3]);
-#pragma unroll
-        for (int pt = 0; pt < TP; ++pt) {
-          const bf16x4 xv = *reinterpret_cast<const bf16x4*>(&s_x[xo + pt * 16 * SL::XP]);
-          acc[pt] = mfma_16x16x16_bf16(a, xv, acc[pt]);
-          if (diag)  // x rows 16 jt + 4 qd + e are this lane's output rows
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[pt][e] += s_D[pt * 16 + r] * static_cast<float>(xv[e]);
-        }
-      }
-      if (Z) {
-        // output gate on the lane's elements (rows past the sequence read a clamped address)
-        const __bf16* zh = Z + ((size_t)b * L + t0) * x_tok + (size_t)h * P;
-        float zv[TP][4];
+      for (int pt = 0; pt < TP; ++pt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int i = 16 * s + 4 * qd + e;
-          uint32_t zo = (uint32_t)(i < len ? i : 0) * (uint32_t)x_tok + r;
-          asm volatile("" : "+v"(zo));
-#pragma unroll
-          for (int pt = 0; pt < TP; ++pt) zv[pt][e] = static_cast<float>(zh[zo + pt * 16]);
+          acc[pt][e] *= f0[e];
+          acc1[pt][e] *= f1[e];
         }
+    }
+
+    // the diagonal-block sub-tiles as one software pipeline over the 17 slots: the operands of
+    // slot k + 1 (x^T tile and decay scalars) are read from LDS before slot k's MFMAs, and every
+    // slot accumulates into acc; when strip s0 is complete (after slot w) its results wait in
+    // registers as bf16 and acc takes over strip s1's carried term.
+    struct Ops {
+      bf16x4 x[TP];
+      float4 f0, f1;   // off the diagonal: the column weights; on it: the cumsums and dt'
+      float dc;        // off the diagonal: the cumsum at the column tile's last position
+    };
+    auto read_ops = [&](int jt, bool diag, Ops& o) {
+      const int xj = xo + 16 * jt, wj = wo + 16 * jt;
 #pragma unroll
-        for (int pt = 0; pt < TP; ++pt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[pt][e] *= silu(zv[pt][e]);
+      for (int pt = 0; pt < TP; ++pt) o.x[pt] = *reinterpret_cast<const bf16x4*>(&s_x[xj + pt * 16 * SL::XP]);
+      if (diag) {
+        o.f0 = *reinterpret_cast<const float4*>(&s_da[wj]);
+        o.f1 = *reinterpret_cast<const float4*>(&s_dt[wj]);
+      } else {
+        o.f0 = *reinterpret_cast<const float4*>(&s_w[wj]);
+        o.dc = s_da[16 * jt + 15];
       }
-      if (st == 0) {
+    };
+    const float dr0 = s_da[16 * s0 + r], dr1 = s_da[16 * s1 + r];
+    float Dv[TP];
+#pragma unroll
+    for (int pt = 0; pt < TP; ++pt) Dv[pt] = s_D[pt * 16 + r];
+    // diagonal tile: one exponential per element and the causal mask; the skip term, whose x
+    // values are the lane's own output rows
+    auto diag_tile = [&](const f32x4& cbk, const Ops& o, float dr) {
+      bf16x4 a;
+      a[0] = static_cast<__bf16>((4 * qd + 0 <= r) ? cbk[0] * __builtin_amdgcn_exp2f(dr - o.f0.x) * o.f1.x : 0.f);
+      a[1] = static_cast<__bf16>((4 * qd + 1 <= r) ? cbk[1] * __builtin_amdgcn_exp2f(dr - o.f0.y) * o.f1.y : 0.f);
+      a[2] = static_cast<__bf16>((4 * qd + 2 <= r) ? cbk[2] * __builtin_amdgcn_exp2f(dr - o.f0.z) * o.f1.z : 0.f);
+      a[3] = static_cast<__bf16>((4 * qd + 3 <= r) ? cbk[3] * __builtin_amdgcn_exp2f(dr - o.f0.w) * o.f1.w : 0.f);
+#pragma unroll
+      for (int pt = 0; pt < TP; ++pt) {
+        acc[pt] = mfma_16x16x16_bf16(a, o.x[pt], acc[pt]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[pt][e] += Dv[pt] * static_cast<float>(o.x[pt][e]);
+      }
+    };
+    // below the diagonal: a row factor times the column weights (both <= 1)
+    auto off_tile = [&](const f32x4& cbk, const Ops& o, float dr) {
+      const float ri = __builtin_amdgcn_exp2f(dr - o.dc);
+      bf16x4 a;
+      a[0] = static_cast<__bf16>(cbk[0] * o.f0.x * ri);
+      a[1] = static_cast<__bf16>(cbk[1] * o.f0.y * ri);
+      a[2] = static_cast<__bf16>(cbk[2] * o.f0.z * ri);
+      a[3] = static_cast<__bf16>(cbk[3] * o.f0.w * ri);
+#pragma unroll
+      for (int pt = 0; pt < TP; ++pt) acc[pt] = mfma_16x16x16_bf16(a, o.x[pt], acc[pt]);
+    };
+    // output gate on the lane's elements of strip s (rows past the sequence read a clamped address)
+    auto gate = [&](int s) {
+      const __bf16* zh = Z + ((size_t)b * L + t0) * x_tok + (size_t)h * P;
+      float zv[TP][4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * s + 4 * qd + e;
+        uint32_t zo = (uint32_t)(i < len ? i : 0) * (uint32_t)x_tok + r;
+        asm volatile("" : "+v"(zo));
+#pragma unroll
+        for (int pt = 0; pt < TP; ++pt) zv[pt][e] = static_cast<float>(zh[zo + pt * 16]);
+      }
+#pragma unroll
+      for (int pt = 0; pt < TP; ++pt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[pt][e] *= silu(zv[pt][e]);
+    };
+
+    uint32_t ypk[TP][2];
+    float dr = dr0;
+    Ops cur, nxt;
+    read_ops(w, true, cur);                                  // slot 0: strip s0's diagonal tile
+    read_ops(0, false, nxt);                                 // slot 1: column tile 0 of s0 or s1
+    diag_tile(cb[0], cur, dr0);
+#pragma unroll
+    for (int k = 1; k < kGSub - 1; ++k) {
+      cur = nxt;
+      if (k + 1 < kGSub - 1)
+        read_ops(k + 1 <= w ? k : k - w, false, nxt);
+      else
+        read_ops(s1, true, nxt);
+      if (k == w + 1) {                                      // strip s0 complete
+        if (Z) gate(s0);
 #pragma unroll
         for (int pt = 0; pt < TP; ++pt) {
           ypk[pt][0] = pack_bf16(acc[pt][0], acc[pt][1]);
           ypk[pt][1] = pack_bf16(acc[pt][2], acc[pt][3]);
+          acc[pt] = acc1[pt];
         }
+        dr = dr1;
       }
+      off_tile(cb[k], cur, dr);
     }
+    diag_tile(cb[kGSub - 1], nxt, dr1);                      // slot 16: strip s1's diagonal tile
+    if (Z) gate(s1);
     __syncthreads();                                         // x^T, Hprev and scalars of head h consumed
 #pragma unroll
     for (int pt = 0; pt < TP; ++pt) {
@@ -423,14 +465,17 @@ __global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
         s_y[(16 * s1 + 4 * qd + e) * SL::YP + pt * 16 + r] = static_cast<__bf16>(acc[pt][e]);
       }
     }
-    if (more) hr.template store<SL>(s_x, s_prev, s_da, s_dt, s_w, s_D, tid);
+    if (more) {
+      hr.template store<SL>(s_x, s_prev, s_da, s_dt, s_w, s_D, lt);
+      if (hh + 2 < hs) load_next(h + 2, lt);           // in flight during head h + 1
+    }
     __syncthreads();                                         // y staged; the next head's inputs in LDS
     {
       constexpr int YU = kGQ * P / 8, YPT = YU / kGThreads;
       __bf16* yh = y + ((size_t)b * L + t0) * x_tok + (size_t)h * P;
 #pragma unroll
       for (int u = 0; u < YPT; ++u) {
-        const int v = tid + kGThreads * u;
+        const int v = lt + kGThreads * u;
         const int row = v / (P / 8), cv = (v % (P / 8)) * 8;
         uint32_t yo = (uint32_t)row * (uint32_t)x_tok + cv;
         asm volatile("" : "+v"(yo));
