@@ -21,9 +21,9 @@
 // sub-tile's decay formed in registers (below the diagonal a row factor times a per-column
 // weight, both <= 1: one exponential per lane; on the diagonal one per element and the causal
 // mask) and rounded to bf16 as the A operand of the 16x16x16 bf16 MFMA with the x^T tile; the
-// skip term on the diagonal sub-tiles, whose x values are the lane's own output rows.  The inputs of
-// head h + 2 are loaded into registers as soon as those of head h + 1 are in LDS, so they are in
-// flight during head h + 1's MFMAs and are issued ahead of head h's y stores (two barriers per
+// skip term on the diagonal sub-tiles, whose x values are the lane's own output rows.  The next
+// head's inputs are loaded into registers in parts spread over the first sub-tiles, so their
+// issue overlaps the MFMAs and they are in flight for the rest of the head (two barriers per
 // head); y leaves through an LDS staging tile as 16-byte row stores.
 #include "cb_tiles.h"
 #include "ssd_common.h"
@@ -82,51 +82,51 @@ struct HeadRegs {
 
   // Per-lane element offsets from the head's (wavefront-uniform) base pointers, 32-bit: the
   // loads take a scalar base plus a vector offset.  The offsets are made opaque at each call so
-  // the compiler does not keep precomputed 64-bit addresses alive across the head loop.
+  // the compiler does not keep precomputed 64-bit addresses alive across the head loop.  The
+  // loads come in parts (part = 0 .. kParts - 1) so that a caller can spread their issue.
   // hh: the segment's incoming state (null without segments); first: c opens its segment (no
   // carried part of its own); ecd: the decay exponent since the segment start
-  __device__ __forceinline__ void load(const __bf16* xh, const __bf16* ph, const float* dth, const float* dah,
-                                       const float* Dh, uint32_t x_tok, int len, int tid, const __bf16* hh = nullptr,
-                                       bool first = false, const float* ecd = nullptr) {
-    uint32_t xo[XPT][2], po[PPT];
-    okm = 0;
-#pragma unroll
-    for (int u = 0; u < XPT; ++u) {
+  static constexpr int kParts = XPT + 2;
+  __device__ __forceinline__ void load_part(int part, const __bf16* xh, const __bf16* ph, const float* dth,
+                                            const float* dah, const float* Dh, uint32_t x_tok, int len, int tid,
+                                            const __bf16* hh, bool first, const float* ecd) {
+    if (part < XPT) {
+      const int u = part;
       const int v = tid + kGThreads * u;
       const int vec = (v % PV) * 8, m = v / PV;
       const int tok = 2 * m;
       const bool ok0 = tok < len, ok1 = tok + 1 < len;
-      xo[u][0] = (uint32_t)(ok0 ? tok : 0) * x_tok + vec;
-      xo[u][1] = (uint32_t)(ok1 ? tok + 1 : 0) * x_tok + vec;
-      okm |= ((uint32_t)ok0 << (2 * u)) | ((uint32_t)ok1 << (2 * u + 1));
-      asm volatile("" : "+v"(xo[u][0]), "+v"(xo[u][1]));
-    }
-#pragma unroll
-    for (int u = 0; u < PPT; ++u) {
-      po[u] = (uint32_t)(tid + kGThreads * u) * 8;
-      asm volatile("" : "+v"(po[u]));
-    }
-    uint32_t io = tid & (kGQ - 1), Do = tid & (P - 1);
-    asm volatile("" : "+v"(io), "+v"(Do));
-#pragma unroll
-    for (int u = 0; u < XPT; ++u) {
-      x[u][0] = *reinterpret_cast<const uint4*>(xh + xo[u][0]);
-      x[u][1] = *reinterpret_cast<const uint4*>(xh + xo[u][1]);
-    }
-#pragma unroll
-    for (int u = 0; u < PPT; ++u) pv[u] = *reinterpret_cast<const uint4*>(ph + po[u]);
-    sdec = -1.f;
-    if (hh) {
+      uint32_t xo0 = (uint32_t)(ok0 ? tok : 0) * x_tok + vec;
+      uint32_t xo1 = (uint32_t)(ok1 ? tok + 1 : 0) * x_tok + vec;
+      const uint32_t bits = ((uint32_t)ok0 << (2 * u)) | ((uint32_t)ok1 << (2 * u + 1));
+      okm = u == 0 ? bits : (okm | bits);
+      asm volatile("" : "+v"(xo0), "+v"(xo1));
+      x[u][0] = *reinterpret_cast<const uint4*>(xh + xo0);
+      x[u][1] = *reinterpret_cast<const uint4*>(xh + xo1);
+    } else if (part == XPT) {
+      uint32_t po[PPT];
 #pragma unroll
       for (int u = 0; u < PPT; ++u) {
-        hv[u] = *reinterpret_cast<const uint4*>(hh + po[u]);
-        if (first) pv[u] = make_uint4(0, 0, 0, 0);   // (that slot holds no state of this segment)
+        po[u] = (uint32_t)(tid + kGThreads * u) * 8;
+        asm volatile("" : "+v"(po[u]));
       }
-      sdec = __expf(*ecd);
+#pragma unroll
+      for (int u = 0; u < PPT; ++u) pv[u] = *reinterpret_cast<const uint4*>(ph + po[u]);
+      if (hh) {
+#pragma unroll
+        for (int u = 0; u < PPT; ++u) {
+          hv[u] = *reinterpret_cast<const uint4*>(hh + po[u]);
+          if (first) pv[u] = make_uint4(0, 0, 0, 0);   // (that slot holds no state of this segment)
+        }
+      }
+    } else {
+      uint32_t io = tid & (kGQ - 1), Do = tid & (P - 1);
+      asm volatile("" : "+v"(io), "+v"(Do));
+      sdec = hh ? __expf(*ecd) : -1.f;
+      dt = dth[io];
+      da = dah[io];
+      dd = Dh ? Dh[Do] : 0.f;
     }
-    dt = dth[io];
-    da = dah[io];
-    dd = Dh ? Dh[Do] : 0.f;
   }
 
   // x^T (token pairs packed into one 32-bit store per headdim row), the state rows, and for
@@ -264,12 +264,15 @@ __global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
     creg[u] = *reinterpret_cast<const uint4*>(Cb + (size_t)(row < len ? row : 0) * bc_tok + nv);
   }
   HR hr;
-  {
+  // part `part` of head hn's inputs into hr
+  auto load_part = [&](int part, int hn, int t) {
     const __bf16 *xh, *ph;
     const float *dth, *dah, *Dh;
-    head_ptrs(h0, xh, ph, dth, dah, Dh);
-    hr.load(xh, ph, dth, dah, Dh, (uint32_t)x_tok, len, tid, seg_in(h0), seg_first, seg_dec(h0));
-  }
+    head_ptrs(hn, xh, ph, dth, dah, Dh);
+    hr.load_part(part, xh, ph, dth, dah, Dh, (uint32_t)x_tok, len, t, seg_in(hn), seg_first, seg_dec(hn));
+  };
+#pragma unroll
+  for (int part = 0; part < HR::kParts; ++part) load_part(part, h0, tid);
 #pragma unroll
   for (int u = 0; u < BPT; ++u) {
     const int v = tid + kGThreads * u;
@@ -302,15 +305,6 @@ __global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
   }
   __syncthreads();                                           // s_b consumed: the head regions reuse it
   hr.template store<SL>(s_x, s_prev, s_da, s_dt, s_w, s_D, tid);
-  // the next head's inputs are loaded as soon as the registers are free, before any y store: a
-  // load into registers that a pending store still reads would wait for that store to complete
-  auto load_next = [&](int hn, int t) {
-    const __bf16 *xh, *ph;
-    const float *dth, *dah, *Dh;
-    head_ptrs(hn, xh, ph, dth, dah, Dh);
-    hr.load(xh, ph, dth, dah, Dh, (uint32_t)x_tok, len, t, seg_in(hn), seg_first, seg_dec(hn));
-  };
-  if (hs > 1) load_next(h0 + 1, tid);
   __syncthreads();
 
   for (int hh = 0; hh < hs; ++hh) {
@@ -440,6 +434,9 @@ __global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
         read_ops(k + 1 <= w ? k : k - w, false, nxt);
       else
         read_ops(s1, true, nxt);
+      // the next head's inputs, a part every other slot, in flight for the rest of this head (the
+      // last head reloads its own, unused)
+      if (k % 2 == 1 && k / 2 < HR::kParts) load_part(k / 2, more ? h + 1 : h, lt);
       if (k == w + 1) {                                      // strip s0 complete
         if (Z) gate(s0);
 #pragma unroll
@@ -465,10 +462,7 @@ __global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
         s_y[(16 * s1 + 4 * qd + e) * SL::YP + pt * 16 + r] = static_cast<__bf16>(acc[pt][e]);
       }
     }
-    if (more) {
-      hr.template store<SL>(s_x, s_prev, s_da, s_dt, s_w, s_D, lt);
-      if (hh + 2 < hs) load_next(h + 2, lt);           // in flight during head h + 1
-    }
+    if (more) hr.template store<SL>(s_x, s_prev, s_da, s_dt, s_w, s_D, lt);
     __syncthreads();                                         // y staged; the next head's inputs in LDS
     {
       constexpr int YU = kGQ * P / 8, YPT = YU / kGThreads;
