@@ -15,16 +15,18 @@
 // Eight wavefronts; wavefront w owns the strip pair (w, 15 - w) of the chunk's sixteen 16-row
 // strips, i.e. w + 1 and 16 - w causal 16x16 sub-tiles, 17 for every wavefront.  The CB sub-tiles
 // (16x16x32 bf16 MFMA over dstate, from the chunk's B and C rows staged in LDS) stay in registers
-// for all heads; the C rows stay in LDS for the carried term.  Per head: the carried terms
-// C Hprev^T of both strips on MFMA (Hprev staged in LDS), then the 17 sub-tiles as one software
-// pipeline (the next sub-tile's LDS operands in flight during the current one's MFMAs), each
-// sub-tile's decay formed in registers (below the diagonal a row factor times a per-column
-// weight, both <= 1: one exponential per lane; on the diagonal one per element and the causal
-// mask) and rounded to bf16 as the A operand of the 16x16x16 bf16 MFMA with the x^T tile; the
-// skip term on the diagonal sub-tiles, whose x values are the lane's own output rows.  The next
-// head's inputs are loaded into registers in parts spread over the first sub-tiles, so their
-// issue overlaps the MFMAs and they are in flight for the rest of the head (two barriers per
-// head); y leaves through an LDS staging tile as 16-byte row stores.
+// for all heads; the C rows stay in LDS for the carried term.  Per head, every product formed
+// transposed (y^T = x^T L^T, so that a lane's outputs are four consecutive headdims of one row):
+// the carried terms Hprev C^T of both strips on MFMA (Hprev staged in LDS), then the 17 sub-tiles
+// as one software pipeline (the next sub-tile's LDS operands in flight during the current one's
+// MFMAs), each sub-tile's decay formed in registers (below the diagonal a row factor times a
+// per-column weight, both <= 1: one exponential per lane; on the diagonal one per element and the
+// causal mask) and rounded to bf16 as the B operand of the 16x16x16 bf16 MFMA whose A operand is
+// the x tile read transposed from LDS (x stays token-major there); the skip term on the diagonal
+// sub-tiles.  Global memory traffic is spread over the sub-tiles: the next head's inputs are
+// loaded into registers in parts on every other sub-tile (in flight for the rest of the head),
+// and y, staged in LDS after the head, leaves as 16-byte row stores in parts on the next head's
+// sub-tiles in between (two barriers per head).
 #include "cb_tiles.h"
 #include "ssd_common.h"
 #include "ssd_launch.h"
@@ -39,21 +41,52 @@ constexpr int kGThreads = 512;                  // eight wavefronts
 constexpr int kGSub = kGS + 1;                  // causal sub-tiles per wavefront (strip pair)
 constexpr float kGLog2e = 1.4426950408889634f;
 
-// two fp32 values rounded to bf16 (nearest-even) in one 32-bit word, and back
+typedef float gf32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 gbf16x2 __attribute__((ext_vector_type(2)));
+
+// two fp32 values rounded to bf16 (nearest-even) in one 32-bit word (one two-source conversion
+// instruction), and back
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  const __bf16 l = static_cast<__bf16>(lo), h = static_cast<__bf16>(hi);
-  return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((gf32x2{lo, hi}), gbf16x2));
+}
+// (the two words pass through an empty asm: otherwise the conversion is split into four
+// one-source conversions and two byte permutes)
+__device__ __forceinline__ bf16x4 to_bf16x4(float a, float b, float c, float d) {
+  uint32_t lo = pack_bf16(a, b), hi = pack_bf16(c, d);
+  asm volatile("" : "+v"(lo), "+v"(hi));
+  return __builtin_bit_cast(bf16x4, (uint2{lo, hi}));
 }
 __device__ __forceinline__ float unpack_lo(uint32_t v) { return __builtin_bit_cast(float, v << 16); }
 __device__ __forceinline__ float unpack_hi(uint32_t v) { return __builtin_bit_cast(float, v & 0xffff0000u); }
 
+// 16 bytes at a byte offset from a wavefront-uniform base (scalar base + 32-bit vector offset)
+__device__ __forceinline__ uint4 ld16(const void* base, uint32_t off) {
+  return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(base) + off);
+}
+__device__ __forceinline__ void st16(void* base, uint32_t off, uint4 v) {
+  *reinterpret_cast<uint4*>(reinterpret_cast<char*>(base) + off) = v;
+}
+
+typedef short gi16x4 __attribute__((ext_vector_type(4)));
+// LDS transpose read (ds_read_b64_tr_b16): every lane passes the address of 8 bytes; in each
+// group of 16 lanes, with M[j][q] the q-th 16-bit element at lane j's address, lane i receives
+// element k = M[4 k + i / 4][i % 4].  When lane j of group g points at row 4 g + j / 4, columns
+// 4 (j % 4) .. + 3 of a row-major 16 x 16 tile T, lane (i, g) receives T[4 g + k][i], k = 0..3:
+// the MFMA operand layout of the tile's transpose.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const __bf16* p) {
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                        (__attribute__((address_space(3))) gi16x4*)(p)));
+}
+
 template <int P, int N>
 struct GroupLds {
   static constexpr int BP = N + 8;              // B rows / Hprev rows, n-contiguous (bf16)
-  static constexpr int XP = kGQ + 4;            // x^T rows, token-contiguous (a 130-dword pitch:
-                                                // the 8-byte operand reads of 16 rows hit 32 banks)
+  // x: 16 x 16 tiles (16 tokens x 16 headdims, row-major, 512 bytes), tile (jt, pt) at
+  // (4 jt + pt) XT.  The 32 padding bytes per tile put the four headdim tiles of one token row
+  // in different banks (16-byte stores conflict-free); a tile itself is read contiguously.
+  static constexpr int XT = 16 * 16 + 16;
   static constexpr int YP = P + 8;              // y staging rows
-  static constexpr int X_ELEMS = P * XP;
+  static constexpr int X_ELEMS = (kGQ / 16) * (P / 16) * XT;
   static constexpr int PREV_ELEMS = P * BP;
   static constexpr int Y_ELEMS = kGQ * YP;
   static constexpr int HEAD = X_ELEMS + PREV_ELEMS + Y_ELEMS;   // per-head regions, side by side
@@ -64,8 +97,9 @@ struct GroupLds {
 
 // One head's inputs between their global loads and their LDS stores: x as token pairs (each
 // thread two 16-byte vectors of consecutive tokens at the same headdim offset; eight lanes cover
-// one token row, so every load instruction reads whole rows), the bf16 entering state as 16-byte
-// vectors, the chunk's dt' and cumsum (threads 0..255, one position each) and D (threads 0..P-1).
+// one token row, so every load instruction reads whole rows), stored as they are into the x
+// tiles; the bf16 entering state as 16-byte vectors, the chunk's dt' and cumsum (threads 0..255,
+// one position each) and D (threads 0..P-1).
 template <int P, int N>
 struct HeadRegs {
   static constexpr int PV = P / 8;                          // 16-byte vectors per token row
@@ -96,42 +130,46 @@ struct HeadRegs {
       const int vec = (v % PV) * 8, m = v / PV;
       const int tok = 2 * m;
       const bool ok0 = tok < len, ok1 = tok + 1 < len;
-      uint32_t xo0 = (uint32_t)(ok0 ? tok : 0) * x_tok + vec;
-      uint32_t xo1 = (uint32_t)(ok1 ? tok + 1 : 0) * x_tok + vec;
+      uint32_t xo0 = ((uint32_t)(ok0 ? tok : 0) * x_tok + vec) * 2;      // bytes
+      uint32_t xo1 = ((uint32_t)(ok1 ? tok + 1 : 0) * x_tok + vec) * 2;
       const uint32_t bits = ((uint32_t)ok0 << (2 * u)) | ((uint32_t)ok1 << (2 * u + 1));
       okm = u == 0 ? bits : (okm | bits);
       asm volatile("" : "+v"(xo0), "+v"(xo1));
-      x[u][0] = *reinterpret_cast<const uint4*>(xh + xo0);
-      x[u][1] = *reinterpret_cast<const uint4*>(xh + xo1);
+      x[u][0] = ld16(xh, xo0);
+      x[u][1] = ld16(xh, xo1);
     } else if (part == XPT) {
       uint32_t po[PPT];
 #pragma unroll
       for (int u = 0; u < PPT; ++u) {
-        po[u] = (uint32_t)(tid + kGThreads * u) * 8;
+        po[u] = (uint32_t)(tid + kGThreads * u) * 16;                     // bytes
         asm volatile("" : "+v"(po[u]));
       }
 #pragma unroll
-      for (int u = 0; u < PPT; ++u) pv[u] = *reinterpret_cast<const uint4*>(ph + po[u]);
+      for (int u = 0; u < PPT; ++u) pv[u] = ld16(ph, po[u]);
       if (hh) {
 #pragma unroll
         for (int u = 0; u < PPT; ++u) {
-          hv[u] = *reinterpret_cast<const uint4*>(hh + po[u]);
+          hv[u] = ld16(hh, po[u]);
           if (first) pv[u] = make_uint4(0, 0, 0, 0);   // (that slot holds no state of this segment)
         }
       }
     } else {
-      uint32_t io = tid & (kGQ - 1), Do = tid & (P - 1);
+      // only the wavefronts that store them load the scalars (wavefront-uniform branches)
+      const int wf = __builtin_amdgcn_readfirstlane(tid) / 64;
+      uint32_t io = (tid & (kGQ - 1)) * 4, Do = (tid & (P - 1)) * 4;
       asm volatile("" : "+v"(io), "+v"(Do));
       sdec = hh ? __expf(*ecd) : -1.f;
-      dt = dth[io];
-      da = dah[io];
-      dd = Dh ? Dh[Do] : 0.f;
+      if (wf < kGQ / 64) {
+        dt = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(dth) + io);
+        da = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(dah) + io);
+      }
+      if (wf < P / 64 || (P < 64 && wf == 0)) dd = Dh ? *reinterpret_cast<const float*>(reinterpret_cast<const char*>(Dh) + Do) : 0.f;
     }
   }
 
-  // x^T (token pairs packed into one 32-bit store per headdim row), the state rows, and for
-  // threads 0..255 the log2e-scaled cumsum, dt' and the column weights
-  // W_j = exp2(dAcs_c - dAcs_j) dt'_j, c = j | 15 (the last column of j's 16-column tile)
+  // x into its tiles (16-byte stores), the state rows, and for threads 0..255 the log2e-scaled
+  // cumsum, dt' and the column weights W_j = exp2(dAcs_c - dAcs_j) dt'_j, c = j | 15 (the last
+  // column of j's 16-column tile)
   template <typename L>
   __device__ __forceinline__ void store(__bf16* s_x, __bf16* s_prev, float* s_da, float* s_dt, float* s_w,
                                         float* s_D, int tid) const {
@@ -139,18 +177,13 @@ struct HeadRegs {
     for (int u = 0; u < XPT; ++u) {
       const int v = tid + kGThreads * u;
       const int vec = (v % PV) * 8, m = v / PV;
+      const int tok = 2 * m;                                   // (even: both tokens in one tile)
+      const int o = ((tok >> 4) * (P / 16) + (vec >> 4)) * L::XT + (tok & 15) * 16 + (vec & 15);
       uint4 a = x[u][0], b = x[u][1];
       if (!((okm >> (2 * u)) & 1u)) a = make_uint4(0, 0, 0, 0);
       if (!((okm >> (2 * u + 1)) & 1u)) b = make_uint4(0, 0, 0, 0);
-      const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        // elements 2q (low halves) and 2q + 1 (high halves) of the two tokens
-        const uint32_t lo = (av[q] & 0xffffu) | (bv[q] << 16);
-        const uint32_t hi = (av[q] >> 16) | (bv[q] & 0xffff0000u);
-        *reinterpret_cast<uint32_t*>(&s_x[(vec + 2 * q) * L::XP + 2 * m]) = lo;
-        *reinterpret_cast<uint32_t*>(&s_x[(vec + 2 * q + 1) * L::XP + 2 * m]) = hi;
-      }
+      *reinterpret_cast<uint4*>(&s_x[o]) = a;
+      *reinterpret_cast<uint4*>(&s_x[o + 16]) = b;
     }
 #pragma unroll
     for (int u = 0; u < PPT; ++u) {
@@ -273,6 +306,16 @@ __global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
   };
 #pragma unroll
   for (int part = 0; part < HR::kParts; ++part) load_part(part, h0, tid);
+  // row block u of head hn's y from the staging tile to global memory (16-byte rows pieces)
+  constexpr int kYParts = (kGQ * P / 8) / kGThreads;
+  auto flush_part = [&](int u, int hn, int t) {
+    const int v = t + kGThreads * u;
+    const int row = v / (P / 8), cv = (v % (P / 8)) * 8;
+    uint32_t yo = ((uint32_t)row * (uint32_t)x_tok + cv) * 2;
+    asm volatile("" : "+v"(yo));
+    const uint4 val = *reinterpret_cast<const uint4*>(&s_y[row * SL::YP + cv]);
+    if (row < len) st16(y + ((size_t)b * L + t0) * x_tok + (size_t)hn * P, yo, val);
+  };
 #pragma unroll
   for (int u = 0; u < BPT; ++u) {
     const int v = tid + kGThreads * u;
@@ -316,15 +359,18 @@ __global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
     // this way each read is a base register plus an offset.
     // Every lane-dependent quantity of the loop body is derived from a laundered copy of the
     // thread index for the same reason.
-    int lt = tid;
-    asm volatile("" : "+v"(lt));
+    int lt = tid, wl = w;
+    asm volatile("" : "+v"(lt), "+s"(wl));
     const int r = lt & 15, qd = (lt >> 4) & 3;
-    const int xo = r * SL::XP + 4 * qd, wo = 4 * qd;
+    const int w = wl, s0 = wl, s1 = kGS - 1 - wl;   // (uniform conditions are recomputed per head)
+    const int xo = 4 * (lt & 63), wo = 4 * qd;            // (xo: this lane's 8 bytes of an x tile)
     // likewise C B^T: nothing derived from it is hoisted out of the head loop
 #pragma unroll
     for (int k = 0; k < kGSub; ++k) asm volatile("" : "+v"(cb[k]));
 
-    // carried terms of both strips, exp(dAcs_i) C_i Hprev^T: each state tile is read once for both
+    // Every product is formed transposed, y^T = x^T L^T: lane (r, qd) of accumulator pt holds
+    // y[i = 16 s + r][p = 16 pt + 4 qd + e], four consecutive headdims of one output row.
+    // carried terms of both strips, exp(dAcs_i) Hprev C_i^T: each state tile is read once for both
     f32x4 acc[TP], acc1[TP];
     {
       typename ND::frag cf0, cf1;
@@ -334,26 +380,22 @@ __global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
       for (int pt = 0; pt < TP; ++pt) {
         typename ND::frag pf;
         ND::load(pf, &s_prev[(pt * 16 + r) * SL::BP], qd);
-        acc[pt] = ND::dot(cf0, pf, zero4());
-        acc1[pt] = ND::dot(cf1, pf, zero4());
+        acc[pt] = ND::dot(pf, cf0, zero4());
+        acc1[pt] = ND::dot(pf, cf1, zero4());
       }
-      const float4 e0 = *reinterpret_cast<const float4*>(&s_da[16 * s0 + 4 * qd]);
-      const float4 e1 = *reinterpret_cast<const float4*>(&s_da[16 * s1 + 4 * qd]);
-      const float f0[4] = {__builtin_amdgcn_exp2f(e0.x), __builtin_amdgcn_exp2f(e0.y), __builtin_amdgcn_exp2f(e0.z),
-                           __builtin_amdgcn_exp2f(e0.w)};
-      const float f1[4] = {__builtin_amdgcn_exp2f(e1.x), __builtin_amdgcn_exp2f(e1.y), __builtin_amdgcn_exp2f(e1.z),
-                           __builtin_amdgcn_exp2f(e1.w)};
+      const float f0 = __builtin_amdgcn_exp2f(s_da[16 * s0 + r]), f1 = __builtin_amdgcn_exp2f(s_da[16 * s1 + r]);
 #pragma unroll
       for (int pt = 0; pt < TP; ++pt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          acc[pt][e] *= f0[e];
-          acc1[pt][e] *= f1[e];
+          acc[pt][e] *= f0;
+          acc1[pt][e] *= f1;
         }
     }
 
     // the diagonal-block sub-tiles as one software pipeline over the 17 slots: the operands of
-    // slot k + 1 (x^T tile and decay scalars) are read from LDS before slot k's MFMAs, and every
+    // slot k + 1 (x tiles, transposed as they are read, and decay scalars) are read from LDS
+    // before slot k's MFMAs, and every
     // slot accumulates into acc; when strip s0 is complete (after slot w) its results wait in
     // registers as bf16 and acc takes over strip s1's carried term.
     struct Ops {
@@ -362,9 +404,9 @@ __global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
       float dc;        // off the diagonal: the cumsum at the column tile's last position
     };
     auto read_ops = [&](int jt, bool diag, Ops& o) {
-      const int xj = xo + 16 * jt, wj = wo + 16 * jt;
+      const int xj = xo + jt * (P / 16) * SL::XT, wj = wo + 16 * jt;
 #pragma unroll
-      for (int pt = 0; pt < TP; ++pt) o.x[pt] = *reinterpret_cast<const bf16x4*>(&s_x[xj + pt * 16 * SL::XP]);
+      for (int pt = 0; pt < TP; ++pt) o.x[pt] = lds_read_tr16(&s_x[xj + pt * SL::XT]);
       if (diag) {
         o.f0 = *reinterpret_cast<const float4*>(&s_da[wj]);
         o.f1 = *reinterpret_cast<const float4*>(&s_dt[wj]);
@@ -374,51 +416,48 @@ __global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
       }
     };
     const float dr0 = s_da[16 * s0 + r], dr1 = s_da[16 * s1 + r];
-    float Dv[TP];
-#pragma unroll
-    for (int pt = 0; pt < TP; ++pt) Dv[pt] = s_D[pt * 16 + r];
-    // diagonal tile: one exponential per element and the causal mask; the skip term, whose x
-    // values are the lane's own output rows
-    auto diag_tile = [&](const f32x4& cbk, const Ops& o, float dr) {
-      bf16x4 a;
-      a[0] = static_cast<__bf16>((4 * qd + 0 <= r) ? cbk[0] * __builtin_amdgcn_exp2f(dr - o.f0.x) * o.f1.x : 0.f);
-      a[1] = static_cast<__bf16>((4 * qd + 1 <= r) ? cbk[1] * __builtin_amdgcn_exp2f(dr - o.f0.y) * o.f1.y : 0.f);
-      a[2] = static_cast<__bf16>((4 * qd + 2 <= r) ? cbk[2] * __builtin_amdgcn_exp2f(dr - o.f0.z) * o.f1.z : 0.f);
-      a[3] = static_cast<__bf16>((4 * qd + 3 <= r) ? cbk[3] * __builtin_amdgcn_exp2f(dr - o.f0.w) * o.f1.w : 0.f);
+    // diagonal tile of strip s: one exponential per element and the causal mask; the skip term
+    // D_p x[i][p] from the lane's own output elements of the tile (untransposed reads)
+    auto diag_tile = [&](const f32x4& cbk, const Ops& o, float dr, int s) {
+      const bf16x4 a = to_bf16x4((4 * qd + 0 <= r) ? cbk[0] * __builtin_amdgcn_exp2f(dr - o.f0.x) * o.f1.x : 0.f,
+                                 (4 * qd + 1 <= r) ? cbk[1] * __builtin_amdgcn_exp2f(dr - o.f0.y) * o.f1.y : 0.f,
+                                 (4 * qd + 2 <= r) ? cbk[2] * __builtin_amdgcn_exp2f(dr - o.f0.z) * o.f1.z : 0.f,
+                                 (4 * qd + 3 <= r) ? cbk[3] * __builtin_amdgcn_exp2f(dr - o.f0.w) * o.f1.w : 0.f);
+      const int xr = s * (P / 16) * SL::XT + r * 16 + 4 * qd;
 #pragma unroll
       for (int pt = 0; pt < TP; ++pt) {
-        acc[pt] = mfma_16x16x16_bf16(a, o.x[pt], acc[pt]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[pt][e] += Dv[pt] * static_cast<float>(o.x[pt][e]);
+        const uint2 xv = *reinterpret_cast<const uint2*>(&s_x[xr + pt * SL::XT]);
+        const float4 dv = *reinterpret_cast<const float4*>(&s_D[16 * pt + 4 * qd]);
+        acc[pt] = mfma_16x16x16_bf16(o.x[pt], a, acc[pt]);
+        acc[pt][0] += dv.x * unpack_lo(xv.x);
+        acc[pt][1] += dv.y * unpack_hi(xv.x);
+        acc[pt][2] += dv.z * unpack_lo(xv.y);
+        acc[pt][3] += dv.w * unpack_hi(xv.y);
       }
     };
     // below the diagonal: a row factor times the column weights (both <= 1)
     auto off_tile = [&](const f32x4& cbk, const Ops& o, float dr) {
       const float ri = __builtin_amdgcn_exp2f(dr - o.dc);
-      bf16x4 a;
-      a[0] = static_cast<__bf16>(cbk[0] * o.f0.x * ri);
-      a[1] = static_cast<__bf16>(cbk[1] * o.f0.y * ri);
-      a[2] = static_cast<__bf16>(cbk[2] * o.f0.z * ri);
-      a[3] = static_cast<__bf16>(cbk[3] * o.f0.w * ri);
+      const bf16x4 a = to_bf16x4(cbk[0] * o.f0.x * ri, cbk[1] * o.f0.y * ri, cbk[2] * o.f0.z * ri, cbk[3] * o.f0.w * ri);
 #pragma unroll
-      for (int pt = 0; pt < TP; ++pt) acc[pt] = mfma_16x16x16_bf16(a, o.x[pt], acc[pt]);
+      for (int pt = 0; pt < TP; ++pt) acc[pt] = mfma_16x16x16_bf16(o.x[pt], a, acc[pt]);
     };
     // output gate on the lane's elements of strip s (rows past the sequence read a clamped address)
     auto gate = [&](int s) {
       const __bf16* zh = Z + ((size_t)b * L + t0) * x_tok + (size_t)h * P;
-      float zv[TP][4];
+      const int i = 16 * s + r;
+      uint32_t zo = (uint32_t)(i < len ? i : 0) * (uint32_t)x_tok + 4 * qd;
+      asm volatile("" : "+v"(zo));
+      uint2 zv[TP];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 16 * s + 4 * qd + e;
-        uint32_t zo = (uint32_t)(i < len ? i : 0) * (uint32_t)x_tok + r;
-        asm volatile("" : "+v"(zo));
+      for (int pt = 0; pt < TP; ++pt) zv[pt] = *reinterpret_cast<const uint2*>(zh + zo + pt * 16);
 #pragma unroll
-        for (int pt = 0; pt < TP; ++pt) zv[pt][e] = static_cast<float>(zh[zo + pt * 16]);
+      for (int pt = 0; pt < TP; ++pt) {
+        acc[pt][0] *= silu(unpack_lo(zv[pt].x));
+        acc[pt][1] *= silu(unpack_hi(zv[pt].x));
+        acc[pt][2] *= silu(unpack_lo(zv[pt].y));
+        acc[pt][3] *= silu(unpack_hi(zv[pt].y));
       }
-#pragma unroll
-      for (int pt = 0; pt < TP; ++pt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[pt][e] *= silu(zv[pt][e]);
     };
 
     uint32_t ypk[TP][2];
@@ -426,7 +465,7 @@ __global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
     Ops cur, nxt;
     read_ops(w, true, cur);                                  // slot 0: strip s0's diagonal tile
     read_ops(0, false, nxt);                                 // slot 1: column tile 0 of s0 or s1
-    diag_tile(cb[0], cur, dr0);
+    diag_tile(cb[0], cur, dr0, s0);
 #pragma unroll
     for (int k = 1; k < kGSub - 1; ++k) {
       cur = nxt;
@@ -435,8 +474,10 @@ __global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
       else
         read_ops(s1, true, nxt);
       // the next head's inputs, a part every other slot, in flight for the rest of this head (the
-      // last head reloads its own, unused)
+      // last head reloads its own, unused); between them the previous head's y, a row block per
+      // slot, from its staging tile (rewritten only after this head's first barrier)
       if (k % 2 == 1 && k / 2 < HR::kParts) load_part(k / 2, more ? h + 1 : h, lt);
+      if (k % 2 == 0 && k / 2 - 1 < kYParts && hh > 0) flush_part(k / 2 - 1, h - 1, lt);
       if (k == w + 1) {                                      // strip s0 complete
         if (Z) gate(s0);
 #pragma unroll
@@ -449,35 +490,24 @@ __global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
       }
       off_tile(cb[k], cur, dr);
     }
-    diag_tile(cb[kGSub - 1], nxt, dr1);                      // slot 16: strip s1's diagonal tile
+    diag_tile(cb[kGSub - 1], nxt, dr1, s1);                  // slot 16: strip s1's diagonal tile
     if (Z) gate(s1);
-    __syncthreads();                                         // x^T, Hprev and scalars of head h consumed
+    __syncthreads();                                         // x, Hprev and scalars of head h consumed
 #pragma unroll
     for (int pt = 0; pt < TP; ++pt) {
-      const float y0[4] = {unpack_lo(ypk[pt][0]), unpack_hi(ypk[pt][0]), unpack_lo(ypk[pt][1]),
-                           unpack_hi(ypk[pt][1])};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s_y[(16 * s0 + 4 * qd + e) * SL::YP + pt * 16 + r] = static_cast<__bf16>(y0[e]);
-        s_y[(16 * s1 + 4 * qd + e) * SL::YP + pt * 16 + r] = static_cast<__bf16>(acc[pt][e]);
-      }
+      *reinterpret_cast<uint2*>(&s_y[(16 * s0 + r) * SL::YP + pt * 16 + 4 * qd]) = make_uint2(ypk[pt][0], ypk[pt][1]);
+      *reinterpret_cast<uint2*>(&s_y[(16 * s1 + r) * SL::YP + pt * 16 + 4 * qd]) =
+          make_uint2(pack_bf16(acc[pt][0], acc[pt][1]), pack_bf16(acc[pt][2], acc[pt][3]));
     }
     if (more) hr.template store<SL>(s_x, s_prev, s_da, s_dt, s_w, s_D, lt);
     __syncthreads();                                         // y staged; the next head's inputs in LDS
-    {
-      constexpr int YU = kGQ * P / 8, YPT = YU / kGThreads;
-      __bf16* yh = y + ((size_t)b * L + t0) * x_tok + (size_t)h * P;
+  }
+  // the last head's y
+  {
+    int lt = tid;
+    asm volatile("" : "+v"(lt));
 #pragma unroll
-      for (int u = 0; u < YPT; ++u) {
-        const int v = lt + kGThreads * u;
-        const int row = v / (P / 8), cv = (v % (P / 8)) * 8;
-        uint32_t yo = (uint32_t)row * (uint32_t)x_tok + cv;
-        asm volatile("" : "+v"(yo));
-        if (row < len)
-          *reinterpret_cast<uint4*>(yh + yo) = *reinterpret_cast<const uint4*>(&s_y[row * SL::YP + cv]);
-      }
-    }
-    // s_y is rewritten only after the next head's first barrier: the flush above is complete by then
+    for (int u = 0; u < kYParts; ++u) flush_part(u, h0 + hs - 1, lt);
   }
 }
 
