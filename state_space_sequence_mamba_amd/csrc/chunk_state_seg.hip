@@ -18,13 +18,17 @@
 // One workgroup (8 wavefronts) per (batch, segment, group, slice of HS heads of the group).  Per
 // chunk: dt' and the in-chunk cumsum of dt' A for every head of the slice (wavefront hh, as in
 // chunk_state: a log-step shuffle scan over 64 lanes), written to the workspace for chunk_scan;
-// B^T staged once in LDS (token-contiguous rows) for all the slice's heads, and each wavefront's
-// sixteen dstate columns of it held in registers for the chunk.  Per head: the weighted x^T
-// staged in LDS, L_c written (rounded to bf16) unless c opens the segment, the state scaled by the
-// chunk's decay and the chunk's x^T diag(w) B added on 16x16x32 bf16 MFMA, the state of each head
-// held in the accumulators of the whole segment.  The next chunk's B and dt and the next head's x
-// are loaded into registers while the current ones are in use.  At the segment's end E_s goes out
-// in fp32 with the segment's total exponent; D_c goes out for every chunk.
+// B staged once in LDS for all the slice's heads and each wavefront's sixteen dstate rows of B^T
+// held in registers for the chunk.  Per head: x times the token weights staged in LDS, L_c written
+// (rounded to bf16) unless c opens the segment, the state scaled by the chunk's decay and the
+// chunk's B^T diag(w) x added on 16x16x32 bf16 MFMA, the state of each head held in the
+// accumulators of the whole segment.  B and x stay token-major in LDS (16 x 16 tiles, 16-byte
+// stores) and reach the MFMA through transpose reads (ds_read_b64_tr_b16); the state is formed
+// transposed (S^T[n][p]), so each lane holds four consecutive dstate values of one headdim row
+// and L_c and E_s leave as 8- and 16-byte row stores.  The next chunk's B and dt are loaded into
+// registers while the current ones are in use, and the next head's x in parts between the
+// MFMAs.  At the segment's end E_s goes out in fp32 with the segment's total exponent; D_c goes
+// out for every chunk.
 #include "ssd_common.h"
 #include "ssd_launch.h"
 
@@ -34,66 +38,73 @@ namespace {
 
 constexpr int kSQ = 256;                       // chunk length
 constexpr int kSThreads = 512;
-constexpr int kSXP = kSQ + 8;                  // token-contiguous LDS rows (bf16)
+constexpr int kST = 16 * 16 + 16;              // one 16 x 16 tile (token-major) plus 32 bytes of padding,
+                                               // which put the tiles of one token row in different banks
 
-// One token-pair unit of a (token x 16-byte vector) tile: the same 16-byte slice of two
-// consecutive tokens; consecutive lanes take consecutive token pairs, so the transposed LDS
-// stores (one packed pair of bf16 per row) of a wavefront hit consecutive banks.
-template <int VECS>                               // 16-byte vectors per token row
-struct PairTile {
-  static constexpr int U = (kSQ / 2) * VECS;      // units
+typedef short si16x4 __attribute__((ext_vector_type(4)));
+// LDS transpose read: in each group of 16 lanes, with M[j][q] the q-th 16-bit element at lane j's
+// address, lane i receives element k = M[4 k + i / 4][i % 4]; a 16 x 16 row-major tile read with
+// lane (i, g) at offset 4 (16 g + i) gives lane (i, g) the tile's column i, rows 4 g .. 4 g + 3
+__device__ __forceinline__ uint2 tr16(const __bf16* p) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                       (__attribute__((address_space(3))) si16x4*)(p)));
+}
+// 32 tokens of column i of two vertically adjacent tiles as one 16x16x32 operand: k = 8 g + e
+// stands for token 4 g + e of the first tile (e < 4) and 4 g + e - 4 of the second
+__device__ __forceinline__ bf16x8 tr16x2(const __bf16* t0, const __bf16* t1) {
+  const uint2 a = tr16(t0), b = tr16(t1);
+  return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{lo, hi}), b2));
+}
+
+// Token rows of a (256 token x VECS 16-byte vector) tile in registers: consecutive lanes take
+// consecutive 16-byte vectors of one token row (coalesced loads), and the stores into the
+// 16 x 16 LDS tiles are conflict-free.  Tokens past `len` read row 0 and are stored as zeros.
+template <int VECS>
+struct RowTile {
+  static constexpr int U = kSQ * VECS;
   static constexpr int UPT = U / kSThreads;
   static_assert(U % kSThreads == 0, "shape");
-  uint4 v[UPT][2];
+  uint4 v[UPT];
   uint32_t okm;
 
-  // rows of `stride` elements from `base` (wavefront-uniform), tokens past `len` read row 0
-  __device__ __forceinline__ void load(const __bf16* base, uint32_t stride, int len, int tid) {
-    okm = 0;
-#pragma unroll
-    for (int u = 0; u < UPT; ++u) {
-      const int w = tid + kSThreads * u;
-      const int m = w % (kSQ / 2), vec = (w / (kSQ / 2)) * 8;
-      const int t = 2 * m;
-      const bool ok0 = t < len, ok1 = t + 1 < len;
-      uint32_t o0 = (uint32_t)(ok0 ? t : 0) * stride + vec, o1 = (uint32_t)(ok1 ? t + 1 : 0) * stride + vec;
-      asm volatile("" : "+v"(o0), "+v"(o1));
-      v[u][0] = *reinterpret_cast<const uint4*>(base + o0);
-      v[u][1] = *reinterpret_cast<const uint4*>(base + o1);
-      okm |= ((uint32_t)ok0 << (2 * u)) | ((uint32_t)ok1 << (2 * u + 1));
-    }
+  __device__ __forceinline__ void load_one(int u, const __bf16* base, uint32_t stride, int len, int tid) {
+    const int q = tid + kSThreads * u;
+    const int t = q / VECS, vec = (q % VECS) * 8;
+    const bool ok = t < len;
+    uint32_t o = ((uint32_t)(ok ? t : 0) * stride + vec) * 2;
+    asm volatile("" : "+v"(o));
+    v[u] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(base) + o);
+    okm = (okm & ~(1u << u)) | ((uint32_t)ok << u);
   }
-  // transposed into `dst` rows (element row vec + e, token column 2m), each value times the
-  // token's weight when `wt` is given (weights of tokens past the end are 0, and so are they)
+  __device__ __forceinline__ void load(const __bf16* base, uint32_t stride, int len, int tid) {
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) load_one(u, base, stride, len, tid);
+  }
+  // into tiles (jt, ct) at (jt VECS / 2 + ct) kST; each value times its token's weight when `wt`
+  // is given
   __device__ __forceinline__ void store(__bf16* dst, const float* wt, int tid) const {
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
-      const int w = tid + kSThreads * u;
-      const int m = w % (kSQ / 2), vec = (w / (kSQ / 2)) * 8;
-      uint4 a = v[u][0], b = v[u][1];
-      if (!((okm >> (2 * u)) & 1u)) a = make_uint4(0, 0, 0, 0);
-      if (!((okm >> (2 * u + 1)) & 1u)) b = make_uint4(0, 0, 0, 0);
-      const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+      const int q = tid + kSThreads * u;
+      const int t = q / VECS, vec = (q % VECS) * 8;
+      uint4 a = (okm >> u) & 1u ? v[u] : make_uint4(0, 0, 0, 0);
       if (wt) {
-        const float w0 = wt[2 * m], w1 = wt[2 * m + 1];
+        const float wv = wt[t];
+        const uint32_t av[4] = {a.x, a.y, a.z, a.w};
+        uint32_t o[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float a0 = __builtin_bit_cast(float, av[q] << 16), a1 = __builtin_bit_cast(float, av[q] & 0xffff0000u);
-          const float b0 = __builtin_bit_cast(float, bv[q] << 16), b1 = __builtin_bit_cast(float, bv[q] & 0xffff0000u);
-          const __bf16 pa[2] = {static_cast<__bf16>(a0 * w0), static_cast<__bf16>(b0 * w1)};
-          const __bf16 pb[2] = {static_cast<__bf16>(a1 * w0), static_cast<__bf16>(b1 * w1)};
-          __builtin_memcpy(&dst[(vec + 2 * q) * kSXP + 2 * m], pa, 4);
-          __builtin_memcpy(&dst[(vec + 2 * q + 1) * kSXP + 2 * m], pb, 4);
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t lo = (av[q] & 0xffffu) | (bv[q] << 16);
-          const uint32_t hi = (av[q] >> 16) | (bv[q] & 0xffff0000u);
-          *reinterpret_cast<uint32_t*>(&dst[(vec + 2 * q) * kSXP + 2 * m]) = lo;
-          *reinterpret_cast<uint32_t*>(&dst[(vec + 2 * q + 1) * kSXP + 2 * m]) = hi;
-        }
+        for (int k = 0; k < 4; ++k)
+          o[k] = pack2(__builtin_bit_cast(float, av[k] << 16) * wv, __builtin_bit_cast(float, av[k] & 0xffff0000u) * wv);
+        a = make_uint4(o[0], o[1], o[2], o[3]);
       }
+      const int off = ((t >> 4) * (VECS / 2) + (vec >> 4)) * kST + (t & 15) * 16 + (vec & 15);
+      *reinterpret_cast<uint4*>(&dst[off]) = a;
     }
   }
 };
@@ -109,9 +120,10 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
     uint32_t nblocks) {
   constexpr int P = 64, N = 128, Q = kSQ, TP = P / 16, KS = Q / 32;
   constexpr int EPL = Q / 64;                      // cumsum positions per lane
+  constexpr int XV = P / 8, BV = N / 8;            // 16-byte vectors per token row
 
-  __shared__ __attribute__((aligned(16))) __bf16 s_bt[N * kSXP];   // B^T of the chunk
-  __shared__ __attribute__((aligned(16))) __bf16 s_xt[P * kSXP];   // (x w)^T of one head
+  __shared__ __attribute__((aligned(16))) __bf16 s_b[(Q / 16) * (N / 16) * kST];   // B of the chunk
+  __shared__ __attribute__((aligned(16))) __bf16 s_x[(Q / 16) * (P / 16) * kST];   // x w of one head
   __shared__ __attribute__((aligned(16))) float s_w[HS][Q];         // token weights per head
   __shared__ float s_last[HS];
 
@@ -126,7 +138,7 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
   const int c0 = seg * SL, c1 = min(nc, c0 + SL);
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // this wavefront's 16 dstate columns
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // this wavefront's 16 dstate rows
   const int r = lane & 15, qd = lane >> 4;
   const uint32_t x_tok = (uint32_t)H * P, b_tok = (uint32_t)G * N;
   const size_t PN = (size_t)P * N;
@@ -143,15 +155,17 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
     }
   };
 
-  f32x4 st[HS][TP];                                // the states, n column 16 w + r, rows 16 pt + 4 qd + e
+  // the states, transposed: st[hh][pt] lane (r, qd) holds S^T[n = 16 w + 4 qd + e][p = 16 pt + r]
+  f32x4 st[HS][TP];
 #pragma unroll
   for (int hh = 0; hh < HS; ++hh)
 #pragma unroll
     for (int pt = 0; pt < TP; ++pt) st[hh][pt] = zero4();
   float run = 0.f;                                 // wavefront hh: exponent sum since the segment start
 
-  PairTile<N / 8> breg;
-  PairTile<P / 8> xreg;
+  RowTile<BV> breg;
+  RowTile<XV> xreg;
+  breg.okm = xreg.okm = 0;
   float dtv[EPL];
   breg.load(b_base(c0), b_tok, min(Q, L - c0 * Q), tid);
   xreg.load(x_base(c0, 0), x_tok, min(Q, L - c0 * Q), tid);
@@ -159,8 +173,8 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
 
   for (int c = c0; c < c1; ++c) {
     const int len = min(Q, L - c * Q);
-    __syncthreads();                               // the previous chunk's weights and B^T consumed
-    breg.store(s_bt, nullptr, tid);
+    __syncthreads();                               // the previous chunk's weights and B consumed
+    breg.store(s_b, nullptr, tid);
     if (w < HS) {
       // dt' and the inclusive in-chunk cumsum of dt' A of head h0 + w; weights to the chunk end
       const int h = h0 + w;
@@ -202,53 +216,76 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
       breg.load(b_base(c + 1), b_tok, min(Q, L - (c + 1) * Q), tid);
       load_dt(c + 1, dtv);
     }
-    __syncthreads();                               // B^T, weights and exponents of chunk c in LDS
-    bf16x8 bfr[KS];                                // this wavefront's B^T rows for the whole chunk
+    __syncthreads();                               // B, weights and exponents of chunk c in LDS
+    // this wavefront's B^T rows n = 16 w + r for the whole chunk (A operands)
+    bf16x8 bfr[KS];
+    {
+      int bo = 4 * lane;
+      asm volatile("" : "+v"(bo));
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
-      bfr[kk] = *reinterpret_cast<const bf16x8*>(&s_bt[(16 * w + r) * kSXP + 32 * kk + 8 * qd]);
+      for (int kk = 0; kk < KS; ++kk)
+        bfr[kk] = tr16x2(&s_b[((2 * kk) * (N / 16) + w) * kST + bo], &s_b[((2 * kk + 1) * (N / 16) + w) * kST + bo]);
+    }
 
 #pragma unroll
     for (int hh = 0; hh < HS; ++hh) {
-      if (hh > 0) __syncthreads();                 // the previous head's x^T consumed
-      xreg.store(s_xt, s_w[hh], tid);
-      // the next x tile: the next head of this chunk, or the first head of the next chunk
-      if (hh + 1 < HS)
-        xreg.load(x_base(c, hh + 1), x_tok, len, tid);
-      else if (c + 1 < c1)
-        xreg.load(x_base(c + 1, 0), x_tok, min(Q, L - (c + 1) * Q), tid);
+      if (hh > 0) __syncthreads();                 // the previous head's x consumed
+      xreg.store(s_x, s_w[hh], tid);
       __syncthreads();
       const int h = h0 + hh;
+      // lane-dependent offsets recomputed per head (nothing lane-dependent is hoisted and kept)
+      int lt = tid;
+      asm volatile("" : "+v"(lt));
+      const int rr = lt & 15, qq = (lt >> 4) & 3;
       if (c > c0) {
         // L_c: the state this segment carried into chunk c, rounded to bf16 for the scan
-        __bf16* dst = prev16 + (((size_t)b * nc + c) * H + h) * PN + 16 * w + r;
+        __bf16* dst = prev16 + (((size_t)b * nc + c) * H + h) * PN;
+        uint32_t o = ((uint32_t)rr * N + 16 * w + 4 * qq) * 2;
+        asm volatile("" : "+v"(o));
 #pragma unroll
         for (int pt = 0; pt < TP; ++pt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) dst[(size_t)(16 * pt + 4 * qd + e) * N] = static_cast<__bf16>(st[hh][pt][e]);
+          *reinterpret_cast<uint2*>(reinterpret_cast<char*>(dst) + o + pt * 16 * N * 2) =
+              make_uint2(pack2(st[hh][pt][0], st[hh][pt][1]), pack2(st[hh][pt][2], st[hh][pt][3]));
       }
       const float dec = expf(s_last[hh]);
 #pragma unroll
       for (int pt = 0; pt < TP; ++pt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) st[hh][pt][e] *= dec;
+      // the next x: the next head of this chunk, or the first head of the next chunk, one part
+      // per pair of MFMA steps
+      const bool nxt_here = hh + 1 < HS, nxt_chunk = !nxt_here && c + 1 < c1;
+      const __bf16* xn = nxt_here ? x_base(c, hh + 1) : x_base(c + 1 < c1 ? c + 1 : c, 0);
+      const int ln = nxt_here ? len : min(Q, L - (c + 1 < c1 ? c + 1 : c) * Q);
+      int xo = 4 * (lt & 63);
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk)
+      for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
         for (int pt = 0; pt < TP; ++pt) {
-          const bf16x8 af = *reinterpret_cast<const bf16x8*>(&s_xt[(16 * pt + r) * kSXP + 32 * kk + 8 * qd]);
-          st[hh][pt] = mfma_16x16x32_bf16(af, bfr[kk], st[hh][pt]);
+          const bf16x8 xf = tr16x2(&s_x[((2 * kk) * (P / 16) + pt) * kST + xo],
+                                   &s_x[((2 * kk + 1) * (P / 16) + pt) * kST + xo]);
+          st[hh][pt] = mfma_16x16x32_bf16(bfr[kk], xf, st[hh][pt]);
         }
+        if ((nxt_here || nxt_chunk) && kk % 2 == 1 && kk / 2 < RowTile<XV>::UPT)
+          xreg.load_one(kk / 2, xn, x_tok, ln, lt);
+      }
     }
   }
   // the segment's end states and total exponents
+  {
+    int lt = tid;
+    asm volatile("" : "+v"(lt));
+    const int rr = lt & 15, qq = (lt >> 4) & 3;
 #pragma unroll
-  for (int hh = 0; hh < HS; ++hh) {
-    float* dst = E + (((size_t)b * nseg + seg) * H + h0 + hh) * PN + 16 * w + r;
+    for (int hh = 0; hh < HS; ++hh) {
+      float* dst = E + (((size_t)b * nseg + seg) * H + h0 + hh) * PN;
+      uint32_t o = ((uint32_t)rr * N + 16 * w + 4 * qq) * 4;
+      asm volatile("" : "+v"(o));
 #pragma unroll
-    for (int pt = 0; pt < TP; ++pt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dst[(size_t)(16 * pt + 4 * qd + e) * N] = st[hh][pt][e];
+      for (int pt = 0; pt < TP; ++pt)
+        *reinterpret_cast<float4*>(reinterpret_cast<char*>(dst) + o + pt * 16 * N * 4) =
+            make_float4(st[hh][pt][0], st[hh][pt][1], st[hh][pt][2], st[hh][pt][3]);
+    }
   }
   if (w < HS && lane == 0) segdec[((size_t)b * H + h0 + w) * nseg + seg] = run;
 }
