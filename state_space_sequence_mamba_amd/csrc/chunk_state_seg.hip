@@ -18,8 +18,8 @@
 // One workgroup (8 wavefronts) per (batch, segment, group, slice of HS heads of the group).  Per
 // chunk: dt' and the in-chunk cumsum of dt' A for every head of the slice (wavefront hh, as in
 // chunk_state: a log-step shuffle scan over 64 lanes), written to the workspace for chunk_scan;
-// B staged once in LDS for all the slice's heads and each wavefront's sixteen dstate rows of B^T
-// held in registers for the chunk.  Per head: x times the token weights staged in LDS, L_c written
+// B staged once in LDS for all the slice's heads; each wavefront owns a 32 x 32 block of S^T and
+// holds its 32 dstate rows of B^T in registers for the chunk.  Per head: x times the token weights staged in LDS, L_c written
 // (rounded to bf16) unless c opens the segment, the state scaled by the chunk's decay and the
 // chunk's B^T diag(w) x added on 16x16x32 bf16 MFMA, the state of each head held in the
 // accumulators of the whole segment.  B and x stay token-major in LDS (16 x 16 tiles, 16-byte
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
     float* __restrict__ dAcs, __bf16* __restrict__ prev16, float* __restrict__ E, float* __restrict__ segdec,
     float* __restrict__ cdec, int L, int H, int G, int nc, int SL, int nseg, int clamp, float lo, float hi,
     uint32_t nblocks) {
-  constexpr int P = 64, N = 128, Q = kSQ, TP = P / 16, KS = Q / 32;
+  constexpr int P = 64, N = 128, Q = kSQ, KS = Q / 32;
   constexpr int EPL = Q / 64;                      // cumsum positions per lane
   constexpr int XV = P / 8, BV = N / 8;            // 16-byte vectors per token row
 
@@ -138,7 +138,10 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
   const int c0 = seg * SL, c1 = min(nc, c0 + SL);
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // this wavefront's 16 dstate rows
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // this wavefront's 32 x 32 block of S^T: dstate tiles 2 nb, 2 nb + 1 and headdim tiles 2 pb, 2 pb + 1
+  // (each x operand read from LDS feeds two MFMAs)
+  const int nb = w >> 1, pb = w & 1;
   const int r = lane & 15, qd = lane >> 4;
   const uint32_t x_tok = (uint32_t)H * P, b_tok = (uint32_t)G * N;
   const size_t PN = (size_t)P * N;
@@ -155,12 +158,13 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
     }
   };
 
-  // the states, transposed: st[hh][pt] lane (r, qd) holds S^T[n = 16 w + 4 qd + e][p = 16 pt + r]
-  f32x4 st[HS][TP];
+  // the states, transposed: st[hh][2 ni + pi] lane (r, qd) holds S^T[n = 16 (2 nb + ni) + 4 qd + e]
+  // [p = 16 (2 pb + pi) + r]
+  f32x4 st[HS][4];
 #pragma unroll
   for (int hh = 0; hh < HS; ++hh)
 #pragma unroll
-    for (int pt = 0; pt < TP; ++pt) st[hh][pt] = zero4();
+    for (int j = 0; j < 4; ++j) st[hh][j] = zero4();
   float run = 0.f;                                 // wavefront hh: exponent sum since the segment start
 
   RowTile<BV> breg;
@@ -200,31 +204,31 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
       for (int k = 0; k < EPL; ++k) cs[k] += excl;
       const float last = __shfl(cs[EPL - 1], 63, 64);
       const size_t o = (((size_t)b * H + h) * nc + c) * Q + lane * EPL;
-#pragma unroll
-      for (int k = 0; k < EPL; ++k) {
-        dtp[o + k] = d[k];
-        dAcs[o + k] = cs[k];
-        s_w[w][lane * EPL + k] = expf(last - cs[k]) * d[k];
-      }
+      static_assert(EPL == 4, "one 16-byte store per lane");
+      *reinterpret_cast<float4*>(&dtp[o]) = make_float4(d[0], d[1], d[2], d[3]);
+      *reinterpret_cast<float4*>(&dAcs[o]) = make_float4(cs[0], cs[1], cs[2], cs[3]);
+      *reinterpret_cast<float4*>(&s_w[w][lane * EPL]) =
+          make_float4(expf(last - cs[0]) * d[0], expf(last - cs[1]) * d[1], expf(last - cs[2]) * d[2],
+                      expf(last - cs[3]) * d[3]);
       if (lane == 0) {
         s_last[w] = last;
         cdec[((size_t)b * H + h) * nc + c] = run;
       }
       run += last;
     }
-    if (c + 1 < c1) {
-      breg.load(b_base(c + 1), b_tok, min(Q, L - (c + 1) * Q), tid);
-      load_dt(c + 1, dtv);
-    }
+    if (c + 1 < c1) load_dt(c + 1, dtv);
     __syncthreads();                               // B, weights and exponents of chunk c in LDS
-    // this wavefront's B^T rows n = 16 w + r for the whole chunk (A operands)
-    bf16x8 bfr[KS];
+    // this wavefront's B^T rows n = 16 (2 nb + ni) + r for the whole chunk (A operands)
+    bf16x8 bfr[2][KS];
     {
       int bo = 4 * lane;
       asm volatile("" : "+v"(bo));
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk)
-        bfr[kk] = tr16x2(&s_b[((2 * kk) * (N / 16) + w) * kST + bo], &s_b[((2 * kk + 1) * (N / 16) + w) * kST + bo]);
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+          bfr[ni][kk] = tr16x2(&s_b[((2 * kk) * (N / 16) + 2 * nb + ni) * kST + bo],
+                               &s_b[((2 * kk + 1) * (N / 16) + 2 * nb + ni) * kST + bo]);
     }
 
 #pragma unroll
@@ -240,34 +244,58 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
       if (c > c0) {
         // L_c: the state this segment carried into chunk c, rounded to bf16 for the scan
         __bf16* dst = prev16 + (((size_t)b * nc + c) * H + h) * PN;
-        uint32_t o = ((uint32_t)rr * N + 16 * w + 4 * qq) * 2;
+        uint32_t o = ((uint32_t)(32 * pb + rr) * N + 32 * nb + 4 * qq) * 2;
         asm volatile("" : "+v"(o));
 #pragma unroll
-        for (int pt = 0; pt < TP; ++pt)
-          *reinterpret_cast<uint2*>(reinterpret_cast<char*>(dst) + o + pt * 16 * N * 2) =
-              make_uint2(pack2(st[hh][pt][0], st[hh][pt][1]), pack2(st[hh][pt][2], st[hh][pt][3]));
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<uint2*>(reinterpret_cast<char*>(dst) + o + ((j & 1) * 16 * N + (j >> 1) * 16) * 2) =
+              make_uint2(pack2(st[hh][j][0], st[hh][j][1]), pack2(st[hh][j][2], st[hh][j][3]));
       }
       const float dec = expf(s_last[hh]);
 #pragma unroll
-      for (int pt = 0; pt < TP; ++pt)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) st[hh][pt][e] *= dec;
+        for (int e = 0; e < 4; ++e) st[hh][j][e] *= dec;
       // the next x: the next head of this chunk, or the first head of the next chunk, one part
       // per pair of MFMA steps
       const bool nxt_here = hh + 1 < HS, nxt_chunk = !nxt_here && c + 1 < c1;
       const __bf16* xn = nxt_here ? x_base(c, hh + 1) : x_base(c + 1 < c1 ? c + 1 : c, 0);
       const int ln = nxt_here ? len : min(Q, L - (c + 1 < c1 ? c + 1 : c) * Q);
-      int xo = 4 * (lt & 63);
+      const int xo = 4 * (lt & 63);
+      // the next chunk's B, its parts spread over the heads' MFMA steps (every fourth step a slot
+      // of PPS parts)
+      constexpr int NSTEP = 2 * KS, BUP = RowTile<BV>::UPT, SLOTS = NSTEP / 4,
+                    PPS = (BUP + HS * SLOTS - 1) / (HS * SLOTS);
+      const __bf16* bn = b_base(c + 1 < c1 ? c + 1 : c);
+      const int lbn = min(Q, L - (c + 1 < c1 ? c + 1 : c) * Q);
+      // the MFMA steps (pi outer, kk inner; two MFMAs per x operand), the operand of the next
+      // step read before the current step's MFMAs
+      auto xop = [&](int kk, int pi) {
+        const int pt = 2 * pb + pi;
+        return tr16x2(&s_x[((2 * kk) * (P / 16) + pt) * kST + xo], &s_x[((2 * kk + 1) * (P / 16) + pt) * kST + xo]);
+      };
+      bf16x8 xf = xop(0, 0);
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
+      for (int pi = 0; pi < 2; ++pi) {
 #pragma unroll
-        for (int pt = 0; pt < TP; ++pt) {
-          const bf16x8 xf = tr16x2(&s_x[((2 * kk) * (P / 16) + pt) * kST + xo],
-                                   &s_x[((2 * kk + 1) * (P / 16) + pt) * kST + xo]);
-          st[hh][pt] = mfma_16x16x32_bf16(bfr[kk], xf, st[hh][pt]);
+        for (int kk = 0; kk < KS; ++kk) {
+          const int step = pi * KS + kk;
+          const bf16x8 cur = xf;
+          if (step + 1 < NSTEP) xf = xop((step + 1) % KS, (step + 1) / KS);
+          st[hh][pi] = mfma_16x16x32_bf16(bfr[0][kk], cur, st[hh][pi]);
+          st[hh][2 + pi] = mfma_16x16x32_bf16(bfr[1][kk], cur, st[hh][2 + pi]);
+          if (step % 4 == 1) {
+            const int part = step / 4;             // 0..3: the next x, in parts
+            if ((nxt_here || nxt_chunk) && part < RowTile<XV>::UPT) xreg.load_one(part, xn, x_tok, ln, lt);
+          }
+          if (step % 4 == 3 && c + 1 < c1) {
+#pragma unroll
+            for (int j = 0; j < PPS; ++j) {
+              const int part = (hh * SLOTS + step / 4) * PPS + j;
+              if (part < BUP) breg.load_one(part, bn, b_tok, lbn, lt);
+            }
+          }
         }
-        if ((nxt_here || nxt_chunk) && kk % 2 == 1 && kk / 2 < RowTile<XV>::UPT)
-          xreg.load_one(kk / 2, xn, x_tok, ln, lt);
       }
     }
   }
@@ -279,12 +307,12 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
 #pragma unroll
     for (int hh = 0; hh < HS; ++hh) {
       float* dst = E + (((size_t)b * nseg + seg) * H + h0 + hh) * PN;
-      uint32_t o = ((uint32_t)rr * N + 16 * w + 4 * qq) * 4;
+      uint32_t o = ((uint32_t)(32 * pb + rr) * N + 32 * nb + 4 * qq) * 4;
       asm volatile("" : "+v"(o));
 #pragma unroll
-      for (int pt = 0; pt < TP; ++pt)
-        *reinterpret_cast<float4*>(reinterpret_cast<char*>(dst) + o + pt * 16 * N * 4) =
-            make_float4(st[hh][pt][0], st[hh][pt][1], st[hh][pt][2], st[hh][pt][3]);
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float4*>(reinterpret_cast<char*>(dst) + o + ((j & 1) * 16 * N + (j >> 1) * 16) * 4) =
+            make_float4(st[hh][j][0], st[hh][j][1], st[hh][j][2], st[hh][j][3]);
     }
   }
   if (w < HS && lane == 0) segdec[((size_t)b * H + h0 + w) * nseg + seg] = run;
