@@ -70,5 +70,44 @@ def build(verbose=False, jobs=None):
     return LIB
 
 
+# Host code built with AddressSanitizer (device code unchanged), for the CPU tests of the C ABI's
+# host logic: loaded by a Python process that preloads the clang ASan runtime.
+ASAN_DIR = os.path.join(BUILD, "asan")
+LIB_ASAN = os.path.join(ASAN_DIR, "libssd_asan.so")
+ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+
+
+def asan_runtime():
+    """The clang ASan runtime matching hipcc's host compiler (None if not installed)."""
+    root = os.path.join(os.path.dirname(os.path.dirname(hipcc())), "llvm", "lib", "clang")
+    if not os.path.isdir(root):
+        return None
+    for ver in sorted(os.listdir(root), reverse=True):
+        cand = os.path.join(root, ver, "lib", "linux", "libclang_rt.asan-x86_64.so")
+        if os.path.exists(cand):
+            return cand
+    return None
+
+
+def build_asan(force=False, jobs=None):
+    """Build (or reuse, when newer than every source and header) the host-sanitized library."""
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    deps = [os.path.join(CSRC, f) for f in os.listdir(CSRC)] + [os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE)]
+    if not force and os.path.exists(LIB_ASAN) and os.path.getmtime(LIB_ASAN) > max(map(os.path.getmtime, deps)):
+        return LIB_ASAN
+    cc = hipcc()
+    cmds = [[cc, *FLAGS, *ASAN_FLAGS, "-c", os.path.join(CSRC, src), "-o",
+             os.path.join(ASAN_DIR, os.path.splitext(src)[0] + ".o")] for src in SOURCES]
+    jobs = jobs or min(len(cmds), os.cpu_count() or 4, 8)
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        list(ex.map(_run, cmds))
+    objs = [c[-1] for c in cmds]
+    tmp = LIB_ASAN + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address", "-shared-libasan",
+          "-o", tmp, *objs])
+    os.replace(tmp, LIB_ASAN)
+    return LIB_ASAN
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

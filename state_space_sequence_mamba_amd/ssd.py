@@ -10,7 +10,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libssd.so")
+# SSD_LIBRARY names another build of the same library (the host-sanitized one the CPU tests load)
+LIB_PATH = os.environ.get("SSD_LIBRARY") or os.path.join(_HERE, "libssd.so")
 
 (SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_DEVICE_PTR, SSD_ERR_WORKSPACE, SSD_ERR_HIP,
  SSD_ERR_SCRATCH_LIMIT) = range(7)
