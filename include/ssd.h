@@ -188,6 +188,22 @@ ssd_status_t ssd_bwd(const ssd_dims_t* dims,
                      void* dz, float* dinitial_state,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Gated RMSNorm of the scan output ("Agent 228: MAMBA-2 Reference Implementations Comparison",
+ * section 7.3: item 9, the output gate y * silu(z); item 11, an RMSNorm in front of the final
+ * projection).  Over each token's channels in groups of norm_heads consecutive heads
+ * (norm_heads * P channels; norm_heads = H normalises all of d_inner):
+ *     g = y * silu(z)  (g = y when z is NULL),   out = g / sqrt(mean_group(g^2) + eps) * weight
+ *   y, z, out  (B, L, H, P)  dtype   16-byte aligned; out is y itself (in place) or disjoint
+ *                                    from y and z
+ *   weight     (H * P)       fp32    16-byte aligned, channel order h * P + p
+ * norm_heads must divide H and eps must be finite and >= 0 (else SSD_ERR_INVALID_ARG); headdim a
+ * multiple of 8 (else SSD_ERR_UNSUPPORTED).  dims->dstate, ngroups and dt_min/dt_max are not used
+ * (they must still be valid).  batch == 0 or seqlen == 0 is a no-op; for decoding pass one token
+ * per sequence (seqlen = 1).  The sum of squares is accumulated in fp32 in a fixed order
+ * (deterministic).  One kernel, one pass over y, z and out in HBM. */
+ssd_status_t ssd_gated_rmsnorm(const ssd_dims_t* dims, const void* y, const void* z, const float* weight,
+                               float eps, int norm_heads, void* out, hipStream_t stream);
+
 /* Causal depthwise conv1d + SiLU that produces the scan's x, B and C ("Agent 228: MAMBA-2
  * Implementation Gaps", Gap 2: one filter of width K = conv_width per channel, causal padding
  * K - 1; SiLU after it as in section 3.1 of "Agent 228: MAMBA-2 Reference Implementations

@@ -83,6 +83,12 @@ ssd_status_t ssd_step_ex(const ssd_dims_t* dims, float* state,
                          const void* B, const void* C, const float* D, const void* z,
                          void* y, hipStream_t stream, hipEvent_t* events);
 
+/* ssd_gated_rmsnorm with timing: `events` NULL or 2 caller-created events, the start and stop
+ * of the kernel recorded by its own dispatch.  Refuses a stream under graph capture when events
+ * are given (SSD_ERR_UNSUPPORTED, nothing launched). */
+ssd_status_t ssd_gated_rmsnorm_ex(const ssd_dims_t* dims, const void* y, const void* z, const float* weight,
+                                  float eps, int norm_heads, void* out, hipStream_t stream, hipEvent_t* events);
+
 /* ssd_conv1d_silu with options (field conv_tokens). */
 ssd_status_t ssd_conv1d_silu_ex(const ssd_dims_t* dims, int conv_width, const void* xbc,
                                 const float* weight, const float* bias, const void* conv_state_in,

@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libssd.so")
 
 SOURCES = ["ssd_api.hip", "chunk_state.hip", "chunk_state_seg.hip", "state_passing.hip", "chunk_scan.hip",
            "chunk_scan_group.hip",
-           "ssd_step.hip", "conv1d.hip", "ssd_bwd.hip"]
+           "ssd_step.hip", "conv1d.hip", "ssd_bwd.hip", "gated_norm.hip"]
 # measurement only (bench.py --peak-probe): register-resident MFMA loops, a library of its own
 PEAK_SOURCES = ["peak_probe.hip"]
 LIB_PEAK = os.path.join(PKG, "libssd_peak.so")

@@ -142,7 +142,6 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
   // this wavefront's 32 x 32 block of S^T: dstate tiles 2 nb, 2 nb + 1 and headdim tiles 2 pb, 2 pb + 1
   // (each x operand read from LDS feeds two MFMAs)
   const int nb = w >> 1, pb = w & 1;
-  const int r = lane & 15, qd = lane >> 4;
   const uint32_t x_tok = (uint32_t)H * P, b_tok = (uint32_t)G * N;
   const size_t PN = (size_t)P * N;
 

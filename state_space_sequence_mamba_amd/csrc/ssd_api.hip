@@ -827,6 +827,65 @@ ssd_status_t ssd_bwd_ex(const ssd_dims_t* dims, const void* x, const void* dt, c
                   stage_events);
 }
 
+namespace {
+ssd_status_t norm_impl(const ssd_dims_t* dims, const void* y, const void* z, const float* weight, float eps,
+                       int norm_heads, void* out, hipStream_t stream, hipEvent_t* events) {
+  ssd_status_t st = check_dims(dims, true);
+  if (st != SSD_OK) return st;
+  if (dims->headdim % 8 != 0) return SSD_ERR_UNSUPPORTED;
+  if (norm_heads < 1 || norm_heads > dims->nheads || dims->nheads % norm_heads != 0) return SSD_ERR_INVALID_ARG;
+  if (!(eps >= 0.f) || eps > 3.0e38f) return SSD_ERR_INVALID_ARG;          // (NaN and inf fail)
+  if (norm_heads * dims->headdim > (int64_t)1 << 24) return SSD_ERR_UNSUPPORTED;
+  const int64_t tokens = dims->batch * dims->seqlen;
+  if (tokens * (dims->nheads / norm_heads) > ((int64_t)1 << 32) - 4) return SSD_ERR_UNSUPPORTED;
+  if (tokens == 0) return SSD_OK;
+  if (!y || !weight || !out) return SSD_ERR_INVALID_ARG;
+  if (!aligned(y, 16) || !aligned(out, 16) || (z && !aligned(z, 16)) || !aligned(weight, 16))
+    return SSD_ERR_INVALID_ARG;
+  // out is y itself or disjoint from y and z
+  const size_t bytes = (size_t)tokens * dims->nheads * dims->headdim * elem_bytes(dims->dtype);
+  auto overlap = [&](const void* a) {
+    const char* p = static_cast<const char*>(a);
+    const char* o = static_cast<const char*>(out);
+    return p < o + bytes && o < p + bytes;
+  };
+  if ((out != y && overlap(y)) || (z && overlap(z))) return SSD_ERR_INVALID_ARG;
+  for (const void* p : {y, z, static_cast<const void*>(weight), static_cast<const void*>(out)})
+    if (p && !device_ptr_ok(p)) return SSD_ERR_DEVICE_PTR;
+  if (events) {                                  // (event records cannot be captured)
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return SSD_ERR_HIP;
+    if (cs != hipStreamCaptureStatusNone) return SSD_ERR_UNSUPPORTED;
+  }
+  ssd::NormArgs a;
+  a.tokens = tokens;
+  a.H = (int)dims->nheads;
+  a.P = (int)dims->headdim;
+  a.norm_heads = norm_heads;
+  a.dtype = dims->dtype;
+  a.y = y;
+  a.z = z;
+  a.weight = weight;
+  a.out = out;
+  a.eps = eps;
+  if (events) {
+    a.ev0 = events[0];
+    a.ev1 = events[1];
+  }
+  return ssd::launch_gated_rmsnorm(a, stream) == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+}  // namespace
+
+ssd_status_t ssd_gated_rmsnorm(const ssd_dims_t* dims, const void* y, const void* z, const float* weight, float eps,
+                               int norm_heads, void* out, hipStream_t stream) {
+  return norm_impl(dims, y, z, weight, eps, norm_heads, out, stream, nullptr);
+}
+
+ssd_status_t ssd_gated_rmsnorm_ex(const ssd_dims_t* dims, const void* y, const void* z, const float* weight,
+                                  float eps, int norm_heads, void* out, hipStream_t stream, hipEvent_t* events) {
+  return norm_impl(dims, y, z, weight, eps, norm_heads, out, stream, events);
+}
+
 ssd_status_t ssd_conv1d_silu(const ssd_dims_t* dims, int conv_width, const void* xbc, const float* weight,
                              const float* bias, const void* conv_state_in, void* conv_state_out, void* x, void* B,
                              void* C, hipStream_t stream) {

@@ -153,6 +153,20 @@ hipError_t launch_bwd_finalize(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_reduce(const BwdArgs& a, hipStream_t s);
 hipError_t launch_gate_bwd(const GateArgs& a, hipStream_t s);
 hipError_t launch_conv1d_silu(const ConvArgs& a, hipStream_t s);
+
+// Gated RMSNorm of the scan output (gated_norm.hip).
+struct NormArgs {
+  int64_t tokens;          // B * L
+  int H, P, norm_heads;    // norm_heads divides H
+  int dtype;
+  const void* y;           // (tokens, H, P)
+  const void* z;           // same shape, or null (no gate)
+  const float* weight;     // (H * P)
+  void* out;               // same shape; y itself or disjoint from y and z
+  float eps;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;   // optional dispatch events
+};
+hipError_t launch_gated_rmsnorm(const NormArgs& a, hipStream_t s);
 hipError_t launch_conv1d_silu_step(const ConvArgs& a, hipStream_t s);
 
 }  // namespace ssd

@@ -134,6 +134,17 @@ def make_gate(shape, dtype="f32", seed=0, device="cpu"):
     return torch.randn(*shape, generator=g).to(_torch_dtype(dtype)).to(device)
 
 
+def make_norm_inputs(batch, seqlen, nheads, headdim, dtype="f32", seed=0, device="cpu"):
+    """Inputs of one gated_rmsnorm call: y and z (B,L,H,P) ~ N(0, 1) in `dtype` (the scale of a
+    scan output and its gate), weight (H*P,) fp32 ~ 1 + 0.1 N(0, 1) (norm weights near one)."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    y = torch.randn(batch, seqlen, nheads, headdim, generator=g)
+    z = torch.randn(batch, seqlen, nheads, headdim, generator=g)
+    w = 1.0 + 0.1 * torch.randn(nheads * headdim, generator=g)
+    td = _torch_dtype(dtype)
+    return {"y": y.to(td).to(device), "z": z.to(td).to(device), "weight": w.float().to(device)}
+
+
 def make_conv_inputs(batch, seqlen, nheads, headdim, dstate, ngroups, width=4, dtype="f32", seed=0,
                      with_state=False, device="cpu"):
     """Inputs of one conv1d_silu call, drawn on the CPU and moved to `device`.

@@ -72,6 +72,11 @@ def load_library():
     lib = ctypes.CDLL(LIB_PATH)
     vp, f32p, i32, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     dims_p = ctypes.POINTER(ssd_dims_t)
+    norm_args = [dims_p, vp, vp, f32p, ctypes.c_float, i32, vp, vp]
+    lib.ssd_gated_rmsnorm.argtypes = norm_args
+    lib.ssd_gated_rmsnorm.restype = i32
+    lib.ssd_gated_rmsnorm_ex.argtypes = norm_args + [vp]
+    lib.ssd_gated_rmsnorm_ex.restype = i32
     lib.ssd_fwd_workspace_size.argtypes = [dims_p, i32]
     lib.ssd_fwd_workspace_size.restype = sz
     fwd_args = [dims_p, vp, vp, f32p, f32p, vp, vp, f32p, vp, i32, f32p, vp, f32p, vp, sz, vp]
@@ -250,6 +255,39 @@ def ssd_step(state, x, dt, dt_bias, A, B, C, D=None, y=None, stream=None, z=None
     if st != SSD_OK:
         raise SsdError(st, "ssd_step")
     return y
+
+
+def gated_rmsnorm(y, weight, z=None, eps=1e-5, norm_heads=None, out=None, stream=None, events=None):
+    """out = g / sqrt(mean(g^2) + eps) * weight, g = y * silu(z) (g = y without z), over each token's
+    channels in groups of `norm_heads` heads (default: all H heads).
+
+    y, z, out: (B, L, H, P) or, for one decode token, (B, H, P), one dtype; weight (H*P,) float32.
+    `out` may be `y` itself.  `events` (2 raw hipEvent_t handles) selects ssd_gated_rmsnorm_ex.
+    """
+    if y.dim() not in (3, 4):
+        raise ValueError("y (B, L, H, P) or (B, H, P) expected")
+    b, L, H, P = (y.shape[0], 1, y.shape[1], y.shape[2]) if y.dim() == 3 else tuple(y.shape)
+    if z is not None and (z.shape != y.shape or z.dtype != y.dtype):
+        raise ValueError("z must have y's shape and dtype")
+    if weight.dtype != torch.float32 or weight.numel() != H * P:
+        raise ValueError("weight (H*P,) float32 expected")
+    for t in (y, z, weight, out):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if out is None:
+        out = torch.empty_like(y)
+    elif out.shape != y.shape or out.dtype != y.dtype:
+        raise ValueError("out must have y's shape and dtype")
+    N = 64 if y.dtype == torch.float32 else 128            # (not used by the norm; any supported size)
+    dims = make_dims(b, L, H, P, N, 1, y.dtype)
+    args = [ctypes.byref(dims), _ptr(y), _ptr(z), _ptr(weight), ctypes.c_float(eps),
+            int(H if norm_heads is None else norm_heads), _ptr(out), _stream(stream)]
+    lib = load_library()
+    st = lib.ssd_gated_rmsnorm(*args) if events is None else \
+        lib.ssd_gated_rmsnorm_ex(*args, (ctypes.c_void_p * 2)(*events))
+    if st != SSD_OK:
+        raise SsdError(st, "ssd_gated_rmsnorm")
+    return out
 
 
 def ssd_bwd_workspace_size(dims, chunk_size, with_gate=False):

@@ -281,3 +281,29 @@ def test_noalloc_refuses_oversize_before_any_device_call(lib):
     args[8] = 100                                                       # chunk size
     assert lib.ssd_fwd_noalloc(ctypes.byref(big), *args) == ssd.SSD_ERR_UNSUPPORTED
     assert "scratch" in ssd.ssd_status_string(ssd.SSD_ERR_SCRATCH_LIMIT)
+
+
+def test_gated_rmsnorm_host_validation(lib):
+    vp, f = ctypes.c_void_p, ctypes.c_float
+    p = vp(0x100000)
+    d = _dims()                                   # H = 4
+    # (dims, y, z, weight, eps, norm_heads, out, stream)
+    assert lib.ssd_gated_rmsnorm(None, p, None, p, f(1e-5), 4, p, None) == ssd.SSD_ERR_INVALID_ARG
+    for nh in (0, 3, 5, -1):                      # must divide H
+        assert lib.ssd_gated_rmsnorm(ctypes.byref(d), p, None, p, f(1e-5), nh, p, None) == ssd.SSD_ERR_INVALID_ARG
+    for eps in (-1.0, float("nan"), float("inf")):
+        assert lib.ssd_gated_rmsnorm(ctypes.byref(d), p, None, p, f(eps), 4, p, None) == ssd.SSD_ERR_INVALID_ARG
+    assert lib.ssd_gated_rmsnorm(ctypes.byref(d), None, None, p, f(1e-5), 4, p, None) == ssd.SSD_ERR_INVALID_ARG
+    assert lib.ssd_gated_rmsnorm(ctypes.byref(d), p, None, None, f(1e-5), 2, p, None) == ssd.SSD_ERR_INVALID_ARG
+    assert lib.ssd_gated_rmsnorm(ctypes.byref(d), vp(0x100008), None, p, f(1e-5), 2, vp(0x900000),
+                                 None) == ssd.SSD_ERR_INVALID_ARG        # y not 16-byte aligned
+    # out overlapping y without being y, or overlapping z
+    assert lib.ssd_gated_rmsnorm(ctypes.byref(d), p, None, vp(0x800000), f(1e-5), 1, vp(0x100010),
+                                 None) == ssd.SSD_ERR_INVALID_ARG
+    assert lib.ssd_gated_rmsnorm(ctypes.byref(d), p, vp(0x200000), vp(0x800000), f(1e-5), 1, vp(0x200000),
+                                 None) == ssd.SSD_ERR_INVALID_ARG
+    # no tokens: nothing to do, the pointers may be NULL
+    assert lib.ssd_gated_rmsnorm(ctypes.byref(_dims(batch=0)), None, None, None, f(0.0), 4, None,
+                                 None) == ssd.SSD_OK
+    assert lib.ssd_gated_rmsnorm(ctypes.byref(_dims(seqlen=0)), None, None, None, f(0.0), 2, None,
+                                 None) == ssd.SSD_OK
