@@ -490,6 +490,69 @@ def run_conv(w, args, dev, opts=None):
     return out
 
 
+def run_norm(w, args, dev):
+    """The gated RMSNorm workload: K launches over one resident batch (HIP graph replay); the
+    kernel's own duration from dispatch-recorded events over K more eager launches."""
+    c = I.make_norm_inputs(w.batch, w.seqlen, w.nheads, w.headdim, w.dtype, w.seed, device=dev)
+    out_t = torch.empty_like(c["y"])
+
+    def step(events=None):
+        ssd.gated_rmsnorm(c["y"], c["weight"], z=c["z"], out=out_t, events=events)
+
+    K, W = args.steps, args.warmup
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    use_graph = not args.no_graph
+    if use_graph:
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(graph, stream=cap):
+            for _ in range(K):
+                step()
+        torch.cuda.synchronize()
+    hev = HipEvents()
+    t0, t1 = hev.create(), hev.create()
+    wall0 = time.perf_counter()
+    hev.record(t0)
+    if use_graph:
+        graph.replay()
+    else:
+        for _ in range(K):
+            step()
+    hev.record(t1)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = hev.elapsed_ms(t0, t1) / K
+    # the kernel alone: dispatch events around each eager launch
+    kev = [(hev.create(), hev.create()) for _ in range(K)]
+    for a, b in kev:
+        step(events=[a, b])
+    torch.cuda.synchronize()
+    k_ms = sum(hev.elapsed_ms(a, b) for a, b in kev) / K
+    hev.close()
+    e = 2 if w.dtype == "bf16" else 4
+    ch = w.nheads * w.headdim
+    alg_bytes = 3 * w.batch * w.seqlen * ch * e + ch * 4          # y, z in; out; the weights
+    ach = alg_bytes / (k_ms * 1e-3) / 1e9
+    return {
+        "metric": "gated RMSNorm tokens/sec at 1 MI355X + % of HBM roofline",
+        "value": round(w.batch * w.seqlen / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) y and z, weights 1 + 0.1 N(0,1))",
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "channels": ch,
+                   "norm_heads": w.nheads},
+        "roofline": {"kernel": "gated_rmsnorm", "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic(workload_slug(w.name), "gated_rmsnorm"),
+                     "alg_bytes_per_launch": alg_bytes, "kernel_us": round(k_ms * 1e3, 3)},
+        "launch": "hip_graph" if use_graph else "eager",
+        "wall_s_timed_region": round(wall, 4),
+    }
+
+
 def fwd_summary(out):
     """The fields of a forward or decode line that the configs array keeps."""
     r = out["roofline"]
@@ -671,6 +734,8 @@ def main():
         out = run_bwd(w, args, dev, opts)
     elif w.entry == "conv":
         out = run_conv(w, args, dev, opts)
+    elif w.entry == "norm":
+        out = run_norm(w, args, dev)
     else:
         out = run_fwd(w, args, dev, opts, with_cpu=not args.no_cpu_baseline)
         if w.name == DEFAULT_WORKLOAD and not args.no_configs:
@@ -685,6 +750,8 @@ def main():
                     configs.append(fwd_summary(run_fwd(cw, args, dev, None, with_cpu=False)))
                 torch.cuda.empty_cache()
             out["configs"] = configs
+            # the optional gated RMSNorm after the scan, on the headline forward's output size
+            out["extras"] = [fwd_summary(run_norm(I.workload("gated_rmsnorm bf16 B2 L16384 H80 P64"), args, dev))]
     emit(args, dev, out)
 
 

@@ -6,9 +6,9 @@
 //
 // The norm couples all the channels of a group of heads of one token, while the scan's
 // workgroups own slices of heads (and write a head's y before the next head is computed), so it
-// runs as its own pass: one wavefront per (token, group) reads the group's y and z once from
-// HBM (the second sweep, after the wavefront's sum of squares, hits the caches), and writes out
-// once -- an HBM-bound pass of 3 tensors (2 without a gate).  16-byte vectors of 8 channels per
+// runs as its own pass: one wavefront per (token, group) reads the group's y and z once (kept in
+// registers for groups up to 5120 channels; larger groups sweep them a second time from cache)
+// and writes out once -- an HBM-bound pass of 3 tensors (2 without a gate).  16-byte vectors of 8 channels per
 // lane; the sum of squares in fp32 in a fixed order (deterministic).
 #include "ssd_common.h"
 #include "ssd_launch.h"
@@ -67,6 +67,10 @@ __device__ __forceinline__ void gated(const T* y, const T* z, size_t o, float (&
 
 }  // namespace
 
+// Groups of up to kRegChunks * 512 channels keep g in registers between the sum of squares and
+// the output (one read of y and z); larger groups read them twice (the second time from cache).
+constexpr int kRegChunks = 10;
+
 template <typename T>
 __global__ __launch_bounds__(kNThreads) void gated_rmsnorm_kernel(const T* __restrict__ y, const T* __restrict__ z,
                                                                  const float* __restrict__ weight, T* out,
@@ -78,6 +82,33 @@ __global__ __launch_bounds__(kNThreads) void gated_rmsnorm_kernel(const T* __res
   const size_t base = ((size_t)tok * gpt + grp) * gl;
   const float* wg = weight + (size_t)grp * gl;
   float ss = 0.f;
+  if (gl <= kRegChunks * 512) {
+    float g[kRegChunks][8];
+#pragma unroll
+    for (int c = 0; c < kRegChunks; ++c) {
+      const int i = c * 512 + 8 * lane;
+      if (i < gl) {
+        gated(y, z, base + i, g[c]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) ss += g[c][k] * g[c][k];
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    const float scale = 1.0f / sqrtf(ss / (float)gl + eps);
+#pragma unroll
+    for (int c = 0; c < kRegChunks; ++c) {
+      const int i = c * 512 + 8 * lane;
+      if (i < gl) {
+        const float4 w0 = *reinterpret_cast<const float4*>(wg + i), w1 = *reinterpret_cast<const float4*>(wg + i + 4);
+        const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) g[c][k] = g[c][k] * scale * wv[k];
+        Vec8<T>::store(out + base + i, g[c]);
+      }
+    }
+    return;
+  }
   for (int i = 8 * lane; i < gl; i += 8 * 64) {
     float g[8];
     gated(y, z, base + i, g);

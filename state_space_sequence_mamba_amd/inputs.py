@@ -30,7 +30,7 @@ DT_MAX = 1e-1
 @dataclass(frozen=True)
 class Workload:
     name: str
-    entry: str            # "fwd", "bwd", "step" or "conv"
+    entry: str            # "fwd", "bwd", "step", "conv" or "norm"
     dtype: str            # "f32" or "bf16" (x, dt, B, C, y)
     batch: int
     nheads: int
@@ -70,6 +70,10 @@ WORKLOADS = {w.name: w for w in [
     # the conv in front of the scan, on the channels of the B8 L4096 bf16 forward (Dc 2304)
     Workload("conv1d_silu bf16 B8 L4096 H32 P64 N128 G1 K4", "conv", "bf16", 8, 32, 64, 128, 1, 5, "ones",
              seqlen=4096, width=4),
+    # the gated RMSNorm after the scan, over the B2 L16384 H80 bf16 forward's output (all 80 heads
+    # of a token normalised together)
+    Workload("gated_rmsnorm bf16 B2 L16384 H80 P64", "norm", "bf16", 2, 80, 64, 128, 1, 6, "ones",
+             seqlen=16384),
 ]}
 WORKLOAD_LIST = list(WORKLOADS.values())
 

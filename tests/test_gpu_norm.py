@@ -29,6 +29,7 @@ CASES = [
     # (B, L, H, P, norm_heads)
     (2, 37, 4, 64, 4), (2, 37, 4, 64, 1), (2, 37, 4, 64, 2), (1, 5, 6, 32, 6), (1, 5, 6, 32, 3),
     (3, 1, 3, 16, 3), (1, 130, 10, 64, 10), (2, 3, 16, 64, 16),
+    (1, 3, 96, 64, 96), (1, 2, 81, 64, 81),            # groups beyond the 5120 channels kept in registers
 ]
 
 
