@@ -153,7 +153,8 @@ def summary(args):
     events = {}
     if bench:
         for k, v in bench.get("kernels", {}).items():
-            events[k] = v["us"]
+            # (bench.py names state_passing over segments after its role; the trace, after its kernel)
+            events["state_passing" if k == "state_passing_seg" else k] = v["us"]
         rl = bench.get("roofline", {})
         if rl.get("kernel"):
             events.setdefault(rl["kernel"], None)
