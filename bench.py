@@ -681,7 +681,8 @@ def run_fwd(w, args, dev, opts, with_cpu):
 
 def launch_options(args):
     o = {k: getattr(args, k) for k in ("scan_variant", "heads_per_block", "rows_group", "state_path",
-                                       "state_slice", "conv_tokens", "state_heads", "state_chunks") if getattr(args, k)}
+                                       "state_slice", "conv_tokens", "state_heads", "state_chunks", "bwd_heads")
+         if getattr(args, k)}
     return o or None
 
 
@@ -717,6 +718,8 @@ def main():
                     help="segmented chunk states: heads per workgroup (0 = built-in)")
     ap.add_argument("--state-chunks", type=int, default=0,
                     help="segmented chunk states: chunks per segment (0 = built-in)")
+    ap.add_argument("--bwd-heads", type=int, default=0,
+                    help="ssd_bwd: heads per bwd_dxdb / bwd_dc workgroup, dB / dC summed on chip (0 = built-in)")
     ap.add_argument("--conv-tokens", type=int, default=0,
                     help="conv1d_silu tokens per thread, a multiple of 4 (0 = built-in)")
     args = ap.parse_args()

@@ -42,6 +42,10 @@ typedef struct {
   int32_t conv_tokens;      /* ssd_conv1d_silu tokens per thread (rounded up to a multiple of 4) */
   int32_t state_heads;      /* segmented chunk states: heads per workgroup (1, 2, 4 or 5) */
   int32_t state_chunks;     /* segmented chunk states: chunks per segment (at least 2) */
+  int32_t bwd_heads;        /* ssd_bwd: heads per bwd_dxdb workgroup, whose dB contributions are
+                             * summed in registers before they leave the chip: 1, or 4 for SSD_BF16
+                             * when it divides nheads / ngroups (else 1); the summation order
+                             * changes, results agree to rounding */
 } ssd_launch_opts_t;
 
 /* ssd_fwd with options and per-kernel timing.  `opts` may be NULL.  `stage_events` is NULL or

@@ -19,12 +19,14 @@
 // kernels.
 //
 // Kernels here, each one workgroup of 256 threads:
-//   bwd_dxdb   per (b, c, 64-row block R, h): the anti-causal sums over row blocks I >= R
+//   bwd_dxdb   per (b, c, 64-row block R, slice of hs heads of a group): the anti-causal sums
+//              over row blocks I >= R, head after head, dB summed over the slice in registers
 //              (fp32: C B^T read from transposed blocks the forward recompute formed)
-//   bwd_dc     per (b, c, R, h): the causal sums over row blocks J <= R (fp32: C B^T read from
-//              the blocks the forward recompute formed once per group)
+//   bwd_dc     per (b, c, R, slice of heads): the causal sums over row blocks J <= R, dC summed
+//              over the slice (fp32: C B^T read from the blocks the forward recompute formed once
+//              per group)
 //   bwd_finalize per (b, c, h): dS, its reverse cumsum, d(dt), and the dA / d dt_bias partials
-//   bwd_reduce_*: per-head dB, dC summed over the heads of each group; parameter partials
+//   bwd_reduce_*: per-slice dB, dC summed over the slices of each group; parameter partials
 //                 summed in a fixed order (results are run-to-run deterministic)
 //   gate_bwd:  dy = dout silu(z) and dz = dout y~ silu'(z)
 // Token tiles are staged in LDS in the input dtype (bf16 -> fp32 is exact, so the fp32 MFMA
@@ -213,7 +215,7 @@ __device__ __forceinline__ float sum_qd(float v) {
 // (i, j) tiles of C B^T and dy x^T for every i of the block I, weights them in registers,
 // and feeds them straight into xi[j][:] and dB[j][:] as MFMA A operands.  The tiles of block
 // I + 1 are loaded into registers while block I is computed.
-template <typename T, int P, int N, bool PRECB>
+template <typename T, int P, int N, bool PRECB, int HS>
 __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, const T* __restrict__ Bm,
                                                        const T* __restrict__ Cm, const T* __restrict__ dy,
                                                        const float* __restrict__ dtp, const float* __restrict__ dAcs,
@@ -224,6 +226,7 @@ __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, 
                                                        float* __restrict__ dSa, float* __restrict__ Ub,
                                                        float* __restrict__ pD, int L, int H, int G, int nc, int Q,
                                                        uint32_t nblocks) {
+  constexpr int hs = HS;
   constexpr int PP = Pitch<T, P>::v, NP = Pitch<T, N>::v, NPF = N + 4, TPm = P / 16, TNm = N / 16;
   constexpr int C_BYTES = KT * NP * (int)sizeof(T), DY_BYTES = KT * PP * (int)sizeof(T);
   constexpr int G_BYTES = P * NPF * 4;                             // Gnext staged in fp32
@@ -237,40 +240,66 @@ __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, 
   T* s_dy = reinterpret_cast<T*>(s_un + C_BYTES);
   float* s_g = reinterpret_cast<float*>(s_un);
 
-  const int nrb = Q / KT;
+  // a workgroup takes `hs` consecutive heads of one group (one after the other) and sums their
+  // dB contributions in registers, in head order: dB leaves per slice of heads, not per head
+  const int nrb = Q / KT, nsl = H / hs;
   uint32_t id = xcd_swizzle(blockIdx.x, nblocks);
-  const int h = id % H;
-  id /= H;
+  const int hsl = id % nsl;
+  id /= nsl;
   const int R = id % nrb;
   id /= nrb;
   const int c = id % nc, b = id / nc;
-  const int g = h / (H / G);
+  const int h0 = hsl * hs;
+  const int g = h0 / (H / G);
   const int t0 = c * Q, len = min(Q, L - t0);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane & 15, qd = lane >> 4;
   if (R * KT >= len) {                 // a row block past the end of the sequence: no rows,
-    if (tid < P)                       // but its dD partial is still summed
-      pD[(((size_t)b * nc + c) * nrb + R) * (size_t)(H * P) + (size_t)h * P + tid] = 0.f;
+    if (tid < P)                       // but its dD partials are still summed
+      for (int hh = 0; hh < hs; ++hh)
+        pD[(((size_t)b * nc + c) * nrb + R) * (size_t)(H * P) + (size_t)(h0 + hh) * P + tid] = 0.f;
     return;
   }
   const int lenR = min(KT, len - R * KT);
   const size_t xs = (size_t)H * P, bs = (size_t)G * N;
-  const size_t cq = (((size_t)b * H + h) * nc + c) * Q;
   const int tk = min(tid, KT - 1);
   const T* Cg = Cm + ((size_t)b * L + t0) * bs + (size_t)g * N;
-  const T* dyg = dy + ((size_t)b * L + t0) * xs + (size_t)h * P;
 
-  // prologue: the own block's B and x, block I = R's C and dy, and the cumsums, all in flight
   RowTile<T, N> tb, tc;
   RowTile<T, P> tx, tdy;
-  tb.load(Bm + ((size_t)b * L + t0 + R * KT) * bs + (size_t)g * N, bs, lenR, tid);
+  if constexpr (HS > 1) {                          // the own block's B, once for the slice's heads
+    tb.load(Bm + ((size_t)b * L + t0 + R * KT) * bs + (size_t)g * N, bs, lenR, tid);
+    tb.store(s_b, tid);
+  }
+  f32x4 dbs[TNm];                                  // sum over the slice's heads of d_j dB_h[j][n]
+#pragma unroll
+  for (int m = 0; m < TNm; ++m) dbs[m] = zero4();
+  float djs[4];
+
+#pragma unroll 1
+  for (int hh = 0; hh < hs; ++hh) {
+  // lane-dependent values re-derived from an opaque copy of the thread index each head, so that
+  // nothing per lane is hoisted out of the head loop and kept live across it
+  int tid_l = threadIdx.x;
+  if constexpr (HS > 1) asm volatile("" : "+v"(tid_l));
+  const int tid = tid_l, lane = tid & 63, w = tid >> 6;
+  const int r = lane & 15, qd = lane >> 4;
+  const int tk = min(tid, KT - 1);
+  const int h = h0 + hh;
+  if (hh > 0) __syncthreads();                     // the previous head's tiles and partials consumed
+  const size_t cq = (((size_t)b * H + h) * nc + c) * Q;
+  const T* dyg = dy + ((size_t)b * L + t0) * xs + (size_t)h * P;
+
+  // prologue: the own block's B (once for the slice's heads) and x, block I = R's C and dy, and
+  // the cumsums, all in flight
+  if constexpr (HS == 1) tb.load(Bm + ((size_t)b * L + t0 + R * KT) * bs + (size_t)g * N, bs, lenR, tid);
   tx.load(x + ((size_t)b * L + t0 + R * KT) * xs + (size_t)h * P, xs, lenR, tid);
   tc.load(Cg + (size_t)(R * KT) * bs, bs, lenR, tid);
   tdy.load(dyg + (size_t)(R * KT) * xs, xs, lenR, tid);
   const float sR = dAcs[cq + R * KT + tk], dR = dtp[cq + R * KT + tk];
   float sI = sR;
   const float Slast = dAcs[cq + Q - 1];
-  tb.store(s_b, tid);
+  if constexpr (HS == 1) tb.store(s_b, tid);
   tx.store(s_x, tid);
   if (tid < KT) {
     s_SR[tid] = sR;
@@ -410,13 +439,18 @@ __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, 
       if (ok) dx[tok * xs + (size_t)h * P + p] = from_f32<T>(dw * dyv + dj[e] * xi[m][e]);
       dDp[m] += dyv * ld1(s_x + j * PP + p);
     }
-    if (ok) {
+    if constexpr (HS == 1) {                       // one head: dB straight out
+      if (ok) {
 #pragma unroll
-      for (int m = 0; m < TNm; ++m) dBh[(tok * H + h) * (size_t)N + 16 * m + r] = dj[e] * db[m][e];
-      if (r == 0) {
-        ddir[cq + R * KT + j] = dd[e];
-        Ub[cq + R * KT + j] = U[e];
+        for (int m = 0; m < TNm; ++m) dBh[(tok * H + h) * (size_t)N + 16 * m + r] = dj[e] * db[m][e];
       }
+    } else {
+#pragma unroll
+      for (int m = 0; m < TNm; ++m) dbs[m][e] += dj[e] * db[m][e];
+    }
+    if (ok && r == 0) {
+      ddir[cq + R * KT + j] = dd[e];
+      Ub[cq + R * KT + j] = U[e];
     }
   }
   // the column sums belong to column j = 16 w + r; its U was computed by the lane holding row j
@@ -439,6 +473,19 @@ __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, 
   if (tid < P)
     pD[(((size_t)b * nc + c) * nrb + R) * (size_t)(H * P) + (size_t)h * P + tid] =
         s_red[0][tid] + s_red[1][tid] + s_red[2][tid] + s_red[3][tid];
+  }  // heads of the slice
+  (void)djs;
+  if constexpr (HS == 1) return;
+  // dB of the slice: rows j = 16 w + 4 qd + e of R
+  const size_t row0s = (size_t)b * L + t0 + R * KT;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int j = 16 * w + 4 * qd + e;
+    if (j < lenR) {
+#pragma unroll
+      for (int m = 0; m < TNm; ++m) dBh[((row0s + j) * nsl + hsl) * (size_t)N + 16 * m + r] = dbs[m][e];
+    }
+  }
 }
 
 // ------------------------------------------------------------------ causal: dC
@@ -446,7 +493,7 @@ __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, 
 // transposed tiles (j, i) of B C^T and x dy^T for every j of block J, so that the weighted
 // tile feeds dC[i][:] directly as an MFMA A operand.  The tiles of block J + 1 are loaded
 // into registers while block J is computed.
-template <typename T, int P, int N, bool PRECB>
+template <typename T, int P, int N, bool PRECB, int HS>
 __global__ __launch_bounds__(256) void bwd_dc_kernel(const T* __restrict__ x, const T* __restrict__ Bm,
                                                      const T* __restrict__ Cm, const T* __restrict__ dy,
                                                      const float* __restrict__ dtp, const float* __restrict__ dAcs,
@@ -454,6 +501,7 @@ __global__ __launch_bounds__(256) void bwd_dc_kernel(const T* __restrict__ x, co
                                                      const float* __restrict__ cbp, float* __restrict__ dCh,
                                                      float* __restrict__ dSc, int L, int H, int G, int nc, int Q,
                                                      uint32_t nblocks) {
+  constexpr int hs = HS;
   constexpr int PP = Pitch<T, P>::v, NP = Pitch<T, N>::v, TNm = N / 16;
   constexpr int B_BYTES = KT * NP * (int)sizeof(T), X_BYTES = KT * PP * (int)sizeof(T);
   constexpr int H_BYTES = P * NP * (int)sizeof(T);                // Hprev staged in T
@@ -466,29 +514,49 @@ __global__ __launch_bounds__(256) void bwd_dc_kernel(const T* __restrict__ x, co
   T* s_x = reinterpret_cast<T*>(s_un + B_BYTES);
   T* s_h = reinterpret_cast<T*>(s_un);
 
-  const int nrb = Q / KT;
+  // a workgroup takes `hs` consecutive heads of one group (one after the other) and sums their
+  // dC contributions in registers, in head order: dC leaves per slice of heads, not per head
+  const int nrb = Q / KT, nsl = H / hs;
   uint32_t id = xcd_swizzle(blockIdx.x, nblocks);
-  const int h = id % H;
-  id /= H;
+  const int hsl = id % nsl;
+  id /= nsl;
   const int R = id % nrb;
   id /= nrb;
   const int c = id % nc, b = id / nc;
-  const int g = h / (H / G);
+  const int h0 = hsl * hs;
+  const int g = h0 / (H / G);
   const int t0 = c * Q, len = min(Q, L - t0);
   if (R * KT >= len) return;
   const int lenR = min(KT, len - R * KT);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane & 15, qd = lane >> 4;
   const size_t xs = (size_t)H * P, bs = (size_t)G * N;
-  const size_t cq = (((size_t)b * H + h) * nc + c) * Q;
   const int tk = min(tid, KT - 1);
   const T* Bg = Bm + ((size_t)b * L + t0) * bs + (size_t)g * N;
-  const T* xg = x + ((size_t)b * L + t0) * xs + (size_t)h * P;
 
-  // prologue: the own block's C and dy, block J = 0's B and x, and the cumsums, all in flight
   RowTile<T, N> tc, tb;
   RowTile<T, P> tdy, tx;
-  tc.load(Cm + ((size_t)b * L + t0 + R * KT) * bs + (size_t)g * N, bs, lenR, tid);
+  f32x4 dcs[TNm];                                  // sum over the slice's heads of dC_h[i][n]
+#pragma unroll
+  for (int m = 0; m < TNm; ++m) dcs[m] = zero4();
+
+#pragma unroll 1
+  for (int hh = 0; hh < hs; ++hh) {
+  // lane-dependent values re-derived from an opaque copy of the thread index each head, so that
+  // nothing per lane is hoisted out of the head loop and kept live across it
+  int tid_l = threadIdx.x;
+  if constexpr (HS > 1) asm volatile("" : "+v"(tid_l));
+  const int tid = tid_l, lane = tid & 63, w = tid >> 6;
+  const int r = lane & 15, qd = lane >> 4;
+  const int tk = min(tid, KT - 1);
+  const int h = h0 + hh;
+  if (hh > 0) __syncthreads();                     // the previous head's tiles and partials consumed
+  const size_t cq = (((size_t)b * H + h) * nc + c) * Q;
+  const T* xg = x + ((size_t)b * L + t0) * xs + (size_t)h * P;
+
+  // prologue: the own block's C (once for the slice's heads) and dy, block J = 0's B and x, and
+  // the cumsums, all in flight
+  if (HS == 1 || hh == 0) tc.load(Cm + ((size_t)b * L + t0 + R * KT) * bs + (size_t)g * N, bs, lenR, tid);
   tdy.load(dy + ((size_t)b * L + t0 + R * KT) * xs + (size_t)h * P, xs, lenR, tid);
   const int len0 = min(KT, len);
   tb.load(Bg, bs, len0, tid);
@@ -505,7 +573,7 @@ __global__ __launch_bounds__(256) void bwd_dc_kernel(const T* __restrict__ x, co
 #pragma unroll
     for (int tj = 0; tj < 4; ++tj) cbr[tj] = *reinterpret_cast<const f32x4*>(cb_lane + 256 * tj);
   }
-  tc.store(s_c, tid);
+  if (HS == 1 || hh == 0) tc.store(s_c, tid);
   tdy.store(s_dy, tid);
   if (tid < KT) s_SR[tid] = sR;
 
@@ -589,14 +657,30 @@ __global__ __launch_bounds__(256) void bwd_dc_kernel(const T* __restrict__ x, co
     const int i = 16 * w + 4 * qd + e;
     const float rv = ei[e] * sum_r(rr[e]);
     if (r == 0) s_rr[i] = rv;
-    if (i < lenR) {
-      const size_t tok = row0 + i;
+    if constexpr (HS == 1) {                       // one head: dC straight out
+      if (i < lenR) {
 #pragma unroll
-      for (int m = 0; m < TNm; ++m) dCh[(tok * H + h) * (size_t)N + 16 * m + r] = dc[m][e];
+        for (int m = 0; m < TNm; ++m) dCh[((row0 + i) * H + h) * (size_t)N + 16 * m + r] = dc[m][e];
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < TNm; ++m) dcs[m][e] += dc[m][e];
     }
   }
   __syncthreads();
   if (qd == 0 && il < lenR) dSc[cq + R * KT + il] = rsum + s_rr[il];
+  }  // heads of the slice
+  if constexpr (HS == 1) return;
+  // dC of the slice: rows i = 16 w + 4 qd + e of R
+  const size_t row0s = (size_t)b * L + t0 + R * KT;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = 16 * w + 4 * qd + e;
+    if (i < lenR) {
+#pragma unroll
+      for (int m = 0; m < TNm; ++m) dCh[((row0s + i) * nsl + hsl) * (size_t)N + 16 * m + r] = dcs[m][e];
+    }
+  }
 }
 
 // ------------------------------------------------------------------ per-chunk finalize
@@ -691,7 +775,8 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(const T* __restrict__
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restrict__ dBh,
                                                             const float* __restrict__ dCh, T* __restrict__ dB,
-                                                            T* __restrict__ dC, int H, int G, int N, size_t total4) {
+                                                            T* __restrict__ dC, int H, int G, int N, size_t total4,
+                                                            int nsl_b, int nsl_c) {
   const size_t e4 = (size_t)blockIdx.x * 256 + threadIdx.x;   // index into (B, L, G, N / 4)
   if (e4 >= total4) return;
   const int N4 = N / 4;
@@ -699,34 +784,32 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restr
   const size_t bg = e4 / N4;
   const int g = (int)(bg % G);
   const size_t bl = bg / G;
-  const int hpg = H / G;
-  const float* pb = dBh + (bl * H + (size_t)g * hpg) * N + n;
-  const float* pc = dCh + (bl * H + (size_t)g * hpg) * N + n;
-  float4 sb = make_float4(0.f, 0.f, 0.f, 0.f), sc = sb;
+  (void)H;
+  // dB and dC: per slice of heads, nsl_b / nsl_c slices per batch-token row, hb / hc per group
+  const int hb = nsl_b / G, hc = nsl_c / G;
+  const float* pb = dBh + (bl * nsl_b + (size_t)g * hb) * N + n;
+  const float* pc = dCh + (bl * nsl_c + (size_t)g * hc) * N + n;
   auto add = [](float4& acc, const float4& v) {
     acc.x += v.x;
     acc.y += v.y;
     acc.z += v.z;
     acc.w += v.w;
   };
-  int k = 0;
-  for (; k + 4 <= hpg; k += 4) {
-    float4 vb[4], vc[4];
+  // the slices of one tensor in order, four loads in flight
+  auto sum = [&](const float* p, int k_n) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    int k = 0;
+    for (; k + 4 <= k_n; k += 4) {
+      float4 v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      vb[u] = *reinterpret_cast<const float4*>(pb + (size_t)(k + u) * N);
-      vc[u] = *reinterpret_cast<const float4*>(pc + (size_t)(k + u) * N);
-    }
+      for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4*>(p + (size_t)(k + u) * N);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      add(sb, vb[u]);
-      add(sc, vc[u]);
+      for (int u = 0; u < 4; ++u) add(acc, v[u]);
     }
-  }
-  for (; k < hpg; ++k) {
-    add(sb, *reinterpret_cast<const float4*>(pb + (size_t)k * N));
-    add(sc, *reinterpret_cast<const float4*>(pc + (size_t)k * N));
-  }
+    for (; k < k_n; ++k) add(acc, *reinterpret_cast<const float4*>(p + (size_t)k * N));
+    return acc;
+  };
+  const float4 sb = sum(pb, hb), sc = sum(pc, hc);
   const size_t e = e4 * 4;
   dB[e + 0] = from_f32<T>(sb.x);
   dB[e + 1] = from_f32<T>(sb.y);
@@ -803,13 +886,13 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(const T* __restrict__ dou
 }
 
 // ------------------------------------------------------------------ launchers
-template <typename T, int P, int N>
-static hipError_t launch_dxdb_impl(const BwdArgs& a, hipStream_t s) {
+template <typename T, int P, int N, int HS>
+static hipError_t launch_dxdb_hs(const BwdArgs& a, hipStream_t s) {
   const FwdArgs& f = a.f;
-  const uint32_t nblocks = (uint32_t)f.B * f.nc * (f.Q / KT) * f.H;
-  auto kern = bwd_dxdb_kernel<T, P, N, false>;
+  const uint32_t nblocks = (uint32_t)f.B * f.nc * (f.Q / KT) * (f.H / HS);
+  auto kern = bwd_dxdb_kernel<T, P, N, false, HS>;
   if constexpr (sizeof(T) == 4)
-    if (f.cbT) kern = bwd_dxdb_kernel<T, P, N, true>;  // fp32: C B^T read from the transposed blocks
+    if (f.cbT) kern = bwd_dxdb_kernel<T, P, N, true, HS>;  // fp32: C B^T read from the transposed blocks
   hipExtLaunchKernelGGL(kern, dim3(nblocks), dim3(256), 0, s, f.ev0, f.ev1, 0,
       static_cast<const T*>(f.x), static_cast<const T*>(f.Bm), static_cast<const T*>(f.Cm),
       static_cast<const T*>(a.dy), f.dtp, f.dAcs, a.gstates, f.cbT, f.D, static_cast<T*>(a.dx), a.dBh, a.ddir,
@@ -817,19 +900,34 @@ static hipError_t launch_dxdb_impl(const BwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename T, int P, int N>
-static hipError_t launch_dc_impl(const BwdArgs& a, hipStream_t s) {
+template <typename T, int P, int N, int HS>
+static hipError_t launch_dc_hs(const BwdArgs& a, hipStream_t s) {
   const FwdArgs& f = a.f;
-  const uint32_t nblocks = (uint32_t)f.B * f.nc * (f.Q / KT) * f.H;
-  auto kern = bwd_dc_kernel<T, P, N, false>;
+  const uint32_t nblocks = (uint32_t)f.B * f.nc * (f.Q / KT) * (f.H / HS);
+  auto kern = bwd_dc_kernel<T, P, N, false, HS>;
   if constexpr (sizeof(T) == 4)
-    if (f.cb) kern = bwd_dc_kernel<T, P, N, true>;     // fp32: C B^T read from the shared blocks
+    if (f.cb) kern = bwd_dc_kernel<T, P, N, true, HS>;     // fp32: C B^T read from the shared blocks
   hipExtLaunchKernelGGL(kern, dim3(nblocks),
       dim3(256), 0, s, f.ev0, f.ev1, 0,
       static_cast<const T*>(f.x), static_cast<const T*>(f.Bm), static_cast<const T*>(f.Cm),
       static_cast<const T*>(a.dy), f.dtp, f.dAcs, f.states, f.cb, a.dCh, a.dSc, f.L, f.H, f.G, f.nc, f.Q,
       nblocks);
   return hipGetLastError();
+}
+
+// slices of 4 heads exist for bf16 inputs (fp32 keeps one head per workgroup)
+template <typename T, int P, int N>
+static hipError_t launch_dxdb_impl(const BwdArgs& a, hipStream_t s) {
+  if constexpr (sizeof(T) == 2)
+    if (a.hs_dxdb == 4) return launch_dxdb_hs<T, P, N, 4>(a, s);
+  return a.hs_dxdb == 1 ? launch_dxdb_hs<T, P, N, 1>(a, s) : hipErrorInvalidValue;
+}
+
+template <typename T, int P, int N>
+static hipError_t launch_dc_impl(const BwdArgs& a, hipStream_t s) {
+  if constexpr (sizeof(T) == 2)
+    if (a.hs_dc == 4) return launch_dc_hs<T, P, N, 4>(a, s);
+  return a.hs_dc == 1 ? launch_dc_hs<T, P, N, 1>(a, s) : hipErrorInvalidValue;
 }
 
 template <typename T, int P, int N>
@@ -852,7 +950,7 @@ static hipError_t launch_reduce_impl(const BwdArgs& a, hipStream_t s) {
     const size_t total4 = total / 4;                // N is a multiple of 16
     hipExtLaunchKernelGGL(bwd_reduce_bc_kernel<T>, dim3((unsigned)((total4 + 255) / 256)), dim3(256), 0, s, start,
                           nullptr, 0, a.dBh, a.dCh, static_cast<T*>(a.dB), static_cast<T*>(a.dC), f.H, f.G, f.N,
-                          total4);
+                          total4, f.H / a.hs_dxdb, f.H / a.hs_dc);
     start = nullptr;
   }
   hipExtLaunchKernelGGL(bwd_reduce_params_kernel, dim3(f.H), dim3(256), 0, s, start, f.ev1, 0, a.pA, a.pbias, a.pD,

@@ -68,8 +68,11 @@ struct BwdArgs {
   FwdArgs f;               // forward sizes, inputs and recomputed intermediates
   const void* dy;          // (B, L, H, P) dtype: gradient of the pre-gate output
   float* gstates;          // (B, nc, H, P, N): gradient of the state leaving each chunk
-  float* dBh;              // (B, L, H, N) per-head dB
-  float* dCh;              // (B, L, H, N) per-head dC
+  int hs_dxdb = 1;         // heads per slice: bwd_dxdb sums dB over a slice of hs_dxdb consecutive
+                           // heads of one group in registers (1, or 4 for bf16; divides H / G)
+  int hs_dc = 1;           // the same for bwd_dc and dC
+  float* dBh;              // (B, L, H / hs_dxdb, N) per-slice dB
+  float* dCh;              // (B, L, H / hs_dc, N) per-slice dC
   float* ddir;             // (B, H, nc, Q) direct d(dt') term
   float* dSa;              // (B, H, nc, Q) anti-causal part of d(dAcs)
   float* dSc;              // (B, H, nc, Q) causal part of d(dAcs)

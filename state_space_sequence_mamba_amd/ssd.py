@@ -32,7 +32,7 @@ class ssd_launch_opts_t(ctypes.Structure):
     _fields_ = [("scan_variant", ctypes.c_int32), ("heads_per_block", ctypes.c_int32),
                 ("min_blocks", ctypes.c_int32), ("rows_group", ctypes.c_int32), ("state_path", ctypes.c_int32),
                 ("state_slice", ctypes.c_int32), ("conv_tokens", ctypes.c_int32), ("state_heads", ctypes.c_int32),
-                ("state_chunks", ctypes.c_int32)]
+                ("state_chunks", ctypes.c_int32), ("bwd_heads", ctypes.c_int32)]
 
 
 def launch_opts(**fields):
