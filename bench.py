@@ -223,9 +223,10 @@ BWD_STAGES = ["chunk_state", "state_passing", "gate_fwd", "gate_bwd", "chunk_sta
               "state_passing_rev", "bwd_dxdb", "bwd_dc", "bwd_finalize", "bwd_reduce"]
 
 
-def backward_cost(w):
+def backward_cost(w, hs=1):
     """Algorithmic bytes and flops of each backward kernel per launch.  C B^T and dy x^T are
-    counted once (in bwd_dxdb; bwd_dc recomputes them, which is not algorithmic work)."""
+    counted once (in bwd_dxdb; bwd_dc recomputes them, which is not algorithmic work).  hs: heads
+    per bwd_dxdb workgroup (its dB leaves per slice of hs heads)."""
     e = 4 if w.dtype == "f32" else 2
     B, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
     nc = (L + Q - 1) // Q
@@ -246,7 +247,7 @@ def backward_cost(w):
         "state_passing_rev": dict(bytes=2 * st + 2 * fin + B * H * nc * 4, flops=2 * B * nc * H * P * N),
         # C B^T, dy x^T and the weighted products contract tiles of the input dtype (MFMA in
         # that dtype); the carried terms through the fp32 state gradients run on fp32 MFMA
-        "bwd_dxdb": dict(bytes=2 * x + 2 * bc + 2 * cum + st + x + perh + 3 * B * H * L * 4,
+        "bwd_dxdb": dict(bytes=2 * x + 2 * bc + 2 * cum + st + x + perh // hs + 3 * B * H * L * 4,
                          flops=2 * N * tri * B * G + 2 * P * tri * B * H * 2 + 2 * N * tri * B * H
                          + 4 * B * H * L * P * N,
                          flops_in=2 * N * tri * B * G + 2 * P * tri * B * H * 2 + 2 * N * tri * B * H),
@@ -254,7 +255,7 @@ def backward_cost(w):
                        flops=2 * N * tri * B * H + 2 * B * H * L * P * N,
                        flops_in=2 * N * tri * B * H),
         "bwd_finalize": dict(bytes=2 * st + 5 * cum + B * L * H * e * 2, flops=2 * B * nc * H * P * N),
-        "bwd_reduce": dict(bytes=2 * perh + 2 * bc, flops=2 * B * L * H * N),
+        "bwd_reduce": dict(bytes=perh // hs + perh + 2 * bc, flops=2 * B * L * H * N),
     }
     for k, v in cost.items():
         # chunk_state contracts on MFMA in the input dtype; the backward kernels' products run
@@ -328,7 +329,9 @@ def run_bwd(w, args, dev, opts=None):
     torch.cuda.synchronize()
     per_kernel_ms = {k: sum(hev.elapsed_ms(ev[2 * i], ev[2 * i + 1]) for ev in events) / K
                      for i, k in enumerate(BWD_STAGES)}
-    cost = backward_cost(w)
+    dims_b = ssd.make_dims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, inp["x"].dtype)
+    hs = ssd.bwd_heads(dims_b, w.chunk, opts)
+    cost = backward_cost(w, hs)
     kernels = {}
     for k in BWD_STAGES:
         if k.startswith("gate"):
@@ -342,6 +345,11 @@ def run_bwd(w, args, dev, opts=None):
         kernels[k] = {"us": round(per_kernel_ms[k] * 1e3, 3), "bound": c["bound"], "achieved": round(ach, 2),
                       "peak": peak, "unit": unit, "frac": round(ach / peak, 4), "alg_bytes": c["bytes"],
                       "alg_flops": c["flops"]}
+        if c["bound"] == "mfma":
+            # also against the dense MFMA peak of the input dtype alone (the blend above counts the
+            # fp32 share of the products at the fp32 peak)
+            p_in = MFMA_PEAK_TFLOPS[w.dtype]
+            kernels[k]["frac_of_input_dtype_peak"] = round(ach / p_in, 4)
     dom = max(kernels, key=lambda k: kernels[k]["us"])
     kd = kernels[dom]
     res = {
@@ -351,7 +359,8 @@ def run_bwd(w, args, dev, opts=None):
         "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) x/B/C/dt/dout/dfinal, log-uniform dt bias, A=-U[1,16])",
         "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads,
-                   "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups, "chunk_size": w.chunk},
+                   "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups, "chunk_size": w.chunk,
+                   "bwd_heads_per_workgroup": hs},
         "roofline": {"kernel": dom, "bound": kd["bound"], "achieved": kd["achieved"], "peak": kd["peak"],
                      "unit": kd["unit"], "frac": kd["frac"], "traffic": load_traffic(workload_slug(w.name), dom)},
         "kernels": kernels,

@@ -111,6 +111,11 @@ int ssd_fwd_state_path(const ssd_dims_t* dims, int chunk_size, const ssd_launch_
  * or for invalid or empty arguments.  Pure host logic. */
 int ssd_fwd_state_segment_chunks(const ssd_dims_t* dims, int chunk_size, const ssd_launch_opts_t* opts);
 
+/* Heads per bwd_dxdb workgroup that ssd_bwd_ex takes for these sizes and options (NULL = the
+ * built-in choice of ssd_bwd): 1, or 4 when dB is summed over slices of four heads on chip;
+ * 0 for invalid arguments.  Pure host logic. */
+int ssd_bwd_heads(const ssd_dims_t* dims, int chunk_size, const ssd_launch_opts_t* opts);
+
 #ifdef __cplusplus
 }
 #endif

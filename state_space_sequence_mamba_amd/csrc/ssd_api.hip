@@ -817,6 +817,11 @@ ssd_status_t ssd_step_ex(const ssd_dims_t* dims, float* state, const void* x, co
   return step_impl(dims, state, x, dt, dt_bias, A, B, C, D, z, y, stream, events);
 }
 
+int ssd_bwd_heads(const ssd_dims_t* dims, int chunk_size, const ssd_launch_opts_t* opts) {
+  if (check_dims(dims, true) != SSD_OK || !chunk_ok(chunk_size)) return 0;
+  return pick_bwd_heads(dims, chunk_size, opts_or_builtin(opts));
+}
+
 size_t ssd_bwd_workspace_size(const ssd_dims_t* dims, int chunk_size, int with_gate) {
   if (check_dims(dims, true) != SSD_OK || !chunk_ok(chunk_size)) return 0;
   return bwd_layout(dims, chunk_size, with_gate != 0).total;

@@ -113,6 +113,8 @@ def load_library():
     lib.ssd_fwd_state_segment_chunks.argtypes = [dims_p, i32, opts_p]
     lib.ssd_fwd_state_segment_chunks.restype = i32
     lib.ssd_fwd_state_path.restype = i32
+    lib.ssd_bwd_heads.argtypes = lib.ssd_fwd_state_path.argtypes
+    lib.ssd_bwd_heads.restype = i32
     _lib = lib
     return lib
 
@@ -409,6 +411,11 @@ def conv1d_silu_step(conv_state, xbc, weight, bias, nheads, headdim, dstate, ngr
     if st != SSD_OK:
         raise SsdError(st, "ssd_conv1d_silu_step")
     return x, B, C
+
+
+def bwd_heads(dims, chunk_size, opts=None):
+    """Heads per bwd_dxdb workgroup ssd_bwd takes (1, or 4: dB summed over four heads on chip)."""
+    return int(load_library().ssd_bwd_heads(ctypes.byref(dims), int(chunk_size), _opts_ref(opts)))
 
 
 def fwd_state_path(dims, chunk_size, opts=None):
