@@ -573,6 +573,7 @@ def fwd_summary(out):
 def run_fwd(w, args, dev, opts, with_cpu):
     """K ssd_fwd calls over one batch (HIP graph replay), per-kernel durations from an eager pass
     of the same calls with dispatch-recorded events."""
+    with_cpu = with_cpu and not getattr(args, "gate", False)   # (the oracle sample has no gate)
     inp = I.make_workload_inputs(w)
     d = {k: v.to(dev) for k, v in inp.items()}
     y = torch.empty_like(d["x"])
@@ -586,6 +587,9 @@ def run_fwd(w, args, dev, opts, with_cpu):
     state = torch.empty(w.batch, w.nheads, w.headdim, w.dstate, dtype=torch.float32, device=dev)
     dims = ssd.make_dims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, d["x"].dtype)
     ws = torch.empty(max(1, ssd.ssd_fwd_workspace_size(dims, w.chunk)), dtype=torch.uint8, device=dev)
+    # --gate: the output gate y * silu(z) fused into the scan (z of x's shape, one copy)
+    z = I.make_gate(tuple(d["x"].shape), w.dtype, seed=w.seed + 100, device=dev) if getattr(args, "gate", False) \
+        else None
 
     K, W = args.steps, args.warmup
     use_graph = not args.no_graph
@@ -597,7 +601,7 @@ def run_fwd(w, args, dev, opts, with_cpu):
         # launches go to the current stream (the capture stream while a graph is captured)
         c = copies[i % R]
         ssd.ssd_fwd(c["x"], c["dt"], c["dt_bias"], c["A"], c["B"], c["C"], c["D"], chunk_size=w.chunk,
-                    y=c["y"], final_state=state, workspace=ws, stage_events=evs, opts=opts)
+                    y=c["y"], final_state=state, workspace=ws, stage_events=evs, opts=opts, z=z)
 
     for i in range(W):
         step(i)
@@ -685,6 +689,8 @@ def run_fwd(w, args, dev, opts, with_cpu):
     hev.close()
     if with_cpu:
         out["cpu_baseline"], out["parity_sample"] = cpu_baseline(w, inp, copies[(W + K - 1) % R]["y"], args.cpu_budget)
+    if z is not None:
+        out["config"]["gate"] = True
     return out
 
 
@@ -727,6 +733,8 @@ def main():
                     help="segmented chunk states: heads per workgroup (0 = built-in)")
     ap.add_argument("--state-chunks", type=int, default=0,
                     help="segmented chunk states: chunks per segment (0 = built-in)")
+    ap.add_argument("--gate", action="store_true",
+                    help="forward workloads: with the output gate y * silu(z) (z drawn like x)")
     ap.add_argument("--bwd-heads", type=int, default=0,
                     help="ssd_bwd: heads per bwd_dxdb / bwd_dc workgroup, dB / dC summed on chip (0 = built-in)")
     ap.add_argument("--conv-tokens", type=int, default=0,
