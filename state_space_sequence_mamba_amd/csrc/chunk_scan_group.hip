@@ -111,7 +111,10 @@ struct HeadRegs {
   uint4 x[XPT][2];
   uint4 pv[PPT];
   uint4 hv[PPT];           // segmented states: the state entering the segment (else unused)
-  float dt, da, dd, sdec;  // sdec: exp of the decay since the segment start; < 0: no segments
+  float dt, da, dd;
+  float ecdv;              // segmented states: the decay exponent since the segment start
+  bool seg;                // segmented states
+  bool pz;                 // segmented states, c opens its segment: no carried state of its own
   uint32_t okm;
 
   // Per-lane element offsets from the head's (wavefront-uniform) base pointers, 32-bit: the
@@ -148,17 +151,25 @@ struct HeadRegs {
       for (int u = 0; u < PPT; ++u) pv[u] = ld16(ph, po[u]);
       if (hh) {
 #pragma unroll
-        for (int u = 0; u < PPT; ++u) {
-          hv[u] = ld16(hh, po[u]);
-          if (first) pv[u] = make_uint4(0, 0, 0, 0);   // (that slot holds no state of this segment)
-        }
+        for (int u = 0; u < PPT; ++u) hv[u] = ld16(hh, po[u]);
       }
+      // (a segment's first chunk drops the loaded state at the store: overwriting the registers
+      // here would wait for their loads)
+      pz = hh && first;
     } else {
       // only the wavefronts that store them load the scalars (wavefront-uniform branches)
       const int wf = __builtin_amdgcn_readfirstlane(tid) / 64;
       uint32_t io = (tid & (kGQ - 1)) * 4, Do = (tid & (P - 1)) * 4;
       asm volatile("" : "+v"(io), "+v"(Do));
-      sdec = hh ? __expf(*ecd) : -1.f;
+      // (the exponent is loaded by a vector load, opaque offset 0, and taken at the store: a
+      // scalar load would be waited for, and the value moved to a vector register, right here
+      // between the MFMAs)
+      // (loaded on every path, without segments from the cumsum, so that no select or branch
+      // on the loaded value pulls its use forward)
+      seg = hh != nullptr;
+      uint32_t zo = 0;
+      asm volatile("" : "+v"(zo));
+      ecdv = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(hh ? ecd : dah) + zo);
       if (wf < kGQ / 64) {
         dt = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(dth) + io);
         da = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(dah) + io);
@@ -185,15 +196,17 @@ struct HeadRegs {
       *reinterpret_cast<uint4*>(&s_x[o]) = a;
       *reinterpret_cast<uint4*>(&s_x[o + 16]) = b;
     }
+    const float sdec = __expf(ecdv);   // exp of the decay since the segment start (with segments)
 #pragma unroll
     for (int u = 0; u < PPT; ++u) {
       const int v = tid + kGThreads * u;
       const int p = (v * 8) / N, n = (v * 8) % N;
       uint4 o = pv[u];
-      if (sdec >= 0.f) {
+      if (pz) o = make_uint4(0, 0, 0, 0);            // (that slot holds no state of this segment)
+      if (seg) {
         // segmented states: the entering state is the segment's own carry plus the decayed
         // state that entered the segment, rounded to bf16 as the scan reads it
-        const uint32_t lv[4] = {pv[u].x, pv[u].y, pv[u].z, pv[u].w}, iv[4] = {hv[u].x, hv[u].y, hv[u].z, hv[u].w};
+        const uint32_t lv[4] = {o.x, o.y, o.z, o.w}, iv[4] = {hv[u].x, hv[u].y, hv[u].z, hv[u].w};
         uint32_t ov[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
