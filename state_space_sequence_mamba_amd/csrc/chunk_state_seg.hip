@@ -29,6 +29,7 @@
 // registers while the current ones are in use, and the next head's x in parts between the
 // MFMAs.  At the segment's end E_s goes out in fp32 with the segment's total exponent; D_c goes
 // out for every chunk.
+#include <type_traits>
 #include "ssd_common.h"
 #include "ssd_launch.h"
 
@@ -55,6 +56,16 @@ __device__ __forceinline__ bf16x8 tr16x2(const __bf16* t0, const __bf16* t1) {
   const uint2 a = tr16(t0), b = tr16(t1);
   return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
 }
+
+// A workgroup barrier for LDS data only: this wavefront's LDS accesses complete, then s_barrier,
+// with no memory fence.  (__syncthreads' fence would also wait for the direct-to-LDS loads of the
+// next chunk's B in flight and, loads completing in order, for the x loads issued before them.)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// every vector memory operation of this wavefront complete but the last four: s_waitcnt vmcnt(4)
+// (the four x loads of the previous head stay in flight; the direct-to-LDS loads issued before
+// them have landed, and the compiler, which takes an explicit wait into account, adds none of
+// its own for them before the next LDS stores)
+__device__ __forceinline__ void vm_keep4() { __builtin_amdgcn_s_waitcnt(0x0F74); }
 
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   typedef float f2 __attribute__((ext_vector_type(2)));
@@ -120,7 +131,7 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
     uint32_t nblocks) {
   constexpr int P = 64, N = 128, Q = kSQ, KS = Q / 32;
   constexpr int EPL = Q / 64;                      // cumsum positions per lane
-  constexpr int XV = P / 8, BV = N / 8;            // 16-byte vectors per token row
+  constexpr int XV = P / 8;                        // 16-byte vectors per x token row
 
   __shared__ __attribute__((aligned(16))) __bf16 s_b[(Q / 16) * (N / 16) * kST];   // B of the chunk
   __shared__ __attribute__((aligned(16))) __bf16 s_x[(Q / 16) * (P / 16) * kST];   // x w of one head
@@ -147,13 +158,16 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
 
   auto x_base = [&](int c, int hh) { return x + ((size_t)b * L + (size_t)c * Q) * x_tok + (size_t)(h0 + hh) * P; };
   auto b_base = [&](int c) { return Bm + ((size_t)b * L + (size_t)c * Q) * b_tok + (size_t)g * N; };
-  // dt of the positions this lane scans (wavefront hh < HS: head h0 + hh), clamped in bounds
-  auto load_dt = [&](int c, float (&dv)[EPL]) {
+  // dt of the positions this lane scans (wavefront hh < HS: head h0 + hh), clamped in bounds, as
+  // raw bf16 bits: widened only where the cumsum uses them (a conversion here would wait for
+  // each load on the spot)
+  auto load_dt = [&](int c, uint32_t (&dv)[EPL]) {
     const int hh = w < HS ? w : 0;
+    const unsigned short* d16 = reinterpret_cast<const unsigned short*>(dt);
 #pragma unroll
     for (int k = 0; k < EPL; ++k) {
       const int t = min(c * Q + lane * EPL + k, L - 1);
-      dv[k] = static_cast<float>(dt[((size_t)b * L + t) * H + h0 + hh]);
+      dv[k] = d16[((size_t)b * L + t) * H + h0 + hh];
     }
   };
 
@@ -166,18 +180,62 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
     for (int j = 0; j < 4; ++j) st[hh][j] = zero4();
   float run = 0.f;                                 // wavefront hh: exponent sum since the segment start
 
-  RowTile<BV> breg;
-  RowTile<XV> xreg;
-  breg.okm = xreg.okm = 0;
-  float dtv[EPL];
-  breg.load(b_base(c0), b_tok, min(Q, L - c0 * Q), tid);
-  xreg.load(x_base(c0, 0), x_tok, min(Q, L - c0 * Q), tid);
+  // B of a chunk straight into s_b (16-byte direct-to-LDS loads): block q (q = w, w + 8, ...) of
+  // 64 consecutive 16-byte LDS slots per instruction; slot S is slot S % 34 of tile S / 34 (tile
+  // (jt, ct) = 8 jt + ct: token row 16 jt + s / 2, dstate 16 ct + 8 (s % 2) for s < 32; slots 32
+  // and 33 are the tile's padding and take a copy of its first vector).  Tokens past the end
+  // read row 0: their weights and x are zero, so they add nothing.
+  constexpr int BBLK = (Q / 16) * (N / 16) * kST / (64 * 8);       // 1 KiB blocks of s_b
+  static_assert(kST * 2 == 34 * 16 && BBLK * 64 * 8 == (Q / 16) * (N / 16) * kST, "B tiles: 34 slots each");
+  constexpr int BJ = (BBLK + 7) / 8;                               // blocks per wavefront (at most)
+  auto b_block = [&](int j, int c, int t) {
+    int q = 8 * j + w;
+    asm volatile("" : "+s"(q));
+    if (q < BBLK) {
+      const int S = 64 * q + (t & 63);
+      const int T = S / 34, si = S % 34;
+      const int row = 16 * (T >> 3) + (si < 32 ? si >> 1 : 0);
+      const int n = 16 * (T & 7) + (si < 32 ? (si & 1) * 8 : 0);
+      const int lenc = min(Q, L - c * Q);
+      uint32_t o = ((uint32_t)(row < lenc ? row : 0) * b_tok + n) * 2;
+      asm volatile("" : "+v"(o));
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(reinterpret_cast<const char*>(b_base(c)) + o),
+          (__attribute__((address_space(3))) void*)(s_b + q * 64 * 8), 16, 0, 0);
+    }
+  };
+
+  // x two heads ahead: the heads of the segment in order (chunk-major) alternate between two
+  // register tiles; head n's tile is stored into LDS at its start and then refilled with head
+  // n + 2's x, in parts between head n's MFMAs
+  RowTile<XV> xr[2];
+  xr[0].okm = xr[1].okm = 0;
+  // global head n + k after head hh of chunk c, clamped to the segment (a clamped load is unused)
+  auto head_after = [&](int c, int hh, int k, int& cn, int& hn) {
+    cn = c + (hh + k) / HS;
+    hn = (hh + k) % HS;
+    if (cn >= c1) {
+      cn = c;
+      hn = hh;
+    }
+  };
+  uint32_t dtv[EPL];
+#pragma unroll
+  for (int j = 0; j < BJ; ++j) b_block(j, c0, tid);
+  {
+    int cn, hn;
+    xr[0].load(x_base(c0, 0), x_tok, min(Q, L - c0 * Q), tid);
+    head_after(c0, 0, 1, cn, hn);
+    xr[1].load(x_base(cn, hn), x_tok, min(Q, L - cn * Q), tid);
+  }
   load_dt(c0, dtv);
 
-  for (int c = c0; c < c1; ++c) {
+  // one chunk; CP: the chunk's parity in the segment (which register tile each head uses)
+  auto chunk = [&](int c, auto cp_tag) {
+    constexpr int CP = decltype(cp_tag)::value;
     const int len = min(Q, L - c * Q);
-    __syncthreads();                               // the previous chunk's weights and B consumed
-    breg.store(s_b, nullptr, tid);
+    vm_keep4();                                    // the previous chunk's last B blocks landed
+    lds_barrier();                                 // the previous chunk's weights and exponents consumed
     if (w < HS) {
       // dt' and the inclusive in-chunk cumsum of dt' A of head h0 + w; weights to the chunk end
       const int h = h0 + w;
@@ -185,7 +243,7 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
       float d[EPL], cs[EPL], run_l = 0.f;
 #pragma unroll
       for (int k = 0; k < EPL; ++k) {
-        float v = softplus(dtv[k] + bias);
+        float v = softplus(__builtin_bit_cast(float, dtv[k] << 16) + bias);
         if (clamp) v = fminf(fmaxf(v, lo), hi);
         d[k] = lane * EPL + k < len ? v : 0.f;
         run_l += d[k] * av;
@@ -216,7 +274,7 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
       run += last;
     }
     if (c + 1 < c1) load_dt(c + 1, dtv);
-    __syncthreads();                               // B, weights and exponents of chunk c in LDS
+    __syncthreads();                               // B (loaded during the previous chunk), weights and exponents in LDS
     // this wavefront's B^T rows n = 16 (2 nb + ni) + r for the whole chunk (A operands)
     bf16x8 bfr[2][KS];
     {
@@ -232,9 +290,13 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
 
 #pragma unroll
     for (int hh = 0; hh < HS; ++hh) {
-      if (hh > 0) __syncthreads();                 // the previous head's x consumed
-      xreg.store(s_x, s_w[hh], tid);
-      __syncthreads();
+      RowTile<XV>& xb = xr[(CP * HS + hh) & 1];
+      if (hh > 0) {
+        vm_keep4();                                // the previous head's B blocks landed
+        lds_barrier();                             // the previous head's x consumed
+      }
+      xb.store(s_x, s_w[hh], tid);
+      lds_barrier();                               // (at head 0 also: every wavefront's B^T rows read)
       const int h = h0 + hh;
       // lane-dependent offsets recomputed per head (nothing lane-dependent is hoisted and kept)
       int lt = tid;
@@ -255,18 +317,16 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) st[hh][j][e] *= dec;
-      // the next x: the next head of this chunk, or the first head of the next chunk, one part
-      // per pair of MFMA steps
-      const bool nxt_here = hh + 1 < HS, nxt_chunk = !nxt_here && c + 1 < c1;
-      const __bf16* xn = nxt_here ? x_base(c, hh + 1) : x_base(c + 1 < c1 ? c + 1 : c, 0);
-      const int ln = nxt_here ? len : min(Q, L - (c + 1 < c1 ? c + 1 : c) * Q);
+      // head n + 2's x into the tile just stored, a part every fourth MFMA step
+      int cn, hn;
+      head_after(c, hh, 2, cn, hn);
+      const __bf16* xn = x_base(cn, hn);
+      const int ln = min(Q, L - cn * Q);
       const int xo = 4 * (lt & 63);
-      // the next chunk's B, its parts spread over the heads' MFMA steps (every fourth step a slot
-      // of PPS parts)
-      constexpr int NSTEP = 2 * KS, BUP = RowTile<BV>::UPT, SLOTS = NSTEP / 4,
-                    PPS = (BUP + HS * SLOTS - 1) / (HS * SLOTS);
-      const __bf16* bn = b_base(c + 1 < c1 ? c + 1 : c);
-      const int lbn = min(Q, L - (c + 1 < c1 ? c + 1 : c) * Q);
+      // the next chunk's B into s_b (free once every wavefront has read its B^T rows): BPH
+      // blocks per head, at the head's first step, before its x loads; the fenced barrier before
+      // the next chunk's B^T reads waits for them
+      constexpr int NSTEP = 2 * KS, BPH = (BJ + HS - 1) / HS;
       // the MFMA steps (pi outer, kk inner; two MFMAs per x operand), the operand of the next
       // step read before the current step's MFMAs
       auto xop = [&](int kk, int pi) {
@@ -284,20 +344,29 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
           st[hh][pi] = mfma_16x16x32_bf16(bfr[0][kk], cur, st[hh][pi]);
           st[hh][2 + pi] = mfma_16x16x32_bf16(bfr[1][kk], cur, st[hh][2 + pi]);
           if (step % 4 == 1) {
-            const int part = step / 4;             // 0..3: the next x, in parts
-            if ((nxt_here || nxt_chunk) && part < RowTile<XV>::UPT) xreg.load_one(part, xn, x_tok, ln, lt);
+            const int part = step / 4;             // 0..3: head n + 2's x, in parts
+            if (part < RowTile<XV>::UPT) xb.load_one(part, xn, x_tok, ln, lt);
           }
-          if (step % 4 == 3 && c + 1 < c1) {
+          if (step == 0 && c + 1 < c1) {
 #pragma unroll
-            for (int j = 0; j < PPS; ++j) {
-              const int part = (hh * SLOTS + step / 4) * PPS + j;
-              if (part < BUP) breg.load_one(part, bn, b_tok, lbn, lt);
-            }
+            for (int j = 0; j < BPH; ++j)
+              if (hh * BPH + j < BJ) b_block(hh * BPH + j, c + 1, lt);
           }
+          if (step == 0) asm volatile("" ::: "memory");   // (the B blocks issued before the x loads)
         }
       }
     }
+  };
+
+  // pairs of chunks (an even number of heads: the tiles have the same roles at every pair's
+  // start), then a last single chunk; no chunk is conditional inside the loop, so that no
+  // control-flow join makes the compiler copy (and so wait for) the x tiles in flight
+  int c = c0;
+  for (; c + 1 < c1; c += 2) {
+    chunk(c, std::integral_constant<int, 0>());
+    chunk(c + 1, std::integral_constant<int, 1>());
   }
+  if (c < c1) chunk(c, std::integral_constant<int, 0>());
   // the segment's end states and total exponents
   {
     int lt = tid;
