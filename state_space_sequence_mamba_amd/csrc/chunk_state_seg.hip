@@ -97,23 +97,24 @@ struct RowTile {
 #pragma unroll
     for (int u = 0; u < UPT; ++u) load_one(u, base, stride, len, tid);
   }
-  // into tiles (jt, ct) at (jt VECS / 2 + ct) kST; each value times its token's weight when `wt`
-  // is given
+  // into tiles (jt, ct) at (jt VECS / 2 + ct) kST, each value times its token's weight wt[t]
+  // (straight-line: every weight read issued before the first is used, out-of-range tokens
+  // masked by bits, not branches)
   __device__ __forceinline__ void store(__bf16* dst, const float* wt, int tid) const {
+    float wv[UPT];
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) wv[u] = wt[(tid + kSThreads * u) / VECS];
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
       const int q = tid + kSThreads * u;
       const int t = q / VECS, vec = (q % VECS) * 8;
-      uint4 a = (okm >> u) & 1u ? v[u] : make_uint4(0, 0, 0, 0);
-      if (wt) {
-        const float wv = wt[t];
-        const uint32_t av[4] = {a.x, a.y, a.z, a.w};
-        uint32_t o[4];
+      const uint32_t m = 0u - ((okm >> u) & 1u);
+      const uint32_t av[4] = {v[u].x & m, v[u].y & m, v[u].z & m, v[u].w & m};
+      uint32_t o[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-          o[k] = pack2(__builtin_bit_cast(float, av[k] << 16) * wv, __builtin_bit_cast(float, av[k] & 0xffff0000u) * wv);
-        a = make_uint4(o[0], o[1], o[2], o[3]);
-      }
+      for (int k = 0; k < 4; ++k)
+        o[k] = pack2(__builtin_bit_cast(float, av[k] << 16) * wv[u], __builtin_bit_cast(float, av[k] & 0xffff0000u) * wv[u]);
+      const uint4 a = make_uint4(o[0], o[1], o[2], o[3]);
       const int off = ((t >> 4) * (VECS / 2) + (vec >> 4)) * kST + (t & 15) * 16 + (vec & 15);
       *reinterpret_cast<uint4*>(&dst[off]) = a;
     }
@@ -327,20 +328,23 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
       // blocks per head, at the head's first step, before its x loads; the fenced barrier before
       // the next chunk's B^T reads waits for them
       constexpr int NSTEP = 2 * KS, BPH = (BJ + HS - 1) / HS;
-      // the MFMA steps (pi outer, kk inner; two MFMAs per x operand), the operand of the next
-      // step read before the current step's MFMAs
+      // the MFMA steps (pi outer, kk inner; two MFMAs per x operand), the operand of step + XD
+      // read before step's MFMAs (LDS latency covered by XD steps)
       auto xop = [&](int kk, int pi) {
         const int pt = 2 * pb + pi;
         return tr16x2(&s_x[((2 * kk) * (P / 16) + pt) * kST + xo], &s_x[((2 * kk + 1) * (P / 16) + pt) * kST + xo]);
       };
-      bf16x8 xf = xop(0, 0);
+      constexpr int XD = 3;
+      bf16x8 xq[XD];
+#pragma unroll
+      for (int k = 0; k < XD; ++k) xq[k] = xop(k % KS, k / KS);
 #pragma unroll
       for (int pi = 0; pi < 2; ++pi) {
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
           const int step = pi * KS + kk;
-          const bf16x8 cur = xf;
-          if (step + 1 < NSTEP) xf = xop((step + 1) % KS, (step + 1) / KS);
+          const bf16x8 cur = xq[step % XD];
+          if (step + XD < NSTEP) xq[step % XD] = xop((step + XD) % KS, (step + XD) / KS);
           st[hh][pi] = mfma_16x16x32_bf16(bfr[0][kk], cur, st[hh][pi]);
           st[hh][2 + pi] = mfma_16x16x32_bf16(bfr[1][kk], cur, st[hh][2 + pi]);
           if (step % 4 == 1) {
