@@ -163,18 +163,26 @@ StatePath pick_state_path(int dtype, int64_t B, int64_t H, int64_t G, int P, int
     return sp;
   }
   if (dtype != ssd::DT_BF16 || P != 64 || N != 128) return sp;
-  if (B * H >= 256) {
+  // enough chains for the one pass: it is kept except on long sequences whose groups have at
+  // least four slices of heads sharing B, where segments win.  Measured on MI355X (forward, ms,
+  // one pass / segments): B8 L4096 H32 G1 0.207 / 0.192, B16 L4096 H32 0.420 / 0.373, B8 L8192
+  // H32 0.417 / 0.382; kept: B16 L2048 H32 0.207 / 0.236, B8 L1024 H32 0.066 / 0.097, B4 L4096
+  // H64 G8 (two slices per group) 0.228 / 0.253
+  const int hs_seg = seg_heads((int)(H / G), o.state_heads);
+  const bool seg_long = hs_seg > 0 && scan_variant == 3 && ssd::chunk_state_seg_supported(dtype, P, N, Q, hs_seg) &&
+                        nc >= 16 && (H / G) / hs_seg >= 4;
+  if (B * H >= 256 && !seg_long) {
     if (ssd::chunk_state_seq_supported(a, 64)) {
       sp.path = 2;
       sp.ps = 64;
     }
     return sp;
   }
-  // fewer chains than CUs: segments, sized for at least 256 workgroups.  Measured on MI355X, bf16
+  // fewer chains than CUs (or the long sequences above): segments, sized for at least 256
+  // workgroups.  Measured on MI355X, bf16
   // B2 L16384 H80 G8 (64 chunks, 5 heads per workgroup): segments of 8 / 4 / 2 chunks 0.701 /
   // 0.724 / 0.752 ms per forward against 0.808 for two launches (chunk_state 256 + state_passing
-  // 85 us -> 209 + 11 us; the scan's correction costs it 404 -> 445 us); the one-pass path keeps
-  // B8 L4096 H32 (0.252 ms against 0.266 with segments of 4)
+  // 85 us -> 209 + 11 us; the scan's correction costs it 404 -> 445 us)
   // (segment sizes given in the options apply here too)
   const int hs = seg_heads((int)(H / G), o.state_heads);
   if (hs > 0 && scan_variant == 3 && ssd::chunk_state_seg_supported(dtype, P, N, Q, hs) && nc >= 3) {

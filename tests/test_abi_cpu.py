@@ -238,12 +238,14 @@ def test_product_package_never_imports_the_oracle():
 
 def test_fwd_state_path_choice_is_host_logic():
     """The chunk-state path ssd_fwd takes (pure host logic, no GPU needed): one pass for bf16
-    P64 N128 from batch x heads >= 256, segments below that at chunk 256 (three or more chunks),
-    two launches otherwise; per-call options force a path where an instantiation exists; invalid
-    or empty sizes give 0."""
+    P64 N128 from batch x heads >= 256 (segments instead at chunk 256 for 16 or more chunks when a
+    group has at least four slices of heads), segments below that at chunk 256 (three or more
+    chunks), two launches otherwise; per-call options force a path where an instantiation exists;
+    invalid or empty sizes give 0."""
     import torch
     bf, f32 = torch.bfloat16, torch.float32
-    cases = [((8, 4096, 32, 64, 128, 1, bf), 256, 2), ((8, 4096, 32, 64, 128, 1, bf), 128, 2),
+    cases = [((8, 4096, 32, 64, 128, 1, bf), 256, 3), ((8, 4096, 32, 64, 128, 1, bf), 128, 2),
+             ((16, 2048, 32, 64, 128, 1, bf), 256, 2), ((4, 4096, 64, 64, 128, 8, bf), 256, 2),
              ((8, 4096, 32, 64, 128, 1, bf), 64, 1), ((4, 4096, 32, 64, 128, 1, bf), 256, 3),
              ((2, 16384, 80, 64, 128, 8, bf), 256, 3), ((2, 512, 8, 64, 128, 1, bf), 256, 1),
              ((4, 4096, 32, 64, 128, 1, bf), 128, 1), ((8, 4096, 32, 64, 64, 1, bf), 256, 1),
@@ -260,10 +262,12 @@ def test_fwd_state_path_choice_is_host_logic():
     # segments of 8 chunks for the B2 L16384 H80 G8 shape (at least 256 workgroups), forced sizes
     assert ssd.fwd_state_segment_chunks(p(2, 16384, 80, 64, 128, 8, bf), 256) == 8
     assert ssd.fwd_state_segment_chunks(p(2, 16384, 80, 64, 128, 8, bf), 256, {"state_chunks": 4}) == 4
-    assert ssd.fwd_state_segment_chunks(p(8, 4096, 32, 64, 128, 1, bf), 256) == 0
-    assert ssd.fwd_state_path(p(8, 4096, 32, 64, 128, 1, bf), 256, {"state_path": 3, "state_heads": 4}) == 3
+    assert ssd.fwd_state_segment_chunks(p(8, 4096, 32, 64, 128, 1, bf), 256) == 4
+    assert ssd.fwd_state_segment_chunks(p(16, 2048, 32, 64, 128, 1, bf), 256) == 0
+    assert ssd.fwd_state_path(p(16, 2048, 32, 64, 128, 1, bf), 256, {"state_path": 3, "state_heads": 4}) == 3
+    assert ssd.fwd_state_path(p(8, 4096, 32, 64, 128, 1, bf), 256, {"state_path": 2}) == 2
     # options are per call: nothing of the calls above is kept
-    assert ssd.fwd_state_path(p(8, 4096, 32, 64, 128, 1, bf), 256) == 2
+    assert ssd.fwd_state_path(p(16, 2048, 32, 64, 128, 1, bf), 256) == 2
     assert ssd.fwd_state_path(p(4, 1024, 24, 64, 64, 1, f32), 256, ssd.launch_opts()) == 1
 
 

@@ -102,25 +102,26 @@ def test_workload_fwd_bf16_full_size_sampled(widx):
 
 
 # weak decay: the carried state survives many chunks, so an error in how it is passed from
-# far back is not damped below the bar (A = 0 is the spec invariant: the scan becomes a
-# cumulative sum)
+# far back is not damped below the bar (with A = 0 the scan reduces to a cumulative sum)
 LONG_CHAIN = [
-    # (batch, seqlen, heads, groups, A): the B2 L16384 H80 G8 launch (64 chunks in segments of 8),
-    # the same with a ragged last chunk, and the B8 L4096 H32 launch (16 chunks, one pass)
-    (2, 16384, 80, 8, 0.0), (2, 16384, 80, 8, -1e-3), (2, 16307, 80, 8, -1e-3),
-    (8, 4096, 32, 1, 0.0), (8, 4096, 32, 1, -1e-3),
+    # (batch, seqlen, heads, groups, A, options): the B2 L16384 H80 G8 launch (64 chunks in
+    # segments of 8), the same with a ragged last chunk, and the B8 L4096 H32 launch (16 chunks
+    # in segments of 4, and forced onto the one-pass path)
+    (2, 16384, 80, 8, 0.0, None), (2, 16384, 80, 8, -1e-3, None), (2, 16307, 80, 8, -1e-3, None),
+    (8, 4096, 32, 1, 0.0, None), (8, 4096, 32, 1, -1e-3, None),
+    (8, 4096, 32, 1, 0.0, {"state_path": 2}), (8, 4096, 32, 1, -1e-3, {"state_path": 2}),
 ]
 
 
-@pytest.mark.parametrize("Bt,L,H,G,Aval", LONG_CHAIN)
-def test_bf16_weak_decay_long_chain(Bt, L, H, G, Aval):
-    _say(f"weak decay bf16 B{Bt} L{L} H{H} G{G} A={Aval}")
+@pytest.mark.parametrize("Bt,L,H,G,Aval,opts", LONG_CHAIN)
+def test_bf16_weak_decay_long_chain(Bt, L, H, G, Aval, opts):
+    _say(f"weak decay bf16 B{Bt} L{L} H{H} G{G} A={Aval} opts={opts}")
     inp = I.make_fwd_inputs(Bt, L, H, 64, 128, G, "bf16", seed=70 + Bt + G, d_init="normal")
     inp["A"] = torch.full_like(inp["A"], Aval)
     dims = ssd.make_dims(Bt, L, H, 64, 128, G, torch.bfloat16)
-    path = ssd.fwd_state_path(dims, 256)
-    assert path == (2 if Bt * H >= 256 else 3)       # one pass, or segments of chunks
-    y, fin = _fwd_gpu(inp, 256)
+    path = ssd.fwd_state_path(dims, 256, opts)
+    assert path == (2 if opts else 3)                # one pass, or segments of chunks
+    y, fin = _fwd_gpu(inp, 256, opts=opts)
     hpg = H // G
     pairs = sorted({(b, g * hpg + (5 * b + 3 * g) % hpg) for b in range(Bt) for g in range(G)
                     if (b + g) % 2 == 0 or Bt * G <= 8} | {(Bt - 1, H - 1)})
