@@ -231,7 +231,9 @@ struct HeadRegs {
 
 }  // namespace
 
-template <int P, int N>
+// GATE: z is given (a separate instantiation, so that the ungated kernel carries none of the
+// gate's registers)
+template <int P, int N, bool GATE>
 __global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
     const __bf16* __restrict__ x, const __bf16* __restrict__ Bm, const __bf16* __restrict__ Cm,
     const float* __restrict__ dtp, const float* __restrict__ dAcs, const __bf16* __restrict__ prev16,
@@ -455,15 +457,23 @@ __global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
 #pragma unroll
       for (int pt = 0; pt < TP; ++pt) acc[pt] = mfma_16x16x16_bf16(o.x[pt], a, acc[pt]);
     };
-    // output gate on the lane's elements of strip s (rows past the sequence read a clamped address)
-    auto gate = [&](int s) {
+    // output gate on the lane's elements of strip s (rows past the sequence read a clamped
+    // address); z of both strips is loaded at the head's start, so that the gate waits for z
+    // alone and not for the next head's inputs issued after it
+    auto load_z = [&](int s, uint2 (&zv)[TP]) {
       const __bf16* zh = Z + ((size_t)b * L + t0) * x_tok + (size_t)h * P;
       const int i = 16 * s + r;
       uint32_t zo = (uint32_t)(i < len ? i : 0) * (uint32_t)x_tok + 4 * qd;
       asm volatile("" : "+v"(zo));
-      uint2 zv[TP];
 #pragma unroll
       for (int pt = 0; pt < TP; ++pt) zv[pt] = *reinterpret_cast<const uint2*>(zh + zo + pt * 16);
+    };
+    uint2 zv0[TP], zv1[TP];
+    if constexpr (GATE) {
+      load_z(s0, zv0);
+      load_z(s1, zv1);
+    }
+    auto gate = [&](const uint2 (&zv)[TP]) {
 #pragma unroll
       for (int pt = 0; pt < TP; ++pt) {
         acc[pt][0] *= silu(unpack_lo(zv[pt].x));
@@ -492,7 +502,7 @@ __global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
       if (k % 2 == 1 && k / 2 < HR::kParts) load_part(k / 2, more ? h + 1 : h, lt);
       if (k % 2 == 0 && k / 2 - 1 < kYParts && hh > 0) flush_part(k / 2 - 1, h - 1, lt);
       if (k == w + 1) {                                      // strip s0 complete
-        if (Z) gate(s0);
+        if constexpr (GATE) gate(zv0);
 #pragma unroll
         for (int pt = 0; pt < TP; ++pt) {
           ypk[pt][0] = pack_bf16(acc[pt][0], acc[pt][1]);
@@ -504,7 +514,7 @@ __global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
       off_tile(cb[k], cur, dr);
     }
     diag_tile(cb[kGSub - 1], nxt, dr1, s1);                  // slot 16: strip s1's diagonal tile
-    if (Z) gate(s1);
+    if constexpr (GATE) gate(zv1);
     __syncthreads();                                         // x, Hprev and scalars of head h consumed
 #pragma unroll
     for (int pt = 0; pt < TP; ++pt) {
@@ -534,7 +544,8 @@ hipError_t launch_chunk_scan_group(const FwdArgs& a, int hs, hipStream_t s) {
   if (hs < 1 || hpg % hs != 0) return hipErrorInvalidValue;
   const uint32_t nblocks = (uint32_t)a.B * a.nc * a.G * (hpg / hs);
   if (nblocks == 0) return hipSuccess;
-  hipExtLaunchKernelGGL(chunk_scan_group_kernel<64, 128>, dim3(nblocks), dim3(kGThreads), 0, s, a.ev0, a.ev1, 0,
+  hipExtLaunchKernelGGL(a.z ? chunk_scan_group_kernel<64, 128, true> : chunk_scan_group_kernel<64, 128, false>,
+                        dim3(nblocks), dim3(kGThreads), 0, s, a.ev0, a.ev1, 0,
                         static_cast<const __bf16*>(a.x), static_cast<const __bf16*>(a.Bm),
                         static_cast<const __bf16*>(a.Cm), a.dtp, a.dAcs, static_cast<const __bf16*>(a.prev16), a.D,
                         static_cast<const __bf16*>(a.z), static_cast<__bf16*>(a.y), a.L, a.H, a.G, a.nc, hs, nblocks,
