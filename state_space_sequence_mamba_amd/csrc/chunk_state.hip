@@ -59,15 +59,9 @@ __device__ __forceinline__ void chunk_cumsum_wave(const T* __restrict__ dt, floa
     run += v * a;
     cs[k] = run;
   }
-  // inclusive scan of the lane totals, then shift by one lane for the exclusive prefix
-  float incl = run;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float t = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += t;
-  }
-  float excl = __shfl_up(incl, 1, 64);
-  if (lane == 0) excl = 0.f;
+  // inclusive scan of the lane totals (DPP lane moves), then shifted by one lane for the
+  // exclusive prefix
+  const float excl = wave_shr1(wave_incl_scan(run));
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     if (k < epl) {
@@ -509,17 +503,11 @@ __global__ __launch_bounds__(NTHR) void chunk_state_seq_kernel(
         run += d[k] * av;
         cs[k] = run;
       }
-      float incl = run;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float t = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += t;
-      }
-      float excl = __shfl_up(incl, 1, 64);
-      if (lane == 0) excl = 0.f;
+      const float excl = wave_shr1(wave_incl_scan(run));
 #pragma unroll
       for (int k = 0; k < EPL; ++k) cs[k] += excl;
-      const float last = __shfl(cs[EPL - 1], 63, 64);      // the stored dAcs[Q - 1]
+      // the stored dAcs[Q - 1]
+      const float last = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cs[EPL - 1]), 63));
 #pragma unroll
       for (int k = 0; k < EPL; ++k) s_w[lane * EPL + k] = expf(last - cs[k]) * d[k];
       if (lane == 0) s_last = last;

@@ -16,8 +16,8 @@
 // to L_c when it stages the entering state.
 //
 // One workgroup (8 wavefronts) per (batch, segment, group, slice of HS heads of the group).  Per
-// chunk: dt' and the in-chunk cumsum of dt' A for every head of the slice (wavefront hh, as in
-// chunk_state: a log-step shuffle scan over 64 lanes), written to the workspace for chunk_scan;
+// chunk: dt' and the in-chunk cumsum of dt' A for every head of the slice (wavefront hh: a DPP
+// prefix scan over 64 lanes), written to the workspace for chunk_scan;
 // B staged once in LDS for all the slice's heads; each wavefront owns a 32 x 32 block of S^T and
 // holds its 32 dstate rows of B^T in registers for the chunk.  Per head: x times the token weights staged in LDS, L_c written
 // (rounded to bf16) unless c opens the segment, the state scaled by the chunk's decay and the
@@ -250,17 +250,10 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
         run_l += d[k] * av;
         cs[k] = run_l;
       }
-      float incl = run_l;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float t = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += t;
-      }
-      float excl = __shfl_up(incl, 1, 64);
-      if (lane == 0) excl = 0.f;
+      const float excl = wave_shr1(wave_incl_scan(run_l));   // sum over the lanes before this one
 #pragma unroll
       for (int k = 0; k < EPL; ++k) cs[k] += excl;
-      const float last = __shfl(cs[EPL - 1], 63, 64);
+      const float last = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cs[EPL - 1]), 63));
       const size_t o = (((size_t)b * H + h) * nc + c) * Q + lane * EPL;
       static_assert(EPL == 4, "one 16-byte store per lane");
       *reinterpret_cast<float4*>(&dtp[o]) = make_float4(d[0], d[1], d[2], d[3]);

@@ -262,7 +262,6 @@ __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, 
   }
   const int lenR = min(KT, len - R * KT);
   const size_t xs = (size_t)H * P, bs = (size_t)G * N;
-  const int tk = min(tid, KT - 1);
   const T* Cg = Cm + ((size_t)b * L + t0) * bs + (size_t)g * N;
 
   RowTile<T, N> tb, tc;
@@ -531,7 +530,6 @@ __global__ __launch_bounds__(256) void bwd_dc_kernel(const T* __restrict__ x, co
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane & 15, qd = lane >> 4;
   const size_t xs = (size_t)H * P, bs = (size_t)G * N;
-  const int tk = min(tid, KT - 1);
   const T* Bg = Bm + ((size_t)b * L + t0) * bs + (size_t)g * N;
 
   RowTile<T, N> tc, tb;

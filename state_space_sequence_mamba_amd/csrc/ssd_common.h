@@ -75,6 +75,29 @@ __device__ __forceinline__ Vec16<T> load16_if(const T* p, bool ok) {
 // fp32 resolution of v, so v itself is returned (and e^v never overflows).
 __device__ __forceinline__ float softplus(float v) { return v > 20.f ? v : log1pf(expf(v)); }
 
+// Inclusive prefix sum over the 64 lanes of a wavefront with DPP lane moves (no LDS round
+// trips): Hillis-Steele within each row of 16 lanes (row_shr 1, 2, 4, 8; lanes shifted in from
+// before the row's start add 0), then each odd row adds the total of the row before it
+// (row_bcast:15 into rows 1 and 3) and rows 2 and 3 the total of rows 0 and 1 (row_bcast:31).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float x) {
+  const int t = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xf, false);
+  return x + __builtin_bit_cast(float, t);
+}
+__device__ __forceinline__ float wave_incl_scan(float x) {
+  x = dpp_add<0x111, 0xf>(x);   // row_shr:1
+  x = dpp_add<0x112, 0xf>(x);   // row_shr:2
+  x = dpp_add<0x114, 0xf>(x);   // row_shr:4
+  x = dpp_add<0x118, 0xf>(x);   // row_shr:8
+  x = dpp_add<0x142, 0xa>(x);   // row_bcast:15 into rows 1, 3
+  x = dpp_add<0x143, 0xc>(x);   // row_bcast:31 into rows 2, 3
+  return x;
+}
+// the value of the lane before (lane 0: 0), by a wave_shr:1 lane move
+__device__ __forceinline__ float wave_shr1(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x138, 0xf, 0xf, false));
+}
+
 // silu(u) = u / (1 + e^-u) with the hardware exp2 and reciprocal (each within ~1 ulp; the
 // result is within a few ulp).  Saturates cleanly: u -> -inf gives -0, u -> +inf gives u.
 __device__ __forceinline__ float silu(float u) {
