@@ -147,15 +147,17 @@ struct HeadRegs {
         po[u] = (uint32_t)(tid + kGThreads * u) * 16;                     // bytes
         asm volatile("" : "+v"(po[u]));
       }
+      // (a segment's first chunk has no carried state of its own: it drops the loaded one at the
+      // store, since overwriting the registers here would wait for their loads, and loads it
+      // from the incoming state's address, so that the bytes come from the L2)
+      pz = hh && first;
+      const __bf16* pp = pz ? hh : ph;
 #pragma unroll
-      for (int u = 0; u < PPT; ++u) pv[u] = ld16(ph, po[u]);
+      for (int u = 0; u < PPT; ++u) pv[u] = ld16(pp, po[u]);
       if (hh) {
 #pragma unroll
         for (int u = 0; u < PPT; ++u) hv[u] = ld16(hh, po[u]);
       }
-      // (a segment's first chunk drops the loaded state at the store: overwriting the registers
-      // here would wait for their loads)
-      pz = hh && first;
     } else {
       // only the wavefronts that store them load the scalars (wavefront-uniform branches)
       const int wf = __builtin_amdgcn_readfirstlane(tid) / 64;
