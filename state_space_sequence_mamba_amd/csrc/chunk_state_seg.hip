@@ -61,11 +61,24 @@ __device__ __forceinline__ bf16x8 tr16x2(const __bf16* t0, const __bf16* t1) {
 // with no memory fence.  (__syncthreads' fence would also wait for the direct-to-LDS loads of the
 // next chunk's B in flight and, loads completing in order, for the x loads issued before them.)
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-// every vector memory operation of this wavefront complete but the last four: s_waitcnt vmcnt(4)
-// (the four x loads of the previous head stay in flight; the direct-to-LDS loads issued before
-// them have landed, and the compiler, which takes an explicit wait into account, adds none of
-// its own for them before the next LDS stores)
-__device__ __forceinline__ void vm_keep4() { __builtin_amdgcn_s_waitcnt(0x0F74); }
+// f(integral_constant<int, i>) for i = 0 .. N - 1, unrolled at compile time
+template <int... I, class F>
+__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, I...>, F&& f) {
+  (f(std::integral_constant<int, I>()), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(std::make_integer_sequence<int, N>(), f);
+}
+// every vector memory operation of this wavefront complete but the last N: s_waitcnt vmcnt(N)
+// (loads complete in order, so a load issued before N more loads and stores has landed, while
+// these stay in flight; the compiler takes an explicit wait into account and adds none of its own
+// for what it covers)
+template <int N>
+__device__ __forceinline__ void vm_keep() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | 0x0F70 | ((N >> 4) << 14));
+}
 
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   typedef float f2 __attribute__((ext_vector_type(2)));
@@ -104,11 +117,15 @@ struct RowTile {
     float wv[UPT];
 #pragma unroll
     for (int u = 0; u < UPT; ++u) wv[u] = wt[(tid + kSThreads * u) / VECS];
+    // (the mask bits made opaque here: known at the load, the masking would be folded into a
+    // select right behind it, which waits for the load on the spot)
+    uint32_t om = okm;
+    asm volatile("" : "+v"(om));
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
       const int q = tid + kSThreads * u;
       const int t = q / VECS, vec = (q % VECS) * 8;
-      const uint32_t m = 0u - ((okm >> u) & 1u);
+      const uint32_t m = 0u - ((om >> u) & 1u);
       const uint32_t av[4] = {v[u].x & m, v[u].y & m, v[u].z & m, v[u].w & m};
       uint32_t o[4];
 #pragma unroll
@@ -116,7 +133,12 @@ struct RowTile {
         o[k] = pack2(__builtin_bit_cast(float, av[k] << 16) * wv[u], __builtin_bit_cast(float, av[k] & 0xffff0000u) * wv[u]);
       const uint4 a = make_uint4(o[0], o[1], o[2], o[3]);
       const int off = ((t >> 4) * (VECS / 2) + (vec >> 4)) * kST + (t & 15) * 16 + (vec & 15);
-      *reinterpret_cast<uint4*>(&dst[off]) = a;
+      // (an inline-asm LDS store: the compiler does not order it behind the direct-to-LDS B loads
+      // in flight, which write other tiles, as it would a plain store; their landing is waited
+      // for only before the next chunk's B^T reads)
+      typedef unsigned su32x4 __attribute__((ext_vector_type(4)));
+      const uint32_t la = (uint32_t)reinterpret_cast<uintptr_t>(&dst[off]);
+      asm volatile("ds_write_b128 %0, %1" ::"v"(la), "v"(su32x4{a.x, a.y, a.z, a.w}) : "memory");
     }
   }
 };
@@ -164,7 +186,12 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
   // each load on the spot)
   auto load_dt = [&](int c, uint32_t (&dv)[EPL]) {
     const int hh = w < HS ? w : 0;
-    const unsigned short* d16 = reinterpret_cast<const unsigned short*>(dt);
+    // (through an opaque pointer: a load known not to alias any store would be moved down to
+    // its use in the next chunk, inside the branch of the wavefronts that scan, and waited for
+    // there on the spot)
+    typedef const __attribute__((address_space(1))) unsigned short gu16;
+    gu16* d16 = (gu16*)dt;
+    asm volatile("" : "+s"(d16));
 #pragma unroll
     for (int k = 0; k < EPL; ++k) {
       const int t = min(c * Q + lane * EPL + k, L - 1);
@@ -189,10 +216,13 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
   constexpr int BBLK = (Q / 16) * (N / 16) * kST / (64 * 8);       // 1 KiB blocks of s_b
   static_assert(kST * 2 == 34 * 16 && BBLK * 64 * 8 == (Q / 16) * (N / 16) * kST, "B tiles: 34 slots each");
   constexpr int BJ = (BBLK + 7) / 8;                               // blocks per wavefront (at most)
-  auto b_block = [&](int j, int c, int t) {
+  auto b_block = [&](int j, int c, int t, bool idle) {
     int q = 8 * j + w;
+    // (the last round of blocks: wavefronts past the end load the block eight before again, into
+    // the same slots, so that no load is conditional)
+    if (8 * (j + 1) > BBLK) q = q < BBLK ? q : q - 8;
     asm volatile("" : "+s"(q));
-    if (q < BBLK) {
+    {
       const int S = 64 * q + (t & 63);
       const int T = S / 34, si = S % 34;
       const int row = 16 * (T >> 3) + (si < 32 ? si >> 1 : 0);
@@ -200,6 +230,7 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
       const int lenc = min(Q, L - c * Q);
       uint32_t o = ((uint32_t)(row < lenc ? row : 0) * b_tok + n) * 2;
       asm volatile("" : "+v"(o));
+      o = idle ? 0u : o;                           // (an idle load: one 16-byte vector for all lanes)
       __builtin_amdgcn_global_load_lds(
           (const __attribute__((address_space(1))) void*)(reinterpret_cast<const char*>(b_base(c)) + o),
           (__attribute__((address_space(3))) void*)(s_b + q * 64 * 8), 16, 0, 0);
@@ -222,20 +253,25 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
   };
   uint32_t dtv[EPL];
 #pragma unroll
-  for (int j = 0; j < BJ; ++j) b_block(j, c0, tid);
+  for (int j = 0; j < BJ; ++j) b_block(j, c0, tid, false);
+  load_dt(c0, dtv);
   {
     int cn, hn;
     xr[0].load(x_base(c0, 0), x_tok, min(Q, L - c0 * Q), tid);
     head_after(c0, 0, 1, cn, hn);
     xr[1].load(x_base(cn, hn), x_tok, min(Q, L - cn * Q), tid);
   }
-  load_dt(c0, dtv);
 
   // one chunk; CP: the chunk's parity in the segment (which register tile each head uses)
   auto chunk = [&](int c, auto cp_tag) {
     constexpr int CP = decltype(cp_tag)::value;
     const int len = min(Q, L - c * Q);
-    vm_keep4();                                    // the previous chunk's last B blocks landed
+    // the B blocks of this chunk landed.  Every load and store of a chunk is unconditional (no
+    // count the compiler tracks depends on a branch), in this order per head: its L_c stores, its
+    // share of the next chunk's B (heads 0 .. HS - 2; one head: in it), its four x loads.  After
+    // the last B block come head HS - 2's x loads and head HS - 1's stores and loads (one head:
+    // its x loads); after the segment's first B, dt and two heads' x
+    vm_keep<HS == 1 ? 4 : 12>();
     lds_barrier();                                 // the previous chunk's weights and exponents consumed
     if (w < HS) {
       // dt' and the inclusive in-chunk cumsum of dt' A of head h0 + w; weights to the chunk end
@@ -267,8 +303,8 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
       }
       run += last;
     }
-    if (c + 1 < c1) load_dt(c + 1, dtv);
-    __syncthreads();                               // B (loaded during the previous chunk), weights and exponents in LDS
+    load_dt(min(c + 1, c1 - 1), dtv);
+    lds_barrier();                                 // B (landed before the first barrier), weights and exponents in LDS
     // this wavefront's B^T rows n = 16 (2 nb + ni) + r for the whole chunk (A operands)
     bf16x8 bfr[2][KS];
     {
@@ -282,11 +318,18 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
                                &s_b[((2 * kk + 1) * (N / 16) + 2 * nb + ni) * kST + bo]);
     }
 
-#pragma unroll
-    for (int hh = 0; hh < HS; ++hh) {
+    static_for<HS>([&](auto hc) {
+      constexpr int hh = decltype(hc)::value;
       RowTile<XV>& xb = xr[(CP * HS + hh) & 1];
-      if (hh > 0) {
-        vm_keep4();                                // the previous head's B blocks landed
+      constexpr int NSTEP = 2 * KS, BH = HS > 1 ? HS - 1 : 1, BPH = (BJ + BH - 1) / BH;
+      // B blocks issued in head k
+      constexpr auto nbk = [](int k) { return k < BH ? (BJ - k * BPH < BPH ? (BJ - k * BPH > 0 ? BJ - k * BPH : 0) : BPH) : 0; };
+      if constexpr (hh > 0) {
+        // this head's x (loaded two heads back) landed: after it come, per head, the L_c stores,
+        // the B blocks and the x loads (at head 1: the chunk start's dt loads and head 0's; the
+        // scanning wavefronts' stores there only add to the count)
+        constexpr int KEEP = hh == 1 ? 12 + nbk(0) : 8 + nbk(hh - 1);
+        vm_keep<KEEP>();
         lds_barrier();                             // the previous head's x consumed
       }
       xb.store(s_x, s_w[hh], tid);
@@ -296,11 +339,14 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
       int lt = tid;
       asm volatile("" : "+v"(lt));
       const int rr = lt & 15, qq = (lt >> 4) & 3;
-      if (c > c0) {
-        // L_c: the state this segment carried into chunk c, rounded to bf16 for the scan
+      {
+        // L_c: the state this segment carried into chunk c, rounded to bf16 for the scan (none
+        // for the segment's first chunk, whose slot the scan does not read: there every lane
+        // stores into its first vector, so that no store is conditional)
         __bf16* dst = prev16 + (((size_t)b * nc + c) * H + h) * PN;
         uint32_t o = ((uint32_t)(32 * pb + rr) * N + 32 * nb + 4 * qq) * 2;
         asm volatile("" : "+v"(o));
+        o = c > c0 ? o : 0u;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           *reinterpret_cast<uint2*>(reinterpret_cast<char*>(dst) + o + ((j & 1) * 16 * N + (j >> 1) * 16) * 2) =
@@ -318,9 +364,8 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
       const int ln = min(Q, L - cn * Q);
       const int xo = 4 * (lt & 63);
       // the next chunk's B into s_b (free once every wavefront has read its B^T rows): BPH
-      // blocks per head, at the head's first step, before its x loads; the fenced barrier before
-      // the next chunk's B^T reads waits for them
-      constexpr int NSTEP = 2 * KS, BPH = (BJ + HS - 1) / HS;
+      // blocks per head in every head but the last (one head: in it), at the head's first step,
+      // before its x loads
       // the MFMA steps (pi outer, kk inner; two MFMAs per x operand), the operand of step + XD
       // read before step's MFMAs (LDS latency covered by XD steps)
       auto xop = [&](int kk, int pi) {
@@ -344,15 +389,15 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
             const int part = step / 4;             // 0..3: head n + 2's x, in parts
             if (part < RowTile<XV>::UPT) xb.load_one(part, xn, x_tok, ln, lt);
           }
-          if (step == 0 && c + 1 < c1) {
+          if (step == 0) {
+            // (at the segment's last chunk idle loads: s_b is no longer read)
 #pragma unroll
-            for (int j = 0; j < BPH; ++j)
-              if (hh * BPH + j < BJ) b_block(hh * BPH + j, c + 1, lt);
+            for (int j = 0; j < nbk(hh); ++j) b_block(hh * BPH + j, min(c + 1, c1 - 1), lt, c + 1 >= c1);
           }
           if (step == 0) asm volatile("" ::: "memory");   // (the B blocks issued before the x loads)
         }
       }
-    }
+    });
   };
 
   // pairs of chunks (an even number of heads: the tiles have the same roles at every pair's
@@ -364,6 +409,9 @@ __global__ __launch_bounds__(kSThreads, 1) void chunk_state_seg_kernel(
     chunk(c + 1, std::integral_constant<int, 1>());
   }
   if (c < c1) chunk(c, std::integral_constant<int, 0>());
+  // the last chunk's B loads into LDS (issued unconditionally, unused) land before the
+  // workgroup ends
+  vm_keep<0>();
   // the segment's end states and total exponents
   {
     int lt = tid;
