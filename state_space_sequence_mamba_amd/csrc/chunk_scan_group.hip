@@ -305,13 +305,22 @@ __global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
     const int row = v / (N / 8), nv = (v % (N / 8)) * 8;
     breg[u] = *reinterpret_cast<const uint4*>(Bb + (size_t)(row < len ? row : 0) * bc_tok + nv);
   }
-  // C rows past the end read row 0 (they reach only output rows that are never stored)
+  // C rows past the end read row 0 (they reach only output rows that are never stored).  (Read
+  // through an opaque pointer and fenced: loads known to be invariant would be moved down to
+  // their LDS stores, each then waited for on its own.)
   uint4 creg[BPT];
+  {
+    typedef unsigned gu32x4 __attribute__((ext_vector_type(4)));
+    typedef const __attribute__((address_space(1))) gu32x4 gv4;
+    gv4* cg = (gv4*)Cb;
+    asm volatile("" : "+s"(cg));
 #pragma unroll
-  for (int u = 0; u < BPT; ++u) {
-    const int v = tid + kGThreads * u;
-    const int row = v / (N / 8), nv = (v % (N / 8)) * 8;
-    creg[u] = *reinterpret_cast<const uint4*>(Cb + (size_t)(row < len ? row : 0) * bc_tok + nv);
+    for (int u = 0; u < BPT; ++u) {
+      const int v = tid + kGThreads * u;
+      const int row = v / (N / 8), nv = (v % (N / 8)) * 8;
+      const gu32x4 t = cg[((size_t)(row < len ? row : 0) * bc_tok + nv) / 8];
+      creg[u] = make_uint4(t.x, t.y, t.z, t.w);
+    }
   }
   HR hr;
   // part `part` of head hn's inputs into hr
@@ -323,6 +332,7 @@ __global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
   };
 #pragma unroll
   for (int part = 0; part < HR::kParts; ++part) load_part(part, h0, tid);
+  asm volatile("" ::: "memory");
   // row block u of head hn's y from the staging tile to global memory (16-byte rows pieces)
   constexpr int kYParts = (kGQ * P / 8) / kGThreads;
   auto flush_part = [&](int u, int hn, int t) {
