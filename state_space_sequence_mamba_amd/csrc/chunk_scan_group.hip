@@ -63,9 +63,6 @@ __device__ __forceinline__ float unpack_hi(uint32_t v) { return __builtin_bit_ca
 __device__ __forceinline__ uint4 ld16(const void* base, uint32_t off) {
   return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(base) + off);
 }
-__device__ __forceinline__ void st16(void* base, uint32_t off, uint4 v) {
-  *reinterpret_cast<uint4*>(reinterpret_cast<char*>(base) + off) = v;
-}
 
 typedef short gi16x4 __attribute__((ext_vector_type(4)));
 // LDS transpose read (ds_read_b64_tr_b16): every lane passes the address of 8 bytes; in each
@@ -333,15 +330,27 @@ __global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
 #pragma unroll
   for (int part = 0; part < HR::kParts; ++part) load_part(part, h0, tid);
   asm volatile("" ::: "memory");
-  // row block u of head hn's y from the staging tile to global memory (16-byte rows pieces)
+  // row block u of a head's y, from the staging tile (y_part) to global memory (y_flush), in
+  // 16-byte row pieces, through a buffer resource bounded to the chunk's len rows: stores past
+  // it are dropped by the hardware, so no store is conditional (live = false: every store is)
   constexpr int kYParts = (kGQ * P / 8) / kGThreads;
-  auto flush_part = [&](int u, int hn, int t) {
+  typedef unsigned yu32x4 __attribute__((ext_vector_type(4)));
+  auto y_rsrc = [&](int hn, bool live) {
+    const __bf16* base = y + ((size_t)b * L + t0) * x_tok + (size_t)hn * P;
+    const int nbytes = live ? (int)(((uint32_t)(len - 1) * (uint32_t)x_tok + P) * 2) : 0;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nbytes, 0x00020000);
+  };
+  auto y_part = [&](int u, int t) {
+    const int v = t + kGThreads * u;
+    const int row = v / (P / 8), cv = (v % (P / 8)) * 8;
+    return *reinterpret_cast<const uint4*>(&s_y[row * SL::YP + cv]);
+  };
+  auto y_flush = [&](int u, const uint4& val, __amdgpu_buffer_rsrc_t rs, int t) {
     const int v = t + kGThreads * u;
     const int row = v / (P / 8), cv = (v % (P / 8)) * 8;
     uint32_t yo = ((uint32_t)row * (uint32_t)x_tok + cv) * 2;
     asm volatile("" : "+v"(yo));
-    const uint4 val = *reinterpret_cast<const uint4*>(&s_y[row * SL::YP + cv]);
-    if (row < len) st16(y + ((size_t)b * L + t0) * x_tok + (size_t)hn * P, yo, val);
+    __builtin_amdgcn_raw_buffer_store_b128((yu32x4){val.x, val.y, val.z, val.w}, rs, yo, 0, 0);
   };
 #pragma unroll
   for (int u = 0; u < BPT; ++u) {
@@ -497,6 +506,8 @@ __global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
 
     uint32_t ypk[TP][2];
     float dr = dr0;
+    const __amdgpu_buffer_rsrc_t yrs = y_rsrc(h - 1, hh > 0);   // the previous head's y (none at the first)
+    uint4 yv;
     Ops cur, nxt;
     read_ops(w, true, cur);                                  // slot 0: strip s0's diagonal tile
     read_ops(0, false, nxt);                                 // slot 1: column tile 0 of s0 or s1
@@ -504,6 +515,9 @@ __global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
 #pragma unroll
     for (int k = 1; k < kGSub - 1; ++k) {
       cur = nxt;
+      // (each y row block read from LDS a slot before its store, ahead of the operand reads: the
+      // store then waits for it alone)
+      if (k % 2 == 1 && k / 2 < kYParts) yv = y_part(k / 2, lt);
       if (k + 1 < kGSub - 1)
         read_ops(k + 1 <= w ? k : k - w, false, nxt);
       else
@@ -512,7 +526,7 @@ __global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
       // last head reloads its own, unused); between them the previous head's y, a row block per
       // slot, from its staging tile (rewritten only after this head's first barrier)
       if (k % 2 == 1 && k / 2 < HR::kParts) load_part(k / 2, more ? h + 1 : h, lt);
-      if (k % 2 == 0 && k / 2 - 1 < kYParts && hh > 0) flush_part(k / 2 - 1, h - 1, lt);
+      if (k % 2 == 0 && k / 2 - 1 < kYParts) y_flush(k / 2 - 1, yv, yrs, lt);
       if (k == w + 1) {                                      // strip s0 complete
         if constexpr (GATE) gate(zv0);
 #pragma unroll
@@ -541,8 +555,9 @@ __global__ __launch_bounds__(kGThreads, 1) void chunk_scan_group_kernel(
   {
     int lt = tid;
     asm volatile("" : "+v"(lt));
+    const __amdgpu_buffer_rsrc_t yrs = y_rsrc(h0 + hs - 1, true);
 #pragma unroll
-    for (int u = 0; u < kYParts; ++u) flush_part(u, h0 + hs - 1, lt);
+    for (int u = 0; u < kYParts; ++u) y_flush(u, y_part(u, lt), yrs, lt);
   }
 }
 
