@@ -9,7 +9,9 @@ B1 L256 and B4 L1024 forwards, the bf16 B8 L4096 forward, and 1000 consecutive s
 calls over B256 H80), each with its tokens/s and its dominant kernel's roofline fraction.
 Other workloads alone (--workload): any forward or backward size, the decode loop, the conv1d +
 SiLU in front of the scan.  Inputs are seeded synthetic tensors resident in HBM before the timed
-region.  Prints ONE JSON line.
+region.  Each timed region follows --settle-ms (default 300) of untimed replays of the same steps,
+so that it measures the GPU at its sustained clocks rather than the ramp after set-up ("settle" in
+the line).  Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME] [--no-configs]
 """
@@ -159,6 +161,21 @@ def cpu_baseline(w, inp, y_gpu, budget_s):
     return base, parity
 
 
+def settle(run, args):
+    """Untimed sustained load right before a timed region.  The GPU's clocks rise over the first
+    tens of milliseconds of load (the same K steps measured 0.496 ms each right after set-up and
+    0.438 ms each inside a 300-step region), so a short region timed straight after the
+    set-up's idle stretches (graph capture, allocation) would measure part of that ramp instead of
+    the sustained rate.  `run` enqueues one batch of the workload's own steps; it is repeated,
+    each time to completion, until `--settle-ms` of wall time have passed."""
+    n, t0 = 0, time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < args.settle_ms:
+        run()
+        torch.cuda.synchronize()
+        n += 1
+    return {"ms": round((time.perf_counter() - t0) * 1e3, 1), "runs": n}
+
+
 def decode_cost(w):
     e = 2 if w.dtype == "bf16" else 4
     B, H, P, N, G = w.batch, w.nheads, w.headdim, w.dstate, w.ngroups
@@ -181,6 +198,7 @@ def run_decode(w, args, dev):
 
     for t in range(W):
         call(t)
+    settled = settle(lambda: [call(t) for t in range(w.steps)], args)
     state.copy_(inp["state0"])
     torch.cuda.synchronize()
     hev = HipEvents()
@@ -215,6 +233,7 @@ def run_decode(w, args, dev):
                      "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
                      "traffic": load_traffic(workload_slug(w.name), "ssd_step"),
                      "kernel_us": round(k_ms * 1e3, 3), "alg_bytes_per_launch": alg_bytes},
+        "settle": settled,
         "wall_s_timed_region": round(wall, 4),
     }
 
@@ -310,6 +329,7 @@ def run_bwd(w, args, dev, opts=None):
             for i in range(K):
                 step(W + i)
         torch.cuda.synchronize()
+    settled = settle(graph.replay if use_graph else (lambda: [step(W + i) for i in range(K)]), args)
     hev = HipEvents()
     t0, t1 = hev.create(), hev.create()
     wall0 = time.perf_counter()
@@ -367,6 +387,7 @@ def run_bwd(w, args, dev, opts=None):
         "launch": ("hip_graph (per-kernel times from an eager pass of the same K steps)" if use_graph
                    else "eager"),
         "input_copies": R,
+        "settle": settled,
         "wall_s_timed_region": round(wall, 4),
     }
     hev.close()
@@ -462,6 +483,7 @@ def run_conv(w, args, dev, opts=None):
             for _ in range(K):
                 step()
         torch.cuda.synchronize()
+    settled = settle(graph.replay if use_graph else (lambda: [step() for _ in range(K)]), args)
     hev = HipEvents()
     t0, t1 = hev.create(), hev.create()
     wall0 = time.perf_counter()
@@ -494,6 +516,7 @@ def run_conv(w, args, dev, opts=None):
                      "traffic": load_traffic(workload_slug(w.name), "conv1d_silu"),
                      "alg_bytes_per_launch": alg_bytes},
         "launch": "hip_graph" if use_graph else "eager",
+        "settle": settled,
         "wall_s_timed_region": round(wall, 4),
     }
     return out
@@ -521,6 +544,7 @@ def run_norm(w, args, dev):
             for _ in range(K):
                 step()
         torch.cuda.synchronize()
+    settled = settle(graph.replay if use_graph else (lambda: [step() for _ in range(K)]), args)
     hev = HipEvents()
     t0, t1 = hev.create(), hev.create()
     wall0 = time.perf_counter()
@@ -558,6 +582,7 @@ def run_norm(w, args, dev):
                      "traffic": load_traffic(workload_slug(w.name), "gated_rmsnorm"),
                      "alg_bytes_per_launch": alg_bytes, "kernel_us": round(k_ms * 1e3, 3)},
         "launch": "hip_graph" if use_graph else "eager",
+        "settle": settled,
         "wall_s_timed_region": round(wall, 4),
     }
 
@@ -615,6 +640,7 @@ def run_fwd(w, args, dev, opts, with_cpu):
             for i in range(K):
                 step(W + i)
         torch.cuda.synchronize()
+    settled = settle(graph.replay if use_graph else (lambda: [step(W + i) for i in range(K)]), args)
     wall0 = time.perf_counter()
     hev.record(t_start)
     if use_graph:
@@ -684,6 +710,7 @@ def run_fwd(w, args, dev, opts, with_cpu):
         "launch": ("hip_graph (per-kernel times from an eager pass of the same K steps)" if use_graph
                    else "eager"),
         "input_copies": R,
+        "settle": settled,
         "wall_s_timed_region": round(wall, 4),
     }
     hev.close()
@@ -712,6 +739,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch the timed steps eagerly, not as a HIP graph")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed sustained load (the workload's own steps) right before each timed region, "
+                         "so that the region measures the GPU at its sustained clocks (0 = none)")
     ap.add_argument("--rotate-mb", type=int, default=256,
                     help="forward steps rotate over copies of x, dt, B, C, y totalling at least twice "
                          "this many MiB, so inputs come from HBM, not the last-level cache (0 = one copy)")
