@@ -157,7 +157,8 @@ def summary(args):
             events["state_passing" if k == "state_passing_seg" else k] = v["us"]
         rl = bench.get("roofline", {})
         if rl.get("kernel"):
-            events.setdefault(rl["kernel"], None)
+            # (the decode line carries its kernel's dispatch-event average in the roofline)
+            events.setdefault(rl["kernel"], rl.get("kernel_us"))
     out = [f"# Kernel trace: {args.workload} (MI355X, gfx950)", "",
            "Command (from the repository root, TMPDIR=/tmp):", "", f"    {args.command}", "",
            "Summarised with `python -m state_space_sequence_mamba_amd.profiling summary` from the run's "
