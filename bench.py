@@ -245,7 +245,7 @@ BWD_STAGES = ["chunk_state", "state_passing", "gate_fwd", "gate_bwd", "chunk_sta
 def backward_cost(w, hs=1):
     """Algorithmic bytes and flops of each backward kernel per launch.  C B^T and dy x^T are
     counted once (in bwd_dxdb; bwd_dc recomputes them, which is not algorithmic work).  hs: heads
-    per bwd_dxdb workgroup (its dB leaves per slice of hs heads)."""
+    per bwd_dxdb and bwd_dc workgroup (dB and dC leave per slice of hs heads)."""
     e = 4 if w.dtype == "f32" else 2
     B, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
     nc = (L + Q - 1) // Q
@@ -270,11 +270,11 @@ def backward_cost(w, hs=1):
                          flops=2 * N * tri * B * G + 2 * P * tri * B * H * 2 + 2 * N * tri * B * H
                          + 4 * B * H * L * P * N,
                          flops_in=2 * N * tri * B * G + 2 * P * tri * B * H * 2 + 2 * N * tri * B * H),
-        "bwd_dc": dict(bytes=2 * x + 2 * bc + 2 * cum + st + perh + B * H * L * 4,
+        "bwd_dc": dict(bytes=2 * x + 2 * bc + 2 * cum + st + perh // hs + B * H * L * 4,
                        flops=2 * N * tri * B * H + 2 * B * H * L * P * N,
                        flops_in=2 * N * tri * B * H),
         "bwd_finalize": dict(bytes=2 * st + 5 * cum + B * L * H * e * 2, flops=2 * B * nc * H * P * N),
-        "bwd_reduce": dict(bytes=perh // hs + perh + 2 * bc, flops=2 * B * L * H * N),
+        "bwd_reduce": dict(bytes=2 * (perh // hs) + 2 * bc, flops=2 * B * L * H * N),
     }
     for k, v in cost.items():
         # chunk_state contracts on MFMA in the input dtype; the backward kernels' products run

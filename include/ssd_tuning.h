@@ -42,10 +42,10 @@ typedef struct {
   int32_t conv_tokens;      /* ssd_conv1d_silu tokens per thread (rounded up to a multiple of 4) */
   int32_t state_heads;      /* segmented chunk states: heads per workgroup (1, 2, 4 or 5) */
   int32_t state_chunks;     /* segmented chunk states: chunks per segment (at least 2) */
-  int32_t bwd_heads;        /* ssd_bwd: heads per bwd_dxdb workgroup, whose dB contributions are
-                             * summed in registers before they leave the chip: 1, or 4 for SSD_BF16
-                             * when it divides nheads / ngroups (else 1); the summation order
-                             * changes, results agree to rounding */
+  int32_t bwd_heads;        /* ssd_bwd: heads per bwd_dxdb and bwd_dc workgroup, whose dB and dC
+                             * contributions are summed in registers before they leave the chip: 1,
+                             * or 4 for SSD_BF16 when it divides nheads / ngroups (else 1); the
+                             * summation order changes, results agree to rounding */
 } ssd_launch_opts_t;
 
 /* ssd_fwd with options and per-kernel timing.  `opts` may be NULL.  `stage_events` is NULL or
@@ -111,9 +111,9 @@ int ssd_fwd_state_path(const ssd_dims_t* dims, int chunk_size, const ssd_launch_
  * or for invalid or empty arguments.  Pure host logic. */
 int ssd_fwd_state_segment_chunks(const ssd_dims_t* dims, int chunk_size, const ssd_launch_opts_t* opts);
 
-/* Heads per bwd_dxdb workgroup that ssd_bwd_ex takes for these sizes and options (NULL = the
- * built-in choice of ssd_bwd): 1, or 4 when dB is summed over slices of four heads on chip;
- * 0 for invalid arguments.  Pure host logic. */
+/* Heads per bwd_dxdb and bwd_dc workgroup that ssd_bwd_ex takes for these sizes and options
+ * (NULL = the built-in choice of ssd_bwd): 1, or 4 when dB and dC are summed over slices of four
+ * heads on chip; 0 for invalid arguments.  Pure host logic. */
 int ssd_bwd_heads(const ssd_dims_t* dims, int chunk_size, const ssd_launch_opts_t* opts);
 
 #ifdef __cplusplus

@@ -541,7 +541,7 @@ ssd_status_t bwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   a.dy = z ? static_cast<const void*>(ws + wl.dyg) : dout;
   // (bwd_dc keeps one head per workgroup: four measured 470 -> 801 us at bf16 B8 L4096 H32)
   a.hs_dxdb = pick_bwd_heads(dims, chunk_size, o);
-  a.hs_dc = 1;
+  a.hs_dc = a.hs_dxdb;
   a.gstates = reinterpret_cast<float*>(ws + wl.gstates);
   a.dBh = reinterpret_cast<float*>(ws + wl.dBh);
   a.dCh = reinterpret_cast<float*>(ws + wl.dCh);

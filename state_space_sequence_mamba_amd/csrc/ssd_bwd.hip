@@ -493,7 +493,7 @@ __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, 
 // tile feeds dC[i][:] directly as an MFMA A operand.  The tiles of block J + 1 are loaded
 // into registers while block J is computed.
 template <typename T, int P, int N, bool PRECB, int HS>
-__global__ __launch_bounds__(256) void bwd_dc_kernel(const T* __restrict__ x, const T* __restrict__ Bm,
+__global__ __launch_bounds__(256, 2) void bwd_dc_kernel(const T* __restrict__ x, const T* __restrict__ Bm,
                                                      const T* __restrict__ Cm, const T* __restrict__ dy,
                                                      const float* __restrict__ dtp, const float* __restrict__ dAcs,
                                                      const float* __restrict__ states,
@@ -534,9 +534,11 @@ __global__ __launch_bounds__(256) void bwd_dc_kernel(const T* __restrict__ x, co
 
   RowTile<T, N> tc, tb;
   RowTile<T, P> tdy, tx;
-  f32x4 dcs[TNm];                                  // sum over the slice's heads of dC_h[i][n]
+  // dC[i][n] of this lane, accumulated over the slice's heads in head order (the accumulators are
+  // not reset between heads: one set of registers instead of a per-head set and a sum)
+  f32x4 dc[TNm];
 #pragma unroll
-  for (int m = 0; m < TNm; ++m) dcs[m] = zero4();
+  for (int m = 0; m < TNm; ++m) dc[m] = zero4();
 
 #pragma unroll 1
   for (int hh = 0; hh < hs; ++hh) {
@@ -575,9 +577,6 @@ __global__ __launch_bounds__(256) void bwd_dc_kernel(const T* __restrict__ x, co
   tdy.store(s_dy, tid);
   if (tid < KT) s_SR[tid] = sR;
 
-  f32x4 dc[TNm];
-#pragma unroll
-  for (int m = 0; m < TNm; ++m) dc[m] = zero4();
   float rs = 0.f;                                  // row i = 16 w + r: sum_j T_ij (partial over qd)
   const int il = 16 * w + r;
   for (int J = 0; J <= R; ++J) {
@@ -660,9 +659,6 @@ __global__ __launch_bounds__(256) void bwd_dc_kernel(const T* __restrict__ x, co
 #pragma unroll
         for (int m = 0; m < TNm; ++m) dCh[((row0 + i) * H + h) * (size_t)N + 16 * m + r] = dc[m][e];
       }
-    } else {
-#pragma unroll
-      for (int m = 0; m < TNm; ++m) dcs[m][e] += dc[m][e];
     }
   }
   __syncthreads();
@@ -676,7 +672,7 @@ __global__ __launch_bounds__(256) void bwd_dc_kernel(const T* __restrict__ x, co
     const int i = 16 * w + 4 * qd + e;
     if (i < lenR) {
 #pragma unroll
-      for (int m = 0; m < TNm; ++m) dCh[((row0s + i) * nsl + hsl) * (size_t)N + 16 * m + r] = dcs[m][e];
+      for (int m = 0; m < TNm; ++m) dCh[((row0s + i) * nsl + hsl) * (size_t)N + 16 * m + r] = dc[m][e];
     }
   }
 }

@@ -34,12 +34,12 @@ def _upstream(Bt, L, H, P, N, dtype, seed):
     return dout, dfin
 
 
-def _run(inp, Q, dout, dfin=None, init=None, z=None, dt_limit=None):
+def _run(inp, Q, dout, dfin=None, init=None, z=None, dt_limit=None, opts=None):
     d = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
     out = ssd.ssd_bwd(d["x"], d["dt"], d["dt_bias"], d["A"], d["B"], d["C"], dout.to(DEV), D=d.get("D"),
                       chunk_size=Q, initial_state=None if init is None else init.to(DEV),
                       dfinal_state=None if dfin is None else dfin.to(DEV),
-                      z=None if z is None else z.to(DEV), dt_limit=dt_limit)
+                      z=None if z is None else z.to(DEV), dt_limit=dt_limit, opts=opts)
     torch.cuda.synchronize()
     return {k: (None if v is None else to64(v)) for k, v in out.items()}
 
@@ -94,6 +94,27 @@ def test_bwd_gate_clamp_initial_state(dtype, gate, clamp, init):
     lim = LIMIT if clamp else None
     got = _run(inp, 128, dout, dfin, init=h0, z=z, dt_limit=lim)
     _compare(got, _oracle(inp, dout, dfin, init=h0, z=z, dt_limit=lim), TOL[dtype])
+
+
+@pytest.mark.parametrize("L,Q,init", [(300, 128, False), (517, 256, True)])
+def test_bwd_bf16_head_slices_on_chip(L, Q, init):
+    """bf16 with slices of four heads per bwd_dxdb / bwd_dc workgroup (dB and dC summed over the
+    slice in registers before they leave the chip) and with one head per workgroup: both against
+    the oracle, and dB, dC of the two agree to the rounding of their bf16 outputs."""
+    Bt, H, P, N, G = 2, 8, 64, 128, 2
+    _say(f"bwd bf16 head slices L={L} Q={Q} init={init}")
+    inp = I.make_fwd_inputs(Bt, L, H, P, N, G, "bf16", seed=260 + L, d_init="normal")
+    dout, dfin = _upstream(Bt, L, H, P, N, "bf16", seed=261 + L)
+    h0 = torch.randn(Bt, H, P, N, generator=torch.Generator().manual_seed(262)) if init else None
+    dims = ssd.make_dims(Bt, L, H, P, N, G, torch.bfloat16)
+    assert ssd.bwd_heads(dims, Q, {"bwd_heads": 4}) == 4 and ssd.bwd_heads(dims, Q, {"bwd_heads": 1}) == 1
+    ref = _oracle(inp, dout, dfin, init=h0)
+    four = _run(inp, Q, dout, dfin, init=h0, opts={"bwd_heads": 4})
+    one = _run(inp, Q, dout, dfin, init=h0, opts={"bwd_heads": 1})
+    _compare(four, ref, TOL["bf16"])
+    _compare(one, ref, TOL["bf16"])
+    for k in ("dB", "dC"):
+        assert rel_err(four[k], one[k]) <= 1e-2, k
 
 
 def test_bwd_gate_with_shared_cb_blocks():
