@@ -265,7 +265,9 @@ def backward_cost(w, hs=1):
         "chunk_state_grad": dict(bytes=x + bc + cum + st, flops=2 * B * H * L * P * N),
         "state_passing_rev": dict(bytes=2 * st + 2 * fin + B * H * nc * 4, flops=2 * B * nc * H * P * N),
         # C B^T, dy x^T and the weighted products contract tiles of the input dtype (MFMA in
-        # that dtype); the carried terms through the fp32 state gradients run on fp32 MFMA
+        # that dtype); the carried terms through the fp32 state gradients run on fp32 MFMA for
+        # fp32 inputs and on bf16 MFMA for bf16 inputs (two passes over the gradients' bf16 hi
+        # and lo parts: the algorithmic flops count them once)
         "bwd_dxdb": dict(bytes=2 * x + 2 * bc + 2 * cum + st + x + perh // hs + 3 * B * H * L * 4,
                          flops=2 * N * tri * B * G + 2 * P * tri * B * H * 2 + 2 * N * tri * B * H
                          + 4 * B * H * L * P * N,
@@ -281,7 +283,8 @@ def backward_cost(w, hs=1):
         # on fp32 MFMA except the flops_in share (input-dtype MFMA): the peak is the blend that
         # the split implies, flops / (flops_in / peak_in + rest / peak_f32)
         p_in, p_32 = MFMA_PEAK_TFLOPS[w.dtype], MFMA_PEAK_TFLOPS["f32"]
-        if k.startswith("chunk_state"):
+        if k.startswith("chunk_state") or w.dtype == "bf16":
+            v.pop("flops_in", None)
             v["peak"] = p_in
         else:
             f_in = v.pop("flops_in", 0)
@@ -365,11 +368,12 @@ def run_bwd(w, args, dev, opts=None):
         kernels[k] = {"us": round(per_kernel_ms[k] * 1e3, 3), "bound": c["bound"], "achieved": round(ach, 2),
                       "peak": peak, "unit": unit, "frac": round(ach / peak, 4), "alg_bytes": c["bytes"],
                       "alg_flops": c["flops"]}
-        if c["bound"] == "mfma":
-            # also against the dense MFMA peak of the input dtype alone (the blend above counts the
-            # fp32 share of the products at the fp32 peak)
-            p_in = MFMA_PEAK_TFLOPS[w.dtype]
-            kernels[k]["frac_of_input_dtype_peak"] = round(ach / p_in, 4)
+        if c["flops"]:
+            # the algorithmic flops' rate against the dense MFMA peak of the input dtype alone
+            # (for fp32 inputs the blend above counts nothing else)
+            tf = c["flops"] / t / 1e12
+            kernels[k]["mfma_tflops"] = round(tf, 2)
+            kernels[k]["frac_of_input_dtype_peak"] = round(tf / MFMA_PEAK_TFLOPS[w.dtype], 4)
     dom = max(kernels, key=lambda k: kernels[k]["us"])
     kd = kernels[dom]
     res = {

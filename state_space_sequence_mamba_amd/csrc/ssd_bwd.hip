@@ -120,6 +120,34 @@ __device__ __forceinline__ void stage_state(S* dst, const float* src, int tid) {
   }
 }
 
+// Stage a (P x N) fp32 state as two bf16 arrays of rows of pitch Pitch<bf16, N>: hi = v rounded
+// to bf16 (nearest even) and lo = (v - hi) rounded to bf16, so that hi + lo carries v to about
+// 2^-17 of its magnitude.  A contraction of a bf16 tile with the state then runs as two bf16 MFMA
+// passes (hi, then lo, into one fp32 accumulator) whose products are exact in fp32.
+template <int P, int N>
+__device__ __forceinline__ void stage_state_split(__bf16* hi, __bf16* lo, const float* src, int tid) {
+  constexpr int UNITS = P * N / 4, NIT = (UNITS + 255) / 256, PN = Pitch<__bf16, N>::v;
+  float4 v[NIT];
+#pragma unroll
+  for (int k = 0; k < NIT; ++k) v[k] = reinterpret_cast<const float4*>(src)[min(tid + 256 * k, UNITS - 1)];
+#pragma unroll
+  for (int k = 0; k < NIT; ++k) {
+    const int u = tid + 256 * k;
+    if (u < UNITS) {
+      const int o = ((4 * u) / N) * PN + (4 * u) % N;
+      const float vv[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+      bf16x4 qh, ql;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qh[e] = static_cast<__bf16>(vv[e]);
+        ql[e] = static_cast<__bf16>(vv[e] - static_cast<float>(qh[e]));
+      }
+      *reinterpret_cast<bf16x4*>(hi + o) = qh;
+      *reinterpret_cast<bf16x4*>(lo + o) = ql;
+    }
+  }
+}
+
 // One 16 x 16 tile of A Bt^T over a contraction of length K along both operands' rows:
 //   out[i][j] += sum_k A[i][k] * Bt[j][k]     (A, Bt: 16 rows each, pitch PA / PB)
 // Lane (r, qd) feeds A row r and Bt row r with k = (K/4) qd + 4 m + c, one LDS read each per
@@ -229,7 +257,8 @@ __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, 
   constexpr int hs = HS;
   constexpr int PP = Pitch<T, P>::v, NP = Pitch<T, N>::v, NPF = N + 4, TPm = P / 16, TNm = N / 16;
   constexpr int C_BYTES = KT * NP * (int)sizeof(T), DY_BYTES = KT * PP * (int)sizeof(T);
-  constexpr int G_BYTES = P * NPF * 4;                             // Gnext staged in fp32
+  // Gnext staged in fp32, or for bf16 tiles as bf16 hi and lo parts (stage_state_split)
+  constexpr int G_BYTES = sizeof(T) == 2 ? 2 * P * NP * 2 : P * NPF * 4;
   constexpr int U_BYTES = C_BYTES + DY_BYTES > G_BYTES ? C_BYTES + DY_BYTES : G_BYTES;
   __shared__ __attribute__((aligned(16))) T s_b[KT * NP];       // B of the own block R
   __shared__ __attribute__((aligned(16))) T s_x[KT * PP];       // x of R
@@ -239,6 +268,8 @@ __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, 
   T* s_c = reinterpret_cast<T*>(s_un);
   T* s_dy = reinterpret_cast<T*>(s_un + C_BYTES);
   float* s_g = reinterpret_cast<float*>(s_un);
+  __bf16* s_ghi = reinterpret_cast<__bf16*>(s_un);
+  __bf16* s_glo = s_ghi + P * NP;
 
   // a workgroup takes `hs` consecutive heads of one group (one after the other) and sums their
   // dB contributions in registers, in head order: dB leaves per slice of heads, not per head
@@ -378,9 +409,13 @@ __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, 
       block(std::true_type());
   }
 
-  // carried terms through the gradient of the state leaving the chunk
+  // carried terms through the gradient of the state leaving the chunk (for bf16 tiles on bf16
+  // MFMA: two passes over Gnext's hi and lo parts, B and x being exact in bf16)
   __syncthreads();
-  stage_state<float, P, N>(s_g, gstates + (((size_t)b * nc + c) * H + h) * (size_t)(P * N), tid);
+  if constexpr (sizeof(T) == 2)
+    stage_state_split<P, N>(s_ghi, s_glo, gstates + (((size_t)b * nc + c) * H + h) * (size_t)(P * N), tid);
+  else
+    stage_state<float, P, N>(s_g, gstates + (((size_t)b * nc + c) * H + h) * (size_t)(P * N), tid);
   __syncthreads();
   // lane rows j = 16 w + 4 qd + e from here on
   float f[4], dj[4];
@@ -394,7 +429,13 @@ __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, 
 #pragma unroll
   for (int m = 0; m < TPm; ++m) {
     // tmp[j][p] = sum_n B[j][n] Gnext[p][n]
-    const f32x4 tmp = mm_rows<N, NP, NPF>(zero4(), s_b + 16 * w * NP, s_g + 16 * m * NPF, r, qd);
+    f32x4 tmp;
+    if constexpr (sizeof(T) == 2) {
+      tmp = mm_rows<N, NP, NP>(zero4(), s_b + 16 * w * NP, s_ghi + 16 * m * NP, r, qd);
+      tmp = mm_rows<N, NP, NP>(tmp, s_b + 16 * w * NP, s_glo + 16 * m * NP, r, qd);
+    } else {
+      tmp = mm_rows<N, NP, NPF>(zero4(), s_b + 16 * w * NP, s_g + 16 * m * NPF, r, qd);
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       u[e] += ld1(s_x + (16 * w + 4 * qd + e) * PP + 16 * m + r) * tmp[e];
@@ -404,7 +445,13 @@ __global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, 
 #pragma unroll
   for (int m = 0; m < TNm; ++m) {
     // xg[j][n] = sum_p x[j][p] Gnext[p][n]
-    const f32x4 xg = mm_cols<P, PP, NPF>(zero4(), s_x + 16 * w * PP, s_g, 16 * m, r, qd);
+    f32x4 xg;
+    if constexpr (sizeof(T) == 2) {
+      xg = mm_cols<P, PP, NP>(zero4(), s_x + 16 * w * PP, s_ghi, 16 * m, r, qd);
+      xg = mm_cols<P, PP, NP>(xg, s_x + 16 * w * PP, s_glo, 16 * m, r, qd);
+    } else {
+      xg = mm_cols<P, PP, NPF>(zero4(), s_x + 16 * w * PP, s_g, 16 * m, r, qd);
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) db[m][e] += f[e] * xg[e];
   }
