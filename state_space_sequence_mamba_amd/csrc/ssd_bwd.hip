@@ -182,16 +182,33 @@ __device__ __forceinline__ f32x4 mm_rows(f32x4 acc, const SA* A, const SB* Bt, i
 // operand), and V rows k (pitch PV) are read from LDS at column c0 + r.
 // bf16 tiles: one 16x16x16 bf16 MFMA with M rounded to bf16 (the A operand layout is the same:
 // lane (r, qd) holds k = 4 qd + e), as the forward rounds its weighted C B^T for (L o CB) X.
+typedef short bwd_i16x4 __attribute__((ext_vector_type(4)));
+typedef float bwd_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bwd_bf16x2 __attribute__((ext_vector_type(2)));
+// Four consecutive rows of one column of a bf16 LDS tile as an MFMA B operand, in one transpose
+// read (ds_read_b64_tr_b16): in each group of 16 lanes, with M[j][q] the q-th 16-bit element at
+// lane j's 8-byte address, lane i receives M[4 k + i / 4][i % 4], k = 0..3.  Lane j of group qd
+// points at row row0 + j / 4, columns c0 + 4 (j % 4) .. + 3, so lane (r, qd) receives
+// V[row0 + k][c0 + r]: row0 = the group's first row (pitch PV and c0 multiples of 4: 8-byte
+// aligned addresses).
+template <int PV>
+__device__ __forceinline__ bf16x4 col4_tr(const __bf16* V, int row0, int c0, int r) {
+  const __bf16* p = V + (row0 + r / 4) * PV + c0 + 4 * (r % 4);
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                        (__attribute__((address_space(3))) bwd_i16x4*)(p)));
+}
+// four fp32 values rounded to bf16 (nearest even) by two two-value conversions
+__device__ __forceinline__ bf16x4 round4(const f32x4& m) {
+  const bwd_bf16x2 lo = __builtin_convertvector((bwd_f32x2{m[0], m[1]}), bwd_bf16x2);
+  const bwd_bf16x2 hi = __builtin_convertvector((bwd_f32x2{m[2], m[3]}), bwd_bf16x2);
+  return bf16x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
 template <int PV, typename SV>
 __device__ __forceinline__ f32x4 mm_regs(f32x4 acc, const f32x4& m, const SV* V, int c0, int r, int qd) {
   if constexpr (sizeof(SV) == 2) {
-    bf16x4 a, b;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      a[e] = static_cast<__bf16>(m[e]);
-      b[e] = V[(4 * qd + e) * PV + c0 + r];
-    }
-    acc = mfma_16x16x16_bf16(a, b, acc);
+    static_assert(PV % 4 == 0, "8-byte aligned transpose reads");
+    acc = mfma_16x16x16_bf16(round4(m), col4_tr<PV>(V, 4 * qd, c0, r), acc);
   } else {
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc = mfma_16x16x4_f32(m[e], ld1(V + (4 * qd + e) * PV + c0 + r), acc);
@@ -208,11 +225,9 @@ __device__ __forceinline__ f32x4 mm_cols(f32x4 acc, const SA* A, const SV* V, in
   for (int m = 0; m < K / 16; ++m) {
     const int k0 = (K / 4) * qd + 4 * m;
     if constexpr (sizeof(SA) == 2 && sizeof(SV) == 2) {
+      static_assert(PV % 4 == 0, "8-byte aligned transpose reads");
       const bf16x4 a = *reinterpret_cast<const bf16x4*>(A + r * PA + k0);
-      bf16x4 b;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) b[e] = V[(k0 + e) * PV + c0 + r];
-      acc = mfma_16x16x16_bf16(a, b, acc);
+      acc = mfma_16x16x16_bf16(a, col4_tr<PV>(V, k0, c0, r), acc);
     } else {
       const float4 a = ld4(A + r * PA + k0);
       acc = mfma_16x16x4_f32(a.x, ld1(V + (k0 + 0) * PV + c0 + r), acc);
@@ -244,7 +259,7 @@ __device__ __forceinline__ float sum_qd(float v) {
 // and feeds them straight into xi[j][:] and dB[j][:] as MFMA A operands.  The tiles of block
 // I + 1 are loaded into registers while block I is computed.
 template <typename T, int P, int N, bool PRECB, int HS>
-__global__ __launch_bounds__(256) void bwd_dxdb_kernel(const T* __restrict__ x, const T* __restrict__ Bm,
+__global__ __launch_bounds__(256, 2) void bwd_dxdb_kernel(const T* __restrict__ x, const T* __restrict__ Bm,
                                                        const T* __restrict__ Cm, const T* __restrict__ dy,
                                                        const float* __restrict__ dtp, const float* __restrict__ dAcs,
                                                        const float* __restrict__ gstates,
