@@ -358,6 +358,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dxdb_kernel(const T* __restrict__ 
   for (int m = 0; m < TNm; ++m) db[m] = zero4();
   float cs = 0.f;                                  // column j = 16 w + r: sum_i M1 DX (partial over qd)
   const int jl = 16 * w + r;                       // this lane's column of R
+  // bf16: the own block's dy at the lane's output positions (rows j = 16 w + 4 qd + e, columns
+  // p = 16 m + r), taken from the staged tile of the first block (I = R) for the skip term and
+  // the dD partial at the end, instead of global loads there
+  bf16x4 dyR[TPm];
 
   const int nI = (len + KT - 1) / KT;
   // PRECB: the C B^T sub-tiles (row tiles of block I, own column tile w of R) come from the
@@ -386,6 +390,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dxdb_kernel(const T* __restrict__ 
       sI = dAcs[cq + (I + 1) * KT + tk];
     }
     __syncthreads();
+    if constexpr (sizeof(T) == 2) {
+      if (I == R) {
+#pragma unroll
+        for (int m = 0; m < TPm; ++m) dyR[m] = col4_tr<PP>(s_dy, 16 * w + 4 * qd, 16 * m, r);
+      }
+    }
     const float sj = s_SR[jl];
     // MASK: the diagonal block or a block that crosses the end of the sequence; other blocks
     // (every i after every j, all rows real) run as straight-line code without the mask
@@ -495,7 +505,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dxdb_kernel(const T* __restrict__ 
 #pragma unroll
     for (int m = 0; m < TPm; ++m) {
       const int p = 16 * m + r;
-      const float dyv = ok ? to_f32(dy[tok * xs + (size_t)h * P + p]) : 0.f;
+      float dyv;
+      if constexpr (sizeof(T) == 2)
+        dyv = ok ? static_cast<float>(dyR[m][e]) : 0.f;
+      else
+        dyv = ok ? to_f32(dy[tok * xs + (size_t)h * P + p]) : 0.f;
       const float dw = Dw ? Dw[(size_t)h * P + p] : 0.f;
       if (ok) dx[tok * xs + (size_t)h * P + p] = from_f32<T>(dw * dyv + dj[e] * xi[m][e]);
       dDp[m] += dyv * ld1(s_x + j * PP + p);
