@@ -451,6 +451,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dxdb_kernel(const T* __restrict__ 
     dj[e] = s_dR[j];
   }
   float u[4] = {0.f, 0.f, 0.f, 0.f};
+  // x of the own block at the lane's positions (rows j = 16 w + 4 qd + e, columns p = 16 m + r):
+  // for bf16 tiles by transpose reads, once for the carried terms, dd and the dD partial
+  auto x_at = [&](int m, int e) -> float { return ld1(s_x + (16 * w + 4 * qd + e) * PP + 16 * m + r); };
+  bf16x4 xR[TPm];
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int m = 0; m < TPm; ++m) xR[m] = col4_tr<PP>(s_x, 16 * w + 4 * qd, 16 * m, r);
+  }
+  auto xv = [&](int m, int e) -> float {
+    if constexpr (sizeof(T) == 2) return static_cast<float>(xR[m][e]);
+    else return x_at(m, e);
+  };
 #pragma unroll
   for (int m = 0; m < TPm; ++m) {
     // tmp[j][p] = sum_n B[j][n] Gnext[p][n]
@@ -463,7 +475,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dxdb_kernel(const T* __restrict__ 
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      u[e] += ld1(s_x + (16 * w + 4 * qd + e) * PP + 16 * m + r) * tmp[e];
+      u[e] += xv(m, e) * tmp[e];
       xi[m][e] += f[e] * tmp[e];
     }
   }
@@ -483,10 +495,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dxdb_kernel(const T* __restrict__ 
   float U[4], dd[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int j = 16 * w + 4 * qd + e;
     float q = 0.f;
 #pragma unroll
-    for (int m = 0; m < TPm; ++m) q += ld1(s_x + j * PP + 16 * m + r) * xi[m][e];
+    for (int m = 0; m < TPm; ++m) q += xv(m, e) * xi[m][e];
     U[e] = f[e] * dj[e] * sum_r(u[e]);
     dd[e] = sum_r(q);
   }
@@ -512,7 +523,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dxdb_kernel(const T* __restrict__ 
         dyv = ok ? to_f32(dy[tok * xs + (size_t)h * P + p]) : 0.f;
       const float dw = Dw ? Dw[(size_t)h * P + p] : 0.f;
       if (ok) dx[tok * xs + (size_t)h * P + p] = from_f32<T>(dw * dyv + dj[e] * xi[m][e]);
-      dDp[m] += dyv * ld1(s_x + j * PP + p);
+      dDp[m] += dyv * xv(m, e);
     }
     if constexpr (HS == 1) {                       // one head: dB straight out
       if (ok) {
@@ -717,10 +728,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dc_kernel(const T* __restrict__ x,
   for (int m = 0; m < TNm; ++m) {
     // cr[i][n] = sum_p dy[i][p] Hprev[p][n]
     const f32x4 cr = mm_cols<P, PP, NP>(zero4(), s_dy + 16 * w * PP, s_h, 16 * m, r, qd);
+    // C[i][n] at the lane's positions (rows i = 16 w + 4 qd + e, column n = 16 m + r); for bf16
+    // tiles one transpose read
+    bf16x4 cT;
+    if constexpr (sizeof(T) == 2) cT = col4_tr<NP>(s_c, 16 * w + 4 * qd, 16 * m, r);
+    auto cv = [&](int e) -> float {
+      if constexpr (sizeof(T) == 2) return static_cast<float>(cT[e]);
+      else return ld1(s_c + (16 * w + 4 * qd + e) * NP + 16 * m + r);
+    };
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int i = 16 * w + 4 * qd + e;
-      rr[e] += cr[e] * ld1(s_c + i * NP + 16 * m + r);
+      rr[e] += cr[e] * cv(e);
       dc[m][e] += ei[e] * cr[e];
     }
   }
