@@ -39,10 +39,11 @@ KERNELS = ["chunk_state", "state_passing", "chunk_scan"]
 MAX_WORKERS = 16          # the host's CPU share per GPU
 
 
-def algorithmic_cost(w, seg_chunks=0):
+def algorithmic_cost(w, seg_chunks=0, gate=False):
     """Bytes each kernel must move (its inputs once, its outputs once) and the flops it must
     do (causal half of the in-chunk products, C B^T once per group), per launch.  seg_chunks:
-    chunks per segment on the segmented chunk-state path (0 = not that path)."""
+    chunks per segment on the segmented chunk-state path (0 = not that path); gate: the output
+    gate's z (x's shape) is read once more by chunk_scan."""
     e = 4 if w.dtype == "f32" else 2
     B, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
     nc = (L + Q - 1) // Q
@@ -74,7 +75,7 @@ def algorithmic_cost(w, seg_chunks=0):
         # fp32 reads the C B^T blocks back once per head; bf16 forms C B^T inside chunk_scan
         # (segmented states: also each segment's incoming state, bf16, once per segment)
         "chunk_scan": dict(bytes=2 * x + (cbr if pre else 2 * bc) + cum + (st if pre else st // 2) + H * P * 4
-                           + (nseg * B * H * P * N * 2 if seg_chunks else 0),
+                           + (nseg * B * H * P * N * 2 if seg_chunks else 0) + (x if gate else 0),
                            flops=2 * B * H * P * tri + 2 * B * H * L * N * P + (0 if pre else 2 * B * G * N * tri)),
         # segmented: dt in, dt' and the cumsum out, x and B once, the states each segment carried
         # into its chunks out (bf16, none for a segment's first chunk), the segments' end states
@@ -674,7 +675,7 @@ def run_fwd(w, args, dev, opts, with_cpu):
             if k:
                 per_kernel_ms[k] += hev.elapsed_ms(evs[2 * i], evs[2 * i + 1]) / K
 
-    cost = algorithmic_cost(w, ssd.fwd_state_segment_chunks(dims, w.chunk, opts))
+    cost = algorithmic_cost(w, ssd.fwd_state_segment_chunks(dims, w.chunk, opts), gate=z is not None)
     kernels = {}
     for k in per_kernel_ms:
         t = per_kernel_ms[k] * 1e-3
