@@ -157,7 +157,8 @@ ssd_status_t ssd_step(const ssd_dims_t* dims, float* state,
 
 /* Workspace bytes ssd_bwd needs for these sizes and chunk size, with or without a gate
  * (with_gate != 0 adds room for the pre-gate output and the gated gradient).  0 if the sizes
- * are invalid or unsupported.  The workspace holds the recomputed forward intermediates, the
+ * are invalid or unsupported.  The workspace holds the recomputed forward intermediates (for
+ * bf16 inputs with a bf16 copy of the entering states, B * nc * H * P * N bf16), the
  * state gradients of every chunk (2 * B * nc * H * P * N fp32), per-head dB and dC
  * (2 * B * L * H * N fp32) and small per-token and per-chunk partials. */
 size_t ssd_bwd_workspace_size(const ssd_dims_t* dims, int chunk_size, int with_gate);

@@ -442,7 +442,7 @@ BwdLayout bwd_layout(const ssd_dims_t* d, int Q, bool gate) {
   w.dyg = o; o += act;
   w.cb = o; o += (gate || d->dtype == SSD_F32) ? cb_bytes(d, Q) : 0;
   w.cbT = o; o += d->dtype == SSD_F32 ? cb_bytes(d, Q) : 0;
-  w.prev16 = o; o += gate ? prev16_bytes(d, Q) : 0;
+  w.prev16 = o; o += prev16_bytes(d, Q);                // (bf16 only: zero bytes for fp32)
   w.total = o;
   return w;
 }
@@ -526,8 +526,10 @@ ssd_status_t bwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   f.cb = cb_shared(dims) && (z || dims->dtype == SSD_F32) ? reinterpret_cast<float*>(ws + wl.cb) : nullptr;
   // fp32: the same blocks transposed for bwd_dxdb
   f.cbT = dims->dtype == SSD_F32 ? reinterpret_cast<float*>(ws + wl.cbT) : nullptr;
-  f.prev16 = z && dims->dtype == SSD_BF16 ? static_cast<void*>(ws + wl.prev16) : nullptr;
-  f.keep_f32_states = 1;                              // the backward kernels read the fp32 states
+  // bf16: state_passing also writes the entering states rounded to bf16, which bwd_dc stages
+  // (and the gated path's pre-gate chunk_scan reads)
+  f.prev16 = dims->dtype == SSD_BF16 ? static_cast<void*>(ws + wl.prev16) : nullptr;
+  f.keep_f32_states = 1;                              // bwd_finalize (and fp32 bwd_dc) read the fp32 states
   f.scan_variant = pick_scan_variant(dims, chunk_size, o);
   f.rows_group = pick_rows_group(o);
   f.heads_per_block = pick_heads_per_block(f.B, f.nc, f.H, f.G, f.scan_variant, o);
@@ -539,7 +541,6 @@ ssd_status_t bwd_impl(const ssd_dims_t* dims, const void* x, const void* dt, con
   f.cdec = nullptr;
   f.ev0 = f.ev1 = nullptr;
   a.dy = z ? static_cast<const void*>(ws + wl.dyg) : dout;
-  // (bwd_dc keeps one head per workgroup: four measured 470 -> 801 us at bf16 B8 L4096 H32)
   a.hs_dxdb = pick_bwd_heads(dims, chunk_size, o);
   a.hs_dc = a.hs_dxdb;
   a.gstates = reinterpret_cast<float*>(ws + wl.gstates);

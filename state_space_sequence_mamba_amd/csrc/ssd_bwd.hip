@@ -32,7 +32,10 @@
 // Token tiles are staged in LDS in the input dtype (bf16 -> fp32 is exact, so the fp32 MFMA
 // arithmetic is the same either way and bf16 tiles take half the LDS), with row pitches that
 // start consecutive rows on different banks; the fp32 state tiles (Hprev, Gnext) reuse the
-// space of the token tiles once those are consumed.
+// space of the token tiles once those are consumed.  For bf16 inputs every product runs on bf16
+// MFMA: the weighted tiles are rounded to bf16 (as the forward rounds its weighted C B^T), Hprev
+// is rounded to bf16 (as the forward's carried term reads it), and Gnext, a gradient the forward
+// never rounds, is split into bf16 hi and lo parts contracted in two exact passes.
 #include <type_traits>
 
 #include "cb_tiles.h"
@@ -145,6 +148,20 @@ __device__ __forceinline__ void stage_state_split(__bf16* hi, __bf16* lo, const 
       *reinterpret_cast<bf16x4*>(hi + o) = qh;
       *reinterpret_cast<bf16x4*>(lo + o) = ql;
     }
+  }
+}
+
+// Stage a (P x N) bf16 state as rows of pitch Pitch<bf16, N> (16-byte vectors, copied as they are).
+template <int P, int N>
+__device__ __forceinline__ void stage_state16(__bf16* dst, const __bf16* src, int tid) {
+  constexpr int UNITS = P * N / 8, NIT = (UNITS + 255) / 256, PN = Pitch<__bf16, N>::v;
+  uint4 v[NIT];
+#pragma unroll
+  for (int k = 0; k < NIT; ++k) v[k] = reinterpret_cast<const uint4*>(src)[min(tid + 256 * k, UNITS - 1)];
+#pragma unroll
+  for (int k = 0; k < NIT; ++k) {
+    const int u = tid + 256 * k;
+    if (u < UNITS) *reinterpret_cast<uint4*>(dst + ((8 * u) / N) * PN + (8 * u) % N) = v[k];
   }
 }
 
@@ -584,6 +601,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dc_kernel(const T* __restrict__ x,
                                                      const T* __restrict__ Cm, const T* __restrict__ dy,
                                                      const float* __restrict__ dtp, const float* __restrict__ dAcs,
                                                      const float* __restrict__ states,
+                                                     const __bf16* __restrict__ states16,
                                                      const float* __restrict__ cbp, float* __restrict__ dCh,
                                                      float* __restrict__ dSc, int L, int H, int G, int nc, int Q,
                                                      uint32_t nblocks) {
@@ -717,7 +735,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dc_kernel(const T* __restrict__ x,
       block(std::true_type());
   }
   __syncthreads();
-  stage_state<T, P, N>(s_h, states + (((size_t)b * nc + c) * H + h) * (size_t)(P * N), tid);
+  // Hprev in T; for bf16, the copy state_passing rounded to bf16 when it wrote the states (the
+  // same rounding, half the bytes) when there is one
+  if constexpr (sizeof(T) == 2) {
+    if (states16)
+      stage_state16<P, N>(s_h, states16 + (((size_t)b * nc + c) * H + h) * (size_t)(P * N), tid);
+    else
+      stage_state<T, P, N>(s_h, states + (((size_t)b * nc + c) * H + h) * (size_t)(P * N), tid);
+  } else {
+    stage_state<T, P, N>(s_h, states + (((size_t)b * nc + c) * H + h) * (size_t)(P * N), tid);
+  }
   __syncthreads();
   // lane rows i = 16 w + 4 qd + e from here on
   const size_t row0 = (size_t)b * L + t0 + R * KT;
@@ -998,8 +1025,8 @@ static hipError_t launch_dc_hs(const BwdArgs& a, hipStream_t s) {
   hipExtLaunchKernelGGL(kern, dim3(nblocks),
       dim3(256), 0, s, f.ev0, f.ev1, 0,
       static_cast<const T*>(f.x), static_cast<const T*>(f.Bm), static_cast<const T*>(f.Cm),
-      static_cast<const T*>(a.dy), f.dtp, f.dAcs, f.states, f.cb, a.dCh, a.dSc, f.L, f.H, f.G, f.nc, f.Q,
-      nblocks);
+      static_cast<const T*>(a.dy), f.dtp, f.dAcs, f.states, static_cast<const __bf16*>(f.prev16), f.cb, a.dCh,
+      a.dSc, f.L, f.H, f.G, f.nc, f.Q, nblocks);
   return hipGetLastError();
 }
 
