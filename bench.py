@@ -260,7 +260,9 @@ def backward_cost(w, hs=1):
     perh = B * L * H * N * 4
     cost = {
         "chunk_state": dict(bytes=B * L * H * e + 8 * H + cum + x + bc + st, flops=2 * B * H * L * P * N),
-        "state_passing": dict(bytes=2 * st + B * H * nc * 4, flops=2 * B * nc * H * P * N),
+        # (bf16: also the entering states rounded to bf16, which bwd_dc reads)
+        "state_passing": dict(bytes=2 * st + (st // 2 if e == 2 else 0) + B * H * nc * 4,
+                              flops=2 * B * nc * H * P * N),
         "gate_fwd": dict(bytes=0, flops=0),
         "gate_bwd": dict(bytes=0, flops=0),
         "chunk_state_grad": dict(bytes=x + bc + cum + st, flops=2 * B * H * L * P * N),
@@ -273,7 +275,7 @@ def backward_cost(w, hs=1):
                          flops=2 * N * tri * B * G + 2 * P * tri * B * H * 2 + 2 * N * tri * B * H
                          + 4 * B * H * L * P * N,
                          flops_in=2 * N * tri * B * G + 2 * P * tri * B * H * 2 + 2 * N * tri * B * H),
-        "bwd_dc": dict(bytes=2 * x + 2 * bc + 2 * cum + st + perh // hs + B * H * L * 4,
+        "bwd_dc": dict(bytes=2 * x + 2 * bc + 2 * cum + (st // 2 if e == 2 else st) + perh // hs + B * H * L * 4,
                        flops=2 * N * tri * B * H + 2 * B * H * L * P * N,
                        flops_in=2 * N * tri * B * H),
         "bwd_finalize": dict(bytes=2 * st + 5 * cum + B * L * H * e * 2, flops=2 * B * nc * H * P * N),
