@@ -17,7 +17,7 @@ namespace ssd {
 
 namespace {
 
-constexpr int kNThreads = 256;                   // four wavefronts, one (token, group) each
+constexpr int kNThreads = 512;                   // eight wavefronts, one (token, group) each
 
 template <typename T>
 struct Vec8;
@@ -68,47 +68,68 @@ __device__ __forceinline__ void gated(const T* y, const T* z, size_t o, float (&
 }  // namespace
 
 // Groups of up to kRegChunks * 512 channels keep g in registers between the sum of squares and
-// the output (one read of y and z); larger groups read them twice (the second time from cache).
+// the output (one read of y and z); a workgroup then takes one group of kTokens * 8 consecutive
+// tokens (kTokens per wavefront) with the group's weights staged once in LDS, instead of every
+// wavefront reading them for its token.  Larger groups take one (token, group) per wavefront and
+// read y and z twice (the second time from cache).
 constexpr int kRegChunks = 10;
+constexpr int kTokens = 1;
+
+__host__ __device__ inline uint32_t norm_workgroups(uint32_t tokens, int gl, int gpt) {
+  constexpr uint32_t per = kTokens * (kNThreads / 64);
+  return gl <= kRegChunks * 512 ? (tokens + per - 1) / per * (uint32_t)gpt
+                                : (tokens * (uint32_t)gpt + kNThreads / 64 - 1) / (kNThreads / 64);
+}
 
 template <typename T>
 __global__ __launch_bounds__(kNThreads) void gated_rmsnorm_kernel(const T* __restrict__ y, const T* __restrict__ z,
                                                                  const float* __restrict__ weight, T* out,
-                                                                 uint32_t nunits, int gl, int gpt, float eps) {
-  const uint32_t unit = blockIdx.x * (kNThreads / 64) + (threadIdx.x >> 6);   // (token, group)
-  if (unit >= nunits) return;                                                // (whole wavefronts)
-  const int lane = threadIdx.x & 63;
-  const uint32_t tok = unit / gpt, grp = unit % gpt;
-  const size_t base = ((size_t)tok * gpt + grp) * gl;
-  const float* wg = weight + (size_t)grp * gl;
-  float ss = 0.f;
+                                                                 uint32_t tokens, int gl, int gpt, float eps) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (gl <= kRegChunks * 512) {
-    float g[kRegChunks][8];
+    __shared__ __attribute__((aligned(16))) float s_w[kRegChunks * 512];
+    const uint32_t grp = blockIdx.x % gpt, tb = blockIdx.x / gpt;
+    const float* wg = weight + (size_t)grp * gl;
+    for (int i = 4 * threadIdx.x; i < gl; i += 4 * kNThreads)
+      *reinterpret_cast<float4*>(&s_w[i]) = *reinterpret_cast<const float4*>(wg + i);
+    __syncthreads();
+    const uint32_t t0 = (tb * (kNThreads / 64) + wave) * kTokens, t1 = min(t0 + kTokens, tokens);
+    for (uint32_t tok = t0; tok < t1; ++tok) {
+      const size_t base = ((size_t)tok * gpt + grp) * gl;
+      float g[kRegChunks][8];
+      float ss = 0.f;
 #pragma unroll
-    for (int c = 0; c < kRegChunks; ++c) {
-      const int i = c * 512 + 8 * lane;
-      if (i < gl) {
-        gated(y, z, base + i, g[c]);
+      for (int c = 0; c < kRegChunks; ++c) {
+        const int i = c * 512 + 8 * lane;
+        if (i < gl) {
+          gated(y, z, base + i, g[c]);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) ss += g[c][k] * g[c][k];
+          for (int k = 0; k < 8; ++k) ss += g[c][k] * g[c][k];
+        }
       }
-    }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
-    const float scale = 1.0f / sqrtf(ss / (float)gl + eps);
+      for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+      const float scale = 1.0f / sqrtf(ss / (float)gl + eps);
 #pragma unroll
-    for (int c = 0; c < kRegChunks; ++c) {
-      const int i = c * 512 + 8 * lane;
-      if (i < gl) {
-        const float4 w0 = *reinterpret_cast<const float4*>(wg + i), w1 = *reinterpret_cast<const float4*>(wg + i + 4);
-        const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      for (int c = 0; c < kRegChunks; ++c) {
+        const int i = c * 512 + 8 * lane;
+        if (i < gl) {
+          const float4 w0 = *reinterpret_cast<const float4*>(&s_w[i]), w1 = *reinterpret_cast<const float4*>(&s_w[i + 4]);
+          const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
-        for (int k = 0; k < 8; ++k) g[c][k] = g[c][k] * scale * wv[k];
-        Vec8<T>::store(out + base + i, g[c]);
+          for (int k = 0; k < 8; ++k) g[c][k] = g[c][k] * scale * wv[k];
+          Vec8<T>::store(out + base + i, g[c]);
+        }
       }
     }
     return;
   }
+  const uint32_t unit = blockIdx.x * (kNThreads / 64) + wave;                 // (token, group)
+  if (unit >= tokens * (uint32_t)gpt) return;                                // (whole wavefronts)
+  const uint32_t tok = unit / gpt, grp = unit % gpt;
+  const size_t base = ((size_t)tok * gpt + grp) * gl;
+  const float* wg = weight + (size_t)grp * gl;
+  float ss = 0.f;
   for (int i = 8 * lane; i < gl; i += 8 * 64) {
     float g[8];
     gated(y, z, base + i, g);
@@ -130,18 +151,18 @@ __global__ __launch_bounds__(kNThreads) void gated_rmsnorm_kernel(const T* __res
 }
 
 hipError_t launch_gated_rmsnorm(const NormArgs& a, hipStream_t s) {
-  const uint32_t nunits = (uint32_t)(a.tokens * (a.H / a.norm_heads));
-  if (nunits == 0) return hipSuccess;
   const int gl = a.norm_heads * a.P, gpt = a.H / a.norm_heads;
-  const dim3 grid((nunits + kNThreads / 64 - 1) / (kNThreads / 64));
+  const uint32_t nwg = norm_workgroups((uint32_t)a.tokens, gl, gpt);
+  if (nwg == 0) return hipSuccess;
+  const dim3 grid(nwg);
   if (a.dtype == DT_BF16)
     hipExtLaunchKernelGGL(gated_rmsnorm_kernel<__bf16>, grid, dim3(kNThreads), 0, s, a.ev0, a.ev1, 0,
                           static_cast<const __bf16*>(a.y), static_cast<const __bf16*>(a.z), a.weight,
-                          static_cast<__bf16*>(a.out), nunits, gl, gpt, a.eps);
+                          static_cast<__bf16*>(a.out), (uint32_t)a.tokens, gl, gpt, a.eps);
   else
     hipExtLaunchKernelGGL(gated_rmsnorm_kernel<float>, grid, dim3(kNThreads), 0, s, a.ev0, a.ev1, 0,
                           static_cast<const float*>(a.y), static_cast<const float*>(a.z), a.weight,
-                          static_cast<float*>(a.out), nunits, gl, gpt, a.eps);
+                          static_cast<float*>(a.out), (uint32_t)a.tokens, gl, gpt, a.eps);
   return hipGetLastError();
 }
 
