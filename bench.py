@@ -157,8 +157,12 @@ def cpu_baseline(w, inp, y_gpu, budget_s):
             "sample": f"float64 sequential recurrence over the first {T} of {w.seqlen} tokens of batch row 0 "
                       f"(all {w.nheads} heads, {workers} threads of numpy), {secs:.2f} s",
             "cpu_model": cpu_model(), "host_cores": len(os.sched_getaffinity(0))}
-    parity = {"tokens": T, "batch_row": 0, "rel_err": err, "p99_9_rel_err": p999,
-              "tolerance": 1e-4 if w.dtype == "f32" else 2e-2}
+    # rel_err = max |gpu - oracle| / max |oracle| is the quantity the tolerance bounds; the 99.9th
+    # percentile of the elementwise |gpu - oracle| / (|oracle| + 1e-3 max |oracle|) is reported
+    # beside it without a bar (near-zero outputs make elementwise ratios large by construction)
+    parity = {"tokens": T, "batch_row": 0, "rel_err": err, "rel_err_tolerance": 1e-4 if w.dtype == "f32" else 2e-2,
+              "within_tolerance": bool(err <= (1e-4 if w.dtype == "f32" else 2e-2)),
+              "p99_9_elementwise_rel_err": p999}
     return base, parity
 
 
