@@ -75,10 +75,11 @@ __device__ __forceinline__ void gated(const T* y, const T* z, size_t o, float (&
 constexpr int kRegChunks = 10;
 constexpr int kTokens = 1;
 
+// (64-bit arithmetic: tokens * gpt may come within a few units of 2^32)
 __host__ __device__ inline uint32_t norm_workgroups(uint32_t tokens, int gl, int gpt) {
-  constexpr uint32_t per = kTokens * (kNThreads / 64);
-  return gl <= kRegChunks * 512 ? (tokens + per - 1) / per * (uint32_t)gpt
-                                : (tokens * (uint32_t)gpt + kNThreads / 64 - 1) / (kNThreads / 64);
+  constexpr uint64_t per = kTokens * (kNThreads / 64);
+  return (uint32_t)(gl <= kRegChunks * 512 ? ((uint64_t)tokens + per - 1) / per * (uint64_t)gpt
+                                           : ((uint64_t)tokens * gpt + kNThreads / 64 - 1) / (kNThreads / 64));
 }
 
 template <typename T>
